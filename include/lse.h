@@ -1,0 +1,159 @@
+/*
+ * lse.h — C ABI of the MI355X (gfx950) max-shifted log-sum-exp engine.
+ *
+ * Every operation here evaluates  LSE(v) = m + log(sum_i exp(v_i - m)),
+ * m = max_i v_i, over some set of fp32 values, in one of three layouts.
+ * Sources, cited by page and passage (three kernel-benchmark transcripts):
+ *   [LSE0]  POPCORNBENCH FW-GLM-5-1 l1_p29 — torch.logsumexp(x, dim=0) on an
+ *           (R,B,D) tensor; the benchmark spec and the max / sum / log plan.
+ *   [LSM]   POPCORNBENCH Kimi-K2.6 l1_p24 — LogSoftmax over dim 1 of
+ *           (4096, 393216); the opening formula, the online (max, sum)
+ *           recurrence, the pairwise combine and the multi-block-per-row idea.
+ *   [CHAIN] POPCORNBENCH Kimi-K2.6 l2_p92 — Conv2d -> GroupNorm -> Tanh ->
+ *           Hardswish -> residual add -> LogSumExp over dim 1.
+ *
+ * Conventions for every entry point:
+ *   - Data pointers are DEVICE pointers the caller owns (allocated with
+ *     hipMalloc or a framework allocator on the current device).  The library
+ *     never allocates, frees or synchronises; every call only enqueues kernels
+ *     on `stream` (0 = the null stream) and returns.
+ *   - All tensors are fp32, dense and row-major (C order).  Sizes are int64.
+ *     Any pointer alignment is accepted; 16-byte aligned pointers with the
+ *     innermost size a multiple of 4 take the 128-bit load path.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     failure nothing is launched, a status != LSE_OK is returned and
+ *     lse_last_error() describes it (thread-local string, valid until the next
+ *     call on the same thread).  LSE_ERR_HIP reports a failed launch.
+ *   - Non-finite values follow log(sum(exp(v))) literally: -inf entries are
+ *     ignored (exp(-inf) = 0); all entries -inf gives -inf; any +inf gives
+ *     +inf; any NaN gives NaN.  log_softmax is x - LSE(row) elementwise.
+ *   - Outputs must not overlap inputs (LSE_ERR_OVERLAP where detectable).
+ *   - Concurrent calls that share a workspace race; give each in-flight call
+ *     its own workspace.
+ */
+#ifndef LSE_MI355X_H
+#define LSE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One (max, sum) partial of a set of values: LSE(set) = m + log(s).
+ *   m = largest non-NaN value (-inf if none);
+ *   s = sum of exp(v - m): 0 when m = -inf; when m = +inf, the number of +inf
+ *       values; NaN when the set holds a NaN.
+ * The identity of the combine is {-inf, 0}.                 [LSM] pairwise combine */
+typedef struct lse_pair_t {
+  float m;
+  float s;
+} lse_pair_t;
+
+typedef enum lse_status_t {
+  LSE_OK = 0,
+  LSE_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  LSE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent           */
+  LSE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
+  LSE_ERR_OVERLAP = 4,     /* an output overlaps an input                      */
+  LSE_ERR_HIP = 5,         /* the HIP runtime reported an error on launch      */
+  LSE_ERR_UNSUPPORTED = 6  /* valid request outside what this build implements */
+} lse_status_t;
+
+/* Short static name of a status code ("LSE_OK", ...). */
+const char *lse_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *lse_last_error(void);
+/* ABI version of this header (bumped on any incompatible change). */
+int lse_abi_version(void);
+#define LSE_ABI_VERSION 1
+
+/* ---------------------------------------------------------------- case A
+ * logsumexp over the leading axis.                   [LSE0] task statement
+ *   out[j] = LSE_{r < R} x[r * inner + j],   0 <= j < inner.
+ * x: (R, inner) row-major, i.e. an (R, B, D) tensor reduced over dim 0 has
+ * inner = B * D.  out: inner floats.  R >= 1, inner >= 0 (inner == 0 is a
+ * no-op).  out must not overlap x. */
+lse_status_t lse_reduce_axis0(const float *x, float *out, int64_t R,
+                              int64_t inner, hipStream_t stream);
+
+/* ---------------------------------------------------------------- case B
+ * Row-wise log_softmax over the last axis.           [LSM] opening formula
+ *   y[r, c] = x[r, c] - LSE_c x[r, :],   (rows, cols) row-major.
+ * Rows longer than one workgroup's register tile are split across several
+ * workgroups whose (max, sum) partials are merged through `ws`
+ *                                           [LSM] multi-block-per-row idea.
+ * ws: device workspace of at least log_softmax_rows_workspace_bytes(rows,
+ * cols) bytes (0 for short rows, in which case ws may be NULL).  Its contents
+ * on entry are irrelevant: the call clears what it uses with a kernel on
+ * `stream`.  y must not overlap x (no in-place).  rows >= 0, cols >= 1. */
+size_t log_softmax_rows_workspace_bytes(int64_t rows, int64_t cols);
+lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows,
+                              int64_t cols, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+/* Bound on how long a workgroup of a split row polls for its row's partials
+ * (default 2^24 polls; independently, a workgroup never waits longer than
+ * about 0.1 s, far beyond any real wait).  A workgroup that runs out
+ * writes NaN for its chunk and sets the 32-bit word at byte offset 4 of the
+ * workspace to nonzero.  Affects calls enqueued after it returns; intended
+ * for tests of that failure path. */
+void lse_set_spin_limit(uint32_t polls);
+/* The split log_softmax_rows will use for a row length: *nchunks workgroups
+ * per row, each covering *chunk consecutive columns (the last may be short).
+ * Host-only; enqueues nothing. */
+lse_status_t log_softmax_rows_plan(int64_t cols, int64_t *nchunks,
+                                   int64_t *chunk);
+
+/* Case B building blocks: per-chunk partials, then their merge.  Together
+ * they give the row logsumexp of a row split across workgroups (or across
+ * devices, by merging gathered partials).     [LSM] multi-block-per-row idea
+ *   lse_rows_num_chunks(cols, chunk) = ceil(cols / chunk)  (-1 if invalid).
+ *   lse_rows_partial: partials[r * nchunks + k] = the lse_pair_t of columns
+ *     [k*chunk, min((k+1)*chunk, cols)) of row r.  chunk >= 1.
+ *   lse_rows_merge: row_lse[r] = LSE of the nchunks pairs of row r:
+ *     M = max_k m_k, S = sum_k s_k * (m_k == M ? 1 : exp(m_k - M)),
+ *     row_lse = M + log(S)  (= M when M is +-inf, NaN if any pair has NaN).
+ *                                                  [LSM] pairwise combine */
+int64_t lse_rows_num_chunks(int64_t cols, int64_t chunk);
+lse_status_t lse_rows_partial(const float *x, int64_t rows, int64_t cols,
+                              int64_t chunk, lse_pair_t *partials,
+                              hipStream_t stream);
+lse_status_t lse_rows_merge(const lse_pair_t *partials, int64_t rows,
+                            int64_t nchunks, float *row_lse,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------- case C
+ * The chain conv2d -> GroupNorm -> tanh -> hardswish -> residual add ->
+ * logsumexp over channels, fused.                [CHAIN] the model's forward
+ *   v0  = conv2d(x, w, b)   stride 1, no padding: (N, Cout, Ho, Wo),
+ *         Ho = H - K + 1, Wo = W - K + 1
+ *   v1  = GroupNorm(v0; groups, eps, gamma, beta)  (population variance over
+ *         the Cout/groups channels and Ho*Wo pixels of each (sample, group))
+ *   v4  = v0 + hardswish(tanh(v1)),  hardswish(t) = t * min(max(t+3,0),6) / 6
+ *   out[n, 0, h, w] = LSE_c v4[n, c, h, w]          (N, 1, Ho, Wo)
+ * x (N, Cin, H, W); w (Cout, Cin, K, K); b (Cout) or NULL; gamma, beta (Cout)
+ * or NULL (meaning 1 and 0).  This build implements K == 3, Cin == 8,
+ * Cout == 64 and groups dividing 64 into groups of 4 channels or more
+ * (LSE_ERR_UNSUPPORTED otherwise).  ws: at least
+ * fused_conv_gn_act_lse_workspace_bytes(...) bytes; on return (once the
+ * stream has run the call) its first 2 * N * groups floats hold the
+ * per-(n, g) mean followed by the per-(n, g) 1/sqrt(var + eps). */
+size_t fused_conv_gn_act_lse_workspace_bytes(int64_t N, int64_t Cin, int64_t H,
+                                             int64_t W, int64_t Cout,
+                                             int64_t K, int64_t groups);
+lse_status_t fused_conv_gn_act_lse(const float *x, const float *w,
+                                   const float *b, const float *gamma,
+                                   const float *beta, int64_t N, int64_t Cin,
+                                   int64_t H, int64_t W, int64_t Cout,
+                                   int64_t K, int64_t groups, float eps,
+                                   float *out, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSE_MI355X_H */

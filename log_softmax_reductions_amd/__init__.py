@@ -1,1 +1,183 @@
-"""MI355X-native max-shifted log-sum-exp engine (placeholder; binding follows)."""
+"""MI355X-native max-shifted log-sum-exp engine: Python binding of liblse.so.
+
+Each function has the name of the C entry point it calls and does argument
+marshalling only: it checks that tensors are fp32, contiguous and on the GPU,
+allocates outputs / workspaces with torch when the caller passes none, and
+enqueues the library call on torch's current stream.  All arithmetic runs in
+the HIP kernels of liblse.so; there is no CPU path, and a missing library
+raises ImportError on first use.
+
+  lse_reduce_axis0(x)           logsumexp over dim 0 of an (R, ...) tensor
+  log_softmax_rows(x)           log_softmax over the last dim of a 2-D tensor
+  lse_rows_partial(x, chunk)    (max, sum) pair per (row, chunk)
+  lse_rows_merge(partials)      row logsumexp from the pairs
+  fused_conv_gn_act_lse(...)    conv3x3 -> GroupNorm -> tanh -> hardswish ->
+                                residual -> logsumexp over channels
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import LseError  # noqa: F401
+
+__all__ = [
+    "lse_reduce_axis0", "log_softmax_rows", "log_softmax_rows_workspace_bytes",
+    "log_softmax_rows_plan", "lse_set_spin_limit", "lse_rows_num_chunks", "lse_rows_partial",
+    "lse_rows_merge", "fused_conv_gn_act_lse", "fused_conv_gn_act_lse_workspace_bytes",
+    "lse_abi_version", "LseError",
+]
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _dev(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32 (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ptr_or_null(t, name):
+    return None if t is None else _dev(t, name)
+
+
+def _workspace(nbytes, device, ws):
+    import torch
+    if nbytes == 0:
+        return ws, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ws, ws.numel() * ws.element_size()
+
+
+def lse_abi_version() -> int:
+    return int(_lib.load().lse_abi_version())
+
+
+def lse_reduce_axis0(x, out=None, stream=None):
+    """out[...] = logsumexp over dim 0 of x (shape x.shape[1:])."""
+    import torch
+    lib = _lib.load()
+    R = x.shape[0]
+    inner = x[0].numel() if x.dim() > 0 and R > 0 else 0
+    if out is None:
+        out = torch.empty(x.shape[1:], dtype=torch.float32, device=x.device)
+    if out.numel() != inner:
+        raise ValueError("out has the wrong number of elements")
+    _lib.check(lib.lse_reduce_axis0(_dev(x, "x"), _dev(out, "out"), R, inner, _stream(stream)),
+               "lse_reduce_axis0")
+    return out
+
+
+def log_softmax_rows_workspace_bytes(rows: int, cols: int) -> int:
+    return int(_lib.load().log_softmax_rows_workspace_bytes(rows, cols))
+
+
+def log_softmax_rows_plan(cols: int):
+    """(nchunks, chunk): workgroups per row and columns per workgroup."""
+    n, c = ctypes.c_int64(), ctypes.c_int64()
+    _lib.check(_lib.load().log_softmax_rows_plan(cols, ctypes.byref(n), ctypes.byref(c)),
+               "log_softmax_rows_plan")
+    return n.value, c.value
+
+
+def lse_set_spin_limit(polls: int) -> None:
+    _lib.load().lse_set_spin_limit(int(polls))
+
+
+def log_softmax_rows(x, y=None, ws=None, stream=None):
+    """y = log_softmax(x, dim=-1) for a 2-D fp32 GPU tensor x."""
+    import torch
+    lib = _lib.load()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows, cols)")
+    rows, cols = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    if y.shape != x.shape:
+        raise ValueError("y must have x's shape")
+    ws, ws_bytes = _workspace(log_softmax_rows_workspace_bytes(rows, cols), x.device, ws)
+    _lib.check(lib.log_softmax_rows(_dev(x, "x"), _dev(y, "y"), rows, cols,
+                                    None if ws is None else ctypes.c_void_p(ws.data_ptr()),
+                                    ws_bytes, _stream(stream)), "log_softmax_rows")
+    return y
+
+
+def lse_rows_num_chunks(cols: int, chunk: int) -> int:
+    return int(_lib.load().lse_rows_num_chunks(cols, chunk))
+
+
+def lse_rows_partial(x, chunk: int, partials=None, stream=None):
+    """(rows, nchunks, 2) float32 tensor of (m, s) pairs per chunk of each row."""
+    import torch
+    lib = _lib.load()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows, cols)")
+    rows, cols = x.shape
+    k = lse_rows_num_chunks(cols, chunk)
+    if k < 1:
+        raise ValueError("invalid cols / chunk")
+    if partials is None:
+        partials = torch.empty((rows, k, 2), dtype=torch.float32, device=x.device)
+    if partials.numel() != rows * k * 2:
+        raise ValueError("partials has the wrong size")
+    _lib.check(lib.lse_rows_partial(_dev(x, "x"), rows, cols, chunk,
+                                    _dev(partials, "partials"), _stream(stream)),
+               "lse_rows_partial")
+    return partials
+
+
+def lse_rows_merge(partials, row_lse=None, stream=None):
+    """(rows,) row logsumexp from a (rows, nchunks, 2) tensor of pairs."""
+    import torch
+    lib = _lib.load()
+    if partials.dim() != 3 or partials.shape[2] != 2:
+        raise ValueError("partials must be (rows, nchunks, 2)")
+    rows, k, _ = partials.shape
+    if row_lse is None:
+        row_lse = torch.empty(rows, dtype=torch.float32, device=partials.device)
+    _lib.check(lib.lse_rows_merge(_dev(partials, "partials"), rows, k, _dev(row_lse, "row_lse"),
+                                  _stream(stream)), "lse_rows_merge")
+    return row_lse
+
+
+def fused_conv_gn_act_lse_workspace_bytes(N, Cin, H, W, Cout, K, groups) -> int:
+    return int(_lib.load().fused_conv_gn_act_lse_workspace_bytes(N, Cin, H, W, Cout, K, groups))
+
+
+def fused_conv_gn_act_lse(x, w, b, gamma, beta, groups: int, eps: float = 1e-5, out=None,
+                          ws=None, stream=None):
+    """(N, 1, Ho, Wo) = logsumexp_c(conv + hardswish(tanh(GroupNorm(conv))))."""
+    import torch
+    lib = _lib.load()
+    if x.dim() != 4 or w.dim() != 4:
+        raise ValueError("x must be (N, Cin, H, W) and w (Cout, Cin, K, K)")
+    N, Cin, H, W = x.shape
+    Cout, Cin2, K, K2 = w.shape
+    if Cin2 != Cin or K2 != K:
+        raise ValueError("w does not match x")
+    Ho, Wo = H - K + 1, W - K + 1
+    if out is None:
+        out = torch.empty((N, 1, Ho, Wo), dtype=torch.float32, device=x.device)
+    ws, ws_bytes = _workspace(
+        fused_conv_gn_act_lse_workspace_bytes(N, Cin, H, W, Cout, K, groups), x.device, ws)
+    _lib.check(lib.fused_conv_gn_act_lse(
+        _dev(x, "x"), _dev(w, "w"), _ptr_or_null(b, "b"), _ptr_or_null(gamma, "gamma"),
+        _ptr_or_null(beta, "beta"), N, Cin, H, W, Cout, K, groups, float(eps), _dev(out, "out"),
+        None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream(stream)),
+        "fused_conv_gn_act_lse")
+    return out

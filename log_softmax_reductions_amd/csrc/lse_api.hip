@@ -1,0 +1,241 @@
+// lse_api.hip — the extern "C" entry points declared in include/lse.h.
+// Every argument is checked on the host before anything is enqueued; the
+// launchers in the kernel files assume checked arguments.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/lse.h"
+#include "lse_internal.hpp"
+
+#define LSE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lse_status_t fail(lse_status_t st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+lse_status_t ok() {
+  g_last_error.clear();
+  return LSE_OK;
+}
+
+lse_status_t from_hip(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(LSE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// a * b without int64 overflow (both >= 0); false on overflow.
+bool mul_ok(int64_t a, int64_t b, int64_t *r) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *r = a * b;
+  return true;
+}
+
+bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes) {
+  const uintptr_t a0 = (uintptr_t)a, a1 = a0 + (uintptr_t)a_bytes;
+  const uintptr_t b0 = (uintptr_t)b, b1 = b0 + (uintptr_t)b_bytes;
+  return a_bytes > 0 && b_bytes > 0 && a0 < b1 && b0 < a1;
+}
+
+constexpr int64_t kMaxElems = INT64_MAX / 16;  // keeps every byte offset in range
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+}  // namespace
+
+LSE_EXPORT const char *lse_status_string(int status) {
+  switch (status) {
+    case LSE_OK: return "LSE_OK";
+    case LSE_ERR_NULL: return "LSE_ERR_NULL";
+    case LSE_ERR_SHAPE: return "LSE_ERR_SHAPE";
+    case LSE_ERR_WORKSPACE: return "LSE_ERR_WORKSPACE";
+    case LSE_ERR_OVERLAP: return "LSE_ERR_OVERLAP";
+    case LSE_ERR_HIP: return "LSE_ERR_HIP";
+    case LSE_ERR_UNSUPPORTED: return "LSE_ERR_UNSUPPORTED";
+    default: return "LSE_ERR_UNKNOWN";
+  }
+}
+
+LSE_EXPORT const char *lse_last_error(void) { return g_last_error.c_str(); }
+
+LSE_EXPORT int lse_abi_version(void) { return LSE_ABI_VERSION; }
+
+LSE_EXPORT void lse_set_spin_limit(uint32_t polls) { lse::set_spin_limit(polls); }
+
+// ------------------------------------------------------------------ case A
+LSE_EXPORT lse_status_t lse_reduce_axis0(const float *x, float *out, int64_t R, int64_t inner,
+                                         hipStream_t stream) {
+  if (R < 1) return fail(LSE_ERR_SHAPE, "lse_reduce_axis0: R = %lld must be >= 1", (long long)R);
+  if (inner < 0)
+    return fail(LSE_ERR_SHAPE, "lse_reduce_axis0: inner = %lld must be >= 0", (long long)inner);
+  int64_t total;
+  if (!mul_ok(R, inner, &total) || total > kMaxElems)
+    return fail(LSE_ERR_SHAPE, "lse_reduce_axis0: R * inner overflows");
+  if (inner == 0) return ok();
+  if (!x || !out) return fail(LSE_ERR_NULL, "lse_reduce_axis0: x and out must be non-NULL");
+  if (overlaps(x, total * 4, out, inner * 4))
+    return fail(LSE_ERR_OVERLAP, "lse_reduce_axis0: out overlaps x");
+  if ((inner + 255) / 256 > kMaxGrid)
+    return fail(LSE_ERR_SHAPE, "lse_reduce_axis0: inner too large for one launch");
+  return from_hip(lse::launch_lse_axis0(x, out, R, inner, stream), "lse_reduce_axis0 launch");
+}
+
+// ------------------------------------------------------------------ case B
+static lse_status_t check_rows(const char *who, int64_t rows, int64_t cols, int64_t *total) {
+  if (rows < 0) return fail(LSE_ERR_SHAPE, "%s: rows = %lld must be >= 0", who, (long long)rows);
+  if (cols < 1) return fail(LSE_ERR_SHAPE, "%s: cols = %lld must be >= 1", who, (long long)cols);
+  if (!mul_ok(rows, cols, total) || *total > kMaxElems)
+    return fail(LSE_ERR_SHAPE, "%s: rows * cols overflows", who);
+  return LSE_OK;
+}
+
+LSE_EXPORT lse_status_t log_softmax_rows_plan(int64_t cols, int64_t *nchunks, int64_t *chunk) {
+  if (cols < 1) return fail(LSE_ERR_SHAPE, "log_softmax_rows_plan: cols must be >= 1");
+  if (!nchunks || !chunk) return fail(LSE_ERR_NULL, "log_softmax_rows_plan: NULL output");
+  const lse::RowsPlan p = lse::rows_plan(cols);
+  *nchunks = p.nchunks;
+  *chunk = p.nchunks == 1 ? cols : p.chunk;
+  return ok();
+}
+
+LSE_EXPORT size_t log_softmax_rows_workspace_bytes(int64_t rows, int64_t cols) {
+  int64_t total;
+  if (rows < 0 || cols < 1 || !mul_ok(rows, cols, &total)) return 0;
+  return lse::rows_workspace_bytes(rows, cols);
+}
+
+LSE_EXPORT lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
+                                         void *ws, size_t ws_bytes, hipStream_t stream) {
+  int64_t total;
+  lse_status_t st = check_rows("log_softmax_rows", rows, cols, &total);
+  if (st != LSE_OK) return st;
+  if (rows == 0) return ok();
+  if (!x || !y) return fail(LSE_ERR_NULL, "log_softmax_rows: x and y must be non-NULL");
+  if (overlaps(x, total * 4, y, total * 4))
+    return fail(LSE_ERR_OVERLAP, "log_softmax_rows: y overlaps x (in-place is not supported)");
+  const lse::RowsPlan p = lse::rows_plan(cols);
+  if (p.nchunks > lse::kRowsMaxChunks)
+    return fail(LSE_ERR_SHAPE, "log_softmax_rows: cols = %lld too long", (long long)cols);
+  int64_t wgs;
+  if (!mul_ok(rows, p.nchunks, &wgs) || wgs > kMaxGrid)
+    return fail(LSE_ERR_SHAPE, "log_softmax_rows: rows * chunks = too many workgroups");
+  if (p.nchunks > 1) {
+    const size_t need = lse::rows_workspace_bytes(rows, cols);
+    if (!ws) return fail(LSE_ERR_WORKSPACE, "log_softmax_rows: needs %zu workspace bytes", need);
+    if (ws_bytes < need)
+      return fail(LSE_ERR_WORKSPACE, "log_softmax_rows: workspace %zu < required %zu", ws_bytes,
+                  need);
+    if (overlaps(ws, (int64_t)need, x, total * 4) || overlaps(ws, (int64_t)need, y, total * 4))
+      return fail(LSE_ERR_OVERLAP, "log_softmax_rows: workspace overlaps x or y");
+  }
+  return from_hip(lse::launch_log_softmax_rows(x, y, rows, cols, ws, stream),
+                  "log_softmax_rows launch");
+}
+
+LSE_EXPORT int64_t lse_rows_num_chunks(int64_t cols, int64_t chunk) {
+  if (cols < 1 || chunk < 1) return -1;
+  return (cols + chunk - 1) / chunk;
+}
+
+LSE_EXPORT lse_status_t lse_rows_partial(const float *x, int64_t rows, int64_t cols,
+                                         int64_t chunk, lse_pair_t *partials,
+                                         hipStream_t stream) {
+  int64_t total;
+  lse_status_t st = check_rows("lse_rows_partial", rows, cols, &total);
+  if (st != LSE_OK) return st;
+  if (chunk < 1)
+    return fail(LSE_ERR_SHAPE, "lse_rows_partial: chunk = %lld must be >= 1", (long long)chunk);
+  if (rows == 0) return ok();
+  if (!x || !partials) return fail(LSE_ERR_NULL, "lse_rows_partial: NULL pointer");
+  const int64_t k = (cols + chunk - 1) / chunk;
+  int64_t wgs;
+  if (!mul_ok(rows, k, &wgs) || wgs > kMaxGrid)
+    return fail(LSE_ERR_SHAPE, "lse_rows_partial: rows * chunks = too many workgroups");
+  if (overlaps(x, total * 4, partials, wgs * 8))
+    return fail(LSE_ERR_OVERLAP, "lse_rows_partial: partials overlap x");
+  return from_hip(lse::launch_lse_rows_partial(x, rows, cols, chunk, partials, stream),
+                  "lse_rows_partial launch");
+}
+
+LSE_EXPORT lse_status_t lse_rows_merge(const lse_pair_t *partials, int64_t rows,
+                                       int64_t nchunks, float *row_lse, hipStream_t stream) {
+  if (rows < 0) return fail(LSE_ERR_SHAPE, "lse_rows_merge: rows must be >= 0");
+  if (nchunks < 1) return fail(LSE_ERR_SHAPE, "lse_rows_merge: nchunks must be >= 1");
+  int64_t total;
+  if (!mul_ok(rows, nchunks, &total) || total > kMaxElems)
+    return fail(LSE_ERR_SHAPE, "lse_rows_merge: rows * nchunks overflows");
+  if (rows == 0) return ok();
+  if (!partials || !row_lse) return fail(LSE_ERR_NULL, "lse_rows_merge: NULL pointer");
+  if ((rows + 3) / 4 > kMaxGrid) return fail(LSE_ERR_SHAPE, "lse_rows_merge: too many rows");
+  if (overlaps(partials, total * 8, row_lse, rows * 4))
+    return fail(LSE_ERR_OVERLAP, "lse_rows_merge: row_lse overlaps partials");
+  return from_hip(lse::launch_lse_rows_merge(partials, rows, nchunks, row_lse, stream),
+                  "lse_rows_merge launch");
+}
+
+// ------------------------------------------------------------------ case C
+static lse_status_t check_chain(int64_t N, int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                                int64_t K, int64_t groups) {
+  if (N < 0) return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: N must be >= 0");
+  if (Cin < 1 || Cout < 1 || K < 1 || groups < 1)
+    return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: Cin, Cout, K, groups must be >= 1");
+  if (H < K || W < K) return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: H, W must be >= K");
+  if (Cout % groups != 0)
+    return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: Cout %% groups != 0");
+  if (H > 65536 || W > 65536) return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: H, W > 65536");
+  int64_t t;
+  if (!mul_ok(N, Cin, &t) || !mul_ok(t, H, &t) || !mul_ok(t, W, &t) || t > kMaxElems)
+    return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: input size overflows");
+  if (N > 65535) return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: N > 65535");
+  if (K != 3 || Cin != 8 || Cout != 64 || (16 % groups) != 0)
+    return fail(LSE_ERR_UNSUPPORTED,
+                "fused_conv_gn_act_lse: this build implements K=3, Cin=8, Cout=64 and groups "
+                "in {1,2,4,8,16} (got K=%lld Cin=%lld Cout=%lld groups=%lld)",
+                (long long)K, (long long)Cin, (long long)Cout, (long long)groups);
+  return LSE_OK;
+}
+
+LSE_EXPORT size_t fused_conv_gn_act_lse_workspace_bytes(int64_t N, int64_t Cin, int64_t H,
+                                                        int64_t W, int64_t Cout, int64_t K,
+                                                        int64_t groups) {
+  if (N < 0 || Cin < 1 || Cout < 1 || K < 1 || groups < 1 || H < K || W < K) return 0;
+  return lse::conv_chain_workspace_bytes(N, Cin, H, W, Cout, K, groups);
+}
+
+LSE_EXPORT lse_status_t fused_conv_gn_act_lse(const float *x, const float *w, const float *b,
+                                              const float *gamma, const float *beta, int64_t N,
+                                              int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                                              int64_t K, int64_t groups, float eps, float *out,
+                                              void *ws, size_t ws_bytes, hipStream_t stream) {
+  lse_status_t st = check_chain(N, Cin, H, W, Cout, K, groups);
+  if (st != LSE_OK) return st;
+  if (!(eps >= 0.0f)) return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: eps must be >= 0");
+  if (N == 0) return ok();
+  if (!x || !w || !out) return fail(LSE_ERR_NULL, "fused_conv_gn_act_lse: x, w, out required");
+  const size_t need = lse::conv_chain_workspace_bytes(N, Cin, H, W, Cout, K, groups);
+  if (!ws) return fail(LSE_ERR_WORKSPACE, "fused_conv_gn_act_lse: needs %zu bytes", need);
+  if (ws_bytes < need)
+    return fail(LSE_ERR_WORKSPACE, "fused_conv_gn_act_lse: workspace %zu < required %zu",
+                ws_bytes, need);
+  const int64_t in_bytes = N * Cin * H * W * 4;
+  const int64_t out_bytes = N * (H - K + 1) * (W - K + 1) * 4;
+  if (overlaps(x, in_bytes, out, out_bytes) || overlaps(ws, (int64_t)need, out, out_bytes) ||
+      overlaps(ws, (int64_t)need, x, in_bytes))
+    return fail(LSE_ERR_OVERLAP, "fused_conv_gn_act_lse: out / workspace overlap an input");
+  return from_hip(lse::launch_conv_chain(x, w, b, gamma, beta, N, Cin, H, W, Cout, K, groups,
+                                         eps, out, ws, stream),
+                  "fused_conv_gn_act_lse launch");
+}

@@ -1,0 +1,112 @@
+// lse_device.hpp — device building blocks shared by the gfx950 kernels:
+// wave64 all-reductions on DPP row permutes plus the gfx950 permlane swaps,
+// a workgroup all-reduce through LDS, the (max, sum) pair and its packing
+// into one 64-bit word for cross-workgroup publication.
+//
+// The pair follows the pairwise combine on POPCORNBENCH Kimi-K2.6 l1_p24
+// (LogSoftmax over dim 1): (m1,s1),(m2,s2) -> (M, s1 e^(m1-M) + s2 e^(m2-M)),
+// M = max(m1,m2), with the weight of a term whose m equals M written as the
+// exact 1 it is.  That keeps the identity (-inf, 0) and (+inf, n) pairs free of
+// inf - inf, the NaN that page's own 32-lane reduction runs into when most
+// lanes hold no data.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lse {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.44269504088896340736f;  // log2(e)
+
+__device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float bitsf(uint32_t v) { return __builtin_bit_cast(float, v); }
+
+// exp(d) through the hardware base-2 exponential: 2^(d * log2 e).  Used for the
+// bulk sums, where d = v - m <= 0 and the terms that matter have |d| small, so
+// the rounding of d * log2 e costs well under an ulp of the sum.
+__device__ __forceinline__ float exp_base2(float d) {
+  return __builtin_amdgcn_exp2f(d * kLog2e);
+}
+
+__device__ __forceinline__ bool is_finite(float v) { return __builtin_isfinite(v); }
+
+// ----------------------------------------------------------------- wave64
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return bitsf(__builtin_amdgcn_update_dpp(0u, fbits(v), CTRL, 0xF, 0xF, false));
+}
+
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpSum {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+
+// All 64 lanes end with op over the wave, bitwise identical in every lane
+// (each step combines the same two values, only in swapped operand order).
+template <class Op>
+__device__ __forceinline__ float wave_allreduce(float v, Op op) {
+  v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  v = op(v, dpp_mov<0x141>(v));  // row_half_mirror: pairs the quads of 8 lanes
+  v = op(v, dpp_mov<0x140>(v));  // row_mirror: pairs the halves of a 16-lane row
+  // v_permlane16_swap: the returned pair holds, in every lane, the values of
+  // rows (0,1) or (2,3) of its row pair, so op of the two is the 32-lane result.
+  auto p = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+  v = op(bitsf(p[0]), bitsf(p[1]));
+  // v_permlane32_swap: the pair holds lane l % 32 and lane 32 + l % 32.
+  auto q = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
+  v = op(bitsf(q[0]), bitsf(q[1]));
+  return v;
+}
+
+// Workgroup all-reduce of NW waves through `lds` (NW floats).  Every thread
+// gets the same value; the trailing barrier lets the caller reuse `lds`.
+template <int NW, class Op>
+__device__ __forceinline__ float block_allreduce(float v, Op op, float *lds) {
+  v = wave_allreduce(v, op);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) lds[w] = v;
+  __syncthreads();
+  float r = lds[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = op(r, lds[i]);
+  __syncthreads();
+  return r;
+}
+
+// ------------------------------------------------------------------ pairs
+// Term of the sum for a value v against the set's max m (m = max of the
+// non-NaN values).  For finite m this is exp(v - m) (v = -inf gives 0, NaN
+// gives NaN).  For m = -inf every non-NaN value is -inf and contributes 0; for
+// m = +inf a +inf value contributes exactly 1 and a finite one 0.
+__device__ __forceinline__ float pair_term_general(float v, float m) {
+  if (v == m) return (m == -__builtin_inff()) ? 0.0f : 1.0f;
+  return expf(v - m);
+}
+
+// Weight of a partial whose max is mk inside a merge whose max is M.
+__device__ __forceinline__ float merge_weight(float mk, float M) {
+  return (mk == M) ? 1.0f : expf(mk - M);
+}
+
+// Packed pair for single-word publication: low 32 bits m, high 32 bits s.  A
+// real pair never packs to 0 (m = +0 implies s >= 1), so 0 means "not yet
+// written" in a cleared workspace.
+__device__ __forceinline__ uint64_t pack_pair(float m, float s) {
+  return (uint64_t)fbits(m) | ((uint64_t)fbits(s) << 32);
+}
+__device__ __forceinline__ float pair_m(uint64_t p) { return bitsf((uint32_t)p); }
+__device__ __forceinline__ float pair_s(uint64_t p) { return bitsf((uint32_t)(p >> 32)); }
+
+__device__ __forceinline__ void store_pair_agent(uint64_t *slot, uint64_t p) {
+  __hip_atomic_store(slot, p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_pair_agent(const uint64_t *slot) {
+  return __hip_atomic_load(const_cast<uint64_t *>(slot), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace lse

@@ -1,0 +1,56 @@
+// lse_internal.hpp — host-side interface between the C ABI (lse_api.hip) and
+// the kernel launchers.  Launchers assume validated arguments and return the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lse {
+
+// ---------------------------------------------------------------- case A
+hipError_t launch_lse_axis0(const float *x, float *out, int64_t R, int64_t inner,
+                            hipStream_t stream);
+
+// ---------------------------------------------------------------- case B
+constexpr int kRowsThreads = 256;              // one workgroup = 4 waves
+constexpr int kRowsMaxVpl = 64;                // floats held per lane
+constexpr int64_t kRowsTile = (int64_t)kRowsThreads * kRowsMaxVpl;  // 16384
+constexpr int64_t kRowsMaxChunks = 1 << 20;
+
+// Split workspace: a 256-byte header, then rows * nchunks packed pairs.
+struct RowsWsHeader {
+  uint32_t ticket;   // next (row, chunk) ticket to hand out
+  uint32_t error;    // nonzero once a workgroup gave up waiting
+  uint32_t pad[62];
+};
+static_assert(sizeof(RowsWsHeader) == 256, "header is 256 bytes");
+
+struct RowsPlan {
+  int64_t nchunks;
+  int64_t chunk;
+};
+RowsPlan rows_plan(int64_t cols);
+size_t rows_workspace_bytes(int64_t rows, int64_t cols);
+
+hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows,
+                                   int64_t cols, void *ws, hipStream_t stream);
+hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols,
+                                   int64_t chunk, void *partials,
+                                   hipStream_t stream);
+hipError_t launch_lse_rows_merge(const void *partials, int64_t rows,
+                                 int64_t nchunks, float *row_lse,
+                                 hipStream_t stream);
+void set_spin_limit(uint32_t polls);
+
+// ---------------------------------------------------------------- case C
+size_t conv_chain_workspace_bytes(int64_t N, int64_t Cin, int64_t H, int64_t W,
+                                  int64_t Cout, int64_t K, int64_t groups);
+hipError_t launch_conv_chain(const float *x, const float *w, const float *b,
+                             const float *gamma, const float *beta, int64_t N,
+                             int64_t Cin, int64_t H, int64_t W, int64_t Cout,
+                             int64_t K, int64_t groups, float eps, float *out,
+                             void *ws, hipStream_t stream);
+
+}  // namespace lse

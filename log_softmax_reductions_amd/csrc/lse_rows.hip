@@ -1,0 +1,420 @@
+// lse_rows.hip — row-wise log_softmax over long contiguous rows, and the
+// per-chunk (max, sum) partial / merge building blocks.
+//
+// POPCORNBENCH Kimi-K2.6 l1_p24 (LogSoftmax over dim 1 of (4096, 393216)):
+//   y_i = x_i - max - log(sum_j exp(x_j - max)); the minimum traffic is one
+//   read and one write of the array; one row is 1.5 MiB; a row can be split
+//   across blocks that each reduce their portion to a local (max, sum) and a
+//   second phase combines them.  That page stays with one block per row and
+//   re-reads the row for the write pass, and its warp-shuffle combine returns
+//   NaN once idle lanes holding (-inf, 0) meet.
+//
+// Design here (gfx950):
+//   * A workgroup of 256 lanes owns one chunk of up to 16384 columns and keeps
+//     it in VGPRs (64 floats per lane, 16 global_load_dwordx4 per lane), so the
+//     chunk is read from HBM exactly once and written exactly once.
+//   * Exact chunk max (DPP/permlane wave reduce + LDS), then the sum of
+//     exp(x - max) over the registers: one exponential per element.
+//   * A row of k > 1 chunks: each workgroup publishes its pair as one packed
+//     64-bit word with an agent-scope atomic store, then wave 0 polls the row's
+//     k words until all are written and every workgroup of the row merges the
+//     same k pairs in the same order (so all get the bitwise-same row LSE).
+//     Work is handed out by an atomic ticket counter, so the chunks of a row
+//     are always claimed by workgroups that are already running: a waiting
+//     workgroup only waits on chunks whose owners are resident and never wait
+//     themselves before publishing.  The wait is bounded in polls
+//     (set_spin_limit) and in time (0.1 s); a workgroup that gives up flags
+//     the workspace and writes NaN.
+//   * The write is y = (x - M) - log(S): x - M is exact for the large entries,
+//     so the result keeps its accuracy when |M| is large.
+#include "lse_device.hpp"
+#include "lse_internal.hpp"
+
+namespace lse {
+namespace {
+
+constexpr int kNW = kRowsThreads / kWave;  // waves per workgroup
+uint32_t h_spin_limit = 1u << 24;
+
+// Load a chunk of `len` values starting at p into v (lane-strided so that each
+// wave's load is one contiguous span), padding with -inf.
+template <int VPL, bool VEC>
+__device__ __forceinline__ void load_chunk(const float *__restrict__ p, int64_t len,
+                                           float (&v)[VPL]) {
+  const int t = threadIdx.x;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int q = 0; q < VPL / 4; ++q) {
+      const int64_t idx = ((int64_t)q * kRowsThreads + t) * 4;
+      if (idx < len) {
+        const float4 f = *reinterpret_cast<const float4 *>(p + idx);
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * q + e] = -__builtin_inff();
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) {
+      const int64_t idx = (int64_t)e * kRowsThreads + t;
+      v[e] = (idx < len) ? p[idx] : -__builtin_inff();
+    }
+  }
+}
+
+template <int VPL, bool VEC>
+__device__ __forceinline__ void store_chunk(float *__restrict__ p, int64_t len,
+                                            const float (&v)[VPL], float M, float lnS) {
+  const int t = threadIdx.x;
+  if constexpr (VEC) {
+#pragma unroll
+    for (int q = 0; q < VPL / 4; ++q) {
+      const int64_t idx = ((int64_t)q * kRowsThreads + t) * 4;
+      if (idx < len) {
+        float4 f;
+        f.x = (v[4 * q] - M) - lnS;
+        f.y = (v[4 * q + 1] - M) - lnS;
+        f.z = (v[4 * q + 2] - M) - lnS;
+        f.w = (v[4 * q + 3] - M) - lnS;
+        *reinterpret_cast<float4 *>(p + idx) = f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) {
+      const int64_t idx = (int64_t)e * kRowsThreads + t;
+      if (idx < len) p[idx] = (v[e] - M) - lnS;
+    }
+  }
+}
+
+// The chunk's pair (exact max, sum of exp(v - max)); identical in every lane.
+template <int VPL>
+__device__ __forceinline__ void chunk_pair(const float (&v)[VPL], float *red, float &m,
+                                           float &s) {
+  float lm = v[0];
+#pragma unroll
+  for (int e = 1; e < VPL; ++e) lm = fmaxf(lm, v[e]);
+  m = block_allreduce<kNW>(lm, OpMax{}, red);
+  float ls = 0.0f;
+  if (is_finite(m)) {  // uniform branch: m is the same in every lane
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) ls += exp_base2(v[e] - m);
+  } else {
+    for (int e = 0; e < VPL; ++e) ls += pair_term_general(v[e], m);
+  }
+  s = block_allreduce<kNW>(ls, OpSum{}, red);
+}
+
+// Merge the k pairs at pairs[0..k) held by one wave; every lane returns the
+// same (M, S).  Lanes stride over the pairs; the order is fixed.
+__device__ __forceinline__ void wave_merge_pairs(const uint64_t *pairs, int64_t k, float &M,
+                                                 float &S) {
+  const int lane = threadIdx.x % kWave;
+  float lm = -__builtin_inff();
+  bool nan_seen = false;
+  for (int64_t j = lane; j < k; j += kWave) {
+    const uint64_t p = load_pair_agent(pairs + j);
+    const float mj = pair_m(p), sj = pair_s(p);
+    nan_seen |= (mj != mj) || (sj != sj);
+    lm = fmaxf(lm, mj);
+  }
+  M = wave_allreduce(lm, OpMax{});
+  float ls = 0.0f;
+  for (int64_t j = lane; j < k; j += kWave) {
+    const uint64_t p = load_pair_agent(pairs + j);
+    ls += pair_s(p) * merge_weight(pair_m(p), M);
+  }
+  S = wave_allreduce(ls, OpSum{});
+  if (__builtin_amdgcn_ballot_w64(nan_seen) != 0) {
+    M = __builtin_nanf("");
+    S = __builtin_nanf("");
+  }
+}
+
+// Longest a workgroup waits for its row, in ticks of the 100 MHz real-time
+// counter: 0.1 s, some four orders of magnitude above a real wait.
+constexpr uint64_t kWaitTicks = 10000000ull;
+
+// Wave 0 waits until all k pair words of a row are non-zero.  Returns false
+// when the poll limit or the time limit runs out.
+__device__ __forceinline__ bool wave_wait_pairs(const uint64_t *pairs, int64_t k,
+                                                uint32_t limit) {
+  const int lane = threadIdx.x % kWave;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (uint32_t it = 0;; ++it) {
+    bool missing = false;
+    for (int64_t j = lane; j < k; j += kWave) missing |= (load_pair_agent(pairs + j) == 0);
+    if (__builtin_amdgcn_ballot_w64(missing) == 0) return true;
+    if (it >= limit || __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// One workgroup = one (row, chunk).  SPLIT: rows of nchunks > 1 chunks, work
+// handed out by ticket, pairs merged through the workspace.  !SPLIT: one
+// workgroup per row (nchunks == 1), blockIdx.x is the row.
+template <int VPL, bool VEC, bool SPLIT>
+__global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
+    const float *__restrict__ x, float *__restrict__ y, int64_t cols, int64_t nchunks,
+    int64_t chunk, RowsWsHeader *__restrict__ hdr, uint64_t *__restrict__ pairs,
+    uint32_t spin_limit) {
+  __shared__ float red[kNW];
+  __shared__ uint32_t s_ticket;
+  __shared__ float s_final[2];
+  int64_t row, c;
+  if constexpr (SPLIT) {
+    if (threadIdx.x == 0)
+      s_ticket = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t t = s_ticket;
+    row = t / nchunks;
+    c = t - row * nchunks;
+  } else {
+    row = blockIdx.x;
+    c = 0;
+  }
+  const int64_t c0 = c * chunk;
+  const int64_t len = (cols - c0 < chunk) ? (cols - c0) : chunk;
+  const float *xr = x + row * cols + c0;
+  float *yr = y + row * cols + c0;
+
+  float v[VPL];
+  load_chunk<VPL, VEC>(xr, len, v);
+  float m, s;
+  chunk_pair<VPL>(v, red, m, s);
+
+  float M, lnS;
+  if constexpr (SPLIT) {
+    uint64_t *row_pairs = pairs + row * nchunks;
+    if (threadIdx.x == 0) store_pair_agent(row_pairs + c, pack_pair(m, s));
+    if (threadIdx.x < kWave) {
+      float Mw, Sw;
+      if (wave_wait_pairs(row_pairs, nchunks, spin_limit)) {
+        wave_merge_pairs(row_pairs, nchunks, Mw, Sw);
+      } else {
+        Mw = Sw = __builtin_nanf("");
+        if (threadIdx.x == 0)
+          __hip_atomic_store(&hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (threadIdx.x == 0) {
+        s_final[0] = Mw;
+        s_final[1] = logf(Sw);
+      }
+    }
+    __syncthreads();
+    M = s_final[0];
+    lnS = s_final[1];
+  } else {
+    M = m;
+    lnS = logf(s);
+  }
+  store_chunk<VPL, VEC>(yr, len, v, M, lnS);
+}
+
+// Clear n 64-bit words (the workspace header and pair slots).
+__global__ __launch_bounds__(256) void clear_words_kernel(uint64_t *__restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// ------------------------------------------------------------ partial/merge
+// One workgroup per (row, chunk) of a chunk that fits the register tile.
+template <int VPL, bool VEC>
+__global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_kernel(
+    const float *__restrict__ x, int64_t cols, int64_t nchunks, int64_t chunk,
+    float2 *__restrict__ partials) {
+  __shared__ float red[kNW];
+  const int64_t t = blockIdx.x;
+  const int64_t row = t / nchunks, c = t - row * nchunks;
+  const int64_t c0 = c * chunk;
+  const int64_t len = (cols - c0 < chunk) ? (cols - c0) : chunk;
+  float v[VPL];
+  load_chunk<VPL, VEC>(x + row * cols + c0, len, v);
+  float m, s;
+  chunk_pair<VPL>(v, red, m, s);
+  if (threadIdx.x == 0) partials[t] = make_float2(m, s);
+}
+
+// Chunks longer than the register tile: an exact-max pass, then a sum pass,
+// both streaming through the chunk (the second read is served by cache).
+__global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_stream_kernel(
+    const float *__restrict__ x, int64_t cols, int64_t nchunks, int64_t chunk,
+    float2 *__restrict__ partials) {
+  __shared__ float red[kNW];
+  const int64_t t = blockIdx.x;
+  const int64_t row = t / nchunks, c = t - row * nchunks;
+  const int64_t c0 = c * chunk;
+  const int64_t len = (cols - c0 < chunk) ? (cols - c0) : chunk;
+  const float *p = x + row * cols + c0;
+  float lm = -__builtin_inff();
+  for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) lm = fmaxf(lm, p[i]);
+  const float m = block_allreduce<kNW>(lm, OpMax{}, red);
+  float ls = 0.0f;
+  if (is_finite(m)) {
+    for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) ls += exp_base2(p[i] - m);
+  } else {
+    for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) ls += pair_term_general(p[i], m);
+  }
+  const float s = block_allreduce<kNW>(ls, OpSum{}, red);
+  if (threadIdx.x == 0) partials[t] = make_float2(m, s);
+}
+
+// One wave per row: row_lse = M + log(S) of the row's nchunks pairs.
+__global__ __launch_bounds__(256) void lse_rows_merge_kernel(const float2 *__restrict__ partials,
+                                                             int64_t rows, int64_t nchunks,
+                                                             float *__restrict__ row_lse) {
+  const int64_t row = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (row >= rows) return;  // whole wave exits together
+  const int lane = threadIdx.x % kWave;
+  const float2 *pr = partials + row * nchunks;
+  float lm = -__builtin_inff();
+  bool nan_seen = false;
+  for (int64_t j = lane; j < nchunks; j += kWave) {
+    const float2 p = pr[j];
+    nan_seen |= (p.x != p.x) || (p.y != p.y);
+    lm = fmaxf(lm, p.x);
+  }
+  const float M = wave_allreduce(lm, OpMax{});
+  float ls = 0.0f;
+  for (int64_t j = lane; j < nchunks; j += kWave) {
+    const float2 p = pr[j];
+    ls += p.y * merge_weight(p.x, M);
+  }
+  const float S = wave_allreduce(ls, OpSum{});
+  if (lane == 0) {
+    float r;
+    if (__builtin_amdgcn_ballot_w64(nan_seen) != 0)
+      r = __builtin_nanf("");
+    else
+      r = is_finite(M) ? M + logf(S) : M;
+    row_lse[row] = r;
+  }
+}
+
+int vpl_for(int64_t len) {
+  // smallest register tile (floats per lane) covering len columns
+  if (len <= 4 * kRowsThreads) return 4;
+  if (len <= 8 * kRowsThreads) return 8;
+  if (len <= 16 * kRowsThreads) return 16;
+  if (len <= 32 * kRowsThreads) return 32;
+  return 64;
+}
+
+template <bool SPLIT>
+hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *y, int64_t cols,
+                           int64_t nchunks, int64_t chunk, RowsWsHeader *hdr, uint64_t *pairs,
+                           uint32_t spin_limit, hipStream_t stream) {
+#define LSE_ROWS_CASE(V)                                                                     \
+  case V:                                                                                    \
+    if (vec)                                                                                 \
+      hipLaunchKernelGGL((log_softmax_rows_kernel<V, true, SPLIT>), grid, dim3(kRowsThreads), \
+                         0, stream, x, y, cols, nchunks, chunk, hdr, pairs, spin_limit);     \
+    else                                                                                     \
+      hipLaunchKernelGGL((log_softmax_rows_kernel<V, false, SPLIT>), grid,                   \
+                         dim3(kRowsThreads), 0, stream, x, y, cols, nchunks, chunk, hdr,     \
+                         pairs, spin_limit);                                                 \
+    break;
+  switch (vpl) {
+    LSE_ROWS_CASE(4)
+    LSE_ROWS_CASE(8)
+    LSE_ROWS_CASE(16)
+    LSE_ROWS_CASE(32)
+    LSE_ROWS_CASE(64)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef LSE_ROWS_CASE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void set_spin_limit(uint32_t polls) { h_spin_limit = polls; }
+
+RowsPlan rows_plan(int64_t cols) {
+  RowsPlan p;
+  p.nchunks = (cols + kRowsTile - 1) / kRowsTile;
+  if (p.nchunks < 1) p.nchunks = 1;
+  // balance the chunks, keeping them a multiple of 4 columns
+  int64_t chunk = (cols + p.nchunks - 1) / p.nchunks;
+  chunk = (chunk + 3) / 4 * 4;
+  if (chunk > kRowsTile) chunk = kRowsTile;
+  p.chunk = chunk;
+  p.nchunks = (cols + chunk - 1) / chunk;
+  return p;
+}
+
+size_t rows_workspace_bytes(int64_t rows, int64_t cols) {
+  const RowsPlan p = rows_plan(cols);
+  if (p.nchunks <= 1) return 0;
+  return sizeof(RowsWsHeader) + (size_t)rows * (size_t)p.nchunks * sizeof(uint64_t);
+}
+
+hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
+                                   void *ws, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const RowsPlan p = rows_plan(cols);
+  const bool vec = (cols % 4 == 0) && (p.chunk % 4 == 0) && ((uintptr_t)x % 16 == 0) &&
+                   ((uintptr_t)y % 16 == 0);
+  if (p.nchunks == 1) {
+    return launch_rows_vpl<false>(vpl_for(cols), vec, dim3((uint32_t)rows), x, y, cols, 1, cols,
+                                  nullptr, nullptr, 0u, stream);
+  }
+  auto *hdr = reinterpret_cast<RowsWsHeader *>(ws);
+  auto *pairs = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws) + sizeof(RowsWsHeader));
+  const int64_t words = (int64_t)(rows_workspace_bytes(rows, cols) / sizeof(uint64_t));
+  hipLaunchKernelGGL(clear_words_kernel, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0,
+                     stream, reinterpret_cast<uint64_t *>(ws), words);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_rows_vpl<true>(vpl_for(p.chunk), vec, dim3((uint32_t)(rows * p.nchunks)), x, y,
+                               cols, p.nchunks, p.chunk, hdr, pairs, h_spin_limit, stream);
+}
+
+hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, int64_t chunk,
+                                   void *partials, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int64_t nchunks = (cols + chunk - 1) / chunk;
+  const dim3 grid((uint32_t)(rows * nchunks));
+  auto *out = reinterpret_cast<float2 *>(partials);
+  if (chunk > kRowsTile) {
+    hipLaunchKernelGGL(lse_rows_partial_stream_kernel, grid, dim3(kRowsThreads), 0, stream, x,
+                       cols, nchunks, chunk, out);
+    return hipGetLastError();
+  }
+  const bool vec = (cols % 4 == 0) && (chunk % 4 == 0) && ((uintptr_t)x % 16 == 0);
+#define LSE_PART_CASE(V)                                                                       \
+  case V:                                                                                      \
+    if (vec)                                                                                   \
+      hipLaunchKernelGGL((lse_rows_partial_kernel<V, true>), grid, dim3(kRowsThreads), 0,      \
+                         stream, x, cols, nchunks, chunk, out);                                \
+    else                                                                                       \
+      hipLaunchKernelGGL((lse_rows_partial_kernel<V, false>), grid, dim3(kRowsThreads), 0,     \
+                         stream, x, cols, nchunks, chunk, out);                                \
+    break;
+  switch (vpl_for(chunk)) {
+    LSE_PART_CASE(4)
+    LSE_PART_CASE(8)
+    LSE_PART_CASE(16)
+    LSE_PART_CASE(32)
+    LSE_PART_CASE(64)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef LSE_PART_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_rows_merge(const void *partials, int64_t rows, int64_t nchunks,
+                                 float *row_lse, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const int64_t blocks = (rows + 3) / 4;
+  hipLaunchKernelGGL(lse_rows_merge_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const float2 *>(partials), rows, nchunks, row_lse);
+  return hipGetLastError();
+}
+
+}  // namespace lse

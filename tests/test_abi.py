@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export exactly the functions include/lse.h declares,
+and reject bad arguments with the documented status codes before it touches
+the HIP runtime (every call below fails validation, so nothing is launched).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lse.h")
+
+LSE_OK, LSE_ERR_NULL, LSE_ERR_SHAPE, LSE_ERR_WORKSPACE, LSE_ERR_OVERLAP = 0, 1, 2, 3, 4
+LSE_ERR_UNSUPPORTED = 6
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: every call here fails validation
+FAKE2 = ctypes.c_void_p(0x900000000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    keywords = {"sizeof", "defined"}
+    return sorted(set(n for n in names if n not in keywords))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from log_softmax_reductions_amd import _lib
+    return _lib.load()
+
+
+def test_exports_match_header(lib):
+    import subprocess
+    from log_softmax_reductions_amd import _lib
+    declared = declared_functions()
+    assert len(declared) == 13
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines()
+                      if l.split()[-2] in ("T", "W") and not l.split()[-1].startswith("_"))
+    assert exported == declared
+    assert set(_lib.SIGNATURES) == set(declared)
+
+
+def test_status_strings(lib):
+    assert lib.lse_status_string(0) == b"LSE_OK"
+    assert lib.lse_status_string(3) == b"LSE_ERR_WORKSPACE"
+    assert lib.lse_abi_version() == 1
+
+
+def test_axis0_validation(lib):
+    assert lib.lse_reduce_axis0(FAKE, FAKE2, 0, 5, None) == LSE_ERR_SHAPE
+    assert lib.lse_reduce_axis0(FAKE, FAKE2, 3, -1, None) == LSE_ERR_SHAPE
+    assert lib.lse_reduce_axis0(None, FAKE2, 3, 5, None) == LSE_ERR_NULL
+    assert lib.lse_reduce_axis0(FAKE, None, 3, 5, None) == LSE_ERR_NULL
+    assert lib.lse_reduce_axis0(FAKE, FAKE2, 1 << 40, 1 << 40, None) == LSE_ERR_SHAPE
+    # out inside x's range
+    assert lib.lse_reduce_axis0(FAKE, ctypes.c_void_p(0x100010), 4, 64, None) == LSE_ERR_OVERLAP
+    assert b"overlaps" in lib.lse_last_error()
+    # inner == 0 is a no-op that succeeds without touching anything
+    assert lib.lse_reduce_axis0(None, None, 3, 0, None) == LSE_OK
+
+
+def test_rows_validation(lib):
+    assert lib.log_softmax_rows(FAKE, FAKE2, -1, 8, None, 0, None) == LSE_ERR_SHAPE
+    assert lib.log_softmax_rows(FAKE, FAKE2, 4, 0, None, 0, None) == LSE_ERR_SHAPE
+    assert lib.log_softmax_rows(None, FAKE2, 4, 8, None, 0, None) == LSE_ERR_NULL
+    assert lib.log_softmax_rows(FAKE, FAKE, 4, 8, None, 0, None) == LSE_ERR_OVERLAP
+    # a split row needs a workspace of the advertised size
+    need = lib.log_softmax_rows_workspace_bytes(16, 393216)
+    assert need == 256 + 16 * 24 * 8
+    assert lib.log_softmax_rows(FAKE, FAKE2, 16, 393216, None, 0, None) == LSE_ERR_WORKSPACE
+    assert lib.log_softmax_rows(FAKE, FAKE2, 16, 393216, ctypes.c_void_p(0x7000000000), need - 1,
+                                None) == LSE_ERR_WORKSPACE
+    assert lib.log_softmax_rows_workspace_bytes(128, 4096) == 0
+    assert lib.log_softmax_rows(None, None, 0, 8, None, 0, None) == LSE_OK
+
+
+def test_rows_plan(lib):
+    from log_softmax_reductions_amd import log_softmax_rows_plan
+    assert log_softmax_rows_plan(393216) == (24, 16384)
+    assert log_softmax_rows_plan(4096) == (1, 4096)
+    assert log_softmax_rows_plan(16384) == (1, 16384)
+    for cols in (16385, 20000, 100001, 393216, 1 << 22):
+        k, chunk = log_softmax_rows_plan(cols)
+        assert k > 1 and chunk % 4 == 0 and chunk <= 16384
+        assert (k - 1) * chunk < cols <= k * chunk
+
+
+def test_partial_merge_validation(lib):
+    assert lib.lse_rows_num_chunks(100, 7) == 15
+    assert lib.lse_rows_num_chunks(0, 7) == -1
+    assert lib.lse_rows_partial(FAKE, 4, 100, 0, FAKE2, None) == LSE_ERR_SHAPE
+    assert lib.lse_rows_partial(None, 4, 100, 7, FAKE2, None) == LSE_ERR_NULL
+    assert lib.lse_rows_merge(FAKE, 4, 0, FAKE2, None) == LSE_ERR_SHAPE
+    assert lib.lse_rows_merge(None, 4, 3, FAKE2, None) == LSE_ERR_NULL
+
+
+def test_chain_validation(lib):
+    args = lambda K=3, Cin=8, Cout=64, G=16, ws=FAKE2, wsb=1 << 30: (
+        FAKE, FAKE, None, None, None, 2, Cin, 10, 10, Cout, K, G, ctypes.c_float(1e-5),
+        ctypes.c_void_p(0x5000000000), ws, wsb, None)
+    assert lib.fused_conv_gn_act_lse(*args(K=5)) == LSE_ERR_UNSUPPORTED
+    assert lib.fused_conv_gn_act_lse(*args(Cin=3)) == LSE_ERR_UNSUPPORTED
+    assert lib.fused_conv_gn_act_lse(*args(G=3)) == LSE_ERR_SHAPE          # 64 % 3 != 0
+    assert lib.fused_conv_gn_act_lse(*args(G=32)) == LSE_ERR_UNSUPPORTED   # 2-channel groups
+    assert lib.fused_conv_gn_act_lse(*args(ws=None)) == LSE_ERR_WORKSPACE
+    assert lib.fused_conv_gn_act_lse(*args(wsb=16)) == LSE_ERR_WORKSPACE
+    need = lib.fused_conv_gn_act_lse_workspace_bytes(128, 8, 128, 128, 64, 3, 16)
+    assert need == 2 * 128 * 16 * 4 + 128 * 16 * 63 * 16   # mean, rstd, then tile partials

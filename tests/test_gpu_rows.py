@@ -1,0 +1,153 @@
+"""GPU parity of log_softmax_rows, lse_rows_partial and lse_rows_merge (through
+the C ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import log_softmax_reductions_amd as L
+from log_softmax_reductions_amd import inputs
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _lsm(x_dev, ws=None):
+    y = L.log_softmax_rows(x_dev, ws=ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def test_rows_small_workload(orc):
+    """(128, 4096) with 1% x50 outliers and 1% -inf entries."""
+    x = inputs.make("rows_small", DEV)
+    y = _lsm(x)
+    ref, _ = orc.log_softmax_rows(x.cpu().numpy())
+    s = compare(y, ref, what="rows_small")
+    print("rows_small", s)
+
+
+@pytest.mark.parametrize("cols", [1, 3, 4, 63, 64, 65, 1000, 1024, 1025, 4097, 16383, 16384,
+                                  16385, 20000, 49153, 100001, 131072])
+@pytest.mark.parametrize("rows", [1, 3, 7])
+def test_rows_shapes(orc, rows, cols):
+    x = inputs.normal((rows, cols), seed=rows * 1000003 + cols, sigma=4.0, device=DEV)
+    ref, _ = orc.log_softmax_rows(x.cpu().numpy())
+    compare(_lsm(x), ref, what=f"rows={rows} cols={cols}")
+
+
+@pytest.mark.parametrize("cols", [4096, 65536])
+def test_rows_misaligned(orc, cols):
+    buf = inputs.normal((3 * cols + 1,), seed=cols, device=DEV)
+    x = buf[1:].view(3, cols)
+    ref, _ = orc.log_softmax_rows(x.cpu().numpy())
+    compare(_lsm(x), ref, what="misaligned")
+
+
+def test_rows_special_values(orc):
+    cols = 40000   # split across 3 workgroups
+    x = inputs.normal((8, cols), seed=5, device=DEV).cpu()
+    x[0, :] = -float("inf")                       # all -inf -> NaN row
+    x[1, 12345] = float("inf")                    # +inf -> -inf / NaN
+    x[2, 30000] = float("nan")                    # NaN -> NaN row
+    x[3, :] = -float("inf"); x[3, 39999] = 2.5    # one finite entry -> 0 there
+    x[4, :] = 3.0                                 # equal -> -log(cols)
+    x[5, :20000] = -float("inf")                  # first chunks entirely -inf
+    x[6, ::2] = -float("inf")
+    x[7, 17] = 1e30
+    y = _lsm(x.to(DEV))
+    ref, _ = orc.log_softmax_rows(x.numpy())
+    compare(y, ref, what="special")
+    assert np.isnan(y[0]).all() and np.isnan(y[2]).all()
+    assert y[3, 39999] == 0.0
+
+
+def test_rows_mostly_empty_workgroup(orc):
+    """Workgroups in which most lanes and whole waves hold no data: the (-inf, 0)
+    identity must not turn into NaN (the failure the log_softmax page hit)."""
+    for cols in (5, 70, 16385):
+        x = inputs.normal((4, cols), seed=cols, device=DEV)
+        ref, _ = orc.log_softmax_rows(x.cpu().numpy())
+        y = _lsm(x)
+        assert np.isfinite(y).all()
+        compare(y, ref, what=f"cols={cols}")
+
+
+def test_rows_workspace_contents_irrelevant(orc):
+    x = inputs.normal((16, 50000), seed=77, device=DEV)
+    nbytes = L.log_softmax_rows_workspace_bytes(16, 50000)
+    ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device=DEV)
+    ref, _ = orc.log_softmax_rows(x.cpu().numpy())
+    compare(_lsm(x, ws), ref, what="dirty workspace")
+    compare(_lsm(x, ws), ref, what="reused workspace")
+
+
+def test_rows_large_workload_sampled(orc):
+    """(4096, 393216) N(0, 1): 24 workgroups per row.  Sampled rows against the
+    oracle, every row against properties that hold at any size, and
+    run-to-run bit equality."""
+    rows, cols = 4096, 393216
+    x = inputs.make("rows_large", DEV)
+    assert L.log_softmax_rows_plan(cols) == (24, 16384)
+    y = L.log_softmax_rows(x)
+    torch.cuda.synchronize()
+    sample = [0, 1, 2, 777, 1500, 2047, 2048, 3000, 4093, 4094, 4095]
+    xs = x[sample].cpu().numpy()
+    ref, _ = orc.log_softmax_rows(xs)
+    s = compare(y[sample].cpu().numpy(), ref, what="rows_large sampled")
+    print("rows_large sampled", s)
+    # every row: logsumexp of y is 0 and y <= 0, evaluated in fp64 on the GPU
+    lse = torch.logsumexp(y.double(), dim=1)
+    assert lse.abs().max().item() < 1e-5
+    assert (y <= 0).all().item()
+    y2 = L.log_softmax_rows(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+# ------------------------------------------------------------ partial/merge
+
+@pytest.mark.parametrize("cols,chunk", [(393216 // 8, 49152 // 24), (4096, 4096), (4096, 2048),
+                                        (4096, 1366), (50000, 2084), (4096, 64), (999, 7),
+                                        (70000, 70000), (70000, 20000)])
+def test_partials_and_merge(orc, cols, chunk):
+    rows = 6
+    x = inputs.normal((rows, cols), seed=cols + chunk, sigma=2.0, device=DEV)
+    p = L.lse_rows_partial(x, chunk)
+    lse = L.lse_rows_merge(p)
+    torch.cuda.synchronize()
+    xn = x.cpu().numpy()
+    m_ref, s_ref = orc.lse_chunk_partials(xn, chunk)
+    pc = p.cpu().numpy()
+    assert np.array_equal(pc[..., 0], m_ref.astype(np.float32)), "chunk max must be exact"
+    compare(pc[..., 1], s_ref, atol=0.0, rtol=1e-5, what="chunk sums")
+    _, lse_ref = orc.log_softmax_rows(xn, want_y=False)
+    compare(lse.cpu().numpy(), lse_ref, what="merged row lse")
+
+
+def test_merge_of_oracle_pairs(orc):
+    """lse_rows_merge on given pairs (including identities and +inf pairs)."""
+    rng = np.random.default_rng(3)
+    m = rng.normal(scale=10, size=(5, 40)).astype(np.float32)
+    s = rng.uniform(1, 50, size=(5, 40)).astype(np.float32)
+    m[1, :] = -np.inf; s[1, :] = 0          # all identity -> -inf
+    m[2, 5:] = -np.inf; s[2, 5:] = 0        # mostly identity
+    m[3, 7] = np.inf; s[3, 7] = 2           # +inf pair -> +inf
+    s[4, 9] = np.nan                        # NaN -> NaN
+    pairs = torch.from_numpy(np.stack([m, s], axis=-1)).to(DEV)
+    got = L.lse_rows_merge(pairs).cpu().numpy()
+    ref, _, _ = orc.lse_merge(m.astype(np.float64), s.astype(np.float64))
+    compare(got, ref, what="merge")
+
+
+def test_partials_special_values(orc):
+    x = torch.tensor([[-np.inf, -np.inf, 1.0, 2.0, np.inf, np.inf, np.nan, 0.0, -np.inf, np.nan]],
+                     dtype=torch.float32)
+    p = L.lse_rows_partial(x.to(DEV), 2).cpu().numpy()[0]
+    m_ref, s_ref = orc.lse_chunk_partials(x.numpy(), 2)
+    assert p[0, 0] == -np.inf and p[0, 1] == 0.0
+    assert p[1, 0] == 2.0 and abs(p[1, 1] - s_ref[0, 1]) < 1e-6
+    assert p[2, 0] == np.inf and p[2, 1] == 2.0
+    assert p[3, 0] == 0.0 and np.isnan(p[3, 1])
+    assert p[4, 0] == -np.inf and np.isnan(p[4, 1])
+    assert np.array_equal(p[:, 0], m_ref[0].astype(np.float32))
