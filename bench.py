@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the log-sum-exp engine on one MI355X.
+
+One step = one log_softmax_rows call over the 4096 x 393216 fp32 workload
+(N(0,1), seed 4) with the input already resident in HBM.  W untimed warm-up
+steps, then exactly K timed steps bracketed by torch.cuda.synchronize();
+rank 0 prints ONE JSON line.
+
+  value      algorithmic bytes (read x once + write y once = 8 B/element)
+             divided by the wall time per step, in GB/s (1e9 B/s)
+  roofline   the same algorithmic bytes over the average duration of one
+             launch measured with HIP events on the launch stream, against
+             MI355X's 8 TB/s HBM peak; `traffic` is the HBM bytes per launch
+             read from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+             summary (null when the kernel sources changed since)
+  cpu_baseline  the fp64 C oracle on a bounded sample of the same rows
+  secondary  the other hot-path cases, each timed the same way: logsumexp
+             over dim 0 of (32, 2048, 4096), the conv chain on
+             (128, 8, 128, 128), and the two small cases
+
+Flags: --gpus N (only 1 is supported: this build runs on one GPU),
+--steps K, --warmup W, --no-cpu-baseline, --no-secondary,
+--only {rows_large,axis0_large,conv_chain,copy} to run just that kernel
+(for profiler runs; prints timing only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
+METRIC = "GB/s and % of HBM roofline for log_softmax 4096x393216 fp32 on 1 MI355X"
+ROWS, COLS = 4096, 393216
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "log_softmax_rows_4096x393216_traffic.md")
+KERNEL_SOURCES = ["log_softmax_reductions_amd/csrc/lse_rows.hip",
+                  "log_softmax_reductions_amd/csrc/lse_device.hpp",
+                  "log_softmax_reductions_amd/csrc/lse_internal.hpp"]
+
+
+def kernel_source_hash(files=KERNEL_SOURCES) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from the committed counter summary, or None if the
+    summary is missing or was taken on different kernel sources."""
+    try:
+        text = open(PROFILE_TRAFFIC).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel source hash:\s*`?([0-9a-f]{16})", text)
+    m_bytes = re.search(r"HBM bytes per launch \(scaled\):\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def timed_launches(fn, steps, warmup):
+    """Run fn warmup times, then `steps` times with a HIP event pair around each
+    launch on the current stream.  Returns (wall_ms_per_step, event_ms_list)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(x_dev, target_s=10.0):
+    """The fp64 oracle (as it stands) on whole rows of the workload, timed on
+    the host's cores; rows are added in blocks until about target_s of wall
+    time has been spent."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    oracle.load()
+    rows_done, secs, block = 0, 0.0, 16
+    while rows_done < ROWS:
+        xs = x_dev[rows_done:rows_done + block].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.log_softmax_rows(xs, want_y=True, nthreads=threads)
+        secs += time.perf_counter() - t0
+        rows_done += block
+        if secs >= target_s:
+            break
+        per_row = secs / rows_done
+        block = int(min(64, max(16, (target_s - secs) / per_row)))
+        block = min(block, ROWS - rows_done)
+    nbytes = rows_done * COLS * 8
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows_done} of {ROWS} rows (x {COLS} cols) of the same workload, "
+                      f"fp64 log_softmax incl. the y write, {secs:.1f} s wall"}
+
+
+def bench_rows_large(steps, warmup):
+    import torch
+    import log_softmax_reductions_amd as L
+    from log_softmax_reductions_amd import inputs
+    x = inputs.make("rows_large", "cuda")
+    y = torch.empty_like(x)
+    ws = torch.empty(L.log_softmax_rows_workspace_bytes(ROWS, COLS), dtype=torch.uint8,
+                     device="cuda")
+    wall, ev = timed_launches(lambda: L.log_softmax_rows(x, y, ws), steps, warmup)
+    return x, wall, ev
+
+
+def bench_secondary(steps=10, warmup=3):
+    import torch
+    import log_softmax_reductions_amd as L
+    from log_softmax_reductions_amd import inputs
+    out = {}
+    # logsumexp over dim 0 of (32, 2048, 4096): 1 GiB read + 32 MiB written
+    x = inputs.make("axis0_large", "cuda")
+    o = torch.empty(x.shape[1:], device="cuda")
+    wall, ev = timed_launches(lambda: L.lse_reduce_axis0(x, o), steps, warmup)
+    nbytes = x.numel() * 4 + o.numel() * 4
+    avg = sum(ev) / len(ev)
+    out["axis0_large"] = {"workload": "logsumexp dim=0 (32,2048,4096) fp32 N(0,4)",
+                          "ms": round(avg, 4), "GB/s": round(nbytes / avg / 1e6, 1),
+                          "hbm_frac": round(nbytes / avg / 1e6 / HBM_PEAK_GBS, 4)}
+    del x, o
+    # conv chain (128, 8, 128, 128) -> (128, 1, 126, 126)
+    x, w, b, g, be = inputs.make("conv_chain", "cuda")
+    o = torch.empty((128, 1, 126, 126), device="cuda")
+    ws = torch.empty(L.fused_conv_gn_act_lse_workspace_bytes(128, 8, 128, 128, 64, 3, 16),
+                     dtype=torch.uint8, device="cuda")
+    wall, ev = timed_launches(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, o, ws),
+                              steps, warmup)
+    avg = sum(ev) / len(ev)
+    flop = 2 * 128 * 64 * 8 * 9 * 126 * 126   # one conv, counted once
+    out["conv_chain"] = {"workload": "conv3x3 8->64, GN16, tanh, hardswish, +res, LSE dim=1, "
+                                     "x (128,8,128,128)",
+                         "ms": round(avg, 4), "conv_TFLOP/s": round(flop / avg / 1e9, 2),
+                         "mfma_frac_of_fp32_peak": round(flop / avg / 1e9 / FP32_MFMA_PEAK_TFLOPS,
+                                                         4),
+                         "note": "GroupNorm needs whole-sample statistics, so the conv runs "
+                                 "twice (stats pass, then epilogue pass); TFLOP/s counts it once"}
+    del x, w, b, g, be, o, ws
+    # small cases: hot latency per call
+    x = inputs.make("rows_small", "cuda")
+    y = torch.empty_like(x)
+    wall, ev = timed_launches(lambda: L.log_softmax_rows(x, y), 50, 10)
+    out["rows_small"] = {"workload": "log_softmax dim=1 (128,4096) with -inf/x50 entries",
+                         "us": round(1e3 * sum(ev) / len(ev), 2)}
+    x = inputs.make("axis0_small", "cuda")
+    o = torch.empty((10, 32), device="cuda")
+    wall, ev = timed_launches(lambda: L.lse_reduce_axis0(x, o), 50, 10)
+    out["axis0_small"] = {"workload": "logsumexp dim=0 (4,10,32)",
+                          "us": round(1e3 * sum(ev) / len(ev), 2)}
+    return out
+
+
+def run_only(which, steps, warmup):
+    """Run one kernel alone (profiler runs) and print its event timing."""
+    import torch
+    import log_softmax_reductions_amd as L
+    from log_softmax_reductions_amd import inputs
+    if which == "rows_large":
+        _, wall, ev = bench_rows_large(steps, warmup)
+    elif which == "axis0_large":
+        x = inputs.make("axis0_large", "cuda")
+        o = torch.empty(x.shape[1:], device="cuda")
+        wall, ev = timed_launches(lambda: L.lse_reduce_axis0(x, o), steps, warmup)
+    elif which == "conv_chain":
+        x, w, b, g, be = inputs.make("conv_chain", "cuda")
+        o = torch.empty((128, 1, 126, 126), device="cuda")
+        wall, ev = timed_launches(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, o),
+                                  steps, warmup)
+    elif which == "copy":
+        # plain device copy of 1 GiB: calibrates the HBM byte counters
+        a = torch.empty(1 << 28, device="cuda")
+        c = torch.empty_like(a)
+        wall, ev = timed_launches(lambda: c.copy_(a), steps, warmup)
+    else:
+        raise SystemExit(f"unknown --only {which}")
+    print(json.dumps({"only": which, "steps": steps, "wall_ms": round(wall, 4),
+                      "event_ms_avg": round(sum(ev) / len(ev), 4),
+                      "event_ms_min": round(min(ev), 4)}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--only", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.only:
+        run_only(args.only, args.steps, args.warmup)
+        return
+
+    x, wall_ms, ev = bench_rows_large(args.steps, args.warmup)
+    alg_bytes = 2 * 4 * ROWS * COLS
+    value = alg_bytes / (wall_ms * 1e-3) / 1e9
+    ev_avg = sum(ev) / len(ev)
+    achieved = alg_bytes / (ev_avg * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "log_softmax dim=1, x (4096, 393216) fp32 i.i.d. N(0,1), seed 4",
+                   "rows": ROWS, "cols": COLS, "elements_per_s": round(ROWS * COLS /
+                                                                       (wall_ms * 1e-3), 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(),
+                     "kernel": "log_softmax_rows_kernel<64, true, true>",
+                     "event_ms_avg": round(ev_avg, 4), "event_ms_min": round(min(ev), 4)},
+    }
+    if not args.no_secondary:
+        line["secondary"] = bench_secondary()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
