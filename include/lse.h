@@ -94,12 +94,14 @@ size_t log_softmax_rows_workspace_bytes(int64_t rows, int64_t cols);
 lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows,
                               int64_t cols, void *ws, size_t ws_bytes,
                               hipStream_t stream);
-/* Bound on how long a workgroup of a split row polls for its row's partials
- * (default 2^24 polls; independently, a workgroup never waits longer than
- * about 0.1 s, far beyond any real wait).  A workgroup that runs out
- * writes NaN for its chunk and sets the 32-bit word at byte offset 4 of the
- * workspace to nonzero.  Affects calls enqueued after it returns; intended
- * for tests of that failure path. */
+/* How many times a workgroup of a split row polls for its siblings' (max,
+ * sum) pairs before it computes the missing ones itself from x (default 2^24;
+ * independently it never waits longer than about 50 us).  The results are
+ * the same either way.  After a call has run, the 32-bit word at byte offset
+ * 4 of the workspace holds the number of pairs computed that way.  A limit of
+ * 0 also stops each workgroup from publishing its own pair, so that every
+ * pair comes from that path (the count is then rows x chunks).  Affects calls
+ * enqueued after it returns; intended for tests of that path. */
 void lse_set_spin_limit(uint32_t polls);
 /* The split log_softmax_rows will use for a row length: *nchunks workgroups
  * per row, each covering *chunk consecutive columns (the last may be short).

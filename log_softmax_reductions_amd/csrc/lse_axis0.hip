@@ -21,7 +21,20 @@
 namespace lse {
 namespace {
 
-constexpr int kAxis0Threads = 256;
+#ifndef LSE_AXIS0_THREADS
+#define LSE_AXIS0_THREADS 64   // one wave per workgroup measured fastest
+#endif
+#ifndef LSE_AXIS0_W
+#define LSE_AXIS0_W 4   // outputs per lane on the 128-bit path (4 or 8)
+#endif
+#ifndef LSE_AXIS0_RBMAX
+#define LSE_AXIS0_RBMAX 32   // planes held in registers at once
+#endif
+#ifndef LSE_AXIS0_NT_LOAD
+#define LSE_AXIS0_NT_LOAD 1   // x is read exactly once: non-temporal loads
+#endif
+constexpr int kAxis0Threads = LSE_AXIS0_THREADS;
+constexpr int kVecW = LSE_AXIS0_W;
 
 __device__ __forceinline__ float safe_shift(float m) { return is_finite(m) ? m : 0.0f; }
 
@@ -41,10 +54,29 @@ __device__ __forceinline__ void fold_block(const float (&v)[NB], float &m, float
   s = acc;
 }
 
+// W consecutive values of one plane into column i of v (128-bit loads for W >= 4).
+template <int W, int RB>
+__device__ __forceinline__ void load_plane(const float *p, float (&v)[W][RB], int i) {
+  if constexpr (W == 1) {
+    v[0][i] = *p;
+  } else {
+#pragma unroll
+    for (int h = 0; h < W / 4; ++h) {
+#if LSE_AXIS0_NT_LOAD
+      typedef float v4f __attribute__((ext_vector_type(4)));
+      const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p + 4 * h));
+#else
+      const float4 t = *reinterpret_cast<const float4 *>(p + 4 * h);
+#endif
+      v[4 * h][i] = t.x; v[4 * h + 1][i] = t.y; v[4 * h + 2][i] = t.z; v[4 * h + 3][i] = t.w;
+    }
+  }
+}
+
 template <int RB, int W>
 __global__ __launch_bounds__(kAxis0Threads) void lse_axis0_kernel(
     const float *__restrict__ x, float *__restrict__ out, int64_t R, int64_t inner) {
-  const int64_t nq = inner / W;  // W == 4: inner % 4 == 0 by dispatch
+  const int64_t nq = inner / W;  // W > 1: inner % W == 0 by dispatch
   const int64_t q = (int64_t)blockIdx.x * kAxis0Threads + threadIdx.x;
   if (q >= nq) return;
   float m[W], s[W];
@@ -59,24 +91,12 @@ __global__ __launch_bounds__(kAxis0Threads) void lse_axis0_kernel(
     const float *base = x + r0 * inner + q * W;
     if (nb == RB) {
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        if constexpr (W == 4) {
-          const float4 t = *reinterpret_cast<const float4 *>(base + (int64_t)i * inner);
-          v[0][i] = t.x; v[1][i] = t.y; v[2][i] = t.z; v[3][i] = t.w;
-        } else {
-          v[0][i] = base[(int64_t)i * inner];
-        }
-      }
+      for (int i = 0; i < RB; ++i) load_plane<W>(base + (int64_t)i * inner, v, i);
     } else {
 #pragma unroll
       for (int i = 0; i < RB; ++i) {
         if (i < nb) {
-          if constexpr (W == 4) {
-            const float4 t = *reinterpret_cast<const float4 *>(base + (int64_t)i * inner);
-            v[0][i] = t.x; v[1][i] = t.y; v[2][i] = t.z; v[3][i] = t.w;
-          } else {
-            v[0][i] = base[(int64_t)i * inner];
-          }
+          load_plane<W>(base + (int64_t)i * inner, v, i);
         } else {
 #pragma unroll
           for (int w = 0; w < W; ++w) v[w][i] = -__builtin_inff();  // identity
@@ -89,20 +109,23 @@ __global__ __launch_bounds__(kAxis0Threads) void lse_axis0_kernel(
   float r[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) r[w] = m[w] + logf(s[w]);
-  if constexpr (W == 4) {
-    *reinterpret_cast<float4 *>(out + q * 4) = make_float4(r[0], r[1], r[2], r[3]);
-  } else {
+  if constexpr (W == 1) {
     out[q] = r[0];
+  } else {
+#pragma unroll
+    for (int h = 0; h < W / 4; ++h)
+      *reinterpret_cast<float4 *>(out + q * W + 4 * h) =
+          make_float4(r[4 * h], r[4 * h + 1], r[4 * h + 2], r[4 * h + 3]);
   }
 }
 
 template <int RB>
 hipError_t launch_rb(const float *x, float *out, int64_t R, int64_t inner, bool vec,
                      hipStream_t stream) {
-  const int64_t items = vec ? inner / 4 : inner;
+  const int64_t items = vec ? inner / kVecW : inner;
   const int64_t blocks = (items + kAxis0Threads - 1) / kAxis0Threads;
   if (vec)
-    hipLaunchKernelGGL((lse_axis0_kernel<RB, 4>), dim3((uint32_t)blocks), dim3(kAxis0Threads),
+    hipLaunchKernelGGL((lse_axis0_kernel<RB, kVecW>), dim3((uint32_t)blocks), dim3(kAxis0Threads),
                        0, stream, x, out, R, inner);
   else
     hipLaunchKernelGGL((lse_axis0_kernel<RB, 1>), dim3((uint32_t)blocks), dim3(kAxis0Threads),
@@ -115,10 +138,10 @@ hipError_t launch_rb(const float *x, float *out, int64_t R, int64_t inner, bool 
 hipError_t launch_lse_axis0(const float *x, float *out, int64_t R, int64_t inner,
                             hipStream_t stream) {
   if (inner == 0) return hipSuccess;
-  const bool vec = (inner % 4 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)out % 16 == 0);
+  const bool vec = (inner % kVecW == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)out % 16 == 0);
   if (R <= 4) return launch_rb<4>(x, out, R, inner, vec, stream);
-  if (R <= 8) return launch_rb<8>(x, out, R, inner, vec, stream);
-  if (R <= 16) return launch_rb<16>(x, out, R, inner, vec, stream);
+  if (R <= 8 || LSE_AXIS0_RBMAX <= 8) return launch_rb<8>(x, out, R, inner, vec, stream);
+  if (R <= 16 || LSE_AXIS0_RBMAX <= 16) return launch_rb<16>(x, out, R, inner, vec, stream);
   return launch_rb<32>(x, out, R, inner, vec, stream);
 }
 

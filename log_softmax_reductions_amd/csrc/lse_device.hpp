@@ -87,6 +87,13 @@ __device__ __forceinline__ float pair_term_general(float v, float m) {
   return expf(v - m);
 }
 
+// The same term when m is known to be +-inf: v == m counts 1 for m = +inf
+// and 0 for m = -inf, a NaN stays NaN, and anything else is exp(-inf) = 0.
+__device__ __forceinline__ float pair_term_nonfinite(float v, float m) {
+  const float hit = (m > 0.0f) ? 1.0f : 0.0f;
+  return (v == m) ? hit : ((v != v) ? v : 0.0f);
+}
+
 // Weight of a partial whose max is mk inside a merge whose max is M.
 __device__ __forceinline__ float merge_weight(float mk, float M) {
   return (mk == M) ? 1.0f : expf(mk - M);
@@ -101,8 +108,11 @@ __device__ __forceinline__ uint64_t pack_pair(float m, float s) {
 __device__ __forceinline__ float pair_m(uint64_t p) { return bitsf((uint32_t)p); }
 __device__ __forceinline__ float pair_s(uint64_t p) { return bitsf((uint32_t)(p >> 32)); }
 
-__device__ __forceinline__ void store_pair_agent(uint64_t *slot, uint64_t p) {
-  __hip_atomic_store(slot, p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Publish p into an empty (zero) slot; false if the slot was already written.
+__device__ __forceinline__ bool publish_pair_once(uint64_t *slot, uint64_t p) {
+  uint64_t expected = 0;
+  return __hip_atomic_compare_exchange_strong(slot, &expected, p, __ATOMIC_RELAXED,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t load_pair_agent(const uint64_t *slot) {
   return __hip_atomic_load(const_cast<uint64_t *>(slot), __ATOMIC_RELAXED,

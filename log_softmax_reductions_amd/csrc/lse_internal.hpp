@@ -14,15 +14,22 @@ hipError_t launch_lse_axis0(const float *x, float *out, int64_t R, int64_t inner
                             hipStream_t stream);
 
 // ---------------------------------------------------------------- case B
-constexpr int kRowsThreads = 256;              // one workgroup = 4 waves
-constexpr int kRowsMaxVpl = 64;                // floats held per lane
-constexpr int64_t kRowsTile = (int64_t)kRowsThreads * kRowsMaxVpl;  // 16384
+// Tile geometry of the row kernels (overridable at build time for sweeps).
+#ifndef LSE_ROWS_THREADS
+#define LSE_ROWS_THREADS 512
+#endif
+#ifndef LSE_ROWS_MAX_VPL
+#define LSE_ROWS_MAX_VPL 32
+#endif
+constexpr int kRowsThreads = LSE_ROWS_THREADS;  // lanes per workgroup
+constexpr int kRowsMaxVpl = LSE_ROWS_MAX_VPL;   // floats held per lane
+constexpr int64_t kRowsTile = (int64_t)kRowsThreads * kRowsMaxVpl;  // 16384 columns
 constexpr int64_t kRowsMaxChunks = 1 << 20;
 
 // Split workspace: a 256-byte header, then rows * nchunks packed pairs.
 struct RowsWsHeader {
-  uint32_t ticket;   // next (row, chunk) ticket to hand out
-  uint32_t error;    // nonzero once a workgroup gave up waiting
+  uint32_t reserved;
+  uint32_t helped;   // chunk pairs computed by a sibling workgroup, not their owner
   uint32_t pad[62];
 };
 static_assert(sizeof(RowsWsHeader) == 256, "header is 256 bytes");

@@ -10,21 +10,20 @@
 //   NaN once idle lanes holding (-inf, 0) meet.
 //
 // Design here (gfx950):
-//   * A workgroup of 256 lanes owns one chunk of up to 16384 columns and keeps
-//     it in VGPRs (64 floats per lane, 16 global_load_dwordx4 per lane), so the
-//     chunk is read from HBM exactly once and written exactly once.
+//   * A workgroup of 512 lanes owns one chunk of up to 16384 columns and keeps
+//     it in VGPRs (32 floats per lane, 8 global_load_dwordx4 per lane), so the
+//     chunk is read from HBM exactly once and written exactly once; loads and
+//     stores are non-temporal (nothing is re-read through the caches).
 //   * Exact chunk max (DPP/permlane wave reduce + LDS), then the sum of
 //     exp(x - max) over the registers: one exponential per element.
 //   * A row of k > 1 chunks: each workgroup publishes its pair as one packed
-//     64-bit word with an agent-scope atomic store, then wave 0 polls the row's
-//     k words until all are written and every workgroup of the row merges the
-//     same k pairs in the same order (so all get the bitwise-same row LSE).
-//     Work is handed out by an atomic ticket counter, so the chunks of a row
-//     are always claimed by workgroups that are already running: a waiting
-//     workgroup only waits on chunks whose owners are resident and never wait
-//     themselves before publishing.  The wait is bounded in polls
-//     (set_spin_limit) and in time (0.1 s); a workgroup that gives up flags
-//     the workspace and writes NaN.
+//     64-bit word (agent-scope compare-and-swap from 0), wave 0 polls the
+//     row's k words, and every workgroup of the row merges the same k pairs in
+//     the same order (so all get the bitwise-same row LSE) and writes its
+//     chunk of y from registers.  A workgroup that has waited 50 us computes
+//     any still-missing sibling pair itself from x; the first writer of a slot
+//     wins.  No global counter is touched and no workgroup can wait on one
+//     that never starts, whatever the dispatch order.
 //   * The write is y = (x - M) - log(S): x - M is exact for the large entries,
 //     so the result keeps its accuracy when |M| is large.
 #include "lse_device.hpp"
@@ -34,15 +33,39 @@ namespace lse {
 namespace {
 
 constexpr int kNW = kRowsThreads / kWave;  // waves per workgroup
+#ifndef LSE_ROWS_SLEEP
+#define LSE_ROWS_SLEEP 8          // s_sleep argument between polls (x 64 clocks)
+#endif
+#ifndef LSE_ROWS_NT_LOAD
+#define LSE_ROWS_NT_LOAD 1        // x is read once from HBM: non-temporal loads
+#endif
+#ifndef LSE_ROWS_NT_STORE
+#define LSE_ROWS_NT_STORE 1       // y is never re-read: non-temporal stores
+#endif
 uint32_t h_spin_limit = 1u << 24;
 
 // Load a chunk of `len` values starting at p into v (lane-strided so that each
-// wave's load is one contiguous span), padding with -inf.
+// wave's load is one contiguous span), padding with -inf.  A full chunk (the
+// common case) takes an unchecked path.
 template <int VPL, bool VEC>
 __device__ __forceinline__ void load_chunk(const float *__restrict__ p, int64_t len,
                                            float (&v)[VPL]) {
   const int t = threadIdx.x;
   if constexpr (VEC) {
+    if (len == (int64_t)VPL * kRowsThreads) {
+      typedef float v4 __attribute__((ext_vector_type(4)));
+      const v4 *p4 = reinterpret_cast<const v4 *>(p) + t;
+#pragma unroll
+      for (int q = 0; q < VPL / 4; ++q) {
+#if LSE_ROWS_NT_LOAD
+        const v4 f = __builtin_nontemporal_load(p4 + q * kRowsThreads);
+#else
+        const v4 f = p4[q * kRowsThreads];
+#endif
+        v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+      }
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < VPL / 4; ++q) {
       const int64_t idx = ((int64_t)q * kRowsThreads + t) * 4;
@@ -63,22 +86,29 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ p, int64_t 
   }
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// y is written once and never re-read here: non-temporal 128-bit stores.
+__device__ __forceinline__ void store4(float *p, float a, float b, float c, float d) {
+#if LSE_ROWS_NT_STORE
+  __builtin_nontemporal_store(v4f{a, b, c, d}, reinterpret_cast<v4f *>(p));
+#else
+  *reinterpret_cast<float4 *>(p) = make_float4(a, b, c, d);
+#endif
+}
+
 template <int VPL, bool VEC>
 __device__ __forceinline__ void store_chunk(float *__restrict__ p, int64_t len,
                                             const float (&v)[VPL], float M, float lnS) {
   const int t = threadIdx.x;
   if constexpr (VEC) {
+    const bool full = (len == (int64_t)VPL * kRowsThreads);
 #pragma unroll
     for (int q = 0; q < VPL / 4; ++q) {
       const int64_t idx = ((int64_t)q * kRowsThreads + t) * 4;
-      if (idx < len) {
-        float4 f;
-        f.x = (v[4 * q] - M) - lnS;
-        f.y = (v[4 * q + 1] - M) - lnS;
-        f.z = (v[4 * q + 2] - M) - lnS;
-        f.w = (v[4 * q + 3] - M) - lnS;
-        *reinterpret_cast<float4 *>(p + idx) = f;
-      }
+      if (full || idx < len)
+        store4(p + idx, (v[4 * q] - M) - lnS, (v[4 * q + 1] - M) - lnS,
+               (v[4 * q + 2] - M) - lnS, (v[4 * q + 3] - M) - lnS);
     }
   } else {
 #pragma unroll
@@ -90,19 +120,40 @@ __device__ __forceinline__ void store_chunk(float *__restrict__ p, int64_t len,
 }
 
 // The chunk's pair (exact max, sum of exp(v - max)); identical in every lane.
+// Four independent accumulators shorten the dependency chains.
 template <int VPL>
 __device__ __forceinline__ void chunk_pair(const float (&v)[VPL], float *red, float &m,
                                            float &s) {
-  float lm = v[0];
+  static_assert(VPL % 4 == 0, "VPL is a multiple of 4");
+  float lm[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
-  for (int e = 1; e < VPL; ++e) lm = fmaxf(lm, v[e]);
-  m = block_allreduce<kNW>(lm, OpMax{}, red);
-  float ls = 0.0f;
+  for (int e = 4; e < VPL; ++e) lm[e % 4] = fmaxf(lm[e % 4], v[e]);
+  m = block_allreduce<kNW>(fmaxf(fmaxf(lm[0], lm[1]), fmaxf(lm[2], lm[3])), OpMax{}, red);
+  float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (is_finite(m)) {  // uniform branch: m is the same in every lane
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) ls += exp_base2(v[e] - m);
+    for (int e = 0; e < VPL; ++e) ls[e % 4] += exp_base2(v[e] - m);
   } else {
-    for (int e = 0; e < VPL; ++e) ls += pair_term_general(v[e], m);
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) ls[e % 4] += pair_term_nonfinite(v[e], m);
+  }
+  s = block_allreduce<kNW>((ls[0] + ls[1]) + (ls[2] + ls[3]), OpSum{}, red);
+}
+
+// The pair of a chunk streamed from memory by the whole workgroup: an exact
+// max pass, then a sum pass (the second read is served by cache).  Used for
+// chunks longer than the register tile and by a workgroup that computes a
+// sibling's missing pair.
+__device__ __forceinline__ void stream_chunk_pair(const float *__restrict__ p, int64_t len,
+                                                  float *red, float &m, float &s) {
+  float lm = -__builtin_inff();
+  for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) lm = fmaxf(lm, p[i]);
+  m = block_allreduce<kNW>(lm, OpMax{}, red);
+  float ls = 0.0f;
+  if (is_finite(m)) {
+    for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) ls += exp_base2(p[i] - m);
+  } else {
+    for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) ls += pair_term_general(p[i], m);
   }
   s = block_allreduce<kNW>(ls, OpSum{}, red);
 }
@@ -133,12 +184,13 @@ __device__ __forceinline__ void wave_merge_pairs(const uint64_t *pairs, int64_t 
   }
 }
 
-// Longest a workgroup waits for its row, in ticks of the 100 MHz real-time
-// counter: 0.1 s, some four orders of magnitude above a real wait.
-constexpr uint64_t kWaitTicks = 10000000ull;
+// How long a workgroup waits for its siblings before computing their pairs
+// itself, in ticks of the 100 MHz real-time counter (50 us; a real wait is a
+// few microseconds).
+constexpr uint64_t kHelpTicks = 5000ull;
 
-// Wave 0 waits until all k pair words of a row are non-zero.  Returns false
-// when the poll limit or the time limit runs out.
+// Wave 0 polls until all k pair words of a row are non-zero (true), or the
+// poll limit or the time threshold runs out (false).
 __device__ __forceinline__ bool wave_wait_pairs(const uint64_t *pairs, int64_t k,
                                                 uint32_t limit) {
   const int lane = threadIdx.x % kWave;
@@ -147,29 +199,36 @@ __device__ __forceinline__ bool wave_wait_pairs(const uint64_t *pairs, int64_t k
     bool missing = false;
     for (int64_t j = lane; j < k; j += kWave) missing |= (load_pair_agent(pairs + j) == 0);
     if (__builtin_amdgcn_ballot_w64(missing) == 0) return true;
-    if (it >= limit || __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) return false;
-    __builtin_amdgcn_s_sleep(2);
+    if (it >= limit || __builtin_amdgcn_s_memrealtime() - t0 > kHelpTicks) return false;
+    __builtin_amdgcn_s_sleep(LSE_ROWS_SLEEP);
   }
 }
 
-// One workgroup = one (row, chunk).  SPLIT: rows of nchunks > 1 chunks, work
-// handed out by ticket, pairs merged through the workspace.  !SPLIT: one
-// workgroup per row (nchunks == 1), blockIdx.x is the row.
+// One workgroup = one (row, chunk).  SPLIT: rows of nchunks > 1 chunks whose
+// pairs are merged through the workspace.  !SPLIT: one workgroup per row.
+//
+// Split rows: blockIdx.x, in row-major order, picks the (row, chunk), so the
+// chunks of a row are dispatched together and the workgroups in flight
+// stream one contiguous region of x and y.  (Giving each of the 8 XCDs its
+// own run of whole rows instead was measured 30% slower.)  Each workgroup
+// publishes its pair with a compare-and-swap from 0 and waits for its
+// siblings.  A workgroup that has waited kHelpTicks (or spin_limit polls)
+// computes every still-missing sibling pair itself from x, which is
+// read-only, and publishes it the same way; the first writer of a slot wins,
+// so all workgroups of a row merge identical pairs.  Progress therefore never
+// depends on the order or timing in which blocks are dispatched: no workgroup
+// waits on one that has not started.
 template <int VPL, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
-    const float *__restrict__ x, float *__restrict__ y, int64_t cols, int64_t nchunks,
-    int64_t chunk, RowsWsHeader *__restrict__ hdr, uint64_t *__restrict__ pairs,
-    uint32_t spin_limit) {
+    const float *__restrict__ x, float *__restrict__ y, int64_t rows, int64_t cols,
+    int64_t nchunks, int64_t chunk, RowsWsHeader *__restrict__ hdr,
+    uint64_t *__restrict__ pairs, uint32_t spin_limit) {
   __shared__ float red[kNW];
-  __shared__ uint32_t s_ticket;
+  __shared__ int s_state;
   __shared__ float s_final[2];
   int64_t row, c;
   if constexpr (SPLIT) {
-    if (threadIdx.x == 0)
-      s_ticket = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int64_t t = s_ticket;
+    const int64_t t = blockIdx.x;
     row = t / nchunks;
     c = t - row * nchunks;
   } else {
@@ -189,16 +248,35 @@ __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
   float M, lnS;
   if constexpr (SPLIT) {
     uint64_t *row_pairs = pairs + row * nchunks;
-    if (threadIdx.x == 0) store_pair_agent(row_pairs + c, pack_pair(m, s));
+    // spin_limit == 0 is a test mode: the owner leaves its slot to the
+    // helping path, so every pair of the row is computed by a helper.
+    if (threadIdx.x == 0 && spin_limit != 0) publish_pair_once(row_pairs + c, pack_pair(m, s));
+    for (;;) {
+      if (threadIdx.x < kWave) {
+        const bool all = wave_wait_pairs(row_pairs, nchunks, spin_limit);
+        if (threadIdx.x == 0) s_state = all ? 1 : 0;
+      }
+      __syncthreads();
+      if (s_state == 1) break;  // uniform: every thread read the same LDS word
+      // Help: compute each still-missing sibling pair from x.
+      for (int64_t j = 0; j < nchunks; ++j) {
+        __syncthreads();
+        if (threadIdx.x == 0) s_state = (load_pair_agent(row_pairs + j) == 0) ? 2 : 0;
+        __syncthreads();
+        if (s_state == 2) {
+          const int64_t j0 = j * chunk;
+          const int64_t lj = (cols - j0 < chunk) ? (cols - j0) : chunk;
+          float hm, hs;
+          stream_chunk_pair(x + row * cols + j0, lj, red, hm, hs);
+          if (threadIdx.x == 0 && publish_pair_once(row_pairs + j, pack_pair(hm, hs)))
+            __hip_atomic_fetch_add(&hdr->helped, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __syncthreads();
+    }
     if (threadIdx.x < kWave) {
       float Mw, Sw;
-      if (wave_wait_pairs(row_pairs, nchunks, spin_limit)) {
-        wave_merge_pairs(row_pairs, nchunks, Mw, Sw);
-      } else {
-        Mw = Sw = __builtin_nanf("");
-        if (threadIdx.x == 0)
-          __hip_atomic_store(&hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      wave_merge_pairs(row_pairs, nchunks, Mw, Sw);
       if (threadIdx.x == 0) {
         s_final[0] = Mw;
         s_final[1] = logf(Sw);
@@ -238,8 +316,7 @@ __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_kernel(
   if (threadIdx.x == 0) partials[t] = make_float2(m, s);
 }
 
-// Chunks longer than the register tile: an exact-max pass, then a sum pass,
-// both streaming through the chunk (the second read is served by cache).
+// Chunks longer than the register tile.
 __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_stream_kernel(
     const float *__restrict__ x, int64_t cols, int64_t nchunks, int64_t chunk,
     float2 *__restrict__ partials) {
@@ -248,17 +325,8 @@ __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_stream_kernel(
   const int64_t row = t / nchunks, c = t - row * nchunks;
   const int64_t c0 = c * chunk;
   const int64_t len = (cols - c0 < chunk) ? (cols - c0) : chunk;
-  const float *p = x + row * cols + c0;
-  float lm = -__builtin_inff();
-  for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) lm = fmaxf(lm, p[i]);
-  const float m = block_allreduce<kNW>(lm, OpMax{}, red);
-  float ls = 0.0f;
-  if (is_finite(m)) {
-    for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) ls += exp_base2(p[i] - m);
-  } else {
-    for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) ls += pair_term_general(p[i], m);
-  }
-  const float s = block_allreduce<kNW>(ls, OpSum{}, red);
+  float m, s;
+  stream_chunk_pair(x + row * cols + c0, len, red, m, s);
   if (threadIdx.x == 0) partials[t] = make_float2(m, s);
 }
 
@@ -304,18 +372,19 @@ int vpl_for(int64_t len) {
 }
 
 template <bool SPLIT>
-hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *y, int64_t cols,
+hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *y, int64_t rows,
+                           int64_t cols,
                            int64_t nchunks, int64_t chunk, RowsWsHeader *hdr, uint64_t *pairs,
                            uint32_t spin_limit, hipStream_t stream) {
 #define LSE_ROWS_CASE(V)                                                                     \
   case V:                                                                                    \
     if (vec)                                                                                 \
       hipLaunchKernelGGL((log_softmax_rows_kernel<V, true, SPLIT>), grid, dim3(kRowsThreads), \
-                         0, stream, x, y, cols, nchunks, chunk, hdr, pairs, spin_limit);     \
+                         0, stream, x, y, rows, cols, nchunks, chunk, hdr, pairs, spin_limit);\
     else                                                                                     \
       hipLaunchKernelGGL((log_softmax_rows_kernel<V, false, SPLIT>), grid,                   \
-                         dim3(kRowsThreads), 0, stream, x, y, cols, nchunks, chunk, hdr,     \
-                         pairs, spin_limit);                                                 \
+                         dim3(kRowsThreads), 0, stream, x, y, rows, cols, nchunks, chunk,    \
+                         hdr, pairs, spin_limit);                                            \
     break;
   switch (vpl) {
     LSE_ROWS_CASE(4)
@@ -360,7 +429,8 @@ hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows, int64
   const bool vec = (cols % 4 == 0) && (p.chunk % 4 == 0) && ((uintptr_t)x % 16 == 0) &&
                    ((uintptr_t)y % 16 == 0);
   if (p.nchunks == 1) {
-    return launch_rows_vpl<false>(vpl_for(cols), vec, dim3((uint32_t)rows), x, y, cols, 1, cols,
+    return launch_rows_vpl<false>(vpl_for(cols), vec, dim3((uint32_t)rows), x, y, rows, cols, 1,
+                                  cols,
                                   nullptr, nullptr, 0u, stream);
   }
   auto *hdr = reinterpret_cast<RowsWsHeader *>(ws);
@@ -371,7 +441,7 @@ hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows, int64
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_rows_vpl<true>(vpl_for(p.chunk), vec, dim3((uint32_t)(rows * p.nchunks)), x, y,
-                               cols, p.nchunks, p.chunk, hdr, pairs, h_spin_limit, stream);
+                               rows, cols, p.nchunks, p.chunk, hdr, pairs, h_spin_limit, stream);
 }
 
 hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, int64_t chunk,

@@ -151,3 +151,30 @@ def test_partials_special_values(orc):
     assert p[3, 0] == 0.0 and np.isnan(p[3, 1])
     assert p[4, 0] == -np.inf and np.isnan(p[4, 1])
     assert np.array_equal(p[:, 0], m_ref[0].astype(np.float32))
+
+
+def test_rows_helping_path(orc):
+    """With the poll limit at 0 no workgroup publishes its own pair: every pair is
+    computed from x by the helping path (a workgroup that finds a sibling's
+    slot empty).  Results must match the oracle and the workspace must count
+    exactly rows x chunks helped pairs."""
+    rows, cols = 64, 393216
+    x = inputs.normal((rows, cols), seed=31, device=DEV)
+    nbytes = L.log_softmax_rows_workspace_bytes(rows, cols)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    sample = [0, 5, 33, 63]
+    ref, _ = orc.log_softmax_rows(x[sample].cpu().numpy())
+    try:
+        L.lse_set_spin_limit(0)
+        y = L.log_softmax_rows(x, ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        L.lse_set_spin_limit(1 << 24)
+    helped = int(ws[4:8].view(torch.int32).item())
+    assert helped == rows * 24, helped      # every pair came from the helping path
+    compare(y[sample].cpu().numpy(), ref, what="helping path")
+    assert torch.logsumexp(y.double(), dim=1).abs().max().item() < 1e-5
+    print("pairs computed by a sibling:", helped)
+    y2 = L.log_softmax_rows(x, ws=ws)
+    torch.cuda.synchronize()
+    compare(y2[sample].cpu().numpy(), ref, what="default path after")
