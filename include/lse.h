@@ -100,8 +100,11 @@ lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows,
  * the same either way.  After a call has run, the 32-bit word at byte offset
  * 4 of the workspace holds the number of pairs computed that way.  A limit of
  * 0 also stops each workgroup from publishing its own pair, so that every
- * pair comes from that path (the count is then rows x chunks).  Affects calls
- * enqueued after it returns; intended for tests of that path. */
+ * pair comes from that path (the count is then rows x chunks).  The same limit
+ * bounds fused_conv_gn_act_lse's wait for the statistics of a sample (there a
+ * workgroup that runs out writes NaN and sets the word after the mean / rstd
+ * block of its workspace, at byte offset align256(8 N groups) + 4).  Affects
+ * calls enqueued after it returns; intended for tests. */
 void lse_set_spin_limit(uint32_t polls);
 /* The split log_softmax_rows will use for a row length: *nchunks workgroups
  * per row, each covering *chunk consecutive columns (the last may be short).

@@ -7,13 +7,23 @@
 // x_conv + that; logsumexp over dim 1 with keepdim.  That page keeps the conv
 // in the vendor library and runs a stats kernel plus a one-block-per-pixel
 // epilogue over the materialised conv output.  Here the conv output is never
-// written to memory:
+// written to memory and the conv runs once:
 //
-//   pass 1  conv tile on MFMA -> per-(sample, group, tile) (count, mean, M2)
-//   merge   Chan's parallel update over a sample's tiles, in fp64 -> mean, rstd
-//   pass 2  the same conv tile recomputed on MFMA -> normalise, tanh,
-//           hardswish, residual, and the 64-channel logsumexp in registers ->
-//           one float per pixel
+//   each workgroup takes a 2 x 128 pixel tile of one sample (tiles handed out
+//   by an atomic ticket, in sample order), stages the x tile in LDS, runs the
+//   conv on MFMA into registers, and publishes the tile's per-group
+//   (mean, M2); it then waits until every tile of its sample has published,
+//   merges the sample's statistics with Chan's parallel update in fp64, and
+//   runs normalise, tanh, hardswish, residual and the 64-channel logsumexp
+//   on the accumulators it still holds, writing one float per pixel.
+//
+// The wait is deadlock-free because tickets are claimed only by running
+// workgroups, in order, and every workgroup publishes before it waits: the
+// tiles of any sample that has a waiting workgroup are all held by running
+// workgroups once its last ticket is claimed, which needs only as many
+// co-resident workgroups as a sample has tiles (63 for 126 x 126; hundreds
+// fit).  The wait is still bounded (poll count and 0.1 s); a workgroup that
+// gives up flags the workspace and writes NaN.
 //
 // GEMM shape per sample: D[c][p] = sum_k W[c][k] * patch[k][p] with c the 64
 // output channels (M), p the pixels (N) and k = (ci, kh, kw), 72 values (K).
@@ -38,18 +48,34 @@ constexpr int kCin = 8, kCout = 64, kKs = 3, kKdim = kCin * kKs * kKs;  // 72
 constexpr int kKSteps = kKdim / 4;                                       // 18
 constexpr int kMT = kCout / 16;                                          // 4 M-tiles
 constexpr int kTileH = 2, kTileW = 128;                                  // output pixels
-constexpr int kLdsH = kTileH + kKs - 1, kLdsW = kTileW + kKs - 1;        // 4 x 130
+constexpr int kLdsH = kTileH + kKs - 1;                                  // 4 input rows
+constexpr int kLdsW = kTileW + 4;     // 130 input columns needed, padded to 33 float4
+constexpr int kF4PerRow = kLdsW / 4;                                     // 33
+constexpr int kStageF4 = kCin * kLdsH * kF4PerRow;                       // 1056
 constexpr int kNB = 4;   // 16-pixel blocks per wave: 4 waves x 4 x 16 = 2 x 128
 constexpr int kThreads = 256;
+// W in LDS, one 72-value row per output channel padded to 76 floats: the A
+// fragment read of a K-step (lane l -> row 16t + l % 16, column 4s + l / 16)
+// then hits 64 distinct banks (row stride 76 = 12 banks mod 64).
+constexpr int kWStride = kKdim + 4;                                      // 76
+constexpr int kWF4 = kCout * kKdim / 4;                                  // 1152 float4
+
+struct ChainWsHeader {
+  uint32_t ticket;  // next tile ticket
+  uint32_t error;   // nonzero once a workgroup gave up waiting
+  uint32_t pad[62];
+};
 
 struct ChainArgs {
   const float *x, *w, *b, *gamma, *beta;
-  int64_t N;
-  int32_t H, W, Ho, Wo, G, tiles_w, tiles;
+  int32_t N, H, W, Ho, Wo, G, log2G, tiles_w, tiles;
+  float eps;
+  uint32_t spin_limit;
   float *out;
-  float4 *part;       // (N, G, tiles) of (count, mean, M2, 0)
-  float *mean;        // (N, G)
-  float *rstd;        // (N, G)
+  float *mean;           // (N, G), written by tile 0 of each sample
+  float *rstd;           // (N, G)
+  ChainWsHeader *hdr;
+  uint64_t *stats;       // (N, tiles, G) packed (mean, -M2); 0 = not yet written
 };
 
 // Row-of-16 all-reduce (lanes sharing l / 16) on DPP only.
@@ -70,48 +96,96 @@ __device__ __forceinline__ float across_quads(float v, Op op) {
   return op(bitsf(q[0]), bitsf(q[1]));
 }
 
-// tanh(z) = 1 - 2 / (exp(2z) + 1): exp overflow gives 1, underflow -1; the
-// absolute error is a few 1e-7, far inside the chain's tolerance.
+// tanh(z) = 1 - 2 / (exp(2z) + 1): exp overflow gives 1, underflow -1, so the
+// result always lies in [-1, 1]; the absolute error is a few 1e-7, far inside
+// the chain's tolerance.
 __device__ __forceinline__ float tanh_fast(float z) {
   const float e = __builtin_amdgcn_exp2f(z * (2.0f * kLog2e));
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
 }
 
-__device__ __forceinline__ float hardswish(float t) {
-  return t * fminf(fmaxf(t + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
+// hardswish(t) = t * min(max(t + 3, 0), 6) / 6.  The chain only applies it to
+// tanh outputs, t in [-1, 1], where t + 3 lies in [2, 4] and the clamp never
+// binds: there it is exactly t * (t + 3) / 6.
+__device__ __forceinline__ float hardswish_of_tanh(float t) {
+  return t * (t + 3.0f) * (1.0f / 6.0f);
 }
 
-// Stage the x tile (8 channels x 4 rows x 130 cols) of sample n into LDS.
+// Stage the x tile (8 channels x 4 rows x 132 columns) of sample n into LDS:
+// every global load of the tile is issued before the first LDS write, so the
+// tile costs one memory latency.  128-bit loads when rows are 16-byte aligned;
+// columns past W (and rows past H) read as 0 and feed only masked pixels.
+constexpr int kStageIters = (kStageF4 + kThreads - 1) / kThreads;        // 5
+
 __device__ __forceinline__ void stage_x(const ChainArgs &a, int64_t n, int h0, int w0,
                                        float (*xs)[kLdsH][kLdsW]) {
   const float *xn = a.x + n * (int64_t)kCin * a.H * a.W;
-  for (int i = threadIdx.x; i < kCin * kLdsH * kLdsW; i += kThreads) {
-    const int ci = i / (kLdsH * kLdsW);
-    const int rem = i - ci * (kLdsH * kLdsW);
-    const int r = rem / kLdsW, c = rem - r * kLdsW;
-    const int hh = h0 + r, ww = w0 + c;
-    xs[ci][r][c] = (hh < a.H && ww < a.W) ? xn[((int64_t)ci * a.H + hh) * a.W + ww] : 0.0f;
+  const bool vec = ((a.W & 3) == 0) && (((uintptr_t)a.x & 15) == 0);
+  float4 buf[kStageIters];
+#pragma unroll
+  for (int it = 0; it < kStageIters; ++it) {
+    const int f = threadIdx.x + it * kThreads;
+    float4 val = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (f < kStageF4) {
+      const int row = f / kF4PerRow, c4 = f - row * kF4PerRow;
+      const int ci = row / kLdsH, r = row - ci * kLdsH;
+      const int hh = h0 + r, ww = w0 + 4 * c4;
+      if (hh < a.H) {
+        const float *src = xn + ((int64_t)ci * a.H + hh) * a.W + ww;
+        if (vec && ww + 3 < a.W) {
+          val = *reinterpret_cast<const float4 *>(src);
+        } else {
+          if (ww < a.W) val.x = src[0];
+          if (ww + 1 < a.W) val.y = src[1];
+          if (ww + 2 < a.W) val.z = src[2];
+          if (ww + 3 < a.W) val.w = src[3];
+        }
+      }
+    }
+    buf[it] = val;
+  }
+  float *flat = &xs[0][0][0];
+#pragma unroll
+  for (int it = 0; it < kStageIters; ++it) {
+    const int f = threadIdx.x + it * kThreads;
+    if (f < kStageF4) *reinterpret_cast<float4 *>(flat + 4 * f) = buf[it];
+  }
+}
+
+// Stage W (64 x 72, contiguous) into LDS rows of kWStride floats.
+__device__ __forceinline__ void stage_w(const float *__restrict__ w, float *wl) {
+  constexpr int iters = (kWF4 + kThreads - 1) / kThreads;                // 5
+  float4 buf[iters];
+#pragma unroll
+  for (int it = 0; it < iters; ++it) {
+    const int f = threadIdx.x + it * kThreads;
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (f < kWF4) {
+      if (((uintptr_t)w & 15) == 0) {
+        v = reinterpret_cast<const float4 *>(w)[f];
+      } else {
+        v.x = w[4 * f]; v.y = w[4 * f + 1]; v.z = w[4 * f + 2]; v.w = w[4 * f + 3];
+      }
+    }
+    buf[it] = v;
+  }
+#pragma unroll
+  for (int it = 0; it < iters; ++it) {
+    const int f = threadIdx.x + it * kThreads;
+    if (f < kWF4) {
+      const int o = f / (kKdim / 4), c4 = f - o * (kKdim / 4);
+      *reinterpret_cast<float4 *>(wl + o * kWStride + 4 * c4) = buf[it];
+    }
   }
 }
 
 // The wave's conv tile: acc[blk][t] for its kNB 16-pixel blocks and 4 M-tiles,
-// bias included.
-__device__ __forceinline__ void conv_tile(const ChainArgs &a, float (*xs)[kLdsH][kLdsW],
+// bias included.  Outer-product order: each K-step reads 4 A fragments (W)
+// and 4 B fragments (x patches) from LDS and issues 16 MFMAs.
+__device__ __forceinline__ void conv_tile(const ChainArgs &a, const float *xs, const float *wl,
                                           int pr, int pc0, f32x4 (&acc)[kNB][kMT]) {
   const int lane = threadIdx.x % kWave;
   const int li = lane % 16, q = lane / 16;
-  float wa[kMT][kKSteps];
-#pragma unroll
-  for (int t = 0; t < kMT; ++t)
-#pragma unroll
-    for (int s = 0; s < kKSteps; ++s) wa[t][s] = a.w[(16 * t + li) * kKdim + 4 * s + q];
-  int boff[kKSteps];
-#pragma unroll
-  for (int s = 0; s < kKSteps; ++s) {
-    const int k = 4 * s + q;
-    const int ci = k / 9, kh = (k % 9) / 3, kw = k % 3;
-    boff[s] = (ci * kLdsH + kh) * kLdsW + kw;
-  }
 #pragma unroll
   for (int t = 0; t < kMT; ++t) {
     f32x4 bias;
@@ -120,37 +194,81 @@ __device__ __forceinline__ void conv_tile(const ChainArgs &a, float (*xs)[kLdsH]
 #pragma unroll
     for (int blk = 0; blk < kNB; ++blk) acc[blk][t] = bias;
   }
-  const float *xflat = &xs[0][0][0];
+  const float *xb = xs + pr * kLdsW + pc0 + li;
+  const float *wa = wl + li * kWStride + q;
 #pragma unroll
-  for (int blk = 0; blk < kNB; ++blk) {
-    const float *xb = xflat + pr * kLdsW + pc0 + 16 * blk + li;
+  for (int s = 0; s < kKSteps; ++s) {
+    const int k = 4 * s + q;  // this lane's K index: (ci, kh, kw) = (k / 9, k % 9 / 3, k % 3)
+    const int boff = ((k / 9) * kLdsH + (k % 9) / 3) * kLdsW + k % 3;
+    float af[kMT], bf[kNB];
 #pragma unroll
-    for (int s = 0; s < kKSteps; ++s) {
-      const float bf = xb[boff[s]];
+    for (int t = 0; t < kMT; ++t) af[t] = wa[16 * t * kWStride + 4 * s];
+#pragma unroll
+    for (int blk = 0; blk < kNB; ++blk) bf[blk] = xb[boff + 16 * blk];
+#pragma unroll
+    for (int blk = 0; blk < kNB; ++blk)
 #pragma unroll
       for (int t = 0; t < kMT; ++t)
-        acc[blk][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[t][s], bf, acc[blk][t], 0, 0, 0);
-    }
+        acc[blk][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[t], bf[blk], acc[blk][t], 0, 0, 0);
   }
 }
 
-template <int PASS>
-__global__ __launch_bounds__(kThreads) void conv_chain_kernel(ChainArgs a) {
+// Tile-statistics word: low 32 bits the tile mean, high 32 bits -M2.  M2 >= 0,
+// so the high word always has its sign bit set and a written word is never 0.
+__device__ __forceinline__ uint64_t pack_stats(float mean, float m2) {
+  return (uint64_t)fbits(mean) | ((uint64_t)fbits(-m2) << 32);
+}
+
+// Values counted in group statistics for tile j: 4 channels per quad, qpg
+// quads per group, times the tile's valid pixels.  Only the last tile row and
+// the last tile column can be partial, so no division is needed when the
+// sample is one tile wide.
+__device__ __forceinline__ double tile_count(const ChainArgs &a, int j, int qpg) {
+  const int tiles_h = a.tiles / a.tiles_w;
+  int th, tw;
+  if (a.tiles_w == 1) {
+    th = j;
+    tw = 0;
+  } else {
+    th = j / a.tiles_w;
+    tw = j - th * a.tiles_w;
+  }
+  const int vr = (th == tiles_h - 1) ? a.Ho - th * kTileH : kTileH;
+  const int vc = (tw == a.tiles_w - 1) ? a.Wo - tw * kTileW : kTileW;
+  return (double)(4 * qpg) * (double)vr * (double)vc;
+}
+
+constexpr uint64_t kChainWaitTicks = 10000000ull;  // 0.1 s of the 100 MHz counter
+
+#ifndef LSE_CHAIN_WAVES_PER_EU
+#define LSE_CHAIN_WAVES_PER_EU 3
+#endif
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LSE_CHAIN_WAVES_PER_EU)))
+void conv_chain_kernel(ChainArgs a) {
   __shared__ float xs[kCin][kLdsH][kLdsW];
+  __shared__ float wl[kCout * kWStride];
   __shared__ float qred[kThreads / kWave][16];
   __shared__ float gmean[16];
-  const int64_t n = blockIdx.y;
-  const int tile = blockIdx.x;
+  __shared__ double mrg[kWave][3];
+  __shared__ float s_mu[16], s_rs[16];
+  __shared__ uint32_t s_ticket;
+  if (threadIdx.x == 0)
+    s_ticket = __hip_atomic_fetch_add(&a.hdr->ticket, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int64_t n = s_ticket / (uint32_t)a.tiles;
+  const int tile = (int)(s_ticket - (uint32_t)n * (uint32_t)a.tiles);
   const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
   const int h0 = th * kTileH, w0 = tw * kTileW;
   stage_x(a, n, h0, w0, xs);
+  stage_w(a.w, wl);
   __syncthreads();
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int li = lane % 16, q = lane / 16;
   const int pr = wave / 2, pc0 = (wave % 2) * 64;  // wave's row and first column in the tile
   f32x4 acc[kNB][kMT];
-  conv_tile(a, xs, pr, pc0, acc);
+  conv_tile(a, &xs[0][0][0], wl, pr, pc0, acc);
 
   const int h = h0 + pr;
   bool valid[kNB];
@@ -158,10 +276,9 @@ __global__ __launch_bounds__(kThreads) void conv_chain_kernel(ChainArgs a) {
   for (int blk = 0; blk < kNB; ++blk) valid[blk] = (h < a.Ho) && (w0 + pc0 + 16 * blk + li < a.Wo);
   const int qpg = 16 / a.G;  // channel quads per group
 
-  if constexpr (PASS == 1) {
-    // Tile statistics per group: count, mean, then M2 about the tile mean.
-    const int vr = min(kTileH, a.Ho - h0), vc = min(kTileW, a.Wo - w0);
-    const float cnt = (float)(4 * qpg) * (float)vr * (float)vc;
+  // 1. Tile statistics per group: mean, then M2 about the tile mean.
+  {
+    const float cnt = (float)tile_count(a, tile, qpg);
     for (int stage = 0; stage < 2; ++stage) {
       float qv[kMT];
 #pragma unroll
@@ -193,86 +310,157 @@ __global__ __launch_bounds__(kThreads) void conv_chain_kernel(ChainArgs a) {
         if (stage == 0) {
           gmean[g] = tot / cnt;
         } else {
-          a.part[(n * a.G + g) * a.tiles + tile] = make_float4(cnt, gmean[g], tot, 0.0f);
+          __hip_atomic_store(a.stats + (n * a.tiles + tile) * a.G + g, pack_stats(gmean[g], tot),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       __syncthreads();
     }
-  } else {
-    // Fold GroupNorm and the affine into one multiply-add per channel.
-    float sc[kMT][4], sh[kMT][4];
+  }
+
+  // 2. Wait for every tile of this sample, then merge its statistics (wave 0).
+  // Lane l reads words l, l + 64, ... of the sample's (tile, group) block, so
+  // all its words belong to group l % G.  Per lane, in fp64: C = sum n_j,
+  // S1 = sum n_j mean_j, S2 = sum (M2_j + n_j mean_j^2); per group
+  // mean = S1 / C and M2 = S2 - C mean^2.  Up to 16 words per lane stay in
+  // registers from the last poll; larger samples re-read them.
+  if (wave == 0) {
+    const uint64_t *ws = a.stats + n * a.tiles * a.G;
+    const int words = a.tiles * a.G;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    constexpr int kHeld = 16;
+    uint64_t held[kHeld];
+    bool ok = true;
+    for (uint32_t it = 0;; ++it) {
+      bool missing = false;
 #pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-      const int g = (4 * t + q) / qpg;
-      const float mu = a.mean[n * a.G + g], rs = a.rstd[n * a.G + g];
+      for (int i = 0; i < kHeld; ++i) {
+        const int idx = lane + kWave * i;
+        held[i] = (idx < words) ? load_pair_agent(ws + idx) : 1ull;
+        missing |= (held[i] == 0);
+      }
+      for (int idx = lane + kWave * kHeld; idx < words; idx += kWave)
+        missing |= (load_pair_agent(ws + idx) == 0);
+      if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
+      if (it >= a.spin_limit || __builtin_amdgcn_s_memrealtime() - t0 > kChainWaitTicks) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    double C = 0.0, S1 = 0.0, S2 = 0.0;
+    auto add = [&](int idx, uint64_t wd) {
+      const double c = tile_count(a, idx >> a.log2G, qpg);  // G is a power of 2
+      const double m = (double)bitsf((uint32_t)wd);
+      C += c;
+      S1 += c * m;
+      S2 += -(double)bitsf((uint32_t)(wd >> 32)) + c * m * m;
+    };
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+      const int idx = lane + kWave * i;
+      if (idx < words) add(idx, held[i]);
+    }
+    for (int idx = lane + kWave * kHeld; idx < words; idx += kWave) add(idx, load_pair_agent(ws + idx));
+    mrg[lane][0] = C;
+    mrg[lane][1] = S1;
+    mrg[lane][2] = S2;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < a.G) {
+      double Cg = 0.0, S1g = 0.0, S2g = 0.0;
+      for (int l = lane; l < kWave; l += a.G) {
+        Cg += mrg[l][0];
+        S1g += mrg[l][1];
+        S2g += mrg[l][2];
+      }
+      const double MU = S1g / Cg;
+      const double M2 = fmax(S2g - Cg * MU * MU, 0.0);
+      float fm = (float)MU, fr = (float)(1.0 / sqrt(M2 / Cg + (double)a.eps));
+      if (!ok) fm = fr = __builtin_nanf("");
+      s_mu[lane] = fm;
+      s_rs[lane] = fr;
+      if (tile == 0) {
+        a.mean[n * a.G + lane] = fm;
+        a.rstd[n * a.G + lane] = fr;
+      }
+      if (!ok && lane == 0)
+        __hip_atomic_store(&a.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+
+  // 3. Epilogue on the accumulators: GroupNorm and the affine folded into one
+  // multiply-add per channel, tanh, hardswish, residual, LSE over 64 channels.
+  float sc[kMT][4], sh[kMT][4];
+#pragma unroll
+  for (int t = 0; t < kMT; ++t) {
+    const int g = (4 * t + q) / qpg;
+    const float mu = s_mu[g], rs = s_rs[g];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 16 * t + 4 * q + r;
+      const float ga = a.gamma ? a.gamma[c] : 1.0f;
+      const float be = a.beta ? a.beta[c] : 0.0f;
+      sc[t][r] = rs * ga;
+      sh[t][r] = be - mu * rs * ga;
+    }
+  }
+#pragma unroll
+  for (int blk = 0; blk < kNB; ++blk) {
+    float u[kMT][4];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < kMT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int c = 16 * t + 4 * q + r;
-        const float ga = a.gamma ? a.gamma[c] : 1.0f;
-        const float be = a.beta ? a.beta[c] : 0.0f;
-        sc[t][r] = rs * ga;
-        sh[t][r] = be - mu * rs * ga;
+        const float v = acc[blk][t][r];
+        const float z = v * sc[t][r] + sh[t][r];
+        u[t][r] = v + hardswish_of_tanh(tanh_fast(z));
+        m = fmaxf(m, u[t][r]);
       }
-    }
+    const float M = across_quads(m, OpMax{});
+    const float c = is_finite(M) ? M : 0.0f;
+    float s = 0.0f;
 #pragma unroll
-    for (int blk = 0; blk < kNB; ++blk) {
-      float u[kMT][4];
-      float m = -__builtin_inff();
+    for (int t = 0; t < kMT; ++t)
 #pragma unroll
-      for (int t = 0; t < kMT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = acc[blk][t][r];
-          const float z = v * sc[t][r] + sh[t][r];
-          u[t][r] = v + hardswish(tanh_fast(z));
-          m = fmaxf(m, u[t][r]);
-        }
-      const float M = across_quads(m, OpMax{});
-      const float c = is_finite(M) ? M : 0.0f;
-      float s = 0.0f;
-#pragma unroll
-      for (int t = 0; t < kMT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s += exp_base2(u[t][r] - c);
-      const float S = across_quads(s, OpSum{});
-      if (q == 0 && valid[blk]) {
-        const int wcol = w0 + pc0 + 16 * blk + li;
-        a.out[(n * a.Ho + h) * (int64_t)a.Wo + wcol] = M + logf(S);
-      }
+      for (int r = 0; r < 4; ++r) s += exp_base2(u[t][r] - c);
+    const float S = across_quads(s, OpSum{});
+    if (q == 0 && valid[blk]) {
+      const int wcol = w0 + pc0 + 16 * blk + li;
+      a.out[(n * a.Ho + h) * (int64_t)a.Wo + wcol] = M + logf(S);
     }
   }
 }
 
-// One thread per (n, g): Chan's pairwise update of (count, mean, M2) over the
-// sample's tiles, in fp64; then rstd = 1 / sqrt(M2 / count + eps).
-__global__ __launch_bounds__(256) void gn_stats_merge_kernel(const float4 *__restrict__ part,
-                                                             int64_t NG, int tiles, float eps,
-                                                             float *__restrict__ mean,
-                                                             float *__restrict__ rstd) {
+// Clear n 64-bit words (the ticket / error header and the statistics words).
+__global__ __launch_bounds__(256) void chain_clear_kernel(uint64_t *__restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= NG) return;
-  double cnt = 0.0, mu = 0.0, m2 = 0.0;
-  for (int t = 0; t < tiles; ++t) {
-    const float4 p = part[i * tiles + t];
-    if (p.x == 0.0f) continue;
-    const double c2 = p.x, tot = cnt + c2, d = (double)p.y - mu;
-    mu += d * c2 / tot;
-    m2 += (double)p.z + d * d * cnt * c2 / tot;
-    cnt = tot;
-  }
-  mean[i] = (float)mu;
-  rstd[i] = (float)(1.0 / sqrt(m2 / cnt + (double)eps));
+  if (i < n) p[i] = 0;
 }
 
 }  // namespace
 
+namespace {
+struct ChainLayout {
+  int64_t tiles_w, tiles;
+  size_t head, stats_off, total;
+};
+ChainLayout chain_layout(int64_t N, int64_t H, int64_t W, int64_t K, int64_t groups) {
+  ChainLayout L;
+  const int64_t Ho = H - K + 1, Wo = W - K + 1;
+  L.tiles_w = (Wo + kTileW - 1) / kTileW;
+  L.tiles = ((Ho + kTileH - 1) / kTileH) * L.tiles_w;
+  L.head = ((size_t)(2 * N * groups) * sizeof(float) + 255) / 256 * 256;  // mean, rstd
+  L.stats_off = L.head + sizeof(ChainWsHeader);
+  L.total = L.stats_off + (size_t)(N * L.tiles * groups) * sizeof(uint64_t);
+  return L;
+}
+}  // namespace
+
 size_t conv_chain_workspace_bytes(int64_t N, int64_t /*Cin*/, int64_t H, int64_t W,
                                   int64_t /*Cout*/, int64_t K, int64_t groups) {
-  const int64_t Ho = H - K + 1, Wo = W - K + 1;
-  const int64_t tiles = ((Ho + kTileH - 1) / kTileH) * ((Wo + kTileW - 1) / kTileW);
-  const size_t head = (size_t)(2 * N * groups) * sizeof(float);
-  const size_t head_aligned = (head + 255) / 256 * 256;
-  return head_aligned + (size_t)(N * groups * tiles) * sizeof(float4);
+  return chain_layout(N, H, W, K, groups).total;
 }
 
 hipError_t launch_conv_chain(const float *x, const float *w, const float *b, const float *gamma,
@@ -280,31 +468,33 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
                              int64_t Cout, int64_t K, int64_t groups, float eps, float *out,
                              void *ws, hipStream_t stream) {
   if (N == 0) return hipSuccess;
+  (void)Cin; (void)Cout;
+  const ChainLayout L = chain_layout(N, H, W, K, groups);
   ChainArgs a;
   a.x = x; a.w = w; a.b = b; a.gamma = gamma; a.beta = beta;
-  a.N = N;
+  a.N = (int32_t)N;
   a.H = (int32_t)H; a.W = (int32_t)W;
   a.Ho = (int32_t)(H - K + 1); a.Wo = (int32_t)(W - K + 1);
   a.G = (int32_t)groups;
-  a.tiles_w = (a.Wo + kTileW - 1) / kTileW;
-  a.tiles = ((a.Ho + kTileH - 1) / kTileH) * a.tiles_w;
+  a.log2G = 0;
+  while ((1 << a.log2G) < a.G) ++a.log2G;
+  a.tiles_w = (int32_t)L.tiles_w;
+  a.tiles = (int32_t)L.tiles;
+  a.eps = eps;
+  a.spin_limit = chain_spin_limit();
   a.out = out;
-  const size_t head = (size_t)(2 * N * groups) * sizeof(float);
-  const size_t head_aligned = (head + 255) / 256 * 256;
-  a.mean = reinterpret_cast<float *>(ws);
+  char *base = reinterpret_cast<char *>(ws);
+  a.mean = reinterpret_cast<float *>(base);
   a.rstd = a.mean + N * groups;
-  a.part = reinterpret_cast<float4 *>(reinterpret_cast<char *>(ws) + head_aligned);
-  (void)Cin; (void)Cout;
-  const dim3 grid((uint32_t)a.tiles, (uint32_t)N);
-  hipLaunchKernelGGL(conv_chain_kernel<1>, grid, dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
+  a.hdr = reinterpret_cast<ChainWsHeader *>(base + L.head);
+  a.stats = reinterpret_cast<uint64_t *>(base + L.stats_off);
+  const int64_t words = (int64_t)((L.total - L.head) / sizeof(uint64_t));
+  hipLaunchKernelGGL(chain_clear_kernel, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0,
+                     stream, reinterpret_cast<uint64_t *>(base + L.head), words);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t NG = N * groups;
-  hipLaunchKernelGGL(gn_stats_merge_kernel, dim3((uint32_t)((NG + 255) / 256)), dim3(256), 0,
-                     stream, a.part, NG, a.tiles, eps, a.mean, a.rstd);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(conv_chain_kernel<2>, grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(conv_chain_kernel, dim3((uint32_t)(N * L.tiles)), dim3(kThreads), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

@@ -50,6 +50,7 @@ hipError_t launch_lse_rows_merge(const void *partials, int64_t rows,
                                  int64_t nchunks, float *row_lse,
                                  hipStream_t stream);
 void set_spin_limit(uint32_t polls);
+uint32_t chain_spin_limit();
 
 // ---------------------------------------------------------------- case C
 size_t conv_chain_workspace_bytes(int64_t N, int64_t Cin, int64_t H, int64_t W,

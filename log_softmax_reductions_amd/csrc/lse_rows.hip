@@ -402,6 +402,7 @@ hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *
 }  // namespace
 
 void set_spin_limit(uint32_t polls) { h_spin_limit = polls; }
+uint32_t chain_spin_limit() { return h_spin_limit; }
 
 RowsPlan rows_plan(int64_t cols) {
   RowsPlan p;

@@ -113,4 +113,5 @@ def test_chain_validation(lib):
     assert lib.fused_conv_gn_act_lse(*args(ws=None)) == LSE_ERR_WORKSPACE
     assert lib.fused_conv_gn_act_lse(*args(wsb=16)) == LSE_ERR_WORKSPACE
     need = lib.fused_conv_gn_act_lse_workspace_bytes(128, 8, 128, 128, 64, 3, 16)
-    assert need == 2 * 128 * 16 * 4 + 128 * 16 * 63 * 16   # mean, rstd, then tile partials
+    # mean and rstd (N x G floats each), a 256-byte header, one 8-byte word per (n, tile, g)
+    assert need == 2 * 128 * 16 * 4 + 256 + 128 * 63 * 16 * 8
