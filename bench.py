@@ -155,8 +155,8 @@ def bench_secondary(steps=10, warmup=3):
                          "ms": round(avg, 4), "conv_TFLOP/s": round(flop / avg / 1e9, 2),
                          "mfma_frac_of_fp32_peak": round(flop / avg / 1e9 / FP32_MFMA_PEAK_TFLOPS,
                                                          4),
-                         "note": "GroupNorm needs whole-sample statistics, so the conv runs "
-                                 "twice (stats pass, then epilogue pass); TFLOP/s counts it once"}
+                         "note": "one fused kernel: the conv runs once on fp32 MFMA; each "
+                                 "sample's GroupNorm statistics are merged across workgroups"}
     del x, w, b, g, be, o, ws
     # small cases: hot latency per call
     x = inputs.make("rows_small", "cuda")
