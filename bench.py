@@ -158,18 +158,45 @@ def bench_secondary(steps=10, warmup=3):
                          "note": "one fused kernel: the conv runs once on fp32 MFMA; each "
                                  "sample's GroupNorm statistics are merged across workgroups"}
     del x, w, b, g, be, o, ws
-    # small cases: hot latency per call
+    # small cases: hot latency per call, eagerly from Python (host launch
+    # included) and as back-to-back calls replayed from a HIP graph
     x = inputs.make("rows_small", "cuda")
     y = torch.empty_like(x)
     wall, ev = timed_launches(lambda: L.log_softmax_rows(x, y), 50, 10)
     out["rows_small"] = {"workload": "log_softmax dim=1 (128,4096) with -inf/x50 entries",
-                         "us": round(1e3 * sum(ev) / len(ev), 2)}
+                         "us": round(1e3 * sum(ev) / len(ev), 2),
+                         "us_graph": graph_us_per_call(lambda: L.log_softmax_rows(x, y))}
     x = inputs.make("axis0_small", "cuda")
     o = torch.empty((10, 32), device="cuda")
     wall, ev = timed_launches(lambda: L.lse_reduce_axis0(x, o), 50, 10)
     out["axis0_small"] = {"workload": "logsumexp dim=0 (4,10,32)",
-                          "us": round(1e3 * sum(ev) / len(ev), 2)}
+                          "us": round(1e3 * sum(ev) / len(ev), 2),
+                          "us_graph": graph_us_per_call(lambda: L.lse_reduce_axis0(x, o))}
     return out
+
+
+def graph_us_per_call(fn, calls=100, replays=10):
+    """Per-call GPU time of `calls` back-to-back calls captured in one HIP graph."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return round(1e3 * a.elapsed_time(b) / (calls * replays), 2)
 
 
 def run_only(which, steps, warmup):

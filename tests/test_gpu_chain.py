@@ -79,3 +79,22 @@ def test_chain_full_workload_sampled(orc):
     out2 = L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
+
+
+def test_chain_nan_input_poisons_only_its_sample(orc):
+    """A NaN in sample 1's input makes that sample's GroupNorm statistics NaN, so
+    every output of sample 1 is NaN (as in the oracle) and the others are
+    untouched."""
+    x, w, b, g, be = _chain_inputs(3, 12, 12, seed=21)
+    x[1, 3, 5, 7] = float("nan")
+    ws = torch.empty(L.fused_conv_gn_act_lse_workspace_bytes(3, 8, 12, 12, 64, 3, 16),
+                     dtype=torch.uint8, device=DEV)
+    out = L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, ws=ws)
+    torch.cuda.synchronize()
+    oc = out.cpu().numpy()
+    cpu = lambda t: t.cpu().numpy()
+    ref, _, _ = orc.fused_chain(cpu(x), cpu(w), cpu(b), cpu(g), cpu(be), 16, 1e-5)
+    assert np.isnan(ref[1]).all() and np.isfinite(ref[[0, 2]]).all()
+    compare(oc, ref, rtol=RTOL_CHAIN, what="nan sample")
+    err_word = ws[256 * ((2 * 3 * 16 * 4 + 255) // 256) + 4:][:4].view(torch.int32).item()
+    assert err_word == 0          # the wait itself completed normally

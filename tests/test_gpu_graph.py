@@ -1,0 +1,84 @@
+"""Every entry point captured in a HIP graph (via torch.cuda.graph) must give,
+on every replay, bit-for-bit the result of the same call made eagerly.  The
+library enqueues only kernels (workspace clears included), so capture needs no
+special mode.  Replays are interleaved with unrelated eager work and host
+synchronisations, as a caller's loop would be."""
+import pytest
+import torch
+
+import log_softmax_reductions_amd as L
+from log_softmax_reductions_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _eager_noise():
+    a = torch.randn(1 << 20, device=DEV)
+    (a * 2).sum().item()
+
+
+def _check_graph(run, outs, replays=4):
+    """run() enqueues the library calls writing into `outs`."""
+    run()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for o in outs:
+        o.fill_(float("nan"))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):        # warm up on a side stream before capture
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(replays):
+        for o in outs:
+            o.fill_(float("nan"))
+        _eager_noise()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {i} differs from the eager result"
+
+
+def test_graph_axis0():
+    x = inputs.normal((32, 64, 1024), seed=1, sigma=2.0, device=DEV)
+    out = torch.empty((64, 1024), device=DEV)
+    _check_graph(lambda: L.lse_reduce_axis0(x, out), [out])
+
+
+def test_graph_rows_split_and_short():
+    x1 = inputs.normal((16, 393216), seed=2, device=DEV)
+    y1 = torch.empty_like(x1)
+    ws = torch.empty(L.log_softmax_rows_workspace_bytes(16, 393216), dtype=torch.uint8,
+                     device=DEV)
+    x2 = inputs.make("rows_small", DEV)
+    y2 = torch.empty_like(x2)
+
+    def run():
+        L.log_softmax_rows(x1, y1, ws)
+        L.log_softmax_rows(x2, y2)
+    _check_graph(run, [y1, y2])
+
+
+def test_graph_partial_merge():
+    x = inputs.normal((8, 50000), seed=3, device=DEV)
+    p = torch.empty((8, L.lse_rows_num_chunks(50000, 4096), 2), device=DEV)
+    lse = torch.empty(8, device=DEV)
+
+    def run():
+        L.lse_rows_partial(x, 4096, p)
+        L.lse_rows_merge(p, lse)
+    _check_graph(run, [p, lse])
+
+
+def test_graph_conv_chain():
+    x, w, b, g, be = inputs.conv_chain_inputs(N=8, H=40, W=40, seed=5, device=DEV)
+    out = torch.empty((8, 1, 38, 38), device=DEV)
+    ws = torch.empty(L.fused_conv_gn_act_lse_workspace_bytes(8, 8, 40, 40, 64, 3, 16),
+                     dtype=torch.uint8, device=DEV)
+    _check_graph(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, out, ws), [out])
