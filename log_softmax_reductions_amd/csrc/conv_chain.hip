@@ -9,20 +9,21 @@
 // epilogue over the materialised conv output.  Here the conv output is never
 // written to memory and the conv runs once:
 //
-//   each workgroup takes a 2 x 128 pixel tile of one sample (tiles handed out
-//   by an atomic ticket, in sample order), stages the x tile in LDS, runs the
-//   conv on MFMA into registers, and publishes the tile's per-group
-//   (mean, M2); it then waits until every tile of its sample has published,
-//   merges the sample's statistics with Chan's parallel update in fp64, and
-//   runs normalise, tanh, hardswish, residual and the 64-channel logsumexp
-//   on the accumulators it still holds, writing one float per pixel.
+//   each workgroup takes a pair of 2 x 128 pixel tiles of one sample (pairs
+//   handed out by an atomic ticket, in sample order), stages x and W in
+//   LDS, runs the conv of each tile on MFMA into registers (the second
+//   tile's x loads in flight during the first tile's MFMAs) and publishes
+//   each tile's per-group (mean, M2); it then waits until every tile of its
+//   sample has published, merges the sample's statistics in fp64, and runs
+//   normalise, tanh, hardswish, residual and the 64-channel logsumexp on the
+//   accumulators it still holds, writing one float per pixel.
 //
 // The wait is deadlock-free because tickets are claimed only by running
 // workgroups, in order, and every workgroup publishes before it waits: the
 // tiles of any sample that has a waiting workgroup are all held by running
 // workgroups once its last ticket is claimed, which needs only as many
-// co-resident workgroups as a sample has tiles (63 for 126 x 126; hundreds
-// fit).  The wait is still bounded (poll count and 0.1 s); a workgroup that
+// co-resident workgroups as a sample has tile pairs (32 for 126 x 126;
+// hundreds fit).  The wait is still bounded (poll count and 0.1 s); a workgroup that
 // gives up flags the workspace and writes NaN.
 //
 // GEMM shape per sample: D[c][p] = sum_k W[c][k] * patch[k][p] with c the 64
@@ -111,17 +112,22 @@ __device__ __forceinline__ float hardswish_of_tanh(float t) {
   return t * (t + 3.0f) * (1.0f / 6.0f);
 }
 
-// Stage the x tile (8 channels x 4 rows x 132 columns) of sample n into LDS:
-// every global load of the tile is issued before the first LDS write, so the
-// tile costs one memory latency.  128-bit loads when rows are 16-byte aligned;
-// columns past W (and rows past H) read as 0 and feed only masked pixels.
+// The x tile of sample n at (h0, w0): 8 channels x 4 rows x 132 columns.  It
+// is loaded into registers with every global load of the tile in flight at
+// once (128-bit loads when rows are 16-byte aligned), then stored to LDS, so
+// a tile costs one memory latency and the next tile's loads can be in flight
+// while the current one is on the MFMAs.  Columns past W and rows past H read
+// as 0 and feed only masked pixels.
 constexpr int kStageIters = (kStageF4 + kThreads - 1) / kThreads;        // 5
 
-__device__ __forceinline__ void stage_x(const ChainArgs &a, int64_t n, int h0, int w0,
-                                       float (*xs)[kLdsH][kLdsW]) {
+struct XRegs {
+  float4 v[kStageIters];
+};
+
+__device__ __forceinline__ void load_x(const ChainArgs &a, int64_t n, int h0, int w0,
+                                       XRegs &xr) {
   const float *xn = a.x + n * (int64_t)kCin * a.H * a.W;
   const bool vec = ((a.W & 3) == 0) && (((uintptr_t)a.x & 15) == 0);
-  float4 buf[kStageIters];
 #pragma unroll
   for (int it = 0; it < kStageIters; ++it) {
     const int f = threadIdx.x + it * kThreads;
@@ -142,39 +148,50 @@ __device__ __forceinline__ void stage_x(const ChainArgs &a, int64_t n, int h0, i
         }
       }
     }
-    buf[it] = val;
-  }
-  float *flat = &xs[0][0][0];
-#pragma unroll
-  for (int it = 0; it < kStageIters; ++it) {
-    const int f = threadIdx.x + it * kThreads;
-    if (f < kStageF4) *reinterpret_cast<float4 *>(flat + 4 * f) = buf[it];
+    xr.v[it] = val;
   }
 }
 
-// Stage W (64 x 72, contiguous) into LDS rows of kWStride floats.
-__device__ __forceinline__ void stage_w(const float *__restrict__ w, float *wl) {
-  constexpr int iters = (kWF4 + kThreads - 1) / kThreads;                // 5
-  float4 buf[iters];
+__device__ __forceinline__ void store_x(const XRegs &xr, float *xs) {
 #pragma unroll
-  for (int it = 0; it < iters; ++it) {
+  for (int it = 0; it < kStageIters; ++it) {
+    const int f = threadIdx.x + it * kThreads;
+    if (f < kStageF4) *reinterpret_cast<float4 *>(xs + 4 * f) = xr.v[it];
+  }
+}
+
+// W (64 x 72, contiguous) through registers into LDS rows of kWStride floats;
+// the loads do not depend on the tile, so they are issued first.
+constexpr int kWIters = (kWF4 + kThreads - 1) / kThreads;                // 5
+
+struct WRegs {
+  float4 v[kWIters];
+};
+
+__device__ __forceinline__ void load_w(const float *__restrict__ w, WRegs &wr) {
+  const bool vec = ((uintptr_t)w & 15) == 0;
+#pragma unroll
+  for (int it = 0; it < kWIters; ++it) {
     const int f = threadIdx.x + it * kThreads;
     float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (f < kWF4) {
-      if (((uintptr_t)w & 15) == 0) {
+      if (vec) {
         v = reinterpret_cast<const float4 *>(w)[f];
       } else {
         v.x = w[4 * f]; v.y = w[4 * f + 1]; v.z = w[4 * f + 2]; v.w = w[4 * f + 3];
       }
     }
-    buf[it] = v;
+    wr.v[it] = v;
   }
+}
+
+__device__ __forceinline__ void store_w(const WRegs &wr, float *wl) {
 #pragma unroll
-  for (int it = 0; it < iters; ++it) {
+  for (int it = 0; it < kWIters; ++it) {
     const int f = threadIdx.x + it * kThreads;
     if (f < kWF4) {
       const int o = f / (kKdim / 4), c4 = f - o * (kKdim / 4);
-      *reinterpret_cast<float4 *>(wl + o * kWStride + 4 * c4) = buf[it];
+      *reinterpret_cast<float4 *>(wl + o * kWStride + 4 * c4) = wr.v[it];
     }
   }
 }
@@ -240,91 +257,82 @@ __device__ __forceinline__ double tile_count(const ChainArgs &a, int j, int qpg)
 
 constexpr uint64_t kChainWaitTicks = 10000000ull;  // 0.1 s of the 100 MHz counter
 
-#ifndef LSE_CHAIN_WAVES_PER_EU
-#define LSE_CHAIN_WAVES_PER_EU 3
-#endif
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LSE_CHAIN_WAVES_PER_EU)))
-void conv_chain_kernel(ChainArgs a) {
-  __shared__ float xs[kCin][kLdsH][kLdsW];
-  __shared__ float wl[kCout * kWStride];
-  __shared__ float qred[kThreads / kWave][16];
-  __shared__ float gmean[16];
-  __shared__ double mrg[kWave][3];
-  __shared__ float s_mu[16], s_rs[16];
-  __shared__ uint32_t s_ticket;
-  if (threadIdx.x == 0)
-    s_ticket = __hip_atomic_fetch_add(&a.hdr->ticket, 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int64_t n = s_ticket / (uint32_t)a.tiles;
-  const int tile = (int)(s_ticket - (uint32_t)n * (uint32_t)a.tiles);
-  const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
-  const int h0 = th * kTileH, w0 = tw * kTileW;
-  stage_x(a, n, h0, w0, xs);
-  stage_w(a.w, wl);
-  __syncthreads();
+// LDS scratch of one workgroup besides the x and W tiles.
+struct ChainLds {
+  float qred[kThreads / kWave][16];
+  float gmean[16];
+  double mrg[kWave][3];
+  float mu[16], rs[16];
+};
 
+__device__ __forceinline__ void tile_valid(const ChainArgs &a, int tile, bool (&valid)[kNB]) {
+  const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
+  const int wave = threadIdx.x / kWave, li = threadIdx.x % 16;
+  const int h = th * kTileH + wave / 2, w = tw * kTileW + (wave % 2) * 64 + li;
+#pragma unroll
+  for (int blk = 0; blk < kNB; ++blk) valid[blk] = (h < a.Ho) && (w + 16 * blk < a.Wo);
+}
+
+// Per-group (mean, M2 about the tile mean) of one tile, published as one word
+// per group.  Called by the whole workgroup; ends with a barrier.
+__device__ __forceinline__ void publish_tile_stats(const ChainArgs &a, int64_t n, int tile,
+                                                   const f32x4 (&acc)[kNB][kMT],
+                                                   const bool (&valid)[kNB], ChainLds &L) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int li = lane % 16, q = lane / 16;
-  const int pr = wave / 2, pc0 = (wave % 2) * 64;  // wave's row and first column in the tile
-  f32x4 acc[kNB][kMT];
-  conv_tile(a, &xs[0][0][0], wl, pr, pc0, acc);
-
-  const int h = h0 + pr;
-  bool valid[kNB];
-#pragma unroll
-  for (int blk = 0; blk < kNB; ++blk) valid[blk] = (h < a.Ho) && (w0 + pc0 + 16 * blk + li < a.Wo);
   const int qpg = 16 / a.G;  // channel quads per group
-
-  // 1. Tile statistics per group: mean, then M2 about the tile mean.
-  {
-    const float cnt = (float)tile_count(a, tile, qpg);
-    for (int stage = 0; stage < 2; ++stage) {
-      float qv[kMT];
+  const float cnt = (float)tile_count(a, tile, qpg);
+  for (int stage = 0; stage < 2; ++stage) {
+    float qv[kMT];
 #pragma unroll
-      for (int t = 0; t < kMT; ++t) {
-        const float mu = stage ? gmean[(4 * t + q) / qpg] : 0.0f;
-        float sacc = 0.0f;
+    for (int t = 0; t < kMT; ++t) {
+      const float mu = stage ? L.gmean[(4 * t + q) / qpg] : 0.0f;
+      float sacc = 0.0f;
 #pragma unroll
-        for (int blk = 0; blk < kNB; ++blk) {
-          if (valid[blk]) {
+      for (int blk = 0; blk < kNB; ++blk) {
+        if (valid[blk]) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float d = acc[blk][t][r] - mu;
-              sacc += stage ? d * d : d;
-            }
+          for (int r = 0; r < 4; ++r) {
+            const float d = acc[blk][t][r] - mu;
+            sacc += stage ? d * d : d;
           }
         }
-        qv[t] = row16_sum(sacc);
       }
-      if (li == 0) {
-#pragma unroll
-        for (int t = 0; t < kMT; ++t) qred[wave][4 * t + q] = qv[t];
-      }
-      __syncthreads();
-      if (threadIdx.x < a.G) {
-        const int g = threadIdx.x;
-        float tot = 0.0f;
-        for (int w = 0; w < kThreads / kWave; ++w)
-          for (int Q = g * qpg; Q < (g + 1) * qpg; ++Q) tot += qred[w][Q];
-        if (stage == 0) {
-          gmean[g] = tot / cnt;
-        } else {
-          __hip_atomic_store(a.stats + (n * a.tiles + tile) * a.G + g, pack_stats(gmean[g], tot),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-      __syncthreads();
+      qv[t] = row16_sum(sacc);
     }
+    if (li == 0) {
+#pragma unroll
+      for (int t = 0; t < kMT; ++t) L.qred[wave][4 * t + q] = qv[t];
+    }
+    __syncthreads();
+    if (threadIdx.x < a.G) {
+      const int g = threadIdx.x;
+      float tot = 0.0f;
+      for (int w = 0; w < kThreads / kWave; ++w)
+        for (int Q = g * qpg; Q < (g + 1) * qpg; ++Q) tot += L.qred[w][Q];
+      if (stage == 0) {
+        L.gmean[g] = tot / cnt;
+      } else {
+        __hip_atomic_store(a.stats + (n * a.tiles + tile) * a.G + g, pack_stats(L.gmean[g], tot),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
   }
+}
 
-  // 2. Wait for every tile of this sample, then merge its statistics (wave 0).
-  // Lane l reads words l, l + 64, ... of the sample's (tile, group) block, so
-  // all its words belong to group l % G.  Per lane, in fp64: C = sum n_j,
-  // S1 = sum n_j mean_j, S2 = sum (M2_j + n_j mean_j^2); per group
-  // mean = S1 / C and M2 = S2 - C mean^2.  Up to 16 words per lane stay in
-  // registers from the last poll; larger samples re-read them.
+// Wait until every tile of sample n has published, then merge the sample's
+// statistics into L.mu / L.rs (wave 0; the whole workgroup calls this and it
+// ends with a barrier).  Lane l reads words l, l + 64, ... of the sample's
+// (tile, group) block, so all its words belong to group l % G.  Per lane, in
+// fp64: C = sum n_j, S1 = sum n_j mean_j, S2 = sum (M2_j + n_j mean_j^2); per
+// group mean = S1 / C and M2 = S2 - C mean^2.  Up to 16 words per lane stay
+// in registers from the last poll; larger samples re-read them.
+__device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bool write_global,
+                                               ChainLds &L) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if (wave == 0) {
+    const int qpg = 16 / a.G;
     const uint64_t *ws = a.stats + n * a.tiles * a.G;
     const int words = a.tiles * a.G;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -362,24 +370,24 @@ void conv_chain_kernel(ChainArgs a) {
       if (idx < words) add(idx, held[i]);
     }
     for (int idx = lane + kWave * kHeld; idx < words; idx += kWave) add(idx, load_pair_agent(ws + idx));
-    mrg[lane][0] = C;
-    mrg[lane][1] = S1;
-    mrg[lane][2] = S2;
+    L.mrg[lane][0] = C;
+    L.mrg[lane][1] = S1;
+    L.mrg[lane][2] = S2;
     __builtin_amdgcn_wave_barrier();
     if (lane < a.G) {
       double Cg = 0.0, S1g = 0.0, S2g = 0.0;
       for (int l = lane; l < kWave; l += a.G) {
-        Cg += mrg[l][0];
-        S1g += mrg[l][1];
-        S2g += mrg[l][2];
+        Cg += L.mrg[l][0];
+        S1g += L.mrg[l][1];
+        S2g += L.mrg[l][2];
       }
       const double MU = S1g / Cg;
       const double M2 = fmax(S2g - Cg * MU * MU, 0.0);
       float fm = (float)MU, fr = (float)(1.0 / sqrt(M2 / Cg + (double)a.eps));
       if (!ok) fm = fr = __builtin_nanf("");
-      s_mu[lane] = fm;
-      s_rs[lane] = fr;
-      if (tile == 0) {
+      L.mu[lane] = fm;
+      L.rs[lane] = fr;
+      if (write_global) {
         a.mean[n * a.G + lane] = fm;
         a.rstd[n * a.G + lane] = fr;
       }
@@ -388,14 +396,24 @@ void conv_chain_kernel(ChainArgs a) {
     }
   }
   __syncthreads();
+}
 
-  // 3. Epilogue on the accumulators: GroupNorm and the affine folded into one
-  // multiply-add per channel, tanh, hardswish, residual, LSE over 64 channels.
+// Epilogue of one tile on its accumulators: GroupNorm and the affine folded
+// into one multiply-add per channel, tanh, hardswish, residual, and the LSE
+// over the 64 channels of each pixel; one float written per valid pixel.
+__device__ __forceinline__ void tile_epilogue(const ChainArgs &a, int64_t n, int tile,
+                                              const f32x4 (&acc)[kNB][kMT],
+                                              const bool (&valid)[kNB], const ChainLds &L) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int li = lane % 16, q = lane / 16;
+  const int qpg = 16 / a.G;
+  const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
+  const int h = th * kTileH + wave / 2, w0 = tw * kTileW + (wave % 2) * 64;
   float sc[kMT][4], sh[kMT][4];
 #pragma unroll
   for (int t = 0; t < kMT; ++t) {
     const int g = (4 * t + q) / qpg;
-    const float mu = s_mu[g], rs = s_rs[g];
+    const float mu = L.mu[g], rs = L.rs[g];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = 16 * t + 4 * q + r;
@@ -426,11 +444,72 @@ void conv_chain_kernel(ChainArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) s += exp_base2(u[t][r] - c);
     const float S = across_quads(s, OpSum{});
-    if (q == 0 && valid[blk]) {
-      const int wcol = w0 + pc0 + 16 * blk + li;
-      a.out[(n * a.Ho + h) * (int64_t)a.Wo + wcol] = M + logf(S);
-    }
+    if (q == 0 && valid[blk])
+      a.out[(n * a.Ho + h) * (int64_t)a.Wo + w0 + 16 * blk + li] = M + logf(S);
   }
+}
+
+#ifndef LSE_CHAIN_WAVES_PER_EU
+#define LSE_CHAIN_WAVES_PER_EU 2
+#endif
+
+// One workgroup = a pair of vertically adjacent tiles (A = 2p, B = 2p + 1) of
+// one sample, handed out by ticket in sample order.  B's x loads are in
+// flight while A is on the MFMAs; both tiles publish their statistics before
+// the workgroup waits for its sample, and W staging, the wait and the merge
+// are paid once per pair.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LSE_CHAIN_WAVES_PER_EU)))
+void conv_chain_kernel(ChainArgs a) {
+  __shared__ float xs[kCin * kLdsH * kLdsW];
+  __shared__ float wl[kCout * kWStride];
+  __shared__ ChainLds L;
+  __shared__ uint32_t s_ticket;
+  WRegs wr;
+  load_w(a.w, wr);  // in flight while the ticket is claimed
+  if (threadIdx.x == 0)
+    s_ticket = __hip_atomic_fetch_add(&a.hdr->ticket, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t pairs = (uint32_t)(a.tiles + 1) / 2;
+  const int64_t n = s_ticket / pairs;
+  const int p = (int)(s_ticket - (uint32_t)n * pairs);
+  const int tA = 2 * p, tB = 2 * p + 1;
+  const bool hasB = tB < a.tiles;  // uniform
+
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int pr = wave / 2, pc0 = (wave % 2) * 64;  // wave's row and first column in a tile
+  auto origin = [&](int tile, int &h0, int &w0) {
+    const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
+    h0 = th * kTileH;
+    w0 = tw * kTileW;
+  };
+  int hA, wA, hB, wB;
+  origin(tA, hA, wA);
+  origin(hasB ? tB : tA, hB, wB);
+
+  XRegs xa, xb;
+  load_x(a, n, hA, wA, xa);
+  if (hasB) load_x(a, n, hB, wB, xb);
+  store_w(wr, wl);
+  store_x(xa, xs);
+  __syncthreads();
+
+  f32x4 accA[kNB][kMT], accB[kNB][kMT];
+  bool vA[kNB], vB[kNB];
+  conv_tile(a, xs, wl, pr, pc0, accA);
+  tile_valid(a, tA, vA);
+  publish_tile_stats(a, n, tA, accA, vA, L);  // ends with a barrier: xs is free again
+  if (hasB) {
+    store_x(xb, xs);
+    __syncthreads();
+    conv_tile(a, xs, wl, pr, pc0, accB);
+    tile_valid(a, tB, vB);
+    publish_tile_stats(a, n, tB, accB, vB, L);
+  }
+  (void)lane;
+  wait_and_merge(a, n, tA == 0, L);
+  tile_epilogue(a, n, tA, accA, vA, L);
+  if (hasB) tile_epilogue(a, n, tB, accB, vB, L);
 }
 
 // Clear n 64-bit words (the ticket / error header and the statistics words).
@@ -493,7 +572,8 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
                      stream, reinterpret_cast<uint64_t *>(base + L.head), words);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(conv_chain_kernel, dim3((uint32_t)(N * L.tiles)), dim3(kThreads), 0, stream,
+  const int64_t pairs = (L.tiles + 1) / 2;
+  hipLaunchKernelGGL(conv_chain_kernel, dim3((uint32_t)(N * pairs)), dim3(kThreads), 0, stream,
                      a);
   return hipGetLastError();
 }
