@@ -108,10 +108,16 @@ def cpu_baseline(x_dev, target_s=10.0):
         block = int(min(64, max(16, (target_s - secs) / per_row)))
         block = min(block, ROWS - rows_done)
     nbytes = rows_done * COLS * 8
+    # the same oracle on one core, over 16 rows
+    xs = x_dev[:16].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.log_softmax_rows(xs, want_y=True, nthreads=1)
+    one = 16 * COLS * 8 / (time.perf_counter() - t0) / 1e9
     return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{rows_done} of {ROWS} rows (x {COLS} cols) of the same workload, "
-                      f"fp64 log_softmax incl. the y write, {secs:.1f} s wall"}
+                      f"fp64 log_softmax incl. the y write, {secs:.1f} s wall",
+            "value_1core": round(one, 4)}
 
 
 def bench_rows_large(steps, warmup):
@@ -123,7 +129,15 @@ def bench_rows_large(steps, warmup):
     ws = torch.empty(L.log_softmax_rows_workspace_bytes(ROWS, COLS), dtype=torch.uint8,
                      device="cuda")
     wall, ev = timed_launches(lambda: L.log_softmax_rows(x, y, ws), steps, warmup)
-    return x, wall, ev
+    return x, y, wall, ev
+
+
+def copy_ceiling(x, y, steps=5, warmup=2):
+    """GB/s of a plain device-to-device copy of the same bytes (read x, write
+    y): a second, achievable denominator beside the 8 TB/s peak."""
+    wall, ev = timed_launches(lambda: y.copy_(x), steps, warmup)
+    avg = sum(ev) / len(ev)
+    return round(2 * x.numel() * 4 / (avg * 1e-3) / 1e9, 1)
 
 
 def bench_secondary(steps=10, warmup=3):
@@ -205,7 +219,7 @@ def run_only(which, steps, warmup):
     import log_softmax_reductions_amd as L
     from log_softmax_reductions_amd import inputs
     if which == "rows_large":
-        _, wall, ev = bench_rows_large(steps, warmup)
+        _, _, wall, ev = bench_rows_large(steps, warmup)
     elif which == "axis0_large":
         x = inputs.make("axis0_large", "cuda")
         o = torch.empty(x.shape[1:], device="cuda")
@@ -249,7 +263,7 @@ def main():
         run_only(args.only, args.steps, args.warmup)
         return
 
-    x, wall_ms, ev = bench_rows_large(args.steps, args.warmup)
+    x, y, wall_ms, ev = bench_rows_large(args.steps, args.warmup)
     alg_bytes = 2 * 4 * ROWS * COLS
     value = alg_bytes / (wall_ms * 1e-3) / 1e9
     ev_avg = sum(ev) / len(ev)
@@ -276,6 +290,9 @@ def main():
                      "kernel": "log_softmax_rows_kernel<32, true, true>",
                      "event_ms_avg": round(ev_avg, 4), "event_ms_min": round(min(ev), 4)},
     }
+    copy_gbs = copy_ceiling(x, y)
+    line["roofline"]["copy_ceiling_GBs"] = copy_gbs
+    line["roofline"]["frac_of_copy"] = round(achieved / copy_gbs, 4)
     if not args.no_secondary:
         line["secondary"] = bench_secondary()
     if not args.no_cpu_baseline:

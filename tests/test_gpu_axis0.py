@@ -70,3 +70,19 @@ def test_axis0_large_workload(orc):
     print("axis0_large", s)
     again = _run(x)
     assert np.array_equal(got, again, equal_nan=True), "run-to-run results differ"
+
+
+def test_axis0_beyond_2g_elements(orc):
+    """(3, 800_000_000): 2.4e9 elements (9.6 GB), past 32-bit element and byte
+    offsets.  Sampled outputs, each from its own R values, against the oracle."""
+    R, inner = 3, 800_000_000
+    x = inputs.normal((R, inner), seed=44, sigma=3.0, device=DEV)
+    out = L.lse_reduce_axis0(x)
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(7)
+    idx = torch.cat([torch.tensor([0, 1, inner // 2, inner - 2, inner - 1]),
+                     torch.randint(0, inner, (2000,), generator=gen)]).to(DEV)
+    cols = x[:, idx].cpu().numpy()              # (R, samples)
+    compare(out[idx].cpu().numpy(), orc.lse_axis0(cols), what="axis0 > 2^31 elements")
+    del x, out
+    torch.cuda.empty_cache()

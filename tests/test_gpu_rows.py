@@ -178,3 +178,19 @@ def test_rows_helping_path(orc):
     y2 = L.log_softmax_rows(x, ws=ws)
     torch.cuda.synchronize()
     compare(y2[sample].cpu().numpy(), ref, what="default path after")
+
+
+def test_rows_beyond_2g_elements(orc):
+    """(6000, 393216): 2.36e9 elements (9.4 GB in, 9.4 GB out), past 32-bit
+    element offsets; sampled rows against the oracle, every row by property."""
+    rows, cols = 6000, 393216
+    x = inputs.normal((rows, cols), seed=45, device=DEV)
+    y = L.log_softmax_rows(x)
+    torch.cuda.synchronize()
+    sample = [0, 1, 2999, 5461, 5462, 5998, 5999]
+    ref, _ = orc.log_softmax_rows(x[sample].cpu().numpy())
+    compare(y[sample].cpu().numpy(), ref, what="rows > 2^31 elements")
+    lse = torch.stack([torch.logsumexp(y[i:i + 500].double(), dim=1) for i in range(0, rows, 500)])
+    assert lse.abs().max().item() < 1e-5
+    del x, y
+    torch.cuda.empty_cache()
