@@ -11,6 +11,9 @@ from .oracle import (  # noqa: F401
     load,
     lse_axis0,
     log_softmax_rows,
+    softmax_rows,
+    lse_axis,
+    log_softmax_axis,
     lse_chunk_partials,
     lse_merge,
     hardswish,

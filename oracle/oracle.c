@@ -102,6 +102,55 @@ int oracle_log_softmax_rows(const float *x, int64_t rows, int64_t cols,
   return 0;
 }
 
+/* O2b — row-wise softmax, the non-log form:
+ *   y[r,c] = exp(x[r,c] - lse[r]) = exp(x[r,c]) / sum_c exp(x[r,c])
+ * [LSM] the standard-softmax variant it mentions (write exp(x - max), then
+ * divide by the sum). */
+int oracle_softmax_rows(const float *x, int64_t rows, int64_t cols, double *y,
+                        int nthreads) {
+  if (!x || !y || rows < 0 || cols < 1) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(clamp_threads(nthreads))
+  for (int64_t r = 0; r < rows; ++r) {
+    const float *row = x + r * cols;
+    const double L = lse_strided(row, cols, 1);
+    double *yr = y + r * cols;
+    for (int64_t c = 0; c < cols; ++c) yr[c] = exp((double)row[c] - L);
+  }
+  return 0;
+}
+
+/* O1b — logsumexp over the middle axis of a row-major (outer, R, inner) array:
+ *   out[o, j] = log(sum_r exp(x[o, r, j]))
+ * outer = 1 is O1; the chain's channel reduction of an (N, C, H, W) tensor is
+ * outer = N, R = C, inner = H * W.     [LSE0] task statement, [CHAIN] the
+ * logsumexp over dim 1 of the residual sum. */
+int oracle_lse_axis(const float *x, int64_t outer, int64_t R, int64_t inner,
+                    double *out, int nthreads) {
+  if (!x || !out || outer < 0 || R < 1 || inner < 0) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static) num_threads(clamp_threads(nthreads))
+  for (int64_t i = 0; i < outer * inner; ++i) {
+    const int64_t o = i / inner, j = i - o * inner;
+    out[i] = lse_strided(x + o * R * inner + j, R, inner);
+  }
+  return 0;
+}
+
+/* O2c — log_softmax over the middle axis of (outer, R, inner):
+ *   y[o, r, j] = x[o, r, j] - log(sum_r' exp(x[o, r', j]))      [LSM] formula */
+int oracle_log_softmax_axis(const float *x, int64_t outer, int64_t R,
+                            int64_t inner, double *y, int nthreads) {
+  if (!x || !y || outer < 0 || R < 1 || inner < 0) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static) num_threads(clamp_threads(nthreads))
+  for (int64_t i = 0; i < outer * inner; ++i) {
+    const int64_t o = i / inner, j = i - o * inner;
+    const float *base = x + o * R * inner + j;
+    const double L = lse_strided(base, R, inner);
+    for (int64_t r = 0; r < R; ++r)
+      y[(o * R + r) * inner + j] = (double)base[r * inner] - L;
+  }
+  return 0;
+}
+
 /* O3a — the (max, sum) pair of every chunk of every row.       [LSM] the
  * multi-block-per-row idea: each block reduces a portion of the row to its
  * local max and sum, which a second phase combines.

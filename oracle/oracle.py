@@ -66,8 +66,12 @@ def load():
                                            _i64, _i64, _i64, _i64, _i64, _i64,
                                            ctypes.c_double, _f64p, _f64p, _f64p,
                                            ctypes.c_int]
+        lib.oracle_softmax_rows.argtypes = [_f32p, _i64, _i64, _f64p, ctypes.c_int]
+        lib.oracle_lse_axis.argtypes = [_f32p, _i64, _i64, _i64, _f64p, ctypes.c_int]
+        lib.oracle_log_softmax_axis.argtypes = [_f32p, _i64, _i64, _i64, _f64p, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
-        for name in ("oracle_lse_axis0", "oracle_log_softmax_rows",
+        for name in ("oracle_lse_axis0", "oracle_log_softmax_rows", "oracle_softmax_rows",
+                     "oracle_lse_axis", "oracle_log_softmax_axis",
                      "oracle_lse_chunk_partials", "oracle_lse_merge",
                      "oracle_conv2d", "oracle_fused_chain"):
             getattr(lib, name).restype = ctypes.c_int
@@ -121,6 +125,38 @@ def log_softmax_rows(x, want_y=True, nthreads=None):
     _check(load().oracle_log_softmax_rows(_p32(x), rows, cols, _p64(y), _p64(lse),
                                           _threads(nthreads)), "log_softmax_rows")
     return y, lse
+
+
+def softmax_rows(x, nthreads=None):
+    """Row-wise softmax of a 2-D array (float64)."""
+    x = _f32(x)
+    rows, cols = x.shape
+    y = np.empty((rows, cols), dtype=np.float64)
+    _check(load().oracle_softmax_rows(_p32(x), rows, cols, _p64(y), _threads(nthreads)),
+           "softmax_rows")
+    return y
+
+
+def lse_axis(x, nthreads=None):
+    """logsumexp over axis 1 of an (outer, R, inner...) array -> (outer, inner...)."""
+    x = _f32(x)
+    outer, R = x.shape[0], x.shape[1]
+    inner = int(np.prod(x.shape[2:], dtype=np.int64))
+    out = np.empty(outer * inner, dtype=np.float64)
+    _check(load().oracle_lse_axis(_p32(x), outer, R, inner, _p64(out), _threads(nthreads)),
+           "lse_axis")
+    return out.reshape((outer,) + x.shape[2:])
+
+
+def log_softmax_axis(x, nthreads=None):
+    """log_softmax over axis 1 of an (outer, R, inner...) array (float64)."""
+    x = _f32(x)
+    outer, R = x.shape[0], x.shape[1]
+    inner = int(np.prod(x.shape[2:], dtype=np.int64))
+    y = np.empty(x.shape, dtype=np.float64)
+    _check(load().oracle_log_softmax_axis(_p32(x), outer, R, inner, _p64(y),
+                                          _threads(nthreads)), "log_softmax_axis")
+    return y
 
 
 def lse_chunk_partials(x, chunk, nthreads=None):

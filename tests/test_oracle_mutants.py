@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PIN_TESTS = ["tests/test_oracle_lse.py", "tests/test_oracle_partials.py",
-             "tests/test_oracle_chain.py"]
+             "tests/test_oracle_chain.py", "tests/test_oracle_axis_softmax.py"]
 
 MUTANTS = {
     "lse_drops_max": ("  return m + log(s);\n}", "  return log(s);\n}"),
@@ -43,6 +43,14 @@ MUTANTS = {
                           "const double v4 = oracle_hardswish(tanh(v1));"),
     "chain_no_tanh": ("oracle_hardswish(tanh(v1))", "oracle_hardswish(v1)"),
     "chain_lse_drops_max": ("          r = m + log(s);", "          r = log(s);"),
+    "softmax_sign_flip": ("yr[c] = exp((double)row[c] - L);", "yr[c] = exp(L - (double)row[c]);"),
+    "softmax_unnormalised": ("yr[c] = exp((double)row[c] - L);", "yr[c] = exp((double)row[c]);"),
+    "axis_outer_stride": ("lse_strided(x + o * R * inner + j, R, inner)",
+                          "lse_strided(x + o * inner + j, R, inner)"),
+    "axis_wrong_stride": ("lse_strided(x + o * R * inner + j, R, inner)",
+                          "lse_strided(x + o * R * inner + j, R, 1)"),
+    "lsm_axis_wrong_out": ("y[(o * R + r) * inner + j] = (double)base[r * inner] - L;",
+                           "y[(o * R + r) * inner + j] = (double)base[r] - L;"),
 }
 
 
