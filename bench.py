@@ -20,7 +20,8 @@ rank 0 prints ONE JSON line.
 
 Flags: --gpus N (only 1 is supported: this build runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --no-secondary,
---only {rows_large,axis0_large,conv_chain,copy} to run just that kernel
+--only {rows_large,axis0_large,conv_chain,softmax_large,axis_chain_layout,copy}
+to run just that kernel
 (for profiler runs; prints timing only).
 """
 from __future__ import annotations
@@ -172,6 +173,35 @@ def bench_secondary(steps=10, warmup=3):
                          "note": "one fused kernel: the conv runs once on fp32 MFMA; each "
                                  "sample's GroupNorm statistics are merged across workgroups"}
     del x, w, b, g, be, o, ws
+    # widened rows: softmax on the same 4096 x 393216 workload, and the
+    # middle-axis reductions on the chain's (N, C, H*W) = (128, 64, 15876) layout
+    x = inputs.make("rows_large", "cuda")
+    y = torch.empty_like(x)
+    ws = torch.empty(L.log_softmax_rows_workspace_bytes(ROWS, COLS), dtype=torch.uint8,
+                     device="cuda")
+    wall, ev = timed_launches(lambda: L.softmax_rows(x, y, ws), steps, warmup)
+    avg = sum(ev) / len(ev)
+    out["softmax_large"] = {"workload": "softmax dim=1 (4096,393216) fp32 N(0,1)",
+                            "ms": round(avg, 4), "GB/s": round(8 * x.numel() / avg / 1e6, 1),
+                            "hbm_frac": round(8 * x.numel() / avg / 1e6 / HBM_PEAK_GBS, 4)}
+    del x, y, ws
+    x = inputs.normal((128, 64, 126 * 126), seed=12, device="cuda")
+    o = torch.empty((128, 126 * 126), device="cuda")
+    wall, ev = timed_launches(lambda: L.lse_reduce_axis(x, 1, o), steps, warmup)
+    avg = sum(ev) / len(ev)
+    nb = 4 * (x.numel() + o.numel())
+    out["lse_axis_chain_layout"] = {"workload": "logsumexp dim=1 of (128,64,15876) fp32 N(0,1)",
+                                    "ms": round(avg, 4), "GB/s": round(nb / avg / 1e6, 1),
+                                    "hbm_frac": round(nb / avg / 1e6 / HBM_PEAK_GBS, 4)}
+    y = torch.empty_like(x)
+    wall, ev = timed_launches(lambda: L.log_softmax_axis(x, 1, y), steps, warmup)
+    avg = sum(ev) / len(ev)
+    nb = 8 * x.numel()
+    out["log_softmax_axis_chain_layout"] = {
+        "workload": "log_softmax dim=1 of (128,64,15876) fp32 N(0,1)",
+        "ms": round(avg, 4), "GB/s": round(nb / avg / 1e6, 1),
+        "hbm_frac": round(nb / avg / 1e6 / HBM_PEAK_GBS, 4)}
+    del x, o, y
     # small cases: hot latency per call, eagerly from Python (host launch
     # included) and as back-to-back calls replayed from a HIP graph
     x = inputs.make("rows_small", "cuda")
@@ -229,6 +259,18 @@ def run_only(which, steps, warmup):
         o = torch.empty((128, 1, 126, 126), device="cuda")
         wall, ev = timed_launches(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, o),
                                   steps, warmup)
+    elif which == "softmax_large":
+        x = inputs.make("rows_large", "cuda")
+        y = torch.empty_like(x)
+        ws = torch.empty(L.log_softmax_rows_workspace_bytes(ROWS, COLS), dtype=torch.uint8,
+                         device="cuda")
+        wall, ev = timed_launches(lambda: L.softmax_rows(x, y, ws), steps, warmup)
+    elif which == "axis_chain_layout":
+        x = inputs.normal((128, 64, 126 * 126), seed=12, device="cuda")
+        o = torch.empty((128, 126 * 126), device="cuda")
+        y = torch.empty_like(x)
+        wall, ev = timed_launches(lambda: (L.lse_reduce_axis(x, 1, o),
+                                           L.log_softmax_axis(x, 1, y)), steps, warmup)
     elif which == "copy":
         # plain device copy of 1 GiB: calibrates the HBM byte counters
         a = torch.empty(1 << 28, device="cuda")

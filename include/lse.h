@@ -80,6 +80,21 @@ int lse_abi_version(void);
 lse_status_t lse_reduce_axis0(const float *x, float *out, int64_t R,
                               int64_t inner, hipStream_t stream);
 
+/* The same reduction over the middle axis of a row-major (outer, R, inner)
+ * array; outer = 1 is lse_reduce_axis0.  An (N, C, H, W) tensor reduced over
+ * dim 1 is outer = N, R = C, inner = H * W.   [LSE0] task statement; [CHAIN]
+ * the logsumexp over dim 1.
+ *   lse_reduce_axis:  out[o * inner + j] = LSE_r x[(o * R + r) * inner + j]
+ *                     (out: outer x inner floats)
+ *   log_softmax_axis: y[(o*R + r)*inner + j] = x[...] - LSE_r' x[(o*R + r')*inner + j]
+ *                     (y: same shape as x; one read of x when R <= 32, two
+ *                     otherwise)
+ * outer, inner >= 0 (0 is a no-op), R >= 1; outputs must not overlap x. */
+lse_status_t lse_reduce_axis(const float *x, float *out, int64_t outer,
+                             int64_t R, int64_t inner, hipStream_t stream);
+lse_status_t log_softmax_axis(const float *x, float *y, int64_t outer,
+                              int64_t R, int64_t inner, hipStream_t stream);
+
 /* ---------------------------------------------------------------- case B
  * Row-wise log_softmax over the last axis.           [LSM] opening formula
  *   y[r, c] = x[r, c] - LSE_c x[r, :],   (rows, cols) row-major.
@@ -94,6 +109,11 @@ size_t log_softmax_rows_workspace_bytes(int64_t rows, int64_t cols);
 lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows,
                               int64_t cols, void *ws, size_t ws_bytes,
                               hipStream_t stream);
+/* Row-wise softmax, the non-log form: y[r, c] = exp(x[r, c] - LSE_c x[r, :]).
+ * Same layout, split and workspace (log_softmax_rows_workspace_bytes) as
+ * log_softmax_rows.                          [LSM] the standard-softmax variant */
+lse_status_t softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
 /* How many times a workgroup of a split row polls for its siblings' (max,
  * sum) pairs before it computes the missing ones itself from x (default 2^24;
  * independently it never waits longer than about 50 us).  The results are

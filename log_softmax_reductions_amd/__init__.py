@@ -8,7 +8,10 @@ the HIP kernels of liblse.so; there is no CPU path, and a missing library
 raises ImportError on first use.
 
   lse_reduce_axis0(x)           logsumexp over dim 0 of an (R, ...) tensor
+  lse_reduce_axis(x, dim)       logsumexp over any dim of a contiguous tensor
+  log_softmax_axis(x, dim)      log_softmax over any dim of a contiguous tensor
   log_softmax_rows(x)           log_softmax over the last dim of a 2-D tensor
+  softmax_rows(x)               softmax over the last dim of a 2-D tensor
   lse_rows_partial(x, chunk)    (max, sum) pair per (row, chunk)
   lse_rows_merge(partials)      row logsumexp from the pairs
   fused_conv_gn_act_lse(...)    conv3x3 -> GroupNorm -> tanh -> hardswish ->
@@ -22,7 +25,7 @@ from . import _lib
 from ._lib import LseError  # noqa: F401
 
 __all__ = [
-    "lse_reduce_axis0", "log_softmax_rows", "log_softmax_rows_workspace_bytes",
+    "lse_reduce_axis0", "lse_reduce_axis", "log_softmax_axis", "softmax_rows", "log_softmax_rows", "log_softmax_rows_workspace_bytes",
     "log_softmax_rows_plan", "lse_set_spin_limit", "lse_rows_num_chunks", "lse_rows_partial",
     "lse_rows_merge", "fused_conv_gn_act_lse", "fused_conv_gn_act_lse_workspace_bytes",
     "lse_abi_version", "LseError",
@@ -81,6 +84,65 @@ def lse_reduce_axis0(x, out=None, stream=None):
     _lib.check(lib.lse_reduce_axis0(_dev(x, "x"), _dev(out, "out"), R, inner, _stream(stream)),
                "lse_reduce_axis0")
     return out
+
+
+def _axis_view(x, dim):
+    """(outer, R, inner) of contiguous x reduced over `dim`."""
+    d = dim % x.dim()
+    outer = 1
+    for n in x.shape[:d]:
+        outer *= n
+    inner = 1
+    for n in x.shape[d + 1:]:
+        inner *= n
+    return d, outer, x.shape[d], inner
+
+
+def lse_reduce_axis(x, dim, out=None, stream=None):
+    """logsumexp over `dim` of a contiguous fp32 GPU tensor (dim removed)."""
+    import torch
+    lib = _lib.load()
+    d, outer, R, inner = _axis_view(x, dim)
+    shape = tuple(x.shape[:d]) + tuple(x.shape[d + 1:])
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    if out.numel() != outer * inner:
+        raise ValueError("out has the wrong number of elements")
+    _lib.check(lib.lse_reduce_axis(_dev(x, "x"), _dev(out, "out"), outer, R, inner,
+                                   _stream(stream)), "lse_reduce_axis")
+    return out
+
+
+def log_softmax_axis(x, dim, y=None, stream=None):
+    """log_softmax over `dim` of a contiguous fp32 GPU tensor."""
+    import torch
+    lib = _lib.load()
+    _, outer, R, inner = _axis_view(x, dim)
+    if y is None:
+        y = torch.empty_like(x)
+    if y.shape != x.shape:
+        raise ValueError("y must have x's shape")
+    _lib.check(lib.log_softmax_axis(_dev(x, "x"), _dev(y, "y"), outer, R, inner,
+                                    _stream(stream)), "log_softmax_axis")
+    return y
+
+
+def softmax_rows(x, y=None, ws=None, stream=None):
+    """y = softmax(x, dim=-1) for a 2-D fp32 GPU tensor x."""
+    import torch
+    lib = _lib.load()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows, cols)")
+    rows, cols = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    if y.shape != x.shape:
+        raise ValueError("y must have x's shape")
+    ws, ws_bytes = _workspace(log_softmax_rows_workspace_bytes(rows, cols), x.device, ws)
+    _lib.check(lib.softmax_rows(_dev(x, "x"), _dev(y, "y"), rows, cols,
+                                None if ws is None else ctypes.c_void_p(ws.data_ptr()),
+                                ws_bytes, _stream(stream)), "softmax_rows")
+    return y
 
 
 def log_softmax_rows_workspace_bytes(rows: int, cols: int) -> int:

@@ -16,7 +16,10 @@ SIGNATURES = {
     "lse_last_error": (ctypes.c_char_p, []),
     "lse_abi_version": (ctypes.c_int, []),
     "lse_reduce_axis0": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
+    "lse_reduce_axis": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp]),
+    "log_softmax_axis": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "log_softmax_rows_workspace_bytes": (_sz, [_i64, _i64]),
+    "softmax_rows": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
     "log_softmax_rows": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
     "lse_set_spin_limit": (None, [ctypes.c_uint32]),
     "log_softmax_rows_plan": (ctypes.c_int, [_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),

@@ -88,9 +88,49 @@ LSE_EXPORT lse_status_t lse_reduce_axis0(const float *x, float *out, int64_t R, 
   if (!x || !out) return fail(LSE_ERR_NULL, "lse_reduce_axis0: x and out must be non-NULL");
   if (overlaps(x, total * 4, out, inner * 4))
     return fail(LSE_ERR_OVERLAP, "lse_reduce_axis0: out overlaps x");
-  if ((inner + 255) / 256 > kMaxGrid)
+  if ((inner + 63) / 64 > kMaxGrid)
     return fail(LSE_ERR_SHAPE, "lse_reduce_axis0: inner too large for one launch");
-  return from_hip(lse::launch_lse_axis0(x, out, R, inner, stream), "lse_reduce_axis0 launch");
+  return from_hip(lse::launch_lse_axis(x, out, 1, R, inner, stream), "lse_reduce_axis0 launch");
+}
+
+// ------------------------------------------------------------ middle axis
+static lse_status_t check_axis(const char *who, const void *x, const void *out, int64_t outer,
+                               int64_t R, int64_t inner, int64_t out_per_outer,
+                               int64_t *total) {
+  if (outer < 0 || R < 1 || inner < 0)
+    return fail(LSE_ERR_SHAPE, "%s: need outer >= 0, R >= 1, inner >= 0 (got %lld, %lld, %lld)",
+                who, (long long)outer, (long long)R, (long long)inner);
+  int64_t t;
+  if (!mul_ok(outer, R, &t) || !mul_ok(t, inner, total) || *total > kMaxElems)
+    return fail(LSE_ERR_SHAPE, "%s: outer * R * inner overflows", who);
+  if (*total == 0) return LSE_OK;
+  if (!x || !out) return fail(LSE_ERR_NULL, "%s: NULL pointer", who);
+  if (overlaps(x, *total * 4, out, outer * out_per_outer * 4))
+    return fail(LSE_ERR_OVERLAP, "%s: output overlaps x", who);
+  if ((outer * inner + 63) / 64 > kMaxGrid)
+    return fail(LSE_ERR_SHAPE, "%s: too many outputs for one launch", who);
+  return LSE_OK;
+}
+
+LSE_EXPORT lse_status_t lse_reduce_axis(const float *x, float *out, int64_t outer, int64_t R,
+                                        int64_t inner, hipStream_t stream) {
+  int64_t total;
+  const lse_status_t st = check_axis("lse_reduce_axis", x, out, outer, R, inner, inner, &total);
+  if (st != LSE_OK) return st;
+  if (total == 0) return ok();
+  return from_hip(lse::launch_lse_axis(x, out, outer, R, inner, stream),
+                  "lse_reduce_axis launch");
+}
+
+LSE_EXPORT lse_status_t log_softmax_axis(const float *x, float *y, int64_t outer, int64_t R,
+                                         int64_t inner, hipStream_t stream) {
+  int64_t total;
+  const lse_status_t st =
+      check_axis("log_softmax_axis", x, y, outer, R, inner, R * inner, &total);
+  if (st != LSE_OK) return st;
+  if (total == 0) return ok();
+  return from_hip(lse::launch_log_softmax_axis(x, y, outer, R, inner, stream),
+                  "log_softmax_axis launch");
 }
 
 // ------------------------------------------------------------------ case B
@@ -117,32 +157,41 @@ LSE_EXPORT size_t log_softmax_rows_workspace_bytes(int64_t rows, int64_t cols) {
   return lse::rows_workspace_bytes(rows, cols);
 }
 
-LSE_EXPORT lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
-                                         void *ws, size_t ws_bytes, hipStream_t stream) {
+static lse_status_t rows_call(const char *who, bool softmax, const float *x, float *y,
+                              int64_t rows, int64_t cols, void *ws, size_t ws_bytes,
+                              hipStream_t stream) {
   int64_t total;
-  lse_status_t st = check_rows("log_softmax_rows", rows, cols, &total);
+  lse_status_t st = check_rows(who, rows, cols, &total);
   if (st != LSE_OK) return st;
   if (rows == 0) return ok();
-  if (!x || !y) return fail(LSE_ERR_NULL, "log_softmax_rows: x and y must be non-NULL");
+  if (!x || !y) return fail(LSE_ERR_NULL, "%s: x and y must be non-NULL", who);
   if (overlaps(x, total * 4, y, total * 4))
-    return fail(LSE_ERR_OVERLAP, "log_softmax_rows: y overlaps x (in-place is not supported)");
+    return fail(LSE_ERR_OVERLAP, "%s: y overlaps x (in-place is not supported)", who);
   const lse::RowsPlan p = lse::rows_plan(cols);
   if (p.nchunks > lse::kRowsMaxChunks)
-    return fail(LSE_ERR_SHAPE, "log_softmax_rows: cols = %lld too long", (long long)cols);
+    return fail(LSE_ERR_SHAPE, "%s: cols = %lld too long", who, (long long)cols);
   int64_t wgs;
   if (!mul_ok(rows, p.nchunks, &wgs) || wgs > kMaxGrid)
-    return fail(LSE_ERR_SHAPE, "log_softmax_rows: rows * chunks = too many workgroups");
+    return fail(LSE_ERR_SHAPE, "%s: rows * chunks = too many workgroups", who);
   if (p.nchunks > 1) {
     const size_t need = lse::rows_workspace_bytes(rows, cols);
-    if (!ws) return fail(LSE_ERR_WORKSPACE, "log_softmax_rows: needs %zu workspace bytes", need);
+    if (!ws) return fail(LSE_ERR_WORKSPACE, "%s: needs %zu workspace bytes", who, need);
     if (ws_bytes < need)
-      return fail(LSE_ERR_WORKSPACE, "log_softmax_rows: workspace %zu < required %zu", ws_bytes,
-                  need);
+      return fail(LSE_ERR_WORKSPACE, "%s: workspace %zu < required %zu", who, ws_bytes, need);
     if (overlaps(ws, (int64_t)need, x, total * 4) || overlaps(ws, (int64_t)need, y, total * 4))
-      return fail(LSE_ERR_OVERLAP, "log_softmax_rows: workspace overlaps x or y");
+      return fail(LSE_ERR_OVERLAP, "%s: workspace overlaps x or y", who);
   }
-  return from_hip(lse::launch_log_softmax_rows(x, y, rows, cols, ws, stream),
-                  "log_softmax_rows launch");
+  return from_hip(lse::launch_log_softmax_rows(x, y, rows, cols, ws, stream, softmax), who);
+}
+
+LSE_EXPORT lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
+                                         void *ws, size_t ws_bytes, hipStream_t stream) {
+  return rows_call("log_softmax_rows", false, x, y, rows, cols, ws, ws_bytes, stream);
+}
+
+LSE_EXPORT lse_status_t softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
+                                     void *ws, size_t ws_bytes, hipStream_t stream) {
+  return rows_call("softmax_rows", true, x, y, rows, cols, ws, ws_bytes, stream);
 }
 
 LSE_EXPORT int64_t lse_rows_num_chunks(int64_t cols, int64_t chunk) {

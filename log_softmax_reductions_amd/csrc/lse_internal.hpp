@@ -10,8 +10,10 @@
 namespace lse {
 
 // ---------------------------------------------------------------- case A
-hipError_t launch_lse_axis0(const float *x, float *out, int64_t R, int64_t inner,
-                            hipStream_t stream);
+hipError_t launch_lse_axis(const float *x, float *out, int64_t outer, int64_t R, int64_t inner,
+                           hipStream_t stream);
+hipError_t launch_log_softmax_axis(const float *x, float *y, int64_t outer, int64_t R,
+                                   int64_t inner, hipStream_t stream);
 
 // ---------------------------------------------------------------- case B
 // Tile geometry of the row kernels (overridable at build time for sweeps).
@@ -42,7 +44,8 @@ RowsPlan rows_plan(int64_t cols);
 size_t rows_workspace_bytes(int64_t rows, int64_t cols);
 
 hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows,
-                                   int64_t cols, void *ws, hipStream_t stream);
+                                   int64_t cols, void *ws, hipStream_t stream,
+                                   bool softmax = false);
 hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols,
                                    int64_t chunk, void *partials,
                                    hipStream_t stream);

@@ -97,9 +97,19 @@ __device__ __forceinline__ void store4(float *p, float a, float b, float c, floa
 #endif
 }
 
-template <int VPL, bool VEC>
+// The output of one value: log_softmax (x - M) - log S, or softmax
+// exp(x - M) * (1 / S); `k` is log S or 1 / S accordingly.
+template <bool SOFTMAX>
+__device__ __forceinline__ float out_value(float v, float M, float k) {
+  if constexpr (SOFTMAX)
+    return exp_base2(v - M) * k;
+  else
+    return (v - M) - k;
+}
+
+template <int VPL, bool VEC, bool SOFTMAX>
 __device__ __forceinline__ void store_chunk(float *__restrict__ p, int64_t len,
-                                            const float (&v)[VPL], float M, float lnS) {
+                                            const float (&v)[VPL], float M, float k) {
   const int t = threadIdx.x;
   if constexpr (VEC) {
     const bool full = (len == (int64_t)VPL * kRowsThreads);
@@ -107,16 +117,25 @@ __device__ __forceinline__ void store_chunk(float *__restrict__ p, int64_t len,
     for (int q = 0; q < VPL / 4; ++q) {
       const int64_t idx = ((int64_t)q * kRowsThreads + t) * 4;
       if (full || idx < len)
-        store4(p + idx, (v[4 * q] - M) - lnS, (v[4 * q + 1] - M) - lnS,
-               (v[4 * q + 2] - M) - lnS, (v[4 * q + 3] - M) - lnS);
+        store4(p + idx, out_value<SOFTMAX>(v[4 * q], M, k), out_value<SOFTMAX>(v[4 * q + 1], M, k),
+               out_value<SOFTMAX>(v[4 * q + 2], M, k), out_value<SOFTMAX>(v[4 * q + 3], M, k));
     }
   } else {
 #pragma unroll
     for (int e = 0; e < VPL; ++e) {
       const int64_t idx = (int64_t)e * kRowsThreads + t;
-      if (idx < len) p[idx] = (v[e] - M) - lnS;
+      if (idx < len) p[idx] = out_value<SOFTMAX>(v[e], M, k);
     }
   }
+}
+
+// log S for log_softmax, 1 / S for softmax.
+template <bool SOFTMAX>
+__device__ __forceinline__ float out_scale(float S) {
+  if constexpr (SOFTMAX)
+    return 1.0f / S;
+  else
+    return logf(S);
 }
 
 // The chunk's pair (exact max, sum of exp(v - max)); identical in every lane.
@@ -218,7 +237,7 @@ __device__ __forceinline__ bool wave_wait_pairs(const uint64_t *pairs, int64_t k
 // so all workgroups of a row merge identical pairs.  Progress therefore never
 // depends on the order or timing in which blocks are dispatched: no workgroup
 // waits on one that has not started.
-template <int VPL, bool VEC, bool SPLIT>
+template <int VPL, bool VEC, bool SPLIT, bool SOFTMAX>
 __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
     const float *__restrict__ x, float *__restrict__ y, int64_t rows, int64_t cols,
     int64_t nchunks, int64_t chunk, RowsWsHeader *__restrict__ hdr,
@@ -279,7 +298,7 @@ __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
       wave_merge_pairs(row_pairs, nchunks, Mw, Sw);
       if (threadIdx.x == 0) {
         s_final[0] = Mw;
-        s_final[1] = logf(Sw);
+        s_final[1] = out_scale<SOFTMAX>(Sw);
       }
     }
     __syncthreads();
@@ -287,9 +306,9 @@ __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
     lnS = s_final[1];
   } else {
     M = m;
-    lnS = logf(s);
+    lnS = out_scale<SOFTMAX>(s);
   }
-  store_chunk<VPL, VEC>(yr, len, v, M, lnS);
+  store_chunk<VPL, VEC, SOFTMAX>(yr, len, v, M, lnS);
 }
 
 // Clear n 64-bit words (the workspace header and pair slots).
@@ -371,20 +390,20 @@ int vpl_for(int64_t len) {
   return 64;
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool SOFTMAX>
 hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *y, int64_t rows,
-                           int64_t cols,
-                           int64_t nchunks, int64_t chunk, RowsWsHeader *hdr, uint64_t *pairs,
-                           uint32_t spin_limit, hipStream_t stream) {
-#define LSE_ROWS_CASE(V)                                                                     \
-  case V:                                                                                    \
-    if (vec)                                                                                 \
-      hipLaunchKernelGGL((log_softmax_rows_kernel<V, true, SPLIT>), grid, dim3(kRowsThreads), \
-                         0, stream, x, y, rows, cols, nchunks, chunk, hdr, pairs, spin_limit);\
-    else                                                                                     \
-      hipLaunchKernelGGL((log_softmax_rows_kernel<V, false, SPLIT>), grid,                   \
-                         dim3(kRowsThreads), 0, stream, x, y, rows, cols, nchunks, chunk,    \
-                         hdr, pairs, spin_limit);                                            \
+                           int64_t cols, int64_t nchunks, int64_t chunk, RowsWsHeader *hdr,
+                           uint64_t *pairs, uint32_t spin_limit, hipStream_t stream) {
+#define LSE_ROWS_CASE(V)                                                                      \
+  case V:                                                                                     \
+    if (vec)                                                                                  \
+      hipLaunchKernelGGL((log_softmax_rows_kernel<V, true, SPLIT, SOFTMAX>), grid,            \
+                         dim3(kRowsThreads), 0, stream, x, y, rows, cols, nchunks, chunk,     \
+                         hdr, pairs, spin_limit);                                             \
+    else                                                                                      \
+      hipLaunchKernelGGL((log_softmax_rows_kernel<V, false, SPLIT, SOFTMAX>), grid,           \
+                         dim3(kRowsThreads), 0, stream, x, y, rows, cols, nchunks, chunk,     \
+                         hdr, pairs, spin_limit);                                             \
     break;
   switch (vpl) {
     LSE_ROWS_CASE(4)
@@ -397,6 +416,28 @@ hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *
   }
 #undef LSE_ROWS_CASE
   return hipGetLastError();
+}
+
+template <bool SOFTMAX>
+hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols, void *ws,
+                            hipStream_t stream) {
+  const RowsPlan p = rows_plan(cols);
+  const bool vec = (cols % 4 == 0) && (p.chunk % 4 == 0) && ((uintptr_t)x % 16 == 0) &&
+                   ((uintptr_t)y % 16 == 0);
+  if (p.nchunks == 1) {
+    return launch_rows_vpl<false, SOFTMAX>(vpl_for(cols), vec, dim3((uint32_t)rows), x, y, rows,
+                                           cols, 1, cols, nullptr, nullptr, 0u, stream);
+  }
+  auto *hdr = reinterpret_cast<RowsWsHeader *>(ws);
+  auto *pairs = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws) + sizeof(RowsWsHeader));
+  const int64_t words = (int64_t)(rows_workspace_bytes(rows, cols) / sizeof(uint64_t));
+  hipLaunchKernelGGL(clear_words_kernel, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0,
+                     stream, reinterpret_cast<uint64_t *>(ws), words);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_rows_vpl<true, SOFTMAX>(vpl_for(p.chunk), vec,
+                                        dim3((uint32_t)(rows * p.nchunks)), x, y, rows, cols,
+                                        p.nchunks, p.chunk, hdr, pairs, h_spin_limit, stream);
 }
 
 }  // namespace
@@ -424,25 +465,10 @@ size_t rows_workspace_bytes(int64_t rows, int64_t cols) {
 }
 
 hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
-                                   void *ws, hipStream_t stream) {
+                                   void *ws, hipStream_t stream, bool softmax) {
   if (rows == 0) return hipSuccess;
-  const RowsPlan p = rows_plan(cols);
-  const bool vec = (cols % 4 == 0) && (p.chunk % 4 == 0) && ((uintptr_t)x % 16 == 0) &&
-                   ((uintptr_t)y % 16 == 0);
-  if (p.nchunks == 1) {
-    return launch_rows_vpl<false>(vpl_for(cols), vec, dim3((uint32_t)rows), x, y, rows, cols, 1,
-                                  cols,
-                                  nullptr, nullptr, 0u, stream);
-  }
-  auto *hdr = reinterpret_cast<RowsWsHeader *>(ws);
-  auto *pairs = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws) + sizeof(RowsWsHeader));
-  const int64_t words = (int64_t)(rows_workspace_bytes(rows, cols) / sizeof(uint64_t));
-  hipLaunchKernelGGL(clear_words_kernel, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0,
-                     stream, reinterpret_cast<uint64_t *>(ws), words);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_rows_vpl<true>(vpl_for(p.chunk), vec, dim3((uint32_t)(rows * p.nchunks)), x, y,
-                               rows, cols, p.nchunks, p.chunk, hdr, pairs, h_spin_limit, stream);
+  return softmax ? launch_rows_mode<true>(x, y, rows, cols, ws, stream)
+                 : launch_rows_mode<false>(x, y, rows, cols, ws, stream);
 }
 
 hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, int64_t chunk,

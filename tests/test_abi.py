@@ -37,7 +37,7 @@ def test_exports_match_header(lib):
     import subprocess
     from log_softmax_reductions_amd import _lib
     declared = declared_functions()
-    assert len(declared) == 13
+    assert len(declared) == 16
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -65,6 +65,19 @@ def test_axis0_validation(lib):
     assert b"overlaps" in lib.lse_last_error()
     # inner == 0 is a no-op that succeeds without touching anything
     assert lib.lse_reduce_axis0(None, None, 3, 0, None) == LSE_OK
+
+
+def test_axis_and_softmax_validation(lib):
+    assert lib.lse_reduce_axis(FAKE, FAKE2, 2, 0, 5, None) == LSE_ERR_SHAPE
+    assert lib.lse_reduce_axis(FAKE, FAKE2, -1, 3, 5, None) == LSE_ERR_SHAPE
+    assert lib.lse_reduce_axis(None, FAKE2, 2, 3, 5, None) == LSE_ERR_NULL
+    assert lib.lse_reduce_axis(FAKE, ctypes.c_void_p(0x100004), 2, 3, 5, None) == LSE_ERR_OVERLAP
+    assert lib.lse_reduce_axis(None, None, 0, 3, 5, None) == LSE_OK        # empty: no-op
+    assert lib.log_softmax_axis(FAKE, FAKE, 2, 3, 5, None) == LSE_ERR_OVERLAP
+    assert lib.log_softmax_axis(FAKE, FAKE2, 1 << 40, 1 << 20, 1 << 10, None) == LSE_ERR_SHAPE
+    assert lib.softmax_rows(None, FAKE2, 4, 8, None, 0, None) == LSE_ERR_NULL
+    assert lib.softmax_rows(FAKE, FAKE2, 16, 393216, None, 0, None) == LSE_ERR_WORKSPACE
+    assert b"softmax_rows" in lib.lse_last_error()
 
 
 def test_rows_validation(lib):

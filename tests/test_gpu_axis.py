@@ -1,0 +1,66 @@
+"""GPU parity of lse_reduce_axis and log_softmax_axis (middle axis of an
+(outer, R, inner) array) through the C ABI against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import log_softmax_reductions_amd as L
+from log_softmax_reductions_amd import inputs
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("outer,R,inner", [(1, 4, 320), (3, 5, 7), (2, 64, 36), (4, 1, 9),
+                                           (5, 33, 1), (7, 32, 1000), (2, 70, 65), (128, 64, 100),
+                                           (3, 17, 4097), (1, 100, 8)])
+def test_lse_and_log_softmax_axis(orc, outer, R, inner):
+    x = inputs.normal((outer, R, inner), seed=outer * 7919 + R * 31 + inner, sigma=3.0,
+                      device=DEV)
+    out = L.lse_reduce_axis(x, 1)
+    y = L.log_softmax_axis(x, 1)
+    torch.cuda.synchronize()
+    xc = x.cpu().numpy()
+    compare(out.cpu().numpy(), orc.lse_axis(xc), what=f"lse_axis {outer}x{R}x{inner}")
+    compare(y.cpu().numpy(), orc.log_softmax_axis(xc), what=f"lsm_axis {outer}x{R}x{inner}")
+
+
+def test_axis_dims_of_a_4d_tensor(orc):
+    """The binding's dim argument: reducing each dim of an (N, C, H, W) tensor."""
+    x = inputs.normal((3, 6, 5, 8), seed=11, device=DEV)
+    xc = x.cpu().numpy()
+    for d in range(4):
+        got = L.lse_reduce_axis(x, d).cpu().numpy()
+        outer = int(np.prod(xc.shape[:d])) if d else 1
+        ref = orc.lse_axis(xc.reshape(outer, xc.shape[d], -1)).reshape(got.shape)
+        compare(got, ref, what=f"dim {d}")
+
+
+def test_axis_misaligned_and_special(orc):
+    buf = inputs.normal((2 * 9 * 33 + 1,), seed=5, device=DEV)
+    x = buf[1:].view(2, 9, 33).clone()
+    x[0, :, 0] = -float("inf")
+    x[1, 3, 5] = float("inf")
+    x[1, 4, 6] = float("nan")
+    xm = torch.empty(x.numel() + 1, device=DEV)[1:].view_as(x)   # misaligned copy
+    xm.copy_(x)
+    for t in (x, xm):
+        compare(L.lse_reduce_axis(t, 1).cpu().numpy(), orc.lse_axis(x.cpu().numpy()),
+                what="lse special")
+        compare(L.log_softmax_axis(t, 1).cpu().numpy(), orc.log_softmax_axis(x.cpu().numpy()),
+                what="lsm special")
+
+
+def test_chain_layout_channel_lse(orc):
+    """The chain's channel reduction layout: (128, 64, 126*126), sampled outer
+    slices against the oracle, every output against torch-free properties."""
+    x = inputs.normal((128, 64, 126 * 126), seed=12, device=DEV)
+    out = L.lse_reduce_axis(x, 1)
+    y = L.log_softmax_axis(x, 1)
+    torch.cuda.synchronize()
+    for o in (0, 77, 127):
+        xs = x[o:o + 1].cpu().numpy()
+        compare(out[o:o + 1].cpu().numpy(), orc.lse_axis(xs), what=f"chain layout lse {o}")
+        compare(y[o:o + 1].cpu().numpy(), orc.log_softmax_axis(xs), what=f"chain layout lsm {o}")
+    assert (torch.logsumexp(y.double(), dim=1).abs() < 1e-5).all()

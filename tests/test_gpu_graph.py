@@ -82,3 +82,18 @@ def test_graph_conv_chain():
     ws = torch.empty(L.fused_conv_gn_act_lse_workspace_bytes(8, 8, 40, 40, 64, 3, 16),
                      dtype=torch.uint8, device=DEV)
     _check_graph(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, out, ws), [out])
+
+
+def test_graph_axis_and_softmax():
+    x = inputs.normal((16, 64, 500), seed=6, device=DEV)
+    o1 = torch.empty((16, 500), device=DEV)
+    o2 = torch.empty_like(x)
+    x3 = inputs.normal((8, 100000), seed=7, device=DEV)
+    o3 = torch.empty_like(x3)
+    ws = torch.empty(L.log_softmax_rows_workspace_bytes(8, 100000), dtype=torch.uint8, device=DEV)
+
+    def run():
+        L.lse_reduce_axis(x, 1, o1)
+        L.log_softmax_axis(x, 1, o2)
+        L.softmax_rows(x3, o3, ws)
+    _check_graph(run, [o1, o2, o3])

@@ -194,3 +194,30 @@ def test_rows_beyond_2g_elements(orc):
     assert lse.abs().max().item() < 1e-5
     del x, y
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------- softmax
+SOFTMAX_ATOL, SOFTMAX_RTOL = 1e-37, 1e-5
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 63), (7, 4096), (2, 16385), (4, 100001),
+                                       (3, 393216)])
+def test_softmax_rows(orc, rows, cols):
+    x = inputs.normal((rows, cols), seed=rows * 13 + cols, sigma=3.0, device=DEV)
+    y = L.softmax_rows(x)
+    torch.cuda.synchronize()
+    compare(y.cpu().numpy(), orc.softmax_rows(x.cpu().numpy()), atol=SOFTMAX_ATOL,
+            rtol=SOFTMAX_RTOL, what=f"softmax {rows}x{cols}")
+
+
+def test_softmax_rows_small_workload_and_special(orc):
+    x = inputs.make("rows_small", DEV)
+    compare(L.softmax_rows(x).cpu().numpy(), orc.softmax_rows(x.cpu().numpy()),
+            atol=SOFTMAX_ATOL, rtol=SOFTMAX_RTOL, what="softmax rows_small")
+    s = inputs.normal((4, 40000), seed=9, device=DEV).cpu()
+    s[0, :] = -float("inf")
+    s[1, 7] = float("inf")
+    s[2, 39000] = float("nan")
+    s[3, :30000] = -float("inf")
+    compare(L.softmax_rows(s.to(DEV)).cpu().numpy(), orc.softmax_rows(s.numpy()),
+            atol=SOFTMAX_ATOL, rtol=SOFTMAX_RTOL, what="softmax special")
