@@ -248,7 +248,9 @@ static lse_status_t check_chain(int64_t N, int64_t Cin, int64_t H, int64_t W, in
   int64_t t;
   if (!mul_ok(N, Cin, &t) || !mul_ok(t, H, &t) || !mul_ok(t, W, &t) || t > kMaxElems)
     return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: input size overflows");
-  if (N > 65535) return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: N > 65535");
+  const int64_t tiles = ((H - K + 2) / 2) * ((W - K + 128) / 128);  // 2 x 128 pixel tiles
+  if (!mul_ok(N, (tiles + 1) / 2, &t) || t > 0xffffffffll)
+    return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: N x tiles too large for one launch");
   if (K != 3 || Cin != 8 || Cout != 64 || (16 % groups) != 0)
     return fail(LSE_ERR_UNSUPPORTED,
                 "fused_conv_gn_act_lse: this build implements K=3, Cin=8, Cout=64 and groups "

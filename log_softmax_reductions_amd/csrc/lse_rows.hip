@@ -26,6 +26,8 @@
 //     that never starts, whatever the dispatch order.
 //   * The write is y = (x - M) - log(S): x - M is exact for the large entries,
 //     so the result keeps its accuracy when |M| is large.
+#include <atomic>
+
 #include "lse_device.hpp"
 #include "lse_internal.hpp"
 
@@ -42,7 +44,7 @@ constexpr int kNW = kRowsThreads / kWave;  // waves per workgroup
 #ifndef LSE_ROWS_NT_STORE
 #define LSE_ROWS_NT_STORE 1       // y is never re-read: non-temporal stores
 #endif
-uint32_t h_spin_limit = 1u << 24;
+std::atomic<uint32_t> h_spin_limit{1u << 24};
 
 // Load a chunk of `len` values starting at p into v (lane-strided so that each
 // wave's load is one contiguous span), padding with -inf.  A full chunk (the
@@ -437,13 +439,14 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
   if (e != hipSuccess) return e;
   return launch_rows_vpl<true, SOFTMAX>(vpl_for(p.chunk), vec,
                                         dim3((uint32_t)(rows * p.nchunks)), x, y, rows, cols,
-                                        p.nchunks, p.chunk, hdr, pairs, h_spin_limit, stream);
+                                        p.nchunks, p.chunk, hdr, pairs,
+                                        h_spin_limit.load(std::memory_order_relaxed), stream);
 }
 
 }  // namespace
 
-void set_spin_limit(uint32_t polls) { h_spin_limit = polls; }
-uint32_t chain_spin_limit() { return h_spin_limit; }
+void set_spin_limit(uint32_t polls) { h_spin_limit.store(polls, std::memory_order_relaxed); }
+uint32_t chain_spin_limit() { return h_spin_limit.load(std::memory_order_relaxed); }
 
 RowsPlan rows_plan(int64_t cols) {
   RowsPlan p;
