@@ -14,6 +14,11 @@
 // is the channel reduction of an (N, C, H, W) tensor (outer = N, R = C,
 // inner = H W), the logsumexp over dim 1 on POPCORNBENCH Kimi-K2.6 l2_p92.
 //
+// log_softmax over R > 32 planes, and logsumexp over long R with few outputs,
+// split the planes of one run of outputs across the waves of a workgroup
+// (axis_split_kernel below): each wave keeps at most 16 planes x 4 outputs per
+// lane in VGPRs, and the waves' (max, sum) pairs are merged in LDS.
+//
 // Running state per output: m = max so far, s = sum of exp(v - c(m)) with the
 // shift c(m) = m when m is finite and 0 when m is +-inf (all values -inf, or
 // some +inf), which makes m + log(s) the literal log(sum(exp(v))) in every
@@ -37,11 +42,29 @@ namespace {
 #ifndef LSE_AXIS0_NT_LOAD
 #define LSE_AXIS0_NT_LOAD 1   // x is read exactly once: non-temporal loads
 #endif
-#ifndef LSE_AXIS_LSM64_W
-#define LSE_AXIS_LSM64_W 4   // outputs per lane of log_softmax when 32 < R <= 64
-#endif
 #ifndef LSE_AXIS_LSM_THREADS
 #define LSE_AXIS_LSM_THREADS 128   // log_softmax writes R planes: two waves per workgroup
+#endif
+#ifndef LSE_AXIS_NT_STORE
+#define LSE_AXIS_NT_STORE 1   // log_softmax output is not re-read here: non-temporal stores
+#endif
+#ifndef LSE_AXIS_SPLIT_RBW
+#define LSE_AXIS_SPLIT_RBW 16   // planes per wave held in registers by the plane-split kernel
+#endif
+#ifndef LSE_AXIS_SPLIT_WAVES
+#define LSE_AXIS_SPLIT_WAVES 8   // waves per workgroup: G = max(1, this / P) groups
+#endif
+#ifndef LSE_AXIS_LSM_SPLIT_MINR
+#define LSE_AXIS_LSM_SPLIT_MINR 33   // log_softmax: plane split from this R up
+#endif
+#ifndef LSE_AXIS_LSE_SPLIT_MINR
+#define LSE_AXIS_LSE_SPLIT_MINR 33   // logsumexp: plane split from this R up ...
+#endif
+#ifndef LSE_AXIS_LSE_SPLIT_MAXWAVES
+#define LSE_AXIS_LSE_SPLIT_MAXWAVES 256   // ... when one wave per 256 outputs gives this few
+#endif
+#ifndef LSE_AXIS_LSE_SPLIT_TARGET
+#define LSE_AXIS_LSE_SPLIT_TARGET 2048   // waves the logsumexp split aims for
 #endif
 constexpr int kAxis0Threads = LSE_AXIS0_THREADS;
 constexpr int kLsmThreads = LSE_AXIS_LSM_THREADS;
@@ -208,6 +231,125 @@ __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
   }
 }
 
+template <int W>
+__device__ __forceinline__ void store_w_nt(float *p, const float (&r)[W]) {
+  if constexpr (W < 4) {
+    store_w<W>(p, r);
+  } else {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int h = 0; h < W / 4; ++h) {
+      v4f t = {r[4 * h], r[4 * h + 1], r[4 * h + 2], r[4 * h + 3]};
+      __builtin_nontemporal_store(t, reinterpret_cast<v4f *>(p + 4 * h));
+    }
+  }
+}
+
+// Plane-split variant of both reductions: a workgroup has G x P waves.  The P
+// waves of one group cover the same 64 x W outputs, and wave p takes the
+// contiguous slice of per = ceil(R / P) planes starting at p * per; the G
+// groups cover consecutive runs of outputs, so each plane is read as one
+// contiguous G x 64 x W span per workgroup.  Each wave folds its slice (blocks
+// of RBW planes) into per-output (m, s) pairs, the P pairs of a group meet in
+// LDS and every wave of the group merges them into the same (M, S) with the
+// rule of fold_block.  With per <= RBW a wave's planes stay in VGPRs from the
+// load to the log_softmax write (one read, one write of x's bytes), and a lane
+// holds RBW x W values instead of R x W, so more waves fit on a SIMD to keep
+// loads in flight.  Larger R reads x a second time for the write.
+template <int RBW, int W, int P, int G, bool LSM>
+__global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
+    const float *__restrict__ x, float *__restrict__ out, int64_t outer, int64_t R,
+    int64_t inner) {
+  __shared__ float lds_m[G][P][W][kWave];
+  __shared__ float lds_s[G][P][W][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wv = wid % P, grp = wid / P;
+  const int64_t nq = inner / W;  // W > 1: inner % W == 0 by dispatch
+  const int64_t item = ((int64_t)blockIdx.x * G + grp) * kWave + lane;
+  const bool valid = item < outer * nq;
+  int64_t o = 0, q = 0;
+  if (valid) {
+    o = (outer == 1) ? 0 : item / nq;
+    q = item - o * nq;
+  }
+  const int64_t per = (R + P - 1) / P;
+  const int64_t r0 = (int64_t)wv * per;
+  int64_t nr = R - r0;  // planes of this wave's slice (0 for the last waves when P > R)
+  nr = nr < 0 ? 0 : (nr > per ? per : nr);
+  const int64_t off = o * R * inner + q * W;
+  const float *xs = x + off + r0 * inner;
+
+  float m[W], s[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    m[w] = -__builtin_inff();
+    s[w] = 0.0f;
+  }
+  float v[W][RBW];
+  const bool resident = per <= RBW;  // uniform
+  for (int64_t b = 0; b < nr; b += RBW) {
+    const int64_t nb = valid ? ((nr - b < RBW) ? (nr - b) : RBW) : 0;
+    load_block<RBW, W>(xs + b * inner, inner, nb, v);
+#pragma unroll
+    for (int w = 0; w < W; ++w) fold_block<RBW>(v[w], m[w], s[w]);
+  }
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    lds_m[grp][wv][w][lane] = m[w];
+    lds_s[grp][wv][w][lane] = s[w];
+  }
+  __syncthreads();
+  // Merge the P pairs in the same order in every wave: identical (M, S).
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    float mm = lds_m[grp][0][w][lane];
+#pragma unroll
+    for (int p = 1; p < P; ++p) mm = fmaxf(mm, lds_m[grp][p][w][lane]);
+    const float c = safe_shift(mm);
+    float acc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const float sp = lds_s[grp][p][w][lane];
+      // A pair that counted nothing is skipped: its weight may be inf.
+      if (sp != 0.0f) acc += sp * exp_base2(safe_shift(lds_m[grp][p][w][lane]) - c);
+    }
+    m[w] = mm;
+    s[w] = acc;
+  }
+  if (!valid) return;
+  if constexpr (!LSM) {
+    if (wv == 0) {
+      float r[W];
+#pragma unroll
+      for (int w = 0; w < W; ++w) r[w] = m[w] + logf(s[w]);
+      store_w<W>(out + o * inner + q * W, r);
+    }
+  } else {
+    float lns[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) lns[w] = logf(s[w]);
+    float *ys = out + off + r0 * inner;
+    for (int64_t b = 0; b < nr; b += RBW) {
+      const int64_t nb = (nr - b < RBW) ? (nr - b) : RBW;
+      if (!resident) load_block<RBW, W>(xs + b * inner, inner, nb, v);
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) {
+        if (i < nb) {
+          float r[W];
+#pragma unroll
+          for (int w = 0; w < W; ++w) r[w] = (v[w][i] - m[w]) - lns[w];
+#if LSE_AXIS_NT_STORE
+          store_w_nt<W>(ys + (b + i) * inner, r);
+#else
+          store_w<W>(ys + (b + i) * inner, r);
+#endif
+        }
+      }
+    }
+  }
+}
+
 template <int RB, bool LSM>
 hipError_t launch_rb(const float *x, float *out, int64_t outer, int64_t R, int64_t inner,
                      bool vec, hipStream_t stream) {
@@ -232,26 +374,62 @@ hipError_t launch_rb(const float *x, float *out, int64_t outer, int64_t R, int64
   return hipGetLastError();
 }
 
+template <int RBW, int W, int P, bool LSM>
+hipError_t launch_split(const float *x, float *out, int64_t outer, int64_t R, int64_t inner,
+                        hipStream_t stream) {
+  constexpr int G = (LSE_AXIS_SPLIT_WAVES / P) > 1 ? (LSE_AXIS_SPLIT_WAVES / P) : 1;
+  const int64_t items = outer * (inner / W);
+  const dim3 grid((uint32_t)((items + kWave * G - 1) / (kWave * G)));
+  hipLaunchKernelGGL((axis_split_kernel<RBW, W, P, G, LSM>), grid, dim3(kWave * P * G), 0,
+                     stream, x, out, outer, R, inner);
+  return hipGetLastError();
+}
+
+template <int RBW, bool LSM>
+hipError_t launch_split_p(int P, const float *x, float *out, int64_t outer, int64_t R,
+                          int64_t inner, hipStream_t stream) {
+  switch (P) {
+    case 1: return launch_split<RBW, kVecW, 1, LSM>(x, out, outer, R, inner, stream);
+    case 2: return launch_split<RBW, kVecW, 2, LSM>(x, out, outer, R, inner, stream);
+    case 4: return launch_split<RBW, kVecW, 4, LSM>(x, out, outer, R, inner, stream);
+    case 8: return launch_split<RBW, kVecW, 8, LSM>(x, out, outer, R, inner, stream);
+    default: return launch_split<RBW, kVecW, 16, LSM>(x, out, outer, R, inner, stream);
+  }
+}
+
 template <bool LSM>
 hipError_t launch_axis(const float *x, float *out, int64_t outer, int64_t R, int64_t inner,
                        hipStream_t stream) {
   if (inner == 0 || outer == 0) return hipSuccess;
   const uintptr_t a = (uintptr_t)x | (uintptr_t)out;
   const bool vec = (inner % kVecW == 0) && (a % 16 == 0);
+  constexpr int RBW = LSE_AXIS_SPLIT_RBW;
+  if (vec && LSM && R >= LSE_AXIS_LSM_SPLIT_MINR) {
+    // log_softmax: the fewest waves (a power of two up to 16) whose slices of
+    // ceil(R / P) planes fit RBW registers each, so x is read once up to
+    // R = 16 RBW.
+    int P = 1;
+    while (P < 16 && (int64_t)P * RBW < R) P *= 2;
+    return launch_split_p<RBW, true>(P, x, out, outer, R, inner, stream);
+  }
+  const int64_t waves = (outer * (inner / kVecW) + kWave - 1) / kWave;
+  if (vec && !LSM && R >= LSE_AXIS_LSE_SPLIT_MINR && waves <= LSE_AXIS_LSE_SPLIT_MAXWAVES) {
+    // logsumexp over long R with few outputs: one wave per 256 outputs would
+    // leave most of the GPU idle, so P waves share each output run, each
+    // streaming at least 8 planes.
+    int P = 1;
+    while (P < 16 && waves * P < LSE_AXIS_LSE_SPLIT_TARGET) P *= 2;
+    while (P > 1 && R < 8 * (int64_t)P) P /= 2;
+    if (P > 1) return launch_split_p<RBW, false>(P, x, out, outer, R, inner, stream);
+  }
   if (R <= 4) return launch_rb<4, LSM>(x, out, outer, R, inner, vec, stream);
   if (R <= 8 || LSE_AXIS0_RBMAX <= 8) return launch_rb<8, LSM>(x, out, outer, R, inner, vec, stream);
   if (R <= 16 || LSE_AXIS0_RBMAX <= 16)
     return launch_rb<16, LSM>(x, out, outer, R, inner, vec, stream);
-  if (LSM && R > 32 && R <= 64 && LSE_AXIS_LSM64_W == 4 && vec) {
-    const dim3 grid((uint32_t)((outer * (inner / 4) + kLsmThreads - 1) / kLsmThreads));
-    hipLaunchKernelGGL((log_softmax_axis_kernel<64, 4>), grid, dim3(kLsmThreads), 0, stream,
-                       x, out, outer, R, inner);
-    return hipGetLastError();
-  }
   if (LSM && R > 32 && R <= 128) {
-    // log_softmax keeps all R values in registers for the write: narrow the
-    // per-lane vector so that R x W stays at 128 values (2 outputs per lane
-    // up to 64 planes, 1 up to 128) instead of reading x twice.
+    // Unaligned log_softmax keeps all R values in registers for the write:
+    // narrow the per-lane vector so that R x W stays at 128 values (2 outputs
+    // per lane up to 64 planes, 1 up to 128) instead of reading x twice.
     const int64_t items = outer * (R <= 64 && inner % 2 == 0 && a % 8 == 0 ? inner / 2 : inner);
     const dim3 grid((uint32_t)((items + kLsmThreads - 1) / kLsmThreads));
     if (R <= 64 && inner % 2 == 0 && a % 8 == 0)

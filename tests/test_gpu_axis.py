@@ -14,7 +14,12 @@ DEV = "cuda"
 
 @pytest.mark.parametrize("outer,R,inner", [(1, 4, 320), (3, 5, 7), (2, 64, 36), (4, 1, 9),
                                            (5, 33, 1), (7, 32, 1000), (2, 70, 65), (128, 64, 100),
-                                           (3, 17, 4097), (1, 100, 8)])
+                                           (3, 17, 4097), (1, 100, 8),
+                                           # plane-split paths: ragged last slice, resident
+                                           # up to 16 slices of 16 planes, streamed beyond
+                                           (1, 33, 256), (1, 40, 4), (2, 200, 128),
+                                           (8, 128, 4096), (1, 257, 64), (3, 1024, 32),
+                                           (1, 2048, 8192)])
 def test_lse_and_log_softmax_axis(orc, outer, R, inner):
     x = inputs.normal((outer, R, inner), seed=outer * 7919 + R * 31 + inner, sigma=3.0,
                       device=DEV)
@@ -64,3 +69,28 @@ def test_chain_layout_channel_lse(orc):
         compare(out[o:o + 1].cpu().numpy(), orc.lse_axis(xs), what=f"chain layout lse {o}")
         compare(y[o:o + 1].cpu().numpy(), orc.log_softmax_axis(xs), what=f"chain layout lsm {o}")
     assert (torch.logsumexp(y.double(), dim=1).abs() < 1e-5).all()
+
+
+@pytest.mark.parametrize("R", [40, 96, 300])
+def test_axis_split_special_values(orc, R):
+    """Non-finite values confined to one wave's slice of planes: a slice that
+    counts nothing (all -inf) must drop out of the merge, a +inf in one slice
+    must win over finite slices, NaN must poison only its own output."""
+    x = inputs.normal((2, R, 64), seed=R, sigma=4.0, device=DEV)
+    x[0, :, 0] = -float("inf")                 # every plane: LSE -inf, log_softmax NaN
+    x[0, : R // 4, 1] = -float("inf")          # the first slice(s) empty
+    x[0, R // 2:, 2] = -float("inf")           # the last slices empty
+    x[1, R - 1, 3] = float("inf")              # +inf in the last slice only
+    x[1, 0, 4] = float("inf")
+    x[1, R // 2, 4] = float("inf")             # two +inf in different slices
+    x[1, R // 3, 5] = float("nan")
+    x[0, :, 6] = 80.0                          # equal values: v + log R
+    x[0, 1, 7] = -80.0
+    xc = x.cpu().numpy()
+    compare(L.lse_reduce_axis(x, 1).cpu().numpy(), orc.lse_axis(xc), what=f"split lse R={R}")
+    compare(L.log_softmax_axis(x, 1).cpu().numpy(), orc.log_softmax_axis(xc),
+            what=f"split lsm R={R}")
+    xm = torch.empty(x.numel() + 1, device=DEV)[1:].view_as(x)   # misaligned: scalar path
+    xm.copy_(x)
+    compare(L.log_softmax_axis(xm, 1).cpu().numpy(), orc.log_softmax_axis(xc),
+            what=f"misaligned lsm R={R}")
