@@ -51,6 +51,9 @@ namespace {
 #ifndef LSE_AXIS_SPLIT_RBW
 #define LSE_AXIS_SPLIT_RBW 16   // planes per wave held in registers by the plane-split kernel
 #endif
+#ifndef LSE_AXIS_SPLIT_LSM_NT_LOAD
+#define LSE_AXIS_SPLIT_LSM_NT_LOAD 0   // the log_softmax split reads x with cached loads
+#endif
 #ifndef LSE_AXIS_SPLIT_WAVES
 #define LSE_AXIS_SPLIT_WAVES 8   // waves per workgroup: G = max(1, this / P) groups
 #endif
@@ -91,7 +94,7 @@ __device__ __forceinline__ void fold_block(const float (&v)[NB], float &m, float
 
 // W consecutive values of one plane into column i of v (64-bit loads for W = 2,
 // 128-bit loads for W >= 4).
-template <int W, int RB>
+template <int W, int RB, bool NT = LSE_AXIS0_NT_LOAD>
 __device__ __forceinline__ void load_plane(const float *p, float (&v)[W][RB], int i) {
   if constexpr (W == 1) {
     v[0][i] = *p;
@@ -101,12 +104,12 @@ __device__ __forceinline__ void load_plane(const float *p, float (&v)[W][RB], in
   } else {
 #pragma unroll
     for (int h = 0; h < W / 4; ++h) {
-#if LSE_AXIS0_NT_LOAD
       typedef float v4f __attribute__((ext_vector_type(4)));
-      const v4f t = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p + 4 * h));
-#else
-      const float4 t = *reinterpret_cast<const float4 *>(p + 4 * h);
-#endif
+      v4f t;
+      if constexpr (NT)
+        t = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p + 4 * h));
+      else
+        t = *reinterpret_cast<const v4f *>(p + 4 * h);
       v[4 * h][i] = t.x; v[4 * h + 1][i] = t.y; v[4 * h + 2][i] = t.z; v[4 * h + 3][i] = t.w;
     }
   }
@@ -126,17 +129,17 @@ __device__ __forceinline__ bool axis_item(int64_t outer, int64_t R, int64_t inne
 
 // Load planes r0 .. r0 + nb - 1 (nb <= RB) of W lanes' outputs into v,
 // padding with the identity -inf; all loads are issued before any is used.
-template <int RB, int W>
+template <int RB, int W, bool NT = LSE_AXIS0_NT_LOAD>
 __device__ __forceinline__ void load_block(const float *base, int64_t inner, int64_t nb,
                                            float (&v)[W][RB]) {
   if (nb == RB) {
 #pragma unroll
-    for (int i = 0; i < RB; ++i) load_plane<W>(base + (int64_t)i * inner, v, i);
+    for (int i = 0; i < RB; ++i) load_plane<W, RB, NT>(base + (int64_t)i * inner, v, i);
   } else {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if (i < nb) {
-        load_plane<W>(base + (int64_t)i * inner, v, i);
+        load_plane<W, RB, NT>(base + (int64_t)i * inner, v, i);
       } else {
 #pragma unroll
         for (int w = 0; w < W; ++w) v[w][i] = -__builtin_inff();
@@ -260,6 +263,9 @@ template <int RBW, int W, int P, int G, bool LSM>
 __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
     const float *__restrict__ x, float *__restrict__ out, int64_t outer, int64_t R,
     int64_t inner) {
+  // log_softmax's split measured faster with cached loads (neighbouring
+  // workgroups share the cache lines at their segment boundaries).
+  constexpr bool kSplitNt = LSM ? (LSE_AXIS_SPLIT_LSM_NT_LOAD != 0) : (LSE_AXIS0_NT_LOAD != 0);
   __shared__ float lds_m[G][P][W][kWave];
   __shared__ float lds_s[G][P][W][kWave];
   const int lane = threadIdx.x & (kWave - 1);
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   const bool resident = per <= RBW;  // uniform
   for (int64_t b = 0; b < nr; b += RBW) {
     const int64_t nb = valid ? ((nr - b < RBW) ? (nr - b) : RBW) : 0;
-    load_block<RBW, W>(xs + b * inner, inner, nb, v);
+    load_block<RBW, W, kSplitNt>(xs + b * inner, inner, nb, v);
 #pragma unroll
     for (int w = 0; w < W; ++w) fold_block<RBW>(v[w], m[w], s[w]);
   }
@@ -332,7 +338,7 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
     float *ys = out + off + r0 * inner;
     for (int64_t b = 0; b < nr; b += RBW) {
       const int64_t nb = (nr - b < RBW) ? (nr - b) : RBW;
-      if (!resident) load_block<RBW, W>(xs + b * inner, inner, nb, v);
+      if (!resident) load_block<RBW, W, kSplitNt>(xs + b * inner, inner, nb, v);
 #pragma unroll
       for (int i = 0; i < RBW; ++i) {
         if (i < nb) {
