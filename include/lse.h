@@ -87,13 +87,39 @@ lse_status_t lse_reduce_axis0(const float *x, float *out, int64_t R,
  *   lse_reduce_axis:  out[o * inner + j] = LSE_r x[(o * R + r) * inner + j]
  *                     (out: outer x inner floats)
  *   log_softmax_axis: y[(o*R + r)*inner + j] = x[...] - LSE_r' x[(o*R + r')*inner + j]
- *                     (y: same shape as x; one read of x when R <= 32, two
- *                     otherwise)
+ *                     (y: same shape as x; x is read once when R <= 256 and
+ *                     inner, x and y allow 16-byte vectors, or R <= 128
+ *                     otherwise; twice beyond)
  * outer, inner >= 0 (0 is a no-op), R >= 1; outputs must not overlap x. */
 lse_status_t lse_reduce_axis(const float *x, float *out, int64_t outer,
                              int64_t R, int64_t inner, hipStream_t stream);
 lse_status_t log_softmax_axis(const float *x, float *y, int64_t outer,
                               int64_t R, int64_t inner, hipStream_t stream);
+/* Strided forms of the two calls above, for views into larger buffers (a
+ * slice of planes or of the inner run, a padded channel pitch).  Strides are
+ * in elements, >= 0; the inner index is contiguous:
+ *   lse_reduce_axis_strided:  out[o * out_stride_outer + j]
+ *                               = LSE_r x[o * x_stride_outer + r * x_stride_r + j]
+ *   log_softmax_axis_strided: y[o * y_stride_outer + r * y_stride_r + j]
+ *                               = x[o * x_stride_outer + r * x_stride_r + j] - LSE_r' (...)
+ * The contiguous calls are x_stride_outer = R inner, x_stride_r = inner (and
+ * the same for y; out_stride_outer = inner).  Outputs may not collide:
+ * y_stride_r >= inner when R > 1, and the outer stride of the output is at
+ * least the extent of one outer block ((R - 1) y_stride_r + inner, or inner
+ * for logsumexp) when outer > 1; otherwise LSE_ERR_SHAPE.  x may overlap
+ * itself (it is only read).  The whole address range of the output may not
+ * intersect that of x (LSE_ERR_OVERLAP, even where the two would interleave
+ * without sharing an element).  The fast 16-byte path needs every stride and
+ * inner to be a multiple of 4 and 16-byte aligned x and output. */
+lse_status_t lse_reduce_axis_strided(const float *x, float *out, int64_t outer,
+                                     int64_t R, int64_t inner,
+                                     int64_t x_stride_outer, int64_t x_stride_r,
+                                     int64_t out_stride_outer, hipStream_t stream);
+lse_status_t log_softmax_axis_strided(const float *x, float *y, int64_t outer,
+                                      int64_t R, int64_t inner,
+                                      int64_t x_stride_outer, int64_t x_stride_r,
+                                      int64_t y_stride_outer, int64_t y_stride_r,
+                                      hipStream_t stream);
 
 /* ---------------------------------------------------------------- case B
  * Row-wise log_softmax over the last axis.           [LSM] opening formula
@@ -114,6 +140,19 @@ lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows,
  * log_softmax_rows.                          [LSM] the standard-softmax variant */
 lse_status_t softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
                           void *ws, size_t ws_bytes, hipStream_t stream);
+/* log_softmax_rows / softmax_rows over rows that sit ldx (x) and ldy (y)
+ * elements apart, e.g. the first cols columns of a wider matrix: row r of x
+ * starts at x + r * ldx.  ldx, ldy >= cols (else LSE_ERR_SHAPE); the
+ * workspace is the same as for the contiguous call.  The address ranges
+ * spanned by x and y may not intersect (LSE_ERR_OVERLAP).  The 16-byte
+ * path needs ldx, ldy and cols to be multiples of 4. */
+lse_status_t log_softmax_rows_strided(const float *x, float *y, int64_t rows,
+                                      int64_t cols, int64_t ldx, int64_t ldy,
+                                      void *ws, size_t ws_bytes,
+                                      hipStream_t stream);
+lse_status_t softmax_rows_strided(const float *x, float *y, int64_t rows,
+                                  int64_t cols, int64_t ldx, int64_t ldy,
+                                  void *ws, size_t ws_bytes, hipStream_t stream);
 /* How many times a workgroup of a split row polls for its siblings' (max,
  * sum) pairs before it computes the missing ones itself from x (default 2^24;
  * independently it never waits longer than about 50 us).  The results are

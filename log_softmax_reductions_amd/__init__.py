@@ -8,9 +8,10 @@ the HIP kernels of liblse.so; there is no CPU path, and a missing library
 raises ImportError on first use.
 
   lse_reduce_axis0(x)           logsumexp over dim 0 of an (R, ...) tensor
-  lse_reduce_axis(x, dim)       logsumexp over any dim of a contiguous tensor
-  log_softmax_axis(x, dim)      log_softmax over any dim of a contiguous tensor
+  lse_reduce_axis(x, dim)       logsumexp over any dim (strided views accepted)
+  log_softmax_axis(x, dim)      log_softmax over any dim (strided views accepted)
   log_softmax_rows(x)           log_softmax over the last dim of a 2-D tensor
+                                (rows may be ld apart: column slices accepted)
   softmax_rows(x)               softmax over the last dim of a 2-D tensor
   lse_rows_partial(x, chunk)    (max, sum) pair per (row, chunk)
   lse_rows_merge(partials)      row logsumexp from the pairs
@@ -25,7 +26,8 @@ from . import _lib
 from ._lib import LseError  # noqa: F401
 
 __all__ = [
-    "lse_reduce_axis0", "lse_reduce_axis", "log_softmax_axis", "softmax_rows", "log_softmax_rows", "log_softmax_rows_workspace_bytes",
+    "lse_reduce_axis0", "lse_reduce_axis", "log_softmax_axis", "softmax_rows", "log_softmax_rows",
+    "log_softmax_rows_workspace_bytes",
     "log_softmax_rows_plan", "lse_set_spin_limit", "lse_rows_num_chunks", "lse_rows_partial",
     "lse_rows_merge", "fused_conv_gn_act_lse", "fused_conv_gn_act_lse_workspace_bytes",
     "lse_abi_version", "LseError",
@@ -39,7 +41,7 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream.cuda_stream))
 
 
-def _dev(t, name):
+def _dev(t, name, contiguous=True):
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -47,7 +49,7 @@ def _dev(t, name):
         raise ValueError(f"{name} must be on the GPU (got {t.device})")
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32 (got {t.dtype})")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
 
@@ -98,51 +100,99 @@ def _axis_view(x, dim):
     return d, outer, x.shape[d], inner
 
 
+def _collapse(shape, strides, name):
+    """Stride of the dims of `shape` merged into one run, or None when they
+    do not merge (size-1 dims are ignored; an empty or all-size-1 set merges
+    to stride 0)."""
+    dims = [(n, st) for n, st in zip(shape, strides) if n != 1]
+    for (n0, s0), (n1, s1) in zip(dims, dims[1:]):
+        if s0 != s1 * n1:
+            return None
+    return dims[-1][1] if dims else 0
+
+
+def _strided_axis(t, d, name):
+    """(outer_stride, r_stride) of t viewed as (outer, R, inner) around dim d,
+    the inner run contiguous.  Raises ValueError for layouts the strided
+    entry points cannot express (no silent copy is made)."""
+    shape, strides = tuple(t.shape), tuple(t.stride())
+    inner_st = _collapse(shape[d + 1:], strides[d + 1:], name)
+    if inner_st not in (0, 1):
+        raise ValueError(f"{name}: the dims after the reduced one must form one contiguous run")
+    outer_st = _collapse(shape[:d], strides[:d], name)
+    if outer_st is None:
+        raise ValueError(f"{name}: the dims before the reduced one must merge into one stride")
+    return outer_st, strides[d]
+
+
 def lse_reduce_axis(x, dim, out=None, stream=None):
-    """logsumexp over `dim` of a contiguous fp32 GPU tensor (dim removed)."""
+    """logsumexp over `dim` of an fp32 GPU tensor (dim removed).  x and out
+    may be strided views whose dims after `dim` form one contiguous run and
+    whose dims before it merge into one stride."""
     import torch
     lib = _lib.load()
     d, outer, R, inner = _axis_view(x, dim)
     shape = tuple(x.shape[:d]) + tuple(x.shape[d + 1:])
     if out is None:
         out = torch.empty(shape, dtype=torch.float32, device=x.device)
-    if out.numel() != outer * inner:
-        raise ValueError("out has the wrong number of elements")
-    _lib.check(lib.lse_reduce_axis(_dev(x, "x"), _dev(out, "out"), outer, R, inner,
-                                   _stream(stream)), "lse_reduce_axis")
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out must have shape {shape}")
+    xso, xsr = _strided_axis(x, d, "x")
+    oso, _ = _strided_axis(out.unsqueeze(d), d, "out")
+    _lib.check(lib.lse_reduce_axis_strided(_dev(x, "x", False), _dev(out, "out", False), outer,
+                                           R, inner, xso, xsr, oso, _stream(stream)),
+               "lse_reduce_axis")
     return out
 
 
 def log_softmax_axis(x, dim, y=None, stream=None):
-    """log_softmax over `dim` of a contiguous fp32 GPU tensor."""
+    """log_softmax over `dim` of an fp32 GPU tensor; x and y may be strided
+    views as for lse_reduce_axis (a new y is contiguous)."""
     import torch
     lib = _lib.load()
-    _, outer, R, inner = _axis_view(x, dim)
+    d, outer, R, inner = _axis_view(x, dim)
     if y is None:
-        y = torch.empty_like(x)
+        y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     if y.shape != x.shape:
         raise ValueError("y must have x's shape")
-    _lib.check(lib.log_softmax_axis(_dev(x, "x"), _dev(y, "y"), outer, R, inner,
-                                    _stream(stream)), "log_softmax_axis")
+    xso, xsr = _strided_axis(x, d, "x")
+    yso, ysr = _strided_axis(y, d, "y")
+    _lib.check(lib.log_softmax_axis_strided(_dev(x, "x", False), _dev(y, "y", False), outer, R,
+                                            inner, xso, xsr, yso, ysr, _stream(stream)),
+               "log_softmax_axis")
     return y
 
 
-def softmax_rows(x, y=None, ws=None, stream=None):
-    """y = softmax(x, dim=-1) for a 2-D fp32 GPU tensor x."""
+def _ld(t, name):
+    """Row pitch of a 2-D tensor whose rows are contiguous."""
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: each row must be contiguous (stride 1 along dim 1)")
+    return t.stride(0) if rows > 1 else cols
+
+
+def _rows_call(fn, name, x, y, ws, stream):
     import torch
     lib = _lib.load()
     if x.dim() != 2:
         raise ValueError("x must be 2-D (rows, cols)")
     rows, cols = x.shape
     if y is None:
-        y = torch.empty_like(x)
+        y = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
     if y.shape != x.shape:
         raise ValueError("y must have x's shape")
+    ldx, ldy = _ld(x, "x"), _ld(y, "y")
     ws, ws_bytes = _workspace(log_softmax_rows_workspace_bytes(rows, cols), x.device, ws)
-    _lib.check(lib.softmax_rows(_dev(x, "x"), _dev(y, "y"), rows, cols,
+    _lib.check(getattr(lib, fn)(_dev(x, "x", False), _dev(y, "y", False), rows, cols, ldx, ldy,
                                 None if ws is None else ctypes.c_void_p(ws.data_ptr()),
-                                ws_bytes, _stream(stream)), "softmax_rows")
+                                ws_bytes, _stream(stream)), name)
     return y
+
+
+def softmax_rows(x, y=None, ws=None, stream=None):
+    """y = softmax(x, dim=-1) for a 2-D fp32 GPU tensor x whose rows are
+    contiguous (rows may be any pitch apart)."""
+    return _rows_call("softmax_rows_strided", "softmax_rows", x, y, ws, stream)
 
 
 def log_softmax_rows_workspace_bytes(rows: int, cols: int) -> int:
@@ -162,21 +212,9 @@ def lse_set_spin_limit(polls: int) -> None:
 
 
 def log_softmax_rows(x, y=None, ws=None, stream=None):
-    """y = log_softmax(x, dim=-1) for a 2-D fp32 GPU tensor x."""
-    import torch
-    lib = _lib.load()
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D (rows, cols)")
-    rows, cols = x.shape
-    if y is None:
-        y = torch.empty_like(x)
-    if y.shape != x.shape:
-        raise ValueError("y must have x's shape")
-    ws, ws_bytes = _workspace(log_softmax_rows_workspace_bytes(rows, cols), x.device, ws)
-    _lib.check(lib.log_softmax_rows(_dev(x, "x"), _dev(y, "y"), rows, cols,
-                                    None if ws is None else ctypes.c_void_p(ws.data_ptr()),
-                                    ws_bytes, _stream(stream)), "log_softmax_rows")
-    return y
+    """y = log_softmax(x, dim=-1) for a 2-D fp32 GPU tensor x whose rows are
+    contiguous (rows may be any pitch apart)."""
+    return _rows_call("log_softmax_rows_strided", "log_softmax_rows", x, y, ws, stream)
 
 
 def lse_rows_num_chunks(cols: int, chunk: int) -> int:

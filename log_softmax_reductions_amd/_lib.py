@@ -18,6 +18,12 @@ SIGNATURES = {
     "lse_reduce_axis0": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "lse_reduce_axis": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "log_softmax_axis": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _vp]),
+    "lse_reduce_axis_strided": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                               _vp]),
+    "log_softmax_axis_strided": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                _i64, _vp]),
+    "log_softmax_rows_strided": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "softmax_rows_strided": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     "log_softmax_rows_workspace_bytes": (_sz, [_i64, _i64]),
     "softmax_rows": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
     "log_softmax_rows": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),

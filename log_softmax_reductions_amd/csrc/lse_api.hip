@@ -54,6 +54,22 @@ bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes) {
 constexpr int64_t kMaxElems = INT64_MAX / 16;  // keeps every byte offset in range
 constexpr int64_t kMaxGrid = 0x7fffffff;
 
+// a + b (both >= 0) capped: false when the sum passes kMaxElems.
+bool add_ok(int64_t a, int64_t b, int64_t *r) {
+  if (a > kMaxElems || b > kMaxElems - a) return false;
+  *r = a + b;
+  return true;
+}
+
+// Elements from the first to one past the last element of a row-major
+// (n1, n2, inner) array with strides s1, s2 and contiguous inner index:
+// (n1 - 1) s1 + (n2 - 1) s2 + inner.  All sizes >= 1, strides >= 0.
+bool span_ok(int64_t n1, int64_t s1, int64_t n2, int64_t s2, int64_t inner, int64_t *span) {
+  int64_t a, b, t;
+  return mul_ok(n1 - 1, s1, &a) && mul_ok(n2 - 1, s2, &b) && add_ok(a, b, &t) &&
+         add_ok(t, inner, span);
+}
+
 }  // namespace
 
 LSE_EXPORT const char *lse_status_string(int status) {
@@ -90,47 +106,91 @@ LSE_EXPORT lse_status_t lse_reduce_axis0(const float *x, float *out, int64_t R, 
     return fail(LSE_ERR_OVERLAP, "lse_reduce_axis0: out overlaps x");
   if ((inner + 63) / 64 > kMaxGrid)
     return fail(LSE_ERR_SHAPE, "lse_reduce_axis0: inner too large for one launch");
-  return from_hip(lse::launch_lse_axis(x, out, 1, R, inner, stream), "lse_reduce_axis0 launch");
+  const lse::AxisDims d{1, R, inner, R * inner, inner, inner, 0};
+  return from_hip(lse::launch_lse_axis(x, out, d, stream), "lse_reduce_axis0 launch");
 }
 
 // ------------------------------------------------------------ middle axis
+// Checks a strided axis call: x[o xso + r xsr + j], output y[o yso + r ysr + j]
+// (logsumexp: ysr = 0 and R_out = 1).  Writes must not collide, so
+// consecutive output planes / outer blocks may not overlap (ysr >= inner,
+// yso >= (R_out - 1) ysr + inner); x's span and the output's span must be
+// disjoint (checked on the byte ranges, conservatively).
 static lse_status_t check_axis(const char *who, const void *x, const void *out, int64_t outer,
-                               int64_t R, int64_t inner, int64_t out_per_outer,
-                               int64_t *total) {
+                               int64_t R, int64_t inner, int64_t xso, int64_t xsr, int64_t yso,
+                               int64_t ysr, bool lsm, int64_t *total) {
   if (outer < 0 || R < 1 || inner < 0)
     return fail(LSE_ERR_SHAPE, "%s: need outer >= 0, R >= 1, inner >= 0 (got %lld, %lld, %lld)",
                 who, (long long)outer, (long long)R, (long long)inner);
+  if (xso < 0 || xsr < 0 || yso < 0 || ysr < 0)
+    return fail(LSE_ERR_SHAPE, "%s: strides must be >= 0", who);
   int64_t t;
   if (!mul_ok(outer, R, &t) || !mul_ok(t, inner, total) || *total > kMaxElems)
     return fail(LSE_ERR_SHAPE, "%s: outer * R * inner overflows", who);
   if (*total == 0) return LSE_OK;
+  const int64_t r_out = lsm ? R : 1;
+  if (r_out > 1 && ysr < inner)
+    return fail(LSE_ERR_SHAPE, "%s: output planes overlap (stride %lld < inner %lld)", who,
+                (long long)ysr, (long long)inner);
+  int64_t plane_span;
+  if (!span_ok(r_out, ysr, 1, 0, inner, &plane_span))
+    return fail(LSE_ERR_SHAPE, "%s: output extent overflows", who);
+  if (outer > 1 && yso < plane_span)
+    return fail(LSE_ERR_SHAPE, "%s: output blocks overlap (outer stride %lld < %lld)", who,
+                (long long)yso, (long long)plane_span);
+  int64_t xspan, yspan;
+  if (!span_ok(outer, xso, R, xsr, inner, &xspan) || !span_ok(outer, yso, r_out, ysr, inner, &yspan))
+    return fail(LSE_ERR_SHAPE, "%s: strided extent overflows", who);
   if (!x || !out) return fail(LSE_ERR_NULL, "%s: NULL pointer", who);
-  if (overlaps(x, *total * 4, out, outer * out_per_outer * 4))
+  if (overlaps(x, xspan * 4, out, yspan * 4))
     return fail(LSE_ERR_OVERLAP, "%s: output overlaps x", who);
   if ((outer * inner + 63) / 64 > kMaxGrid)
     return fail(LSE_ERR_SHAPE, "%s: too many outputs for one launch", who);
   return LSE_OK;
 }
 
-LSE_EXPORT lse_status_t lse_reduce_axis(const float *x, float *out, int64_t outer, int64_t R,
-                                        int64_t inner, hipStream_t stream) {
+LSE_EXPORT lse_status_t lse_reduce_axis_strided(const float *x, float *out, int64_t outer,
+                                                int64_t R, int64_t inner,
+                                                int64_t x_stride_outer, int64_t x_stride_r,
+                                                int64_t out_stride_outer, hipStream_t stream) {
   int64_t total;
-  const lse_status_t st = check_axis("lse_reduce_axis", x, out, outer, R, inner, inner, &total);
+  const lse_status_t st = check_axis("lse_reduce_axis", x, out, outer, R, inner, x_stride_outer,
+                                     x_stride_r, out_stride_outer, 0, false, &total);
   if (st != LSE_OK) return st;
   if (total == 0) return ok();
-  return from_hip(lse::launch_lse_axis(x, out, outer, R, inner, stream),
-                  "lse_reduce_axis launch");
+  const lse::AxisDims d{outer, R, inner, x_stride_outer, x_stride_r, out_stride_outer, 0};
+  return from_hip(lse::launch_lse_axis(x, out, d, stream), "lse_reduce_axis launch");
+}
+
+LSE_EXPORT lse_status_t lse_reduce_axis(const float *x, float *out, int64_t outer, int64_t R,
+                                        int64_t inner, hipStream_t stream) {
+  int64_t xso = 0;  // negative sizes are reported by the strided call's checks
+  if (!mul_ok(R, inner, &xso) && R >= 1 && inner >= 0)
+    return fail(LSE_ERR_SHAPE, "lse_reduce_axis: outer * R * inner overflows");
+  return lse_reduce_axis_strided(x, out, outer, R, inner, xso, inner, inner, stream);
+}
+
+LSE_EXPORT lse_status_t log_softmax_axis_strided(const float *x, float *y, int64_t outer,
+                                                 int64_t R, int64_t inner,
+                                                 int64_t x_stride_outer, int64_t x_stride_r,
+                                                 int64_t y_stride_outer, int64_t y_stride_r,
+                                                 hipStream_t stream) {
+  int64_t total;
+  const lse_status_t st =
+      check_axis("log_softmax_axis", x, y, outer, R, inner, x_stride_outer, x_stride_r,
+                 y_stride_outer, y_stride_r, true, &total);
+  if (st != LSE_OK) return st;
+  if (total == 0) return ok();
+  const lse::AxisDims d{outer, R, inner, x_stride_outer, x_stride_r, y_stride_outer, y_stride_r};
+  return from_hip(lse::launch_log_softmax_axis(x, y, d, stream), "log_softmax_axis launch");
 }
 
 LSE_EXPORT lse_status_t log_softmax_axis(const float *x, float *y, int64_t outer, int64_t R,
                                          int64_t inner, hipStream_t stream) {
-  int64_t total;
-  const lse_status_t st =
-      check_axis("log_softmax_axis", x, y, outer, R, inner, R * inner, &total);
-  if (st != LSE_OK) return st;
-  if (total == 0) return ok();
-  return from_hip(lse::launch_log_softmax_axis(x, y, outer, R, inner, stream),
-                  "log_softmax_axis launch");
+  int64_t so = 0;  // negative sizes are reported by the strided call's checks
+  if (!mul_ok(R, inner, &so) && R >= 1 && inner >= 0)
+    return fail(LSE_ERR_SHAPE, "log_softmax_axis: outer * R * inner overflows");
+  return log_softmax_axis_strided(x, y, outer, R, inner, so, inner, so, inner, stream);
 }
 
 // ------------------------------------------------------------------ case B
@@ -158,14 +218,20 @@ LSE_EXPORT size_t log_softmax_rows_workspace_bytes(int64_t rows, int64_t cols) {
 }
 
 static lse_status_t rows_call(const char *who, bool softmax, const float *x, float *y,
-                              int64_t rows, int64_t cols, void *ws, size_t ws_bytes,
-                              hipStream_t stream) {
+                              int64_t rows, int64_t cols, int64_t ldx, int64_t ldy, void *ws,
+                              size_t ws_bytes, hipStream_t stream) {
   int64_t total;
   lse_status_t st = check_rows(who, rows, cols, &total);
   if (st != LSE_OK) return st;
+  if (ldx < cols || ldy < cols)
+    return fail(LSE_ERR_SHAPE, "%s: ldx = %lld and ldy = %lld must be >= cols = %lld", who,
+                (long long)ldx, (long long)ldy, (long long)cols);
   if (rows == 0) return ok();
+  int64_t xspan, yspan;
+  if (!span_ok(rows, ldx, 1, 0, cols, &xspan) || !span_ok(rows, ldy, 1, 0, cols, &yspan))
+    return fail(LSE_ERR_SHAPE, "%s: rows * ld overflows", who);
   if (!x || !y) return fail(LSE_ERR_NULL, "%s: x and y must be non-NULL", who);
-  if (overlaps(x, total * 4, y, total * 4))
+  if (overlaps(x, xspan * 4, y, yspan * 4))
     return fail(LSE_ERR_OVERLAP, "%s: y overlaps x (in-place is not supported)", who);
   const lse::RowsPlan p = lse::rows_plan(cols);
   if (p.nchunks > lse::kRowsMaxChunks)
@@ -178,20 +244,35 @@ static lse_status_t rows_call(const char *who, bool softmax, const float *x, flo
     if (!ws) return fail(LSE_ERR_WORKSPACE, "%s: needs %zu workspace bytes", who, need);
     if (ws_bytes < need)
       return fail(LSE_ERR_WORKSPACE, "%s: workspace %zu < required %zu", who, ws_bytes, need);
-    if (overlaps(ws, (int64_t)need, x, total * 4) || overlaps(ws, (int64_t)need, y, total * 4))
+    if (overlaps(ws, (int64_t)need, x, xspan * 4) || overlaps(ws, (int64_t)need, y, yspan * 4))
       return fail(LSE_ERR_OVERLAP, "%s: workspace overlaps x or y", who);
   }
-  return from_hip(lse::launch_log_softmax_rows(x, y, rows, cols, ws, stream, softmax), who);
+  return from_hip(lse::launch_log_softmax_rows(x, y, rows, cols, ldx, ldy, ws, stream, softmax),
+                  who);
 }
 
 LSE_EXPORT lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
                                          void *ws, size_t ws_bytes, hipStream_t stream) {
-  return rows_call("log_softmax_rows", false, x, y, rows, cols, ws, ws_bytes, stream);
+  return rows_call("log_softmax_rows", false, x, y, rows, cols, cols, cols, ws, ws_bytes,
+                   stream);
 }
 
 LSE_EXPORT lse_status_t softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
                                      void *ws, size_t ws_bytes, hipStream_t stream) {
-  return rows_call("softmax_rows", true, x, y, rows, cols, ws, ws_bytes, stream);
+  return rows_call("softmax_rows", true, x, y, rows, cols, cols, cols, ws, ws_bytes, stream);
+}
+
+LSE_EXPORT lse_status_t log_softmax_rows_strided(const float *x, float *y, int64_t rows,
+                                                 int64_t cols, int64_t ldx, int64_t ldy,
+                                                 void *ws, size_t ws_bytes,
+                                                 hipStream_t stream) {
+  return rows_call("log_softmax_rows", false, x, y, rows, cols, ldx, ldy, ws, ws_bytes, stream);
+}
+
+LSE_EXPORT lse_status_t softmax_rows_strided(const float *x, float *y, int64_t rows,
+                                             int64_t cols, int64_t ldx, int64_t ldy, void *ws,
+                                             size_t ws_bytes, hipStream_t stream) {
+  return rows_call("softmax_rows", true, x, y, rows, cols, ldx, ldy, ws, ws_bytes, stream);
 }
 
 LSE_EXPORT int64_t lse_rows_num_chunks(int64_t cols, int64_t chunk) {
@@ -215,7 +296,7 @@ LSE_EXPORT lse_status_t lse_rows_partial(const float *x, int64_t rows, int64_t c
     return fail(LSE_ERR_SHAPE, "lse_rows_partial: rows * chunks = too many workgroups");
   if (overlaps(x, total * 4, partials, wgs * 8))
     return fail(LSE_ERR_OVERLAP, "lse_rows_partial: partials overlap x");
-  return from_hip(lse::launch_lse_rows_partial(x, rows, cols, chunk, partials, stream),
+  return from_hip(lse::launch_lse_rows_partial(x, rows, cols, cols, chunk, partials, stream),
                   "lse_rows_partial launch");
 }
 

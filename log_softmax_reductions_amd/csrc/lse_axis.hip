@@ -115,31 +115,38 @@ __device__ __forceinline__ void load_plane(const float *p, float (&v)[W][RB], in
   }
 }
 
+// Each kernel takes its strides from the call's AxisDims when STR, else it
+// uses those of a contiguous (outer, R, inner) array, so that the x and y
+// offsets are one expression to the compiler (shared address arithmetic, fewer
+// VGPRs).  They are written out as scalar locals in every kernel: read through
+// a reference to the by-value kernel argument (a helper, a struct) they cost
+// the plane-split kernel ~75 VGPRs.
+
 // One lane = W consecutive inner outputs of one outer index.
 template <int W>
-__device__ __forceinline__ bool axis_item(int64_t outer, int64_t R, int64_t inner, int64_t &o,
-                                          int64_t &q) {
-  const int64_t nq = inner / W;  // W > 1: inner % W == 0 by dispatch
+__device__ __forceinline__ bool axis_item(const AxisDims &d, int64_t &o, int64_t &q) {
+  const int64_t nq = d.inner / W;  // W > 1: inner % W == 0 by dispatch
   const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (item >= outer * nq) return false;
-  o = (outer == 1) ? 0 : item / nq;
+  if (item >= d.outer * nq) return false;
+  o = (d.outer == 1) ? 0 : item / nq;
   q = item - o * nq;
   return true;
 }
 
-// Load planes r0 .. r0 + nb - 1 (nb <= RB) of W lanes' outputs into v,
-// padding with the identity -inf; all loads are issued before any is used.
+// Load planes r0 .. r0 + nb - 1 (nb <= RB, `stride` elements apart) of W
+// lanes' outputs into v, padding with the identity -inf; all loads are issued
+// before any is used.
 template <int RB, int W, bool NT = LSE_AXIS0_NT_LOAD>
-__device__ __forceinline__ void load_block(const float *base, int64_t inner, int64_t nb,
+__device__ __forceinline__ void load_block(const float *base, int64_t stride, int64_t nb,
                                            float (&v)[W][RB]) {
   if (nb == RB) {
 #pragma unroll
-    for (int i = 0; i < RB; ++i) load_plane<W, RB, NT>(base + (int64_t)i * inner, v, i);
+    for (int i = 0; i < RB; ++i) load_plane<W, RB, NT>(base + (int64_t)i * stride, v, i);
   } else {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if (i < nb) {
-        load_plane<W, RB, NT>(base + (int64_t)i * inner, v, i);
+        load_plane<W, RB, NT>(base + (int64_t)i * stride, v, i);
       } else {
 #pragma unroll
         for (int w = 0; w < W; ++w) v[w][i] = -__builtin_inff();
@@ -163,13 +170,16 @@ __device__ __forceinline__ void store_w(float *p, const float (&r)[W]) {
 }
 
 // out[o, j] = LSE_r x[o, r, j]
-template <int RB, int W>
+template <int RB, int W, bool STR>
 __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
-    const float *__restrict__ x, float *__restrict__ out, int64_t outer, int64_t R,
-    int64_t inner) {
+    const float *__restrict__ x, float *__restrict__ out, AxisDims d) {
   int64_t o, q;
-  if (!axis_item<W>(outer, R, inner, o, q)) return;
-  const float *xo = x + o * R * inner + q * W;
+  if (!axis_item<W>(d, o, q)) return;
+  const int64_t st_xsr = STR ? d.xsr : d.inner;
+  const int64_t st_xso = STR ? d.xso : d.R * d.inner;
+  const int64_t st_yso = STR ? d.yso : d.inner;
+  const int64_t R = d.R;
+  const float *xo = x + o * st_xso + q * W;
   float m[W], s[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) {
@@ -178,26 +188,31 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
   }
   for (int64_t r0 = 0; r0 < R; r0 += RB) {
     float v[W][RB];
-    load_block<RB, W>(xo + r0 * inner, inner, (R - r0 < RB) ? (R - r0) : RB, v);
+    load_block<RB, W>(xo + r0 * st_xsr, st_xsr, (R - r0 < RB) ? (R - r0) : RB, v);
 #pragma unroll
     for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
   }
   float r[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) r[w] = m[w] + logf(s[w]);
-  store_w<W>(out + o * inner + q * W, r);
+  store_w<W>(out + o * st_yso + q * W, r);
 }
 
 // y[o, r, j] = x[o, r, j] - LSE_r' x[o, r', j].  With R <= RB the R values stay
 // in registers between the reduction and the write (one read, one write);
 // otherwise a streaming reduction pass and a write pass (two reads).
-template <int RB, int W>
+template <int RB, int W, bool STR>
 __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
-    const float *__restrict__ x, float *__restrict__ y, int64_t outer, int64_t R,
-    int64_t inner) {
+    const float *__restrict__ x, float *__restrict__ y, AxisDims d) {
   int64_t o, q;
-  if (!axis_item<W>(outer, R, inner, o, q)) return;
-  const int64_t off = o * R * inner + q * W;
+  if (!axis_item<W>(d, o, q)) return;
+  const int64_t st_xsr = STR ? d.xsr : d.inner;
+  const int64_t st_xso = STR ? d.xso : d.R * d.inner;
+  const int64_t st_ysr = STR ? d.ysr : d.inner;
+  const int64_t st_yso = STR ? d.yso : d.R * d.inner;
+  const int64_t R = d.R;
+  const float *xo = x + o * st_xso + q * W;
+  float *yo = y + o * st_yso + q * W;
   float m[W], s[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) {
@@ -206,12 +221,12 @@ __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
   }
   float v[W][RB];
   if (R <= RB) {  // uniform
-    load_block<RB, W>(x + off, inner, R, v);
+    load_block<RB, W>(xo, st_xsr, R, v);
 #pragma unroll
     for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
   } else {
     for (int64_t r0 = 0; r0 < R; r0 += RB) {
-      load_block<RB, W>(x + off + r0 * inner, inner, (R - r0 < RB) ? (R - r0) : RB, v);
+      load_block<RB, W>(xo + r0 * st_xsr, st_xsr, (R - r0 < RB) ? (R - r0) : RB, v);
 #pragma unroll
       for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
     }
@@ -221,14 +236,14 @@ __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
   for (int w = 0; w < W; ++w) lns[w] = logf(s[w]);
   for (int64_t r0 = 0; r0 < R; r0 += RB) {
     const int64_t nb = (R - r0 < RB) ? (R - r0) : RB;
-    if (R > RB) load_block<RB, W>(x + off + r0 * inner, inner, nb, v);
+    if (R > RB) load_block<RB, W>(xo + r0 * st_xsr, st_xsr, nb, v);
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if (i < nb) {
         float r[W];
 #pragma unroll
         for (int w = 0; w < W; ++w) r[w] = (v[w][i] - m[w]) - lns[w];
-        store_w<W>(y + off + (r0 + i) * inner, r);
+        store_w<W>(yo + (r0 + i) * st_ysr, r);
       }
     }
   }
@@ -259,10 +274,13 @@ __device__ __forceinline__ void store_w_nt(float *p, const float (&r)[W]) {
 // load to the log_softmax write (one read, one write of x's bytes), and a lane
 // holds RBW x W values instead of R x W, so more waves fit on a SIMD to keep
 // loads in flight.  Larger R reads x a second time for the write.
-template <int RBW, int W, int P, int G, bool LSM>
+template <int RBW, int W, int P, int G, bool LSM, bool STR>
 __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
-    const float *__restrict__ x, float *__restrict__ out, int64_t outer, int64_t R,
-    int64_t inner) {
+    const float *__restrict__ x, float *__restrict__ out, AxisDims d) {
+  const int64_t st_xsr = STR ? d.xsr : d.inner;
+  const int64_t st_xso = STR ? d.xso : d.R * d.inner;
+  const int64_t st_ysr = STR ? d.ysr : d.inner;
+  const int64_t st_yso = STR ? d.yso : (LSM ? d.R * d.inner : d.inner);
   // log_softmax's split measured faster with cached loads (neighbouring
   // workgroups share the cache lines at their segment boundaries).
   constexpr bool kSplitNt = LSM ? (LSE_AXIS_SPLIT_LSM_NT_LOAD != 0) : (LSE_AXIS0_NT_LOAD != 0);
@@ -271,20 +289,22 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wv = wid % P, grp = wid / P;
-  const int64_t nq = inner / W;  // W > 1: inner % W == 0 by dispatch
+  const int64_t R = d.R;
+  const int64_t nq = d.inner / W;  // W > 1: inner % W == 0 by dispatch
   const int64_t item = ((int64_t)blockIdx.x * G + grp) * kWave + lane;
-  const bool valid = item < outer * nq;
+  const bool valid = item < d.outer * nq;
   int64_t o = 0, q = 0;
   if (valid) {
-    o = (outer == 1) ? 0 : item / nq;
+    o = (d.outer == 1) ? 0 : item / nq;
     q = item - o * nq;
   }
   const int64_t per = (R + P - 1) / P;
   const int64_t r0 = (int64_t)wv * per;
   int64_t nr = R - r0;  // planes of this wave's slice (0 for the last waves when P > R)
   nr = nr < 0 ? 0 : (nr > per ? per : nr);
-  const int64_t off = o * R * inner + q * W;
-  const float *xs = x + off + r0 * inner;
+  const int64_t xoff = o * st_xso + q * W + r0 * st_xsr;
+  const int64_t yoff = o * st_yso + q * W + r0 * st_ysr;  // == xoff when contiguous
+  const float *xs = x + xoff;
 
   float m[W], s[W];
 #pragma unroll
@@ -296,7 +316,7 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   const bool resident = per <= RBW;  // uniform
   for (int64_t b = 0; b < nr; b += RBW) {
     const int64_t nb = valid ? ((nr - b < RBW) ? (nr - b) : RBW) : 0;
-    load_block<RBW, W, kSplitNt>(xs + b * inner, inner, nb, v);
+    load_block<RBW, W, kSplitNt>(xs + b * st_xsr, st_xsr, nb, v);
 #pragma unroll
     for (int w = 0; w < W; ++w) fold_block<RBW>(v[w], m[w], s[w]);
   }
@@ -329,16 +349,16 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
       float r[W];
 #pragma unroll
       for (int w = 0; w < W; ++w) r[w] = m[w] + logf(s[w]);
-      store_w<W>(out + o * inner + q * W, r);
+      store_w<W>(out + o * st_yso + q * W, r);
     }
   } else {
     float lns[W];
 #pragma unroll
     for (int w = 0; w < W; ++w) lns[w] = logf(s[w]);
-    float *ys = out + off + r0 * inner;
+    float *ys = out + yoff;
     for (int64_t b = 0; b < nr; b += RBW) {
       const int64_t nb = (nr - b < RBW) ? (nr - b) : RBW;
-      if (!resident) load_block<RBW, W, kSplitNt>(xs + b * inner, inner, nb, v);
+      if (!resident) load_block<RBW, W, kSplitNt>(xs + b * st_xsr, st_xsr, nb, v);
 #pragma unroll
       for (int i = 0; i < RBW; ++i) {
         if (i < nb) {
@@ -346,9 +366,9 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
 #pragma unroll
           for (int w = 0; w < W; ++w) r[w] = (v[w][i] - m[w]) - lns[w];
 #if LSE_AXIS_NT_STORE
-          store_w_nt<W>(ys + (b + i) * inner, r);
+          store_w_nt<W>(ys + (b + i) * st_ysr, r);
 #else
-          store_w<W>(ys + (b + i) * inner, r);
+          store_w<W>(ys + (b + i) * st_ysr, r);
 #endif
         }
       }
@@ -356,59 +376,60 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   }
 }
 
-template <int RB, bool LSM>
-hipError_t launch_rb(const float *x, float *out, int64_t outer, int64_t R, int64_t inner,
-                     bool vec, hipStream_t stream) {
-  const int64_t items = outer * (vec ? inner / kVecW : inner);
+template <int RB, bool LSM, bool STR>
+hipError_t launch_rb(const float *x, float *out, const AxisDims &d, bool vec,
+                     hipStream_t stream) {
+  const int64_t items = d.outer * (vec ? d.inner / kVecW : d.inner);
   const dim3 grid((uint32_t)((items + kAxis0Threads - 1) / kAxis0Threads));
   if constexpr (LSM) {
     const dim3 lgrid((uint32_t)((items + kLsmThreads - 1) / kLsmThreads));
     if (vec)
-      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, kVecW>), lgrid, dim3(kLsmThreads), 0,
-                         stream, x, out, outer, R, inner);
+      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, kVecW, STR>), lgrid, dim3(kLsmThreads), 0,
+                         stream, x, out, d);
     else
-      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, 1>), lgrid, dim3(kLsmThreads), 0, stream,
-                         x, out, outer, R, inner);
+      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, 1, STR>), lgrid, dim3(kLsmThreads), 0, stream,
+                         x, out, d);
   } else {
     if (vec)
-      hipLaunchKernelGGL((lse_axis_kernel<RB, kVecW>), grid, dim3(kAxis0Threads), 0, stream, x,
-                         out, outer, R, inner);
+      hipLaunchKernelGGL((lse_axis_kernel<RB, kVecW, STR>), grid, dim3(kAxis0Threads), 0, stream, x,
+                         out, d);
     else
-      hipLaunchKernelGGL((lse_axis_kernel<RB, 1>), grid, dim3(kAxis0Threads), 0, stream, x, out,
-                         outer, R, inner);
+      hipLaunchKernelGGL((lse_axis_kernel<RB, 1, STR>), grid, dim3(kAxis0Threads), 0, stream, x, out,
+                         d);
   }
   return hipGetLastError();
 }
 
-template <int RBW, int W, int P, bool LSM>
-hipError_t launch_split(const float *x, float *out, int64_t outer, int64_t R, int64_t inner,
-                        hipStream_t stream) {
+template <int RBW, int W, int P, bool LSM, bool STR>
+hipError_t launch_split(const float *x, float *out, const AxisDims &d, hipStream_t stream) {
   constexpr int G = (LSE_AXIS_SPLIT_WAVES / P) > 1 ? (LSE_AXIS_SPLIT_WAVES / P) : 1;
-  const int64_t items = outer * (inner / W);
+  const int64_t items = d.outer * (d.inner / W);
   const dim3 grid((uint32_t)((items + kWave * G - 1) / (kWave * G)));
-  hipLaunchKernelGGL((axis_split_kernel<RBW, W, P, G, LSM>), grid, dim3(kWave * P * G), 0,
-                     stream, x, out, outer, R, inner);
+  hipLaunchKernelGGL((axis_split_kernel<RBW, W, P, G, LSM, STR>), grid, dim3(kWave * P * G), 0,
+                     stream, x, out, d);
   return hipGetLastError();
 }
 
-template <int RBW, bool LSM>
-hipError_t launch_split_p(int P, const float *x, float *out, int64_t outer, int64_t R,
-                          int64_t inner, hipStream_t stream) {
+template <int RBW, bool LSM, bool STR>
+hipError_t launch_split_p(int P, const float *x, float *out, const AxisDims &d,
+                          hipStream_t stream) {
   switch (P) {
-    case 1: return launch_split<RBW, kVecW, 1, LSM>(x, out, outer, R, inner, stream);
-    case 2: return launch_split<RBW, kVecW, 2, LSM>(x, out, outer, R, inner, stream);
-    case 4: return launch_split<RBW, kVecW, 4, LSM>(x, out, outer, R, inner, stream);
-    case 8: return launch_split<RBW, kVecW, 8, LSM>(x, out, outer, R, inner, stream);
-    default: return launch_split<RBW, kVecW, 16, LSM>(x, out, outer, R, inner, stream);
+    case 1: return launch_split<RBW, kVecW, 1, LSM, STR>(x, out, d, stream);
+    case 2: return launch_split<RBW, kVecW, 2, LSM, STR>(x, out, d, stream);
+    case 4: return launch_split<RBW, kVecW, 4, LSM, STR>(x, out, d, stream);
+    case 8: return launch_split<RBW, kVecW, 8, LSM, STR>(x, out, d, stream);
+    default: return launch_split<RBW, kVecW, 16, LSM, STR>(x, out, d, stream);
   }
 }
 
-template <bool LSM>
-hipError_t launch_axis(const float *x, float *out, int64_t outer, int64_t R, int64_t inner,
-                       hipStream_t stream) {
-  if (inner == 0 || outer == 0) return hipSuccess;
+template <bool LSM, bool STR>
+hipError_t launch_axis_t(const float *x, float *out, const AxisDims &d, hipStream_t stream) {
+  if (d.inner == 0 || d.outer == 0) return hipSuccess;
+  const int64_t R = d.R;
   const uintptr_t a = (uintptr_t)x | (uintptr_t)out;
-  const bool vec = (inner % kVecW == 0) && (a % 16 == 0);
+  // Every plane and output row must start on the vector boundary too.
+  const int64_t st = d.inner | d.xso | d.xsr | d.yso | (LSM ? d.ysr : 0);
+  const bool vec = (st % kVecW == 0) && (a % 16 == 0);
   constexpr int RBW = LSE_AXIS_SPLIT_RBW;
   if (vec && LSM && R >= LSE_AXIS_LSM_SPLIT_MINR) {
     // log_softmax: the fewest waves (a power of two up to 16) whose slices of
@@ -416,9 +437,9 @@ hipError_t launch_axis(const float *x, float *out, int64_t outer, int64_t R, int
     // R = 16 RBW.
     int P = 1;
     while (P < 16 && (int64_t)P * RBW < R) P *= 2;
-    return launch_split_p<RBW, true>(P, x, out, outer, R, inner, stream);
+    return launch_split_p<RBW, true, STR>(P, x, out, d, stream);
   }
-  const int64_t waves = (outer * (inner / kVecW) + kWave - 1) / kWave;
+  const int64_t waves = (d.outer * (d.inner / kVecW) + kWave - 1) / kWave;
   if (vec && !LSM && R >= LSE_AXIS_LSE_SPLIT_MINR && waves <= LSE_AXIS_LSE_SPLIT_MAXWAVES) {
     // logsumexp over long R with few outputs: one wave per 256 outputs would
     // leave most of the GPU idle, so P waves share each output run, each
@@ -426,39 +447,48 @@ hipError_t launch_axis(const float *x, float *out, int64_t outer, int64_t R, int
     int P = 1;
     while (P < 16 && waves * P < LSE_AXIS_LSE_SPLIT_TARGET) P *= 2;
     while (P > 1 && R < 8 * (int64_t)P) P /= 2;
-    if (P > 1) return launch_split_p<RBW, false>(P, x, out, outer, R, inner, stream);
+    if (P > 1) return launch_split_p<RBW, false, STR>(P, x, out, d, stream);
   }
-  if (R <= 4) return launch_rb<4, LSM>(x, out, outer, R, inner, vec, stream);
-  if (R <= 8 || LSE_AXIS0_RBMAX <= 8) return launch_rb<8, LSM>(x, out, outer, R, inner, vec, stream);
-  if (R <= 16 || LSE_AXIS0_RBMAX <= 16)
-    return launch_rb<16, LSM>(x, out, outer, R, inner, vec, stream);
+  if (R <= 4) return launch_rb<4, LSM, STR>(x, out, d, vec, stream);
+  if (R <= 8 || LSE_AXIS0_RBMAX <= 8) return launch_rb<8, LSM, STR>(x, out, d, vec, stream);
+  if (R <= 16 || LSE_AXIS0_RBMAX <= 16) return launch_rb<16, LSM, STR>(x, out, d, vec, stream);
   if (LSM && R > 32 && R <= 128) {
     // Unaligned log_softmax keeps all R values in registers for the write:
     // narrow the per-lane vector so that R x W stays at 128 values (2 outputs
     // per lane up to 64 planes, 1 up to 128) instead of reading x twice.
-    const int64_t items = outer * (R <= 64 && inner % 2 == 0 && a % 8 == 0 ? inner / 2 : inner);
+    const bool two = R <= 64 && st % 2 == 0 && a % 8 == 0;
+    const int64_t items = d.outer * (two ? d.inner / 2 : d.inner);
     const dim3 grid((uint32_t)((items + kLsmThreads - 1) / kLsmThreads));
-    if (R <= 64 && inner % 2 == 0 && a % 8 == 0)
-      hipLaunchKernelGGL((log_softmax_axis_kernel<64, 2>), grid, dim3(kLsmThreads), 0, stream,
-                         x, out, outer, R, inner);
+    if (two)
+      hipLaunchKernelGGL((log_softmax_axis_kernel<64, 2, STR>), grid, dim3(kLsmThreads), 0, stream,
+                         x, out, d);
     else
-      hipLaunchKernelGGL((log_softmax_axis_kernel<128, 1>), grid, dim3(kLsmThreads), 0,
-                         stream, x, out, outer, R, inner);
+      hipLaunchKernelGGL((log_softmax_axis_kernel<128, 1, STR>), grid, dim3(kLsmThreads), 0,
+                         stream, x, out, d);
     return hipGetLastError();
   }
-  return launch_rb<32, LSM>(x, out, outer, R, inner, vec, stream);
+  return launch_rb<32, LSM, STR>(x, out, d, vec, stream);
+}
+
+// Contiguous calls take instantiations whose strides derive from R and inner.
+template <bool LSM>
+hipError_t launch_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream) {
+  const bool contiguous = d.xsr == d.inner && (d.outer == 1 || d.xso == d.R * d.inner) &&
+                          (LSM ? (d.ysr == d.inner && (d.outer == 1 || d.yso == d.R * d.inner))
+                               : (d.outer == 1 || d.yso == d.inner));
+  return contiguous ? launch_axis_t<LSM, false>(x, out, d, stream)
+                    : launch_axis_t<LSM, true>(x, out, d, stream);
 }
 
 }  // namespace
 
-hipError_t launch_lse_axis(const float *x, float *out, int64_t outer, int64_t R, int64_t inner,
-                           hipStream_t stream) {
-  return launch_axis<false>(x, out, outer, R, inner, stream);
+hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream) {
+  return launch_axis<false>(x, out, d, stream);
 }
 
-hipError_t launch_log_softmax_axis(const float *x, float *y, int64_t outer, int64_t R,
-                                   int64_t inner, hipStream_t stream) {
-  return launch_axis<true>(x, y, outer, R, inner, stream);
+hipError_t launch_log_softmax_axis(const float *x, float *y, const AxisDims &d,
+                                   hipStream_t stream) {
+  return launch_axis<true>(x, y, d, stream);
 }
 
 }  // namespace lse

@@ -10,10 +10,17 @@
 namespace lse {
 
 // ---------------------------------------------------------------- case A
-hipError_t launch_lse_axis(const float *x, float *out, int64_t outer, int64_t R, int64_t inner,
-                           hipStream_t stream);
-hipError_t launch_log_softmax_axis(const float *x, float *y, int64_t outer, int64_t R,
-                                   int64_t inner, hipStream_t stream);
+// Geometry of an axis reduction, strides in elements: x[o * xso + r * xsr + j]
+// for o < outer, r < R, j < inner (j contiguous).  The logsumexp output is
+// out[o * yso + j]; the log_softmax output is y[o * yso + r * ysr + j].
+struct AxisDims {
+  int64_t outer, R, inner;
+  int64_t xso, xsr;
+  int64_t yso, ysr;
+};
+hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream);
+hipError_t launch_log_softmax_axis(const float *x, float *y, const AxisDims &d,
+                                   hipStream_t stream);
 
 // ---------------------------------------------------------------- case B
 // Tile geometry of the row kernels (overridable at build time for sweeps).
@@ -43,12 +50,12 @@ struct RowsPlan {
 RowsPlan rows_plan(int64_t cols);
 size_t rows_workspace_bytes(int64_t rows, int64_t cols);
 
-hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows,
-                                   int64_t cols, void *ws, hipStream_t stream,
+// Row r of x starts at x + r * ldx, of y at y + r * ldy (ld >= cols).
+hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
+                                   int64_t ldx, int64_t ldy, void *ws, hipStream_t stream,
                                    bool softmax = false);
-hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols,
-                                   int64_t chunk, void *partials,
-                                   hipStream_t stream);
+hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, int64_t ldx,
+                                   int64_t chunk, void *partials, hipStream_t stream);
 hipError_t launch_lse_rows_merge(const void *partials, int64_t rows,
                                  int64_t nchunks, float *row_lse,
                                  hipStream_t stream);

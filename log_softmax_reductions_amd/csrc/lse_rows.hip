@@ -242,7 +242,7 @@ __device__ __forceinline__ bool wave_wait_pairs(const uint64_t *pairs, int64_t k
 template <int VPL, bool VEC, bool SPLIT, bool SOFTMAX>
 __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
     const float *__restrict__ x, float *__restrict__ y, int64_t rows, int64_t cols,
-    int64_t nchunks, int64_t chunk, RowsWsHeader *__restrict__ hdr,
+    int64_t ldx, int64_t ldy, int64_t nchunks, int64_t chunk, RowsWsHeader *__restrict__ hdr,
     uint64_t *__restrict__ pairs, uint32_t spin_limit) {
   __shared__ float red[kNW];
   __shared__ int s_state;
@@ -258,8 +258,8 @@ __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
   }
   const int64_t c0 = c * chunk;
   const int64_t len = (cols - c0 < chunk) ? (cols - c0) : chunk;
-  const float *xr = x + row * cols + c0;
-  float *yr = y + row * cols + c0;
+  const float *xr = x + row * ldx + c0;
+  float *yr = y + row * ldy + c0;
 
   float v[VPL];
   load_chunk<VPL, VEC>(xr, len, v);
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
           const int64_t j0 = j * chunk;
           const int64_t lj = (cols - j0 < chunk) ? (cols - j0) : chunk;
           float hm, hs;
-          stream_chunk_pair(x + row * cols + j0, lj, red, hm, hs);
+          stream_chunk_pair(x + row * ldx + j0, lj, red, hm, hs);
           if (threadIdx.x == 0 && publish_pair_once(row_pairs + j, pack_pair(hm, hs)))
             __hip_atomic_fetch_add(&hdr->helped, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void clear_words_kernel(uint64_t *__restrict__
 // One workgroup per (row, chunk) of a chunk that fits the register tile.
 template <int VPL, bool VEC>
 __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_kernel(
-    const float *__restrict__ x, int64_t cols, int64_t nchunks, int64_t chunk,
+    const float *__restrict__ x, int64_t cols, int64_t ldx, int64_t nchunks, int64_t chunk,
     float2 *__restrict__ partials) {
   __shared__ float red[kNW];
   const int64_t t = blockIdx.x;
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_kernel(
   const int64_t c0 = c * chunk;
   const int64_t len = (cols - c0 < chunk) ? (cols - c0) : chunk;
   float v[VPL];
-  load_chunk<VPL, VEC>(x + row * cols + c0, len, v);
+  load_chunk<VPL, VEC>(x + row * ldx + c0, len, v);
   float m, s;
   chunk_pair<VPL>(v, red, m, s);
   if (threadIdx.x == 0) partials[t] = make_float2(m, s);
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_kernel(
 
 // Chunks longer than the register tile.
 __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_stream_kernel(
-    const float *__restrict__ x, int64_t cols, int64_t nchunks, int64_t chunk,
+    const float *__restrict__ x, int64_t cols, int64_t ldx, int64_t nchunks, int64_t chunk,
     float2 *__restrict__ partials) {
   __shared__ float red[kNW];
   const int64_t t = blockIdx.x;
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_stream_kernel(
   const int64_t c0 = c * chunk;
   const int64_t len = (cols - c0 < chunk) ? (cols - c0) : chunk;
   float m, s;
-  stream_chunk_pair(x + row * cols + c0, len, red, m, s);
+  stream_chunk_pair(x + row * ldx + c0, len, red, m, s);
   if (threadIdx.x == 0) partials[t] = make_float2(m, s);
 }
 
@@ -394,18 +394,19 @@ int vpl_for(int64_t len) {
 
 template <bool SPLIT, bool SOFTMAX>
 hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *y, int64_t rows,
-                           int64_t cols, int64_t nchunks, int64_t chunk, RowsWsHeader *hdr,
-                           uint64_t *pairs, uint32_t spin_limit, hipStream_t stream) {
+                           int64_t cols, int64_t ldx, int64_t ldy, int64_t nchunks,
+                           int64_t chunk, RowsWsHeader *hdr, uint64_t *pairs,
+                           uint32_t spin_limit, hipStream_t stream) {
 #define LSE_ROWS_CASE(V)                                                                      \
   case V:                                                                                     \
     if (vec)                                                                                  \
       hipLaunchKernelGGL((log_softmax_rows_kernel<V, true, SPLIT, SOFTMAX>), grid,            \
-                         dim3(kRowsThreads), 0, stream, x, y, rows, cols, nchunks, chunk,     \
-                         hdr, pairs, spin_limit);                                             \
+                         dim3(kRowsThreads), 0, stream, x, y, rows, cols, ldx, ldy, nchunks,  \
+                         chunk, hdr, pairs, spin_limit);                                      \
     else                                                                                      \
       hipLaunchKernelGGL((log_softmax_rows_kernel<V, false, SPLIT, SOFTMAX>), grid,           \
-                         dim3(kRowsThreads), 0, stream, x, y, rows, cols, nchunks, chunk,     \
-                         hdr, pairs, spin_limit);                                             \
+                         dim3(kRowsThreads), 0, stream, x, y, rows, cols, ldx, ldy, nchunks,  \
+                         chunk, hdr, pairs, spin_limit);                                      \
     break;
   switch (vpl) {
     LSE_ROWS_CASE(4)
@@ -421,14 +422,15 @@ hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *
 }
 
 template <bool SOFTMAX>
-hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols, void *ws,
-                            hipStream_t stream) {
+hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols, int64_t ldx,
+                            int64_t ldy, void *ws, hipStream_t stream) {
   const RowsPlan p = rows_plan(cols);
-  const bool vec = (cols % 4 == 0) && (p.chunk % 4 == 0) && ((uintptr_t)x % 16 == 0) &&
-                   ((uintptr_t)y % 16 == 0);
+  const bool vec = (cols % 4 == 0) && (p.chunk % 4 == 0) && (ldx % 4 == 0) &&
+                   (ldy % 4 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0);
   if (p.nchunks == 1) {
     return launch_rows_vpl<false, SOFTMAX>(vpl_for(cols), vec, dim3((uint32_t)rows), x, y, rows,
-                                           cols, 1, cols, nullptr, nullptr, 0u, stream);
+                                           cols, ldx, ldy, 1, cols, nullptr, nullptr, 0u,
+                                           stream);
   }
   auto *hdr = reinterpret_cast<RowsWsHeader *>(ws);
   auto *pairs = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws) + sizeof(RowsWsHeader));
@@ -439,7 +441,7 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
   if (e != hipSuccess) return e;
   return launch_rows_vpl<true, SOFTMAX>(vpl_for(p.chunk), vec,
                                         dim3((uint32_t)(rows * p.nchunks)), x, y, rows, cols,
-                                        p.nchunks, p.chunk, hdr, pairs,
+                                        ldx, ldy, p.nchunks, p.chunk, hdr, pairs,
                                         h_spin_limit.load(std::memory_order_relaxed), stream);
 }
 
@@ -468,32 +470,34 @@ size_t rows_workspace_bytes(int64_t rows, int64_t cols) {
 }
 
 hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
-                                   void *ws, hipStream_t stream, bool softmax) {
+                                   int64_t ldx, int64_t ldy, void *ws, hipStream_t stream,
+                                   bool softmax) {
   if (rows == 0) return hipSuccess;
-  return softmax ? launch_rows_mode<true>(x, y, rows, cols, ws, stream)
-                 : launch_rows_mode<false>(x, y, rows, cols, ws, stream);
+  return softmax ? launch_rows_mode<true>(x, y, rows, cols, ldx, ldy, ws, stream)
+                 : launch_rows_mode<false>(x, y, rows, cols, ldx, ldy, ws, stream);
 }
 
-hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, int64_t chunk,
-                                   void *partials, hipStream_t stream) {
+hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, int64_t ldx,
+                                   int64_t chunk, void *partials, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const int64_t nchunks = (cols + chunk - 1) / chunk;
   const dim3 grid((uint32_t)(rows * nchunks));
   auto *out = reinterpret_cast<float2 *>(partials);
   if (chunk > kRowsTile) {
     hipLaunchKernelGGL(lse_rows_partial_stream_kernel, grid, dim3(kRowsThreads), 0, stream, x,
-                       cols, nchunks, chunk, out);
+                       cols, ldx, nchunks, chunk, out);
     return hipGetLastError();
   }
-  const bool vec = (cols % 4 == 0) && (chunk % 4 == 0) && ((uintptr_t)x % 16 == 0);
+  const bool vec =
+      (cols % 4 == 0) && (chunk % 4 == 0) && (ldx % 4 == 0) && ((uintptr_t)x % 16 == 0);
 #define LSE_PART_CASE(V)                                                                       \
   case V:                                                                                      \
     if (vec)                                                                                   \
       hipLaunchKernelGGL((lse_rows_partial_kernel<V, true>), grid, dim3(kRowsThreads), 0,      \
-                         stream, x, cols, nchunks, chunk, out);                                \
+                         stream, x, cols, ldx, nchunks, chunk, out);                           \
     else                                                                                       \
       hipLaunchKernelGGL((lse_rows_partial_kernel<V, false>), grid, dim3(kRowsThreads), 0,     \
-                         stream, x, cols, nchunks, chunk, out);                                \
+                         stream, x, cols, ldx, nchunks, chunk, out);                           \
     break;
   switch (vpl_for(chunk)) {
     LSE_PART_CASE(4)

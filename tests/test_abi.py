@@ -37,7 +37,7 @@ def test_exports_match_header(lib):
     import subprocess
     from log_softmax_reductions_amd import _lib
     declared = declared_functions()
-    assert len(declared) == 16
+    assert len(declared) == 20
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -78,6 +78,38 @@ def test_axis_and_softmax_validation(lib):
     assert lib.softmax_rows(None, FAKE2, 4, 8, None, 0, None) == LSE_ERR_NULL
     assert lib.softmax_rows(FAKE, FAKE2, 16, 393216, None, 0, None) == LSE_ERR_WORKSPACE
     assert b"softmax_rows" in lib.lse_last_error()
+
+
+def test_strided_validation(lib):
+    ax, lsm = lib.lse_reduce_axis_strided, lib.log_softmax_axis_strided
+    # negative strides
+    assert ax(FAKE, FAKE2, 2, 3, 8, -1, 8, 8, None) == LSE_ERR_SHAPE
+    assert lsm(FAKE, FAKE2, 2, 3, 8, 24, 8, 24, -8, None) == LSE_ERR_SHAPE
+    # output planes that would collide: y stride over R smaller than inner
+    assert lsm(FAKE, FAKE2, 2, 3, 8, 24, 8, 24, 4, None) == LSE_ERR_SHAPE
+    assert b"overlap" in lib.lse_last_error()
+    # output outer blocks that would collide: (R - 1) * 8 + 8 = 24 > 20
+    assert lsm(FAKE, FAKE2, 2, 3, 8, 24, 8, 20, 8, None) == LSE_ERR_SHAPE
+    assert ax(FAKE, FAKE2, 2, 3, 8, 24, 8, 7, None) == LSE_ERR_SHAPE
+    # extents that overflow
+    assert ax(FAKE, FAKE2, 4, 3, 8, 1 << 61, 8, 8, None) == LSE_ERR_SHAPE
+    # padded x (plane pitch 10 > inner 8) whose range reaches the output
+    span_x = (2 - 1) * 40 + (3 - 1) * 10 + 8
+    assert ax(FAKE, ctypes.c_void_p(0x100000 + 4 * (span_x - 1)), 2, 3, 8, 40, 10, 8,
+              None) == LSE_ERR_OVERLAP
+    assert lsm(FAKE, FAKE, 2, 3, 8, 24, 8, 24, 8, None) == LSE_ERR_OVERLAP
+    assert lsm(None, FAKE2, 2, 3, 8, 24, 8, 24, 8, None) == LSE_ERR_NULL
+    assert ax(None, None, 0, 3, 8, 24, 8, 8, None) == LSE_OK        # empty: no-op
+    # rows with a leading dimension
+    rs = lib.log_softmax_rows_strided
+    assert rs(FAKE, FAKE2, 4, 8, 7, 8, None, 0, None) == LSE_ERR_SHAPE
+    assert rs(FAKE, FAKE2, 4, 8, 8, 7, None, 0, None) == LSE_ERR_SHAPE
+    assert rs(FAKE, FAKE2, 4, 8, 1 << 61, 8, None, 0, None) == LSE_ERR_SHAPE
+    # x rows every 16 floats, y rows 8 floats into x's first row: interleaved ranges
+    assert rs(FAKE, ctypes.c_void_p(0x100000 + 32), 4, 8, 16, 16, None, 0, None) == LSE_ERR_OVERLAP
+    assert lib.softmax_rows_strided(FAKE, FAKE2, 16, 393216, 393220, 393216, None, 0,
+                                    None) == LSE_ERR_WORKSPACE
+    assert rs(None, None, 0, 8, 8, 8, None, 0, None) == LSE_OK
 
 
 def test_rows_validation(lib):

@@ -34,3 +34,32 @@ def test_library_errors_become_exceptions():
     with pytest.raises(_lib.LseError, match="cols must be >= 1"):
         L.log_softmax_rows_plan(0)
     assert L.lse_rows_num_chunks(10, 3) == 4
+
+
+def test_strided_axis_geometry():
+    """Views map to (outer stride, R stride) with a contiguous inner run; the
+    layouts the strided entry points cannot express raise instead of copying."""
+    from log_softmax_reductions_amd import _strided_axis
+    x = torch.empty(3, 6, 5, 8)
+    assert _strided_axis(x, 1, "x") == (240, 40)
+    assert _strided_axis(x, 0, "x") == (0, 240)            # no outer dims
+    assert _strided_axis(x, 3, "x") == (8, 1)              # reduce the last dim
+    assert _strided_axis(x[:, 1:5], 1, "x") == (240, 40)   # a slice of planes
+    assert _strided_axis(x[:, :, 2], 1, "x") == (240, 40)  # a selected dim: (3, 6, 8)
+    xp = torch.empty(3, 6, 48)[:, :, :40].view(3, 6, 40)   # padded plane pitch 48
+    assert _strided_axis(xp, 1, "x") == (288, 48)
+    assert _strided_axis(torch.empty(1, 6, 1, 8), 1, "x") == (0, 8)   # size-1 dims ignored
+    with pytest.raises(ValueError, match="contiguous run"):
+        _strided_axis(x[..., :6], 1, "x")                  # inner dims (5, 6) do not merge
+    with pytest.raises(ValueError, match="contiguous run"):
+        _strided_axis(x.transpose(2, 3), 1, "x")
+    with pytest.raises(ValueError, match="one stride"):
+        _strided_axis(x.transpose(0, 1), 2, "x")           # outer dims (6, 3) do not merge
+
+
+def test_row_pitch():
+    from log_softmax_reductions_amd import _ld
+    assert _ld(torch.empty(4, 128)[:, :100], "x") == 128
+    assert _ld(torch.empty(1, 100), "x") == 100
+    with pytest.raises(ValueError, match="contiguous"):
+        _ld(torch.empty(100, 4).t(), "x")
