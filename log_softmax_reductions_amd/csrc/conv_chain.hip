@@ -125,12 +125,12 @@ struct XRegs {
 };
 
 __device__ __forceinline__ void load_x(const ChainArgs &a, int64_t n, int h0, int w0,
-                                       XRegs &xr) {
+                                       XRegs &xr, int tid) {
   const float *xn = a.x + n * (int64_t)kCin * a.H * a.W;
   const bool vec = ((a.W & 3) == 0) && (((uintptr_t)a.x & 15) == 0);
 #pragma unroll
   for (int it = 0; it < kStageIters; ++it) {
-    const int f = threadIdx.x + it * kThreads;
+    const int f = tid + it * kThreads;
     float4 val = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (f < kStageF4) {
       const int row = f / kF4PerRow, c4 = f - row * kF4PerRow;
@@ -152,27 +152,28 @@ __device__ __forceinline__ void load_x(const ChainArgs &a, int64_t n, int h0, in
   }
 }
 
-__device__ __forceinline__ void store_x(const XRegs &xr, float *xs) {
+__device__ __forceinline__ void store_x(const XRegs &xr, float *xs, int tid) {
 #pragma unroll
   for (int it = 0; it < kStageIters; ++it) {
-    const int f = threadIdx.x + it * kThreads;
+    const int f = tid + it * kThreads;
     if (f < kStageF4) *reinterpret_cast<float4 *>(xs + 4 * f) = xr.v[it];
   }
 }
 
 // W (64 x 72, contiguous) through registers into LDS rows of kWStride floats;
 // the loads do not depend on the tile, so they are issued first.
-constexpr int kWIters = (kWF4 + kThreads - 1) / kThreads;                // 5
-
+template <int NT>
 struct WRegs {
-  float4 v[kWIters];
+  static constexpr int kIters = (kWF4 + NT - 1) / NT;   // 5 for 256 threads, 3 for 512
+  float4 v[kIters];
 };
 
-__device__ __forceinline__ void load_w(const float *__restrict__ w, WRegs &wr) {
+template <int NT>
+__device__ __forceinline__ void load_w(const float *__restrict__ w, WRegs<NT> &wr) {
   const bool vec = ((uintptr_t)w & 15) == 0;
 #pragma unroll
-  for (int it = 0; it < kWIters; ++it) {
-    const int f = threadIdx.x + it * kThreads;
+  for (int it = 0; it < WRegs<NT>::kIters; ++it) {
+    const int f = threadIdx.x + it * NT;
     float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (f < kWF4) {
       if (vec) {
@@ -185,10 +186,11 @@ __device__ __forceinline__ void load_w(const float *__restrict__ w, WRegs &wr) {
   }
 }
 
-__device__ __forceinline__ void store_w(const WRegs &wr, float *wl) {
+template <int NT>
+__device__ __forceinline__ void store_w(const WRegs<NT> &wr, float *wl) {
 #pragma unroll
-  for (int it = 0; it < kWIters; ++it) {
-    const int f = threadIdx.x + it * kThreads;
+  for (int it = 0; it < WRegs<NT>::kIters; ++it) {
+    const int f = threadIdx.x + it * NT;
     if (f < kWF4) {
       const int o = f / (kKdim / 4), c4 = f - o * (kKdim / 4);
       *reinterpret_cast<float4 *>(wl + o * kWStride + 4 * c4) = wr.v[it];
@@ -265,9 +267,10 @@ struct ChainLds {
   float mu[16], rs[16];
 };
 
-__device__ __forceinline__ void tile_valid(const ChainArgs &a, int tile, bool (&valid)[kNB]) {
+__device__ __forceinline__ void tile_valid(const ChainArgs &a, int tile, bool (&valid)[kNB],
+                                           int wave) {
   const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
-  const int wave = threadIdx.x / kWave, li = threadIdx.x % 16;
+  const int li = threadIdx.x % 16;
   const int h = th * kTileH + wave / 2, w = tw * kTileW + (wave % 2) * 64 + li;
 #pragma unroll
   for (int blk = 0; blk < kNB; ++blk) valid[blk] = (h < a.Ho) && (w + 16 * blk < a.Wo);
@@ -326,29 +329,48 @@ __device__ __forceinline__ void publish_tile_stats(const ChainArgs &a, int64_t n
 // ends with a barrier).  Lane l reads words l, l + 64, ... of the sample's
 // (tile, group) block, so all its words belong to group l % G.  Per lane, in
 // fp64: C = sum n_j, S1 = sum n_j mean_j, S2 = sum (M2_j + n_j mean_j^2); per
-// group mean = S1 / C and M2 = S2 - C mean^2.  Up to 16 words per lane stay
-// in registers from the last poll; larger samples re-read them.
+// group mean = S1 / C and M2 = S2 - C mean^2.
+template <class Lds>
 __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bool write_global,
-                                               ChainLds &L) {
+                                               Lds &L) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if (wave == 0) {
     const int qpg = 16 / a.G;
     const uint64_t *ws = a.stats + n * a.tiles * a.G;
     const int words = a.tiles * a.G;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    constexpr int kHeld = 16;
-    uint64_t held[kHeld];
+    // Every poll reads all of the lane's words (8 loads in flight at a time)
+    // and sums the ones present; the sums of the first poll that finds none
+    // missing are the sample's, as a written word never changes.
+    constexpr int kBatch = 8;
+    double C, S1, S2;
     bool ok = true;
     for (uint32_t it = 0;; ++it) {
+      C = S1 = S2 = 0.0;
       bool missing = false;
+      for (int base = lane; base < words; base += kBatch * kWave) {
+        uint64_t wd[kBatch];
 #pragma unroll
-      for (int i = 0; i < kHeld; ++i) {
-        const int idx = lane + kWave * i;
-        held[i] = (idx < words) ? load_pair_agent(ws + idx) : 1ull;
-        missing |= (held[i] == 0);
+        for (int j = 0; j < kBatch; ++j) {
+          const int idx = base + kWave * j;
+          wd[j] = (idx < words) ? load_pair_agent(ws + idx) : 0ull;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int idx = base + kWave * j;
+          if (idx < words) {
+            if (wd[j] == 0) {
+              missing = true;
+            } else {
+              const double c = tile_count(a, idx >> a.log2G, qpg);  // G is a power of 2
+              const double m = (double)bitsf((uint32_t)wd[j]);
+              C += c;
+              S1 += c * m;
+              S2 += -(double)bitsf((uint32_t)(wd[j] >> 32)) + c * m * m;
+            }
+          }
+        }
       }
-      for (int idx = lane + kWave * kHeld; idx < words; idx += kWave)
-        missing |= (load_pair_agent(ws + idx) == 0);
       if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
       if (it >= a.spin_limit || __builtin_amdgcn_s_memrealtime() - t0 > kChainWaitTicks) {
         ok = false;
@@ -356,20 +378,6 @@ __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bo
       }
       __builtin_amdgcn_s_sleep(8);
     }
-    double C = 0.0, S1 = 0.0, S2 = 0.0;
-    auto add = [&](int idx, uint64_t wd) {
-      const double c = tile_count(a, idx >> a.log2G, qpg);  // G is a power of 2
-      const double m = (double)bitsf((uint32_t)wd);
-      C += c;
-      S1 += c * m;
-      S2 += -(double)bitsf((uint32_t)(wd >> 32)) + c * m * m;
-    };
-#pragma unroll
-    for (int i = 0; i < kHeld; ++i) {
-      const int idx = lane + kWave * i;
-      if (idx < words) add(idx, held[i]);
-    }
-    for (int idx = lane + kWave * kHeld; idx < words; idx += kWave) add(idx, load_pair_agent(ws + idx));
     L.mrg[lane][0] = C;
     L.mrg[lane][1] = S1;
     L.mrg[lane][2] = S2;
@@ -401,10 +409,11 @@ __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bo
 // Epilogue of one tile on its accumulators: GroupNorm and the affine folded
 // into one multiply-add per channel, tanh, hardswish, residual, and the LSE
 // over the 64 channels of each pixel; one float written per valid pixel.
+template <class Lds>
 __device__ __forceinline__ void tile_epilogue(const ChainArgs &a, int64_t n, int tile,
                                               const f32x4 (&acc)[kNB][kMT],
-                                              const bool (&valid)[kNB], const ChainLds &L) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+                                              const bool (&valid)[kNB], const Lds &L, int wave) {
+  const int lane = threadIdx.x % kWave;
   const int li = lane % 16, q = lane / 16;
   const int qpg = 16 / a.G;
   const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
@@ -464,7 +473,7 @@ void conv_chain_kernel(ChainArgs a) {
   __shared__ float wl[kCout * kWStride];
   __shared__ ChainLds L;
   __shared__ uint32_t s_ticket;
-  WRegs wr;
+  WRegs<kThreads> wr;
   load_w(a.w, wr);  // in flight while the ticket is claimed
   if (threadIdx.x == 0)
     s_ticket = __hip_atomic_fetch_add(&a.hdr->ticket, 1u, __ATOMIC_RELAXED,
@@ -488,28 +497,201 @@ void conv_chain_kernel(ChainArgs a) {
   origin(hasB ? tB : tA, hB, wB);
 
   XRegs xa, xb;
-  load_x(a, n, hA, wA, xa);
-  if (hasB) load_x(a, n, hB, wB, xb);
+  load_x(a, n, hA, wA, xa, threadIdx.x);
+  if (hasB) load_x(a, n, hB, wB, xb, threadIdx.x);
   store_w(wr, wl);
-  store_x(xa, xs);
+  store_x(xa, xs, threadIdx.x);
   __syncthreads();
 
   f32x4 accA[kNB][kMT], accB[kNB][kMT];
   bool vA[kNB], vB[kNB];
   conv_tile(a, xs, wl, pr, pc0, accA);
-  tile_valid(a, tA, vA);
+  tile_valid(a, tA, vA, wave);
   publish_tile_stats(a, n, tA, accA, vA, L);  // ends with a barrier: xs is free again
   if (hasB) {
-    store_x(xb, xs);
+    store_x(xb, xs, threadIdx.x);
     __syncthreads();
     conv_tile(a, xs, wl, pr, pc0, accB);
-    tile_valid(a, tB, vB);
+    tile_valid(a, tB, vB, wave);
     publish_tile_stats(a, n, tB, accB, vB, L);
   }
   (void)lane;
   wait_and_merge(a, n, tA == 0, L);
-  tile_epilogue(a, n, tA, accA, vA, L);
-  if (hasB) tile_epilogue(a, n, tB, accB, vB, L);
+  tile_epilogue(a, n, tA, accA, vA, L, wave);
+  if (hasB) tile_epilogue(a, n, tB, accB, vB, L, wave);
+}
+
+#ifndef LSE_CHAIN_PAIR_WAVES_PER_EU
+#define LSE_CHAIN_PAIR_WAVES_PER_EU 4
+#endif
+#ifndef LSE_CHAIN_WIDE
+#define LSE_CHAIN_WIDE 1   // 1: the 8-wave pair kernel below; 0: the 4-wave pair kernel above
+#endif
+
+// LDS scratch of the 8-wave pair workgroup besides the x and W tiles.
+struct PairLds {
+  float qred[2 * kThreads / kWave][16];
+  float gmean[2][16];
+  double mrg[kWave][3];
+  float mu[16], rs[16];
+  alignas(16) float sc[kCout];  // per channel: z = conv * sc + sh (read 4 at a time)
+  alignas(16) float sh[kCout];
+};
+
+// GroupNorm and the affine folded into one multiply-add per channel, from the
+// merged statistics (threads 0..63, one channel each; then a barrier).
+__device__ __forceinline__ void fold_affine(const ChainArgs &a, PairLds &L) {
+  if (threadIdx.x < kCout) {
+    const int c = threadIdx.x, g = (c / 4) / (16 / a.G);
+    const float ga = a.gamma ? a.gamma[c] : 1.0f;
+    const float be = a.beta ? a.beta[c] : 0.0f;
+    L.sc[c] = L.rs[g] * ga;
+    L.sh[c] = be - L.mu[g] * L.rs[g] * ga;
+  }
+  __syncthreads();
+}
+
+// tile_epilogue with the per-channel scale and shift read from LDS (four
+// consecutive channels per read) instead of held in 32 registers.
+__device__ __forceinline__ void tile_epilogue_lds(const ChainArgs &a, int64_t n, int tile,
+                                                  const f32x4 (&acc)[kNB][kMT],
+                                                  const bool (&valid)[kNB], const PairLds &L,
+                                                  int wave) {
+  const int lane = threadIdx.x % kWave;
+  const int li = lane % 16, q = lane / 16;
+  const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
+  const int h = th * kTileH + wave / 2, w0 = tw * kTileW + (wave % 2) * 64;
+#pragma unroll
+  for (int blk = 0; blk < kNB; ++blk) {
+    float u[kMT][4];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+      const f32x4 sc = *reinterpret_cast<const f32x4 *>(&L.sc[16 * t + 4 * q]);
+      const f32x4 sh = *reinterpret_cast<const f32x4 *>(&L.sh[16 * t + 4 * q]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = acc[blk][t][r];
+        u[t][r] = v + hardswish_of_tanh(tanh_fast(v * sc[r] + sh[r]));
+        m = fmaxf(m, u[t][r]);
+      }
+    }
+    const float M = across_quads(m, OpMax{});
+    const float c = is_finite(M) ? M : 0.0f;
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kMT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s += exp_base2(u[t][r] - c);
+    const float S = across_quads(s, OpSum{});
+    if (q == 0 && valid[blk])
+      a.out[(n * a.Ho + h) * (int64_t)a.Wo + w0 + 16 * blk + li] = M + logf(S);
+  }
+}
+
+// Per-group (mean, M2) of both tiles of a pair, one team of 4 waves per tile
+// (team 1 idle when the pair has no second tile).  Wave 0 reduces tile A's
+// quads, wave 1 tile B's.  Called by the whole workgroup; ends with a barrier.
+__device__ __forceinline__ void publish_pair_stats(const ChainArgs &a, int64_t n, int tA, int tB,
+                                                   bool hasB, int team, bool active,
+                                                   const f32x4 (&acc)[kNB][kMT],
+                                                   const bool (&valid)[kNB], PairLds &L) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int li = lane % 16, q = lane / 16;
+  const int qpg = 16 / a.G;
+  for (int stage = 0; stage < 2; ++stage) {
+    if (active) {
+      float qv[kMT];
+#pragma unroll
+      for (int t = 0; t < kMT; ++t) {
+        const float mu = stage ? L.gmean[team][(4 * t + q) / qpg] : 0.0f;
+        float sacc = 0.0f;
+#pragma unroll
+        for (int blk = 0; blk < kNB; ++blk) {
+          if (valid[blk]) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float d = acc[blk][t][r] - mu;
+              sacc += stage ? d * d : d;
+            }
+          }
+        }
+        qv[t] = row16_sum(sacc);
+      }
+      if (li == 0) {
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) L.qred[wave][4 * t + q] = qv[t];
+      }
+    }
+    __syncthreads();
+    const int rt = wave;  // wave 0 reduces team 0, wave 1 team 1
+    if (rt < 2 && lane < a.G && (rt == 0 || hasB)) {
+      const int g = lane, tile = rt ? tB : tA;
+      float tot = 0.0f;
+      for (int w = 4 * rt; w < 4 * rt + 4; ++w)
+        for (int Q = g * qpg; Q < (g + 1) * qpg; ++Q) tot += L.qred[w][Q];
+      if (stage == 0) {
+        L.gmean[rt][g] = tot / (float)tile_count(a, tile, qpg);
+      } else {
+        __hip_atomic_store(a.stats + (n * a.tiles + tile) * a.G + g, pack_stats(L.gmean[rt][g], tot),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// One workgroup of 8 waves = a pair of tiles (A = 2p, B = 2p + 1) of one
+// sample, handed out by ticket in sample order.  Waves 0-3 stage and convolve
+// tile A, waves 4-7 tile B, at the same time; each wave holds the 64
+// accumulators of its quarter tile, so four waves fit on a SIMD and one
+// wave's MFMAs overlap others' staging, waiting and epilogue.  W staging and
+// the wait for the sample's statistics are paid once per pair.
+__global__ __launch_bounds__(2 * kThreads)
+__attribute__((amdgpu_waves_per_eu(LSE_CHAIN_PAIR_WAVES_PER_EU)))
+void conv_chain_pair_kernel(ChainArgs a) {
+  __shared__ float xs[2][kCin * kLdsH * kLdsW];
+  __shared__ float wl[kCout * kWStride];
+  __shared__ PairLds L;
+  __shared__ uint32_t s_ticket;
+  WRegs<2 * kThreads> wr;
+  load_w(a.w, wr);  // in flight while the ticket is claimed
+  if (threadIdx.x == 0)
+    s_ticket = __hip_atomic_fetch_add(&a.hdr->ticket, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t pairs = (uint32_t)(a.tiles + 1) / 2;
+  const int64_t n = s_ticket / pairs;
+  const int p = (int)(s_ticket - (uint32_t)n * pairs);
+  const int tA = 2 * p, tB = 2 * p + 1;
+  const bool hasB = tB < a.tiles;  // uniform
+
+  const int team = __builtin_amdgcn_readfirstlane(threadIdx.x / kThreads);  // 0: A, 1: B
+  const int tid = threadIdx.x - team * kThreads;                           // within the team
+  const int twave = tid / kWave;
+  const bool active = team == 0 || hasB;                                   // uniform per wave
+  const int tile = team ? tB : tA;
+  const int pr = twave / 2, pc0 = (twave % 2) * 64;
+
+  XRegs xr;
+  if (active) {
+    const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
+    load_x(a, n, th * kTileH, tw * kTileW, xr, tid);
+  }
+  store_w(wr, wl);
+  if (active) store_x(xr, xs[team], tid);
+  __syncthreads();
+
+  f32x4 acc[kNB][kMT];
+  bool valid[kNB];
+  if (active) {
+    conv_tile(a, xs[team], wl, pr, pc0, acc);
+    tile_valid(a, tile, valid, twave);
+  }
+  publish_pair_stats(a, n, tA, tB, hasB, team, active, acc, valid, L);
+  wait_and_merge(a, n, tA == 0, L);
+  fold_affine(a, L);
+  if (active) tile_epilogue_lds(a, n, tile, acc, valid, L, twave);
 }
 
 // Clear n 64-bit words (the ticket / error header and the statistics words).
@@ -573,8 +755,12 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t pairs = (L.tiles + 1) / 2;
-  hipLaunchKernelGGL(conv_chain_kernel, dim3((uint32_t)(N * pairs)), dim3(kThreads), 0, stream,
-                     a);
+  if (LSE_CHAIN_WIDE)
+    hipLaunchKernelGGL(conv_chain_pair_kernel, dim3((uint32_t)(N * pairs)), dim3(2 * kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(conv_chain_kernel, dim3((uint32_t)(N * pairs)), dim3(kThreads), 0, stream,
+                       a);
   return hipGetLastError();
 }
 
