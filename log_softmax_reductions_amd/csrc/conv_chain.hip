@@ -9,14 +9,14 @@
 // epilogue over the materialised conv output.  Here the conv output is never
 // written to memory and the conv runs once:
 //
-//   each workgroup takes a pair of 2 x 128 pixel tiles of one sample (pairs
-//   handed out by an atomic ticket, in sample order), stages x and W in
-//   LDS, runs the conv of each tile on MFMA into registers (the second
-//   tile's x loads in flight during the first tile's MFMAs) and publishes
-//   each tile's per-group (mean, M2); it then waits until every tile of its
-//   sample has published, merges the sample's statistics in fp64, and runs
-//   normalise, tanh, hardswish, residual and the 64-channel logsumexp on the
-//   accumulators it still holds, writing one float per pixel.
+//   each workgroup of 8 waves takes a pair of 2 x 128 pixel tiles of one
+//   sample (pairs handed out by an atomic ticket, in sample order); waves 0-3
+//   stage and convolve one tile, waves 4-7 the other, on MFMA into registers
+//   (64 accumulators per lane, so four waves fit on a SIMD); the pair
+//   publishes each tile's per-group (mean, M2), waits until every tile of
+//   its sample has published, merges the sample's statistics in fp64, and
+//   runs normalise, tanh, hardswish, residual and the 64-channel logsumexp
+//   on the accumulators it still holds, writing one float per pixel.
 //
 // The wait is deadlock-free because tickets are claimed only by running
 // workgroups, in order, and every workgroup publishes before it waits: the
@@ -97,19 +97,20 @@ __device__ __forceinline__ float across_quads(float v, Op op) {
   return op(bitsf(q[0]), bitsf(q[1]));
 }
 
-// tanh(z) = 1 - 2 / (exp(2z) + 1): exp overflow gives 1, underflow -1, so the
-// result always lies in [-1, 1]; the absolute error is a few 1e-7, far inside
-// the chain's tolerance.
-__device__ __forceinline__ float tanh_fast(float z) {
-  const float e = __builtin_amdgcn_exp2f(z * (2.0f * kLog2e));
-  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+// tanh(z) = 1 - 2 / (exp(2z) + 1), taking y = 2 log2(e) z (the scale is folded
+// into the normalisation's multiply-add): exp overflow gives 1, underflow -1,
+// so the result always lies in [-1, 1]; the absolute error is a few 1e-7, far
+// inside the chain's tolerance.
+__device__ __forceinline__ float tanh_of_scaled(float y) {
+  const float e = __builtin_amdgcn_exp2f(y);
+  return fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
 }
 
 // hardswish(t) = t * min(max(t + 3, 0), 6) / 6.  The chain only applies it to
 // tanh outputs, t in [-1, 1], where t + 3 lies in [2, 4] and the clamp never
-// binds: there it is exactly t * (t + 3) / 6.
+// binds: there it is t * (t + 3) / 6 = t * (t / 6 + 1 / 2).
 __device__ __forceinline__ float hardswish_of_tanh(float t) {
-  return t * (t + 3.0f) * (1.0f / 6.0f);
+  return t * fmaf(t, 1.0f / 6.0f, 0.5f);
 }
 
 // The x tile of sample n at (h0, w0): 8 channels x 4 rows x 132 columns.  It
@@ -242,8 +243,7 @@ __device__ __forceinline__ uint64_t pack_stats(float mean, float m2) {
 // quads per group, times the tile's valid pixels.  Only the last tile row and
 // the last tile column can be partial, so no division is needed when the
 // sample is one tile wide.
-__device__ __forceinline__ double tile_count(const ChainArgs &a, int j, int qpg) {
-  const int tiles_h = a.tiles / a.tiles_w;
+__device__ __forceinline__ double tile_count(const ChainArgs &a, int j, int qpg, int tiles_h) {
   int th, tw;
   if (a.tiles_w == 1) {
     th = j;
@@ -259,14 +259,6 @@ __device__ __forceinline__ double tile_count(const ChainArgs &a, int j, int qpg)
 
 constexpr uint64_t kChainWaitTicks = 10000000ull;  // 0.1 s of the 100 MHz counter
 
-// LDS scratch of one workgroup besides the x and W tiles.
-struct ChainLds {
-  float qred[kThreads / kWave][16];
-  float gmean[16];
-  double mrg[kWave][3];
-  float mu[16], rs[16];
-};
-
 __device__ __forceinline__ void tile_valid(const ChainArgs &a, int tile, bool (&valid)[kNB],
                                            int wave) {
   const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
@@ -276,277 +268,135 @@ __device__ __forceinline__ void tile_valid(const ChainArgs &a, int tile, bool (&
   for (int blk = 0; blk < kNB; ++blk) valid[blk] = (h < a.Ho) && (w + 16 * blk < a.Wo);
 }
 
-// Per-group (mean, M2 about the tile mean) of one tile, published as one word
-// per group.  Called by the whole workgroup; ends with a barrier.
-__device__ __forceinline__ void publish_tile_stats(const ChainArgs &a, int64_t n, int tile,
-                                                   const f32x4 (&acc)[kNB][kMT],
-                                                   const bool (&valid)[kNB], ChainLds &L) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int li = lane % 16, q = lane / 16;
-  const int qpg = 16 / a.G;  // channel quads per group
-  const float cnt = (float)tile_count(a, tile, qpg);
-  for (int stage = 0; stage < 2; ++stage) {
-    float qv[kMT];
-#pragma unroll
-    for (int t = 0; t < kMT; ++t) {
-      const float mu = stage ? L.gmean[(4 * t + q) / qpg] : 0.0f;
-      float sacc = 0.0f;
-#pragma unroll
-      for (int blk = 0; blk < kNB; ++blk) {
-        if (valid[blk]) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float d = acc[blk][t][r] - mu;
-            sacc += stage ? d * d : d;
-          }
-        }
-      }
-      qv[t] = row16_sum(sacc);
-    }
-    if (li == 0) {
-#pragma unroll
-      for (int t = 0; t < kMT; ++t) L.qred[wave][4 * t + q] = qv[t];
-    }
-    __syncthreads();
-    if (threadIdx.x < a.G) {
-      const int g = threadIdx.x;
-      float tot = 0.0f;
-      for (int w = 0; w < kThreads / kWave; ++w)
-        for (int Q = g * qpg; Q < (g + 1) * qpg; ++Q) tot += L.qred[w][Q];
-      if (stage == 0) {
-        L.gmean[g] = tot / cnt;
-      } else {
-        __hip_atomic_store(a.stats + (n * a.tiles + tile) * a.G + g, pack_stats(L.gmean[g], tot),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-  }
-}
-
 // Wait until every tile of sample n has published, then merge the sample's
-// statistics into L.mu / L.rs (wave 0; the whole workgroup calls this and it
-// ends with a barrier).  Lane l reads words l, l + 64, ... of the sample's
-// (tile, group) block, so all its words belong to group l % G.  Per lane, in
-// fp64: C = sum n_j, S1 = sum n_j mean_j, S2 = sum (M2_j + n_j mean_j^2); per
-// group mean = S1 / C and M2 = S2 - C mean^2.
-template <class Lds>
+// statistics into L.mu / L.rs; called by the whole workgroup (NT threads),
+// ends with a barrier.  Thread t polls words t, t + NT, ... of the sample's
+// (tile, group) block: one round trip per poll for up to 2 NT words, whose
+// values stay in registers.  A poll's verdict is the OR of one ballot per
+// wave through LDS, so every wave leaves the loop together.  Then, per thread
+// in fp64: C = sum n_j, S1 = sum n_j mean_j, S2 = sum (M2_j + n_j mean_j^2)
+// over its words, which all belong to group t % G; lanes of a wave with the
+// same group are combined by xor shuffles, the waves in LDS (fixed order:
+// the result is deterministic); per group mean = S1 / C, M2 = S2 - C mean^2.
+template <int NT, class Lds>
 __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bool write_global,
                                                Lds &L) {
+  constexpr int kPer = 2;
+  constexpr int kWaves = NT / kWave;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  if (wave == 0) {
-    const int qpg = 16 / a.G;
-    const uint64_t *ws = a.stats + n * a.tiles * a.G;
-    const int words = a.tiles * a.G;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    // Every poll reads all of the lane's words (8 loads in flight at a time)
-    // and sums the ones present; the sums of the first poll that finds none
-    // missing are the sample's, as a written word never changes.
-    constexpr int kBatch = 8;
-    double C, S1, S2;
-    bool ok = true;
-    for (uint32_t it = 0;; ++it) {
-      C = S1 = S2 = 0.0;
-      bool missing = false;
-      for (int base = lane; base < words; base += kBatch * kWave) {
-        uint64_t wd[kBatch];
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int idx = base + kWave * j;
-          wd[j] = (idx < words) ? load_pair_agent(ws + idx) : 0ull;
-        }
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int idx = base + kWave * j;
-          if (idx < words) {
-            if (wd[j] == 0) {
-              missing = true;
-            } else {
-              const double c = tile_count(a, idx >> a.log2G, qpg);  // G is a power of 2
-              const double m = (double)bitsf((uint32_t)wd[j]);
-              C += c;
-              S1 += c * m;
-              S2 += -(double)bitsf((uint32_t)(wd[j] >> 32)) + c * m * m;
-            }
-          }
-        }
-      }
-      if (__builtin_amdgcn_ballot_w64(missing) == 0) break;
-      if (it >= a.spin_limit || __builtin_amdgcn_s_memrealtime() - t0 > kChainWaitTicks) {
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(8);
-    }
-    L.mrg[lane][0] = C;
-    L.mrg[lane][1] = S1;
-    L.mrg[lane][2] = S2;
-    __builtin_amdgcn_wave_barrier();
-    if (lane < a.G) {
-      double Cg = 0.0, S1g = 0.0, S2g = 0.0;
-      for (int l = lane; l < kWave; l += a.G) {
-        Cg += L.mrg[l][0];
-        S1g += L.mrg[l][1];
-        S2g += L.mrg[l][2];
-      }
-      const double MU = S1g / Cg;
-      const double M2 = fmax(S2g - Cg * MU * MU, 0.0);
-      float fm = (float)MU, fr = (float)(1.0 / sqrt(M2 / Cg + (double)a.eps));
-      if (!ok) fm = fr = __builtin_nanf("");
-      L.mu[lane] = fm;
-      L.rs[lane] = fr;
-      if (write_global) {
-        a.mean[n * a.G + lane] = fm;
-        a.rstd[n * a.G + lane] = fr;
-      }
-      if (!ok && lane == 0)
-        __hip_atomic_store(&a.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __syncthreads();
-}
-
-// Epilogue of one tile on its accumulators: GroupNorm and the affine folded
-// into one multiply-add per channel, tanh, hardswish, residual, and the LSE
-// over the 64 channels of each pixel; one float written per valid pixel.
-template <class Lds>
-__device__ __forceinline__ void tile_epilogue(const ChainArgs &a, int64_t n, int tile,
-                                              const f32x4 (&acc)[kNB][kMT],
-                                              const bool (&valid)[kNB], const Lds &L, int wave) {
-  const int lane = threadIdx.x % kWave;
-  const int li = lane % 16, q = lane / 16;
   const int qpg = 16 / a.G;
-  const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
-  const int h = th * kTileH + wave / 2, w0 = tw * kTileW + (wave % 2) * 64;
-  float sc[kMT][4], sh[kMT][4];
+  const int tiles_h = a.tiles / a.tiles_w;
+  const uint64_t *ws = a.stats + n * a.tiles * a.G;
+  const int words = a.tiles * a.G;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  uint64_t wd[kPer];
+  bool ok = true;
+  for (uint32_t it = 0;; ++it) {
+    bool missing = false;
 #pragma unroll
-  for (int t = 0; t < kMT; ++t) {
-    const int g = (4 * t + q) / qpg;
-    const float mu = L.mu[g], rs = L.rs[g];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = 16 * t + 4 * q + r;
-      const float ga = a.gamma ? a.gamma[c] : 1.0f;
-      const float be = a.beta ? a.beta[c] : 0.0f;
-      sc[t][r] = rs * ga;
-      sh[t][r] = be - mu * rs * ga;
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = threadIdx.x + NT * j;
+      wd[j] = (idx < words) ? load_pair_agent(ws + idx) : 1ull;
+      missing |= (wd[j] == 0);
     }
-  }
-#pragma unroll
-  for (int blk = 0; blk < kNB; ++blk) {
-    float u[kMT][4];
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int t = 0; t < kMT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = acc[blk][t][r];
-        const float z = v * sc[t][r] + sh[t][r];
-        u[t][r] = v + hardswish_of_tanh(tanh_fast(z));
-        m = fmaxf(m, u[t][r]);
-      }
-    const float M = across_quads(m, OpMax{});
-    const float c = is_finite(M) ? M : 0.0f;
-    float s = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kMT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s += exp_base2(u[t][r] - c);
-    const float S = across_quads(s, OpSum{});
-    if (q == 0 && valid[blk])
-      a.out[(n * a.Ho + h) * (int64_t)a.Wo + w0 + 16 * blk + li] = M + logf(S);
-  }
-}
-
-#ifndef LSE_CHAIN_WAVES_PER_EU
-#define LSE_CHAIN_WAVES_PER_EU 2
-#endif
-
-// One workgroup = a pair of vertically adjacent tiles (A = 2p, B = 2p + 1) of
-// one sample, handed out by ticket in sample order.  B's x loads are in
-// flight while A is on the MFMAs; both tiles publish their statistics before
-// the workgroup waits for its sample, and W staging, the wait and the merge
-// are paid once per pair.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LSE_CHAIN_WAVES_PER_EU)))
-void conv_chain_kernel(ChainArgs a) {
-  __shared__ float xs[kCin * kLdsH * kLdsW];
-  __shared__ float wl[kCout * kWStride];
-  __shared__ ChainLds L;
-  __shared__ uint32_t s_ticket;
-  WRegs<kThreads> wr;
-  load_w(a.w, wr);  // in flight while the ticket is claimed
-  if (threadIdx.x == 0)
-    s_ticket = __hip_atomic_fetch_add(&a.hdr->ticket, 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const uint32_t pairs = (uint32_t)(a.tiles + 1) / 2;
-  const int64_t n = s_ticket / pairs;
-  const int p = (int)(s_ticket - (uint32_t)n * pairs);
-  const int tA = 2 * p, tB = 2 * p + 1;
-  const bool hasB = tB < a.tiles;  // uniform
-
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int pr = wave / 2, pc0 = (wave % 2) * 64;  // wave's row and first column in a tile
-  auto origin = [&](int tile, int &h0, int &w0) {
-    const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
-    h0 = th * kTileH;
-    w0 = tw * kTileW;
-  };
-  int hA, wA, hB, wB;
-  origin(tA, hA, wA);
-  origin(hasB ? tB : tA, hB, wB);
-
-  XRegs xa, xb;
-  load_x(a, n, hA, wA, xa, threadIdx.x);
-  if (hasB) load_x(a, n, hB, wB, xb, threadIdx.x);
-  store_w(wr, wl);
-  store_x(xa, xs, threadIdx.x);
-  __syncthreads();
-
-  f32x4 accA[kNB][kMT], accB[kNB][kMT];
-  bool vA[kNB], vB[kNB];
-  conv_tile(a, xs, wl, pr, pc0, accA);
-  tile_valid(a, tA, vA, wave);
-  publish_tile_stats(a, n, tA, accA, vA, L);  // ends with a barrier: xs is free again
-  if (hasB) {
-    store_x(xb, xs, threadIdx.x);
+    for (int idx = threadIdx.x + NT * kPer; idx < words; idx += NT)
+      missing |= (load_pair_agent(ws + idx) == 0);
+    const bool late =
+        it >= a.spin_limit || __builtin_amdgcn_s_memrealtime() - t0 > kChainWaitTicks;
+    const uint64_t mb = __builtin_amdgcn_ballot_w64(missing);
+    const uint64_t lb = __builtin_amdgcn_ballot_w64(late);
+    // Double-buffered by poll parity: a wave can only rewrite a slot after
+    // every wave has passed the next poll's barrier, i.e. has read it.
+    if (lane == 0) L.flags[it & 1][wave] = (mb != 0 ? 1u : 0u) | (lb != 0 ? 2u : 0u);
     __syncthreads();
-    conv_tile(a, xs, wl, pr, pc0, accB);
-    tile_valid(a, tB, vB, wave);
-    publish_tile_stats(a, n, tB, accB, vB, L);
+    uint32_t f = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) f |= L.flags[it & 1][w];
+    if ((f & 1u) == 0) break;
+    if (f & 2u) {
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(8);
   }
-  (void)lane;
-  wait_and_merge(a, n, tA == 0, L);
-  tile_epilogue(a, n, tA, accA, vA, L, wave);
-  if (hasB) tile_epilogue(a, n, tB, accB, vB, L, wave);
+  double C = 0.0, S1 = 0.0, S2 = 0.0;
+  auto add = [&](int idx, uint64_t w) {
+    const double c = tile_count(a, idx >> a.log2G, qpg, tiles_h);  // G is a power of 2
+    const double m = (double)bitsf((uint32_t)w);
+    C += c;
+    S1 += c * m;
+    S2 += -(double)bitsf((uint32_t)(w >> 32)) + c * m * m;
+  };
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int idx = threadIdx.x + NT * j;
+    if (idx < words) add(idx, wd[j]);
+  }
+  for (int idx = threadIdx.x + NT * kPer; idx < words; idx += NT)
+    add(idx, load_pair_agent(ws + idx));
+  for (int o = kWave / 2; o >= a.G; o >>= 1) {  // lanes l, l ^ o share a group while o >= G
+    C += __shfl_xor(C, o);
+    S1 += __shfl_xor(S1, o);
+    S2 += __shfl_xor(S2, o);
+  }
+  if (lane < a.G) {
+    L.mrg[wave][lane][0] = C;
+    L.mrg[wave][lane][1] = S1;
+    L.mrg[wave][lane][2] = S2;
+  }
+  __syncthreads();
+  if (threadIdx.x < a.G) {
+    const int g = threadIdx.x;
+    double Cg = 0.0, S1g = 0.0, S2g = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      Cg += L.mrg[w][g][0];
+      S1g += L.mrg[w][g][1];
+      S2g += L.mrg[w][g][2];
+    }
+    const double MU = S1g / Cg;
+    const double M2 = fmax(S2g - Cg * MU * MU, 0.0);
+    float fm = (float)MU, fr = (float)(1.0 / sqrt(M2 / Cg + (double)a.eps));
+    if (!ok) fm = fr = __builtin_nanf("");
+    L.mu[g] = fm;
+    L.rs[g] = fr;
+    if (write_global) {
+      a.mean[n * a.G + g] = fm;
+      a.rstd[n * a.G + g] = fr;
+    }
+    if (!ok && g == 0)
+      __hip_atomic_store(&a.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
 }
 
 #ifndef LSE_CHAIN_PAIR_WAVES_PER_EU
 #define LSE_CHAIN_PAIR_WAVES_PER_EU 4
-#endif
-#ifndef LSE_CHAIN_WIDE
-#define LSE_CHAIN_WIDE 1   // 1: the 8-wave pair kernel below; 0: the 4-wave pair kernel above
 #endif
 
 // LDS scratch of the 8-wave pair workgroup besides the x and W tiles.
 struct PairLds {
   float qred[2 * kThreads / kWave][16];
   float gmean[2][16];
-  double mrg[kWave][3];
+  double mrg[2 * kThreads / kWave][16][3];  // per wave and group: C, S1, S2
+  uint32_t flags[2][2 * kThreads / kWave];  // per poll parity and wave: 1 missing, 2 gave up
   float mu[16], rs[16];
-  alignas(16) float sc[kCout];  // per channel: z = conv * sc + sh (read 4 at a time)
+  // per channel, read 4 at a time: 2 log2(e) z = conv * sc + sh, z the tanh input
+  alignas(16) float sc[kCout];
   alignas(16) float sh[kCout];
 };
 
-// GroupNorm and the affine folded into one multiply-add per channel, from the
-// merged statistics (threads 0..63, one channel each; then a barrier).
+// GroupNorm, the affine and the 2 log2(e) of tanh's exponential folded into
+// one multiply-add per channel, from the merged statistics (threads 0..63, one
+// channel each; then a barrier).
 __device__ __forceinline__ void fold_affine(const ChainArgs &a, PairLds &L) {
   if (threadIdx.x < kCout) {
     const int c = threadIdx.x, g = (c / 4) / (16 / a.G);
     const float ga = a.gamma ? a.gamma[c] : 1.0f;
     const float be = a.beta ? a.beta[c] : 0.0f;
-    L.sc[c] = L.rs[g] * ga;
-    L.sh[c] = be - L.mu[g] * L.rs[g] * ga;
+    const float sc = L.rs[g] * ga;
+    L.sc[c] = sc * (2.0f * kLog2e);
+    L.sh[c] = (be - L.mu[g] * sc) * (2.0f * kLog2e);
   }
   __syncthreads();
 }
@@ -572,17 +422,19 @@ __device__ __forceinline__ void tile_epilogue_lds(const ChainArgs &a, int64_t n,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = acc[blk][t][r];
-        u[t][r] = v + hardswish_of_tanh(tanh_fast(v * sc[r] + sh[r]));
+        u[t][r] = v + hardswish_of_tanh(tanh_of_scaled(v * sc[r] + sh[r]));
         m = fmaxf(m, u[t][r]);
       }
     }
     const float M = across_quads(m, OpMax{});
-    const float c = is_finite(M) ? M : 0.0f;
+    // exp(u - M) as 2^(u log2 e - M log2 e), one fma per term; the rounding
+    // of M log2 e shifts every term alike (a relative few 1e-7 in S).
+    const float c2 = (is_finite(M) ? M : 0.0f) * kLog2e;
     float s = 0.0f;
 #pragma unroll
     for (int t = 0; t < kMT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s += exp_base2(u[t][r] - c);
+      for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(fmaf(u[t][r], kLog2e, -c2));
     const float S = across_quads(s, OpSum{});
     if (q == 0 && valid[blk])
       a.out[(n * a.Ho + h) * (int64_t)a.Wo + w0 + 16 * blk + li] = M + logf(S);
@@ -631,7 +483,7 @@ __device__ __forceinline__ void publish_pair_stats(const ChainArgs &a, int64_t n
       for (int w = 4 * rt; w < 4 * rt + 4; ++w)
         for (int Q = g * qpg; Q < (g + 1) * qpg; ++Q) tot += L.qred[w][Q];
       if (stage == 0) {
-        L.gmean[rt][g] = tot / (float)tile_count(a, tile, qpg);
+        L.gmean[rt][g] = tot / (float)tile_count(a, tile, qpg, a.tiles / a.tiles_w);
       } else {
         __hip_atomic_store(a.stats + (n * a.tiles + tile) * a.G + g, pack_stats(L.gmean[rt][g], tot),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -689,7 +541,7 @@ void conv_chain_pair_kernel(ChainArgs a) {
     tile_valid(a, tile, valid, twave);
   }
   publish_pair_stats(a, n, tA, tB, hasB, team, active, acc, valid, L);
-  wait_and_merge(a, n, tA == 0, L);
+  wait_and_merge<2 * kThreads>(a, n, tA == 0, L);
   fold_affine(a, L);
   if (active) tile_epilogue_lds(a, n, tile, acc, valid, L, twave);
 }
@@ -755,12 +607,8 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t pairs = (L.tiles + 1) / 2;
-  if (LSE_CHAIN_WIDE)
-    hipLaunchKernelGGL(conv_chain_pair_kernel, dim3((uint32_t)(N * pairs)), dim3(2 * kThreads), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL(conv_chain_kernel, dim3((uint32_t)(N * pairs)), dim3(kThreads), 0, stream,
-                       a);
+  hipLaunchKernelGGL(conv_chain_pair_kernel, dim3((uint32_t)(N * pairs)), dim3(2 * kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
