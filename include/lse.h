@@ -204,7 +204,13 @@ lse_status_t lse_rows_merge(const lse_pair_t *partials, int64_t rows,
  * (LSE_ERR_UNSUPPORTED otherwise).  ws: at least
  * fused_conv_gn_act_lse_workspace_bytes(...) bytes; on return (once the
  * stream has run the call) its first 2 * N * groups floats hold the
- * per-(n, g) mean followed by the per-(n, g) 1/sqrt(var + eps). */
+ * per-(n, g) mean followed by the per-(n, g) 1/sqrt(var + eps).
+ * The conv runs once when a sample's 2 x 256-pixel tile pairs number at most
+ * half of what the device can hold resident (one launch whose workgroups wait
+ * for their sample's statistics); larger samples take two launches, the
+ * first publishing the statistics, the second recomputing the conv and
+ * applying them (the conv runs twice; nothing waits).  Both give identical
+ * results. */
 size_t fused_conv_gn_act_lse_workspace_bytes(int64_t N, int64_t Cin, int64_t H,
                                              int64_t W, int64_t Cout,
                                              int64_t K, int64_t groups);

@@ -37,6 +37,9 @@
 // a group's statistics reduce inside 16-lane DPP rows, and a pixel's 64
 // channels are 16 values in-lane plus the 4 lanes i, i+16, i+32, i+48 (two
 // permlane swaps).
+#include <algorithm>
+#include <atomic>
+
 #include "lse_device.hpp"
 #include "lse_internal.hpp"
 
@@ -494,11 +497,20 @@ __device__ __forceinline__ void publish_pair_stats(const ChainArgs &a, int64_t n
 }
 
 // One workgroup of 8 waves = a pair of tiles (A = 2p, B = 2p + 1) of one
-// sample, handed out by ticket in sample order.  Waves 0-3 stage and convolve
-// tile A, waves 4-7 tile B, at the same time; each wave holds the 64
-// accumulators of its quarter tile, so four waves fit on a SIMD and one
-// wave's MFMAs overlap others' staging, waiting and epilogue.  W staging and
-// the wait for the sample's statistics are paid once per pair.
+// sample.  Waves 0-3 stage and convolve tile A, waves 4-7 tile B, at the same
+// time; each wave holds the 64 accumulators of its quarter tile, so four
+// waves fit on a SIMD and one wave's MFMAs overlap others' staging, waiting
+// and epilogue.  W staging and the wait for the sample's statistics are paid
+// once per pair.
+//   kFused: pairs handed out by ticket in sample order; publish, wait for the
+//           sample, merge, epilogue (one launch; a sample's pairs must fit
+//           on the GPU at once, see launch_conv_chain).
+//   kStats: publish only.  kApply: the statistics are complete (published by
+//           a kStats launch): merge, epilogue.  kStats + kApply compute the
+//           conv twice but never wait on another workgroup.
+enum ChainMode { kFused = 0, kStats = 1, kApply = 2 };
+
+template <int MODE>
 __global__ __launch_bounds__(2 * kThreads)
 __attribute__((amdgpu_waves_per_eu(LSE_CHAIN_PAIR_WAVES_PER_EU)))
 void conv_chain_pair_kernel(ChainArgs a) {
@@ -508,13 +520,17 @@ void conv_chain_pair_kernel(ChainArgs a) {
   __shared__ uint32_t s_ticket;
   WRegs<2 * kThreads> wr;
   load_w(a.w, wr);  // in flight while the ticket is claimed
-  if (threadIdx.x == 0)
-    s_ticket = __hip_atomic_fetch_add(&a.hdr->ticket, 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
+  uint32_t ticket = blockIdx.x;  // kStats, kApply: no workgroup waits, any order will do
+  if constexpr (MODE == kFused) {
+    if (threadIdx.x == 0)
+      s_ticket = __hip_atomic_fetch_add(&a.hdr->ticket, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    ticket = s_ticket;
+  }
   const uint32_t pairs = (uint32_t)(a.tiles + 1) / 2;
-  const int64_t n = s_ticket / pairs;
-  const int p = (int)(s_ticket - (uint32_t)n * pairs);
+  const int64_t n = ticket / pairs;
+  const int p = (int)(ticket - (uint32_t)n * pairs);
   const int tA = 2 * p, tB = 2 * p + 1;
   const bool hasB = tB < a.tiles;  // uniform
 
@@ -540,7 +556,8 @@ void conv_chain_pair_kernel(ChainArgs a) {
     conv_tile(a, xs[team], wl, pr, pc0, acc);
     tile_valid(a, tile, valid, twave);
   }
-  publish_pair_stats(a, n, tA, tB, hasB, team, active, acc, valid, L);
+  if constexpr (MODE != kApply) publish_pair_stats(a, n, tA, tB, hasB, team, active, acc, valid, L);
+  if constexpr (MODE == kStats) return;
   wait_and_merge<2 * kThreads>(a, n, tA == 0, L);
   fold_affine(a, L);
   if (active) tile_epilogue_lds(a, n, tile, acc, valid, L, twave);
@@ -570,6 +587,27 @@ ChainLayout chain_layout(int64_t N, int64_t H, int64_t W, int64_t K, int64_t gro
   return L;
 }
 }  // namespace
+
+// The fused launch needs every pair of a sample resident at once (a waiting
+// workgroup holds its slot).  It is used while a sample has at most half as
+// many pairs as the current device can hold (the other half is headroom for
+// other work sharing the GPU); larger samples take the two-launch path.
+// Queried once per device.
+int64_t fused_pair_limit() {
+  static std::atomic<int64_t> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int64_t v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv_chain_pair_kernel<kFused>,
+                                                   2 * kThreads, 0) != hipSuccess)
+    return 0;  // unknown: always the two-launch path
+  v = std::max<int64_t>(1, (int64_t)cus * per_cu / 2);
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 size_t conv_chain_workspace_bytes(int64_t N, int64_t /*Cin*/, int64_t H, int64_t W,
                                   int64_t /*Cout*/, int64_t K, int64_t groups) {
@@ -607,8 +645,15 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t pairs = (L.tiles + 1) / 2;
-  hipLaunchKernelGGL(conv_chain_pair_kernel, dim3((uint32_t)(N * pairs)), dim3(2 * kThreads), 0,
-                     stream, a);
+  const dim3 grid((uint32_t)(N * pairs)), block(2 * kThreads);
+  if (pairs <= fused_pair_limit()) {
+    hipLaunchKernelGGL(conv_chain_pair_kernel<kFused>, grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(conv_chain_pair_kernel<kStats>, grid, block, 0, stream, a);
+  const hipError_t e2 = hipGetLastError();
+  if (e2 != hipSuccess) return e2;
+  hipLaunchKernelGGL(conv_chain_pair_kernel<kApply>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

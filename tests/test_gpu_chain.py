@@ -52,6 +52,14 @@ def test_chain_groups_and_affine(orc, groups):
     _check(orc, x, w, b, g, be, groups, f"groups={groups}")
 
 
+@pytest.mark.parametrize("N,H,W,groups", [(1, 600, 520, 1), (2, 260, 300, 4)])
+def test_chain_many_tiles(orc, N, H, W, groups):
+    """Samples with more statistics words than two per thread of a workgroup
+    (1495 and 1548 words), across one and several tile columns and rows."""
+    x, w, b, g, be = _chain_inputs(N, H, W, seed=H + W + groups, affine=True)
+    _check(orc, x, w, b, g, be, groups, f"N={N} H={H} W={W} G={groups}")
+
+
 def test_chain_no_bias_no_affine(orc):
     x, w, _, _, _ = _chain_inputs(2, 11, 11, seed=3)
     _check(orc, x, w, None, None, None, 16, "no bias")
