@@ -31,6 +31,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -280,7 +281,8 @@ def run_only(which, steps, warmup):
         raise SystemExit(f"unknown --only {which}")
     print(json.dumps({"only": which, "steps": steps, "wall_ms": round(wall, 4),
                       "event_ms_avg": round(sum(ev) / len(ev), 4),
-                      "event_ms_min": round(min(ev), 4)}), flush=True)
+                      "event_ms_min": round(min(ev), 4),
+                      "event_ms_median": round(statistics.median(ev), 4)}), flush=True)
 
 
 def main():
@@ -330,7 +332,8 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(),
                      "kernel": "log_softmax_rows_kernel<32, true, true, false>",
-                     "event_ms_avg": round(ev_avg, 4), "event_ms_min": round(min(ev), 4)},
+                     "event_ms_avg": round(ev_avg, 4), "event_ms_min": round(min(ev), 4),
+                     "event_ms_median": round(statistics.median(ev), 4)},
     }
     copy_gbs = copy_ceiling(x, y)
     line["roofline"]["copy_ceiling_GBs"] = copy_gbs
