@@ -1,0 +1,271 @@
+/* abi_check.c — the C ABI of include/lse.h driven from plain C, with no
+ * Python and no torch in the process: device buffers from hipMalloc, one
+ * hipStream_t, results copied back and compared with the fp64 oracle
+ * (oracle/oracle.c, linked in: this is test code).
+ *
+ *   abi_check --host   validation paths only (no GPU needed)
+ *   abi_check          every call on the GPU against the oracle
+ *
+ * Inputs come from a SplitMix64 stream (uniforms, Box-Muller normals): the
+ * same host arrays go to the library and to the oracle.  Tolerance as in the
+ * Python parity tests: |gpu - ref| <= atol + rtol |ref| for finite refs,
+ * the same class (-inf, +inf, NaN) otherwise.  Exit status 0 = all passed. */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "lse.h"
+
+/* oracle/oracle.c */
+int oracle_lse_axis0(const float *x, int64_t R, int64_t inner, double *out, int nthreads);
+int oracle_log_softmax_rows(const float *x, int64_t rows, int64_t cols, double *y,
+                            double *lse, int nthreads);
+int oracle_softmax_rows(const float *x, int64_t rows, int64_t cols, double *y, int nthreads);
+int oracle_lse_axis(const float *x, int64_t outer, int64_t R, int64_t inner, double *out,
+                    int nthreads);
+int oracle_log_softmax_axis(const float *x, int64_t outer, int64_t R, int64_t inner,
+                            double *y, int nthreads);
+int oracle_fused_chain(const float *x, const float *w, const float *b, const float *gamma,
+                       const float *beta, int64_t N, int64_t Cin, int64_t H, int64_t W,
+                       int64_t Cout, int64_t K, int64_t G, double eps, double *out,
+                       double *mean_out, double *rstd_out, int nthreads);
+
+static int g_fail = 0;
+
+#define CHECK_HIP(call)                                                              \
+  do {                                                                               \
+    hipError_t e_ = (call);                                                          \
+    if (e_ != hipSuccess) {                                                          \
+      fprintf(stderr, "HIP error %s at %s:%d\n", hipGetErrorString(e_), __FILE__,    \
+              __LINE__);                                                             \
+      exit(2);                                                                       \
+    }                                                                                \
+  } while (0)
+
+#define EXPECT(cond, what)                                                           \
+  do {                                                                               \
+    if (!(cond)) {                                                                   \
+      fprintf(stderr, "FAILED: %s (%s:%d)\n", what, __FILE__, __LINE__);             \
+      ++g_fail;                                                                      \
+    }                                                                                \
+  } while (0)
+
+/* ------------------------------------------------------------- inputs */
+static uint64_t g_state;
+static uint64_t splitmix64(void) {
+  uint64_t z = (g_state += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+static double uniform01(void) { return (double)(splitmix64() >> 11) * 0x1.0p-53; }
+static float *normal_array(int64_t n, double sigma, uint64_t seed) {
+  float *a = (float *)malloc((size_t)n * sizeof(float));
+  g_state = seed;
+  for (int64_t i = 0; i < n; ++i) {
+    const double u1 = 1.0 - uniform01(), u2 = uniform01();
+    a[i] = (float)(sigma * sqrt(-2.0 * log(u1)) * cos(6.283185307179586 * u2));
+  }
+  return a;
+}
+static float *uniform_array(int64_t n, double bound, uint64_t seed) {
+  float *a = (float *)malloc((size_t)n * sizeof(float));
+  g_state = seed;
+  for (int64_t i = 0; i < n; ++i) a[i] = (float)(bound * (2.0 * uniform01() - 1.0));
+  return a;
+}
+
+/* ------------------------------------------------------------- helpers */
+static float *to_device(const float *h, int64_t n) {
+  float *d = NULL;
+  CHECK_HIP(hipMalloc((void **)&d, (size_t)(n > 0 ? n : 1) * sizeof(float)));
+  if (h && n > 0) CHECK_HIP(hipMemcpy(d, h, (size_t)n * sizeof(float), hipMemcpyHostToDevice));
+  return d;
+}
+static float *from_device(const float *d, int64_t n) {
+  float *h = (float *)malloc((size_t)n * sizeof(float));
+  CHECK_HIP(hipMemcpy(h, d, (size_t)n * sizeof(float), hipMemcpyDeviceToHost));
+  return h;
+}
+
+static void compare(const char *what, const float *got, const double *ref, int64_t n,
+                    double atol, double rtol) {
+  int64_t bad = 0;
+  double worst = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    const double g = got[i], r = ref[i];
+    int ok;
+    if (isfinite(r)) {
+      const double err = fabs(g - r);
+      ok = isfinite(g) && err <= atol + rtol * fabs(r);
+      if (isfinite(g) && err > worst) worst = err;
+    } else if (isnan(r)) {
+      ok = isnan(g);
+    } else {
+      ok = (g == r);
+    }
+    if (!ok) {
+      if (bad < 3) fprintf(stderr, "  %s[%lld]: gpu %.9g ref %.9g\n", what, (long long)i, g, r);
+      ++bad;
+    }
+  }
+  printf("%-34s n=%-9lld max |err| %.3g  %s\n", what, (long long)n, worst, bad ? "FAIL" : "ok");
+  if (bad) ++g_fail;
+}
+
+static void check_status(lse_status_t st, const char *what) {
+  if (st != LSE_OK) {
+    fprintf(stderr, "%s: %s: %s\n", what, lse_status_string(st), lse_last_error());
+    ++g_fail;
+  }
+}
+
+/* ------------------------------------------------------------- host-only */
+static void host_checks(void) {
+  float *fake = (float *)(uintptr_t)0x100000, *fake2 = (float *)(uintptr_t)0x900000000ull;
+  EXPECT(lse_abi_version() == LSE_ABI_VERSION, "abi version");
+  EXPECT(strcmp(lse_status_string(LSE_ERR_NULL), "LSE_ERR_NULL") == 0, "status string");
+  EXPECT(lse_reduce_axis0(NULL, fake2, 3, 5, NULL) == LSE_ERR_NULL, "NULL x");
+  EXPECT(strlen(lse_last_error()) > 0, "last error text");
+  EXPECT(lse_reduce_axis0(fake, fake2, 0, 5, NULL) == LSE_ERR_SHAPE, "R = 0");
+  EXPECT(lse_reduce_axis0(NULL, NULL, 3, 0, NULL) == LSE_OK, "empty call");
+  EXPECT(log_softmax_rows(fake, fake, 4, 8, NULL, 0, NULL) == LSE_ERR_OVERLAP, "in place");
+  EXPECT(log_softmax_rows(fake, fake2, 16, 393216, NULL, 0, NULL) == LSE_ERR_WORKSPACE,
+         "missing workspace");
+  EXPECT(log_softmax_rows_workspace_bytes(16, 393216) == 256 + 16 * 24 * 8, "workspace size");
+  EXPECT(log_softmax_axis_strided(fake, fake2, 2, 3, 8, 24, 8, 24, 4, NULL) == LSE_ERR_SHAPE,
+         "colliding output planes");
+  EXPECT(log_softmax_rows_strided(fake, fake2, 4, 8, 7, 8, NULL, 0, NULL) == LSE_ERR_SHAPE,
+         "row pitch below cols");
+  EXPECT(fused_conv_gn_act_lse(fake, fake, NULL, NULL, NULL, 2, 8, 12, 12, 64, 5, 16, 1e-5f,
+                               fake2, fake2, 1u << 20, NULL) == LSE_ERR_UNSUPPORTED,
+         "unsupported kernel size");
+  printf("%-34s %s\n", "host-side validation", g_fail ? "FAIL" : "ok");
+}
+
+/* ------------------------------------------------------------- GPU cases */
+static void case_axis0(hipStream_t s) {
+  const int64_t R = 7, inner = 1000, n = R * inner;
+  float *x = normal_array(n, 2.0, 11), *dx = to_device(x, n), *dout = to_device(NULL, inner);
+  double *ref = (double *)malloc(inner * sizeof(double));
+  check_status(lse_reduce_axis0(dx, dout, R, inner, s), "lse_reduce_axis0");
+  CHECK_HIP(hipStreamSynchronize(s));
+  float *got = from_device(dout, inner);
+  oracle_lse_axis0(x, R, inner, ref, 0);
+  compare("lse_reduce_axis0 (7, 1000)", got, ref, inner, 1e-5, 2e-6);
+  free(x); free(ref); free(got);
+  CHECK_HIP(hipFree(dx)); CHECK_HIP(hipFree(dout));
+}
+
+static void case_rows(hipStream_t s) {
+  const int64_t rows = 3, cols = 100000, n = rows * cols;
+  float *x = normal_array(n, 3.0, 12), *dx = to_device(x, n), *dy = to_device(NULL, n);
+  const size_t wsb = log_softmax_rows_workspace_bytes(rows, cols);
+  void *ws = NULL;
+  CHECK_HIP(hipMalloc(&ws, wsb));
+  double *ref = (double *)malloc(n * sizeof(double)), *lse = (double *)malloc(rows * 8);
+  check_status(log_softmax_rows(dx, dy, rows, cols, ws, wsb, s), "log_softmax_rows");
+  CHECK_HIP(hipStreamSynchronize(s));
+  float *got = from_device(dy, n);
+  oracle_log_softmax_rows(x, rows, cols, ref, lse, 0);
+  compare("log_softmax_rows (3, 100000)", got, ref, n, 1e-5, 2e-6);
+  free(got);
+  check_status(softmax_rows(dx, dy, rows, cols, ws, wsb, s), "softmax_rows");
+  CHECK_HIP(hipStreamSynchronize(s));
+  got = from_device(dy, n);
+  oracle_softmax_rows(x, rows, cols, ref, 0);
+  compare("softmax_rows (3, 100000)", got, ref, n, 1e-37, 1e-5);
+  free(got);
+
+  /* per-chunk pairs and their merge */
+  const int64_t chunk = 4096, k = lse_rows_num_chunks(cols, chunk);
+  float *dp = to_device(NULL, rows * k * 2), *dl = to_device(NULL, rows);
+  check_status(lse_rows_partial(dx, rows, cols, chunk, (lse_pair_t *)dp, s), "lse_rows_partial");
+  check_status(lse_rows_merge((const lse_pair_t *)dp, rows, k, dl, s), "lse_rows_merge");
+  CHECK_HIP(hipStreamSynchronize(s));
+  got = from_device(dl, rows);
+  compare("lse_rows_partial + merge", got, lse, rows, 1e-5, 2e-6);
+  free(got); free(x); free(ref); free(lse);
+  CHECK_HIP(hipFree(dx)); CHECK_HIP(hipFree(dy)); CHECK_HIP(hipFree(ws));
+  CHECK_HIP(hipFree(dp)); CHECK_HIP(hipFree(dl));
+}
+
+static void case_strided(hipStream_t s) {
+  /* (3, 20, 64) planes with a pitch of 80 floats; output rows with a pitch of 72 */
+  const int64_t outer = 3, R = 20, inner = 64, pitch = 80, opitch = 72;
+  const int64_t nbig = outer * R * pitch;
+  float *big = normal_array(nbig, 3.0, 13), *dbig = to_device(big, nbig);
+  float *x = (float *)malloc(outer * R * inner * sizeof(float));
+  for (int64_t o = 0; o < outer; ++o)
+    for (int64_t r = 0; r < R; ++r)
+      memcpy(x + (o * R + r) * inner, big + (o * R + r) * pitch, inner * sizeof(float));
+  float *dout = to_device(NULL, outer * opitch);
+  CHECK_HIP(hipMemset(dout, 0, outer * opitch * sizeof(float)));
+  check_status(lse_reduce_axis_strided(dbig, dout, outer, R, inner, R * pitch, pitch, opitch, s),
+               "lse_reduce_axis_strided");
+  float *dy = to_device(NULL, outer * R * inner);
+  check_status(log_softmax_axis_strided(dbig, dy, outer, R, inner, R * pitch, pitch, R * inner,
+                                        inner, s),
+               "log_softmax_axis_strided");
+  CHECK_HIP(hipStreamSynchronize(s));
+  float *o = from_device(dout, outer * opitch), *got = (float *)malloc(outer * inner * 4);
+  for (int64_t i = 0; i < outer; ++i) memcpy(got + i * inner, o + i * opitch, inner * 4);
+  double *ref = (double *)malloc(outer * R * inner * sizeof(double));
+  oracle_lse_axis(x, outer, R, inner, ref, 0);
+  compare("lse_reduce_axis_strided", got, ref, outer * inner, 1e-5, 2e-6);
+  int pad_ok = 1;
+  for (int64_t i = 0; i < outer; ++i)
+    for (int64_t j = inner; j < opitch; ++j) pad_ok &= (o[i * opitch + j] == 0.0f);
+  EXPECT(pad_ok, "strided output padding untouched");
+  free(got);
+  got = from_device(dy, outer * R * inner);
+  oracle_log_softmax_axis(x, outer, R, inner, ref, 0);
+  compare("log_softmax_axis_strided", got, ref, outer * R * inner, 1e-5, 2e-6);
+  free(big); free(x); free(o); free(got); free(ref);
+  CHECK_HIP(hipFree(dbig)); CHECK_HIP(hipFree(dout)); CHECK_HIP(hipFree(dy));
+}
+
+static void case_chain(hipStream_t s) {
+  const int64_t N = 2, Cin = 8, H = 12, W = 12, Cout = 64, K = 3, G = 16;
+  const int64_t nx = N * Cin * H * W, nw = Cout * Cin * K * K, Ho = H - K + 1, Wo = W - K + 1;
+  const double bound = 1.0 / sqrt((double)(Cin * K * K));
+  float *x = normal_array(nx, 1.0, 14), *w = uniform_array(nw, bound, 15),
+        *b = uniform_array(Cout, bound, 16);
+  float *dx = to_device(x, nx), *dw = to_device(w, nw), *db = to_device(b, Cout);
+  float *dout = to_device(NULL, N * Ho * Wo);
+  const size_t wsb = fused_conv_gn_act_lse_workspace_bytes(N, Cin, H, W, Cout, K, G);
+  void *ws = NULL;
+  CHECK_HIP(hipMalloc(&ws, wsb));
+  check_status(fused_conv_gn_act_lse(dx, dw, db, NULL, NULL, N, Cin, H, W, Cout, K, G, 1e-5f,
+                                     dout, ws, wsb, s),
+               "fused_conv_gn_act_lse");
+  CHECK_HIP(hipStreamSynchronize(s));
+  float *got = from_device(dout, N * Ho * Wo);
+  double *ref = (double *)malloc(N * Ho * Wo * sizeof(double));
+  oracle_fused_chain(x, w, b, NULL, NULL, N, Cin, H, W, Cout, K, G, 1e-5, ref, NULL, NULL, 0);
+  compare("fused_conv_gn_act_lse (2,8,12,12)", got, ref, N * Ho * Wo, 1e-5, 5e-4);
+  free(x); free(w); free(b); free(got); free(ref);
+  CHECK_HIP(hipFree(dx)); CHECK_HIP(hipFree(dw)); CHECK_HIP(hipFree(db));
+  CHECK_HIP(hipFree(dout)); CHECK_HIP(hipFree(ws));
+}
+
+int main(int argc, char **argv) {
+  const int host_only = argc > 1 && strcmp(argv[1], "--host") == 0;
+  host_checks();
+  if (!host_only) {
+    hipStream_t s;
+    CHECK_HIP(hipSetDevice(0));
+    CHECK_HIP(hipStreamCreate(&s));
+    case_axis0(s);
+    case_rows(s);
+    case_strided(s);
+    case_chain(s);
+    CHECK_HIP(hipStreamDestroy(s));
+  }
+  printf(g_fail ? "FAILURES: %d\n" : "ALL OK\n", g_fail);
+  return g_fail ? 1 : 0;
+}
