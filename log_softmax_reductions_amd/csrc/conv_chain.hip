@@ -205,6 +205,13 @@ __device__ __forceinline__ void store_w(const WRegs<NT> &wr, float *wl) {
 // The wave's conv tile: acc[blk][t] for its kNB 16-pixel blocks and 4 M-tiles,
 // bias included.  Outer-product order: each K-step reads 4 A fragments (W)
 // and 4 B fragments (x patches) from LDS and issues 16 MFMAs.
+//
+// K is visited in the order that makes every LDS offset a lane constant plus
+// a compile-time constant: in K-step s, lane quarter q (the MFMA's K row)
+// takes input channel ci = 4 (s / 9) + q and filter tap s % 9 = (kh, kw), i.e.
+// k = 9 ci + 3 kh + kw of W's (Cout, Cin, 3, 3) layout.  A and B use the same
+// order, so the sum over K is the same set of products.  The W reads stay on
+// 64 distinct banks (row stride 76: 12 li + 9 q covers every bank once).
 __device__ __forceinline__ void conv_tile(const ChainArgs &a, const float *xs, const float *wl,
                                           int pr, int pc0, f32x4 (&acc)[kNB][kMT]) {
   const int lane = threadIdx.x % kWave;
@@ -217,15 +224,16 @@ __device__ __forceinline__ void conv_tile(const ChainArgs &a, const float *xs, c
 #pragma unroll
     for (int blk = 0; blk < kNB; ++blk) acc[blk][t] = bias;
   }
-  const float *xb = xs + pr * kLdsW + pc0 + li;
-  const float *wa = wl + li * kWStride + q;
+  const float *xb = xs + q * (kLdsH * kLdsW) + pr * kLdsW + pc0 + li;
+  const float *wa = wl + li * kWStride + 9 * q;
 #pragma unroll
   for (int s = 0; s < kKSteps; ++s) {
-    const int k = 4 * s + q;  // this lane's K index: (ci, kh, kw) = (k / 9, k % 9 / 3, k % 3)
-    const int boff = ((k / 9) * kLdsH + (k % 9) / 3) * kLdsW + k % 3;
+    const int cib = 4 * (s / 9), kh = (s % 9) / 3, kw = s % 3;  // compile-time per step
+    const int boff = (cib * kLdsH + kh) * kLdsW + kw;
+    const int aoff = 9 * cib + 3 * kh + kw;
     float af[kMT], bf[kNB];
 #pragma unroll
-    for (int t = 0; t < kMT; ++t) af[t] = wa[16 * t * kWStride + 4 * s];
+    for (int t = 0; t < kMT; ++t) af[t] = wa[16 * t * kWStride + aoff];
 #pragma unroll
     for (int blk = 0; blk < kNB; ++blk) bf[blk] = xb[boff + 16 * blk];
 #pragma unroll
