@@ -100,20 +100,15 @@ __device__ __forceinline__ float across_quads(float v, Op op) {
   return op(bitsf(q[0]), bitsf(q[1]));
 }
 
-// tanh(z) = 1 - 2 / (exp(2z) + 1), taking y = 2 log2(e) z (the scale is folded
-// into the normalisation's multiply-add): exp overflow gives 1, underflow -1,
-// so the result always lies in [-1, 1]; the absolute error is a few 1e-7, far
-// inside the chain's tolerance.
-__device__ __forceinline__ float tanh_of_scaled(float y) {
-  const float e = __builtin_amdgcn_exp2f(y);
-  return fmaf(-2.0f, __builtin_amdgcn_rcpf(e + 1.0f), 1.0f);
-}
-
-// hardswish(t) = t * min(max(t + 3, 0), 6) / 6.  The chain only applies it to
-// tanh outputs, t in [-1, 1], where t + 3 lies in [2, 4] and the clamp never
-// binds: there it is t * (t + 3) / 6 = t * (t / 6 + 1 / 2).
-__device__ __forceinline__ float hardswish_of_tanh(float t) {
-  return t * fmaf(t, 1.0f / 6.0f, 0.5f);
+// hardswish(tanh(z)), taking y = 2 log2(e) z (the scale is folded into the
+// normalisation's multiply-add).  tanh(z) = 1 - 2 r with r = 1 / (2^y + 1) in
+// [0, 1] (exp overflow gives r = 0, t = 1; underflow r = 1, t = -1), and
+// hardswish(t) = t * min(max(t + 3, 0), 6) / 6 = t (t + 3) / 6 on [-1, 1],
+// where the clamp never binds; in r that is (2 - 5 r + 2 r^2) / 3, two fmas.
+// The absolute error is a few 1e-7, far inside the chain's tolerance.
+__device__ __forceinline__ float hardswish_of_tanh_scaled(float y) {
+  const float r = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(y) + 1.0f);
+  return fmaf(r, fmaf(r, 2.0f / 3.0f, -5.0f / 3.0f), 2.0f / 3.0f);
 }
 
 // The x tile of sample n at (h0, w0): 8 channels x 4 rows x 132 columns.  It
@@ -433,7 +428,7 @@ __device__ __forceinline__ void tile_epilogue_lds(const ChainArgs &a, int64_t n,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = acc[blk][t][r];
-        u[t][r] = v + hardswish_of_tanh(tanh_of_scaled(v * sc[r] + sh[r]));
+        u[t][r] = v + hardswish_of_tanh_scaled(fmaf(v, sc[r], sh[r]));
         m = fmaxf(m, u[t][r]);
       }
     }
