@@ -1,0 +1,59 @@
+"""Empty and degenerate inputs through every entry point on the GPU: empty
+tensors are no-ops that return empty results, and the sizes whose result the
+definition fixes exactly are checked bit for bit (one value reduced gives
+itself; one column gives log_softmax 0 and softmax 1; -inf stays -inf)."""
+import pytest
+import torch
+
+import log_softmax_reductions_amd as L
+from log_softmax_reductions_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def test_empty_inputs():
+    e = torch.empty(0, 7, device=DEV)
+    assert L.log_softmax_rows(e).shape == (0, 7)
+    assert L.softmax_rows(e).shape == (0, 7)
+    assert L.lse_reduce_axis0(torch.empty(3, 0, device=DEV)).shape == (0,)
+    assert L.lse_reduce_axis(torch.empty(0, 5, 9, device=DEV), 1).shape == (0, 9)
+    assert L.log_softmax_axis(torch.empty(2, 5, 0, device=DEV), 1).shape == (2, 5, 0)
+    p = L.lse_rows_partial(e, 4)
+    assert p.shape == (0, 2, 2)
+    assert L.lse_rows_merge(p).shape == (0,)
+    x, w, b, g, be = inputs.conv_chain_inputs(N=1, H=6, W=6, seed=1, device=DEV)
+    out = L.fused_conv_gn_act_lse(x[:0], w, b, g, be, 16, 1e-5)
+    assert out.shape == (0, 1, 4, 4)
+    torch.cuda.synchronize()
+
+
+def test_single_value_reductions_are_exact():
+    x = inputs.normal((1, 4097), seed=7, sigma=30.0, device=DEV)
+    x[0, 5] = -float("inf")
+    # one plane: LSE of one value is that value, m + log(1) with log(1) = 0
+    assert torch.equal(L.lse_reduce_axis0(x), x[0])
+    assert torch.equal(L.lse_reduce_axis(x.view(1, 1, 4097), 1), x.view(1, 4097))
+    # one column: log_softmax is x - x = 0 (NaN for -inf), softmax is 1
+    col = x.view(4097, 1)
+    y = L.log_softmax_rows(col)
+    s = L.softmax_rows(col)
+    torch.cuda.synchronize()
+    fin = torch.isfinite(col)
+    assert torch.equal(y[fin], torch.zeros_like(y[fin]))
+    assert torch.isnan(y[~fin]).all()
+    assert torch.equal(s[fin], torch.ones_like(s[fin]))
+    assert torch.isnan(s[~fin]).all()
+    # log_softmax over an axis of length 1: 0 everywhere finite
+    z = L.log_softmax_axis(x.view(1, 1, 4097), 1)
+    assert torch.equal(z.view(-1)[fin.view(-1)], torch.zeros(int(fin.sum()), device=DEV))
+
+
+def test_constant_rows_are_log_of_length():
+    """A row of equal values v: LSE = v + log(n) and log_softmax = -log(n)."""
+    for cols in (3, 4096, 100000):
+        x = torch.full((2, cols), 2.5, device=DEV)
+        y = L.log_softmax_rows(x)
+        torch.cuda.synchronize()
+        ref = -torch.log(torch.tensor(float(cols), dtype=torch.float64)).item()
+        assert (y.double() - ref).abs().max().item() <= 1e-5 + 2e-6 * abs(ref)
