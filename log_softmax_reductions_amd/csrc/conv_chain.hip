@@ -57,10 +57,11 @@ constexpr int kLdsW = kTileW + 4;     // 130 input columns needed, padded to 33 
 constexpr int kF4PerRow = kLdsW / 4;                                     // 33
 constexpr int kStageF4 = kCin * kLdsH * kF4PerRow;                       // 1056
 constexpr int kNB = 4;   // 16-pixel blocks per wave: 4 waves x 4 x 16 = 2 x 128
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // one tile's team of 4 waves (a pair workgroup has two)
 // W in LDS, one 72-value row per output channel padded to 76 floats: the A
-// fragment read of a K-step (lane l -> row 16t + l % 16, column 4s + l / 16)
-// then hits 64 distinct banks (row stride 76 = 12 banks mod 64).
+// fragment read of a K-step (lane l -> row 16t + l % 16, column 9 (l / 16) plus
+// a per-step constant, see conv_tile) then hits 64 distinct banks
+// (12 (l % 16) + 9 (l / 16) is distinct mod 64 for the 64 lanes).
 constexpr int kWStride = kKdim + 4;                                      // 76
 constexpr int kWF4 = kCout * kKdim / 4;                                  // 1152 float4
 
