@@ -383,8 +383,9 @@ __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bo
 
 // LDS scratch of the 8-wave pair workgroup besides the x and W tiles.
 struct PairLds {
-  float qred[2 * kThreads / kWave][16];
-  float gmean[2][16];
+  float wmean[2 * kThreads / kWave][16];  // per wave and group: mean, M2, count
+  float wm2[2 * kThreads / kWave][16];
+  float wcnt[2 * kThreads / kWave];
   double mrg[2 * kThreads / kWave][16][3];  // per wave and group: C, S1, S2
   uint32_t flags[2][2 * kThreads / kWave];  // per poll parity and wave: 1 missing, 2 gave up
   float mu[16], rs[16];
@@ -448,55 +449,108 @@ __device__ __forceinline__ void tile_epilogue_lds(const ChainArgs &a, int64_t n,
   }
 }
 
+// Sum over the lanes whose quads share a GroupNorm group, for per-lane,
+// per-M-tile values x[t] already summed over their 16-lane row (row r holds
+// quad 4t + r of M-tile t): qpg = 2 pairs rows (0,1) and (2,3), qpg = 4 joins
+// all four rows, qpg = 8 and 16 also join M-tiles.  Every lane ends with the
+// sum of its own quad's group.
+__device__ __forceinline__ void group_sum(float (&x)[kMT], int qpg) {
+  if (qpg >= 2) {
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+      auto p = __builtin_amdgcn_permlane16_swap(fbits(x[t]), fbits(x[t]), false, false);
+      x[t] = bitsf(p[0]) + bitsf(p[1]);
+    }
+  }
+  if (qpg >= 4) {
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+      auto p = __builtin_amdgcn_permlane32_swap(fbits(x[t]), fbits(x[t]), false, false);
+      x[t] = bitsf(p[0]) + bitsf(p[1]);
+    }
+  }
+  if (qpg >= 8) {
+    x[0] = x[1] = x[0] + x[1];
+    x[2] = x[3] = x[2] + x[3];
+  }
+  if (qpg >= 16) x[0] = x[1] = x[2] = x[3] = x[0] + x[2];
+}
+
 // Per-group (mean, M2) of both tiles of a pair, one team of 4 waves per tile
-// (team 1 idle when the pair has no second tile).  Wave 0 reduces tile A's
-// quads, wave 1 tile B's.  Called by the whole workgroup; ends with a barrier.
+// (team 1 idle when the pair has no second tile).  Each wave reduces its
+// quarter tile on its own (DPP rows and permlane swaps, two passes: mean, then
+// M2 about it) and leaves (count, mean, M2) per group in LDS; after the one
+// barrier wave 0 combines tile A's four waves and wave 1 tile B's with the
+// pairwise update of (count, mean, M2) and publishes one word per group.
 __device__ __forceinline__ void publish_pair_stats(const ChainArgs &a, int64_t n, int tA, int tB,
-                                                   bool hasB, int team, bool active,
+                                                   bool hasB, bool active,
                                                    const f32x4 (&acc)[kNB][kMT],
                                                    const bool (&valid)[kNB], PairLds &L) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int li = lane % 16, q = lane / 16;
   const int qpg = 16 / a.G;
-  for (int stage = 0; stage < 2; ++stage) {
-    if (active) {
-      float qv[kMT];
+  if (active) {
+    int px = 0;  // valid pixels of the wave's strip (lanes 0..15 cover its columns)
+#pragma unroll
+    for (int blk = 0; blk < kNB; ++blk)
+      px += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid[blk]) & 0xFFFFull);
+    const float cnt = (float)(4 * qpg * px);
+    float mu[kMT], m2[kMT];
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+      float sacc = 0.0f;
+#pragma unroll
+      for (int blk = 0; blk < kNB; ++blk)
+        if (valid[blk])
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc += acc[blk][t][r];
+      mu[t] = row16_sum(sacc);
+    }
+    group_sum(mu, qpg);
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+      mu[t] = (px > 0) ? mu[t] / cnt : 0.0f;
+      float sacc = 0.0f;
+#pragma unroll
+      for (int blk = 0; blk < kNB; ++blk)
+        if (valid[blk])
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float d = acc[blk][t][r] - mu[t];
+            sacc = fmaf(d, d, sacc);
+          }
+      m2[t] = row16_sum(sacc);
+    }
+    group_sum(m2, qpg);
+    if (li == 0) {
 #pragma unroll
       for (int t = 0; t < kMT; ++t) {
-        const float mu = stage ? L.gmean[team][(4 * t + q) / qpg] : 0.0f;
-        float sacc = 0.0f;
-#pragma unroll
-        for (int blk = 0; blk < kNB; ++blk) {
-          if (valid[blk]) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float d = acc[blk][t][r] - mu;
-              sacc += stage ? d * d : d;
-            }
-          }
+        if ((4 * t + q) % qpg == 0) {  // one writer per group
+          const int g = (4 * t + q) / qpg;
+          L.wmean[wave][g] = mu[t];
+          L.wm2[wave][g] = m2[t];
         }
-        qv[t] = row16_sum(sacc);
       }
-      if (li == 0) {
+      if (q == 0) L.wcnt[wave] = cnt;
+    }
+  }
+  __syncthreads();
+  const int rt = wave;  // wave 0 combines team 0, wave 1 team 1
+  if (rt < 2 && lane < a.G && (rt == 0 || hasB)) {
+    const int g = lane, tile = rt ? tB : tA;
+    float N = 0.0f, mean = 0.0f, M2 = 0.0f;
 #pragma unroll
-        for (int t = 0; t < kMT; ++t) L.qred[wave][4 * t + q] = qv[t];
+    for (int w = 4 * rt; w < 4 * rt + 4; ++w) {
+      const float nw = L.wcnt[w];
+      if (nw > 0.0f) {
+        const float delta = L.wmean[w][g] - mean, Nn = N + nw;
+        mean += delta * (nw / Nn);
+        M2 += L.wm2[w][g] + delta * delta * (N * nw / Nn);
+        N = Nn;
       }
     }
-    __syncthreads();
-    const int rt = wave;  // wave 0 reduces team 0, wave 1 team 1
-    if (rt < 2 && lane < a.G && (rt == 0 || hasB)) {
-      const int g = lane, tile = rt ? tB : tA;
-      float tot = 0.0f;
-      for (int w = 4 * rt; w < 4 * rt + 4; ++w)
-        for (int Q = g * qpg; Q < (g + 1) * qpg; ++Q) tot += L.qred[w][Q];
-      if (stage == 0) {
-        L.gmean[rt][g] = tot / (float)tile_count(a, tile, qpg, a.tiles / a.tiles_w);
-      } else {
-        __hip_atomic_store(a.stats + (n * a.tiles + tile) * a.G + g, pack_stats(L.gmean[rt][g], tot),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
+    __hip_atomic_store(a.stats + (n * a.tiles + tile) * a.G + g, pack_stats(mean, M2),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -560,7 +614,7 @@ void conv_chain_pair_kernel(ChainArgs a) {
     conv_tile(a, xs[team], wl, pr, pc0, acc);
     tile_valid(a, tile, valid, twave);
   }
-  if constexpr (MODE != kApply) publish_pair_stats(a, n, tA, tB, hasB, team, active, acc, valid, L);
+  if constexpr (MODE != kApply) publish_pair_stats(a, n, tA, tB, hasB, active, acc, valid, L);
   if constexpr (MODE == kStats) return;
   wait_and_merge<2 * kThreads>(a, n, tA == 0, L);
   fold_affine(a, L);
