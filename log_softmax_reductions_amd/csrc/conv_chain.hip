@@ -276,18 +276,19 @@ __device__ __forceinline__ void tile_valid(const ChainArgs &a, int tile, bool (&
 }
 
 // Wait until every tile of sample n has published, then merge the sample's
-// statistics into L.mu / L.rs; called by the whole workgroup (NT threads),
-// ends with a barrier.  Thread t polls words t, t + NT, ... of the sample's
+// statistics into the epilogue's per-channel table L.sc / L.sh; called by the
+// whole workgroup (NT threads), ends with a barrier.  Thread t polls words t, t + NT, ... of the sample's
 // (tile, group) block: one round trip per poll for up to 2 NT words, whose
 // values stay in registers.  A poll's verdict is the OR of one ballot per
 // wave through LDS, so every wave leaves the loop together.  Then, per thread
 // in fp64: C = sum n_j, S1 = sum n_j mean_j, S2 = sum (M2_j + n_j mean_j^2)
 // over its words, which all belong to group t % G; lanes of a wave with the
 // same group are combined by xor shuffles, the waves in LDS (fixed order:
-// the result is deterministic); per group mean = S1 / C, M2 = S2 - C mean^2.
+// the result is deterministic); per group mean = S1 / C, M2 = S2 - C mean^2,
+// rstd = 1 / sqrt(M2 / C + eps).
 template <int NT, class Lds>
 __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bool write_global,
-                                               Lds &L) {
+                                               float ga, float be, Lds &L) {
   constexpr int kPer = 2;
   constexpr int kWaves = NT / kWave;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -352,8 +353,12 @@ __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bo
     L.mrg[wave][lane][2] = S2;
   }
   __syncthreads();
-  if (threadIdx.x < a.G) {
-    const int g = threadIdx.x;
+  if (threadIdx.x < kCout) {
+    // Thread c = channel c: its group's statistics (the 4 qpg threads of a
+    // group add the same values in the same order), folded with gamma, beta
+    // (ga, be: this thread's channel, loaded at kernel start) and tanh's
+    // 2 log2(e) into the epilogue's one multiply-add: 2 log2(e) z = v sc + sh.
+    const int c = threadIdx.x, g = (c / 4) / (16 / a.G);
     double Cg = 0.0, S1g = 0.0, S2g = 0.0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -365,13 +370,14 @@ __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bo
     const double M2 = fmax(S2g - Cg * MU * MU, 0.0);
     float fm = (float)MU, fr = (float)(1.0 / sqrt(M2 / Cg + (double)a.eps));
     if (!ok) fm = fr = __builtin_nanf("");
-    L.mu[g] = fm;
-    L.rs[g] = fr;
-    if (write_global) {
+    const float sc = fr * ga;
+    L.sc[c] = sc * (2.0f * kLog2e);
+    L.sh[c] = (be - fm * sc) * (2.0f * kLog2e);
+    if (write_global && c % (4 * (16 / a.G)) == 0) {
       a.mean[n * a.G + g] = fm;
       a.rstd[n * a.G + g] = fr;
     }
-    if (!ok && g == 0)
+    if (!ok && c == 0)
       __hip_atomic_store(&a.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
@@ -388,26 +394,11 @@ struct PairLds {
   float wcnt[2 * kThreads / kWave];
   double mrg[2 * kThreads / kWave][16][3];  // per wave and group: C, S1, S2
   uint32_t flags[2][2 * kThreads / kWave];  // per poll parity and wave: 1 missing, 2 gave up
-  float mu[16], rs[16];
   // per channel, read 4 at a time: 2 log2(e) z = conv * sc + sh, z the tanh input
   alignas(16) float sc[kCout];
   alignas(16) float sh[kCout];
 };
 
-// GroupNorm, the affine and the 2 log2(e) of tanh's exponential folded into
-// one multiply-add per channel, from the merged statistics (threads 0..63, one
-// channel each; then a barrier).
-__device__ __forceinline__ void fold_affine(const ChainArgs &a, PairLds &L) {
-  if (threadIdx.x < kCout) {
-    const int c = threadIdx.x, g = (c / 4) / (16 / a.G);
-    const float ga = a.gamma ? a.gamma[c] : 1.0f;
-    const float be = a.beta ? a.beta[c] : 0.0f;
-    const float sc = L.rs[g] * ga;
-    L.sc[c] = sc * (2.0f * kLog2e);
-    L.sh[c] = (be - L.mu[g] * sc) * (2.0f * kLog2e);
-  }
-  __syncthreads();
-}
 
 // tile_epilogue with the per-channel scale and shift read from LDS (four
 // consecutive channels per read) instead of held in 32 registers.
@@ -578,6 +569,11 @@ void conv_chain_pair_kernel(ChainArgs a) {
   __shared__ uint32_t s_ticket;
   WRegs<2 * kThreads> wr;
   load_w(a.w, wr);  // in flight while the ticket is claimed
+  float ga = 1.0f, be = 0.0f;  // this thread's channel of gamma / beta (threads < 64)
+  if (threadIdx.x < kCout) {
+    if (a.gamma) ga = a.gamma[threadIdx.x];
+    if (a.beta) be = a.beta[threadIdx.x];
+  }
   uint32_t ticket = blockIdx.x;  // kStats, kApply: no workgroup waits, any order will do
   if constexpr (MODE == kFused) {
     if (threadIdx.x == 0)
@@ -616,8 +612,7 @@ void conv_chain_pair_kernel(ChainArgs a) {
   }
   if constexpr (MODE != kApply) publish_pair_stats(a, n, tA, tB, hasB, active, acc, valid, L);
   if constexpr (MODE == kStats) return;
-  wait_and_merge<2 * kThreads>(a, n, tA == 0, L);
-  fold_affine(a, L);
+  wait_and_merge<2 * kThreads>(a, n, tA == 0, ga, be, L);
   if (active) tile_epilogue_lds(a, n, tile, acc, valid, L, twave);
 }
 
