@@ -57,7 +57,15 @@ constexpr int kLdsW = kTileW + 4;     // 130 input columns needed, padded to 33 
 constexpr int kF4PerRow = kLdsW / 4;                                     // 33
 constexpr int kStageF4 = kCin * kLdsH * kF4PerRow;                       // 1056
 constexpr int kNB = 4;   // 16-pixel blocks per wave: 4 waves x 4 x 16 = 2 x 128
-constexpr int kThreads = 256;  // one tile's team of 4 waves (a pair workgroup has two)
+constexpr int kThreads = 256;  // one tile's team of 4 waves
+#ifndef LSE_CHAIN_HELD
+#define LSE_CHAIN_HELD 1024   // statistics words held in registers per workgroup while polling
+#endif
+#ifndef LSE_CHAIN_TEAMS
+#define LSE_CHAIN_TEAMS 2   // tiles (teams of 4 waves) per workgroup: 1 or 2
+#endif
+constexpr int kTeams = LSE_CHAIN_TEAMS;
+static_assert(kTeams == 1 || kTeams == 2, "one or two tiles per workgroup");
 // W in LDS, one 72-value row per output channel padded to 76 floats: the A
 // fragment read of a K-step (lane l -> row 16t + l % 16, column 9 (l / 16) plus
 // a per-step constant, see conv_tile) then hits 64 distinct banks
@@ -278,8 +286,8 @@ __device__ __forceinline__ void tile_valid(const ChainArgs &a, int tile, bool (&
 // Wait until every tile of sample n has published, then merge the sample's
 // statistics into the epilogue's per-channel table L.sc / L.sh; called by the
 // whole workgroup (NT threads), ends with a barrier.  Thread t polls words t, t + NT, ... of the sample's
-// (tile, group) block: one round trip per poll for up to 2 NT words, whose
-// values stay in registers.  A poll's verdict is the OR of one ballot per
+// (tile, group) block: one round trip per poll for up to LSE_CHAIN_HELD words,
+// whose values stay in registers.  A poll's verdict is the OR of one ballot per
 // wave through LDS, so every wave leaves the loop together.  Then, per thread
 // in fp64: C = sum n_j, S1 = sum n_j mean_j, S2 = sum (M2_j + n_j mean_j^2)
 // over its words, which all belong to group t % G; lanes of a wave with the
@@ -289,7 +297,7 @@ __device__ __forceinline__ void tile_valid(const ChainArgs &a, int tile, bool (&
 template <int NT, class Lds>
 __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bool write_global,
                                                float ga, float be, Lds &L) {
-  constexpr int kPer = 2;
+  constexpr int kPer = LSE_CHAIN_HELD / NT;  // words held per thread
   constexpr int kWaves = NT / kWave;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int qpg = 16 / a.G;
@@ -389,11 +397,11 @@ __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bo
 
 // LDS scratch of the 8-wave pair workgroup besides the x and W tiles.
 struct PairLds {
-  float wmean[2 * kThreads / kWave][16];  // per wave and group: mean, M2, count
-  float wm2[2 * kThreads / kWave][16];
-  float wcnt[2 * kThreads / kWave];
-  double mrg[2 * kThreads / kWave][16][3];  // per wave and group: C, S1, S2
-  uint32_t flags[2][2 * kThreads / kWave];  // per poll parity and wave: 1 missing, 2 gave up
+  float wmean[kTeams * kThreads / kWave][16];  // per wave and group: mean, M2, count
+  float wm2[kTeams * kThreads / kWave][16];
+  float wcnt[kTeams * kThreads / kWave];
+  double mrg[kTeams * kThreads / kWave][16][3];  // per wave and group: C, S1, S2
+  uint32_t flags[2][kTeams * kThreads / kWave];  // per poll parity and wave: 1 missing, 2 gave up
   // per channel, read 4 at a time: 2 log2(e) z = conv * sc + sh, z the tanh input
   alignas(16) float sc[kCout];
   alignas(16) float sh[kCout];
@@ -527,7 +535,7 @@ __device__ __forceinline__ void publish_pair_stats(const ChainArgs &a, int64_t n
   }
   __syncthreads();
   const int rt = wave;  // wave 0 combines team 0, wave 1 team 1
-  if (rt < 2 && lane < a.G && (rt == 0 || hasB)) {
+  if (rt < kTeams && lane < a.G && (rt == 0 || hasB)) {
     const int g = lane, tile = rt ? tB : tA;
     float N = 0.0f, mean = 0.0f, M2 = 0.0f;
 #pragma unroll
@@ -560,14 +568,14 @@ __device__ __forceinline__ void publish_pair_stats(const ChainArgs &a, int64_t n
 enum ChainMode { kFused = 0, kStats = 1, kApply = 2 };
 
 template <int MODE>
-__global__ __launch_bounds__(2 * kThreads)
+__global__ __launch_bounds__(kTeams * kThreads)
 __attribute__((amdgpu_waves_per_eu(LSE_CHAIN_PAIR_WAVES_PER_EU)))
 void conv_chain_pair_kernel(ChainArgs a) {
-  __shared__ float xs[2][kCin * kLdsH * kLdsW];
+  __shared__ float xs[kTeams][kCin * kLdsH * kLdsW];
   __shared__ float wl[kCout * kWStride];
   __shared__ PairLds L;
   __shared__ uint32_t s_ticket;
-  WRegs<2 * kThreads> wr;
+  WRegs<kTeams * kThreads> wr;
   load_w(a.w, wr);  // in flight while the ticket is claimed
   float ga = 1.0f, be = 0.0f;  // this thread's channel of gamma / beta (threads < 64)
   if (threadIdx.x < kCout) {
@@ -582,13 +590,13 @@ void conv_chain_pair_kernel(ChainArgs a) {
     __syncthreads();
     ticket = s_ticket;
   }
-  const uint32_t pairs = (uint32_t)(a.tiles + 1) / 2;
-  const int64_t n = ticket / pairs;
-  const int p = (int)(ticket - (uint32_t)n * pairs);
-  const int tA = 2 * p, tB = 2 * p + 1;
-  const bool hasB = tB < a.tiles;  // uniform
+  const uint32_t groups = (uint32_t)(a.tiles + kTeams - 1) / kTeams;  // workgroups per sample
+  const int64_t n = ticket / groups;
+  const int p = (int)(ticket - (uint32_t)n * groups);
+  const int tA = kTeams * p, tB = tA + 1;
+  const bool hasB = kTeams == 2 && tB < a.tiles;  // uniform
 
-  const int team = __builtin_amdgcn_readfirstlane(threadIdx.x / kThreads);  // 0: A, 1: B
+  const int team = kTeams == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kThreads);
   const int tid = threadIdx.x - team * kThreads;                           // within the team
   const int twave = tid / kWave;
   const bool active = team == 0 || hasB;                                   // uniform per wave
@@ -612,7 +620,7 @@ void conv_chain_pair_kernel(ChainArgs a) {
   }
   if constexpr (MODE != kApply) publish_pair_stats(a, n, tA, tB, hasB, active, acc, valid, L);
   if constexpr (MODE == kStats) return;
-  wait_and_merge<2 * kThreads>(a, n, tA == 0, ga, be, L);
+  wait_and_merge<kTeams * kThreads>(a, n, tA == 0, ga, be, L);
   if (active) tile_epilogue_lds(a, n, tile, acc, valid, L, twave);
 }
 
@@ -655,7 +663,7 @@ int64_t fused_pair_limit() {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, conv_chain_pair_kernel<kFused>,
-                                                   2 * kThreads, 0) != hipSuccess)
+                                                   kTeams * kThreads, 0) != hipSuccess)
     return 0;  // unknown: always the two-launch path
   v = std::max<int64_t>(1, (int64_t)cus * per_cu / 2);
   cached[dev].store(v, std::memory_order_relaxed);
@@ -697,9 +705,9 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
                      stream, reinterpret_cast<uint64_t *>(base + L.head), words);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t pairs = (L.tiles + 1) / 2;
-  const dim3 grid((uint32_t)(N * pairs)), block(2 * kThreads);
-  if (pairs <= fused_pair_limit()) {
+  const int64_t per_sample = (L.tiles + kTeams - 1) / kTeams;  // workgroups per sample
+  const dim3 grid((uint32_t)(N * per_sample)), block(kTeams * kThreads);
+  if (per_sample <= fused_pair_limit()) {
     hipLaunchKernelGGL(conv_chain_pair_kernel<kFused>, grid, block, 0, stream, a);
     return hipGetLastError();
   }

@@ -330,7 +330,7 @@ static lse_status_t check_chain(int64_t N, int64_t Cin, int64_t H, int64_t W, in
   if (!mul_ok(N, Cin, &t) || !mul_ok(t, H, &t) || !mul_ok(t, W, &t) || t > kMaxElems)
     return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: input size overflows");
   const int64_t tiles = ((H - K + 2) / 2) * ((W - K + 128) / 128);  // 2 x 128 pixel tiles
-  if (!mul_ok(N, (tiles + 1) / 2, &t) || t > 0xffffffffll)
+  if (!mul_ok(N, tiles, &t) || t > 0xffffffffll)  // workgroups: one or two tiles each
     return fail(LSE_ERR_SHAPE, "fused_conv_gn_act_lse: N x tiles too large for one launch");
   if (K != 3 || Cin != 8 || Cout != 64 || (16 % groups) != 0)
     return fail(LSE_ERR_UNSUPPORTED,
