@@ -50,10 +50,16 @@ KERNEL_SOURCES = ["log_softmax_reductions_amd/csrc/lse_rows.hip",
 
 
 def kernel_source_hash(files=KERNEL_SOURCES) -> str:
+    """sha256 (16 hex digits) of the kernel sources with comments and blank
+    space removed, so that only a change to the code retires a recorded
+    counter summary."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,4 +1,5 @@
-// lse_rows.hip — row-wise log_softmax over long contiguous rows, and the
+// lse_rows.hip — row-wise log_softmax (and softmax) over long rows whose
+// columns are contiguous (rows may sit any pitch ldx / ldy apart), and the
 // per-chunk (max, sum) partial / merge building blocks.
 //
 // POPCORNBENCH Kimi-K2.6 l1_p24 (LogSoftmax over dim 1 of (4096, 393216)):
