@@ -58,12 +58,18 @@ def _ptr_or_null(t, name):
     return None if t is None else _dev(t, name)
 
 
-def _workspace(nbytes, device, ws):
+def _workspace(nbytes, device, ws, stream=None):
+    """The caller's workspace, or a new one from torch's allocator.  A new one
+    is allocated on the current stream; when the call runs on another stream
+    it is recorded there, so the allocator does not reuse it before that
+    stream's kernels are done."""
     import torch
     if nbytes == 0:
         return ws, 0
     if ws is None:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if stream is not None:
+            ws.record_stream(stream)
     if ws.device.type != "cuda" or not ws.is_contiguous():
         raise ValueError("workspace must be a contiguous GPU tensor")
     return ws, ws.numel() * ws.element_size()
@@ -182,7 +188,7 @@ def _rows_call(fn, name, x, y, ws, stream):
     if y.shape != x.shape:
         raise ValueError("y must have x's shape")
     ldx, ldy = _ld(x, "x"), _ld(y, "y")
-    ws, ws_bytes = _workspace(log_softmax_rows_workspace_bytes(rows, cols), x.device, ws)
+    ws, ws_bytes = _workspace(log_softmax_rows_workspace_bytes(rows, cols), x.device, ws, stream)
     _lib.check(getattr(lib, fn)(_dev(x, "x", False), _dev(y, "y", False), rows, cols, ldx, ldy,
                                 None if ws is None else ctypes.c_void_p(ws.data_ptr()),
                                 ws_bytes, _stream(stream)), name)
@@ -274,7 +280,8 @@ def fused_conv_gn_act_lse(x, w, b, gamma, beta, groups: int, eps: float = 1e-5, 
     if out is None:
         out = torch.empty((N, 1, Ho, Wo), dtype=torch.float32, device=x.device)
     ws, ws_bytes = _workspace(
-        fused_conv_gn_act_lse_workspace_bytes(N, Cin, H, W, Cout, K, groups), x.device, ws)
+        fused_conv_gn_act_lse_workspace_bytes(N, Cin, H, W, Cout, K, groups), x.device, ws,
+        stream)
     _lib.check(lib.fused_conv_gn_act_lse(
         _dev(x, "x"), _dev(w, "w"), _ptr_or_null(b, "b"), _ptr_or_null(gamma, "gamma"),
         _ptr_or_null(beta, "beta"), N, Cin, H, W, Cout, K, groups, float(eps), _dev(out, "out"),

@@ -57,3 +57,22 @@ def test_constant_rows_are_log_of_length():
         torch.cuda.synchronize()
         ref = -torch.log(torch.tensor(float(cols), dtype=torch.float64)).item()
         assert (y.double() - ref).abs().max().item() <= 1e-5 + 2e-6 * abs(ref)
+
+
+def test_side_stream_with_internal_workspace(orc):
+    """A split row computed on a side stream with the workspace left to the
+    binding: the workspace is recorded on that stream, so allocations made on
+    the current stream meanwhile cannot take its memory."""
+    from tests.parity import compare
+    x = inputs.normal((8, 100000), seed=31, device=DEV)
+    chain = inputs.conv_chain_inputs(N=2, H=20, W=20, seed=5, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())   # the inputs exist before s reads them
+    y = L.log_softmax_rows(x, stream=s)
+    c = L.fused_conv_gn_act_lse(*chain, 16, 1e-5, stream=s)
+    churn = [torch.full((1 << 18,), 7.0, device=DEV) for _ in range(16)]
+    del churn
+    s.synchronize()
+    ref, _ = orc.log_softmax_rows(x.cpu().numpy(), want_y=True)
+    compare(y.cpu().numpy(), ref, what="side-stream log_softmax")
+    assert torch.isfinite(c).all()
