@@ -160,3 +160,24 @@ def test_chain_validation(lib):
     need = lib.fused_conv_gn_act_lse_workspace_bytes(128, 8, 128, 128, 64, 3, 16)
     # mean and rstd (N x G floats each), a 256-byte header, one 8-byte word per (n, tile, g)
     assert need == 2 * 128 * 16 * 4 + 256 + 128 * 63 * 16 * 8
+
+
+def test_last_error_is_per_thread(lib):
+    """Each host thread sees the detail of its own last failure."""
+    import threading
+    seen = {}
+
+    def worker(i):
+        rows = -1 - i
+        assert lib.log_softmax_rows(FAKE, FAKE2, rows, 8, None, 0, None) == LSE_ERR_SHAPE
+        for _ in range(200):
+            pass
+        seen[i] = lib.lse_last_error().decode()
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    for i in range(8):
+        assert f"rows = {-1 - i}" in seen[i], seen[i]

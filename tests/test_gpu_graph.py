@@ -97,3 +97,46 @@ def test_graph_axis_and_softmax():
         L.log_softmax_axis(x, 1, o2)
         L.softmax_rows(x3, o3, ws)
     _check_graph(run, [o1, o2, o3])
+
+
+def test_graph_strided_calls():
+    big = inputs.normal((6, 40, 300), seed=8, device=DEV)
+    x = big[:, 4:36, :256]                      # strided view: planes 300 apart, 256 wide
+    o1 = torch.empty((6, 256), device=DEV)
+    o2 = torch.empty((6, 32, 256), device=DEV)
+    rows_big = inputs.normal((8, 60004), seed=9, device=DEV)
+    xr = rows_big[:, :60000]                    # row pitch 60004
+    yr = torch.empty((8, 60000), device=DEV)
+    ws = torch.empty(L.log_softmax_rows_workspace_bytes(8, 60000), dtype=torch.uint8,
+                     device=DEV)
+
+    def run():
+        L.lse_reduce_axis(x, 1, o1)
+        L.log_softmax_axis(x, 1, o2)
+        L.log_softmax_rows(xr, yr, ws)
+    _check_graph(run, [o1, o2, yr])
+
+
+def test_concurrent_streams_match_sequential():
+    """Calls on two streams at once, each with its own workspace, give the
+    sequential results bit for bit: no state is shared between calls."""
+    xa = inputs.normal((16, 200000), seed=10, device=DEV)
+    xb = inputs.normal((16, 200000), seed=11, device=DEV)
+    ca = inputs.conv_chain_inputs(N=8, H=60, W=60, seed=12, device=DEV)
+    cb = inputs.conv_chain_inputs(N=8, H=60, W=60, seed=13, device=DEV)
+    seq = [L.log_softmax_rows(xa), L.log_softmax_rows(xb),
+           L.fused_conv_gn_act_lse(*ca, 16, 1e-5), L.fused_conv_gn_act_lse(*cb, 16, 1e-5)]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            ya = L.log_softmax_rows(xa)
+            oa = L.fused_conv_gn_act_lse(*ca, 16, 1e-5)
+        with torch.cuda.stream(s2):
+            yb = L.log_softmax_rows(xb)
+            ob = L.fused_conv_gn_act_lse(*cb, 16, 1e-5)
+        torch.cuda.synchronize()
+        for got, ref in zip((ya, yb, oa, ob), seq):
+            assert torch.equal(got, ref)
