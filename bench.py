@@ -125,7 +125,52 @@ def cpu_baseline(x_dev, target_s=10.0):
             "kind": "oracle",
             "sample": f"{rows_done} of {ROWS} rows (x {COLS} cols) of the same workload, "
                       f"fp64 log_softmax incl. the y write, {secs:.1f} s wall",
-            "value_1core": round(one, 4)}
+            "value_1core": round(one, 4), "cpu_model": cpu_model(),
+            "per_config": oracle_per_config(x_dev, threads)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_per_config(x_rows, threads):
+    """The same oracle on a bounded sample of each other configuration (about
+    a second each), in the unit of that configuration's GPU figure."""
+    import oracle
+    from log_softmax_reductions_amd import inputs
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    res = {}
+    x = inputs.make("axis0_large", "cuda")[:, :512].contiguous().cpu().numpy()   # (32, 512, 4096)
+    sec = timed(lambda: oracle.lse_axis0(x.reshape(32, -1), nthreads=threads))
+    res["axis0_large"] = {"value": round((x.size + x.size // 32) * 4 / sec / 1e9, 3),
+                          "unit": "GB/s", "sample": "512 of 2048 rows of B, all 32 planes"}
+    x = x_rows[:64].cpu().numpy()
+    sec = timed(lambda: oracle.softmax_rows(x, nthreads=threads))
+    res["softmax_large"] = {"value": round(x.size * 8 / sec / 1e9, 3), "unit": "GB/s",
+                            "sample": "64 of 4096 rows"}
+    x = inputs.normal((16, 64, 126 * 126), seed=12, device="cuda").cpu().numpy()
+    sec = timed(lambda: oracle.log_softmax_axis(x, nthreads=threads))
+    res["log_softmax_axis_chain_layout"] = {"value": round(x.size * 8 / sec / 1e9, 3),
+                                            "unit": "GB/s", "sample": "16 of 128 outer slices"}
+    xc, w, b, g, be = (t[:2] if i == 0 else t for i, t in
+                       enumerate(inputs.make("conv_chain", "cuda")))
+    cpu = [t.cpu().numpy() for t in (xc, w, b, g, be)]
+    sec = timed(lambda: oracle.fused_chain(*cpu, 16, 1e-5, nthreads=threads))
+    res["conv_chain"] = {"value": round(2 * 2 * 64 * 72 * 126 * 126 / sec / 1e12, 4),
+                         "unit": "conv TFLOP/s", "sample": "2 of 128 samples"}
+    return res
 
 
 def bench_rows_large(steps, warmup):
