@@ -364,8 +364,14 @@ LSE_EXPORT lse_status_t fused_conv_gn_act_lse(const float *x, const float *w, co
                 ws_bytes, need);
   const int64_t in_bytes = N * Cin * H * W * 4;
   const int64_t out_bytes = N * (H - K + 1) * (W - K + 1) * 4;
-  if (overlaps(x, in_bytes, out, out_bytes) || overlaps(ws, (int64_t)need, out, out_bytes) ||
-      overlaps(ws, (int64_t)need, x, in_bytes))
+  // every input (x, w, b, gamma, beta) against both buffers the call writes
+  const void *ins[5] = {x, w, b, gamma, beta};
+  const int64_t in_sizes[5] = {in_bytes, Cout * Cin * K * K * 4, Cout * 4, Cout * 4, Cout * 4};
+  bool clash = overlaps(ws, (int64_t)need, out, out_bytes);
+  for (int i = 0; i < 5; ++i)
+    clash = clash || (ins[i] && (overlaps(ins[i], in_sizes[i], out, out_bytes) ||
+                                 overlaps(ins[i], in_sizes[i], ws, (int64_t)need)));
+  if (clash)
     return fail(LSE_ERR_OVERLAP, "fused_conv_gn_act_lse: out / workspace overlap an input");
   return from_hip(lse::launch_conv_chain(x, w, b, gamma, beta, N, Cin, H, W, Cout, K, groups,
                                          eps, out, ws, stream),

@@ -157,6 +157,13 @@ def test_chain_validation(lib):
     assert lib.fused_conv_gn_act_lse(*args(G=32)) == LSE_ERR_UNSUPPORTED   # 2-channel groups
     assert lib.fused_conv_gn_act_lse(*args(ws=None)) == LSE_ERR_WORKSPACE
     assert lib.fused_conv_gn_act_lse(*args(wsb=16)) == LSE_ERR_WORKSPACE
+    # out or the workspace on top of w, b, gamma or beta
+    for i in (1, 2, 3, 4):
+        a = list(args())
+        a[i] = ctypes.c_void_p(0x5000000000 + 64)          # inside out
+        assert lib.fused_conv_gn_act_lse(*a) == LSE_ERR_OVERLAP
+        a[i] = ctypes.c_void_p(0x900000000 + 256)          # inside the workspace
+        assert lib.fused_conv_gn_act_lse(*a) == LSE_ERR_OVERLAP
     need = lib.fused_conv_gn_act_lse_workspace_bytes(128, 8, 128, 128, 64, 3, 16)
     # mean and rstd (N x G floats each), a 256-byte header, one 8-byte word per (n, tile, g)
     assert need == 2 * 128 * 16 * 4 + 256 + 128 * 63 * 16 * 8
