@@ -58,6 +58,25 @@ def _ptr_or_null(t, name):
     return None if t is None else _dev(t, name)
 
 
+def _on(*ts):
+    """Context that makes the tensors' GPU the current device, so the library
+    launches on the device that holds the memory; all tensors (None skipped)
+    must be on that one GPU."""
+    import torch
+    devs = {t.device for t in ts if isinstance(t, torch.Tensor)}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one GPU (got {sorted(map(str, devs))})")
+    d = devs.pop() if devs else None
+    if d is None or d.type != "cuda":
+        raise ValueError(f"tensors must be on the GPU (got {d})")
+    return torch.cuda.device(d)
+
+
+def _numel(t, n, name):
+    if t is not None and t.numel() != n:
+        raise ValueError(f"{name} must have {n} elements (got {t.numel()})")
+
+
 def _workspace(nbytes, device, ws, stream=None):
     """The caller's workspace, or a new one from torch's allocator.  A new one
     is allocated on the current stream; when the call runs on another stream
@@ -89,8 +108,9 @@ def lse_reduce_axis0(x, out=None, stream=None):
         out = torch.empty(x.shape[1:], dtype=torch.float32, device=x.device)
     if out.numel() != inner:
         raise ValueError("out has the wrong number of elements")
-    _lib.check(lib.lse_reduce_axis0(_dev(x, "x"), _dev(out, "out"), R, inner, _stream(stream)),
-               "lse_reduce_axis0")
+    with _on(x, out):
+        _lib.check(lib.lse_reduce_axis0(_dev(x, "x"), _dev(out, "out"), R, inner,
+                                        _stream(stream)), "lse_reduce_axis0")
     return out
 
 
@@ -145,9 +165,10 @@ def lse_reduce_axis(x, dim, out=None, stream=None):
         raise ValueError(f"out must have shape {shape}")
     xso, xsr = _strided_axis(x, d, "x")
     oso, _ = _strided_axis(out.unsqueeze(d), d, "out")
-    _lib.check(lib.lse_reduce_axis_strided(_dev(x, "x", False), _dev(out, "out", False), outer,
-                                           R, inner, xso, xsr, oso, _stream(stream)),
-               "lse_reduce_axis")
+    with _on(x, out):
+        _lib.check(lib.lse_reduce_axis_strided(_dev(x, "x", False), _dev(out, "out", False),
+                                               outer, R, inner, xso, xsr, oso, _stream(stream)),
+                   "lse_reduce_axis")
     return out
 
 
@@ -163,9 +184,10 @@ def log_softmax_axis(x, dim, y=None, stream=None):
         raise ValueError("y must have x's shape")
     xso, xsr = _strided_axis(x, d, "x")
     yso, ysr = _strided_axis(y, d, "y")
-    _lib.check(lib.log_softmax_axis_strided(_dev(x, "x", False), _dev(y, "y", False), outer, R,
-                                            inner, xso, xsr, yso, ysr, _stream(stream)),
-               "log_softmax_axis")
+    with _on(x, y):
+        _lib.check(lib.log_softmax_axis_strided(_dev(x, "x", False), _dev(y, "y", False), outer,
+                                                R, inner, xso, xsr, yso, ysr, _stream(stream)),
+                   "log_softmax_axis")
     return y
 
 
@@ -188,10 +210,12 @@ def _rows_call(fn, name, x, y, ws, stream):
     if y.shape != x.shape:
         raise ValueError("y must have x's shape")
     ldx, ldy = _ld(x, "x"), _ld(y, "y")
-    ws, ws_bytes = _workspace(log_softmax_rows_workspace_bytes(rows, cols), x.device, ws, stream)
-    _lib.check(getattr(lib, fn)(_dev(x, "x", False), _dev(y, "y", False), rows, cols, ldx, ldy,
-                                None if ws is None else ctypes.c_void_p(ws.data_ptr()),
-                                ws_bytes, _stream(stream)), name)
+    with _on(x, y, ws):
+        ws, ws_bytes = _workspace(log_softmax_rows_workspace_bytes(rows, cols), x.device, ws,
+                                  stream)
+        _lib.check(getattr(lib, fn)(_dev(x, "x", False), _dev(y, "y", False), rows, cols, ldx,
+                                    ldy, None if ws is None else ctypes.c_void_p(ws.data_ptr()),
+                                    ws_bytes, _stream(stream)), name)
     return y
 
 
@@ -241,9 +265,10 @@ def lse_rows_partial(x, chunk: int, partials=None, stream=None):
         partials = torch.empty((rows, k, 2), dtype=torch.float32, device=x.device)
     if partials.numel() != rows * k * 2:
         raise ValueError("partials has the wrong size")
-    _lib.check(lib.lse_rows_partial(_dev(x, "x"), rows, cols, chunk,
-                                    _dev(partials, "partials"), _stream(stream)),
-               "lse_rows_partial")
+    with _on(x, partials):
+        _lib.check(lib.lse_rows_partial(_dev(x, "x"), rows, cols, chunk,
+                                        _dev(partials, "partials"), _stream(stream)),
+                   "lse_rows_partial")
     return partials
 
 
@@ -256,8 +281,11 @@ def lse_rows_merge(partials, row_lse=None, stream=None):
     rows, k, _ = partials.shape
     if row_lse is None:
         row_lse = torch.empty(rows, dtype=torch.float32, device=partials.device)
-    _lib.check(lib.lse_rows_merge(_dev(partials, "partials"), rows, k, _dev(row_lse, "row_lse"),
-                                  _stream(stream)), "lse_rows_merge")
+    _numel(row_lse, rows, "row_lse")
+    with _on(partials, row_lse):
+        _lib.check(lib.lse_rows_merge(_dev(partials, "partials"), rows, k,
+                                      _dev(row_lse, "row_lse"), _stream(stream)),
+                   "lse_rows_merge")
     return row_lse
 
 
@@ -277,14 +305,19 @@ def fused_conv_gn_act_lse(x, w, b, gamma, beta, groups: int, eps: float = 1e-5, 
     if Cin2 != Cin or K2 != K:
         raise ValueError("w does not match x")
     Ho, Wo = H - K + 1, W - K + 1
+    for t, name in ((b, "b"), (gamma, "gamma"), (beta, "beta")):
+        _numel(t, Cout, name)
     if out is None:
         out = torch.empty((N, 1, Ho, Wo), dtype=torch.float32, device=x.device)
-    ws, ws_bytes = _workspace(
-        fused_conv_gn_act_lse_workspace_bytes(N, Cin, H, W, Cout, K, groups), x.device, ws,
-        stream)
-    _lib.check(lib.fused_conv_gn_act_lse(
-        _dev(x, "x"), _dev(w, "w"), _ptr_or_null(b, "b"), _ptr_or_null(gamma, "gamma"),
-        _ptr_or_null(beta, "beta"), N, Cin, H, W, Cout, K, groups, float(eps), _dev(out, "out"),
-        None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream(stream)),
-        "fused_conv_gn_act_lse")
+    if Ho > 0 and Wo > 0:
+        _numel(out, N * Ho * Wo, "out")
+    with _on(x, w, b, gamma, beta, out, ws):
+        ws, ws_bytes = _workspace(
+            fused_conv_gn_act_lse_workspace_bytes(N, Cin, H, W, Cout, K, groups), x.device, ws,
+            stream)
+        _lib.check(lib.fused_conv_gn_act_lse(
+            _dev(x, "x"), _dev(w, "w"), _ptr_or_null(b, "b"), _ptr_or_null(gamma, "gamma"),
+            _ptr_or_null(beta, "beta"), N, Cin, H, W, Cout, K, groups, float(eps),
+            _dev(out, "out"), None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes,
+            _stream(stream)), "fused_conv_gn_act_lse")
     return out

@@ -63,3 +63,24 @@ def test_row_pitch():
     assert _ld(torch.empty(1, 100), "x") == 100
     with pytest.raises(ValueError, match="contiguous"):
         _ld(torch.empty(100, 4).t(), "x")
+
+
+def test_tensors_must_share_one_gpu():
+    from log_softmax_reductions_amd import _on
+    with pytest.raises(ValueError, match="one GPU"):
+        _on(torch.empty(2), torch.empty(2, device="meta"))
+    with pytest.raises(ValueError, match="on the GPU"):
+        _on(torch.empty(2), None)
+
+
+def test_chain_and_merge_sizes_checked_before_the_call():
+    """Buffers the library would read or write past their end are refused."""
+    x, w = torch.zeros(2, 8, 10, 10), torch.zeros(64, 8, 3, 3)
+    with pytest.raises(ValueError, match="b must have 64"):
+        L.fused_conv_gn_act_lse(x, w, torch.zeros(32), None, None, 16)
+    with pytest.raises(ValueError, match="gamma must have 64"):
+        L.fused_conv_gn_act_lse(x, w, None, torch.zeros(65), None, 16)
+    with pytest.raises(ValueError, match="out must have 128"):
+        L.fused_conv_gn_act_lse(x, w, None, None, None, 16, out=torch.zeros(2, 1, 8, 7))
+    with pytest.raises(ValueError, match="row_lse must have 3"):
+        L.lse_rows_merge(torch.zeros(3, 4, 2), row_lse=torch.zeros(2))
