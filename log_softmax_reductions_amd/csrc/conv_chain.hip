@@ -506,9 +506,10 @@ __device__ __forceinline__ void publish_pair_stats(const ChainArgs &a, int64_t n
       mu[t] = row16_sum(sacc);
     }
     group_sum(mu, qpg);
+    const float inv_cnt = (px > 0) ? 1.0f / cnt : 0.0f;  // one division for the 4 groups
 #pragma unroll
     for (int t = 0; t < kMT; ++t) {
-      mu[t] = (px > 0) ? mu[t] / cnt : 0.0f;
+      mu[t] *= inv_cnt;
       float sacc = 0.0f;
 #pragma unroll
       for (int blk = 0; blk < kNB; ++blk)
