@@ -122,11 +122,36 @@ __device__ __forceinline__ void load_plane(const float *p, float (&v)[W][RB], in
 // a reference to the by-value kernel argument (a helper, a struct) they cost
 // the plane-split kernel ~75 VGPRs.
 
-// One lane = W consecutive inner outputs of one outer index.
-template <int W>
-__device__ __forceinline__ bool axis_item(const AxisDims &d, int64_t &o, int64_t &q) {
+#ifndef LSE_AXIS_XCD_REMAP
+#define LSE_AXIS_XCD_REMAP 1
+#endif
+// Workgroups are handed to the 8 XCDs round robin (workgroup b to XCD b % 8),
+// each XCD with its own L2.  When x or a plane's byte stride is not aligned to
+// the 128-byte cache line, neighbouring output runs share the line at their
+// boundary in every plane, and neighbours on different XCDs both fetch it
+// (measured: 1.11 x the algorithmic bytes read).  Such calls deal the runs to
+// the XCDs in 8 contiguous ranges, neighbours on one XCD: workgroup b takes run
+// (b % 8) F + b / 8, F = grid / 8, for b < 8 F (a bijection; the last grid % 8
+// keep their index).  With aligned planes the plain order measured faster.
+__device__ __forceinline__ int64_t xcd_block(const float *x, int64_t plane_stride) {
+  const int64_t b = blockIdx.x;
+#if LSE_AXIS_XCD_REMAP
+  if (plane_stride % 32 != 0 || ((uintptr_t)x & 127) != 0) {  // uniform
+    const int64_t f = gridDim.x / 8;
+    if (b < 8 * f) return (b % 8) * f + b / 8;
+  }
+#endif
+  return b;
+}
+
+// One lane = W consecutive inner outputs of one outer index; NT threads per
+// workgroup (the launch's block size: a constant, where blockDim.x would be
+// read from the dispatch packet with a vector load).
+template <int W, int NT>
+__device__ __forceinline__ bool axis_item(const AxisDims &d, const float *x, int64_t plane_stride,
+                                          int64_t &o, int64_t &q) {
   const int64_t nq = d.inner / W;  // W > 1: inner % W == 0 by dispatch
-  const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t item = xcd_block(x, plane_stride) * NT + threadIdx.x;
   if (item >= d.outer * nq) return false;
   o = (d.outer == 1) ? 0 : item / nq;
   q = item - o * nq;
@@ -173,9 +198,9 @@ __device__ __forceinline__ void store_w(float *p, const float (&r)[W]) {
 template <int RB, int W, bool STR>
 __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
     const float *__restrict__ x, float *__restrict__ out, AxisDims d) {
-  int64_t o, q;
-  if (!axis_item<W>(d, o, q)) return;
   const int64_t st_xsr = STR ? d.xsr : d.inner;
+  int64_t o, q;
+  if (!axis_item<W, kAxis0Threads>(d, x, st_xsr, o, q)) return;
   const int64_t st_xso = STR ? d.xso : d.R * d.inner;
   const int64_t st_yso = STR ? d.yso : d.inner;
   const int64_t R = d.R;
@@ -204,9 +229,9 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
 template <int RB, int W, bool STR>
 __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
     const float *__restrict__ x, float *__restrict__ y, AxisDims d) {
-  int64_t o, q;
-  if (!axis_item<W>(d, o, q)) return;
   const int64_t st_xsr = STR ? d.xsr : d.inner;
+  int64_t o, q;
+  if (!axis_item<W, kLsmThreads>(d, x, st_xsr, o, q)) return;
   const int64_t st_xso = STR ? d.xso : d.R * d.inner;
   const int64_t st_ysr = STR ? d.ysr : d.inner;
   const int64_t st_yso = STR ? d.yso : d.R * d.inner;
@@ -291,7 +316,7 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   const int wv = wid % P, grp = wid / P;
   const int64_t R = d.R;
   const int64_t nq = d.inner / W;  // W > 1: inner % W == 0 by dispatch
-  const int64_t item = ((int64_t)blockIdx.x * G + grp) * kWave + lane;
+  const int64_t item = (xcd_block(x, st_xsr) * G + grp) * kWave + lane;
   const bool valid = item < d.outer * nq;
   int64_t o = 0, q = 0;
   if (valid) {
