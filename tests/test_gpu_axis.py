@@ -94,3 +94,26 @@ def test_axis_split_special_values(orc, R):
     xm.copy_(x)
     compare(L.log_softmax_axis(xm, 1).cpu().numpy(), orc.log_softmax_axis(xc),
             what=f"misaligned lsm R={R}")
+
+
+@pytest.mark.parametrize("outer,R,inner,offset", [
+    (1, 9, 4 * 64 * 29 + 4, 0),    # misaligned planes: 30 = 8 x 3 + 6 one-wave workgroups
+    (1, 20, 4 * 64 * 5 + 4, 0),    # 6 workgroups, fewer than 8: plain order
+    (3, 40, 4 * 64 * 16 + 12, 0),  # plane split (R >= 33), misaligned planes
+    (2, 9, 4 * 64 * 19, 4),        # aligned stride, x 16 B past a cache line: 38 workgroups
+])
+def test_xcd_order_covers_every_output_once(orc, outer, R, inner, offset):
+    """Misaligned planes or base: workgroups take their output runs in the
+    XCD-grouped order, whose last grid % 8 workgroups keep their own index;
+    every output must still be written exactly once."""
+    buf = inputs.normal((outer * R * inner + offset,), seed=inner + offset, sigma=3.0, device=DEV)
+    x = buf[offset:].view(outer, R, inner)
+    out = torch.full((outer, inner), float("nan"), device=DEV)
+    y = torch.full((outer, R, inner), float("nan"), device=DEV)
+    L.lse_reduce_axis(x, 1, out)
+    L.log_softmax_axis(x, 1, y)
+    torch.cuda.synchronize()
+    xc = x.cpu().numpy()
+    compare(out.cpu().numpy(), orc.lse_axis(xc), what=f"lse_axis {outer}x{R}x{inner}+{offset}")
+    compare(y.cpu().numpy(), orc.log_softmax_axis(xc),
+            what=f"lsm_axis {outer}x{R}x{inner}+{offset}")
