@@ -24,7 +24,10 @@
 // workgroups once its last ticket is claimed, which needs only as many
 // co-resident workgroups as a sample has tile pairs (32 for 126 x 126;
 // hundreds fit).  The wait is still bounded (poll count and 0.1 s); a workgroup that
-// gives up flags the workspace and writes NaN.
+// gives up flags the workspace and writes NaN.  A sample with more tile pairs
+// than half of what the device holds at once takes two launches instead: one
+// publishes the statistics, the next recomputes the conv and applies them
+// (the conv runs twice, nothing waits; the results are identical).
 //
 // GEMM shape per sample: D[c][p] = sum_k W[c][k] * patch[k][p] with c the 64
 // output channels (M), p the pixels (N) and k = (ci, kh, kw), 72 values (K).
