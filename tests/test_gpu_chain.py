@@ -106,3 +106,37 @@ def test_chain_nan_input_poisons_only_its_sample(orc):
     compare(oc, ref, rtol=RTOL_CHAIN, what="nan sample")
     err_word = ws[256 * ((2 * 3 * 16 * 4 + 255) // 256) + 4:][:4].view(torch.int32).item()
     assert err_word == 0          # the wait itself completed normally
+
+
+def test_chain_zero_input_is_log_of_channel_count():
+    """x = 0 without bias: the conv is 0, every group has variance 0, so the
+    normalised value is 0, tanh 0 = 0, hardswish 0 = 0, and each output is the
+    LSE of 64 zeros, log 64; the statistics are mean 0, rstd 1/sqrt(eps)."""
+    x, w, _, _, _ = _chain_inputs(2, 9, 140, seed=8)
+    x.zero_()
+    ws = torch.empty(L.fused_conv_gn_act_lse_workspace_bytes(2, 8, 9, 140, 64, 3, 16),
+                     dtype=torch.uint8, device=DEV)
+    out = L.fused_conv_gn_act_lse(x, w, None, None, None, 16, 1e-5, ws=ws)
+    torch.cuda.synchronize()
+    oc = out.cpu().numpy().astype(np.float64)
+    assert np.abs(oc - math.log(64)).max() <= 1e-6
+    stats = ws[: 2 * 2 * 16 * 4].view(torch.float32).cpu().numpy().astype(np.float64)
+    assert (stats[:32] == 0).all()
+    assert np.abs(stats[32:] - 1 / math.sqrt(1e-5)).max() <= 1e-4 * 316.3
+
+
+@pytest.mark.parametrize("scale", [1e3, 1e-3, -50.0])
+def test_chain_input_scales(orc, scale):
+    """Inputs far from unit scale: large conv values (the LSE shift carries
+    them), tiny ones (GroupNorm rescales them), and a sign flip."""
+    x, w, b, g, be = _chain_inputs(2, 12, 70, seed=int(abs(scale) * 7) + 1, affine=True)
+    x.mul_(scale)
+    _check(orc, x, w, b, g, be, 8, f"scale {scale}")
+
+
+def test_chain_constant_input(orc):
+    """A constant image: each channel's conv is one value over all pixels, so a
+    group's variance is that of its 4 channel values."""
+    x, w, _, _, _ = _chain_inputs(1, 10, 40, seed=9)
+    x.fill_(0.75)
+    _check(orc, x, w, None, None, None, 16, "constant input")
