@@ -1,7 +1,11 @@
 """Empty and degenerate inputs through every entry point on the GPU: empty
 tensors are no-ops that return empty results, and the sizes whose result the
 definition fixes exactly are checked bit for bit (one value reduced gives
-itself; one column gives log_softmax 0 and softmax 1; -inf stays -inf)."""
+itself; one column gives log_softmax 0 and softmax 1; -inf stays -inf).  The
+invariants of the definition are checked on the GPU results too: R equal
+values give v + log R, a shift moves the LSE by the shift, and the order of
+the reduced values does not matter."""
+import numpy as np
 import pytest
 import torch
 
@@ -76,3 +80,46 @@ def test_side_stream_with_internal_workspace(orc):
     ref, _ = orc.log_softmax_rows(x.cpu().numpy(), want_y=True)
     compare(y.cpu().numpy(), ref, what="side-stream log_softmax")
     assert torch.isfinite(c).all()
+
+
+@pytest.mark.parametrize("R,inner", [(4, 320), (32, 4096), (64, 15876), (300, 257)])
+def test_equal_planes_give_value_plus_log_R(R, inner):
+    """R equal values v: LSE = v + log R on every path (register-resident,
+    streamed, plane split); log_softmax is -log R."""
+    for v in (-3.5, 0.0, 1e4):
+        x = torch.full((R, inner), v, device=DEV)
+        out = L.lse_reduce_axis0(x)
+        y = L.log_softmax_axis(x.view(1, R, inner), 1)
+        torch.cuda.synchronize()
+        ref = v + np.log(R)
+        assert np.abs(out.cpu().numpy().astype(np.float64) - ref).max() <= 1e-5 + 2e-6 * abs(ref)
+        lr = -np.log(R)
+        assert np.abs(y.cpu().numpy().astype(np.float64) - lr).max() <= 1e-5 + 2e-6 * abs(lr)
+
+
+def test_shift_moves_lse_by_the_shift():
+    """LSE(x + c) = LSE(x) + c and log_softmax(x + c) = log_softmax(x), up to
+    the rounding of x + c, on the three layouts."""
+    x = inputs.normal((16, 3000), seed=41, sigma=2.0, device=DEV)
+    for c in (-1000.0, 3.75, 1000.0):
+        xc = x + c
+        a0, a1 = L.lse_reduce_axis0(x), L.lse_reduce_axis0(xc)
+        r0, r1 = L.log_softmax_rows(x), L.log_softmax_rows(xc)
+        torch.cuda.synchronize()
+        # |x + c| ~ 1000 carries an fp32 rounding of up to 2^-14 per element
+        tol = 1e-5 + 2e-6 * abs(c) + (6.2e-5 if abs(c) >= 1000 else 0.0)
+        assert (a1.double() - (a0.double() + c)).abs().max().item() <= tol + 2e-6 * abs(c)
+        assert (r1.double() - r0.double()).abs().max().item() <= tol
+
+
+def test_plane_order_does_not_matter():
+    """Permuting the reduced axis permutes nothing in logsumexp (same result up
+    to summation order) and permutes log_softmax's planes alike."""
+    x = inputs.normal((2, 48, 1000), seed=43, sigma=3.0, device=DEV)
+    perm = torch.randperm(48, generator=torch.Generator().manual_seed(5)).to(DEV)
+    xp = x[:, perm].contiguous()
+    a, b = L.lse_reduce_axis(x, 1), L.lse_reduce_axis(xp, 1)
+    y, yp = L.log_softmax_axis(x, 1), L.log_softmax_axis(xp, 1)
+    torch.cuda.synchronize()
+    assert (a.double() - b.double()).abs().max().item() <= 1e-5 + 2e-6 * a.abs().max().item()
+    assert (y[:, perm].double() - yp.double()).abs().max().item() <= 2e-5
