@@ -507,12 +507,31 @@ hipError_t launch_axis(const float *x, float *out, const AxisDims &d, hipStream_
 
 }  // namespace
 
+#ifndef LSE_AXIS_ROWS_MINR_LSE
+#define LSE_AXIS_ROWS_MINR_LSE 512
+#endif
+#ifndef LSE_AXIS_ROWS_MINR_LSM
+#define LSE_AXIS_ROWS_MINR_LSM 256
+#endif
+// A reduction over a contiguous last axis (inner = 1, unit R stride) is a row
+// reduction: from a few hundred values per row on, one workgroup per row
+// reads the row as one contiguous span, where the axis kernels would give each
+// lane a row of its own.
+static bool as_rows(const AxisDims &d, bool lsm) {
+  const int64_t minr = lsm ? LSE_AXIS_ROWS_MINR_LSM : LSE_AXIS_ROWS_MINR_LSE;
+  return d.inner == 1 && d.xsr == 1 && (!lsm || d.ysr == 1) && d.R >= minr &&
+         d.outer <= 0x7fffffff;
+}
+
 hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream) {
+  if (as_rows(d, false)) return launch_rows_lse(x, d.outer, d.R, d.xso, out, d.yso, stream);
   return launch_axis<false>(x, out, d, stream);
 }
 
 hipError_t launch_log_softmax_axis(const float *x, float *y, const AxisDims &d,
                                    hipStream_t stream) {
+  if (as_rows(d, true))
+    return launch_log_softmax_rows_no_ws(x, y, d.outer, d.R, d.xso, d.yso, stream);
   return launch_axis<true>(x, y, d, stream);
 }
 

@@ -59,6 +59,14 @@ hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, i
 hipError_t launch_lse_rows_merge(const void *partials, int64_t rows,
                                  int64_t nchunks, float *row_lse,
                                  hipStream_t stream);
+// One workgroup per row, no workspace: out[r * ldo] = LSE of row r, and
+// log_softmax / softmax of rows of any length (rows longer than the register
+// tile re-read x).
+hipError_t launch_rows_lse(const float *x, int64_t rows, int64_t cols, int64_t ldx, float *out,
+                           int64_t ldo, hipStream_t stream);
+hipError_t launch_log_softmax_rows_no_ws(const float *x, float *y, int64_t rows, int64_t cols,
+                                         int64_t ldx, int64_t ldy, hipStream_t stream,
+                                         bool softmax = false);
 void set_spin_limit(uint32_t polls);
 uint32_t chain_spin_limit();
 

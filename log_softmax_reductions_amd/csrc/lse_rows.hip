@@ -352,6 +352,187 @@ __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_stream_kernel(
   if (threadIdx.x == 0) partials[t] = make_float2(m, s);
 }
 
+// ---------------------------------------------------------- whole rows
+// One workgroup per row and no workspace: the form the generic-axis calls
+// take when they reduce a contiguous last axis (they have no workspace
+// argument).  The logsumexp is written straight to out[row * ldo]; rows that
+// fit the register tile are read once from registers, longer ones are read
+// once with the online (max, sum) recurrence.  log_softmax / softmax of rows
+// longer than the register tile take the pair the same way and then write y
+// in a second pass over x.
+
+// The logsumexp of one (max, sum) pair, with the merge's conventions.
+__device__ __forceinline__ float pair_lse(float m, float s) {
+  if (s != s) return __builtin_nanf("");
+  return is_finite(m) ? m + logf(s) : m;
+}
+
+// stream_chunk_pair with 128-bit loads (VEC: p 16-byte aligned, len % 4 == 0).
+template <bool VEC>
+__device__ __forceinline__ void stream_row_pair(const float *__restrict__ p, int64_t len,
+                                                float *red, float &m, float &s) {
+  if constexpr (!VEC) {
+    stream_chunk_pair(p, len, red, m, s);
+  } else {
+    const v4f *p4 = reinterpret_cast<const v4f *>(p);
+    const int64_t n4 = len / 4;
+    float lm = -__builtin_inff();
+    for (int64_t i = threadIdx.x; i < n4; i += kRowsThreads) {
+      const v4f f = p4[i];
+      lm = fmaxf(lm, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
+    }
+    m = block_allreduce<kNW>(lm, OpMax{}, red);
+    float ls = 0.0f;
+    if (is_finite(m)) {
+      for (int64_t i = threadIdx.x; i < n4; i += kRowsThreads) {
+        const v4f f = p4[i];
+        ls += (exp_base2(f.x - m) + exp_base2(f.y - m)) + (exp_base2(f.z - m) + exp_base2(f.w - m));
+      }
+    } else {
+      for (int64_t i = threadIdx.x; i < n4; i += kRowsThreads) {
+        const v4f f = p4[i];
+        ls += (pair_term_general(f.x, m) + pair_term_general(f.y, m)) +
+              (pair_term_general(f.z, m) + pair_term_general(f.w, m));
+      }
+    }
+    s = block_allreduce<kNW>(ls, OpSum{}, red);
+  }
+}
+
+#ifndef LSE_ROWS_STREAM_ONLINE
+#define LSE_ROWS_STREAM_ONLINE 1   // whole streamed rows: one pass with the online recurrence
+#endif
+
+// Running pair of one lane: fold values into (m, s) with the online
+// recurrence of the log_softmax page: a new maximum rescales the sum by
+// exp(m_old - m_new), then each value adds exp(v - m).  The same conventions
+// as chunk_pair: m is the largest non-NaN value, s counts +inf values when
+// m = +inf, is 0 while m = -inf, and becomes NaN with any NaN.
+struct OnlinePair {
+  float m = -__builtin_inff(), s = 0.0f;
+  __device__ __forceinline__ void rescale_to(float mn) {
+    if (mn != m) {  // m < mn: exp(m - mn) is 0 when m = -inf or mn = +inf
+      s *= exp_base2(m - mn);
+      m = mn;
+    }
+  }
+  __device__ __forceinline__ void add4(float a, float b, float c, float d) {
+    rescale_to(fmaxf(m, fmaxf(fmaxf(a, b), fmaxf(c, d))));
+    if (is_finite(m))
+      s += (exp_base2(a - m) + exp_base2(b - m)) + (exp_base2(c - m) + exp_base2(d - m));
+    else
+      s += (pair_term_nonfinite(a, m) + pair_term_nonfinite(b, m)) +
+           (pair_term_nonfinite(c, m) + pair_term_nonfinite(d, m));
+  }
+  __device__ __forceinline__ void add1(float a) {
+    rescale_to(fmaxf(m, a));
+    s += is_finite(m) ? exp_base2(a - m) : pair_term_nonfinite(a, m);
+  }
+};
+
+// The pair of a whole row read once: each lane folds its strided values with
+// OnlinePair, then the lanes' pairs are merged (weights exp(m_lane - M)).
+template <bool VEC>
+__device__ __forceinline__ void online_row_pair(const float *__restrict__ p, int64_t len,
+                                                float *red, float &M, float &S) {
+  OnlinePair op;
+  if constexpr (VEC) {
+    const v4f *p4 = reinterpret_cast<const v4f *>(p);
+    const int64_t n4 = len / 4;
+    int64_t i = threadIdx.x;
+    constexpr int U = 4;  // loads in flight per lane
+    for (; i + (U - 1) * kRowsThreads < n4; i += U * kRowsThreads) {
+      v4f f[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) f[u] = __builtin_nontemporal_load(p4 + i + u * kRowsThreads);
+#pragma unroll
+      for (int u = 0; u < U; ++u) op.add4(f[u].x, f[u].y, f[u].z, f[u].w);
+    }
+    for (; i < n4; i += kRowsThreads) {
+      const v4f f = __builtin_nontemporal_load(p4 + i);
+      op.add4(f.x, f.y, f.z, f.w);
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) op.add1(p[i]);
+  }
+  M = block_allreduce<kNW>(op.m, OpMax{}, red);
+  const float w = (op.m == M) ? 1.0f : exp_base2(op.m - M);
+  S = block_allreduce<kNW>(op.s * w, OpSum{}, red);
+}
+
+template <bool VEC>
+__device__ __forceinline__ void whole_row_pair(const float *__restrict__ p, int64_t len,
+                                               float *red, float &m, float &s) {
+#if LSE_ROWS_STREAM_ONLINE
+  online_row_pair<VEC>(p, len, red, m, s);
+#else
+  stream_row_pair<VEC>(p, len, red, m, s);
+#endif
+}
+
+template <int VPL, bool VEC>
+__global__ __launch_bounds__(kRowsThreads) void rows_lse_kernel(const float *__restrict__ x,
+                                                                int64_t cols, int64_t ldx,
+                                                                float *__restrict__ out,
+                                                                int64_t ldo) {
+  __shared__ float red[kNW];
+  const int64_t row = blockIdx.x;
+  float v[VPL];
+  load_chunk<VPL, VEC>(x + row * ldx, cols, v);
+  float m, s;
+  chunk_pair<VPL>(v, red, m, s);
+  if (threadIdx.x == 0) out[row * ldo] = pair_lse(m, s);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kRowsThreads) void rows_lse_stream_kernel(
+    const float *__restrict__ x, int64_t cols, int64_t ldx, float *__restrict__ out,
+    int64_t ldo) {
+  __shared__ float red[kNW];
+  const int64_t row = blockIdx.x;
+  float m, s;
+  whole_row_pair<VEC>(x + row * ldx, cols, red, m, s);
+  if (threadIdx.x == 0) out[row * ldo] = pair_lse(m, s);
+}
+
+template <bool VEC, bool SOFTMAX>
+__global__ __launch_bounds__(kRowsThreads) void rows_stream_write_kernel(
+    const float *__restrict__ x, float *__restrict__ y, int64_t cols, int64_t ldx,
+    int64_t ldy) {
+  __shared__ float red[kNW];
+  const int64_t row = blockIdx.x;
+  const float *xr = x + row * ldx;
+  float *yr = y + row * ldy;
+  float M, S;
+  whole_row_pair<VEC>(xr, cols, red, M, S);
+  const float k = out_scale<SOFTMAX>(S);
+  if constexpr (VEC) {
+    const v4f *x4 = reinterpret_cast<const v4f *>(xr);
+    const int64_t n4 = cols / 4;
+    int64_t i = threadIdx.x;
+    constexpr int U = 4;  // loads in flight per lane
+    for (; i + (U - 1) * kRowsThreads < n4; i += U * kRowsThreads) {
+      v4f f[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) f[u] = __builtin_nontemporal_load(x4 + i + u * kRowsThreads);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t j = 4 * (i + u * kRowsThreads);
+        store4(yr + j, out_value<SOFTMAX>(f[u].x, M, k), out_value<SOFTMAX>(f[u].y, M, k),
+               out_value<SOFTMAX>(f[u].z, M, k), out_value<SOFTMAX>(f[u].w, M, k));
+      }
+    }
+    for (; i < n4; i += kRowsThreads) {
+      const v4f f = __builtin_nontemporal_load(x4 + i);
+      store4(yr + 4 * i, out_value<SOFTMAX>(f.x, M, k), out_value<SOFTMAX>(f.y, M, k),
+             out_value<SOFTMAX>(f.z, M, k), out_value<SOFTMAX>(f.w, M, k));
+    }
+  } else {
+    for (int64_t i = threadIdx.x; i < cols; i += kRowsThreads)
+      yr[i] = out_value<SOFTMAX>(xr[i], M, k);
+  }
+}
+
 // One wave per row: row_lse = M + log(S) of the row's nchunks pairs.
 __global__ __launch_bounds__(256) void lse_rows_merge_kernel(const float2 *__restrict__ partials,
                                                              int64_t rows, int64_t nchunks,
@@ -510,6 +691,62 @@ hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, i
       return hipErrorInvalidValue;
   }
 #undef LSE_PART_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_lse(const float *x, int64_t rows, int64_t cols, int64_t ldx, float *out,
+                           int64_t ldo, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((uint32_t)rows);
+  const bool vec = (cols % 4 == 0) && (ldx % 4 == 0) && ((uintptr_t)x % 16 == 0);
+  if (cols > kRowsTile) {
+    if (vec)
+      hipLaunchKernelGGL(rows_lse_stream_kernel<true>, grid, dim3(kRowsThreads), 0, stream, x,
+                         cols, ldx, out, ldo);
+    else
+      hipLaunchKernelGGL(rows_lse_stream_kernel<false>, grid, dim3(kRowsThreads), 0, stream, x,
+                         cols, ldx, out, ldo);
+    return hipGetLastError();
+  }
+#define LSE_ROWLSE_CASE(V)                                                                     \
+  case V:                                                                                      \
+    if (vec)                                                                                   \
+      hipLaunchKernelGGL((rows_lse_kernel<V, true>), grid, dim3(kRowsThreads), 0, stream, x,   \
+                         cols, ldx, out, ldo);                                                 \
+    else                                                                                       \
+      hipLaunchKernelGGL((rows_lse_kernel<V, false>), grid, dim3(kRowsThreads), 0, stream, x,  \
+                         cols, ldx, out, ldo);                                                 \
+    break;
+  switch (vpl_for(cols)) {
+    LSE_ROWLSE_CASE(4)
+    LSE_ROWLSE_CASE(8)
+    LSE_ROWLSE_CASE(16)
+    LSE_ROWLSE_CASE(32)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef LSE_ROWLSE_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_log_softmax_rows_no_ws(const float *x, float *y, int64_t rows, int64_t cols,
+                                         int64_t ldx, int64_t ldy, hipStream_t stream,
+                                         bool softmax) {
+  if (rows == 0) return hipSuccess;
+  if (cols <= kRowsTile)  // one chunk per row: the register kernel needs no workspace
+    return launch_log_softmax_rows(x, y, rows, cols, ldx, ldy, nullptr, stream, softmax);
+  const dim3 grid((uint32_t)rows);
+  const bool vec = (cols % 4 == 0) && (ldx % 4 == 0) && (ldy % 4 == 0) &&
+                   ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0);
+#define LSE_ROWSTREAM(V, S)                                                                    \
+  hipLaunchKernelGGL((rows_stream_write_kernel<V, S>), grid, dim3(kRowsThreads), 0, stream, x, \
+                     y, cols, ldx, ldy)
+  if (vec) {
+    if (softmax) LSE_ROWSTREAM(true, true); else LSE_ROWSTREAM(true, false);
+  } else {
+    if (softmax) LSE_ROWSTREAM(false, true); else LSE_ROWSTREAM(false, false);
+  }
+#undef LSE_ROWSTREAM
   return hipGetLastError();
 }
 

@@ -117,3 +117,44 @@ def test_xcd_order_covers_every_output_once(orc, outer, R, inner, offset):
     compare(out.cpu().numpy(), orc.lse_axis(xc), what=f"lse_axis {outer}x{R}x{inner}+{offset}")
     compare(y.cpu().numpy(), orc.log_softmax_axis(xc),
             what=f"lsm_axis {outer}x{R}x{inner}+{offset}")
+
+
+@pytest.mark.parametrize("rows,cols,pad", [(3, 1024, 0), (5, 5000, 0), (2, 16384, 0),
+                                           (3, 16388, 0), (2, 100000, 0), (1, 393216, 0),
+                                           (4, 1027, 0), (6, 3000, 5), (3, 40000, 4)])
+def test_last_axis_as_rows(orc, rows, cols, pad):
+    """Reducing a contiguous last axis of 1024 values or more runs one
+    workgroup per row (register tile up to 16384 columns, streamed beyond);
+    rows may be `pad` floats apart (a column slice)."""
+    big = inputs.normal((rows, cols + pad), seed=rows * 131 + cols, sigma=3.0, device=DEV)
+    x = big[:, :cols]
+    xc = x.contiguous().cpu().numpy().reshape(rows, cols, 1)
+    out = L.lse_reduce_axis(x, 1)
+    y = L.log_softmax_axis(x, 1)
+    torch.cuda.synchronize()
+    compare(out.cpu().numpy(), orc.lse_axis(xc).reshape(rows), what=f"lse last axis {rows}x{cols}")
+    compare(y.cpu().numpy(), orc.log_softmax_axis(xc).reshape(rows, cols),
+            what=f"lsm last axis {rows}x{cols}")
+    # the same values through the row entry point: log_softmax identical bit for bit
+    # on the register-tile path
+    if cols <= 16384:
+        assert torch.equal(L.log_softmax_rows(x), y)
+
+
+def test_last_axis_special_values(orc):
+    x = inputs.normal((6, 20000), seed=77, sigma=2.0, device=DEV)
+    x[0, :] = -float("inf")
+    x[1, 123] = float("inf")
+    x[2, 4567] = float("nan")
+    x[3, :] = -float("inf"); x[3, 19999] = 1.5
+    x[4, 5] = float("inf"); x[4, 6] = float("nan")
+    for xv in (x, x[:, :5000]):          # streamed rows, register-tile rows
+        xc = xv.contiguous().cpu().numpy()
+        out = L.lse_reduce_axis(xv, 1)
+        y = L.log_softmax_axis(xv, 1)
+        torch.cuda.synchronize()
+        r = xc.shape
+        compare(out.cpu().numpy(), orc.lse_axis(xc.reshape(*r, 1)).reshape(r[0]),
+                what=f"lse last axis special {r}")
+        compare(y.cpu().numpy(), orc.log_softmax_axis(xc.reshape(*r, 1)).reshape(r),
+                what=f"lsm last axis special {r}")
