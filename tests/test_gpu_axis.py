@@ -121,7 +121,9 @@ def test_xcd_order_covers_every_output_once(orc, outer, R, inner, offset):
 
 @pytest.mark.parametrize("rows,cols,pad", [(3, 1024, 0), (5, 5000, 0), (2, 16384, 0),
                                            (3, 16388, 0), (2, 100000, 0), (1, 393216, 0),
-                                           (4, 1027, 0), (6, 3000, 5), (3, 40000, 4)])
+                                           (4, 1027, 0), (6, 3000, 5), (3, 40000, 4),
+                                           # streamed rows with scalar loads
+                                           (2, 20001, 0), (2, 30000, 3)])
 def test_last_axis_as_rows(orc, rows, cols, pad):
     """Reducing a contiguous last axis of 1024 values or more runs one
     workgroup per row (register tile up to 16384 columns, streamed beyond);
