@@ -223,6 +223,164 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
   store_w<W>(out + o * st_yso + q * W, r);
 }
 
+#ifndef LSE_AXIS_WALK
+#define LSE_AXIS_WALK 1   // wide aligned logsumexp over many planes walks them (lse_axis_walk_kernel)
+#endif
+#ifndef LSE_AXIS_WALK_VL
+#define LSE_AXIS_WALK_VL 4   // 16-byte loads per lane and plane
+#endif
+#ifndef LSE_AXIS_WALK_THREADS
+#define LSE_AXIS_WALK_THREADS 512
+#endif
+#ifndef LSE_AXIS_WALK_MINR
+#define LSE_AXIS_WALK_MINR 33   // from here up the walk measured faster than blocks of 32 planes
+#endif
+#ifndef LSE_AXIS_WALK_MIN_BLOCKS
+#define LSE_AXIS_WALK_MIN_BLOCKS 512   // workgroups the walk needs to fill the GPU
+#endif
+constexpr int kWalkThreads = LSE_AXIS_WALK_THREADS;
+constexpr int kWalkVl = LSE_AXIS_WALK_VL;
+constexpr int64_t kWalkCols = (int64_t)kWalkThreads * 4 * kWalkVl;  // outputs per workgroup
+// Sums against the lane's reference value that stay inside [kWalkLo, kWalkHi]
+// are kept: nothing that matters has under- or overflowed, and c and log s
+// (|log s| <= 16.7) cancel by at most a few ulps of 16 when added.
+constexpr float kWalkLo = 9.5367431640625e-07f;  // 2^-20
+constexpr float kWalkHi = 16777216.0f;           // 2^24
+
+// Exact fold of one value into a running (m, s): fold_block with one plane.
+__device__ __forceinline__ void fold_one(float v, float &m, float &s) {
+  const float mn = fmaxf(m, v);
+  const float c = safe_shift(mn);
+  const float acc = (s == 0.0f) ? 0.0f : s * exp_base2(safe_shift(m) - c);
+  m = mn;
+  s = acc + exp_base2(v - c);
+}
+
+// out[o, j] = LSE_r x[o, r, j] for wide aligned planes, planes visited one at a
+// time.  A workgroup owns kWalkCols consecutive outputs; wave w reads the
+// contiguous 64 x 4 x VL outputs' span of each plane (lane l its VL vectors
+// 256 outputs apart), so the workgroup streams kWalkCols x 4 bytes contiguous
+// per plane, where the register-block kernel has each wave touch RB planes
+// 1 KiB at a time.
+//
+// A column's R values no longer sit in registers together, and a running max
+// per column would cost a rescale exponential per new max.  Instead every
+// column of a lane is summed against one reference c, the largest of the
+// lane's plane-0 values: s = sum_r exp(x_r - c), one exponential per value,
+// and LSE = c + log s, the same quantity (and exactly x for a single finite
+// value, v + log R for R equal ones, as with the column's max).  A lane whose
+// sums all stay inside [2^-20, 2^24] is done: no term that matters under- or
+// overflowed, and the final sum loses at most a few ulps.  Any other lane (a
+// column more than ~14 below or ~16 above c, a non-finite value or reference)
+// redoes its columns, one vector at a time, with the exact running fold of
+// fold_block, which also gives the special-value results.
+template <int VL, bool STR>
+__global__ __launch_bounds__(kWalkThreads) void lse_axis_walk_kernel(
+    const float *__restrict__ x, float *__restrict__ out, AxisDims d) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  constexpr int NV = 4 * VL;
+  const int64_t st_xsr = STR ? d.xsr : d.inner;
+  const int64_t st_xso = STR ? d.xso : d.R * d.inner;
+  const int64_t st_yso = STR ? d.yso : d.inner;
+  const int64_t tiles = (d.inner + kWalkCols - 1) / kWalkCols;
+  const int64_t b = blockIdx.x;
+  const int64_t o = (d.outer == 1) ? 0 : b / tiles;
+  const int64_t t = b - o * tiles;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  // The tile's first output; this lane's vector k starts jl + 4 kWave k past it.
+  const int64_t tb = t * kWalkCols;
+  const uint32_t jl = (uint32_t)wave * (kWave * 4 * VL) + 4 * lane;
+  // A ragged last tile clamps the vectors past the end onto the plane's last
+  // vector (inner % 4 == 0): loads stay in bounds, and those columns are not
+  // stored.  Offsets within a tile fit 32 bits, so every load is a uniform
+  // plane pointer plus a 32-bit lane offset.
+  const bool full = tb + kWalkCols <= d.inner;  // uniform
+  uint32_t off[VL];  // byte offsets within the tile
+#pragma unroll
+  for (int k = 0; k < VL; ++k) {
+    const uint32_t j = jl + 4 * kWave * k;
+    off[k] = 4 * ((full || tb + j < d.inner) ? j : (uint32_t)(d.inner - 4 - tb));
+  }
+  const float *xt = x + o * st_xso + tb;
+  const int64_t R = d.R;
+
+  typedef __attribute__((address_space(1))) const char gbyte;
+  typedef __attribute__((address_space(1))) const v4f gv4f;
+  auto load = [&](float (&v)[NV], const float *plane) {
+    // The empty asm statements pin the plane pointer to scalar registers and
+    // the lane offsets to 32-bit vector registers at the loads, so each load
+    // is one scalar base plus a 32-bit offset.  Without them, loop strength
+    // reduction keeps one 64-bit vector pointer per load (32 VGPRs).
+    gbyte *p = (gbyte *)plane;
+    asm volatile("" : "+s"(p));
+#pragma unroll
+    for (int k = 0; k < VL; ++k) {
+      uint32_t ok = off[k];
+      asm volatile("" : "+v"(ok));
+      const v4f q = __builtin_nontemporal_load((gv4f *)(p + ok));
+      v[4 * k] = q.x; v[4 * k + 1] = q.y; v[4 * k + 2] = q.z; v[4 * k + 3] = q.w;
+    }
+  };
+  float va[NV], s[NV];
+  load(va, xt);
+  float lm = va[0];  // the lane's reference c
+#pragma unroll
+  for (int i = 1; i < NV; ++i) lm = fmaxf(lm, va[i]);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) s[i] = 0.0f;
+  auto acc = [&](const float (&v)[NV]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s[i] += exp_base2(v[i] - lm);
+  };
+  acc(va);
+  for (int64_t r = 1; r < R; ++r) {
+    load(va, xt + r * st_xsr);
+    acc(va);
+  }
+  float lo = s[0], hi = s[0], tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    lo = fminf(lo, s[i]);
+    hi = fmaxf(hi, s[i]);
+    tot += s[i];  // a NaN sum survives here (fminf and fmaxf drop it)
+  }
+  float *op = out + o * st_yso + tb;
+  if (lo >= kWalkLo && hi <= kWalkHi && tot <= kWalkHi * NV) {
+#pragma unroll
+    for (int k = 0; k < VL; ++k) {
+      const uint32_t j = jl + 4 * kWave * k;
+      if (full || tb + j < d.inner) {
+        v4f q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = lm + logf(s[4 * k + e]);
+        *reinterpret_cast<v4f *>(op + j) = q;
+      }
+    }
+  } else {
+    // Rare: this lane's columns again, exactly, one vector of 4 at a time.
+    for (int k = 0; k < VL; ++k) {
+      const uint32_t j = jl + 4 * kWave * k;
+      if (!(full || tb + j < d.inner)) continue;
+      float m4[4], s4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m4[e] = -__builtin_inff();
+        s4[e] = 0.0f;
+      }
+      for (int64_t r = 0; r < R; ++r) {
+        const v4f q = *reinterpret_cast<const v4f *>(xt + r * st_xsr + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fold_one(q[e], m4[e], s4[e]);
+      }
+      v4f res;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) res[e] = m4[e] + logf(s4[e]);
+      *reinterpret_cast<v4f *>(op + j) = res;
+    }
+  }
+}
+
 // y[o, r, j] = x[o, r, j] - LSE_r' x[o, r', j].  With R <= RB the R values stay
 // in registers between the reduction and the write (one read, one write);
 // otherwise a streaming reduction pass and a write pass (two reads).
@@ -474,6 +632,20 @@ hipError_t launch_axis_t(const float *x, float *out, const AxisDims &d, hipStrea
     while (P > 1 && R < 8 * (int64_t)P) P /= 2;
     if (P > 1) return launch_split_p<RBW, false, STR>(P, x, out, d, stream);
   }
+#if LSE_AXIS_WALK
+  if constexpr (!LSM) {
+    // Many wide aligned planes: the plane walk, when its tiles are mostly real
+    // columns (at most 1/8 padding) and there are enough of them.  Up to 32
+    // planes the register-block kernel below is as fast or faster.
+    const int64_t tiles = (d.inner + kWalkCols - 1) / kWalkCols;
+    if (vec && R >= LSE_AXIS_WALK_MINR && d.outer * tiles >= LSE_AXIS_WALK_MIN_BLOCKS &&
+        tiles * kWalkCols * 8 <= d.inner * 9 && d.outer * tiles <= 0x7fffffff) {
+      hipLaunchKernelGGL((lse_axis_walk_kernel<kWalkVl, STR>), dim3((uint32_t)(d.outer * tiles)),
+                         dim3(kWalkThreads), 0, stream, x, out, d);
+      return hipGetLastError();
+    }
+  }
+#endif
   if (R <= 4) return launch_rb<4, LSM, STR>(x, out, d, vec, stream);
   if (R <= 8 || LSE_AXIS0_RBMAX <= 8) return launch_rb<8, LSM, STR>(x, out, d, vec, stream);
   if (R <= 16 || LSE_AXIS0_RBMAX <= 16) return launch_rb<16, LSM, STR>(x, out, d, vec, stream);
