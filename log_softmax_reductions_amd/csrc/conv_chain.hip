@@ -42,6 +42,7 @@
 // permlane swaps).
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "lse_device.hpp"
 #include "lse_internal.hpp"
@@ -75,6 +76,17 @@ static_assert(kTeams == 1 || kTeams == 2, "one or two tiles per workgroup");
 // (12 (l % 16) + 9 (l / 16) is distinct mod 64 for the 64 lanes).
 constexpr int kWStride = kKdim + 4;                                      // 76
 constexpr int kWF4 = kCout * kKdim / 4;                                  // 1152 float4
+
+#ifndef LSE_CHAIN_WINO
+#define LSE_CHAIN_WINO 1   // the 3x3 contraction as Winograd F(2x2, 3x3) on MFMA
+#endif
+constexpr bool kWino = LSE_CHAIN_WINO != 0;
+static_assert(!kWino || kTeams == 2, "the Winograd weight staging uses one thread per (o, ci)");
+// Transformed weights U in LDS in MFMA fragment order [p][ks][t][lane]: p the
+// 16 Winograd positions, ks the half of the 8 input channels, t the M-tile,
+// lane 16 q + i holding U[p][16 t + i][4 ks + q].
+constexpr int kWinoU = 16 * 2 * kMT * kWave;                             // 8192 floats
+constexpr int kWLds = kWino ? kWinoU : kCout * kWStride;
 
 struct ChainWsHeader {
   uint32_t ticket;  // next tile ticket
@@ -251,6 +263,124 @@ __device__ __forceinline__ void conv_tile(const ChainArgs &a, const float *xs, c
   }
 }
 
+// Winograd F(2x2, 3x3) (Lavin and Gray, "Fast Algorithms for Convolutional
+// Neural Networks"): a 2 x 2 block of outputs of the 3 x 3 correlation is
+// Y = A^T [(G g G^T) . (B^T d B)] A over the block's 4 x 4 input window d, with
+//   B^T = [1 0 -1 0; 0 1 1 0; 0 -1 1 0; 0 1 0 -1],
+//   G   = [1 0 0; 1/2 1/2 1/2; 1/2 -1/2 1/2; 0 0 1],
+//   A^T = [1 1 1 0; 0 1 -1 -1],
+// so per block and output channel o the 16 products at positions p are sums
+// over the input channels, M[p][o] = sum_ci U[p][o][ci] V[p][ci] (U = G g G^T
+// per (o, ci), V = B^T d B per ci): 16 GEMMs with K = 8 instead of one with
+// K = 72, 2.25 times fewer multiply-adds.  The transforms are exact up to
+// fp32 rounding (coefficients 0, +-1, +-1/2).
+
+// W arrives as (o, ci, kh, kw) rows of 9; thread o * 8 + ci holds its 3 x 3
+// filter (loaded before the ticket is known) and writes its 16 U values.
+struct WinoW {
+  float g[9];
+};
+
+__device__ __forceinline__ void load_w(const float *__restrict__ w, WinoW &r) {
+  const float *g = w + threadIdx.x * 9;  // 512 threads = 64 x 8 filters
+#pragma unroll
+  for (int k = 0; k < 9; ++k) r.g[k] = g[k];
+}
+
+__device__ __forceinline__ void store_w(const WinoW &r, float *ul) {
+  const int o = threadIdx.x / kCin, ci = threadIdx.x % kCin;
+  const int t = o / 16, i = o % 16, ks = ci / 4, q = ci % 4;
+  float h[4][3];  // G g
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const float g0 = r.g[c], g1 = r.g[3 + c], g2 = r.g[6 + c];
+    h[0][c] = g0;
+    h[1][c] = 0.5f * (g0 + g1 + g2);
+    h[2][c] = 0.5f * (g0 - g1 + g2);
+    h[3][c] = g2;
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const float u[4] = {h[a][0], 0.5f * (h[a][0] + h[a][1] + h[a][2]),
+                        0.5f * (h[a][0] - h[a][1] + h[a][2]), h[a][2]};
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      ul[(((4 * a + b) * 2 + ks) * kMT + t) * kWave + 16 * q + i] = u[b];
+  }
+}
+
+// The wave's 16 Winograd blocks (MFMA N = 16: lane i takes block i, output
+// rows 0-1 and columns 32 twave + 2 i + {0, 1} of the tile) for all 64 output
+// channels.  acc[2 dy + dx][t] ends as the conv output (bias included) at
+// (dy, dx) of the lane's block, channels 16 t + 4 q + r: the layout of
+// conv_tile with the pixel of (blk, lane) moved.  Row a of M at a time: the
+// lane builds V for its input channels q and 4 + q (B^T rows need two input
+// rows), then per M-tile 8 MFMAs give M[4 a + j] for j = 0..3, which fold
+// into Y by A (columns) and A^T (row a's sign).
+__device__ __forceinline__ void conv_tile_wino(const ChainArgs &a, const float *xs,
+                                               const float *ul, int twave,
+                                               f32x4 (&acc)[kNB][kMT]) {
+  const int lane = threadIdx.x % kWave;
+  const int li = lane % 16, q = lane / 16;
+#pragma unroll
+  for (int t = 0; t < kMT; ++t) {
+    f32x4 bias;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bias[r] = a.b ? a.b[16 * t + 4 * q + r] : 0.0f;
+#pragma unroll
+    for (int blk = 0; blk < kNB; ++blk) acc[blk][t] = bias;
+  }
+  const float *xq = xs + q * (kLdsH * kLdsW) + 2 * (16 * twave + li);
+  const float *uq = ul + lane;
+#pragma unroll
+  for (int ar = 0; ar < 4; ++ar) {
+    // Row ar of B^T d combines input rows (r0, r1) with sign sg: d_r0 + sg d_r1.
+    const int r0 = (ar == 0) ? 0 : (ar == 2 ? 2 : 1);
+    const int r1 = (ar == 0) ? 2 : (ar == 3 ? 3 : (ar == 1 ? 2 : 1));
+    const float sg = (ar == 1) ? 1.0f : -1.0f;
+    float v[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const float *xc = xq + ks * (4 * kLdsH * kLdsW);
+      const float2 p0 = *reinterpret_cast<const float2 *>(xc + r0 * kLdsW);
+      const float2 p1 = *reinterpret_cast<const float2 *>(xc + r0 * kLdsW + 2);
+      const float2 n0 = *reinterpret_cast<const float2 *>(xc + r1 * kLdsW);
+      const float2 n1 = *reinterpret_cast<const float2 *>(xc + r1 * kLdsW + 2);
+      const float e0 = fmaf(sg, n0.x, p0.x), e1 = fmaf(sg, n0.y, p0.y);
+      const float e2 = fmaf(sg, n1.x, p1.x), e3 = fmaf(sg, n1.y, p1.y);
+      v[ks][0] = e0 - e2;
+      v[ks][1] = e1 + e2;
+      v[ks][2] = e2 - e1;
+      v[ks][3] = e1 - e3;
+    }
+#pragma unroll
+    for (int t = 0; t < kMT; ++t) {
+      f32x4 m[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          m[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+              uq[(((4 * ar + j) * 2 + ks) * kMT + t) * kWave], v[ks][j], m[j], 0, 0, 0);
+      const f32x4 P0 = m[0] + m[1] + m[2];  // (M A) column 0 of row ar
+      const f32x4 P1 = m[1] - m[2] - m[3];  // column 1
+      if (ar <= 2) {                        // A^T row 0: rows 0, 1, 2 with +1
+        acc[0][t] += P0;
+        acc[1][t] += P1;
+      }
+      if (ar == 1) {                        // A^T row 1: +1, -1, -1 on rows 1, 2, 3
+        acc[2][t] += P0;
+        acc[3][t] += P1;
+      } else if (ar >= 2) {
+        acc[2][t] -= P0;
+        acc[3][t] -= P1;
+      }
+    }
+  }
+}
+
 // Tile-statistics word: low 32 bits the tile mean, high 32 bits -M2.  M2 >= 0,
 // so the high word always has its sign bit set and a written word is never 0.
 __device__ __forceinline__ uint64_t pack_stats(float mean, float m2) {
@@ -277,13 +407,29 @@ __device__ __forceinline__ double tile_count(const ChainArgs &a, int j, int qpg,
 
 constexpr uint64_t kChainWaitTicks = 10000000ull;  // 0.1 s of the 100 MHz counter
 
+// Tile-relative pixel of accumulator block blk in lane i of team wave w:
+// direct conv, row w / 2 and 16-pixel block blk of the wave's 64 columns;
+// Winograd, (dy, dx) = (blk / 2, blk % 2) of the lane's 2 x 2 block.
+__device__ __forceinline__ void pixel_of(int blk, int li, int wave, int &dh, int &dw) {
+  if constexpr (kWino) {
+    dh = blk / 2;
+    dw = 32 * wave + 2 * li + blk % 2;
+  } else {
+    dh = wave / 2;
+    dw = (wave % 2) * 64 + 16 * blk + li;
+  }
+}
+
 __device__ __forceinline__ void tile_valid(const ChainArgs &a, int tile, bool (&valid)[kNB],
                                            int wave) {
   const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
   const int li = threadIdx.x % 16;
-  const int h = th * kTileH + wave / 2, w = tw * kTileW + (wave % 2) * 64 + li;
 #pragma unroll
-  for (int blk = 0; blk < kNB; ++blk) valid[blk] = (h < a.Ho) && (w + 16 * blk < a.Wo);
+  for (int blk = 0; blk < kNB; ++blk) {
+    int dh, dw;
+    pixel_of(blk, li, wave, dh, dw);
+    valid[blk] = (th * kTileH + dh < a.Ho) && (tw * kTileW + dw < a.Wo);
+  }
 }
 
 // Wait until every tile of sample n has published, then merge the sample's
@@ -420,7 +566,6 @@ __device__ __forceinline__ void tile_epilogue_lds(const ChainArgs &a, int64_t n,
   const int lane = threadIdx.x % kWave;
   const int li = lane % 16, q = lane / 16;
   const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
-  const int h = th * kTileH + wave / 2, w0 = tw * kTileW + (wave % 2) * 64;
 #pragma unroll
   for (int blk = 0; blk < kNB; ++blk) {
     float u[kMT][4];
@@ -446,8 +591,11 @@ __device__ __forceinline__ void tile_epilogue_lds(const ChainArgs &a, int64_t n,
 #pragma unroll
       for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(fmaf(u[t][r], kLog2e, -c2));
     const float S = across_quads(s, OpSum{});
-    if (q == 0 && valid[blk])
-      a.out[(n * a.Ho + h) * (int64_t)a.Wo + w0 + 16 * blk + li] = M + logf(S);
+    if (q == 0 && valid[blk]) {
+      int dh, dw;
+      pixel_of(blk, li, wave, dh, dw);
+      a.out[(n * a.Ho + th * kTileH + dh) * (int64_t)a.Wo + tw * kTileW + dw] = M + logf(S);
+    }
   }
 }
 
@@ -575,12 +723,13 @@ template <int MODE>
 __global__ __launch_bounds__(kTeams * kThreads)
 __attribute__((amdgpu_waves_per_eu(LSE_CHAIN_PAIR_WAVES_PER_EU)))
 void conv_chain_pair_kernel(ChainArgs a) {
-  __shared__ float xs[kTeams][kCin * kLdsH * kLdsW];
-  __shared__ float wl[kCout * kWStride];
+  __shared__ alignas(16) float xs[kTeams][kCin * kLdsH * kLdsW];
+  __shared__ alignas(16) float wl[kWLds];  // W rows, or U in fragment order (Winograd)
   __shared__ PairLds L;
   __shared__ uint32_t s_ticket;
-  WRegs<kTeams * kThreads> wr;
-  load_w(a.w, wr);  // in flight while the ticket is claimed
+  // W's loads are in flight while the ticket is claimed.
+  std::conditional_t<kWino, WinoW, WRegs<kTeams * kThreads>> wr;
+  load_w(a.w, wr);
   float ga = 1.0f, be = 0.0f;  // this thread's channel of gamma / beta (threads < 64)
   if (threadIdx.x < kCout) {
     if (a.gamma) ga = a.gamma[threadIdx.x];
@@ -612,14 +761,17 @@ void conv_chain_pair_kernel(ChainArgs a) {
     const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
     load_x(a, n, th * kTileH, tw * kTileW, xr, tid);
   }
-  store_w(wr, wl);
+  store_w(wr, wl);  // W rows, or U (Winograd)
   if (active) store_x(xr, xs[team], tid);
   __syncthreads();
 
   f32x4 acc[kNB][kMT];
   bool valid[kNB];
   if (active) {
-    conv_tile(a, xs[team], wl, pr, pc0, acc);
+    if constexpr (kWino)
+      conv_tile_wino(a, xs[team], wl, twave, acc);
+    else
+      conv_tile(a, xs[team], wl, pr, pc0, acc);
     tile_valid(a, tile, valid, twave);
   }
   if constexpr (MODE != kApply) publish_pair_stats(a, n, tA, tB, hasB, active, acc, valid, L);
