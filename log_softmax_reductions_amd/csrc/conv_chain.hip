@@ -1,5 +1,6 @@
 // conv_chain.hip — conv2d 3x3 -> GroupNorm -> tanh -> hardswish -> residual
-// add -> logsumexp over channels, fused around an fp32 MFMA implicit GEMM.
+// add -> logsumexp over channels, fused around the conv on fp32 MFMA (as
+// Winograd F(2x2, 3x3), or a direct implicit GEMM when LSE_CHAIN_WINO=0).
 //
 // POPCORNBENCH Kimi-K2.6 l2_p92: the model's forward is x_conv = conv(x);
 // GroupNorm (mean and population variance per (sample, group) over the
@@ -29,8 +30,11 @@
 // publishes the statistics, the next recomputes the conv and applies them
 // (the conv runs twice, nothing waits; the results are identical).
 //
-// GEMM shape per sample: D[c][p] = sum_k W[c][k] * patch[k][p] with c the 64
-// output channels (M), p the pixels (N) and k = (ci, kh, kw), 72 values (K).
+// Direct form (conv_tile), GEMM shape per sample: D[c][p] = sum_k W[c][k] *
+// patch[k][p] with c the 64 output channels (M), p the pixels (N) and
+// k = (ci, kh, kw), 72 values (K).  The Winograd form (conv_tile_wino) has
+// the same operand roles with p a 2 x 2 output block and K the 8 input
+// channels, once per Winograd position.
 // v_mfma_f32_16x16x4_f32 operands, lane l = 0..63, i = l % 16, q = l / 16:
 //   A (16x4):  lane l holds A[i][q]          -> W[16t + i][4s + q]
 //   B (4x16):  lane l holds B[q][i]          -> patch[4s + q][pixel i]
@@ -81,6 +85,9 @@ constexpr int kWF4 = kCout * kKdim / 4;                                  // 1152
 #define LSE_CHAIN_WINO 1   // the 3x3 contraction as Winograd F(2x2, 3x3) on MFMA
 #endif
 constexpr bool kWino = LSE_CHAIN_WINO != 0;
+#ifndef LSE_CHAIN_WINO_SB
+#define LSE_CHAIN_WINO_SB 2   // scheduling barriers in the Winograd loop: 1 per row of M, 2 also per M-tile
+#endif
 static_assert(!kWino || kTeams == 2, "the Winograd weight staging uses one thread per (o, ci)");
 // Transformed weights U in LDS in MFMA fragment order [p][ks][t][lane]: p the
 // 16 Winograd positions, ks the half of the 8 input channels, t the M-tile,
@@ -377,7 +384,13 @@ __device__ __forceinline__ void conv_tile_wino(const ChainArgs &a, const float *
         acc[2][t] -= P0;
         acc[3][t] -= P1;
       }
+#if LSE_CHAIN_WINO_SB >= 2
+      __builtin_amdgcn_sched_barrier(0);
+#endif
     }
+#if LSE_CHAIN_WINO_SB >= 1
+    __builtin_amdgcn_sched_barrier(0);
+#endif
   }
 }
 
