@@ -20,7 +20,7 @@ rank 0 prints ONE JSON line.
 
 Flags: --gpus N (only 1 is supported: this build runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --no-secondary,
---only {rows_large,axis0_large,conv_chain,softmax_large,axis_chain_layout,copy}
+--only {rows_large,axis0_large,axis0_walk,conv_chain,softmax_large,axis_chain_layout,copy}
 to run just that kernel
 (for profiler runs; prints timing only).
 """
@@ -209,6 +209,16 @@ def bench_secondary(steps=10, warmup=3):
                           "ms": round(avg, 4), "GB/s": round(nbytes / avg / 1e6, 1),
                           "hbm_frac": round(nbytes / avg / 1e6 / HBM_PEAK_GBS, 4)}
     del x, o
+    # many planes: logsumexp over dim 0 of (64, 4194304) takes the plane walk
+    x = inputs.normal((64, 4194304), seed=13, sigma=2.0, device="cuda")
+    o = torch.empty((4194304,), device="cuda")
+    wall, ev = timed_launches(lambda: L.lse_reduce_axis0(x, o), steps, warmup)
+    nbytes = x.numel() * 4 + o.numel() * 4
+    avg = sum(ev) / len(ev)
+    out["axis0_walk"] = {"workload": "logsumexp dim=0 (64,4194304) fp32 N(0,4)",
+                         "ms": round(avg, 4), "GB/s": round(nbytes / avg / 1e6, 1),
+                         "hbm_frac": round(nbytes / avg / 1e6 / HBM_PEAK_GBS, 4)}
+    del x, o
     # conv chain (128, 8, 128, 128) -> (128, 1, 126, 126)
     x, w, b, g, be = inputs.make("conv_chain", "cuda")
     o = torch.empty((128, 1, 126, 126), device="cuda")
@@ -217,14 +227,20 @@ def bench_secondary(steps=10, warmup=3):
     wall, ev = timed_launches(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, o, ws),
                               steps, warmup)
     avg = sum(ev) / len(ev)
-    flop = 2 * 128 * 64 * 8 * 9 * 126 * 126   # one conv, counted once
+    flop = 2 * 128 * 64 * 8 * 9 * 126 * 126   # one direct conv, counted once
+    # Winograd F(2x2, 3x3): 16 positions x 64 x 8 multiply-adds per 2x2 block;
+    # 63 tile rows x 64 blocks per sample (the last block column is padding).
+    mfma_flop = 2 * 16 * 64 * 8 * 63 * 64 * 128
     out["conv_chain"] = {"workload": "conv3x3 8->64, GN16, tanh, hardswish, +res, LSE dim=1, "
                                      "x (128,8,128,128)",
                          "ms": round(avg, 4), "conv_TFLOP/s": round(flop / avg / 1e9, 2),
                          "mfma_frac_of_fp32_peak": round(flop / avg / 1e9 / FP32_MFMA_PEAK_TFLOPS,
                                                          4),
-                         "note": "one fused kernel: the conv runs once on fp32 MFMA; each "
-                                 "sample's GroupNorm statistics are merged across workgroups"}
+                         "executed_mfma_TFLOP/s": round(mfma_flop / avg / 1e9, 2),
+                         "note": "one fused kernel: conv_TFLOP/s counts the direct conv's "
+                                 "18.73 GFLOP; the kernel computes it as Winograd F(2x2,3x3) "
+                                 "on fp32 MFMA (8.46 GFLOP executed); each sample's GroupNorm "
+                                 "statistics are merged across workgroups"}
     del x, w, b, g, be, o, ws
     # widened rows: softmax on the same 4096 x 393216 workload, and the
     # middle-axis reductions on the chain's (N, C, H*W) = (128, 64, 15876) layout
@@ -306,6 +322,10 @@ def run_only(which, steps, warmup):
     elif which == "axis0_large":
         x = inputs.make("axis0_large", "cuda")
         o = torch.empty(x.shape[1:], device="cuda")
+        wall, ev = timed_launches(lambda: L.lse_reduce_axis0(x, o), steps, warmup)
+    elif which == "axis0_walk":
+        x = inputs.normal((64, 4194304), seed=13, sigma=2.0, device="cuda")
+        o = torch.empty((4194304,), device="cuda")
         wall, ev = timed_launches(lambda: L.lse_reduce_axis0(x, o), steps, warmup)
     elif which == "conv_chain":
         x, w, b, g, be = inputs.make("conv_chain", "cuda")
