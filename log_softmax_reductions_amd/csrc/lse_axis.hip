@@ -240,7 +240,12 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
 #endif
 constexpr int kWalkThreads = LSE_AXIS_WALK_THREADS;
 constexpr int kWalkVl = LSE_AXIS_WALK_VL;
-constexpr int64_t kWalkCols = (int64_t)kWalkThreads * 4 * kWalkVl;  // outputs per workgroup
+#ifndef LSE_AXIS_WALK_NARROW
+#define LSE_AXIS_WALK_NARROW 1   // half-width tiles (VL / 2) when wide ones give too few workgroups
+#endif
+// Outputs per workgroup for VL 16-byte vectors per lane.
+template <int VL>
+constexpr int64_t walk_cols() { return (int64_t)kWalkThreads * 4 * VL; }
 // Sums against the lane's reference value that stay inside [kWalkLo, kWalkHi]
 // are kept: nothing that matters has under- or overflowed, and c and log s
 // (|log s| <= 16.7) cancel by at most a few ulps of 16 when added.
@@ -257,9 +262,9 @@ __device__ __forceinline__ void fold_one(float v, float &m, float &s) {
 }
 
 // out[o, j] = LSE_r x[o, r, j] for wide aligned planes, planes visited one at a
-// time.  A workgroup owns kWalkCols consecutive outputs; wave w reads the
+// time.  A workgroup owns walk_cols<VL>() consecutive outputs; wave w reads the
 // contiguous 64 x 4 x VL outputs' span of each plane (lane l its VL vectors
-// 256 outputs apart), so the workgroup streams kWalkCols x 4 bytes contiguous
+// 256 outputs apart), so the workgroup streams walk_cols<VL>() x 4 bytes contiguous
 // per plane, where the register-block kernel has each wave touch RB planes
 // 1 KiB at a time.
 //
@@ -282,6 +287,7 @@ __global__ __launch_bounds__(kWalkThreads) void lse_axis_walk_kernel(
   const int64_t st_xsr = STR ? d.xsr : d.inner;
   const int64_t st_xso = STR ? d.xso : d.R * d.inner;
   const int64_t st_yso = STR ? d.yso : d.inner;
+  constexpr int64_t kWalkCols = walk_cols<VL>();
   const int64_t tiles = (d.inner + kWalkCols - 1) / kWalkCols;
   const int64_t b = blockIdx.x;
   const int64_t o = (d.outer == 1) ? 0 : b / tiles;
@@ -605,6 +611,22 @@ hipError_t launch_split_p(int P, const float *x, float *out, const AxisDims &d,
   }
 }
 
+// Launches the plane walk with VL vectors per lane if its tiling suits d
+// (true, launch status in e); false leaves the call to other kernels.
+template <int VL, bool STR>
+bool launch_walk(const float *x, float *out, const AxisDims &d, hipStream_t stream,
+                 hipError_t &e) {
+  constexpr int64_t cols = walk_cols<VL>();
+  const int64_t tiles = (d.inner + cols - 1) / cols;
+  if (d.outer * tiles < LSE_AXIS_WALK_MIN_BLOCKS || tiles * cols * 8 > d.inner * 9 ||
+      d.outer * tiles > 0x7fffffff)
+    return false;
+  hipLaunchKernelGGL((lse_axis_walk_kernel<VL, STR>), dim3((uint32_t)(d.outer * tiles)),
+                     dim3(kWalkThreads), 0, stream, x, out, d);
+  e = hipGetLastError();
+  return true;
+}
+
 template <bool LSM, bool STR>
 hipError_t launch_axis_t(const float *x, float *out, const AxisDims &d, hipStream_t stream) {
   if (d.inner == 0 || d.outer == 0) return hipSuccess;
@@ -634,15 +656,19 @@ hipError_t launch_axis_t(const float *x, float *out, const AxisDims &d, hipStrea
   }
 #if LSE_AXIS_WALK
   if constexpr (!LSM) {
-    // Many wide aligned planes: the plane walk, when its tiles are mostly real
-    // columns (at most 1/8 padding) and there are enough of them.  Up to 32
-    // planes the register-block kernel below is as fast or faster.
-    const int64_t tiles = (d.inner + kWalkCols - 1) / kWalkCols;
-    if (vec && R >= LSE_AXIS_WALK_MINR && d.outer * tiles >= LSE_AXIS_WALK_MIN_BLOCKS &&
-        tiles * kWalkCols * 8 <= d.inner * 9 && d.outer * tiles <= 0x7fffffff) {
-      hipLaunchKernelGGL((lse_axis_walk_kernel<kWalkVl, STR>), dim3((uint32_t)(d.outer * tiles)),
-                         dim3(kWalkThreads), 0, stream, x, out, d);
-      return hipGetLastError();
+    if (vec && R >= LSE_AXIS_WALK_MINR) {
+      // Many wide aligned planes: the plane walk, with the widest tile that
+      // still gives enough workgroups and at most 1/8 padding.  Up to 32
+      // planes the register-block kernel below is as fast or faster.
+      hipError_t e = hipErrorInvalidValue;
+      if (launch_walk<kWalkVl, STR>(x, out, d, stream, e)) return e;
+#if LSE_AXIS_WALK_NARROW
+      // Half-width tiles (16 KiB per plane and workgroup) still beat the
+      // register-block kernel (the channel layout (128, 64, 15876): 5890 ->
+      // 6480 GB/s); quarter-width ones measured 8 % slower than it.
+      if constexpr (kWalkVl >= 2)
+        if (launch_walk<kWalkVl / 2, STR>(x, out, d, stream, e)) return e;
+#endif
     }
   }
 #endif

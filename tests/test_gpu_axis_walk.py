@@ -1,5 +1,6 @@
 """GPU parity of the plane-walk logsumexp (many wide aligned planes: R >= 33,
-at least 512 tiles of 8192 outputs) through the C ABI against the fp64 oracle.
+at least 512 tiles of 8192 outputs, or of 4096 when 8192 give too few)
+through the C ABI against the fp64 oracle.
 
 The walk sums each lane's columns against one reference value and redoes a
 lane exactly when a sum leaves its safe window, so these cases place columns
@@ -32,6 +33,8 @@ def _lse(x):
     (1, 33, NARROW + 4 * 37),         # ragged last tile (148 outputs)
     (2, 48, 256 * TILE + TILE // 2),  # two outer slices, ragged tiles
     (1, 100, 513 * TILE - 4),         # last tile one vector short
+    (128, 64, 126 * 126),             # half-width tiles: the channel layout, ragged per slice
+    (128, 64, 16384),                 # half-width tiles, full
 ])
 def test_walk_shapes(orc, outer, R, inner):
     x = inputs.normal((outer, R, inner), seed=outer * 131 + R * 7 + inner % 1000, sigma=2.0,
@@ -98,3 +101,19 @@ def test_walk_beyond_2g_elements(orc):
     compare(out[idx].cpu().numpy(), orc.lse_axis0(cols), what="walk > 2^31 elements")
     del x, out
     torch.cuda.empty_cache()
+
+
+def test_walk_half_tiles_special_values(orc):
+    """Half-width tiles (4096 outputs) on the channel layout with non-finite
+    values and columns that leave the reference window."""
+    x = inputs.normal((128, 64, 126 * 126), seed=93, device=DEV).cpu()
+    inf, nan = float("inf"), float("nan")
+    x[0, :, 0] = -inf
+    x[1, 9, 4095] = inf                        # last column of a tile
+    x[2, 0, 4096] = nan                        # first column of the next, in plane 0
+    x[3, :, 15875] -= 300.0                    # last column of the slice, far below
+    x[127, 5, 100] = 90.0                      # far above
+    got = _lse(x.to(DEV)).cpu().numpy()
+    ref = orc.lse_axis(x.numpy())
+    compare(got, ref, what="walk half tiles special")
+    assert got[0, 0] == -np.inf and got[1, 4095] == np.inf and np.isnan(got[2, 4096])
