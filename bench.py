@@ -403,7 +403,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(),
-                     "kernel": "log_softmax_rows_kernel<32, true, true, false>",
+                     "kernel": "log_softmax_rows_kernel<64, true, true, false>",
                      "event_ms_avg": round(ev_avg, 4), "event_ms_min": round(min(ev), 4),
                      "event_ms_median": round(statistics.median(ev), 4)},
     }

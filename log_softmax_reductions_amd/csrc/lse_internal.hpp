@@ -30,9 +30,15 @@ hipError_t launch_log_softmax_axis(const float *x, float *y, const AxisDims &d,
 #ifndef LSE_ROWS_MAX_VPL
 #define LSE_ROWS_MAX_VPL 32
 #endif
+#ifndef LSE_ROWS_SPLIT_VPL
+#define LSE_ROWS_SPLIT_VPL 64   // floats per lane of a log_softmax_rows / softmax_rows chunk
+#endif
 constexpr int kRowsThreads = LSE_ROWS_THREADS;  // lanes per workgroup
 constexpr int kRowsMaxVpl = LSE_ROWS_MAX_VPL;   // floats held per lane
 constexpr int64_t kRowsTile = (int64_t)kRowsThreads * kRowsMaxVpl;  // 16384 columns
+// Chunk of the split log_softmax / softmax rows: 32768 columns (128 KiB)
+// per workgroup measured 5 % faster than 16384 on (4096, 393216).
+constexpr int64_t kRowsSplitTile = (int64_t)kRowsThreads * LSE_ROWS_SPLIT_VPL;
 constexpr int64_t kRowsMaxChunks = 1 << 20;
 
 // Split workspace: a 256-byte header, then rows * nchunks packed pairs.

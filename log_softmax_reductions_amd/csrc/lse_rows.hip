@@ -571,6 +571,9 @@ int vpl_for(int64_t len) {
   if (len <= 8 * kRowsThreads) return 8;
   if (len <= 16 * kRowsThreads) return 16;
   if (len <= 32 * kRowsThreads) return 32;
+#if LSE_ROWS_MAX_VPL >= 128 || LSE_ROWS_SPLIT_VPL >= 128
+  if (len > 64 * kRowsThreads) return 128;
+#endif
   return 64;
 }
 
@@ -596,6 +599,9 @@ hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *
     LSE_ROWS_CASE(16)
     LSE_ROWS_CASE(32)
     LSE_ROWS_CASE(64)
+#if LSE_ROWS_MAX_VPL >= 128 || LSE_ROWS_SPLIT_VPL >= 128
+    LSE_ROWS_CASE(128)
+#endif
     default:
       return hipErrorInvalidValue;
   }
@@ -634,12 +640,12 @@ uint32_t chain_spin_limit() { return h_spin_limit.load(std::memory_order_relaxed
 
 RowsPlan rows_plan(int64_t cols) {
   RowsPlan p;
-  p.nchunks = (cols + kRowsTile - 1) / kRowsTile;
+  p.nchunks = (cols + kRowsSplitTile - 1) / kRowsSplitTile;
   if (p.nchunks < 1) p.nchunks = 1;
   // balance the chunks, keeping them a multiple of 4 columns
   int64_t chunk = (cols + p.nchunks - 1) / p.nchunks;
   chunk = (chunk + 3) / 4 * 4;
-  if (chunk > kRowsTile) chunk = kRowsTile;
+  if (chunk > kRowsSplitTile) chunk = kRowsSplitTile;
   p.chunk = chunk;
   p.nchunks = (cols + chunk - 1) / chunk;
   return p;

@@ -119,7 +119,7 @@ def test_rows_validation(lib):
     assert lib.log_softmax_rows(FAKE, FAKE, 4, 8, None, 0, None) == LSE_ERR_OVERLAP
     # a split row needs a workspace of the advertised size
     need = lib.log_softmax_rows_workspace_bytes(16, 393216)
-    assert need == 256 + 16 * 24 * 8
+    assert need == 256 + 16 * 12 * 8
     assert lib.log_softmax_rows(FAKE, FAKE2, 16, 393216, None, 0, None) == LSE_ERR_WORKSPACE
     assert lib.log_softmax_rows(FAKE, FAKE2, 16, 393216, ctypes.c_void_p(0x7000000000), need - 1,
                                 None) == LSE_ERR_WORKSPACE
@@ -129,12 +129,13 @@ def test_rows_validation(lib):
 
 def test_rows_plan(lib):
     from log_softmax_reductions_amd import log_softmax_rows_plan
-    assert log_softmax_rows_plan(393216) == (24, 16384)
+    assert log_softmax_rows_plan(393216) == (12, 32768)
     assert log_softmax_rows_plan(4096) == (1, 4096)
     assert log_softmax_rows_plan(16384) == (1, 16384)
-    for cols in (16385, 20000, 100001, 393216, 1 << 22):
+    assert log_softmax_rows_plan(32768) == (1, 32768)
+    for cols in (32769, 40000, 100001, 393216, 1 << 22):
         k, chunk = log_softmax_rows_plan(cols)
-        assert k > 1 and chunk % 4 == 0 and chunk <= 16384
+        assert k > 1 and chunk % 4 == 0 and chunk <= 32768
         assert (k - 1) * chunk < cols <= k * chunk
 
 
