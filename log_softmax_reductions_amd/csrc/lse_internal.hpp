@@ -39,6 +39,9 @@ constexpr int64_t kRowsTile = (int64_t)kRowsThreads * kRowsMaxVpl;  // 16384 col
 // Chunk of the split log_softmax / softmax rows: 32768 columns (128 KiB)
 // per workgroup measured 5 % faster than 16384 on (4096, 393216).
 constexpr int64_t kRowsSplitTile = (int64_t)kRowsThreads * LSE_ROWS_SPLIT_VPL;
+static_assert(LSE_ROWS_SPLIT_VPL % 4 == 0 && LSE_ROWS_SPLIT_VPL >= LSE_ROWS_MAX_VPL &&
+                  LSE_ROWS_MAX_VPL <= 32,
+              "register tiles: up to 32 floats per lane, the split chunk at least that");
 constexpr int64_t kRowsMaxChunks = 1 << 20;
 
 // Split workspace: a 256-byte header, then rows * nchunks packed pairs.

@@ -571,10 +571,7 @@ int vpl_for(int64_t len) {
   if (len <= 8 * kRowsThreads) return 8;
   if (len <= 16 * kRowsThreads) return 16;
   if (len <= 32 * kRowsThreads) return 32;
-#if LSE_ROWS_MAX_VPL >= 128 || LSE_ROWS_SPLIT_VPL >= 128
-  if (len > 64 * kRowsThreads) return 128;
-#endif
-  return 64;
+  return LSE_ROWS_SPLIT_VPL;  // a split chunk (up to kRowsSplitTile columns)
 }
 
 template <bool SPLIT, bool SOFTMAX>
@@ -598,9 +595,8 @@ hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *
     LSE_ROWS_CASE(8)
     LSE_ROWS_CASE(16)
     LSE_ROWS_CASE(32)
-    LSE_ROWS_CASE(64)
-#if LSE_ROWS_MAX_VPL >= 128 || LSE_ROWS_SPLIT_VPL >= 128
-    LSE_ROWS_CASE(128)
+#if LSE_ROWS_SPLIT_VPL > 32
+    LSE_ROWS_CASE(LSE_ROWS_SPLIT_VPL)
 #endif
     default:
       return hipErrorInvalidValue;
