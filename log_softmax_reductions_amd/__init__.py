@@ -20,7 +20,9 @@ raises ImportError on first use.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import math
 
 from . import _lib
 from ._lib import LseError  # noqa: F401
@@ -35,8 +37,13 @@ __all__ = [
 
 
 def _stream(stream):
+    """The HIP stream handle: the given torch stream's, else the current stream
+    of the current device (callers run inside _on, so the tensors' GPU)."""
     import torch
     if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:  # the handle without building a Stream object
+            return ctypes.c_void_p(raw(torch._C._cuda_getDevice()))
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(int(stream.cuda_stream))
 
@@ -69,6 +76,8 @@ def _on(*ts):
     d = devs.pop() if devs else None
     if d is None or d.type != "cuda":
         raise ValueError(f"tensors must be on the GPU (got {d})")
+    if d.index is None or d.index == torch.cuda.current_device():
+        return contextlib.nullcontext()  # already current: no device switch
     return torch.cuda.device(d)
 
 
@@ -102,8 +111,10 @@ def lse_reduce_axis0(x, out=None, stream=None):
     """out[...] = logsumexp over dim 0 of x (shape x.shape[1:])."""
     import torch
     lib = _lib.load()
+    if x.dim() == 0:
+        raise ValueError("x must have at least one dimension")
     R = x.shape[0]
-    inner = x[0].numel() if x.dim() > 0 and R > 0 else 0
+    inner = math.prod(x.shape[1:]) if R > 0 else 0
     if out is None:
         out = torch.empty(x.shape[1:], dtype=torch.float32, device=x.device)
     if out.numel() != inner:
