@@ -47,6 +47,23 @@ constexpr int kNW = kRowsThreads / kWave;  // waves per workgroup
 #endif
 std::atomic<uint32_t> h_spin_limit{1u << 24};
 
+#ifndef LSE_ROWS_WAVE_CONTIG
+#define LSE_ROWS_WAVE_CONTIG 1
+#endif
+// Float4 index of register vector q of thread t within a chunk.  Either way a
+// wave's access per q is one contiguous 1 KiB.  Here each wave owns one
+// contiguous run of VPL / 4 KiB (16 KiB for a 32768-column chunk): 2.3 %
+// faster on (4096, 393216) than the 8 waves tiling 8 KiB per q
+// (LSE_ROWS_WAVE_CONTIG=0).
+template <int VPL>
+__device__ __forceinline__ int64_t vec4_index(int q, int t) {
+#if LSE_ROWS_WAVE_CONTIG
+  return ((int64_t)(t / kWave) * (VPL / 4) + q) * kWave + (t % kWave);
+#else
+  return (int64_t)q * kRowsThreads + t;
+#endif
+}
+
 // Load a chunk of `len` values starting at p into v (lane-strided so that each
 // wave's load is one contiguous span), padding with -inf.  A full chunk (the
 // common case) takes an unchecked path.
@@ -57,13 +74,13 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ p, int64_t 
   if constexpr (VEC) {
     if (len == (int64_t)VPL * kRowsThreads) {
       typedef float v4 __attribute__((ext_vector_type(4)));
-      const v4 *p4 = reinterpret_cast<const v4 *>(p) + t;
+      const v4 *p4 = reinterpret_cast<const v4 *>(p);
 #pragma unroll
       for (int q = 0; q < VPL / 4; ++q) {
 #if LSE_ROWS_NT_LOAD
-        const v4 f = __builtin_nontemporal_load(p4 + q * kRowsThreads);
+        const v4 f = __builtin_nontemporal_load(p4 + vec4_index<VPL>(q, t));
 #else
-        const v4 f = p4[q * kRowsThreads];
+        const v4 f = p4[vec4_index<VPL>(q, t)];
 #endif
         v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
       }
@@ -71,7 +88,7 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ p, int64_t 
     }
 #pragma unroll
     for (int q = 0; q < VPL / 4; ++q) {
-      const int64_t idx = ((int64_t)q * kRowsThreads + t) * 4;
+      const int64_t idx = vec4_index<VPL>(q, t) * 4;
       if (idx < len) {
         const float4 f = *reinterpret_cast<const float4 *>(p + idx);
         v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
@@ -118,7 +135,7 @@ __device__ __forceinline__ void store_chunk(float *__restrict__ p, int64_t len,
     const bool full = (len == (int64_t)VPL * kRowsThreads);
 #pragma unroll
     for (int q = 0; q < VPL / 4; ++q) {
-      const int64_t idx = ((int64_t)q * kRowsThreads + t) * 4;
+      const int64_t idx = vec4_index<VPL>(q, t) * 4;
       if (full || idx < len)
         store4(p + idx, out_value<SOFTMAX>(v[4 * q], M, k), out_value<SOFTMAX>(v[4 * q + 1], M, k),
                out_value<SOFTMAX>(v[4 * q + 2], M, k), out_value<SOFTMAX>(v[4 * q + 3], M, k));
