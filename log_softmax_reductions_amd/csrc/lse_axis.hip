@@ -272,8 +272,9 @@ __device__ __forceinline__ void fold_one(float v, float &m, float &s) {
 // per column would cost a rescale exponential per new max.  Instead every
 // column of a lane is summed against one reference c, the largest of the
 // lane's plane-0 values: s = sum_r exp(x_r - c), one exponential per value,
-// and LSE = c + log s, the same quantity (and exactly x for a single finite
-// value, v + log R for R equal ones, as with the column's max).  A lane whose
+// and LSE = c + log s, the same quantity (its closed forms, a single finite
+// value or R equal ones, hold exactly only for a column whose values equal c;
+// otherwise to rounding, like any other result).  A lane whose
 // sums all stay inside [2^-20, 2^24] is done: no term that matters under- or
 // overflowed, and the final sum loses at most a few ulps.  Any other lane (a
 // column more than ~14 below or ~16 above c, a non-finite value or reference)
