@@ -117,3 +117,17 @@ def test_walk_half_tiles_special_values(orc):
     ref = orc.lse_axis(x.numpy())
     compare(got, ref, what="walk half tiles special")
     assert got[0, 0] == -np.inf and got[1, 4095] == np.inf and np.isnan(got[2, 4096])
+
+
+def test_walk_half_tiles_strided(orc):
+    """Half-width tiles through the strided instantiation: padded planes (pitch
+    15880 for 15876 columns) and a slice of the reduced axis (outer stride
+    66 x 15880), output into a padded buffer."""
+    big = inputs.normal((128, 66, 15880), seed=94, device=DEV)
+    x = big[:, 1:65, :15876]                   # (128, 64, 15876)
+    obuf = torch.empty(128, 15880, device=DEV)
+    out = obuf[:, :15876]
+    L.lse_reduce_axis(x, 1, out)
+    torch.cuda.synchronize()
+    ref = orc.lse_axis(x.contiguous().cpu().numpy())
+    compare(out.cpu().numpy(), ref, what="walk half tiles strided")
