@@ -29,7 +29,7 @@ def _untouched(big, view):
 
 @pytest.mark.parametrize("rows,cols,padx,pady", [(64, 4096, 4, 8), (37, 1000, 3, 1),
                                                    (8, 100000, 4, 12), (5, 393216, 1, 4),
-                                                   (16, 50000, 0, 4)])
+                                                   (16, 50000, 0, 4), (4, 65536, 4, 4)])
 def test_rows_with_pitch(orc, rows, cols, padx, pady):
     """log_softmax_rows / softmax_rows on column slices of wider matrices:
     vector and scalar pitches, single-workgroup and split rows."""
