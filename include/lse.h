@@ -140,7 +140,12 @@ lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows,
  * log_softmax_rows.                          [LSM] the standard-softmax variant */
 lse_status_t softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
                           void *ws, size_t ws_bytes, hipStream_t stream);
-/* log_softmax_rows / softmax_rows over rows that sit ldx (x) and ldy (y)
+/* A split row's workgroups wait for each other's (max, sum) pairs; one that
+ * has waited about 50 us computes the missing pairs itself from x, with the
+ * same arithmetic in the same order as their owners, so the results are
+ * bit-identical whichever workgroup computes a pair.
+ *
+ * log_softmax_rows / softmax_rows over rows that sit ldx (x) and ldy (y)
  * elements apart, e.g. the first cols columns of a wider matrix: row r of x
  * starts at x + r * ldx.  ldx, ldy >= cols (else LSE_ERR_SHAPE); the
  * workspace is the same as for the contiguous call.  The address ranges
@@ -153,18 +158,6 @@ lse_status_t log_softmax_rows_strided(const float *x, float *y, int64_t rows,
 lse_status_t softmax_rows_strided(const float *x, float *y, int64_t rows,
                                   int64_t cols, int64_t ldx, int64_t ldy,
                                   void *ws, size_t ws_bytes, hipStream_t stream);
-/* How many times a workgroup of a split row polls for its siblings' (max,
- * sum) pairs before it computes the missing ones itself from x (default 2^24;
- * independently it never waits longer than about 50 us).  The results are
- * the same either way.  After a call has run, the 32-bit word at byte offset
- * 4 of the workspace holds the number of pairs computed that way.  A limit of
- * 0 also stops each workgroup from publishing its own pair, so that every
- * pair comes from that path (the count is then rows x chunks).  The same limit
- * bounds fused_conv_gn_act_lse's wait for the statistics of a sample (there a
- * workgroup that runs out writes NaN and sets the word after the mean / rstd
- * block of its workspace, at byte offset align256(8 N groups) + 4).  Affects
- * calls enqueued after it returns; intended for tests. */
-void lse_set_spin_limit(uint32_t polls);
 /* The split log_softmax_rows will use for a row length: *nchunks workgroups
  * per row, each covering *chunk consecutive columns (the last may be short).
  * Host-only; enqueues nothing. */
@@ -210,7 +203,10 @@ lse_status_t lse_rows_merge(const lse_pair_t *partials, int64_t rows,
  * for their sample's statistics); larger samples take two launches, the
  * first publishing the statistics, the second recomputing the conv and
  * applying them (the conv runs twice; nothing waits).  Both give identical
- * results. */
+ * results.  A workgroup whose wait runs out (about 0.5 ms, e.g. when other
+ * work holds the GPU) leaves its tiles to the launch's last workgroup, which
+ * finishes them once every statistic is in: results are the same either way
+ * and never depend on scheduling. */
 size_t fused_conv_gn_act_lse_workspace_bytes(int64_t N, int64_t Cin, int64_t H,
                                              int64_t W, int64_t Cout,
                                              int64_t K, int64_t groups);

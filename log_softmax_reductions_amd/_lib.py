@@ -7,7 +7,8 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblse.so")
 
-# Every symbol include/lse.h declares, with (restype, argtypes).
+# Every symbol include/lse.h and include/lse_testing.h declare, with (restype,
+# argtypes).
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _sz = ctypes.c_size_t
@@ -27,7 +28,7 @@ SIGNATURES = {
     "log_softmax_rows_workspace_bytes": (_sz, [_i64, _i64]),
     "softmax_rows": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
     "log_softmax_rows": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
-    "lse_set_spin_limit": (None, [ctypes.c_uint32]),
+    "lse_testing_set_spin_limit": (None, [ctypes.c_uint32]),
     "log_softmax_rows_plan": (ctypes.c_int, [_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "lse_rows_num_chunks": (_i64, [_i64, _i64]),
     "lse_rows_partial": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),

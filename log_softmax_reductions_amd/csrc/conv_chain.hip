@@ -19,16 +19,25 @@
 //   runs normalise, tanh, hardswish, residual and the 64-channel logsumexp
 //   on the accumulators it still holds, writing one float per pixel.
 //
-// The wait is deadlock-free because tickets are claimed only by running
-// workgroups, in order, and every workgroup publishes before it waits: the
-// tiles of any sample that has a waiting workgroup are all held by running
-// workgroups once its last ticket is claimed, which needs only as many
-// co-resident workgroups as a sample has tile pairs (32 for 126 x 126;
-// hundreds fit).  The wait is still bounded (poll count and 0.1 s); a workgroup that
-// gives up flags the workspace and writes NaN.  A sample with more tile pairs
-// than half of what the device holds at once takes two launches instead: one
-// publishes the statistics, the next recomputes the conv and applies them
-// (the conv runs twice, nothing waits; the results are identical).
+// The wait normally ends within microseconds: tickets are claimed only by
+// running workgroups, in order, and every workgroup publishes before it
+// waits, so the tiles of a sample that has a waiting workgroup are all held
+// by running workgroups once its last ticket is claimed, which needs only as
+// many co-resident workgroups as a sample has tile pairs (32 for 126 x 126;
+// hundreds fit).  Progress never depends on that, though.  Each workgroup
+// counts its arrival (after publishing) on a per-sample word; one whose wait
+// runs out (kChainWaitTicks, or the test hook's poll limit) counts itself
+// deferred on the same word: if every pair of its sample has arrived by then
+// the statistics are complete and it carries on, otherwise it records its
+// pair in the sample's queue and exits, which frees its slot for the pairs
+// still to come.  The sample's last arrival sees the deferrals made before
+// it and finishes those pairs itself after its own (conv, merge, epilogue;
+// nothing left to wait for).  The two counts share one 64-bit word, so every
+// deferral is either seen by the last arrival or sees it.  A sample with more
+// tile pairs than half of what the device holds at once takes two launches
+// instead: one publishes the statistics, the next recomputes the conv and
+// applies them (the conv runs twice, nothing waits; the results are
+// identical).
 //
 // Direct form (conv_tile), GEMM shape per sample: D[c][p] = sum_k W[c][k] *
 // patch[k][p] with c the 64 output channels (M), p the pixels (N) and
@@ -96,8 +105,8 @@ constexpr int kWinoU = 16 * 2 * kMT * kWave;                             // 8192
 constexpr int kWLds = kWino ? kWinoU : kCout * kWStride;
 
 struct ChainWsHeader {
-  uint32_t ticket;  // next tile ticket
-  uint32_t error;   // nonzero once a workgroup gave up waiting
+  uint32_t ticket;     // next tile-pair ticket
+  uint32_t deferred;   // pairs finished by their sample's last arrival
   uint32_t pad[62];
 };
 
@@ -106,11 +115,14 @@ struct ChainArgs {
   int32_t N, H, W, Ho, Wo, G, log2G, tiles_w, tiles;
   float eps;
   uint32_t spin_limit;
+  uint32_t block_base;   // kStats / kApply: workgroup index of this launch's first pair
   float *out;
   float *mean;           // (N, G), written by tile 0 of each sample
   float *rstd;           // (N, G)
   ChainWsHeader *hdr;
   uint64_t *stats;       // (N, tiles, G) packed (mean, -M2); 0 = not yet written
+  uint64_t *arrivals;    // (N): low 32 bits pairs arrived, high 32 bits pairs deferred
+  uint32_t *queue;       // (N, pairs per sample): deferred pair + 1, in deferral order
 };
 
 // Row-of-16 all-reduce (lanes sharing l / 16) on DPP only.
@@ -418,7 +430,12 @@ __device__ __forceinline__ double tile_count(const ChainArgs &a, int j, int qpg,
   return (double)(4 * qpg) * (double)vr * (double)vc;
 }
 
-constexpr uint64_t kChainWaitTicks = 10000000ull;  // 0.1 s of the 100 MHz counter
+// How long a workgroup waits for its sample's statistics before it defers its
+// pair: 0.5 ms of the 100 MHz real-time counter (a sample's tiles normally
+// publish within a few microseconds of each other).
+constexpr uint64_t kChainWaitTicks = 50000ull;
+// Statistics words a thread keeps in registers from its last poll.
+constexpr int kHeldPer = LSE_CHAIN_HELD / (kTeams * kThreads);
 
 // Tile-relative pixel of accumulator block blk in lane i of team wave w:
 // direct conv, row w / 2 and 16-pixel block blk of the wave's 64 columns;
@@ -445,39 +462,30 @@ __device__ __forceinline__ void tile_valid(const ChainArgs &a, int tile, bool (&
   }
 }
 
-// Wait until every tile of sample n has published, then merge the sample's
-// statistics into the epilogue's per-channel table L.sc / L.sh; called by the
-// whole workgroup (NT threads), ends with a barrier.  Thread t polls words t, t + NT, ... of the sample's
-// (tile, group) block: one round trip per poll for up to LSE_CHAIN_HELD words,
-// whose values stay in registers.  A poll's verdict is the OR of one ballot per
-// wave through LDS, so every wave leaves the loop together.  Then, per thread
-// in fp64: C = sum n_j, S1 = sum n_j mean_j, S2 = sum (M2_j + n_j mean_j^2)
-// over its words, which all belong to group t % G; lanes of a wave with the
-// same group are combined by xor shuffles, the waves in LDS (fixed order:
-// the result is deterministic); per group mean = S1 / C, M2 = S2 - C mean^2,
-// rstd = 1 / sqrt(M2 / C + eps).
+// Poll until every tile of sample n has published its statistics words
+// (true) or the wait runs out (false: kChainWaitTicks or the poll limit);
+// called by the whole workgroup (NT threads), every thread returns the same
+// verdict.  Thread t polls words t, t + NT, ... of the sample's (tile, group)
+// block, one round trip per poll; the first kHeldPer of them stay in wd.  A
+// poll's verdict is the OR of one ballot per wave through LDS, so every wave
+// leaves the loop together.
 template <int NT, class Lds>
-__device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bool write_global,
-                                               float ga, float be, Lds &L) {
-  constexpr int kPer = LSE_CHAIN_HELD / NT;  // words held per thread
+__device__ __forceinline__ bool wait_stats(const ChainArgs &a, int64_t n, Lds &L,
+                                           uint64_t (&wd)[kHeldPer]) {
   constexpr int kWaves = NT / kWave;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int qpg = 16 / a.G;
-  const int tiles_h = a.tiles / a.tiles_w;
   const uint64_t *ws = a.stats + n * a.tiles * a.G;
   const int words = a.tiles * a.G;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  uint64_t wd[kPer];
-  bool ok = true;
   for (uint32_t it = 0;; ++it) {
     bool missing = false;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
+    for (int j = 0; j < kHeldPer; ++j) {
       const int idx = threadIdx.x + NT * j;
       wd[j] = (idx < words) ? load_pair_agent(ws + idx) : 1ull;
       missing |= (wd[j] == 0);
     }
-    for (int idx = threadIdx.x + NT * kPer; idx < words; idx += NT)
+    for (int idx = threadIdx.x + NT * kHeldPer; idx < words; idx += NT)
       missing |= (load_pair_agent(ws + idx) == 0);
     const bool late =
         it >= a.spin_limit || __builtin_amdgcn_s_memrealtime() - t0 > kChainWaitTicks;
@@ -490,13 +498,30 @@ __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bo
     uint32_t f = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) f |= L.flags[it & 1][w];
-    if ((f & 1u) == 0) break;
-    if (f & 2u) {
-      ok = false;
-      break;
-    }
+    if ((f & 1u) == 0) return true;
+    if (f & 2u) return false;
     __builtin_amdgcn_s_sleep(8);
   }
+}
+
+// Merge the sample's statistics (all words present; the first kHeldPer per
+// thread in wd, as left by wait_stats) into the epilogue's per-channel table
+// L.sc / L.sh; ends with a barrier.  Per thread in fp64: C = sum n_j,
+// S1 = sum n_j mean_j, S2 = sum (M2_j + n_j mean_j^2) over its words, which
+// all belong to group t % G; lanes of a wave with the same group are combined
+// by xor shuffles, the waves in LDS (fixed order: the result is
+// deterministic); per group mean = S1 / C, M2 = S2 - C mean^2,
+// rstd = 1 / sqrt(M2 / C + eps).
+template <int NT, class Lds>
+__device__ __forceinline__ void merge_stats(const ChainArgs &a, int64_t n,
+                                            const uint64_t (&wd)[kHeldPer], bool write_global,
+                                            float ga, float be, Lds &L) {
+  constexpr int kWaves = NT / kWave;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int qpg = 16 / a.G;
+  const int tiles_h = a.tiles / a.tiles_w;
+  const uint64_t *ws = a.stats + n * a.tiles * a.G;
+  const int words = a.tiles * a.G;
   double C = 0.0, S1 = 0.0, S2 = 0.0;
   auto add = [&](int idx, uint64_t w) {
     const double c = tile_count(a, idx >> a.log2G, qpg, tiles_h);  // G is a power of 2
@@ -506,11 +531,11 @@ __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bo
     S2 += -(double)bitsf((uint32_t)(w >> 32)) + c * m * m;
   };
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
+  for (int j = 0; j < kHeldPer; ++j) {
     const int idx = threadIdx.x + NT * j;
     if (idx < words) add(idx, wd[j]);
   }
-  for (int idx = threadIdx.x + NT * kPer; idx < words; idx += NT)
+  for (int idx = threadIdx.x + NT * kHeldPer; idx < words; idx += NT)
     add(idx, load_pair_agent(ws + idx));
   for (int o = kWave / 2; o >= a.G; o >>= 1) {  // lanes l, l ^ o share a group while o >= G
     C += __shfl_xor(C, o);
@@ -538,8 +563,7 @@ __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bo
     }
     const double MU = S1g / Cg;
     const double M2 = fmax(S2g - Cg * MU * MU, 0.0);
-    float fm = (float)MU, fr = (float)(1.0 / sqrt(M2 / Cg + (double)a.eps));
-    if (!ok) fm = fr = __builtin_nanf("");
+    const float fm = (float)MU, fr = (float)(1.0 / sqrt(M2 / Cg + (double)a.eps));
     const float sc = fr * ga;
     L.sc[c] = sc * (2.0f * kLog2e);
     L.sh[c] = (be - fm * sc) * (2.0f * kLog2e);
@@ -547,8 +571,6 @@ __device__ __forceinline__ void wait_and_merge(const ChainArgs &a, int64_t n, bo
       a.mean[n * a.G + g] = fm;
       a.rstd[n * a.G + g] = fr;
     }
-    if (!ok && c == 0)
-      __hip_atomic_store(&a.hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 }
@@ -725,12 +747,81 @@ __device__ __forceinline__ void publish_pair_stats(const ChainArgs &a, int64_t n
 // and epilogue.  W staging and the wait for the sample's statistics are paid
 // once per pair.
 //   kFused: pairs handed out by ticket in sample order; publish, wait for the
-//           sample, merge, epilogue (one launch; a sample's pairs must fit
-//           on the GPU at once, see launch_conv_chain).
+//           sample, merge, epilogue (one launch; used while a sample's pairs
+//           fit on the GPU at once, see launch_conv_chain).
 //   kStats: publish only.  kApply: the statistics are complete (published by
 //           a kStats launch): merge, epilogue.  kStats + kApply compute the
 //           conv twice but never wait on another workgroup.
+// In every mode a workgroup whose wait runs out computes the missing tile
+// statistics of its sample itself (see the file comment).
 enum ChainMode { kFused = 0, kStats = 1, kApply = 2 };
+
+// Stage the pair of tiles of sample n with index pr (team 0: tile 2 pr, team
+// 1: tile 2 pr + 1) and convolve it into acc; the caller must have passed a
+// barrier since the last reads of xs.  Inactive waves (no second tile) get
+// zero accumulators and no valid pixels.
+__device__ __forceinline__ void stage_and_convolve(const ChainArgs &a, int64_t n, uint32_t pr,
+                                                   int team, int tid, int twave, float *xs,
+                                                   const float *wl, f32x4 (&acc)[kNB][kMT],
+                                                   bool (&valid)[kNB]) {
+  const int tile = kTeams * (int)pr + team;
+  const bool active = tile < a.tiles;  // uniform per wave
+  if (active) {
+    XRegs xr;
+    const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
+    load_x(a, n, th * kTileH, tw * kTileW, xr, tid);
+    store_x(xr, xs, tid);
+  }
+  __syncthreads();
+  if (active) {
+    if constexpr (kWino)
+      conv_tile_wino(a, xs, wl, twave, acc);
+    else
+      conv_tile(a, xs, wl, twave / 2, (twave % 2) * 64, acc);
+    tile_valid(a, tile, valid, twave);
+  }
+}
+
+// Cold path of the sample's last arrival: finish the ndef pairs of sample n
+// deferred before it (their statistics are all published).  Out of line so
+// that nothing of it stays alive through the common path.
+__device__ __noinline__ void finish_deferred(const ChainArgs a, int64_t n, uint32_t ndef,
+                                             float *xs_team, const float *wl, PairLds *Lp) {
+  PairLds &L = *Lp;
+  __shared__ uint32_t s_pair;
+  const uint32_t groups = (uint32_t)(a.tiles + kTeams - 1) / kTeams;
+  const int team = kTeams == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kThreads);
+  const int tid = threadIdx.x - team * kThreads;
+  const int twave = tid / kWave;
+  float ga = 1.0f, be = 0.0f;
+  if (threadIdx.x < kCout) {
+    if (a.gamma) ga = a.gamma[threadIdx.x];
+    if (a.beta) be = a.beta[threadIdx.x];
+  }
+  for (uint32_t d = 0; d < ndef; ++d) {
+    __syncthreads();  // everyone has read s_pair / finished with xs
+    if (threadIdx.x == 0) {
+      // The entry is stored right after its deferral was counted: it shows up.
+      uint32_t e;
+      while ((e = __hip_atomic_load(a.queue + n * groups + d, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT)) == 0u)
+        __builtin_amdgcn_s_sleep(2);
+      s_pair = e - 1u;
+      __hip_atomic_fetch_add(&a.hdr->deferred, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const uint32_t qp = s_pair;
+    f32x4 acc[kNB][kMT];
+    bool valid[kNB];
+    stage_and_convolve(a, n, qp, team, tid, twave, xs_team, wl, acc, valid);
+    uint64_t wd[kHeldPer];
+    while (!wait_stats<kTeams * kThreads>(a, n, L, wd)) {
+    }
+    merge_stats<kTeams * kThreads>(a, n, wd, qp == 0, ga, be, L);
+    const int tile = kTeams * (int)qp + team;
+    if (tile < a.tiles) tile_epilogue_lds(a, n, tile, acc, valid, L, twave);
+  }
+}
 
 template <int MODE>
 __global__ __launch_bounds__(kTeams * kThreads)
@@ -739,16 +830,12 @@ void conv_chain_pair_kernel(ChainArgs a) {
   __shared__ alignas(16) float xs[kTeams][kCin * kLdsH * kLdsW];
   __shared__ alignas(16) float wl[kWLds];  // W rows, or U in fragment order (Winograd)
   __shared__ PairLds L;
-  __shared__ uint32_t s_ticket;
+  __shared__ uint32_t s_ticket, s_last;
   // W's loads are in flight while the ticket is claimed.
   std::conditional_t<kWino, WinoW, WRegs<kTeams * kThreads>> wr;
   load_w(a.w, wr);
-  float ga = 1.0f, be = 0.0f;  // this thread's channel of gamma / beta (threads < 64)
-  if (threadIdx.x < kCout) {
-    if (a.gamma) ga = a.gamma[threadIdx.x];
-    if (a.beta) be = a.beta[threadIdx.x];
-  }
-  uint32_t ticket = blockIdx.x;  // kStats, kApply: no workgroup waits, any order will do
+  // kStats, kApply: no workgroup waits on another's turn, any order will do.
+  uint32_t ticket = a.block_base + blockIdx.x;
   if constexpr (MODE == kFused) {
     if (threadIdx.x == 0)
       s_ticket = __hip_atomic_fetch_add(&a.hdr->ticket, 1u, __ATOMIC_RELAXED,
@@ -758,8 +845,8 @@ void conv_chain_pair_kernel(ChainArgs a) {
   }
   const uint32_t groups = (uint32_t)(a.tiles + kTeams - 1) / kTeams;  // workgroups per sample
   const int64_t n = ticket / groups;
-  const int p = (int)(ticket - (uint32_t)n * groups);
-  const int tA = kTeams * p, tB = tA + 1;
+  const uint32_t p = ticket - (uint32_t)n * groups;
+  const int tA = kTeams * (int)p, tB = tA + 1;
   const bool hasB = kTeams == 2 && tB < a.tiles;  // uniform
 
   const int team = kTeams == 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x / kThreads);
@@ -767,7 +854,6 @@ void conv_chain_pair_kernel(ChainArgs a) {
   const int twave = tid / kWave;
   const bool active = team == 0 || hasB;                                   // uniform per wave
   const int tile = team ? tB : tA;
-  const int pr = twave / 2, pc0 = (twave % 2) * 64;
 
   XRegs xr;
   if (active) {
@@ -784,19 +870,59 @@ void conv_chain_pair_kernel(ChainArgs a) {
     if constexpr (kWino)
       conv_tile_wino(a, xs[team], wl, twave, acc);
     else
-      conv_tile(a, xs[team], wl, pr, pc0, acc);
+      conv_tile(a, xs[team], wl, twave / 2, (twave % 2) * 64, acc);
     tile_valid(a, tile, valid, twave);
   }
   if constexpr (MODE != kApply) publish_pair_stats(a, n, tA, tB, hasB, active, acc, valid, L);
   if constexpr (MODE == kStats) return;
-  wait_and_merge<kTeams * kThreads>(a, n, tA == 0, ga, be, L);
+  // This thread's channel of gamma / beta (threads < 64), loaded only now so
+  // that they are not held through the conv.
+  float ga = 1.0f, be = 0.0f;
+  if (threadIdx.x < kCout) {
+    if (a.gamma) ga = a.gamma[threadIdx.x];
+    if (a.beta) be = a.beta[threadIdx.x];
+  }
+  // Arrival (after this pair's statistics were published); the returned
+  // counts are needed only after the epilogue, so the round trip overlaps
+  // the wait.
+  uint64_t arrived_before = 0;
+  if (threadIdx.x == 0)
+    arrived_before = __hip_atomic_fetch_add(a.arrivals + n, 1ull, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t wd[kHeldPer];
+  // A poll limit of 0 (test hook) tries to defer without waiting.
+  bool ok = a.spin_limit != 0 && wait_stats<kTeams * kThreads>(a, n, L, wd);  // uniform
+  if (!ok) {
+    if (threadIdx.x == 0) {
+      const uint64_t st = __hip_atomic_fetch_add(a.arrivals + n, 1ull << 32, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+      const bool all_arrived = (uint32_t)st == groups;
+      if (!all_arrived)  // the sample's last arrival finishes this pair
+        __hip_atomic_store(a.queue + n * groups + (uint32_t)(st >> 32), p + 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      s_last = all_arrived ? 1u : 0u;
+    }
+    __syncthreads();
+    if (s_last == 0) return;  // deferred
+    // Every pair of the sample has arrived, so every statistic is published:
+    // poll until all are visible (normally the first poll).
+    while (!wait_stats<kTeams * kThreads>(a, n, L, wd)) {
+    }
+  }
+  // The last arrival of the sample finishes the pairs deferred before it.
+  if (threadIdx.x == 0)
+    s_ticket = ((uint32_t)arrived_before + 1u == groups) ? (uint32_t)(arrived_before >> 32) : 0u;
+  merge_stats<kTeams * kThreads>(a, n, wd, tA == 0, ga, be, L);  // barriers: s_ticket visible
   if (active) tile_epilogue_lds(a, n, tile, acc, valid, L, twave);
+  const uint32_t ndef = s_ticket;
+  if (ndef != 0) finish_deferred(a, n, ndef, xs[team], wl, &L);
 }
 
-// Clear n 64-bit words (the ticket / error header and the statistics words).
+// Clear n 64-bit words (the ticket / helped header and the statistics words);
+// grid-stride, at most 4096 workgroups.
 __global__ __launch_bounds__(256) void chain_clear_kernel(uint64_t *__restrict__ p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0;
 }
 
 }  // namespace
@@ -804,7 +930,7 @@ __global__ __launch_bounds__(256) void chain_clear_kernel(uint64_t *__restrict__
 namespace {
 struct ChainLayout {
   int64_t tiles_w, tiles;
-  size_t head, stats_off, total;
+  size_t head, stats_off, arrivals_off, queue_off, total;
 };
 ChainLayout chain_layout(int64_t N, int64_t H, int64_t W, int64_t K, int64_t groups) {
   ChainLayout L;
@@ -813,7 +939,10 @@ ChainLayout chain_layout(int64_t N, int64_t H, int64_t W, int64_t K, int64_t gro
   L.tiles = ((Ho + kTileH - 1) / kTileH) * L.tiles_w;
   L.head = ((size_t)(2 * N * groups) * sizeof(float) + 255) / 256 * 256;  // mean, rstd
   L.stats_off = L.head + sizeof(ChainWsHeader);
-  L.total = L.stats_off + (size_t)(N * L.tiles * groups) * sizeof(uint64_t);
+  L.arrivals_off = L.stats_off + (size_t)(N * L.tiles * groups) * sizeof(uint64_t);
+  L.queue_off = L.arrivals_off + (size_t)N * sizeof(uint64_t);
+  // one queue slot per tile pair
+  L.total = L.queue_off + ((size_t)(N * ((L.tiles + kTeams - 1) / kTeams)) * 4 + 7) / 8 * 8;
   return L;
 }
 }  // namespace
@@ -869,22 +998,36 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
   a.rstd = a.mean + N * groups;
   a.hdr = reinterpret_cast<ChainWsHeader *>(base + L.head);
   a.stats = reinterpret_cast<uint64_t *>(base + L.stats_off);
+  a.arrivals = reinterpret_cast<uint64_t *>(base + L.arrivals_off);
+  a.queue = reinterpret_cast<uint32_t *>(base + L.queue_off);
+  a.block_base = 0;
+  // The header, the statistics words and the queue start at 0.
   const int64_t words = (int64_t)((L.total - L.head) / sizeof(uint64_t));
-  hipLaunchKernelGGL(chain_clear_kernel, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0,
-                     stream, reinterpret_cast<uint64_t *>(base + L.head), words);
-  const hipError_t e = hipGetLastError();
+  const int64_t clear_blocks = std::min<int64_t>((words + 255) / 256, 4096);
+  hipLaunchKernelGGL(chain_clear_kernel, dim3((uint32_t)clear_blocks), dim3(256), 0, stream,
+                     reinterpret_cast<uint64_t *>(base + L.head), words);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t per_sample = (L.tiles + kTeams - 1) / kTeams;  // workgroups per sample
-  const dim3 grid((uint32_t)(N * per_sample)), block(kTeams * kThreads);
-  if (per_sample <= fused_pair_limit()) {
-    hipLaunchKernelGGL(conv_chain_pair_kernel<kFused>, grid, block, 0, stream, a);
-    return hipGetLastError();
+  const bool fused = per_sample <= fused_pair_limit();
+  // Samples per launch: a dispatch's work-item count must fit 32 bits.  The
+  // fused launches need no offset: each claims the next tickets in order.
+  const int64_t max_n = std::max<int64_t>(1, (0xffffffffll / (kTeams * kThreads)) / per_sample);
+  const dim3 block(kTeams * kThreads);
+  for (int64_t n0 = 0; n0 < N; n0 += max_n) {
+    const int64_t nb = std::min(max_n, N - n0);
+    const dim3 grid((uint32_t)(nb * per_sample));
+    a.block_base = (uint32_t)(n0 * per_sample);
+    if (fused) {
+      hipLaunchKernelGGL(conv_chain_pair_kernel<kFused>, grid, block, 0, stream, a);
+    } else {
+      hipLaunchKernelGGL(conv_chain_pair_kernel<kStats>, grid, block, 0, stream, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(conv_chain_pair_kernel<kApply>, grid, block, 0, stream, a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(conv_chain_pair_kernel<kStats>, grid, block, 0, stream, a);
-  const hipError_t e2 = hipGetLastError();
-  if (e2 != hipSuccess) return e2;
-  hipLaunchKernelGGL(conv_chain_pair_kernel<kApply>, grid, block, 0, stream, a);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace lse

@@ -9,6 +9,7 @@
 #include <string>
 
 #include "../../include/lse.h"
+#include "../../include/lse_testing.h"
 #include "lse_internal.hpp"
 
 #define LSE_EXPORT extern "C" __attribute__((visibility("default")))
@@ -53,6 +54,8 @@ bool overlaps(const void *a, int64_t a_bytes, const void *b, int64_t b_bytes) {
 
 constexpr int64_t kMaxElems = INT64_MAX / 16;  // keeps every byte offset in range
 constexpr int64_t kMaxGrid = 0x7fffffff;
+// Workgroups of 512 lanes whose work-items fit one dispatch (32-bit count).
+constexpr int64_t kMaxWorkgroups512 = 0xffffffffll / 512;
 
 // a + b (both >= 0) capped: false when the sum passes kMaxElems.
 bool add_ok(int64_t a, int64_t b, int64_t *r) {
@@ -89,7 +92,7 @@ LSE_EXPORT const char *lse_last_error(void) { return g_last_error.c_str(); }
 
 LSE_EXPORT int lse_abi_version(void) { return LSE_ABI_VERSION; }
 
-LSE_EXPORT void lse_set_spin_limit(uint32_t polls) { lse::set_spin_limit(polls); }
+LSE_EXPORT void lse_testing_set_spin_limit(uint32_t polls) { lse::set_spin_limit(polls); }
 
 // ------------------------------------------------------------------ case A
 LSE_EXPORT lse_status_t lse_reduce_axis0(const float *x, float *out, int64_t R, int64_t inner,
@@ -294,6 +297,9 @@ LSE_EXPORT lse_status_t lse_rows_partial(const float *x, int64_t rows, int64_t c
   int64_t wgs;
   if (!mul_ok(rows, k, &wgs) || wgs > kMaxGrid)
     return fail(LSE_ERR_SHAPE, "lse_rows_partial: rows * chunks = too many workgroups");
+  if (k > kMaxWorkgroups512)  // one row's chunks must fit one dispatch
+    return fail(LSE_ERR_SHAPE, "lse_rows_partial: %lld chunks per row exceed one launch",
+                (long long)k);
   if (overlaps(x, total * 4, partials, wgs * 8))
     return fail(LSE_ERR_OVERLAP, "lse_rows_partial: partials overlap x");
   return from_hip(lse::launch_lse_rows_partial(x, rows, cols, cols, chunk, partials, stream),

@@ -694,9 +694,36 @@ hipError_t launch_axis_t(const float *x, float *out, const AxisDims &d, hipStrea
   return launch_rb<32, LSM, STR>(x, out, d, vec, stream);
 }
 
+// Outputs per launch: every kernel above runs at most 4 work-items per output
+// (the plane split: P waves per run of 4-column lanes), so 2^29 outputs keep a
+// dispatch's work-item count within 32 bits.
+constexpr int64_t kMaxAxisOutputs = int64_t(1) << 29;
+
 // Contiguous calls take instantiations whose strides derive from R and inner.
+// Larger calls run as several launches of the strided instantiation over
+// consecutive outer blocks, or over 2^29-column slices of the inner run.
 template <bool LSM>
 hipError_t launch_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream) {
+  if (d.outer * d.inner > kMaxAxisOutputs) {
+    hipError_t e = hipSuccess;
+    if (d.inner <= kMaxAxisOutputs) {
+      const int64_t ob = kMaxAxisOutputs / d.inner;
+      for (int64_t o0 = 0; o0 < d.outer && e == hipSuccess; o0 += ob) {
+        AxisDims s = d;
+        s.outer = (d.outer - o0 < ob) ? (d.outer - o0) : ob;
+        e = launch_axis_t<LSM, true>(x + o0 * d.xso, out + o0 * d.yso, s, stream);
+      }
+    } else {
+      for (int64_t o = 0; o < d.outer && e == hipSuccess; ++o)
+        for (int64_t j0 = 0; j0 < d.inner && e == hipSuccess; j0 += kMaxAxisOutputs) {
+          AxisDims s = d;
+          s.outer = 1;
+          s.inner = (d.inner - j0 < kMaxAxisOutputs) ? (d.inner - j0) : kMaxAxisOutputs;
+          e = launch_axis_t<LSM, true>(x + o * d.xso + j0, out + o * d.yso + j0, s, stream);
+        }
+    }
+    return e;
+  }
   const bool contiguous = d.xsr == d.inner && (d.outer == 1 || d.xso == d.R * d.inner) &&
                           (LSM ? (d.ysr == d.inner && (d.outer == 1 || d.yso == d.R * d.inner))
                                : (d.outer == 1 || d.yso == d.inner));

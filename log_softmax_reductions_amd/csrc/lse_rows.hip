@@ -11,10 +11,12 @@
 //   NaN once idle lanes holding (-inf, 0) meet.
 //
 // Design here (gfx950):
-//   * A workgroup of 512 lanes owns one chunk of up to 16384 columns and keeps
-//     it in VGPRs (32 floats per lane, 8 global_load_dwordx4 per lane), so the
-//     chunk is read from HBM exactly once and written exactly once; loads and
-//     stores are non-temporal (nothing is re-read through the caches).
+//   * A workgroup of 512 lanes owns one chunk of up to 32768 columns and keeps
+//     it in VGPRs (64 floats per lane, 16 non-temporal global_load_dwordx4 per
+//     lane; each wave owns one contiguous 16 KiB run of the chunk), so the
+//     chunk is read from HBM exactly once and written exactly once.  Full
+//     chunks are stored through a raw buffer resource with the nt | sc1
+//     cache-policy bits; partial chunks with non-temporal global stores.
 //   * Exact chunk max (DPP/permlane wave reduce + LDS), then the sum of
 //     exp(x - max) over the registers: one exponential per element.
 //   * A row of k > 1 chunks: each workgroup publishes its pair as one packed
@@ -22,11 +24,16 @@
 //     row's k words, and every workgroup of the row merges the same k pairs in
 //     the same order (so all get the bitwise-same row LSE) and writes its
 //     chunk of y from registers.  A workgroup that has waited 50 us computes
-//     any still-missing sibling pair itself from x; the first writer of a slot
-//     wins.  No global counter is touched and no workgroup can wait on one
-//     that never starts, whatever the dispatch order.
+//     any still-missing sibling pair itself from x, in its register tile with
+//     the owner's own code (so the pair is bit-identical whoever computes it),
+//     then reloads its own chunk; the first writer of a slot wins.  No global
+//     counter is touched and no workgroup can wait on one that never starts,
+//     whatever the dispatch order.
 //   * The write is y = (x - M) - log(S): x - M is exact for the large entries,
 //     so the result keeps its accuracy when |M| is large.
+//   * A launch covers at most kMaxRowsWorkgroups workgroups (its work-item
+//     count must fit 32 bits); longer grids are split into launches over
+//     consecutive rows.
 #include <atomic>
 
 #include "lse_device.hpp"
@@ -45,7 +52,13 @@ constexpr int kNW = kRowsThreads / kWave;  // waves per workgroup
 #ifndef LSE_ROWS_NT_STORE
 #define LSE_ROWS_NT_STORE 1       // y is never re-read: non-temporal stores
 #endif
-std::atomic<uint32_t> h_spin_limit{1u << 24};
+constexpr uint32_t kDefaultSpinLimit = 1u << 24;
+// Poll limit of the split rows' and the conv chain's waits, per host thread
+// (a test hook: 0 forces every pair through the helping path).
+thread_local uint32_t h_spin_limit = kDefaultSpinLimit;
+// Workgroups of kRowsThreads lanes per launch: the dispatch's work-item count
+// (workgroups x lanes) must fit 32 bits.
+constexpr int64_t kMaxRowsWorkgroups = 0xffffffffll / kRowsThreads;
 
 #ifndef LSE_ROWS_WAVE_CONTIG
 #define LSE_ROWS_WAVE_CONTIG 1
@@ -185,30 +198,101 @@ __device__ __forceinline__ float out_scale(float S) {
 }
 
 // The chunk's pair (exact max, sum of exp(v - max)); identical in every lane.
-// Four independent accumulators shorten the dependency chains.
+// One running max and one running sum per lane, over e = 0 .. VPL-1 in order
+// (a wave issues dependent VALU operations back to back, so more accumulators
+// would buy no latency hiding), then the workgroup reductions.
 template <int VPL>
 __device__ __forceinline__ void chunk_pair(const float (&v)[VPL], float *red, float &m,
                                            float &s) {
-  static_assert(VPL % 4 == 0, "VPL is a multiple of 4");
-  float lm[4] = {v[0], v[1], v[2], v[3]};
+  float lm = v[0];
 #pragma unroll
-  for (int e = 4; e < VPL; ++e) lm[e % 4] = fmaxf(lm[e % 4], v[e]);
-  m = block_allreduce<kNW>(fmaxf(fmaxf(lm[0], lm[1]), fmaxf(lm[2], lm[3])), OpMax{}, red);
-  float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int e = 1; e < VPL; ++e) lm = fmaxf(lm, v[e]);
+  m = block_allreduce<kNW>(lm, OpMax{}, red);
+  float ls = 0.0f;
   if (is_finite(m)) {  // uniform branch: m is the same in every lane
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) ls[e % 4] += exp_base2(v[e] - m);
+    for (int e = 0; e < VPL; ++e) ls += exp_base2(v[e] - m);
   } else {
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) ls[e % 4] += pair_term_nonfinite(v[e], m);
+    for (int e = 0; e < VPL; ++e) ls += pair_term_nonfinite(v[e], m);
   }
-  s = block_allreduce<kNW>((ls[0] + ls[1]) + (ls[2] + ls[3]), OpSum{}, red);
+  s = block_allreduce<kNW>(ls, OpSum{}, red);
+}
+
+// chunk_pair of a chunk that is not in this workgroup's registers (a
+// sibling's, computed by the helping path): the same values reach the same
+// lanes and meet the same operations in the same order (the running max and
+// the running sum over e = 0 .. VPL-1, the same workgroup reductions), so the
+// pair is bit-identical to the one the chunk's owner computes.  The chunk is
+// streamed twice (max, then sum) instead of held.
+template <int VPL, bool VEC>
+__device__ __forceinline__ void chunk_pair_streamed(const float *__restrict__ p, int64_t len,
+                                                    float *red, float &m, float &s) {
+  const int t = threadIdx.x;
+  // Value e = 4 q + r of lane t: VEC, element r of float4 vec4_index<VPL>(q, t)
+  // (one pointer stepped by kStep4 float4 per q); otherwise element
+  // e * kRowsThreads + t.  -inf past len, as load_chunk pads.
+#if LSE_ROWS_WAVE_CONTIG
+  constexpr int64_t kStep4 = kWave;
+#else
+  constexpr int64_t kStep4 = kRowsThreads;
+#endif
+  const float4 *p4;
+  int64_t idx;
+  auto start = [&]() {
+    p4 = reinterpret_cast<const float4 *>(p) + vec4_index<VPL>(0, t);
+    idx = VEC ? vec4_index<VPL>(0, t) * 4 : (int64_t)t;
+  };
+  auto values = [&](float (&f)[4]) {
+    if constexpr (VEC) {
+      if (idx < len) {
+        const float4 g = *p4;
+        f[0] = g.x; f[1] = g.y; f[2] = g.z; f[3] = g.w;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f[r] = -__builtin_inff();
+      }
+      p4 += kStep4;
+      idx += 4 * kStep4;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f[r] = (idx < len) ? p[idx] : -__builtin_inff();
+        idx += kRowsThreads;
+      }
+    }
+  };
+  start();
+  float lm;
+  {
+    float f[4];
+    values(f);
+    lm = fmaxf(fmaxf(fmaxf(f[0], f[1]), f[2]), f[3]);
+  }
+#pragma unroll 1
+  for (int q = 1; q < VPL / 4; ++q) {
+    float f[4];
+    values(f);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lm = fmaxf(lm, f[r]);
+  }
+  m = block_allreduce<kNW>(lm, OpMax{}, red);
+  start();
+  float ls = 0.0f;
+  const bool fin = is_finite(m);
+#pragma unroll 1
+  for (int q = 0; q < VPL / 4; ++q) {
+    float f[4];
+    values(f);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ls += fin ? exp_base2(f[r] - m) : pair_term_nonfinite(f[r], m);
+  }
+  s = block_allreduce<kNW>(ls, OpSum{}, red);
 }
 
 // The pair of a chunk streamed from memory by the whole workgroup: an exact
 // max pass, then a sum pass (the second read is served by cache).  Used for
-// chunks longer than the register tile and by a workgroup that computes a
-// sibling's missing pair.
+// chunks longer than the register tile.
 __device__ __forceinline__ void stream_chunk_pair(const float *__restrict__ p, int64_t len,
                                                   float *red, float &m, float &s) {
   float lm = -__builtin_inff();
@@ -332,7 +416,7 @@ __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
           const int64_t j0 = j * chunk;
           const int64_t lj = (cols - j0 < chunk) ? (cols - j0) : chunk;
           float hm, hs;
-          stream_chunk_pair(x + row * ldx + j0, lj, red, hm, hs);
+          chunk_pair_streamed<VPL, VEC>(x + row * ldx + j0, lj, red, hm, hs);
           if (threadIdx.x == 0 && publish_pair_once(row_pairs + j, pack_pair(hm, hs)))
             __hip_atomic_fetch_add(&hdr->helped, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -357,10 +441,16 @@ __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
   store_chunk<VPL, VEC, SOFTMAX>(yr, len, v, M, lnS);
 }
 
-// Clear n 64-bit words (the workspace header and pair slots).
+// Clear n 64-bit words (the workspace header and pair slots); grid-stride, so
+// any n fits a grid of at most kClearBlocks workgroups.
+constexpr int64_t kClearBlocks = 4096;
 __global__ __launch_bounds__(256) void clear_words_kernel(uint64_t *__restrict__ p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0;
+}
+uint32_t clear_blocks(int64_t words) {
+  const int64_t b = (words + 255) / 256;
+  return (uint32_t)(b < kClearBlocks ? b : kClearBlocks);
 }
 
 // ------------------------------------------------------------ partial/merge
@@ -648,6 +738,20 @@ hipError_t launch_rows_vpl(int vpl, bool vec, dim3 grid, const float *x, float *
   return hipGetLastError();
 }
 
+// Runs launch(r0, nr) over consecutive row ranges of at most max_rows rows,
+// so that no single dispatch exceeds 32-bit work-item counts; stops at the
+// first failed launch.
+template <class F>
+hipError_t for_row_batches(int64_t rows, int64_t max_rows, F launch) {
+  if (max_rows < 1) return hipErrorInvalidConfiguration;  // one row alone is too large
+  for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
+    const int64_t nr = (rows - r0 < max_rows) ? (rows - r0) : max_rows;
+    const hipError_t e = launch(r0, nr);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <bool SOFTMAX>
 hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols, int64_t ldx,
                             int64_t ldy, void *ws, hipStream_t stream) {
@@ -655,27 +759,32 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
   const bool vec = (cols % 4 == 0) && (p.chunk % 4 == 0) && (ldx % 4 == 0) &&
                    (ldy % 4 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0);
   if (p.nchunks == 1) {
-    return launch_rows_vpl<false, SOFTMAX>(vpl_for(cols), vec, dim3((uint32_t)rows), x, y, rows,
-                                           cols, ldx, ldy, 1, cols, nullptr, nullptr, 0u,
-                                           stream);
+    return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
+      return launch_rows_vpl<false, SOFTMAX>(vpl_for(cols), vec, dim3((uint32_t)nr), x + r0 * ldx,
+                                             y + r0 * ldy, nr, cols, ldx, ldy, 1, cols, nullptr,
+                                             nullptr, 0u, stream);
+    });
   }
   auto *hdr = reinterpret_cast<RowsWsHeader *>(ws);
   auto *pairs = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws) + sizeof(RowsWsHeader));
   const int64_t words = (int64_t)(rows_workspace_bytes(rows, cols) / sizeof(uint64_t));
-  hipLaunchKernelGGL(clear_words_kernel, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0,
-                     stream, reinterpret_cast<uint64_t *>(ws), words);
+  hipLaunchKernelGGL(clear_words_kernel, dim3(clear_blocks(words)), dim3(256), 0, stream,
+                     reinterpret_cast<uint64_t *>(ws), words);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_rows_vpl<true, SOFTMAX>(vpl_for(p.chunk), vec,
-                                        dim3((uint32_t)(rows * p.nchunks)), x, y, rows, cols,
-                                        ldx, ldy, p.nchunks, p.chunk, hdr, pairs,
-                                        h_spin_limit.load(std::memory_order_relaxed), stream);
+  const uint32_t spin = h_spin_limit;
+  return for_row_batches(rows, kMaxRowsWorkgroups / p.nchunks, [&](int64_t r0, int64_t nr) {
+    return launch_rows_vpl<true, SOFTMAX>(vpl_for(p.chunk), vec, dim3((uint32_t)(nr * p.nchunks)),
+                                          x + r0 * ldx, y + r0 * ldy, nr, cols, ldx, ldy,
+                                          p.nchunks, p.chunk, hdr, pairs + r0 * p.nchunks, spin,
+                                          stream);
+  });
 }
 
 }  // namespace
 
-void set_spin_limit(uint32_t polls) { h_spin_limit.store(polls, std::memory_order_relaxed); }
-uint32_t chain_spin_limit() { return h_spin_limit.load(std::memory_order_relaxed); }
+void set_spin_limit(uint32_t polls) { h_spin_limit = polls; }
+uint32_t chain_spin_limit() { return h_spin_limit; }
 
 RowsPlan rows_plan(int64_t cols) {
   RowsPlan p;
@@ -708,70 +817,77 @@ hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, i
                                    int64_t chunk, void *partials, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const int64_t nchunks = (cols + chunk - 1) / chunk;
-  const dim3 grid((uint32_t)(rows * nchunks));
-  auto *out = reinterpret_cast<float2 *>(partials);
-  if (chunk > kRowsTile) {
-    hipLaunchKernelGGL(lse_rows_partial_stream_kernel, grid, dim3(kRowsThreads), 0, stream, x,
-                       cols, ldx, nchunks, chunk, out);
-    return hipGetLastError();
-  }
   const bool vec =
       (cols % 4 == 0) && (chunk % 4 == 0) && (ldx % 4 == 0) && ((uintptr_t)x % 16 == 0);
+  const int vpl = chunk > kRowsTile ? 0 : vpl_for(chunk);
+  return for_row_batches(rows, kMaxRowsWorkgroups / nchunks, [&](int64_t r0, int64_t nr) {
+    const dim3 grid((uint32_t)(nr * nchunks));
+    const float *xb = x + r0 * ldx;
+    auto *out = reinterpret_cast<float2 *>(partials) + r0 * nchunks;
+    if (vpl == 0) {
+      hipLaunchKernelGGL(lse_rows_partial_stream_kernel, grid, dim3(kRowsThreads), 0, stream, xb,
+                         cols, ldx, nchunks, chunk, out);
+      return hipGetLastError();
+    }
 #define LSE_PART_CASE(V)                                                                       \
   case V:                                                                                      \
     if (vec)                                                                                   \
       hipLaunchKernelGGL((lse_rows_partial_kernel<V, true>), grid, dim3(kRowsThreads), 0,      \
-                         stream, x, cols, ldx, nchunks, chunk, out);                           \
+                         stream, xb, cols, ldx, nchunks, chunk, out);                          \
     else                                                                                       \
       hipLaunchKernelGGL((lse_rows_partial_kernel<V, false>), grid, dim3(kRowsThreads), 0,     \
-                         stream, x, cols, ldx, nchunks, chunk, out);                           \
+                         stream, xb, cols, ldx, nchunks, chunk, out);                          \
     break;
-  switch (vpl_for(chunk)) {
-    LSE_PART_CASE(4)
-    LSE_PART_CASE(8)
-    LSE_PART_CASE(16)
-    LSE_PART_CASE(32)
-    LSE_PART_CASE(64)
-    default:
-      return hipErrorInvalidValue;
-  }
+    switch (vpl) {
+      LSE_PART_CASE(4)
+      LSE_PART_CASE(8)
+      LSE_PART_CASE(16)
+      LSE_PART_CASE(32)
+      default:
+        return hipErrorInvalidValue;
+    }
 #undef LSE_PART_CASE
-  return hipGetLastError();
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_rows_lse(const float *x, int64_t rows, int64_t cols, int64_t ldx, float *out,
                            int64_t ldo, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const dim3 grid((uint32_t)rows);
   const bool vec = (cols % 4 == 0) && (ldx % 4 == 0) && ((uintptr_t)x % 16 == 0);
-  if (cols > kRowsTile) {
-    if (vec)
-      hipLaunchKernelGGL(rows_lse_stream_kernel<true>, grid, dim3(kRowsThreads), 0, stream, x,
-                         cols, ldx, out, ldo);
-    else
-      hipLaunchKernelGGL(rows_lse_stream_kernel<false>, grid, dim3(kRowsThreads), 0, stream, x,
-                         cols, ldx, out, ldo);
-    return hipGetLastError();
-  }
+  return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
+    const dim3 grid((uint32_t)nr);
+    const float *xb = x + r0 * ldx;
+    float *ob = out + r0 * ldo;
+    if (cols > kRowsTile) {
+      if (vec)
+        hipLaunchKernelGGL(rows_lse_stream_kernel<true>, grid, dim3(kRowsThreads), 0, stream, xb,
+                           cols, ldx, ob, ldo);
+      else
+        hipLaunchKernelGGL(rows_lse_stream_kernel<false>, grid, dim3(kRowsThreads), 0, stream,
+                           xb, cols, ldx, ob, ldo);
+      return hipGetLastError();
+    }
 #define LSE_ROWLSE_CASE(V)                                                                     \
   case V:                                                                                      \
     if (vec)                                                                                   \
-      hipLaunchKernelGGL((rows_lse_kernel<V, true>), grid, dim3(kRowsThreads), 0, stream, x,   \
-                         cols, ldx, out, ldo);                                                 \
+      hipLaunchKernelGGL((rows_lse_kernel<V, true>), grid, dim3(kRowsThreads), 0, stream, xb,  \
+                         cols, ldx, ob, ldo);                                                  \
     else                                                                                       \
-      hipLaunchKernelGGL((rows_lse_kernel<V, false>), grid, dim3(kRowsThreads), 0, stream, x,  \
-                         cols, ldx, out, ldo);                                                 \
+      hipLaunchKernelGGL((rows_lse_kernel<V, false>), grid, dim3(kRowsThreads), 0, stream, xb, \
+                         cols, ldx, ob, ldo);                                                  \
     break;
-  switch (vpl_for(cols)) {
-    LSE_ROWLSE_CASE(4)
-    LSE_ROWLSE_CASE(8)
-    LSE_ROWLSE_CASE(16)
-    LSE_ROWLSE_CASE(32)
-    default:
-      return hipErrorInvalidValue;
-  }
+    switch (vpl_for(cols)) {
+      LSE_ROWLSE_CASE(4)
+      LSE_ROWLSE_CASE(8)
+      LSE_ROWLSE_CASE(16)
+      LSE_ROWLSE_CASE(32)
+      default:
+        return hipErrorInvalidValue;
+    }
 #undef LSE_ROWLSE_CASE
-  return hipGetLastError();
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_log_softmax_rows_no_ws(const float *x, float *y, int64_t rows, int64_t cols,
@@ -780,28 +896,36 @@ hipError_t launch_log_softmax_rows_no_ws(const float *x, float *y, int64_t rows,
   if (rows == 0) return hipSuccess;
   if (cols <= kRowsTile)  // one chunk per row: the register kernel needs no workspace
     return launch_log_softmax_rows(x, y, rows, cols, ldx, ldy, nullptr, stream, softmax);
-  const dim3 grid((uint32_t)rows);
   const bool vec = (cols % 4 == 0) && (ldx % 4 == 0) && (ldy % 4 == 0) &&
                    ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0);
+  return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
+    const dim3 grid((uint32_t)nr);
+    const float *xb = x + r0 * ldx;
+    float *yb = y + r0 * ldy;
 #define LSE_ROWSTREAM(V, S)                                                                    \
-  hipLaunchKernelGGL((rows_stream_write_kernel<V, S>), grid, dim3(kRowsThreads), 0, stream, x, \
-                     y, cols, ldx, ldy)
-  if (vec) {
-    if (softmax) LSE_ROWSTREAM(true, true); else LSE_ROWSTREAM(true, false);
-  } else {
-    if (softmax) LSE_ROWSTREAM(false, true); else LSE_ROWSTREAM(false, false);
-  }
+  hipLaunchKernelGGL((rows_stream_write_kernel<V, S>), grid, dim3(kRowsThreads), 0, stream,    \
+                     xb, yb, cols, ldx, ldy)
+    if (vec) {
+      if (softmax) LSE_ROWSTREAM(true, true); else LSE_ROWSTREAM(true, false);
+    } else {
+      if (softmax) LSE_ROWSTREAM(false, true); else LSE_ROWSTREAM(false, false);
+    }
 #undef LSE_ROWSTREAM
-  return hipGetLastError();
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_lse_rows_merge(const void *partials, int64_t rows, int64_t nchunks,
                                  float *row_lse, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const int64_t blocks = (rows + 3) / 4;
-  hipLaunchKernelGGL(lse_rows_merge_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const float2 *>(partials), rows, nchunks, row_lse);
-  return hipGetLastError();
+  // one wave per row, 4 rows per 256-lane workgroup
+  return for_row_batches(rows, 4 * (0xffffffffll / 256), [&](int64_t r0, int64_t nr) {
+    const int64_t blocks = (nr + 3) / 4;
+    hipLaunchKernelGGL(lse_rows_merge_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float2 *>(partials) + r0 * nchunks, nr, nchunks,
+                       row_lse + r0);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace lse

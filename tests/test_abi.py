@@ -11,7 +11,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "lse.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("lse.h", "lse_testing.h")]
 
 LSE_OK, LSE_ERR_NULL, LSE_ERR_SHAPE, LSE_ERR_WORKSPACE, LSE_ERR_OVERLAP = 0, 1, 2, 3, 4
 LSE_ERR_UNSUPPORTED = 6
@@ -20,7 +20,9 @@ FAKE2 = ctypes.c_void_p(0x900000000)
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    assert sorted(HEADERS) == sorted(
+        os.path.join(ROOT, "include", h) for h in os.listdir(os.path.join(ROOT, "include")))
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
     keywords = {"sizeof", "defined"}
@@ -148,6 +150,13 @@ def test_partial_merge_validation(lib):
     assert lib.lse_rows_merge(None, 4, 3, FAKE2, None) == LSE_ERR_NULL
 
 
+def test_partial_chunks_per_row_limit(lib):
+    """One row's chunks run in one dispatch: more than 2^32 / 512 of them is a
+    shape error, found before anything is launched."""
+    assert lib.lse_rows_partial(FAKE, 1, 9_000_000, 1, FAKE2, None) == LSE_ERR_SHAPE
+    assert b"exceed one launch" in lib.lse_last_error()
+
+
 def test_chain_validation(lib):
     args = lambda K=3, Cin=8, Cout=64, G=16, ws=FAKE2, wsb=1 << 30: (
         FAKE, FAKE, None, None, None, 2, Cin, 10, 10, Cout, K, G, ctypes.c_float(1e-5),
@@ -166,8 +175,9 @@ def test_chain_validation(lib):
         a[i] = ctypes.c_void_p(0x900000000 + 256)          # inside the workspace
         assert lib.fused_conv_gn_act_lse(*a) == LSE_ERR_OVERLAP
     need = lib.fused_conv_gn_act_lse_workspace_bytes(128, 8, 128, 128, 64, 3, 16)
-    # mean and rstd (N x G floats each), a 256-byte header, one 8-byte word per (n, tile, g)
-    assert need == 2 * 128 * 16 * 4 + 256 + 128 * 63 * 16 * 8
+    # mean and rstd (N x G floats each), a 256-byte header, one 8-byte word per
+    # (n, tile, g), one 4-byte queue slot per tile pair (32 per sample)
+    assert need == 2 * 128 * 16 * 4 + 256 + 128 * 63 * 16 * 8 + 128 * 32 * 4
 
 
 def test_last_error_is_per_thread(lib):

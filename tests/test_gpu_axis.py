@@ -160,3 +160,26 @@ def test_last_axis_special_values(orc):
                 what=f"lse last axis special {r}")
         compare(y.cpu().numpy(), orc.log_softmax_axis(xc.reshape(*r, 1)).reshape(r),
                 what=f"lsm last axis special {r}")
+
+
+@pytest.mark.parametrize("outer,R,inner", [(1, 2, (1 << 29) + 1000), (3, 3, 200_000_000)])
+def test_axis_more_outputs_than_one_launch(orc, outer, R, inner):
+    """More than 2^29 outputs run as several launches (over the inner run,
+    or over outer blocks): sampled columns on both sides of each split
+    against the oracle (logsumexp and log_softmax), and every column by
+    property on a window across a split."""
+    x = inputs.normal((outer, R, inner), seed=inner % 1009, device=DEV)
+    out = L.lse_reduce_axis(x, 1)
+    torch.cuda.synchronize()
+    cols = [0, 1, (1 << 29) - 1, (1 << 29), inner - 1] if outer == 1 else [0, 5, inner - 1]
+    cols = [c for c in cols if c < inner]
+    xs = x[:, :, cols].cpu().numpy()
+    compare(out[:, cols].cpu().numpy(), orc.lse_axis(xs), what="lse split")
+    w = slice(max(0, min(inner, 1 << 29) - 100_000), min(inner, (1 << 29) + 100_000))
+    ref = torch.logsumexp(x[:, :, w].double(), dim=1)
+    assert (out[:, w].double() - ref).abs().max().item() < 1e-5 + 2e-6 * ref.abs().max().item()
+    del out
+    y = L.log_softmax_axis(x, 1)
+    torch.cuda.synchronize()
+    compare(y[:, :, cols].cpu().numpy(), orc.log_softmax_axis(xs), what="lsm split")
+    assert torch.logsumexp(y[:, :, w].double(), dim=1).abs().max().item() < 1e-5

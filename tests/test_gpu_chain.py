@@ -143,3 +143,46 @@ def test_chain_constant_input(orc):
     x, w, _, _, _ = _chain_inputs(1, 10, 40, seed=9)
     x.fill_(0.75)
     _check(orc, x, w, None, None, None, 16, "constant input")
+
+
+def _deferred_word(ws, N, groups):
+    head = (2 * N * groups * 4 + 255) // 256 * 256
+    return int(ws[head + 4: head + 8].view(torch.int32).item())
+
+
+@pytest.mark.parametrize("N,H,W,groups", [(2, 128, 128, 16), (3, 37, 300, 4), (1, 600, 520, 1)])
+def test_chain_deferred_pairs(orc, N, H, W, groups):
+    """With the test hook's poll limit at 0 no workgroup waits: each one whose
+    sample has not fully arrived defers its tile pair, and the sample's last
+    arrival finishes those pairs (the path a workgroup takes when its wait
+    runs out).  Outputs and statistics against the oracle, bit-equality with
+    the default path, and the deferred count: at least one pair per sample
+    (the first arrival cannot see the whole sample), never a sample's last
+    arrival.  Shapes: two config-sized samples, a ragged one (odd tile rows,
+    three tile columns), and a sample large enough for the two-launch path."""
+    x, w, b, g, be = _chain_inputs(N, H, W, seed=7 * N + H + W, affine=True)
+    pairs = N * ((((H - 2) + 1) // 2 * ((W - 2 + 127) // 128) + 1) // 2)
+    ws = torch.empty(L.fused_conv_gn_act_lse_workspace_bytes(N, 8, H, W, 64, 3, groups),
+                     dtype=torch.uint8, device=DEV)
+    try:
+        L.lse_testing_set_spin_limit(0)
+        out = L.fused_conv_gn_act_lse(x, w, b, g, be, groups, 1e-5, ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        L.lse_testing_set_spin_limit(1 << 24)
+    deferred = _deferred_word(ws, N, groups)
+    assert N <= deferred <= pairs - N, (deferred, pairs)
+    print("pairs deferred:", deferred, "of", pairs)
+    NG = N * groups
+    stats = ws[: 2 * NG * 4].view(torch.float32).clone()
+    cpu = lambda t: None if t is None else t.cpu().numpy()
+    ref, mean, rstd = orc.fused_chain(cpu(x), cpu(w), cpu(b), cpu(g), cpu(be), groups, 1e-5)
+    compare(out.cpu().numpy(), ref, rtol=RTOL_CHAIN, what="deferred")
+    compare(stats[:NG].cpu().numpy(), mean.ravel(), atol=1e-6, rtol=1e-4, what="deferred mean")
+    compare(stats[NG:].cpu().numpy(), rstd.ravel(), atol=1e-6, rtol=1e-4, what="deferred rstd")
+    ws2 = torch.empty_like(ws)
+    out2 = L.fused_conv_gn_act_lse(x, w, b, g, be, groups, 1e-5, ws=ws2)
+    torch.cuda.synchronize()
+    assert _deferred_word(ws2, N, groups) == 0
+    assert torch.equal(out, out2)
+    assert torch.equal(stats, ws2[: 2 * NG * 4].view(torch.float32))

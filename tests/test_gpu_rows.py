@@ -155,10 +155,12 @@ def test_partials_special_values(orc):
 
 
 def test_rows_helping_path(orc):
-    """With the poll limit at 0 no workgroup publishes its own pair: every pair is
-    computed from x by the helping path (a workgroup that finds a sibling's
-    slot empty).  Results must match the oracle and the workspace must count
-    exactly rows x chunks helped pairs."""
+    """With the test hook's poll limit at 0 no workgroup publishes its own pair:
+    every pair is computed from x by the helping path (a workgroup that finds
+    a sibling's slot empty).  Results must match the oracle, the workspace
+    must count exactly rows x chunks helped pairs, and the output must be
+    bit-identical to the default path's (a helper reproduces the owner's
+    arithmetic), on full and partial chunks."""
     rows, cols = 64, 393216
     x = inputs.normal((rows, cols), seed=31, device=DEV)
     nbytes = L.log_softmax_rows_workspace_bytes(rows, cols)
@@ -166,11 +168,11 @@ def test_rows_helping_path(orc):
     sample = [0, 5, 33, 63]
     ref, _ = orc.log_softmax_rows(x[sample].cpu().numpy())
     try:
-        L.lse_set_spin_limit(0)
+        L.lse_testing_set_spin_limit(0)
         y = L.log_softmax_rows(x, ws=ws)
         torch.cuda.synchronize()
     finally:
-        L.lse_set_spin_limit(1 << 24)
+        L.lse_testing_set_spin_limit(1 << 24)
     helped = int(ws[4:8].view(torch.int32).item())
     assert helped == rows * 12, helped      # every pair came from the helping path
     compare(y[sample].cpu().numpy(), ref, what="helping path")
@@ -179,6 +181,50 @@ def test_rows_helping_path(orc):
     y2 = L.log_softmax_rows(x, ws=ws)
     torch.cuda.synchronize()
     compare(y2[sample].cpu().numpy(), ref, what="default path after")
+    assert torch.equal(y, y2)
+    assert int(ws[4:8].view(torch.int32).item()) == 0
+
+
+@pytest.mark.parametrize("rows,cols,softmax", [(16, 100003, False), (8, 262147, True),
+                                                (24, 393216, True)])
+def test_rows_helping_path_bit_identical(rows, cols, softmax):
+    """Helping path against the default path, bit for bit: odd row lengths
+    (the scalar path, a partial last chunk) and softmax."""
+    x = inputs.normal((rows, cols), seed=cols % 97, device=DEV)
+    fn = L.softmax_rows if softmax else L.log_softmax_rows
+    ws = torch.empty(L.log_softmax_rows_workspace_bytes(rows, cols), dtype=torch.uint8,
+                     device=DEV)
+    nchunks, _ = L.log_softmax_rows_plan(cols)
+    try:
+        L.lse_testing_set_spin_limit(0)
+        y = fn(x, ws=ws)
+        torch.cuda.synchronize()
+    finally:
+        L.lse_testing_set_spin_limit(1 << 24)
+    assert int(ws[4:8].view(torch.int32).item()) == rows * nchunks
+    y2 = fn(x, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+def test_rows_more_workgroups_than_one_launch(orc):
+    """(8400000, 64): one workgroup per row is more than a single dispatch can
+    hold (8388607 workgroups of 512 lanes), so the rows run as two launches;
+    the partial / merge pair with 2 chunks per row as well.  Sampled rows on
+    both sides of the split against the oracle, every row by property."""
+    rows, cols = 8_400_000, 64
+    x = inputs.normal((rows, cols), seed=77, device=DEV)
+    y = L.log_softmax_rows(x)
+    p = L.lse_rows_partial(x, 32)
+    lse = L.lse_rows_merge(p)
+    torch.cuda.synchronize()
+    sample = [0, 1, 4_194_303, 4_194_304, 8_388_606, 8_388_607, 8_388_608, rows - 1]
+    ref, lref = orc.log_softmax_rows(x[sample].cpu().numpy())
+    compare(y[sample].cpu().numpy(), ref, what="rows")
+    compare(lse[sample].cpu().numpy(), lref, what="partial/merge")
+    tail = slice(rows - 200_000, rows)
+    assert torch.logsumexp(y[tail].double(), dim=1).abs().max().item() < 1e-5
+    assert (lse[tail] - torch.logsumexp(x[tail], dim=1)).abs().max().item() < 1e-4
 
 
 def test_rows_beyond_2g_elements(orc):
