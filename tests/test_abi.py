@@ -176,8 +176,9 @@ def test_chain_validation(lib):
         assert lib.fused_conv_gn_act_lse(*a) == LSE_ERR_OVERLAP
     need = lib.fused_conv_gn_act_lse_workspace_bytes(128, 8, 128, 128, 64, 3, 16)
     # mean and rstd (N x G floats each), a 256-byte header, one 8-byte word per
-    # (n, tile, g), one 4-byte queue slot per tile pair (32 per sample)
-    assert need == 2 * 128 * 16 * 4 + 256 + 128 * 63 * 16 * 8 + 128 * 32 * 4
+    # (n, tile, g), one 8-byte arrival word per sample, one 4-byte queue slot
+    # per tile pair (32 per sample)
+    assert need == 2 * 128 * 16 * 4 + 256 + 128 * 63 * 16 * 8 + 128 * 8 + 128 * 32 * 4
 
 
 def test_last_error_is_per_thread(lib):
