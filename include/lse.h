@@ -135,6 +135,20 @@ size_t log_softmax_rows_workspace_bytes(int64_t rows, int64_t cols);
 lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows,
                               int64_t cols, void *ws, size_t ws_bytes,
                               hipStream_t stream);
+/* log_softmax_rows for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, launches and results as
+ * log_softmax_rows on the same (rows, cols), but the split rows' pair
+ * workspace is a static device array inside the library (1 MiB per GPU the
+ * library runs on, held until the process ends) instead of a caller buffer.
+ * It allocates nothing.  Calls whose rows x chunks pairs exceed that array
+ * (rows x ceil(cols / 32768) > 131040, e.g. more than 10920 rows of 393216
+ * columns) return LSE_ERR_WORKSPACE with nothing launched.  All calls on one
+ * GPU share the array: calls that overlap on one GPU (other streams, other
+ * threads) race and must not be enqueued concurrently; consecutive calls on
+ * one stream are fine (each clears what it uses with a kernel). */
+lse_status_t log_softmax_rows_noalloc(const float *x, float *y, int64_t rows,
+                                      int64_t cols, hipStream_t stream);
 /* Row-wise softmax, the non-log form: y[r, c] = exp(x[r, c] - LSE_c x[r, :]).
  * Same layout, split and workspace (log_softmax_rows_workspace_bytes) as
  * log_softmax_rows.                          [LSM] the standard-softmax variant */

@@ -29,6 +29,7 @@ from ._lib import LseError  # noqa: F401
 
 __all__ = [
     "lse_reduce_axis0", "lse_reduce_axis", "log_softmax_axis", "softmax_rows", "log_softmax_rows",
+    "log_softmax_rows_noalloc",
     "log_softmax_rows_workspace_bytes",
     "log_softmax_rows_plan", "lse_testing_set_spin_limit", "lse_rows_num_chunks", "lse_rows_partial",
     "lse_rows_merge", "fused_conv_gn_act_lse", "fused_conv_gn_act_lse_workspace_bytes",
@@ -227,6 +228,23 @@ def _rows_call(fn, name, x, y, ws, stream):
         _lib.check(getattr(lib, fn)(_dev(x, "x", False), _dev(y, "y", False), rows, cols, ldx,
                                     ldy, None if ws is None else ctypes.c_void_p(ws.data_ptr()),
                                     ws_bytes, _stream(stream)), name)
+    return y
+
+
+def log_softmax_rows_noalloc(x, y, stream=None):
+    """log_softmax_rows with the library's static device scratch instead of a
+    workspace: x and y are contiguous 2-D fp32 tensors on one GPU (y given:
+    the call allocates nothing)."""
+    lib = _lib.load()
+    if x.dim() != 2 or y.shape != x.shape:
+        raise ValueError("x must be 2-D (rows, cols) and y the same shape")
+    if not (x.is_contiguous() and y.is_contiguous()):
+        raise ValueError("log_softmax_rows_noalloc takes contiguous x and y")
+    rows, cols = x.shape
+    with _on(x, y):
+        _lib.check(lib.log_softmax_rows_noalloc(_dev(x, "x", False), _dev(y, "y", False), rows,
+                                                cols, _stream(stream)),
+                   "log_softmax_rows_noalloc")
     return y
 
 

@@ -28,6 +28,7 @@ SIGNATURES = {
     "log_softmax_rows_workspace_bytes": (_sz, [_i64, _i64]),
     "softmax_rows": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
     "log_softmax_rows": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "log_softmax_rows_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "lse_testing_set_spin_limit": (None, [ctypes.c_uint32]),
     "log_softmax_rows_plan": (ctypes.c_int, [_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "lse_rows_num_chunks": (_i64, [_i64, _i64]),

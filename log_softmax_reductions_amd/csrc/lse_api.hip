@@ -260,6 +260,27 @@ LSE_EXPORT lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows,
                    stream);
 }
 
+LSE_EXPORT lse_status_t log_softmax_rows_noalloc(const float *x, float *y, int64_t rows,
+                                                 int64_t cols, hipStream_t stream) {
+  const char *who = "log_softmax_rows_noalloc";
+  int64_t total;
+  lse_status_t st = check_rows(who, rows, cols, &total);
+  if (st != LSE_OK) return st;
+  const size_t need = lse::rows_workspace_bytes(rows, cols);
+  if (need > lse::kNoAllocScratchBytes)
+    return fail(LSE_ERR_WORKSPACE,
+                "%s: rows x chunks = %lld x %lld needs %zu bytes of scratch; the static scratch "
+                "holds %zu (131040 row-chunk pairs); use log_softmax_rows with a workspace",
+                who, (long long)rows, (long long)lse::rows_plan(cols).nchunks, need,
+                lse::kNoAllocScratchBytes);
+  void *ws = nullptr;
+  if (need > 0 && rows > 0) {
+    const hipError_t e = lse::noalloc_scratch(&ws);
+    if (e != hipSuccess) return from_hip(e, "log_softmax_rows_noalloc: scratch address");
+  }
+  return rows_call(who, false, x, y, rows, cols, cols, cols, ws, need, stream);
+}
+
 LSE_EXPORT lse_status_t softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
                                      void *ws, size_t ws_bytes, hipStream_t stream) {
   return rows_call("softmax_rows", true, x, y, rows, cols, cols, cols, ws, ws_bytes, stream);

@@ -79,6 +79,12 @@ hipError_t launch_log_softmax_rows_no_ws(const float *x, float *y, int64_t rows,
 void set_spin_limit(uint32_t polls);
 uint32_t chain_spin_limit();
 
+// Static device scratch of log_softmax_rows_noalloc: a 256-byte header plus
+// (1 MiB - 256) / 8 = 131040 packed pairs.  noalloc_scratch() returns its
+// address on the current device (resolved once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 // ---------------------------------------------------------------- case C
 size_t conv_chain_workspace_bytes(int64_t N, int64_t Cin, int64_t H, int64_t W,
                                   int64_t Cout, int64_t K, int64_t groups);

@@ -39,7 +39,7 @@ def test_exports_match_header(lib):
     import subprocess
     from log_softmax_reductions_amd import _lib
     declared = declared_functions()
-    assert len(declared) == 20
+    assert len(declared) == 21
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -155,6 +155,16 @@ def test_partial_chunks_per_row_limit(lib):
     shape error, found before anything is launched."""
     assert lib.lse_rows_partial(FAKE, 1, 9_000_000, 1, FAKE2, None) == LSE_ERR_SHAPE
     assert b"exceed one launch" in lib.lse_last_error()
+
+
+def test_noalloc_validation(lib):
+    """The static-scratch call refuses, before any launch, more row-chunk pairs
+    than its scratch holds, and the usual shape errors."""
+    assert lib.log_softmax_rows_noalloc(FAKE, FAKE2, 10921, 393216, None) == LSE_ERR_WORKSPACE
+    assert b"131040" in lib.lse_last_error()
+    assert lib.log_softmax_rows_noalloc(FAKE, FAKE2, 4, 0, None) == LSE_ERR_SHAPE
+    assert lib.log_softmax_rows_noalloc(None, FAKE2, 4, 8, None) == LSE_ERR_NULL
+    assert lib.log_softmax_rows_noalloc(FAKE, FAKE, 4, 8, None) == LSE_ERR_OVERLAP
 
 
 def test_chain_validation(lib):
