@@ -20,7 +20,8 @@ rank 0 prints ONE JSON line.
 
 Flags: --gpus N (only 1 is supported: this build runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --no-secondary,
---only {rows_large,axis0_large,axis0_walk,conv_chain,softmax_large,axis_chain_layout,copy}
+--only {rows_large,axis0_large,axis0_walk,conv_chain,softmax_large,axis_chain_layout,copy,
+        copy_tile,copy_stream,rows_odd_cols,rows_offset_view}
 to run just that kernel
 (for profiler runs; prints timing only).
 """
@@ -44,6 +45,8 @@ FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, published
 METRIC = "GB/s and % of HBM roofline for log_softmax 4096x393216 fp32 on 1 MI355X"
 ROWS, COLS = 4096, 393216
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "log_softmax_rows_4096x393216_traffic.md")
+PROFILE_STATS = os.path.join(ROOT, "profiles", "log_softmax_rows_4096x393216_kernel_stats.md")
+BENCH_COPY_LIB = os.path.join(ROOT, "libbench_copy.so")
 KERNEL_SOURCES = ["log_softmax_reductions_amd/csrc/lse_rows.hip",
                   "log_softmax_reductions_amd/csrc/lse_device.hpp",
                   "log_softmax_reductions_amd/csrc/lse_internal.hpp"]
@@ -75,6 +78,17 @@ def traffic_from_profile():
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))
+
+
+def profiled_kernel():
+    """(name, avg ns) of the dominant kernel in the committed rocprofv3 summary
+    of the workload (its first table row), or (None, None)."""
+    try:
+        text = open(PROFILE_STATS).read()
+    except OSError:
+        return None, None
+    m = re.search(r"^\| `(?:void )?([^`]+)` \| \d+ \| (\d+) \|", text, flags=re.M)
+    return (m.group(1), int(m.group(2))) if m else (None, None)
 
 
 def timed_launches(fn, steps, warmup):
@@ -187,11 +201,29 @@ def bench_rows_large(steps, warmup):
 
 
 def copy_ceiling(x, y, steps=5, warmup=2):
-    """GB/s of a plain device-to-device copy of the same bytes (read x, write
-    y): a second, achievable denominator beside the 8 TB/s peak."""
-    wall, ev = timed_launches(lambda: y.copy_(x), steps, warmup)
-    avg = sum(ev) / len(ev)
-    return round(2 * x.numel() * 4 / (avg * 1e-3) / 1e9, 1)
+    """GB/s of device copies of the same bytes (read x, write y): an achievable
+    denominator beside the 8 TB/s peak.  Our own HIP copies (bench_copy.hip:
+    "tile" = the log_softmax kernel's access pattern without the arithmetic,
+    "stream" = grid-stride non-temporal, "plain" = one float4 per work-item)
+    and torch's copy_ (the runtime's blit kernel); the ceiling is the fastest
+    of ours."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(BENCH_COPY_LIB)
+    lib.bench_copy.restype = ctypes.c_int
+    lib.bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                               ctypes.c_void_p]
+    n = x.numel()
+    out = {}
+    for v, name in enumerate(("tile", "stream", "plain")):
+        def run(v=v):
+            st = torch.cuda.current_stream().cuda_stream
+            assert lib.bench_copy(x.data_ptr(), y.data_ptr(), n, v, st) == 0
+        _, ev = timed_launches(run, steps, warmup)
+        out[name] = round(2 * n * 4 / (sum(ev) / len(ev) * 1e-3) / 1e9, 1)
+    _, ev = timed_launches(lambda: y.copy_(x), steps, warmup)
+    out["torch_copy_"] = round(2 * n * 4 / (sum(ev) / len(ev) * 1e-3) / 1e9, 1)
+    return max(out["tile"], out["stream"], out["plain"]), out
 
 
 def bench_secondary(steps=10, warmup=3):
@@ -234,9 +266,11 @@ def bench_secondary(steps=10, warmup=3):
     out["conv_chain"] = {"workload": "conv3x3 8->64, GN16, tanh, hardswish, +res, LSE dim=1, "
                                      "x (128,8,128,128)",
                          "ms": round(avg, 4), "conv_TFLOP/s": round(flop / avg / 1e9, 2),
-                         "mfma_frac_of_fp32_peak": round(flop / avg / 1e9 / FP32_MFMA_PEAK_TFLOPS,
-                                                         4),
+                         "direct_conv_equiv_frac_of_fp32_mfma_peak":
+                             round(flop / avg / 1e9 / FP32_MFMA_PEAK_TFLOPS, 4),
                          "executed_mfma_TFLOP/s": round(mfma_flop / avg / 1e9, 2),
+                         "executed_mfma_frac_of_fp32_peak":
+                             round(mfma_flop / avg / 1e9 / FP32_MFMA_PEAK_TFLOPS, 4),
                          "note": "one fused kernel: conv_TFLOP/s counts the direct conv's "
                                  "18.73 GFLOP; the kernel computes it as Winograd F(2x2,3x3) "
                                  "on fp32 MFMA (8.46 GFLOP executed); each sample's GroupNorm "
@@ -271,6 +305,32 @@ def bench_secondary(steps=10, warmup=3):
         "ms": round(avg, 4), "GB/s": round(nb / avg / 1e6, 1),
         "hbm_frac": round(nb / avg / 1e6 / HBM_PEAK_GBS, 4)}
     del x, o, y
+    # rows that the 16-byte path does not cover as a whole: an odd row length
+    # (every row starts at a different alignment) and the workload viewed one
+    # float past a 16-byte boundary (x misaligned, y aligned)
+    for key, cols, off in (("rows_odd_cols", COLS - 1, 0), ("rows_offset_view", COLS, 1)):
+        buf = inputs.normal((ROWS * cols + off,), seed=41, device="cuda")
+        x = buf[off:].view(ROWS, cols)
+        y = torch.empty((ROWS, cols), device="cuda")
+        ws = torch.empty(L.log_softmax_rows_workspace_bytes(ROWS, cols), dtype=torch.uint8,
+                         device="cuda")
+        wall, ev = timed_launches(lambda: L.log_softmax_rows(x, y, ws), steps, warmup)
+        avg = sum(ev) / len(ev)
+        nb = 8 * x.numel()
+        out[key] = {"workload": f"log_softmax dim=1 ({ROWS},{cols}) fp32 N(0,1), x at byte "
+                                f"offset {4 * off} from a 256-byte boundary",
+                    "ms": round(avg, 4), "GB/s": round(nb / avg / 1e6, 1),
+                    "hbm_frac": round(nb / avg / 1e6 / HBM_PEAK_GBS, 4)}
+        del buf, x, y, ws
+    # the allocation-free entry point on the workload (static device scratch)
+    x = inputs.make("rows_large", "cuda")
+    y = torch.empty_like(x)
+    wall, ev = timed_launches(lambda: L.log_softmax_rows_noalloc(x, y), steps, warmup)
+    avg = sum(ev) / len(ev)
+    out["rows_large_noalloc"] = {"workload": "log_softmax_rows_noalloc (4096,393216) fp32 N(0,1)",
+                                 "ms": round(avg, 4), "GB/s": round(8 * x.numel() / avg / 1e6, 1),
+                                 "hbm_frac": round(8 * x.numel() / avg / 1e6 / HBM_PEAK_GBS, 4)}
+    del x, y
     # small cases: hot latency per call, eagerly from Python (host launch
     # included) and as back-to-back calls replayed from a HIP graph
     x = inputs.make("rows_small", "cuda")
@@ -349,6 +409,24 @@ def run_only(which, steps, warmup):
         a = torch.empty(1 << 28, device="cuda")
         c = torch.empty_like(a)
         wall, ev = timed_launches(lambda: c.copy_(a), steps, warmup)
+    elif which in ("copy_tile", "copy_stream"):
+        # our copy kernels on the workload's bytes (the copy ceiling)
+        import ctypes
+        lib = ctypes.CDLL(BENCH_COPY_LIB)
+        lib.bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_void_p]
+        a = inputs.make("rows_large", "cuda")
+        c = torch.empty_like(a)
+        v = 0 if which == "copy_tile" else 1
+        wall, ev = timed_launches(
+            lambda: lib.bench_copy(a.data_ptr(), c.data_ptr(), a.numel(), v,
+                                   torch.cuda.current_stream().cuda_stream), steps, warmup)
+    elif which in ("rows_odd_cols", "rows_offset_view"):
+        cols, off = (COLS - 1, 0) if which == "rows_odd_cols" else (COLS, 1)
+        buf = inputs.normal((ROWS * cols + off,), seed=41, device="cuda")
+        x = buf[off:].view(ROWS, cols)
+        y = torch.empty((ROWS, cols), device="cuda")
+        wall, ev = timed_launches(lambda: L.log_softmax_rows(x, y), steps, warmup)
     else:
         raise SystemExit(f"unknown --only {which}")
     print(json.dumps({"only": which, "steps": steps, "wall_ms": round(wall, 4),
@@ -384,6 +462,7 @@ def main():
     value = alg_bytes / (wall_ms * 1e-3) / 1e9
     ev_avg = sum(ev) / len(ev)
     achieved = alg_bytes / (ev_avg * 1e-3) / 1e9
+    kname, kns = profiled_kernel()
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -403,12 +482,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(),
-                     "kernel": "log_softmax_rows_kernel<64, true, true, false>",
+                     "kernel": kname, "kernel_avg_ns_rocprof": kns,
                      "event_ms_avg": round(ev_avg, 4), "event_ms_min": round(min(ev), 4),
                      "event_ms_median": round(statistics.median(ev), 4)},
     }
-    copy_gbs = copy_ceiling(x, y)
+    copy_gbs, copies = copy_ceiling(x, y)
     line["roofline"]["copy_ceiling_GBs"] = copy_gbs
+    line["roofline"]["copies_GBs"] = copies
     line["roofline"]["frac_of_copy"] = round(achieved / copy_gbs, 4)
     if not args.no_secondary:
         line["secondary"] = bench_secondary()

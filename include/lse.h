@@ -18,8 +18,12 @@
  *     never allocates, frees or synchronises; every call only enqueues kernels
  *     on `stream` (0 = the null stream) and returns.
  *   - All tensors are fp32, dense and row-major (C order).  Sizes are int64.
- *     Any pointer alignment is accepted; 16-byte aligned pointers with the
- *     innermost size a multiple of 4 take the 128-bit load path.
+ *     Pointers of the row calls (log_softmax_rows, softmax_rows,
+ *     lse_rows_partial and their forms) must be 4-byte aligned, the natural
+ *     alignment of float (LSE_ERR_SHAPE otherwise); the other calls accept
+ *     any alignment.  Rows go through 128-bit loads and stores from their
+ *     first 16-byte boundary on, with a few single-value loads and stores
+ *     for the head and tail of a row that does not start or end on one.
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     failure nothing is launched, a status != LSE_OK is returned and
  *     lse_last_error() describes it (thread-local string, valid until the next

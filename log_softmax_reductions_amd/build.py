@@ -40,6 +40,21 @@ def _compile(src: str) -> str:
     return obj
 
 
+BENCH_COPY_SRC = os.path.join(ROOT, "bench_copy.hip")
+BENCH_COPY_LIB = os.path.join(ROOT, "libbench_copy.so")
+
+
+def build_bench_copy() -> str:
+    """The benchmark's copy kernels (bench_copy.hip, not part of liblse.so)."""
+    tmp = BENCH_COPY_LIB + ".tmp"
+    cmd = [HIPCC, *CFLAGS, "-shared", BENCH_COPY_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on bench_copy.hip:\n{r.stderr}")
+    os.replace(tmp, BENCH_COPY_LIB)
+    return BENCH_COPY_LIB
+
+
 def build() -> str:
     """Compile every source and link liblse.so in-tree; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)

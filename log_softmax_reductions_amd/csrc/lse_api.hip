@@ -234,6 +234,8 @@ static lse_status_t rows_call(const char *who, bool softmax, const float *x, flo
   if (!span_ok(rows, ldx, 1, 0, cols, &xspan) || !span_ok(rows, ldy, 1, 0, cols, &yspan))
     return fail(LSE_ERR_SHAPE, "%s: rows * ld overflows", who);
   if (!x || !y) return fail(LSE_ERR_NULL, "%s: x and y must be non-NULL", who);
+  if (((uintptr_t)x | (uintptr_t)y) & 3u)
+    return fail(LSE_ERR_SHAPE, "%s: x and y must be 4-byte aligned (float)", who);
   if (overlaps(x, xspan * 4, y, yspan * 4))
     return fail(LSE_ERR_OVERLAP, "%s: y overlaps x (in-place is not supported)", who);
   const lse::RowsPlan p = lse::rows_plan(cols);
@@ -314,6 +316,8 @@ LSE_EXPORT lse_status_t lse_rows_partial(const float *x, int64_t rows, int64_t c
     return fail(LSE_ERR_SHAPE, "lse_rows_partial: chunk = %lld must be >= 1", (long long)chunk);
   if (rows == 0) return ok();
   if (!x || !partials) return fail(LSE_ERR_NULL, "lse_rows_partial: NULL pointer");
+  if (((uintptr_t)x | (uintptr_t)partials) & 3u)
+    return fail(LSE_ERR_SHAPE, "lse_rows_partial: x and partials must be 4-byte aligned");
   const int64_t k = (cols + chunk - 1) / chunk;
   int64_t wgs;
   if (!mul_ok(rows, k, &wgs) || wgs > kMaxGrid)

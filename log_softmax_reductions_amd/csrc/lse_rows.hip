@@ -35,6 +35,7 @@
 //     count must fit 32 bits); longer grids are split into launches over
 //     consecutive rows.
 #include <atomic>
+#include <type_traits>
 
 #include "lse_device.hpp"
 #include "lse_internal.hpp"
@@ -77,16 +78,24 @@ __device__ __forceinline__ int64_t vec4_index(int q, int t) {
 #endif
 }
 
+// Four floats loaded or stored as one 16-byte access at an address that is
+// only known to be 4-byte aligned (gfx950 accepts dword-aligned 16-byte
+// accesses).
+typedef float v4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 // Load a chunk of `len` values starting at p into v (lane-strided so that each
 // wave's load is one contiguous span), padding with -inf.  A full chunk (the
-// common case) takes an unchecked path.
-template <int VPL, bool VEC>
+// common case) takes an unchecked path.  p needs 4-byte alignment only (a
+// row whose output is line-aligned and input is not loads 16 bytes at x's own
+// phase); len is a multiple of 4.
+template <int VPL, bool VEC, bool A16 = true>
 __device__ __forceinline__ void load_chunk(const float *__restrict__ p, int64_t len,
                                            float (&v)[VPL]) {
+  typedef float v4a16 __attribute__((ext_vector_type(4)));
+  typedef std::conditional_t<A16, v4a16, v4a4> v4;  // A16: p is 16-byte aligned
   const int t = threadIdx.x;
   if constexpr (VEC) {
     if (len == (int64_t)VPL * kRowsThreads) {
-      typedef float v4 __attribute__((ext_vector_type(4)));
       const v4 *p4 = reinterpret_cast<const v4 *>(p);
 #pragma unroll
       for (int q = 0; q < VPL / 4; ++q) {
@@ -103,7 +112,7 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ p, int64_t 
     for (int q = 0; q < VPL / 4; ++q) {
       const int64_t idx = vec4_index<VPL>(q, t) * 4;
       if (idx < len) {
-        const float4 f = *reinterpret_cast<const float4 *>(p + idx);
+        const v4 f = *reinterpret_cast<const v4 *>(p + idx);
         v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
       } else {
 #pragma unroll
@@ -111,11 +120,7 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ p, int64_t 
       }
     }
   } else {
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) {
-      const int64_t idx = (int64_t)e * kRowsThreads + t;
-      v[e] = (idx < len) ? p[idx] : -__builtin_inff();
-    }
+    static_assert(VEC, "chunks are loaded as aligned tiles (SpanSplit covers the rest)");
   }
 }
 
@@ -180,11 +185,7 @@ __device__ __forceinline__ void store_chunk(float *__restrict__ p, int64_t len,
                out_value<SOFTMAX>(v[4 * q + 2], M, k), out_value<SOFTMAX>(v[4 * q + 3], M, k));
     }
   } else {
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) {
-      const int64_t idx = (int64_t)e * kRowsThreads + t;
-      if (idx < len) p[idx] = out_value<SOFTMAX>(v[e], M, k);
-    }
+    static_assert(VEC, "chunks are stored as aligned tiles (store_chunk_b32 otherwise)");
   }
 }
 
@@ -197,24 +198,63 @@ __device__ __forceinline__ float out_scale(float S) {
     return logf(S);
 }
 
+// A span of values [p, p + len) whose start is 4-byte but not necessarily
+// line aligned (an odd row length, a pitch that is not a multiple of 32
+// floats, a base off a 128-byte boundary): h <= 31 values before the first
+// 128-byte boundary of the frame pointer f (the output row, or the input
+// when there is none), then a body of a multiple of 4 values, then tail <= 3
+// values.  The body goes through the register tile with line-aligned 16-byte
+// accesses on the frame's side; the head and tail values (at most 34) ride
+// in one extra register of lanes 0 .. 33 of wave 0.
+struct SpanSplit {
+  int h, tail;
+  int64_t body;
+  __device__ __forceinline__ SpanSplit(const float *f, int64_t len) {
+    h = (int)((32u - (uint32_t)(((uintptr_t)f >> 2) & 31u)) & 31u);
+    if ((int64_t)h > len) h = (int)len;
+    body = (len - h) & ~(int64_t)3;
+    tail = (int)(len - h - body);
+  }
+};
+
+// This lane's extra value of a span p (-inf and col = -1 if it holds none):
+// lanes 0 .. h-1 take the head when `head`, the next lanes the tail when
+// `tail` (wave 0 only: at most 34 values).
+__device__ __forceinline__ float extra_value(const float *__restrict__ p, const SpanSplit &sp,
+                                             bool head, bool tail, int64_t &col) {
+  const int l = threadIdx.x;
+  const int nh = head ? sp.h : 0, nt = tail ? sp.tail : 0;
+  col = -1;
+  if (l < nh)
+    col = l;
+  else if (l - nh < nt)
+    col = sp.h + sp.body + (l - nh);
+  return col >= 0 ? p[col] : -__builtin_inff();
+}
+
 // The chunk's pair (exact max, sum of exp(v - max)); identical in every lane.
 // One running max and one running sum per lane, over e = 0 .. VPL-1 in order
 // (a wave issues dependent VALU operations back to back, so more accumulators
-// would buy no latency hiding), then the workgroup reductions.
-template <int VPL>
+// would buy no latency hiding), then the lane's extra value when EXTRA (the
+// head / tail of a span that is not 16-byte aligned, -inf in lanes without
+// one), then the workgroup reductions.
+template <int VPL, bool EXTRA = false>
 __device__ __forceinline__ void chunk_pair(const float (&v)[VPL], float *red, float &m,
-                                           float &s) {
+                                           float &s, float xe = 0.0f) {
   float lm = v[0];
 #pragma unroll
   for (int e = 1; e < VPL; ++e) lm = fmaxf(lm, v[e]);
+  if constexpr (EXTRA) lm = fmaxf(lm, xe);
   m = block_allreduce<kNW>(lm, OpMax{}, red);
   float ls = 0.0f;
   if (is_finite(m)) {  // uniform branch: m is the same in every lane
 #pragma unroll
     for (int e = 0; e < VPL; ++e) ls += exp_base2(v[e] - m);
+    if constexpr (EXTRA) ls += exp_base2(xe - m);
   } else {
 #pragma unroll
     for (int e = 0; e < VPL; ++e) ls += pair_term_nonfinite(v[e], m);
+    if constexpr (EXTRA) ls += pair_term_nonfinite(xe, m);
   }
   s = block_allreduce<kNW>(ls, OpSum{}, red);
 }
@@ -222,12 +262,13 @@ __device__ __forceinline__ void chunk_pair(const float (&v)[VPL], float *red, fl
 // chunk_pair of a chunk that is not in this workgroup's registers (a
 // sibling's, computed by the helping path): the same values reach the same
 // lanes and meet the same operations in the same order (the running max and
-// the running sum over e = 0 .. VPL-1, the same workgroup reductions), so the
-// pair is bit-identical to the one the chunk's owner computes.  The chunk is
-// streamed twice (max, then sum) instead of held.
-template <int VPL, bool VEC>
+// the running sum over e = 0 .. VPL-1, then the lane's extra value when
+// EXTRA, the same workgroup reductions), so the pair is bit-identical to the
+// one the chunk's owner computes.  The tile is streamed twice (max, then sum)
+// instead of held.  VEC: p is 4-byte aligned and len a multiple of 4.
+template <int VPL, bool VEC, bool EXTRA>
 __device__ __forceinline__ void chunk_pair_streamed(const float *__restrict__ p, int64_t len,
-                                                    float *red, float &m, float &s) {
+                                                    float xe, float *red, float &m, float &s) {
   const int t = threadIdx.x;
   // Value e = 4 q + r of lane t: VEC, element r of float4 vec4_index<VPL>(q, t)
   // (one pointer stepped by kStep4 float4 per q); otherwise element
@@ -237,16 +278,19 @@ __device__ __forceinline__ void chunk_pair_streamed(const float *__restrict__ p,
 #else
   constexpr int64_t kStep4 = kRowsThreads;
 #endif
-  const float4 *p4;
+  // !EXTRA: a chunk of an aligned row (16-byte aligned p); EXTRA: x's own phase.
+  typedef float v4a16 __attribute__((ext_vector_type(4)));
+  typedef std::conditional_t<EXTRA, v4a4, v4a16> v4;
+  const v4 *p4;
   int64_t idx;
   auto start = [&]() {
-    p4 = reinterpret_cast<const float4 *>(p) + vec4_index<VPL>(0, t);
+    p4 = reinterpret_cast<const v4 *>(p) + vec4_index<VPL>(0, t);
     idx = VEC ? vec4_index<VPL>(0, t) * 4 : (int64_t)t;
   };
   auto values = [&](float (&f)[4]) {
     if constexpr (VEC) {
       if (idx < len) {
-        const float4 g = *p4;
+        const v4 g = *p4;
         f[0] = g.x; f[1] = g.y; f[2] = g.z; f[3] = g.w;
       } else {
 #pragma unroll
@@ -276,6 +320,7 @@ __device__ __forceinline__ void chunk_pair_streamed(const float *__restrict__ p,
 #pragma unroll
     for (int r = 0; r < 4; ++r) lm = fmaxf(lm, f[r]);
   }
+  if constexpr (EXTRA) lm = fmaxf(lm, xe);
   m = block_allreduce<kNW>(lm, OpMax{}, red);
   start();
   float ls = 0.0f;
@@ -287,6 +332,7 @@ __device__ __forceinline__ void chunk_pair_streamed(const float *__restrict__ p,
 #pragma unroll
     for (int r = 0; r < 4; ++r) ls += fin ? exp_base2(f[r] - m) : pair_term_nonfinite(f[r], m);
   }
+  if constexpr (EXTRA) ls += fin ? exp_base2(xe - m) : pair_term_nonfinite(xe, m);
   s = block_allreduce<kNW>(ls, OpSum{}, red);
 }
 
@@ -384,15 +430,33 @@ __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
     row = blockIdx.x;
     c = 0;
   }
-  const int64_t c0 = c * chunk;
-  const int64_t len = (cols - c0 < chunk) ? (cols - c0) : chunk;
-  const float *xr = x + row * ldx + c0;
-  float *yr = y + row * ldy + c0;
+  const float *xrow = x + row * ldx;
+  float *yrow = y + row * ldy;
+  // VEC: every row of x and y 16-byte aligned with cols % 4 == 0; chunk c
+  // covers columns [c chunk, ...).  Otherwise the chunks tile the row's body,
+  // which starts sp.h columns in, where y's row reaches a 128-byte boundary
+  // (so every store is a whole-line 16-byte store; the loads take x's own
+  // phase), and the row's head and tail values ride as extra values with
+  // chunk 0 and the last chunk.
+  int64_t c0 = c * chunk, len;
+  SpanSplit sp(yrow, cols);
+  if constexpr (VEC) {
+    len = (cols - c0 < chunk) ? (cols - c0) : chunk;
+  } else {
+    len = sp.body - c0;
+    len = len < 0 ? 0 : (len < chunk ? len : chunk);
+    c0 += sp.h;
+  }
+  const float *xr = xrow + c0;
+  float *yr = yrow + c0;
 
   float v[VPL];
-  load_chunk<VPL, VEC>(xr, len, v);
+  load_chunk<VPL, true, VEC>(xr, len, v);
+  float xe = 0.0f;
+  int64_t xcol = -1;
+  if constexpr (!VEC) xe = extra_value(xrow, sp, c == 0, c == nchunks - 1, xcol);
   float m, s;
-  chunk_pair<VPL>(v, red, m, s);
+  chunk_pair<VPL, !VEC>(v, red, m, s, xe);
 
   float M, lnS;
   if constexpr (SPLIT) {
@@ -413,10 +477,19 @@ __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
         if (threadIdx.x == 0) s_state = (load_pair_agent(row_pairs + j) == 0) ? 2 : 0;
         __syncthreads();
         if (s_state == 2) {
-          const int64_t j0 = j * chunk;
-          const int64_t lj = (cols - j0 < chunk) ? (cols - j0) : chunk;
+          int64_t j0 = j * chunk, lj;
+          float hxe = 0.0f;
+          if constexpr (VEC) {
+            lj = (cols - j0 < chunk) ? (cols - j0) : chunk;
+          } else {
+            lj = sp.body - j0;
+            lj = lj < 0 ? 0 : (lj < chunk ? lj : chunk);
+            j0 += sp.h;
+            int64_t hcol;
+            hxe = extra_value(xrow, sp, j == 0, j == nchunks - 1, hcol);
+          }
           float hm, hs;
-          chunk_pair_streamed<VPL, VEC>(x + row * ldx + j0, lj, red, hm, hs);
+          chunk_pair_streamed<VPL, true, !VEC>(xrow + j0, lj, hxe, red, hm, hs);
           if (threadIdx.x == 0 && publish_pair_once(row_pairs + j, pack_pair(hm, hs)))
             __hip_atomic_fetch_add(&hdr->helped, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -438,7 +511,9 @@ __global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_kernel(
     M = m;
     lnS = out_scale<SOFTMAX>(s);
   }
-  store_chunk<VPL, VEC, SOFTMAX>(yr, len, v, M, lnS);
+  store_chunk<VPL, true, SOFTMAX>(yr, len, v, M, lnS);
+  if constexpr (!VEC)
+    if (xcol >= 0) yrow[xcol] = out_value<SOFTMAX>(xe, M, lnS);
 }
 
 // Clear n 64-bit words (the workspace header and pair slots); grid-stride, so
@@ -464,10 +539,19 @@ __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_kernel(
   const int64_t row = t / nchunks, c = t - row * nchunks;
   const int64_t c0 = c * chunk;
   const int64_t len = (cols - c0 < chunk) ? (cols - c0) : chunk;
+  const float *xc = x + row * ldx + c0;
   float v[VPL];
-  load_chunk<VPL, VEC>(x + row * ldx + c0, len, v);
   float m, s;
-  chunk_pair<VPL>(v, red, m, s);
+  if constexpr (VEC) {
+    load_chunk<VPL, true>(xc, len, v);
+    chunk_pair<VPL>(v, red, m, s);
+  } else {  // the chunk's aligned body in the tile, its head and tail as extras
+    const SpanSplit sp(xc, len);
+    load_chunk<VPL, true>(xc + sp.h, sp.body, v);
+    int64_t col;
+    const float xe = extra_value(xc, sp, true, true, col);
+    chunk_pair<VPL, true>(v, red, m, s, xe);
+  }
   if (threadIdx.x == 0) partials[t] = make_float2(m, s);
 }
 
@@ -610,10 +694,19 @@ __global__ __launch_bounds__(kRowsThreads) void rows_lse_kernel(const float *__r
                                                                 int64_t ldo) {
   __shared__ float red[kNW];
   const int64_t row = blockIdx.x;
+  const float *xrow = x + row * ldx;
   float v[VPL];
-  load_chunk<VPL, VEC>(x + row * ldx, cols, v);
   float m, s;
-  chunk_pair<VPL>(v, red, m, s);
+  if constexpr (VEC) {
+    load_chunk<VPL, true>(xrow, cols, v);
+    chunk_pair<VPL>(v, red, m, s);
+  } else {  // the row's aligned body in the tile, its head and tail as extras
+    const SpanSplit sp(xrow, cols);
+    load_chunk<VPL, true>(xrow + sp.h, sp.body, v);
+    int64_t col;
+    const float xe = extra_value(xrow, sp, true, true, col);
+    chunk_pair<VPL, true>(v, red, m, s, xe);
+  }
   if (threadIdx.x == 0) out[row * ldo] = pair_lse(m, s);
 }
 

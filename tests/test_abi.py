@@ -157,6 +157,17 @@ def test_partial_chunks_per_row_limit(lib):
     assert b"exceed one launch" in lib.lse_last_error()
 
 
+def test_rows_pointer_alignment(lib):
+    """Row calls take float pointers on 4-byte boundaries (any 16-byte offset
+    is fine); anything else is a shape error before any launch."""
+    odd = ctypes.c_void_p(0x100000 + 2)
+    assert lib.log_softmax_rows(odd, FAKE2, 4, 8, None, 0, None) == LSE_ERR_SHAPE
+    assert b"4-byte aligned" in lib.lse_last_error()
+    assert lib.softmax_rows(FAKE, ctypes.c_void_p(0x900000000 + 1), 4, 8, None, 0,
+                            None) == LSE_ERR_SHAPE
+    assert lib.lse_rows_partial(odd, 4, 8, 4, FAKE2, None) == LSE_ERR_SHAPE
+
+
 def test_noalloc_validation(lib):
     """The static-scratch call refuses, before any launch, more row-chunk pairs
     than its scratch holds, and the usual shape errors."""

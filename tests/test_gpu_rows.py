@@ -268,3 +268,79 @@ def test_softmax_rows_small_workload_and_special(orc):
     s[3, :30000] = -float("inf")
     compare(L.softmax_rows(s.to(DEV)).cpu().numpy(), orc.softmax_rows(s.numpy()),
             atol=SOFTMAX_ATOL, rtol=SOFTMAX_RTOL, what="softmax special")
+
+
+@pytest.mark.parametrize("rows,cols,xoff,yoff,softmax", [
+    (40, 393215, 0, 0, False),     # odd row length: every row starts elsewhere
+    (24, 393216, 1, 0, False),     # x one float past a 16-byte boundary, y aligned
+    (24, 393216, 3, 3, True),      # both off by the same amount: 16-byte stores
+    (16, 100002, 2, 1, False),     # x and y off by different amounts
+    (64, 32767, 0, 0, True),       # one workgroup per row (no split), odd length
+    (33, 5, 1, 2, False),          # rows shorter than a 16-byte vector
+    (7, 3, 0, 0, False)])
+def test_rows_head_tail(orc, rows, cols, xoff, yoff, softmax):
+    """Rows that do not sit on 16-byte boundaries: the aligned body goes
+    through the 128-bit register tile, the head and tail values beside it.
+    Every element against the oracle, and the helping path bit-identical."""
+    xb = inputs.normal((rows * cols + xoff,), seed=cols + 7 * xoff, device=DEV)
+    x = xb[xoff:].view(rows, cols)
+    yb = torch.full((rows * cols + yoff,), float("nan"), device=DEV)
+    y = yb[yoff:].view(rows, cols)
+    fn = L.softmax_rows if softmax else L.log_softmax_rows
+    ws = torch.empty(max(1, L.log_softmax_rows_workspace_bytes(rows, cols)), dtype=torch.uint8,
+                     device=DEV)
+    fn(x, y, ws=ws)
+    torch.cuda.synchronize()
+    xc = x.cpu().numpy()
+    if softmax:
+        compare(y.cpu().numpy(), orc.softmax_rows(xc), atol=1e-37, rtol=1e-5, what="head/tail sm")
+    else:
+        compare(y.cpu().numpy(), orc.log_softmax_rows(xc)[0], what="head/tail")
+    assert torch.isnan(yb[:yoff]).all()
+    nchunks, _ = L.log_softmax_rows_plan(cols)
+    if nchunks > 1:
+        # y2 at y's offset: the same kernel and chunk partition as the first call
+        y2 = torch.empty((rows * cols + yoff,), device=DEV)[yoff:].view(rows, cols)
+        try:
+            L.lse_testing_set_spin_limit(0)
+            fn(x, y2, ws=ws)
+            torch.cuda.synchronize()
+        finally:
+            L.lse_testing_set_spin_limit(1 << 24)
+        assert int(ws[4:8].view(torch.int32).item()) == rows * nchunks
+        diff = (y != y2).nonzero()
+        assert diff.numel() == 0, (f"{diff.shape[0]} differ; first {diff[:6].tolist()}; "
+                                   f"y {y[diff[:6, 0], diff[:6, 1]].tolist()} "
+                                   f"y2 {y2[diff[:6, 0], diff[:6, 1]].tolist()}")
+
+
+@pytest.mark.parametrize("cols,chunk,off", [(5003, 1001, 1), (4096, 1000, 2), (70001, 16383, 3)])
+def test_partials_head_tail(orc, cols, chunk, off):
+    """Chunks whose starts and lengths are not multiples of 4 floats."""
+    xb = inputs.normal((6 * cols + off,), seed=chunk, device=DEV)
+    x = xb[off:].view(6, cols)
+    p = L.lse_rows_partial(x, chunk)
+    lse = L.lse_rows_merge(p)
+    torch.cuda.synchronize()
+    m_ref, s_ref = orc.lse_chunk_partials(x.cpu().numpy(), chunk)
+    pc = p.cpu().numpy()
+    assert np.array_equal(pc[..., 0], m_ref.astype(np.float32))
+    compare(pc[..., 1], s_ref, atol=0.0, rtol=1e-5, what="partial sums")
+    compare(lse.cpu().numpy(), orc.log_softmax_rows(x.cpu().numpy())[1], what="merge")
+
+
+def test_rows_head_tail_full_size(orc):
+    """(4096, 393215) and the (4096, 393216) workload one float off a 16-byte
+    boundary: sampled rows against the oracle, every row by property."""
+    for cols, off in ((393215, 0), (393216, 1)):
+        print(f"case: head/tail full size cols={cols} off={off}", flush=True)
+        xb = inputs.normal((4096 * cols + off,), seed=41, device=DEV)
+        x = xb[off:].view(4096, cols)
+        y = L.log_softmax_rows(x)
+        torch.cuda.synchronize()
+        sample = [0, 1, 2, 3, 2047, 4095]
+        compare(y[sample].cpu().numpy(), orc.log_softmax_rows(x[sample].cpu().numpy())[0],
+                what=f"full size {cols} {off}")
+        for r0 in range(0, 4096, 512):
+            assert torch.logsumexp(y[r0:r0 + 512].double(), dim=1).abs().max().item() < 1e-5
+        del xb, x, y
