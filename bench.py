@@ -204,15 +204,19 @@ def copy_ceiling(x, y, steps=5, warmup=2):
     """GB/s of device copies of the same bytes (read x, write y): an achievable
     denominator beside the 8 TB/s peak.  Our own HIP copies (bench_copy.hip:
     "tile" = the log_softmax kernel's access pattern without the arithmetic,
-    "stream" = grid-stride non-temporal, "plain" = one float4 per work-item)
-    and torch's copy_ (the runtime's blit kernel); the ceiling is the fastest
-    of ours."""
+    "tile_2_per_cu" / "tile_1_per_cu" = the same capped at 2 / 1 workgroups
+    per CU by unused LDS (fewer requests in flight), "stream" = grid-stride
+    non-temporal, "plain" = one float4 per work-item) and torch's copy_ (the
+    runtime's blit kernel); the ceiling is the fastest of ours."""
     import ctypes
     import torch
     lib = ctypes.CDLL(BENCH_COPY_LIB)
     lib.bench_copy.restype = ctypes.c_int
     lib.bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                ctypes.c_void_p]
+    lib.bench_copy_capped.restype = ctypes.c_int
+    lib.bench_copy_capped.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_int, ctypes.c_void_p]
     n = x.numel()
     out = {}
     for v, name in enumerate(("tile", "stream", "plain")):
@@ -221,9 +225,15 @@ def copy_ceiling(x, y, steps=5, warmup=2):
             assert lib.bench_copy(x.data_ptr(), y.data_ptr(), n, v, st) == 0
         _, ev = timed_launches(run, steps, warmup)
         out[name] = round(2 * n * 4 / (sum(ev) / len(ev) * 1e-3) / 1e9, 1)
+    for lds, name in ((54 * 1024, "tile_2_per_cu"), (81 * 1024, "tile_1_per_cu")):
+        def run_capped(lds=lds):
+            st = torch.cuda.current_stream().cuda_stream
+            assert lib.bench_copy_capped(x.data_ptr(), y.data_ptr(), n, lds, st) == 0
+        _, ev = timed_launches(run_capped, steps, warmup)
+        out[name] = round(2 * n * 4 / (sum(ev) / len(ev) * 1e-3) / 1e9, 1)
     _, ev = timed_launches(lambda: y.copy_(x), steps, warmup)
     out["torch_copy_"] = round(2 * n * 4 / (sum(ev) / len(ev) * 1e-3) / 1e9, 1)
-    return max(out["tile"], out["stream"], out["plain"]), out
+    return max(v for k, v in out.items() if k != "torch_copy_"), out
 
 
 def bench_secondary(steps=10, warmup=3):

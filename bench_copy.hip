@@ -13,6 +13,8 @@
 //                       flight per lane, non-temporal 128-bit stores;
 //   variant 2 "plain":  one 128-bit load and store per work-item, default
 //                       cache policy.
+// bench_copy_capped runs "tile" with unused dynamic LDS per workgroup, which
+// caps how many workgroups a CU holds (fewer requests in flight).
 // n must be a multiple of 4 and both pointers 16-byte aligned; variant 0
 // also needs n to be a multiple of 32768 (bench_copy returns -1 otherwise).
 #include <hip/hip_runtime.h>
@@ -64,6 +66,19 @@ __global__ __launch_bounds__(256) void copy_plain(const v4f *__restrict__ x, v4f
 }
 
 }  // namespace
+
+// "tile" with `lds_bytes` of dynamic LDS per workgroup (unused), which caps
+// the workgroups resident per CU (160 KiB of LDS per CU).
+extern "C" __attribute__((visibility("default"))) int bench_copy_capped(const float *x, float *y,
+                                                                         int64_t n, int lds_bytes,
+                                                                         hipStream_t stream) {
+  if (n % kTileFloats != 0 || n / kTileFloats > 0x7fffffff || lds_bytes < 0 ||
+      lds_bytes > 160 * 1024 || ((uintptr_t)x | (uintptr_t)y) % 16 != 0)
+    return -1;
+  hipLaunchKernelGGL(copy_tile, dim3((uint32_t)(n / kTileFloats)), dim3(kTileThreads),
+                     (unsigned)lds_bytes, stream, reinterpret_cast<const v4f *>(x), y);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
 
 extern "C" __attribute__((visibility("default"))) int bench_copy(const float *x, float *y,
                                                                   int64_t n, int variant,
