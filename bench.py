@@ -21,7 +21,8 @@ rank 0 prints ONE JSON line.
 Flags: --gpus N (only 1 is supported: this build runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --no-secondary,
 --only {rows_large,axis0_large,axis0_walk,conv_chain,softmax_large,axis_chain_layout,copy,
-        copy_tile,copy_stream,rows_odd_cols,rows_offset_view}
+        copy_tile,copy_stream,rows_odd_cols,rows_offset_view,chain_600x520_recompute,
+        chain_600x520_staged}
 to run just that kernel
 (for profiler runs; prints timing only).
 """
@@ -273,6 +274,25 @@ def bench_secondary(steps=10, warmup=3):
     # Winograd F(2x2, 3x3): 16 positions x 64 x 8 multiply-adds per 2x2 block;
     # 63 tile rows x 64 blocks per sample (the last block column is padding).
     mfma_flop = 2 * 16 * 64 * 8 * 63 * 64 * 128
+    # the same chain on samples too large for the fused launch (8 x 600 x 520:
+    # 748 tile pairs per sample): statistics launch + apply launch, the apply
+    # recomputing the conv (the default) or reading it back from a staging
+    # area sized for the Infinity Cache
+    xl, wl, bl, gl, bel = inputs.conv_chain_inputs(N=8, H=600, W=520, seed=5, device="cuda")
+    ol = torch.empty((8, 1, 598, 518), device="cuda")
+    two = {}
+    for path, name in ((2, "recompute"), (3, "staged")):
+        L.lse_testing_set_chain_path(path)
+        wsl = torch.empty(L.fused_conv_gn_act_lse_workspace_bytes(8, 8, 600, 520, 64, 3, 16),
+                          dtype=torch.uint8, device="cuda")
+        _, evl = timed_launches(
+            lambda: L.fused_conv_gn_act_lse(xl, wl, bl, gl, bel, 16, 1e-5, ol, wsl), steps, warmup)
+        L.lse_testing_set_chain_path(0)
+        two[name + "_ms"] = round(sum(evl) / len(evl), 4)
+        del wsl
+    out["conv_chain_8x600x520_two_launch"] = {
+        "workload": "the chain on x (8,8,600,520): statistics + apply launches", **two}
+    del xl, wl, bl, gl, bel, ol
     out["conv_chain"] = {"workload": "conv3x3 8->64, GN16, tanh, hardswish, +res, LSE dim=1, "
                                      "x (128,8,128,128)",
                          "ms": round(avg, 4), "conv_TFLOP/s": round(flop / avg / 1e9, 2),
@@ -402,6 +422,16 @@ def run_only(which, steps, warmup):
         o = torch.empty((128, 1, 126, 126), device="cuda")
         wall, ev = timed_launches(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, o),
                                   steps, warmup)
+    elif which in ("chain_600x520_recompute", "chain_600x520_staged"):
+        # the two-launch chain on samples too large for one fused launch
+        x, w, b, g, be = inputs.conv_chain_inputs(N=8, H=600, W=520, seed=5, device="cuda")
+        o = torch.empty((8, 1, 598, 518), device="cuda")
+        L.lse_testing_set_chain_path(2 if which.endswith("recompute") else 3)
+        ws = torch.empty(L.fused_conv_gn_act_lse_workspace_bytes(8, 8, 600, 520, 64, 3, 16),
+                         dtype=torch.uint8, device="cuda")
+        wall, ev = timed_launches(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, o, ws),
+                                  steps, warmup)
+        L.lse_testing_set_chain_path(0)
     elif which == "softmax_large":
         x = inputs.make("rows_large", "cuda")
         y = torch.empty_like(x)

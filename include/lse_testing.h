@@ -28,12 +28,30 @@
 
 #include <stdint.h>
 
+#include "lse.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
 
 /* Poll limit of the waits described above for the calling thread. */
 void lse_testing_set_spin_limit(uint32_t polls);
+
+/* Which launches fused_conv_gn_act_lse uses for calls from the calling
+ * thread (and which size fused_conv_gn_act_lse_workspace_bytes returns):
+ *   0  automatic (the default): one fused launch while a sample's tile pairs
+ *      number at most half of what the device holds at once, else the
+ *      statistics launch followed by an apply launch that recomputes the conv;
+ *   1  one fused launch for any size;
+ *   2  statistics launch + recomputing apply launch;
+ *   3  statistics launch that also stores each tile pair's conv output (128
+ *      KiB per pair) in the workspace + apply launch that reads it back, in
+ *      batches of samples of at most 192 MiB of staged output (samples too
+ *      large for that take 2).
+ * All give the same results.  Returns LSE_OK, or LSE_ERR_SHAPE for another
+ * value (the setting is then unchanged).  Query the workspace size after
+ * setting the path. */
+lse_status_t lse_testing_set_chain_path(int path);
 
 #ifdef __cplusplus
 }

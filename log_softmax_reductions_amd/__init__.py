@@ -31,7 +31,8 @@ __all__ = [
     "lse_reduce_axis0", "lse_reduce_axis", "log_softmax_axis", "softmax_rows", "log_softmax_rows",
     "log_softmax_rows_noalloc",
     "log_softmax_rows_workspace_bytes",
-    "log_softmax_rows_plan", "lse_testing_set_spin_limit", "lse_rows_num_chunks", "lse_rows_partial",
+    "log_softmax_rows_plan", "lse_testing_set_spin_limit", "lse_testing_set_chain_path",
+    "lse_rows_num_chunks", "lse_rows_partial",
     "lse_rows_merge", "fused_conv_gn_act_lse", "fused_conv_gn_act_lse_workspace_bytes",
     "lse_abi_version", "LseError",
 ]
@@ -270,6 +271,13 @@ def lse_testing_set_spin_limit(polls: int) -> None:
     """Test hook (include/lse_testing.h): the poll limit of the split rows' and
     the conv chain's cross-workgroup waits, for calls this thread enqueues."""
     _lib.load().lse_testing_set_spin_limit(int(polls))
+
+
+def lse_testing_set_chain_path(path: int) -> None:
+    """Test hook (include/lse_testing.h): 0 automatic, 1 fused, 2 statistics +
+    recomputing apply, 3 statistics + staged apply, for calls this thread
+    enqueues (and for the workspace size it queries)."""
+    _lib.check(_lib.load().lse_testing_set_chain_path(int(path)), "lse_testing_set_chain_path")
 
 
 def log_softmax_rows(x, y=None, ws=None, stream=None):

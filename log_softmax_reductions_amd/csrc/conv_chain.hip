@@ -116,6 +116,8 @@ struct ChainArgs {
   float eps;
   uint32_t spin_limit;
   uint32_t block_base;   // kStats / kApply: workgroup index of this launch's first pair
+  uint32_t stage_first;  // ticket of the first pair whose conv tiles sit in `stage`
+  float *stage;          // kStats with staging, kApplyStaged: conv tiles of this batch
   float *out;
   float *mean;           // (N, G), written by tile 0 of each sample
   float *rstd;           // (N, G)
@@ -749,12 +751,25 @@ __device__ __forceinline__ void publish_pair_stats(const ChainArgs &a, int64_t n
 //   kFused: pairs handed out by ticket in sample order; publish, wait for the
 //           sample, merge, epilogue (one launch; used while a sample's pairs
 //           fit on the GPU at once, see launch_conv_chain).
-//   kStats: publish only.  kApply: the statistics are complete (published by
+//   kStats: publish only (and, when a.stage is set, store the pair's conv
+//           tiles there).  kApply: the statistics are complete (published by
 //           a kStats launch): merge, epilogue.  kStats + kApply compute the
 //           conv twice but never wait on another workgroup.
+//   kApplyStaged: as kApply, but the conv tiles are read back from a.stage
+//           (written by the kStats launch just before) instead of recomputed.
 // In every mode a workgroup whose wait runs out computes the missing tile
 // statistics of its sample itself (see the file comment).
-enum ChainMode { kFused = 0, kStats = 1, kApply = 2 };
+enum ChainMode { kFused = 0, kStats = 1, kApply = 2, kApplyStaged = 3 };
+
+// Staged conv tiles of one pair: 8 waves x 16 accumulator vectors x 64 lanes
+// of float4 = 128 KiB, in register order, so that each wave's store or load
+// of one accumulator vector is one contiguous 1 KiB.
+constexpr int64_t kStageF4PerPair = (int64_t)kTeams * (kThreads / kWave) * kNB * kMT * kWave;
+__device__ __forceinline__ f32x4 *stage_slot(const ChainArgs &a, uint32_t ticket) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  return reinterpret_cast<f32x4 *>(a.stage) + (int64_t)(ticket - a.stage_first) * kStageF4PerPair +
+         (int64_t)wave * (kNB * kMT * kWave) + lane;
+}
 
 // Stage the pair of tiles of sample n with index pr (team 0: tile 2 pr, team
 // 1: tile 2 pr + 1) and convolve it into acc; the caller must have passed a
@@ -833,7 +848,7 @@ void conv_chain_pair_kernel(ChainArgs a) {
   __shared__ uint32_t s_ticket, s_last;
   // W's loads are in flight while the ticket is claimed.
   std::conditional_t<kWino, WinoW, WRegs<kTeams * kThreads>> wr;
-  load_w(a.w, wr);
+  if constexpr (MODE != kApplyStaged) load_w(a.w, wr);
   // kStats, kApply: no workgroup waits on another's turn, any order will do.
   uint32_t ticket = a.block_base + blockIdx.x;
   if constexpr (MODE == kFused) {
@@ -855,26 +870,46 @@ void conv_chain_pair_kernel(ChainArgs a) {
   const bool active = team == 0 || hasB;                                   // uniform per wave
   const int tile = team ? tB : tA;
 
-  XRegs xr;
-  if (active) {
-    const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
-    load_x(a, n, th * kTileH, tw * kTileW, xr, tid);
-  }
-  store_w(wr, wl);  // W rows, or U (Winograd)
-  if (active) store_x(xr, xs[team], tid);
-  __syncthreads();
-
   f32x4 acc[kNB][kMT];
   bool valid[kNB];
-  if (active) {
-    if constexpr (kWino)
-      conv_tile_wino(a, xs[team], wl, twave, acc);
-    else
-      conv_tile(a, xs[team], wl, twave / 2, (twave % 2) * 64, acc);
-    tile_valid(a, tile, valid, twave);
+  if constexpr (MODE == kApplyStaged) {
+    if (active) {  // the conv tiles from the staging area
+      const f32x4 *src = stage_slot(a, ticket);
+#pragma unroll
+      for (int blk = 0; blk < kNB; ++blk)
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) acc[blk][t] = src[(blk * kMT + t) * kWave];
+      tile_valid(a, tile, valid, twave);
+    }
+  } else {
+    XRegs xr;
+    if (active) {
+      const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
+      load_x(a, n, th * kTileH, tw * kTileW, xr, tid);
+    }
+    store_w(wr, wl);  // W rows, or U (Winograd)
+    if (active) store_x(xr, xs[team], tid);
+    __syncthreads();
+    if (active) {
+      if constexpr (kWino)
+        conv_tile_wino(a, xs[team], wl, twave, acc);
+      else
+        conv_tile(a, xs[team], wl, twave / 2, (twave % 2) * 64, acc);
+      tile_valid(a, tile, valid, twave);
+    }
   }
-  if constexpr (MODE != kApply) publish_pair_stats(a, n, tA, tB, hasB, active, acc, valid, L);
-  if constexpr (MODE == kStats) return;
+  if constexpr (MODE == kFused || MODE == kStats)
+    publish_pair_stats(a, n, tA, tB, hasB, active, acc, valid, L);
+  if constexpr (MODE == kStats) {
+    if (a.stage && active) {  // uniform per wave
+      f32x4 *dst = stage_slot(a, ticket);
+#pragma unroll
+      for (int blk = 0; blk < kNB; ++blk)
+#pragma unroll
+        for (int t = 0; t < kMT; ++t) dst[(blk * kMT + t) * kWave] = acc[blk][t];
+    }
+    return;
+  }
   // This thread's channel of gamma / beta (threads < 64), loaded only now so
   // that they are not held through the conv.
   float ga = 1.0f, be = 0.0f;
@@ -890,8 +925,17 @@ void conv_chain_pair_kernel(ChainArgs a) {
     arrived_before = __hip_atomic_fetch_add(a.arrivals + n, 1ull, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
   uint64_t wd[kHeldPer];
-  // A poll limit of 0 (test hook) tries to defer without waiting.
-  bool ok = a.spin_limit != 0 && wait_stats<kTeams * kThreads>(a, n, L, wd);  // uniform
+  // A poll limit of 0 (test hook) tries to defer without waiting.  The staged
+  // apply never defers: its statistics were complete before it started (and
+  // it holds no conv weights to redo a deferred pair with).
+  bool ok;
+  if constexpr (MODE == kApplyStaged) {
+    while (!wait_stats<kTeams * kThreads>(a, n, L, wd)) {
+    }
+    ok = true;
+  } else {
+    ok = a.spin_limit != 0 && wait_stats<kTeams * kThreads>(a, n, L, wd);  // uniform
+  }
   if (!ok) {
     if (threadIdx.x == 0) {
       const uint64_t st = __hip_atomic_fetch_add(a.arrivals + n, 1ull << 32, __ATOMIC_RELAXED,
@@ -928,24 +972,63 @@ __global__ __launch_bounds__(256) void chain_clear_kernel(uint64_t *__restrict__
 }  // namespace
 
 namespace {
+// Which launches compute the chain: one fused launch, or a statistics launch
+// then an apply launch that recomputes the conv, or one that reads the conv
+// tiles back from a staging area in the workspace (sized for the 256 MB
+// Infinity Cache).
+enum ChainPath { kPathAuto = 0, kPathFused = 1, kPathRecompute = 2, kPathStaged = 3 };
+thread_local int h_chain_path = kPathAuto;  // test hook: force a path on this thread
+
+constexpr size_t kStageBytesPerPair = (size_t)kStageF4PerPair * 16;  // 128 KiB
+constexpr size_t kStageCapBytes = (size_t)192 << 20;  // staged samples per batch fit this
+#ifndef LSE_CHAIN_STAGED_DEFAULT
+#define LSE_CHAIN_STAGED_DEFAULT 0   // two-launch path: 1 stages, 0 recomputes the conv
+#endif
+
+}  // namespace
+int64_t fused_pair_limit();
+namespace {
+
 struct ChainLayout {
-  int64_t tiles_w, tiles;
-  size_t head, stats_off, arrivals_off, queue_off, total;
+  int64_t tiles_w, tiles, per_sample;
+  int path;                // kPathFused, kPathRecompute or kPathStaged
+  int64_t stage_samples;   // samples per staged batch
+  size_t head, stats_off, arrivals_off, queue_off, stage_off, total;
 };
 ChainLayout chain_layout(int64_t N, int64_t H, int64_t W, int64_t K, int64_t groups) {
   ChainLayout L;
   const int64_t Ho = H - K + 1, Wo = W - K + 1;
   L.tiles_w = (Wo + kTileW - 1) / kTileW;
   L.tiles = ((Ho + kTileH - 1) / kTileH) * L.tiles_w;
+  L.per_sample = (L.tiles + kTeams - 1) / kTeams;  // tile pairs = workgroups per sample
+  const bool stage_fits = (size_t)L.per_sample * kStageBytesPerPair <= kStageCapBytes;
+  const int forced = h_chain_path;
+  if (forced == kPathFused || forced == kPathRecompute)
+    L.path = forced;
+  else if (forced == kPathStaged)
+    L.path = stage_fits ? kPathStaged : kPathRecompute;
+  else if (L.per_sample <= fused_pair_limit())
+    L.path = kPathFused;
+  else
+    L.path = (LSE_CHAIN_STAGED_DEFAULT && stage_fits) ? kPathStaged : kPathRecompute;
+  L.stage_samples = 0;
+  if (L.path == kPathStaged) {
+    L.stage_samples = (int64_t)(kStageCapBytes / ((size_t)L.per_sample * kStageBytesPerPair));
+    if (L.stage_samples > N) L.stage_samples = N;
+  }
   L.head = ((size_t)(2 * N * groups) * sizeof(float) + 255) / 256 * 256;  // mean, rstd
   L.stats_off = L.head + sizeof(ChainWsHeader);
   L.arrivals_off = L.stats_off + (size_t)(N * L.tiles * groups) * sizeof(uint64_t);
   L.queue_off = L.arrivals_off + (size_t)N * sizeof(uint64_t);
   // one queue slot per tile pair
-  L.total = L.queue_off + ((size_t)(N * ((L.tiles + kTeams - 1) / kTeams)) * 4 + 7) / 8 * 8;
+  L.stage_off = L.queue_off + ((size_t)(N * L.per_sample) * 4 + 255) / 256 * 256;
+  L.total = L.stage_off + (size_t)L.stage_samples * L.per_sample * kStageBytesPerPair;
+  if (L.path != kPathStaged) L.total = L.queue_off + ((size_t)(N * L.per_sample) * 4 + 7) / 8 * 8;
   return L;
 }
 }  // namespace
+
+void set_chain_path(int path) { h_chain_path = path; }
 
 // The fused launch needs every pair of a sample resident at once (a waiting
 // workgroup holds its slot).  It is used while a sample has at most half as
@@ -1001,29 +1084,37 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
   a.arrivals = reinterpret_cast<uint64_t *>(base + L.arrivals_off);
   a.queue = reinterpret_cast<uint32_t *>(base + L.queue_off);
   a.block_base = 0;
-  // The header, the statistics words and the queue start at 0.
-  const int64_t words = (int64_t)((L.total - L.head) / sizeof(uint64_t));
+  // The header, the statistics words and the queue start at 0 (the staging
+  // area is written before it is read).
+  const size_t clear_end = L.path == kPathStaged ? L.stage_off : L.total;
+  const int64_t words = (int64_t)((clear_end - L.head) / sizeof(uint64_t));
   const int64_t clear_blocks = std::min<int64_t>((words + 255) / 256, 4096);
   hipLaunchKernelGGL(chain_clear_kernel, dim3((uint32_t)clear_blocks), dim3(256), 0, stream,
                      reinterpret_cast<uint64_t *>(base + L.head), words);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t per_sample = (L.tiles + kTeams - 1) / kTeams;  // workgroups per sample
-  const bool fused = per_sample <= fused_pair_limit();
-  // Samples per launch: a dispatch's work-item count must fit 32 bits.  The
-  // fused launches need no offset: each claims the next tickets in order.
-  const int64_t max_n = std::max<int64_t>(1, (0xffffffffll / (kTeams * kThreads)) / per_sample);
+  const int64_t per_sample = L.per_sample;
+  // Samples per launch: a dispatch's work-item count must fit 32 bits (and a
+  // staged batch must fit the staging area).  The fused launches need no
+  // offset: each claims the next tickets in order.
+  int64_t max_n = std::max<int64_t>(1, (0xffffffffll / (kTeams * kThreads)) / per_sample);
+  if (L.path == kPathStaged) max_n = std::min(max_n, L.stage_samples);
+  a.stage = L.path == kPathStaged ? reinterpret_cast<float *>(base + L.stage_off) : nullptr;
   const dim3 block(kTeams * kThreads);
   for (int64_t n0 = 0; n0 < N; n0 += max_n) {
     const int64_t nb = std::min(max_n, N - n0);
     const dim3 grid((uint32_t)(nb * per_sample));
     a.block_base = (uint32_t)(n0 * per_sample);
-    if (fused) {
+    a.stage_first = a.block_base;
+    if (L.path == kPathFused) {
       hipLaunchKernelGGL(conv_chain_pair_kernel<kFused>, grid, block, 0, stream, a);
     } else {
       hipLaunchKernelGGL(conv_chain_pair_kernel<kStats>, grid, block, 0, stream, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      hipLaunchKernelGGL(conv_chain_pair_kernel<kApply>, grid, block, 0, stream, a);
+      if (L.path == kPathStaged)
+        hipLaunchKernelGGL(conv_chain_pair_kernel<kApplyStaged>, grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL(conv_chain_pair_kernel<kApply>, grid, block, 0, stream, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

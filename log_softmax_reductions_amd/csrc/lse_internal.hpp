@@ -86,6 +86,9 @@ constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
 hipError_t noalloc_scratch(void **ptr);
 
 // ---------------------------------------------------------------- case C
+// Test hook: 0 automatic, 1 fused, 2 statistics + recomputing apply,
+// 3 statistics + staged apply (per host thread).
+void set_chain_path(int path);
 size_t conv_chain_workspace_bytes(int64_t N, int64_t Cin, int64_t H, int64_t W,
                                   int64_t Cout, int64_t K, int64_t groups);
 hipError_t launch_conv_chain(const float *x, const float *w, const float *b,

@@ -186,3 +186,44 @@ def test_chain_deferred_pairs(orc, N, H, W, groups):
     assert _deferred_word(ws2, N, groups) == 0
     assert torch.equal(out, out2)
     assert torch.equal(stats, ws2[: 2 * NG * 4].view(torch.float32))
+
+
+@pytest.mark.parametrize("N,H,W,groups", [(3, 128, 128, 16), (2, 37, 300, 4), (1, 600, 520, 1),
+                                          (2, 5, 7, 2)])
+def test_chain_paths_agree(orc, N, H, W, groups):
+    """The fused launch, the statistics + recomputing apply launches and the
+    statistics + staged apply launches (forced through the test hook) against
+    the oracle, and bit-identical to each other."""
+    x, w, b, g, be = _chain_inputs(N, H, W, seed=3 * N + H + 5 * W, affine=True)
+    outs = {}
+    try:
+        for path in (1, 2, 3):
+            L.lse_testing_set_chain_path(path)
+            nbytes = L.fused_conv_gn_act_lse_workspace_bytes(N, 8, H, W, 64, 3, groups)
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+            outs[path] = L.fused_conv_gn_act_lse(x, w, b, g, be, groups, 1e-5, ws=ws)
+            torch.cuda.synchronize()
+    finally:
+        L.lse_testing_set_chain_path(0)
+    cpu = lambda t: None if t is None else t.cpu().numpy()
+    ref, _, _ = orc.fused_chain(cpu(x), cpu(w), cpu(b), cpu(g), cpu(be), groups, 1e-5)
+    compare(outs[3].cpu().numpy(), ref, rtol=RTOL_CHAIN, what="staged")
+    assert torch.equal(outs[1], outs[2])
+    assert torch.equal(outs[1], outs[3])
+
+
+def test_chain_staged_workspace_size():
+    """The staged path's workspace holds one 128 KiB staging slot per tile pair
+    of a batch of samples (at most 192 MiB), beyond the other paths' bytes."""
+    try:
+        L.lse_testing_set_chain_path(2)
+        base = L.fused_conv_gn_act_lse_workspace_bytes(8, 8, 600, 520, 64, 3, 1)
+        L.lse_testing_set_chain_path(3)
+        staged = L.fused_conv_gn_act_lse_workspace_bytes(8, 8, 600, 520, 64, 3, 1)
+    finally:
+        L.lse_testing_set_chain_path(0)
+    pairs = (299 * 5 + 1) // 2                      # 748 tile pairs per 600 x 520 sample
+    per_batch = (192 << 20) // (pairs * 131072)     # 2 samples of 93.5 MiB
+    assert per_batch == 2
+    assert base < staged <= base + 256 + per_batch * pairs * 131072
+    assert staged >= base + per_batch * pairs * 131072
