@@ -22,7 +22,7 @@ Flags: --gpus N (only 1 is supported: this build runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --no-secondary,
 --only {rows_large,axis0_large,axis0_walk,conv_chain,softmax_large,axis_chain_layout,copy,
         copy_tile,copy_stream,rows_odd_cols,rows_offset_view,chain_600x520_recompute,
-        chain_600x520_staged}
+        chain_600x520_staged,rows_large_reread}
 to run just that kernel
 (for profiler runs; prints timing only).
 """
@@ -352,6 +352,21 @@ def bench_secondary(steps=10, warmup=3):
                     "ms": round(avg, 4), "GB/s": round(nb / avg / 1e6, 1),
                     "hbm_frac": round(nb / avg / 1e6 / HBM_PEAK_GBS, 4)}
         del buf, x, y, ws
+    # the split rows re-reading each chunk for the write (through the caches)
+    # instead of keeping it in registers: the comparison design
+    x = inputs.make("rows_large", "cuda")
+    y = torch.empty_like(x)
+    ws = torch.empty(L.log_softmax_rows_workspace_bytes(ROWS, COLS), dtype=torch.uint8,
+                     device="cuda")
+    L.lse_testing_set_rows_reread(True)
+    wall, ev = timed_launches(lambda: L.log_softmax_rows(x, y, ws), steps, warmup)
+    L.lse_testing_set_rows_reread(False)
+    avg = sum(ev) / len(ev)
+    out["rows_large_reread"] = {
+        "workload": "log_softmax (4096,393216) fp32, chunks re-read for the write (comparison)",
+        "ms": round(avg, 4), "GB/s": round(8 * x.numel() / avg / 1e6, 1),
+        "hbm_frac": round(8 * x.numel() / avg / 1e6 / HBM_PEAK_GBS, 4)}
+    del x, y, ws
     # the allocation-free entry point on the workload (static device scratch)
     x = inputs.make("rows_large", "cuda")
     y = torch.empty_like(x)
@@ -432,6 +447,10 @@ def run_only(which, steps, warmup):
         wall, ev = timed_launches(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, o, ws),
                                   steps, warmup)
         L.lse_testing_set_chain_path(0)
+    elif which == "rows_large_reread":
+        L.lse_testing_set_rows_reread(True)
+        _, _, wall, ev = bench_rows_large(steps, warmup)
+        L.lse_testing_set_rows_reread(False)
     elif which == "softmax_large":
         x = inputs.make("rows_large", "cuda")
         y = torch.empty_like(x)

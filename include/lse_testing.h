@@ -37,6 +37,16 @@ extern "C" {
 /* Poll limit of the waits described above for the calling thread. */
 void lse_testing_set_spin_limit(uint32_t polls);
 
+/* enable != 0: split rows of log_softmax_rows / softmax_rows whose rows are
+ * 16-byte aligned (cols a multiple of 4) take the re-read kernel instead of
+ * the register-resident one, for calls from the calling thread: each
+ * workgroup folds its chunk with the online (max, sum) recurrence in few
+ * registers, and after the pairs are merged reads the chunk again (from the
+ * caches when it is still there) to write y.  Same results within the usual
+ * tolerance (another summation order); the same workspace.  A comparison
+ * variant: the default keeps each chunk in registers. */
+void lse_testing_set_rows_reread(int enable);
+
 /* Which launches fused_conv_gn_act_lse uses for calls from the calling
  * thread (and which size fused_conv_gn_act_lse_workspace_bytes returns):
  *   0  automatic (the default): one fused launch while a sample's tile pairs

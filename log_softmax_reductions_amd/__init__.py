@@ -32,7 +32,7 @@ __all__ = [
     "log_softmax_rows_noalloc",
     "log_softmax_rows_workspace_bytes",
     "log_softmax_rows_plan", "lse_testing_set_spin_limit", "lse_testing_set_chain_path",
-    "lse_rows_num_chunks", "lse_rows_partial",
+    "lse_testing_set_rows_reread", "lse_rows_num_chunks", "lse_rows_partial",
     "lse_rows_merge", "fused_conv_gn_act_lse", "fused_conv_gn_act_lse_workspace_bytes",
     "lse_abi_version", "LseError",
 ]
@@ -278,6 +278,12 @@ def lse_testing_set_chain_path(path: int) -> None:
     recomputing apply, 3 statistics + staged apply, for calls this thread
     enqueues (and for the workspace size it queries)."""
     _lib.check(_lib.load().lse_testing_set_chain_path(int(path)), "lse_testing_set_chain_path")
+
+
+def lse_testing_set_rows_reread(enable: bool) -> None:
+    """Test hook (include/lse_testing.h): split rows through the re-read kernel
+    (chunks read again for the write) instead of the register-resident one."""
+    _lib.load().lse_testing_set_rows_reread(1 if enable else 0)
 
 
 def log_softmax_rows(x, y=None, ws=None, stream=None):

@@ -31,6 +31,7 @@ SIGNATURES = {
     "log_softmax_rows_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp]),
     "lse_testing_set_spin_limit": (None, [ctypes.c_uint32]),
     "lse_testing_set_chain_path": (ctypes.c_int, [ctypes.c_int]),
+    "lse_testing_set_rows_reread": (None, [ctypes.c_int]),
     "log_softmax_rows_plan": (ctypes.c_int, [_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "lse_rows_num_chunks": (_i64, [_i64, _i64]),
     "lse_rows_partial": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _vp]),

@@ -94,6 +94,8 @@ LSE_EXPORT int lse_abi_version(void) { return LSE_ABI_VERSION; }
 
 LSE_EXPORT void lse_testing_set_spin_limit(uint32_t polls) { lse::set_spin_limit(polls); }
 
+LSE_EXPORT void lse_testing_set_rows_reread(int enable) { lse::set_rows_reread(enable != 0); }
+
 LSE_EXPORT lse_status_t lse_testing_set_chain_path(int path) {
   if (path < 0 || path > 3) return fail(LSE_ERR_SHAPE, "lse_testing_set_chain_path: 0..3");
   lse::set_chain_path(path);

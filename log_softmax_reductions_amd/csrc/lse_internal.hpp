@@ -77,6 +77,7 @@ hipError_t launch_log_softmax_rows_no_ws(const float *x, float *y, int64_t rows,
                                          int64_t ldx, int64_t ldy, hipStream_t stream,
                                          bool softmax = false);
 void set_spin_limit(uint32_t polls);
+void set_rows_reread(bool on);
 uint32_t chain_spin_limit();
 
 // Static device scratch of log_softmax_rows_noalloc: a 256-byte header plus

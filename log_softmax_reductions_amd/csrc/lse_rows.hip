@@ -57,6 +57,8 @@ constexpr uint32_t kDefaultSpinLimit = 1u << 24;
 // Poll limit of the split rows' and the conv chain's waits, per host thread
 // (a test hook: 0 forces every pair through the helping path).
 thread_local uint32_t h_spin_limit = kDefaultSpinLimit;
+// Test hook: split rows through the MALL re-read kernel (aligned rows only).
+thread_local bool h_rows_reread = false;
 // Workgroups of kRowsThreads lanes per launch: the dispatch's work-item count
 // (workgroups x lanes) must fit 32 bits.
 constexpr int64_t kMaxRowsWorkgroups = 0xffffffffll / kRowsThreads;
@@ -677,6 +679,109 @@ __device__ __forceinline__ void online_row_pair(const float *__restrict__ p, int
   S = block_allreduce<kNW>(op.s * w, OpSum{}, red);
 }
 
+// ------------------------------------------------- MALL re-read variant
+// The split log_softmax in the form that re-reads x for the write instead of
+// keeping the chunk in registers (selected through the test hook, for the
+// comparison with the register-resident kernel): pass 1 folds the chunk with
+// the online (max, sum) recurrence, four 16-byte loads in flight per lane
+// and cached (so that the re-read can hit the L2 or the Infinity Cache),
+// using few registers, so that more workgroups fit; the pairs meet as in the
+// register-resident kernel; pass 2 reads the chunk again and writes y.
+// Aligned rows only (16-byte x and y rows, cols and the chunk multiples of 4).
+__device__ __forceinline__ void cached_chunk_pair(const float *__restrict__ p, int64_t len,
+                                                  float *red, float &M, float &S) {
+  OnlinePair op;
+  const v4f *p4 = reinterpret_cast<const v4f *>(p);
+  const int64_t n4 = len / 4;
+  int64_t i = threadIdx.x;
+  constexpr int U = 4;  // loads in flight per lane
+  for (; i + (U - 1) * kRowsThreads < n4; i += U * kRowsThreads) {
+    v4f f[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) f[u] = p4[i + u * kRowsThreads];
+#pragma unroll
+    for (int u = 0; u < U; ++u) op.add4(f[u].x, f[u].y, f[u].z, f[u].w);
+  }
+  for (; i < n4; i += kRowsThreads) {
+    const v4f f = p4[i];
+    op.add4(f.x, f.y, f.z, f.w);
+  }
+  M = block_allreduce<kNW>(op.m, OpMax{}, red);
+  const float w = (op.m == M) ? 1.0f : exp_base2(op.m - M);
+  S = block_allreduce<kNW>(op.s * w, OpSum{}, red);
+}
+
+template <bool SOFTMAX>
+__global__ __launch_bounds__(kRowsThreads) void log_softmax_rows_reread_kernel(
+    const float *__restrict__ x, float *__restrict__ y, int64_t cols, int64_t ldx, int64_t ldy,
+    int64_t nchunks, int64_t chunk, RowsWsHeader *__restrict__ hdr,
+    uint64_t *__restrict__ pairs, uint32_t spin_limit) {
+  __shared__ float red[kNW];
+  __shared__ int s_state;
+  __shared__ float s_final[2];
+  const int64_t t = blockIdx.x;
+  const int64_t row = t / nchunks, c = t - row * nchunks;
+  const int64_t c0 = c * chunk;
+  const int64_t len = (cols - c0 < chunk) ? (cols - c0) : chunk;
+  const float *xr = x + row * ldx + c0;
+  float *yr = y + row * ldy + c0;
+  float m, s;
+  cached_chunk_pair(xr, len, red, m, s);
+  uint64_t *row_pairs = pairs + row * nchunks;
+  if (threadIdx.x == 0 && spin_limit != 0) publish_pair_once(row_pairs + c, pack_pair(m, s));
+  for (;;) {
+    if (threadIdx.x < kWave) {
+      const bool all = wave_wait_pairs(row_pairs, nchunks, spin_limit);
+      if (threadIdx.x == 0) s_state = all ? 1 : 0;
+    }
+    __syncthreads();
+    if (s_state == 1) break;
+    for (int64_t j = 0; j < nchunks; ++j) {  // help: missing sibling pairs from x
+      __syncthreads();
+      if (threadIdx.x == 0) s_state = (load_pair_agent(row_pairs + j) == 0) ? 2 : 0;
+      __syncthreads();
+      if (s_state == 2) {
+        const int64_t j0 = j * chunk;
+        float hm, hs;
+        cached_chunk_pair(x + row * ldx + j0, (cols - j0 < chunk) ? (cols - j0) : chunk, red, hm,
+                          hs);
+        if (threadIdx.x == 0 && publish_pair_once(row_pairs + j, pack_pair(hm, hs)))
+          __hip_atomic_fetch_add(&hdr->helped, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < kWave) {
+    float Mw, Sw;
+    wave_merge_pairs(row_pairs, nchunks, Mw, Sw);
+    if (threadIdx.x == 0) {
+      s_final[0] = Mw;
+      s_final[1] = out_scale<SOFTMAX>(Sw);
+    }
+  }
+  __syncthreads();
+  const float M = s_final[0], k = s_final[1];
+  const v4f *x4 = reinterpret_cast<const v4f *>(xr);
+  const int64_t n4 = len / 4;
+  int64_t i = threadIdx.x;
+  constexpr int U = 4;
+  for (; i + (U - 1) * kRowsThreads < n4; i += U * kRowsThreads) {
+    v4f f[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) f[u] = x4[i + u * kRowsThreads];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      store4(yr + 4 * (i + u * kRowsThreads), out_value<SOFTMAX>(f[u].x, M, k),
+             out_value<SOFTMAX>(f[u].y, M, k), out_value<SOFTMAX>(f[u].z, M, k),
+             out_value<SOFTMAX>(f[u].w, M, k));
+  }
+  for (; i < n4; i += kRowsThreads) {
+    const v4f f = x4[i];
+    store4(yr + 4 * i, out_value<SOFTMAX>(f.x, M, k), out_value<SOFTMAX>(f.y, M, k),
+           out_value<SOFTMAX>(f.z, M, k), out_value<SOFTMAX>(f.w, M, k));
+  }
+}
+
 template <bool VEC>
 __device__ __forceinline__ void whole_row_pair(const float *__restrict__ p, int64_t len,
                                                float *red, float &m, float &s) {
@@ -866,6 +971,14 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t spin = h_spin_limit;
+  if (h_rows_reread && vec) {
+    return for_row_batches(rows, kMaxRowsWorkgroups / p.nchunks, [&](int64_t r0, int64_t nr) {
+      hipLaunchKernelGGL((log_softmax_rows_reread_kernel<SOFTMAX>), dim3((uint32_t)(nr * p.nchunks)),
+                         dim3(kRowsThreads), 0, stream, x + r0 * ldx, y + r0 * ldy, cols, ldx,
+                         ldy, p.nchunks, p.chunk, hdr, pairs + r0 * p.nchunks, spin);
+      return hipGetLastError();
+    });
+  }
   return for_row_batches(rows, kMaxRowsWorkgroups / p.nchunks, [&](int64_t r0, int64_t nr) {
     return launch_rows_vpl<true, SOFTMAX>(vpl_for(p.chunk), vec, dim3((uint32_t)(nr * p.nchunks)),
                                           x + r0 * ldx, y + r0 * ldy, nr, cols, ldx, ldy,
@@ -877,6 +990,7 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
 }  // namespace
 
 void set_spin_limit(uint32_t polls) { h_spin_limit = polls; }
+void set_rows_reread(bool on) { h_rows_reread = on; }
 uint32_t chain_spin_limit() { return h_spin_limit; }
 
 RowsPlan rows_plan(int64_t cols) {

@@ -344,3 +344,24 @@ def test_rows_head_tail_full_size(orc):
         for r0 in range(0, 4096, 512):
             assert torch.logsumexp(y[r0:r0 + 512].double(), dim=1).abs().max().item() < 1e-5
         del xb, x, y
+
+
+@pytest.mark.parametrize("rows,cols,softmax", [(64, 393216, False), (16, 100000, True),
+                                               (8, 65540, False)])
+def test_rows_reread_variant(orc, rows, cols, softmax):
+    """The MALL re-read form of the split rows (test hook): every element
+    against the oracle; the helping path against the default of the same form
+    within the tolerance."""
+    x = inputs.normal((rows, cols), seed=rows + cols, device=DEV)
+    fn = L.softmax_rows if softmax else L.log_softmax_rows
+    try:
+        L.lse_testing_set_rows_reread(True)
+        y = fn(x)
+        torch.cuda.synchronize()
+    finally:
+        L.lse_testing_set_rows_reread(False)
+    xc = x.cpu().numpy()
+    if softmax:
+        compare(y.cpu().numpy(), orc.softmax_rows(xc), atol=1e-37, rtol=1e-5, what="reread sm")
+    else:
+        compare(y.cpu().numpy(), orc.log_softmax_rows(xc)[0], what="reread")
