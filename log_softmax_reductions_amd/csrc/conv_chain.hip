@@ -797,6 +797,36 @@ __device__ __forceinline__ void stage_and_convolve(const ChainArgs &a, int64_t n
   }
 }
 
+// The epilogue's per-channel table from a sample's merged mean / rstd in the
+// workspace head (written by chain_merge_kernel), with merge_stats' formula:
+// the same floats in, so the same table out.  Ends with a barrier.
+template <class Lds>
+__device__ __forceinline__ void stats_table(const ChainArgs &a, int64_t n, float ga, float be,
+                                            Lds &L) {
+  if (threadIdx.x < kCout) {
+    const int c = threadIdx.x, g = (c / 4) / (16 / a.G);
+    const float fm = a.mean[n * a.G + g], fr = a.rstd[n * a.G + g];
+    const float sc = fr * ga;
+    L.sc[c] = sc * (2.0f * kLog2e);
+    L.sh[c] = (be - fm * sc) * (2.0f * kLog2e);
+  }
+  __syncthreads();
+}
+
+// Between the statistics and apply launches of the two-launch path: one
+// workgroup per sample merges its tiles' statistics once (merge_stats, the
+// fused path's arithmetic and order) and writes mean / rstd for the apply
+// launch, instead of every apply workgroup merging them (a 600 x 520 sample
+// has 23920 words at 16 groups).
+__global__ __launch_bounds__(kTeams * kThreads) void chain_merge_kernel(ChainArgs a) {
+  __shared__ PairLds L;
+  const int64_t n = a.block_base + blockIdx.x;  // here: first sample of the launch + index
+  uint64_t wd[kHeldPer];
+  while (!wait_stats<kTeams * kThreads>(a, n, L, wd)) {  // published by the previous launch
+  }
+  merge_stats<kTeams * kThreads>(a, n, wd, true, 1.0f, 0.0f, L);
+}
+
 // Cold path of the sample's last arrival: finish the ndef pairs of sample n
 // deferred before it (their statistics are all published).  Out of line so
 // that nothing of it stays alive through the common path.
@@ -917,6 +947,13 @@ void conv_chain_pair_kernel(ChainArgs a) {
     if (a.gamma) ga = a.gamma[threadIdx.x];
     if (a.beta) be = a.beta[threadIdx.x];
   }
+  if constexpr (MODE == kApply || MODE == kApplyStaged) {
+    // The sample's mean / rstd were merged by chain_merge_kernel between the
+    // launches: nothing to wait for, no per-workgroup merge.
+    stats_table(a, n, ga, be, L);
+    if (active) tile_epilogue_lds(a, n, tile, acc, valid, L, twave);
+    return;
+  }
   // Arrival (after this pair's statistics were published); the returned
   // counts are needed only after the epilogue, so the round trip overlaps
   // the wait.
@@ -925,17 +962,8 @@ void conv_chain_pair_kernel(ChainArgs a) {
     arrived_before = __hip_atomic_fetch_add(a.arrivals + n, 1ull, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
   uint64_t wd[kHeldPer];
-  // A poll limit of 0 (test hook) tries to defer without waiting.  The staged
-  // apply never defers: its statistics were complete before it started (and
-  // it holds no conv weights to redo a deferred pair with).
-  bool ok;
-  if constexpr (MODE == kApplyStaged) {
-    while (!wait_stats<kTeams * kThreads>(a, n, L, wd)) {
-    }
-    ok = true;
-  } else {
-    ok = a.spin_limit != 0 && wait_stats<kTeams * kThreads>(a, n, L, wd);  // uniform
-  }
+  // A poll limit of 0 (test hook) tries to defer without waiting.
+  bool ok = a.spin_limit != 0 && wait_stats<kTeams * kThreads>(a, n, L, wd);  // uniform
   if (!ok) {
     if (threadIdx.x == 0) {
       const uint64_t st = __hip_atomic_fetch_add(a.arrivals + n, 1ull << 32, __ATOMIC_RELAXED,
@@ -1110,6 +1138,10 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
       hipLaunchKernelGGL(conv_chain_pair_kernel<kFused>, grid, block, 0, stream, a);
     } else {
       hipLaunchKernelGGL(conv_chain_pair_kernel<kStats>, grid, block, 0, stream, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      ChainArgs m = a;
+      m.block_base = (uint32_t)n0;  // the merge takes samples, one workgroup each
+      hipLaunchKernelGGL(chain_merge_kernel, dim3((uint32_t)nb), block, 0, stream, m);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (L.path == kPathStaged)
         hipLaunchKernelGGL(conv_chain_pair_kernel<kApplyStaged>, grid, block, 0, stream, a);

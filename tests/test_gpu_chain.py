@@ -159,17 +159,21 @@ def test_chain_deferred_pairs(orc, N, H, W, groups):
     the default path, and the deferred count: at least one pair per sample
     (the first arrival cannot see the whole sample), never a sample's last
     arrival.  Shapes: two config-sized samples, a ragged one (odd tile rows,
-    three tile columns), and a sample large enough for the two-launch path."""
+    three tile columns), and a sample of 748 tile pairs forced through the
+    fused launch (by default it takes the two-launch path, which never
+    waits and so never defers: checked last)."""
     x, w, b, g, be = _chain_inputs(N, H, W, seed=7 * N + H + W, affine=True)
     pairs = N * ((((H - 2) + 1) // 2 * ((W - 2 + 127) // 128) + 1) // 2)
     ws = torch.empty(L.fused_conv_gn_act_lse_workspace_bytes(N, 8, H, W, 64, 3, groups),
                      dtype=torch.uint8, device=DEV)
     try:
         L.lse_testing_set_spin_limit(0)
+        L.lse_testing_set_chain_path(1)
         out = L.fused_conv_gn_act_lse(x, w, b, g, be, groups, 1e-5, ws=ws)
         torch.cuda.synchronize()
     finally:
         L.lse_testing_set_spin_limit(1 << 24)
+        L.lse_testing_set_chain_path(0)
     deferred = _deferred_word(ws, N, groups)
     assert N <= deferred <= pairs - N, (deferred, pairs)
     print("pairs deferred:", deferred, "of", pairs)
@@ -180,10 +184,16 @@ def test_chain_deferred_pairs(orc, N, H, W, groups):
     compare(out.cpu().numpy(), ref, rtol=RTOL_CHAIN, what="deferred")
     compare(stats[:NG].cpu().numpy(), mean.ravel(), atol=1e-6, rtol=1e-4, what="deferred mean")
     compare(stats[NG:].cpu().numpy(), rstd.ravel(), atol=1e-6, rtol=1e-4, what="deferred rstd")
-    ws2 = torch.empty_like(ws)
-    out2 = L.fused_conv_gn_act_lse(x, w, b, g, be, groups, 1e-5, ws=ws2)
-    torch.cuda.synchronize()
-    assert _deferred_word(ws2, N, groups) == 0
+    ws2 = torch.empty(L.fused_conv_gn_act_lse_workspace_bytes(N, 8, H, W, 64, 3, groups),
+                      dtype=torch.uint8, device=DEV)
+    try:
+        L.lse_testing_set_spin_limit(0)        # the default path at a poll limit of 0
+        out2 = L.fused_conv_gn_act_lse(x, w, b, g, be, groups, 1e-5, ws=ws2)
+        torch.cuda.synchronize()
+    finally:
+        L.lse_testing_set_spin_limit(1 << 24)
+    if H == 600:                               # two launches: nothing waits, nothing deferred
+        assert _deferred_word(ws2, N, groups) == 0
     assert torch.equal(out, out2)
     assert torch.equal(stats, ws2[: 2 * NG * 4].view(torch.float32))
 
