@@ -156,6 +156,13 @@ __device__ __forceinline__ float hardswish_of_tanh_scaled(float y) {
   return fmaf(r, fmaf(r, 2.0f / 3.0f, -5.0f / 3.0f), 2.0f / 3.0f);
 }
 
+// log2(e) x hardswish(tanh(z)) from the same y = 2 log2(e) z: the polynomial
+// in r with its coefficients scaled by log2(e).
+__device__ __forceinline__ float hardswish_of_tanh_scaled_log2e(float y) {
+  const float r = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(y) + 1.0f);
+  return fmaf(r, fmaf(r, 2.0f / 3.0f * kLog2e, -5.0f / 3.0f * kLog2e), 2.0f / 3.0f * kLog2e);
+}
+
 // The x tile of sample n at (h0, w0): 8 channels x 4 rows x 132 columns.  It
 // is loaded into registers with every global load of the tile in flight at
 // once (128-bit loads when rows are 16-byte aligned), then stored to LDS, so
@@ -605,8 +612,9 @@ __device__ __forceinline__ void tile_epilogue_lds(const ChainArgs &a, int64_t n,
   const int th = tile / a.tiles_w, tw = tile - th * a.tiles_w;
 #pragma unroll
   for (int blk = 0; blk < kNB; ++blk) {
-    float u[kMT][4];
-    float m = -__builtin_inff();
+    // w = log2(e) u, u = v + hardswish(tanh(GN(v))): one fma folds the
+    // residual add into the scaling.
+    float w[kMT][4];
 #pragma unroll
     for (int t = 0; t < kMT; ++t) {
       const f32x4 sc = *reinterpret_cast<const f32x4 *>(&L.sc[16 * t + 4 * q]);
@@ -614,24 +622,46 @@ __device__ __forceinline__ void tile_epilogue_lds(const ChainArgs &a, int64_t n,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = acc[blk][t][r];
-        u[t][r] = v + hardswish_of_tanh_scaled(fmaf(v, sc[r], sh[r]));
-        m = fmaxf(m, u[t][r]);
+        w[t][r] = fmaf(v, kLog2e, hardswish_of_tanh_scaled_log2e(fmaf(v, sc[r], sh[r])));
       }
     }
-    const float M = across_quads(m, OpMax{});
-    // exp(u - M) as 2^(u log2 e - M log2 e), one fma per term; the rounding
-    // of M log2 e shifts every term alike (a relative few 1e-7 in S).
-    const float c2 = (is_finite(M) ? M : 0.0f) * kLog2e;
+    // The logsumexp of the pixel's 64 values without the max shift: the sum
+    // of exp(u) = 2^w itself.  Where that sum lies in [2^-60, 2^60] no term
+    // overflowed and none that matters underflowed, and each term is off by
+    // at most |u| x 2^-24 relative (the rounding of w), so log S is within a
+    // few 1e-7 of the shifted form.  Any other pixel (huge or tiny values, a
+    // non-finite one) is done again with the max shift; the wave takes that
+    // branch only if one of its pixels needs it.
     float s = 0.0f;
 #pragma unroll
     for (int t = 0; t < kMT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(fmaf(u[t][r], kLog2e, -c2));
+      for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(w[t][r]);
     const float S = across_quads(s, OpSum{});
+    const bool redo = !(S >= 0x1p-60f && S <= 0x1p60f);  // NaN included
+    float res = logf(S);
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+      float m = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < kMT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, w[t][r]);
+      const float Mw = across_quads(m, OpMax{});  // log2(e) x the max
+      const float c2 = is_finite(Mw) ? Mw : 0.0f;
+      float s2 = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kMT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s2 += __builtin_amdgcn_exp2f(w[t][r] - c2);
+      const float S2 = across_quads(s2, OpSum{});
+      // LSE = ln 2 (Mw + log2 S2); a non-finite Mw passes through.
+      if (redo) res = is_finite(Mw) ? (Mw + __builtin_log2f(S2)) * 0.693147180559945309f : Mw;
+      if (redo && (S2 != S2)) res = S2;
+    }
     if (q == 0 && valid[blk]) {
       int dh, dw;
       pixel_of(blk, li, wave, dh, dw);
-      a.out[(n * a.Ho + th * kTileH + dh) * (int64_t)a.Wo + tw * kTileW + dw] = M + logf(S);
+      a.out[(n * a.Ho + th * kTileH + dh) * (int64_t)a.Wo + tw * kTileW + dw] = res;
     }
   }
 }
