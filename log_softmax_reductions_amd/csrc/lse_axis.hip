@@ -194,8 +194,45 @@ __device__ __forceinline__ void store_w(float *p, const float (&r)[W]) {
   }
 }
 
-// out[o, j] = LSE_r x[o, r, j]
-template <int RB, int W, bool STR>
+#ifndef LSE_AXIS0_SADDR
+#define LSE_AXIS0_SADDR 1
+#endif
+// load_block for 128-bit lanes whose x offsets, o xso + q W elements, fit 32
+// bits as bytes: plane i's pointer is uniform (scalar registers) and the lane
+// adds one 32-bit byte offset, so a load is a scalar base plus a vector offset.
+// The 64-bit per-lane form leaves the compiler one 64-bit vector offset per
+// plane (RB = 32: 64 VGPRs, 208 in all, 2 waves per SIMD).
+template <int RB, bool NT = LSE_AXIS0_NT_LOAD>
+__device__ __forceinline__ void load_block_s(const float *plane0, int64_t stride, int64_t nb,
+                                             uint32_t off, float (&v)[4][RB]) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const char gbyte;
+  typedef __attribute__((address_space(1))) const v4f gv4f;
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    if (nb == RB || i < nb) {
+      // Empty asm statements pin the plane pointer to scalar registers and the
+      // offset to one vector register at each load.
+      gbyte *p = (gbyte *)(plane0 + (int64_t)i * stride);
+      asm volatile("" : "+s"(p));
+      uint32_t ok = off;
+      asm volatile("" : "+v"(ok));
+      v4f t;
+      if constexpr (NT)
+        t = __builtin_nontemporal_load((gv4f *)(p + ok));
+      else
+        t = *(gv4f *)(p + ok);
+      v[0][i] = t.x; v[1][i] = t.y; v[2][i] = t.z; v[3][i] = t.w;
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v[w][i] = -__builtin_inff();
+    }
+  }
+}
+
+// out[o, j] = LSE_r x[o, r, j].  OFF32: W = 4 and every lane's x offset fits
+// 32 bits as bytes (load_block_s).
+template <int RB, int W, bool STR, bool OFF32 = false>
 __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
     const float *__restrict__ x, float *__restrict__ out, AxisDims d) {
   const int64_t st_xsr = STR ? d.xsr : d.inner;
@@ -204,18 +241,29 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
   const int64_t st_xso = STR ? d.xso : d.R * d.inner;
   const int64_t st_yso = STR ? d.yso : d.inner;
   const int64_t R = d.R;
-  const float *xo = x + o * st_xso + q * W;
   float m[W], s[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) {
     m[w] = -__builtin_inff();
     s[w] = 0.0f;
   }
-  for (int64_t r0 = 0; r0 < R; r0 += RB) {
-    float v[W][RB];
-    load_block<RB, W>(xo + r0 * st_xsr, st_xsr, (R - r0 < RB) ? (R - r0) : RB, v);
+  if constexpr (OFF32) {
+    static_assert(W == 4, "scalar-base loads are 128-bit");
+    const uint32_t off = (uint32_t)(o * st_xso + q * W) * 4u;
+    for (int64_t r0 = 0; r0 < R; r0 += RB) {
+      float v[W][RB];
+      load_block_s<RB>(x + r0 * st_xsr, st_xsr, (R - r0 < RB) ? (R - r0) : RB, off, v);
 #pragma unroll
-    for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
+      for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
+    }
+  } else {
+    const float *xo = x + o * st_xso + q * W;
+    for (int64_t r0 = 0; r0 < R; r0 += RB) {
+      float v[W][RB];
+      load_block<RB, W>(xo + r0 * st_xsr, st_xsr, (R - r0 < RB) ? (R - r0) : RB, v);
+#pragma unroll
+      for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
+    }
   }
   float r[W];
 #pragma unroll
@@ -388,10 +436,33 @@ __global__ __launch_bounds__(kWalkThreads) void lse_axis_walk_kernel(
   }
 }
 
+#ifndef LSE_AXIS_LSM_OFF32_NT
+#define LSE_AXIS_LSM_OFF32_NT 1   // the 32-bit-offset log_softmax kernel stores non-temporally
+#endif
+// Store 4 values at a uniform plane pointer plus a 32-bit lane byte offset
+// (the store form of load_block_s).
+template <bool NT>
+__device__ __forceinline__ void store4_s(float *plane, uint32_t off, const float (&r)[4]) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) char gbyte_w;
+  typedef __attribute__((address_space(1))) v4f gv4f_w;
+  gbyte_w *p = (gbyte_w *)plane;
+  asm volatile("" : "+s"(p));
+  uint32_t ok = off;
+  asm volatile("" : "+v"(ok));
+  const v4f t = {r[0], r[1], r[2], r[3]};
+  if constexpr (NT)
+    __builtin_nontemporal_store(t, (gv4f_w *)(p + ok));
+  else
+    *(gv4f_w *)(p + ok) = t;
+}
+
 // y[o, r, j] = x[o, r, j] - LSE_r' x[o, r', j].  With R <= RB the R values stay
 // in registers between the reduction and the write (one read, one write);
-// otherwise a streaming reduction pass and a write pass (two reads).
-template <int RB, int W, bool STR>
+// otherwise a streaming reduction pass and a write pass (two reads).  OFF32:
+// W = 4 and every lane's x and y offsets fit 32 bits as bytes (scalar plane
+// pointers, as in load_block_s).
+template <int RB, int W, bool STR, bool OFF32 = false>
 __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
     const float *__restrict__ x, float *__restrict__ y, AxisDims d) {
   const int64_t st_xsr = STR ? d.xsr : d.inner;
@@ -403,6 +474,15 @@ __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
   const int64_t R = d.R;
   const float *xo = x + o * st_xso + q * W;
   float *yo = y + o * st_yso + q * W;
+  const uint32_t xoff = (uint32_t)(o * st_xso + q * W) * 4u;
+  const uint32_t yoff = (uint32_t)(o * st_yso + q * W) * 4u;
+  // Planes r0 .. r0 + nb - 1 into v.
+  auto load = [&](int64_t r0, int64_t nb, float (&v)[W][RB]) {
+    if constexpr (OFF32)
+      load_block_s<RB>(x + r0 * st_xsr, st_xsr, nb, xoff, v);
+    else
+      load_block<RB, W>(xo + r0 * st_xsr, st_xsr, nb, v);
+  };
   float m[W], s[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) {
@@ -411,12 +491,12 @@ __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
   }
   float v[W][RB];
   if (R <= RB) {  // uniform
-    load_block<RB, W>(xo, st_xsr, R, v);
+    load(0, R, v);
 #pragma unroll
     for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
   } else {
     for (int64_t r0 = 0; r0 < R; r0 += RB) {
-      load_block<RB, W>(xo + r0 * st_xsr, st_xsr, (R - r0 < RB) ? (R - r0) : RB, v);
+      load(r0, (R - r0 < RB) ? (R - r0) : RB, v);
 #pragma unroll
       for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
     }
@@ -426,14 +506,17 @@ __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
   for (int w = 0; w < W; ++w) lns[w] = logf(s[w]);
   for (int64_t r0 = 0; r0 < R; r0 += RB) {
     const int64_t nb = (R - r0 < RB) ? (R - r0) : RB;
-    if (R > RB) load_block<RB, W>(xo + r0 * st_xsr, st_xsr, nb, v);
+    if (R > RB) load(r0, nb, v);
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if (i < nb) {
         float r[W];
 #pragma unroll
         for (int w = 0; w < W; ++w) r[w] = (v[w][i] - m[w]) - lns[w];
-        store_w<W>(yo + (r0 + i) * st_ysr, r);
+        if constexpr (OFF32)
+          store4_s<LSE_AXIS_LSM_OFF32_NT != 0>(y + (r0 + i) * st_ysr, yoff, r);
+        else
+          store_w<W>(yo + (r0 + i) * st_ysr, r);
       }
     }
   }
@@ -566,6 +649,35 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   }
 }
 
+// Workgroups per CU, capped through the LDS each one reserves: 160 KiB per CU,
+// allocated in 1280-byte granules, so a reservation of (160 KiB / c) rounded
+// down to a granule lets exactly c workgroups share a CU (c + 1 do not fit).
+constexpr int kLdsPerCu = 163840;
+constexpr size_t occupancy_lds(int c) { return c > 0 ? (size_t)(kLdsPerCu / c) / 1280 * 1280 : 0; }
+
+#ifndef LSE_AXIS0_CAP
+#define LSE_AXIS0_CAP 1
+#endif
+// One-wave logsumexp workgroups per CU for RB planes (RB 128-bit loads in
+// flight per wave).  With as many waves as the VGPRs allow, the memory system
+// receives more outstanding loads than it turns into bandwidth, and the kernel
+// slows: same-box sweeps of the cap over (R, 2048, 4096) and channel layouts
+// measured the fastest at 6 waves per CU for RB = 32 (192 KiB in flight per
+// CU; 12 allowed by VGPRs: 184 -> 173 us on (32, 2048, 4096)) and RB = 16
+// (102 -> 91 us on (16, 2048, 4096)), 9 for RB = 8 (102 -> 92 us on (8, 4096,
+// 4096)) and 16 for RB = 4 (105 -> 97 us on (4, 8192, 4096)).
+constexpr int axis0_waves_per_cu(int rb) {
+  return !LSE_AXIS0_CAP ? 0 : rb >= 16 ? 6 : rb == 8 ? 9 : 16;
+}
+// Two-wave log_softmax workgroups per CU (128-bit path with 32-bit offsets and
+// non-temporal stores), the fastest of a same-box sweep over 3 .. 8: 3 for
+// RB = 32 ((32, 2048, 4096): 371 us; 403 us at the VGPR limit of 6), 4 for
+// RB = 16 ((16, 2048, 4096): 188 us; 200-212 us at 6-8), 6 for RB = 8 ((8,
+// 4096, 4096): 178 us; 184 us at 4 and 8).
+constexpr int lsm_groups_per_cu(int rb) {
+  return !LSE_AXIS0_CAP ? 0 : rb == 32 ? 3 : rb == 16 ? 4 : rb == 8 ? 6 : 0;
+}
+
 template <int RB, bool LSM, bool STR>
 hipError_t launch_rb(const float *x, float *out, const AxisDims &d, bool vec,
                      hipStream_t stream) {
@@ -573,15 +685,29 @@ hipError_t launch_rb(const float *x, float *out, const AxisDims &d, bool vec,
   const dim3 grid((uint32_t)((items + kAxis0Threads - 1) / kAxis0Threads));
   if constexpr (LSM) {
     const dim3 lgrid((uint32_t)((items + kLsmThreads - 1) / kLsmThreads));
-    if (vec)
-      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, kVecW, STR>), lgrid, dim3(kLsmThreads), 0,
+    // Largest lane offsets, in bytes, of x and y.
+    const int64_t xspan = ((d.outer - 1) * (STR ? d.xso : d.R * d.inner) + d.inner) * 4;
+    const int64_t yspan = ((d.outer - 1) * (STR ? d.yso : d.R * d.inner) + d.inner) * 4;
+    const size_t lds = vec ? occupancy_lds(lsm_groups_per_cu(RB)) : 0;
+    if (vec && kVecW == 4 && LSE_AXIS0_SADDR && xspan <= (int64_t)0xffffffff &&
+        yspan <= (int64_t)0xffffffff)
+      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, 4, STR, true>), lgrid, dim3(kLsmThreads), lds,
+                         stream, x, out, d);
+    else if (vec)
+      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, kVecW, STR>), lgrid, dim3(kLsmThreads), lds,
                          stream, x, out, d);
     else
       hipLaunchKernelGGL((log_softmax_axis_kernel<RB, 1, STR>), lgrid, dim3(kLsmThreads), 0, stream,
                          x, out, d);
   } else {
-    if (vec)
-      hipLaunchKernelGGL((lse_axis_kernel<RB, kVecW, STR>), grid, dim3(kAxis0Threads), 0, stream, x,
+    // Largest lane offset, in bytes, of the 128-bit kernel's loads.
+    const int64_t span = ((d.outer - 1) * (STR ? d.xso : d.R * d.inner) + d.inner) * 4;
+    const size_t lds = vec ? occupancy_lds(axis0_waves_per_cu(RB)) : 0;
+    if (vec && kVecW == 4 && LSE_AXIS0_SADDR && span <= (int64_t)0xffffffff)
+      hipLaunchKernelGGL((lse_axis_kernel<RB, 4, STR, true>), grid, dim3(kAxis0Threads), lds, stream,
+                         x, out, d);
+    else if (vec)
+      hipLaunchKernelGGL((lse_axis_kernel<RB, kVecW, STR>), grid, dim3(kAxis0Threads), lds, stream, x,
                          out, d);
     else
       hipLaunchKernelGGL((lse_axis_kernel<RB, 1, STR>), grid, dim3(kAxis0Threads), 0, stream, x, out,

@@ -183,3 +183,25 @@ def test_axis_more_outputs_than_one_launch(orc, outer, R, inner):
     torch.cuda.synchronize()
     compare(y[:, :, cols].cpu().numpy(), orc.log_softmax_axis(xs), what="lsm split")
     assert torch.logsumexp(y[:, :, w].double(), dim=1).abs().max().item() < 1e-5
+
+
+@pytest.mark.parametrize("outer,R,inner", [(2, 4, 1 << 28), (2, 20, 1 << 26)])
+def test_axis_lane_offsets_beyond_32_bits(orc, outer, R, inner):
+    """x and y larger than 4 GiB per launch (8 and 10.7 GB): the register-block
+    kernels take 64-bit lane offsets instead of one 32-bit offset from a scalar
+    plane pointer.  Sampled columns of both outer slices against the oracle,
+    and a window at the far end of x by property."""
+    x = inputs.normal((outer, R, inner), seed=29 + R, device=DEV)
+    cols = [0, 3, 4, inner // 2 + 1, inner - 5, inner - 1]
+    xs = x[:, :, cols].cpu().numpy()
+    out = L.lse_reduce_axis(x, 1)
+    torch.cuda.synchronize()
+    compare(out[:, cols].cpu().numpy(), orc.lse_axis(xs), what="lse 64-bit offsets")
+    w = slice(inner - 100_000, inner)
+    ref = torch.logsumexp(x[:, :, w].double(), dim=1)
+    assert (out[:, w].double() - ref).abs().max().item() < 1e-5 + 2e-6 * ref.abs().max().item()
+    del out
+    y = L.log_softmax_axis(x, 1)
+    torch.cuda.synchronize()
+    compare(y[:, :, cols].cpu().numpy(), orc.log_softmax_axis(xs), what="lsm 64-bit offsets")
+    assert torch.logsumexp(y[:, :, w].double(), dim=1).abs().max().item() < 1e-5
