@@ -11,7 +11,7 @@
 // written to memory and the conv runs once:
 //
 //   each workgroup of 8 waves takes a pair of 2 x 128 pixel tiles of one
-//   sample (pairs handed out by an atomic ticket, in sample order); waves 0-3
+//   sample (pair = workgroup index, in sample order); waves 0-3
 //   stage and convolve one tile, waves 4-7 the other, on MFMA into registers
 //   (64 accumulators per lane, so four waves fit on a SIMD); the pair
 //   publishes each tile's per-group (mean, M2), waits until every tile of
@@ -19,12 +19,12 @@
 //   runs normalise, tanh, hardswish, residual and the 64-channel logsumexp
 //   on the accumulators it still holds, writing one float per pixel.
 //
-// The wait normally ends within microseconds: tickets are claimed only by
-// running workgroups, in order, and every workgroup publishes before it
-// waits, so the tiles of a sample that has a waiting workgroup are all held
-// by running workgroups once its last ticket is claimed, which needs only as
-// many co-resident workgroups as a sample has tile pairs (32 for 126 x 126;
-// hundreds fit).  Progress never depends on that, though.  Each workgroup
+// The wait normally ends within microseconds: the hardware starts workgroups
+// in index order (dealt round robin to the XCDs), and every workgroup
+// publishes before it waits, so the tiles of a sample that has a waiting
+// workgroup are all held by running workgroups soon after, which needs only
+// as many co-resident workgroups as a sample has tile pairs (32 for 126 x 126;
+// hundreds fit).  Progress never depends on that order, though.  Each workgroup
 // counts its arrival (after publishing) on a per-sample word; one whose wait
 // runs out (kChainWaitTicks, or the test hook's poll limit) counts itself
 // deferred on the same word: if every pair of its sample has arrived by then
@@ -105,7 +105,7 @@ constexpr int kWinoU = 16 * 2 * kMT * kWave;                             // 8192
 constexpr int kWLds = kWino ? kWinoU : kCout * kWStride;
 
 struct ChainWsHeader {
-  uint32_t ticket;     // next tile-pair ticket
+  uint32_t reserved;   // 0
   uint32_t deferred;   // pairs finished by their sample's last arrival
   uint32_t pad[62];
 };
@@ -115,8 +115,8 @@ struct ChainArgs {
   int32_t N, H, W, Ho, Wo, G, log2G, tiles_w, tiles;
   float eps;
   uint32_t spin_limit;
-  uint32_t block_base;   // kStats / kApply: workgroup index of this launch's first pair
-  uint32_t stage_first;  // ticket of the first pair whose conv tiles sit in `stage`
+  uint32_t block_base;   // pair index (over all samples) of this launch's first workgroup
+  uint32_t stage_first;  // pair index of the first pair whose conv tiles sit in `stage`
   float *stage;          // kStats with staging, kApplyStaged: conv tiles of this batch
   float *out;
   float *mean;           // (N, G), written by tile 0 of each sample
@@ -304,7 +304,7 @@ __device__ __forceinline__ void conv_tile(const ChainArgs &a, const float *xs, c
 // fp32 rounding (coefficients 0, +-1, +-1/2).
 
 // W arrives as (o, ci, kh, kw) rows of 9; thread o * 8 + ci holds its 3 x 3
-// filter (loaded before the ticket is known) and writes its 16 U values.
+// filter (loaded at the workgroup's start, with x) and writes its 16 U values.
 struct WinoW {
   float g[9];
 };
@@ -778,7 +778,7 @@ __device__ __forceinline__ void publish_pair_stats(const ChainArgs &a, int64_t n
 // waves fit on a SIMD and one wave's MFMAs overlap others' staging, waiting
 // and epilogue.  W staging and the wait for the sample's statistics are paid
 // once per pair.
-//   kFused: pairs handed out by ticket in sample order; publish, wait for the
+//   kFused: pairs in workgroup order (sample order); publish, wait for the
 //           sample, merge, epilogue (one launch; used while a sample's pairs
 //           fit on the GPU at once, see launch_conv_chain).
 //   kStats: publish only (and, when a.stage is set, store the pair's conv
@@ -795,9 +795,9 @@ enum ChainMode { kFused = 0, kStats = 1, kApply = 2, kApplyStaged = 3 };
 // of float4 = 128 KiB, in register order, so that each wave's store or load
 // of one accumulator vector is one contiguous 1 KiB.
 constexpr int64_t kStageF4PerPair = (int64_t)kTeams * (kThreads / kWave) * kNB * kMT * kWave;
-__device__ __forceinline__ f32x4 *stage_slot(const ChainArgs &a, uint32_t ticket) {
+__device__ __forceinline__ f32x4 *stage_slot(const ChainArgs &a, uint32_t pair) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  return reinterpret_cast<f32x4 *>(a.stage) + (int64_t)(ticket - a.stage_first) * kStageF4PerPair +
+  return reinterpret_cast<f32x4 *>(a.stage) + (int64_t)(pair - a.stage_first) * kStageF4PerPair +
          (int64_t)wave * (kNB * kMT * kWave) + lane;
 }
 
@@ -905,22 +905,17 @@ void conv_chain_pair_kernel(ChainArgs a) {
   __shared__ alignas(16) float xs[kTeams][kCin * kLdsH * kLdsW];
   __shared__ alignas(16) float wl[kWLds];  // W rows, or U in fragment order (Winograd)
   __shared__ PairLds L;
-  __shared__ uint32_t s_ticket, s_last;
-  // W's loads are in flight while the ticket is claimed.
+  __shared__ uint32_t s_ndef, s_last;
+  // W's and x's loads are in flight together.  The pair is the workgroup
+  // index: an atomic ticket (pairs in the order workgroups start) put its
+  // round trip before the x loads and measured 0.209 against 0.195 ms on
+  // (128, 8, 128, 128), with bit-identical results.
   std::conditional_t<kWino, WinoW, WRegs<kTeams * kThreads>> wr;
   if constexpr (MODE != kApplyStaged) load_w(a.w, wr);
-  // kStats, kApply: no workgroup waits on another's turn, any order will do.
-  uint32_t ticket = a.block_base + blockIdx.x;
-  if constexpr (MODE == kFused) {
-    if (threadIdx.x == 0)
-      s_ticket = __hip_atomic_fetch_add(&a.hdr->ticket, 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    ticket = s_ticket;
-  }
+  const uint32_t pair = a.block_base + blockIdx.x;
   const uint32_t groups = (uint32_t)(a.tiles + kTeams - 1) / kTeams;  // workgroups per sample
-  const int64_t n = ticket / groups;
-  const uint32_t p = ticket - (uint32_t)n * groups;
+  const int64_t n = pair / groups;
+  const uint32_t p = pair - (uint32_t)n * groups;
   const int tA = kTeams * (int)p, tB = tA + 1;
   const bool hasB = kTeams == 2 && tB < a.tiles;  // uniform
 
@@ -934,7 +929,7 @@ void conv_chain_pair_kernel(ChainArgs a) {
   bool valid[kNB];
   if constexpr (MODE == kApplyStaged) {
     if (active) {  // the conv tiles from the staging area
-      const f32x4 *src = stage_slot(a, ticket);
+      const f32x4 *src = stage_slot(a, pair);
 #pragma unroll
       for (int blk = 0; blk < kNB; ++blk)
 #pragma unroll
@@ -962,7 +957,7 @@ void conv_chain_pair_kernel(ChainArgs a) {
     publish_pair_stats(a, n, tA, tB, hasB, active, acc, valid, L);
   if constexpr (MODE == kStats) {
     if (a.stage && active) {  // uniform per wave
-      f32x4 *dst = stage_slot(a, ticket);
+      f32x4 *dst = stage_slot(a, pair);
 #pragma unroll
       for (int blk = 0; blk < kNB; ++blk)
 #pragma unroll
@@ -1013,14 +1008,14 @@ void conv_chain_pair_kernel(ChainArgs a) {
   }
   // The last arrival of the sample finishes the pairs deferred before it.
   if (threadIdx.x == 0)
-    s_ticket = ((uint32_t)arrived_before + 1u == groups) ? (uint32_t)(arrived_before >> 32) : 0u;
-  merge_stats<kTeams * kThreads>(a, n, wd, tA == 0, ga, be, L);  // barriers: s_ticket visible
+    s_ndef = ((uint32_t)arrived_before + 1u == groups) ? (uint32_t)(arrived_before >> 32) : 0u;
+  merge_stats<kTeams * kThreads>(a, n, wd, tA == 0, ga, be, L);  // barriers: s_ndef visible
   if (active) tile_epilogue_lds(a, n, tile, acc, valid, L, twave);
-  const uint32_t ndef = s_ticket;
+  const uint32_t ndef = s_ndef;
   if (ndef != 0) finish_deferred(a, n, ndef, xs[team], wl, &L);
 }
 
-// Clear n 64-bit words (the ticket / helped header and the statistics words);
+// Clear n 64-bit words (the header, the statistics words and the queue);
 // grid-stride, at most 4096 workgroups.
 __global__ __launch_bounds__(256) void chain_clear_kernel(uint64_t *__restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
@@ -1153,8 +1148,7 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
   if (e != hipSuccess) return e;
   const int64_t per_sample = L.per_sample;
   // Samples per launch: a dispatch's work-item count must fit 32 bits (and a
-  // staged batch must fit the staging area).  The fused launches need no
-  // offset: each claims the next tickets in order.
+  // staged batch must fit the staging area).
   int64_t max_n = std::max<int64_t>(1, (0xffffffffll / (kTeams * kThreads)) / per_sample);
   if (L.path == kPathStaged) max_n = std::min(max_n, L.stage_samples);
   a.stage = L.path == kPathStaged ? reinterpret_cast<float *>(base + L.stage_off) : nullptr;
