@@ -3,8 +3,11 @@
  * hipStream_t, results copied back and compared with the fp64 oracle
  * (oracle/oracle.c, linked in: this is test code).
  *
- *   abi_check --host   validation paths only (no GPU needed)
- *   abi_check          every call on the GPU against the oracle
+ *   abi_check --host     validation paths only (no GPU needed)
+ *   abi_check --oracle   the oracle's functions alone, against closed forms
+ *                        and each other (no GPU; the CPU suite also runs it
+ *                        built with AddressSanitizer and UBSan)
+ *   abi_check            every call on the GPU against the oracle
  *
  * Inputs come from a SplitMix64 stream (uniforms, Box-Muller normals): the
  * same host arrays go to the library and to the oracle.  Tolerance as in the
@@ -33,6 +36,13 @@ int oracle_fused_chain(const float *x, const float *w, const float *b, const flo
                        const float *beta, int64_t N, int64_t Cin, int64_t H, int64_t W,
                        int64_t Cout, int64_t K, int64_t G, double eps, double *out,
                        double *mean_out, double *rstd_out, int nthreads);
+int oracle_lse_chunk_partials(const float *x, int64_t rows, int64_t cols, int64_t chunk,
+                              double *m_out, double *s_out, int nthreads);
+int oracle_lse_merge(const double *m, const double *s, int64_t rows, int64_t k, double *lse,
+                     double *M_out, double *S_out);
+int oracle_conv2d(const float *x, const float *w, const float *b, int64_t N, int64_t Cin,
+                  int64_t H, int64_t W, int64_t Cout, int64_t K, double *out, int nthreads);
+double oracle_hardswish(double t);
 
 static int g_fail = 0;
 
@@ -147,6 +157,124 @@ static void host_checks(void) {
   printf("%-34s %s\n", "host-side validation", g_fail ? "FAIL" : "ok");
 }
 
+/* ------------------------------------------------------------ oracle-only */
+/* Every oracle function on small host arrays (edge sizes included), checked
+ * against facts that do not restate its formula: closed forms, sums of
+ * probabilities, agreement between independent entry points, a delta-filter
+ * conv.  Run with the sanitizers by the CPU suite. */
+static int close_to(double a, double b, double tol) {
+  if (isnan(a) || isnan(b)) return isnan(a) && isnan(b);
+  if (isinf(a) || isinf(b)) return a == b;
+  return fabs(a - b) <= tol * (1.0 + fabs(b));
+}
+
+static void oracle_checks(void) {
+  const double inf = INFINITY;
+  /* axis 0: R equal values -> v + log R; two values -> max + log1p(exp(-|a - b|)) */
+  {
+    float x[15];
+    for (int i = 0; i < 15; ++i) x[i] = 1.25f;
+    double out[3];
+    EXPECT(oracle_lse_axis0(x, 5, 3, out, 1) == 0, "lse_axis0 status");
+    for (int j = 0; j < 3; ++j) EXPECT(close_to(out[j], 1.25 + log(5.0), 1e-14), "R equal values");
+    const float y[2] = {3.0f, -1.0f};
+    EXPECT(oracle_lse_axis0(y, 2, 1, out, 1) == 0, "two values status");
+    EXPECT(close_to(out[0], 3.0 + log1p(exp(-4.0)), 1e-14), "two values");
+    const float sp[8] = {-(float)inf, (float)inf, NAN, 0.0f,    /* plane 0 */
+                         -(float)inf, 1.0f, (float)inf, NAN};   /* plane 1 */
+    double o4[4];
+    EXPECT(oracle_lse_axis0(sp, 2, 4, o4, 1) == 0, "special status");
+    EXPECT(o4[0] == -inf && o4[1] == inf && isnan(o4[2]) && isnan(o4[3]), "special values");
+    EXPECT(oracle_lse_axis0(NULL, 2, 4, o4, 1) < 0, "NULL rejected");
+  }
+  /* rows: exp(y) sums to 1, x - y is the row's LSE; softmax sums to 1 */
+  {
+    const int64_t rows = 4, cols = 37;
+    float *x = normal_array(rows * cols, 3.0, 11);
+    double *y = malloc(sizeof(double) * rows * cols), lse[4];
+    EXPECT(oracle_log_softmax_rows(x, rows, cols, y, lse, 2) == 0, "log_softmax status");
+    for (int64_t r = 0; r < rows; ++r) {
+      double t = 0.0;
+      for (int64_t c = 0; c < cols; ++c) t += exp(y[r * cols + c]);
+      EXPECT(close_to(t, 1.0, 1e-13), "sum exp(log_softmax) = 1");
+      EXPECT(close_to((double)x[r * cols + 5] - y[r * cols + 5], lse[r], 1e-13), "x - y = lse");
+    }
+    EXPECT(oracle_softmax_rows(x, rows, cols, y, 2) == 0, "softmax status");
+    for (int64_t r = 0; r < rows; ++r) {
+      double t = 0.0;
+      for (int64_t c = 0; c < cols; ++c) t += y[r * cols + c];
+      EXPECT(close_to(t, 1.0, 1e-13), "softmax sums to 1");
+    }
+    /* chunk partials merged = the row LSE, for chunkings that do and do not divide cols */
+    const int64_t chunks[3] = {1, 7, 37};
+    for (int k = 0; k < 3; ++k) {
+      const int64_t nch = (cols + chunks[k] - 1) / chunks[k];
+      double *m = malloc(sizeof(double) * rows * nch), *sm = malloc(sizeof(double) * rows * nch);
+      double merged[4];
+      EXPECT(oracle_lse_chunk_partials(x, rows, cols, chunks[k], m, sm, 2) == 0, "partials");
+      EXPECT(oracle_lse_merge(m, sm, rows, nch, merged, NULL, NULL) == 0, "merge");
+      for (int64_t r = 0; r < rows; ++r) EXPECT(close_to(merged[r], lse[r], 1e-13), "merged LSE");
+      free(m);
+      free(sm);
+    }
+    free(x);
+    free(y);
+  }
+  /* middle axis: each outer slab is an axis-0 problem; log_softmax columns sum to 1 */
+  {
+    const int64_t outer = 3, R = 4, inner = 5;
+    float *x = normal_array(outer * R * inner, 2.0, 12);
+    double out[15], ref[5], y[60];
+    EXPECT(oracle_lse_axis(x, outer, R, inner, out, 2) == 0, "lse_axis status");
+    for (int64_t o = 0; o < outer; ++o) {
+      EXPECT(oracle_lse_axis0(x + o * R * inner, R, inner, ref, 1) == 0, "slab status");
+      for (int64_t j = 0; j < inner; ++j)
+        EXPECT(close_to(out[o * inner + j], ref[j], 1e-15), "slab LSE");
+    }
+    EXPECT(oracle_log_softmax_axis(x, outer, R, inner, y, 2) == 0, "lsm_axis status");
+    for (int64_t o = 0; o < outer; ++o)
+      for (int64_t j = 0; j < inner; ++j) {
+        double t = 0.0;
+        for (int64_t r = 0; r < R; ++r) t += exp(y[(o * R + r) * inner + j]);
+        EXPECT(close_to(t, 1.0, 1e-13), "axis log_softmax sums to 1");
+      }
+    free(x);
+  }
+  /* conv with a delta filter copies a shifted input channel plus the bias;
+   * hardswish at its kinks; the chain with gamma = beta = 0 is LSE_c(conv) */
+  {
+    const int64_t N = 2, Cin = 3, H = 6, W = 7, Cout = 4, K = 3, Ho = 4, Wo = 5;
+    float *x = normal_array(N * Cin * H * W, 1.0, 13);
+    float w[4 * 3 * 9] = {0}, b[4] = {0.5f, -0.25f, 1.0f, 0.0f}, z[4] = {0};
+    for (int64_t o = 0; o < Cout; ++o) w[(o * Cin + o % Cin) * 9 + 4] = 1.0f;  /* centre tap */
+    double conv[2 * 4 * 4 * 5], chain[2 * 4 * 5], mean[4], rstd[4];
+    EXPECT(oracle_conv2d(x, w, b, N, Cin, H, W, Cout, K, conv, 2) == 0, "conv status");
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t o = 0; o < Cout; ++o)
+        for (int64_t h = 0; h < Ho; ++h)
+          for (int64_t q = 0; q < Wo; ++q)
+            EXPECT(conv[((n * Cout + o) * Ho + h) * Wo + q] ==
+                       (double)x[((n * Cin + o % Cin) * H + h + 1) * W + q + 1] + (double)b[o],
+                   "delta-filter conv");
+    EXPECT(oracle_hardswish(-3.0) == 0.0 && oracle_hardswish(3.0) == 3.0 &&
+               oracle_hardswish(0.0) == 0.0 && oracle_hardswish(-4.0) == 0.0 &&
+               oracle_hardswish(5.0) == 5.0 && close_to(oracle_hardswish(1.0), 4.0 / 6.0, 1e-15),
+           "hardswish kinks");
+    EXPECT(oracle_fused_chain(x, w, b, z, z, N, Cin, H, W, Cout, K, 2, 1e-5, chain, mean, rstd,
+                              2) == 0, "chain status");
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t p = 0; p < Ho * Wo; ++p) {
+        double m = -INFINITY, t = 0.0;
+        for (int64_t o = 0; o < Cout; ++o) m = fmax(m, conv[(n * Cout + o) * Ho * Wo + p]);
+        for (int64_t o = 0; o < Cout; ++o) t += exp(conv[(n * Cout + o) * Ho * Wo + p] - m);
+        EXPECT(close_to(chain[n * Ho * Wo + p], m + log(t), 1e-13), "chain = LSE_c(conv)");
+      }
+    for (int g = 0; g < 4; ++g) EXPECT(isfinite(mean[g]) && rstd[g] > 0.0, "group moments");
+    free(x);
+  }
+  printf("%-34s %s\n", "oracle functions", g_fail ? "FAIL" : "ok");
+}
+
 /* ------------------------------------------------------------- GPU cases */
 static void case_axis0(hipStream_t s) {
   const int64_t R = 7, inner = 1000, n = R * inner;
@@ -255,6 +383,12 @@ static void case_chain(hipStream_t s) {
 
 int main(int argc, char **argv) {
   const int host_only = argc > 1 && strcmp(argv[1], "--host") == 0;
+  const int oracle_only = argc > 1 && strcmp(argv[1], "--oracle") == 0;
+  if (oracle_only) {
+    oracle_checks();
+    printf(g_fail ? "FAILURES: %d\n" : "ALL OK\n", g_fail);
+    return g_fail ? 1 : 0;
+  }
   host_checks();
   if (!host_only) {
     hipStream_t s;
