@@ -494,8 +494,17 @@ __device__ __forceinline__ bool wait_stats(const ChainArgs &a, int64_t n, Lds &L
       wd[j] = (idx < words) ? load_pair_agent(ws + idx) : 1ull;
       missing |= (wd[j] == 0);
     }
-    for (int idx = threadIdx.x + NT * kHeldPer; idx < words; idx += NT)
-      missing |= (load_pair_agent(ws + idx) == 0);
+    // Words past the held ones (samples of more than kHeldPer x NT words):
+    // eight loads in flight per thread instead of one round trip per word.
+    int idx = threadIdx.x + NT * kHeldPer;
+    for (; idx + NT * 7 < words; idx += NT * 8) {
+      uint64_t w8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w8[u] = load_pair_agent(ws + idx + NT * u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) missing |= (w8[u] == 0);
+    }
+    for (; idx < words; idx += NT) missing |= (load_pair_agent(ws + idx) == 0);
     const bool late =
         it >= a.spin_limit || __builtin_amdgcn_s_memrealtime() - t0 > kChainWaitTicks;
     const uint64_t mb = __builtin_amdgcn_ballot_w64(missing);
@@ -544,8 +553,16 @@ __device__ __forceinline__ void merge_stats(const ChainArgs &a, int64_t n,
     const int idx = threadIdx.x + NT * j;
     if (idx < words) add(idx, wd[j]);
   }
-  for (int idx = threadIdx.x + NT * kHeldPer; idx < words; idx += NT)
-    add(idx, load_pair_agent(ws + idx));
+  // The rest in the same order, eight loads in flight at a time.
+  int idx = threadIdx.x + NT * kHeldPer;
+  for (; idx + NT * 7 < words; idx += NT * 8) {
+    uint64_t w8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w8[u] = load_pair_agent(ws + idx + NT * u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(idx + NT * u, w8[u]);
+  }
+  for (; idx < words; idx += NT) add(idx, load_pair_agent(ws + idx));
   for (int o = kWave / 2; o >= a.G; o >>= 1) {  // lanes l, l ^ o share a group while o >= G
     C += __shfl_xor(C, o);
     S1 += __shfl_xor(S1, o);
@@ -851,8 +868,15 @@ __device__ __forceinline__ void stats_table(const ChainArgs &a, int64_t n, float
 __global__ __launch_bounds__(kTeams * kThreads) void chain_merge_kernel(ChainArgs a) {
   __shared__ PairLds L;
   const int64_t n = a.block_base + blockIdx.x;  // here: first sample of the launch + index
+  // Every word was published by the statistics launch, which ended before
+  // this one started: nothing to wait for.
+  const uint64_t *ws = a.stats + n * a.tiles * a.G;
+  const int words = a.tiles * a.G;
   uint64_t wd[kHeldPer];
-  while (!wait_stats<kTeams * kThreads>(a, n, L, wd)) {  // published by the previous launch
+#pragma unroll
+  for (int j = 0; j < kHeldPer; ++j) {
+    const int idx = threadIdx.x + kTeams * kThreads * j;
+    wd[j] = (idx < words) ? load_pair_agent(ws + idx) : 1ull;
   }
   merge_stats<kTeams * kThreads>(a, n, wd, true, 1.0f, 0.0f, L);
 }
