@@ -113,8 +113,12 @@ lse_status_t log_softmax_axis(const float *x, float *y, int64_t outer,
  * for logsumexp) when outer > 1; otherwise LSE_ERR_SHAPE.  x may overlap
  * itself (it is only read).  The whole address range of the output may not
  * intersect that of x (LSE_ERR_OVERLAP, even where the two would interleave
- * without sharing an element).  The fast 16-byte path needs every stride and
- * inner to be a multiple of 4 and 16-byte aligned x and output. */
+ * without sharing an element).  Columns are read and written 4 at a time
+ * with 16-byte accesses whenever x and the output are 4-byte aligned and
+ * inner >= 4 (at any 4-byte phase and any stride: the last 4 columns of a
+ * run whose inner is not a multiple of 4 are read as one access and only the
+ * columns not covered before are written); other layouts take one value at a
+ * time. */
 lse_status_t lse_reduce_axis_strided(const float *x, float *out, int64_t outer,
                                      int64_t R, int64_t inner,
                                      int64_t x_stride_outer, int64_t x_stride_r,

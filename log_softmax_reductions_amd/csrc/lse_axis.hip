@@ -19,11 +19,18 @@
 // (axis_split_kernel below): each wave keeps at most 16 planes x 4 outputs per
 // lane in VGPRs, and the waves' (max, sum) pairs are merged in LDS.
 //
+// Layouts off the 16-byte grid (x or the output at another 4-byte phase, or
+// inner not a multiple of 4) keep the 4-column lanes: 16-byte accesses at
+// 4-byte alignment, and the last lane of each run reads the run's last 4
+// columns and writes only those its neighbour does not (ua_columns).
+//
 // Running state per output: m = max so far, s = sum of exp(v - c(m)) with the
 // shift c(m) = m when m is finite and 0 when m is +-inf (all values -inf, or
 // some +inf), which makes m + log(s) the literal log(sum(exp(v))) in every
 // case: -inf -> log 0 = -inf, +inf -> log(inf) = +inf, NaN -> NaN, and
 // (v - m) - log(s) the literal v - LSE for log_softmax.
+#include <type_traits>
+
 #include "lse_device.hpp"
 #include "lse_internal.hpp"
 
@@ -92,9 +99,13 @@ __device__ __forceinline__ void fold_block(const float (&v)[NB], float &m, float
   s = acc;
 }
 
+// Four floats as one 16-byte access at an address known only to be 4-byte
+// aligned (gfx950 accepts dword-aligned 16-byte accesses).
+typedef float v4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 // W consecutive values of one plane into column i of v (64-bit loads for W = 2,
-// 128-bit loads for W >= 4).
-template <int W, int RB, bool NT = LSE_AXIS0_NT_LOAD>
+// 128-bit loads for W >= 4; A4: p is only 4-byte aligned).
+template <int W, int RB, bool NT = LSE_AXIS0_NT_LOAD, bool A4 = false>
 __device__ __forceinline__ void load_plane(const float *p, float (&v)[W][RB], int i) {
   if constexpr (W == 1) {
     v[0][i] = *p;
@@ -104,7 +115,8 @@ __device__ __forceinline__ void load_plane(const float *p, float (&v)[W][RB], in
   } else {
 #pragma unroll
     for (int h = 0; h < W / 4; ++h) {
-      typedef float v4f __attribute__((ext_vector_type(4)));
+      typedef float v4a16 __attribute__((ext_vector_type(4)));
+      typedef std::conditional_t<A4, v4a4, v4a16> v4f;
       v4f t;
       if constexpr (NT)
         t = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(p + 4 * h));
@@ -146,11 +158,13 @@ __device__ __forceinline__ int64_t xcd_block(const float *x, int64_t plane_strid
 
 // One lane = W consecutive inner outputs of one outer index; NT threads per
 // workgroup (the launch's block size: a constant, where blockDim.x would be
-// read from the dispatch packet with a vector load).
-template <int W, int NT>
+// read from the dispatch packet with a vector load).  UA: W = 4 over a ragged
+// inner run (ceil(inner / 4) lanes per outer index; see ua_columns).
+template <int W, int NT, bool UA = false>
 __device__ __forceinline__ bool axis_item(const AxisDims &d, const float *x, int64_t plane_stride,
                                           int64_t &o, int64_t &q) {
-  const int64_t nq = d.inner / W;  // W > 1: inner % W == 0 by dispatch
+  // W > 1 and !UA: inner % W == 0 by dispatch
+  const int64_t nq = UA ? (d.inner + 3) / 4 : d.inner / W;
   const int64_t item = xcd_block(x, plane_stride) * NT + threadIdx.x;
   if (item >= d.outer * nq) return false;
   o = (d.outer == 1) ? 0 : item / nq;
@@ -158,20 +172,34 @@ __device__ __forceinline__ bool axis_item(const AxisDims &d, const float *x, int
   return true;
 }
 
+// Ragged inner runs (UA): lane q's 4 columns start at 4 q, except the last
+// lane of a run whose inner % 4 != 0, which reads the run's last 4 columns
+// (inner >= 4 by dispatch) and owns only the columns from `skip` on (the
+// others belong to its neighbour).  Every load stays inside the plane.
+__device__ __forceinline__ int64_t ua_columns(const AxisDims &d, int64_t q, int &skip) {
+  int64_t j0 = 4 * q;
+  skip = 0;
+  if (j0 + 4 > d.inner) {
+    skip = (int)(j0 + 4 - d.inner);
+    j0 = d.inner - 4;
+  }
+  return j0;
+}
+
 // Load planes r0 .. r0 + nb - 1 (nb <= RB, `stride` elements apart) of W
 // lanes' outputs into v, padding with the identity -inf; all loads are issued
 // before any is used.
-template <int RB, int W, bool NT = LSE_AXIS0_NT_LOAD>
+template <int RB, int W, bool NT = LSE_AXIS0_NT_LOAD, bool A4 = false>
 __device__ __forceinline__ void load_block(const float *base, int64_t stride, int64_t nb,
                                            float (&v)[W][RB]) {
   if (nb == RB) {
 #pragma unroll
-    for (int i = 0; i < RB; ++i) load_plane<W, RB, NT>(base + (int64_t)i * stride, v, i);
+    for (int i = 0; i < RB; ++i) load_plane<W, RB, NT, A4>(base + (int64_t)i * stride, v, i);
   } else {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if (i < nb) {
-        load_plane<W, RB, NT>(base + (int64_t)i * stride, v, i);
+        load_plane<W, RB, NT, A4>(base + (int64_t)i * stride, v, i);
       } else {
 #pragma unroll
         for (int w = 0; w < W; ++w) v[w][i] = -__builtin_inff();
@@ -202,10 +230,11 @@ __device__ __forceinline__ void store_w(float *p, const float (&r)[W]) {
 // adds one 32-bit byte offset, so a load is a scalar base plus a vector offset.
 // The 64-bit per-lane form leaves the compiler one 64-bit vector offset per
 // plane (RB = 32: 64 VGPRs, 208 in all, 2 waves per SIMD).
-template <int RB, bool NT = LSE_AXIS0_NT_LOAD>
+template <int RB, bool NT = LSE_AXIS0_NT_LOAD, bool A4 = false>
 __device__ __forceinline__ void load_block_s(const float *plane0, int64_t stride, int64_t nb,
                                              uint32_t off, float (&v)[4][RB]) {
-  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef float v4a16 __attribute__((ext_vector_type(4)));
+  typedef std::conditional_t<A4, v4a4, v4a16> v4f;
   typedef __attribute__((address_space(1))) const char gbyte;
   typedef __attribute__((address_space(1))) const v4f gv4f;
 #pragma unroll
@@ -230,17 +259,42 @@ __device__ __forceinline__ void load_block_s(const float *plane0, int64_t stride
   }
 }
 
+// Store 4 outputs at a 4-byte aligned p: one 16-byte store, or, for the last
+// lane of a ragged run (skip > 0), only the columns it owns.
+__device__ __forceinline__ void store4_ua(float *p, const float (&r)[4], int skip) {
+  if (skip == 0) {
+    *reinterpret_cast<v4a4 *>(p) = v4a4{r[0], r[1], r[2], r[3]};
+  } else {
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      if (w >= skip) p[w] = r[w];
+  }
+}
+
+// store4_ua with non-temporal 16-byte stores when NT.
+template <bool NT>
+__device__ __forceinline__ void store4_ua_nt(float *p, const float (&r)[4], int skip) {
+  if (NT && skip == 0)
+    __builtin_nontemporal_store(v4a4{r[0], r[1], r[2], r[3]}, reinterpret_cast<v4a4 *>(p));
+  else
+    store4_ua(p, r, skip);
+}
+
 // out[o, j] = LSE_r x[o, r, j].  OFF32: W = 4 and every lane's x offset fits
-// 32 bits as bytes (load_block_s).
-template <int RB, int W, bool STR, bool OFF32 = false>
+// 32 bits as bytes (load_block_s).  UA: W = 4 on a ragged or only 4-byte
+// aligned layout (ua_columns; 16-byte accesses at 4-byte alignment).
+template <int RB, int W, bool STR, bool OFF32 = false, bool UA = false>
 __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
     const float *__restrict__ x, float *__restrict__ out, AxisDims d) {
+  static_assert(!UA || W == 4, "ragged runs take 4 columns per lane");
   const int64_t st_xsr = STR ? d.xsr : d.inner;
   int64_t o, q;
-  if (!axis_item<W, kAxis0Threads>(d, x, st_xsr, o, q)) return;
+  if (!axis_item<W, kAxis0Threads, UA>(d, x, st_xsr, o, q)) return;
   const int64_t st_xso = STR ? d.xso : d.R * d.inner;
   const int64_t st_yso = STR ? d.yso : d.inner;
   const int64_t R = d.R;
+  int skip = 0;
+  const int64_t j0 = UA ? ua_columns(d, q, skip) : q * W;
   float m[W], s[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) {
@@ -249,18 +303,20 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
   }
   if constexpr (OFF32) {
     static_assert(W == 4, "scalar-base loads are 128-bit");
-    const uint32_t off = (uint32_t)(o * st_xso + q * W) * 4u;
+    const uint32_t off = (uint32_t)(o * st_xso + j0) * 4u;
     for (int64_t r0 = 0; r0 < R; r0 += RB) {
       float v[W][RB];
-      load_block_s<RB>(x + r0 * st_xsr, st_xsr, (R - r0 < RB) ? (R - r0) : RB, off, v);
+      load_block_s<RB, LSE_AXIS0_NT_LOAD != 0, UA>(x + r0 * st_xsr, st_xsr,
+                                                   (R - r0 < RB) ? (R - r0) : RB, off, v);
 #pragma unroll
       for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
     }
   } else {
-    const float *xo = x + o * st_xso + q * W;
+    const float *xo = x + o * st_xso + j0;
     for (int64_t r0 = 0; r0 < R; r0 += RB) {
       float v[W][RB];
-      load_block<RB, W>(xo + r0 * st_xsr, st_xsr, (R - r0 < RB) ? (R - r0) : RB, v);
+      load_block<RB, W, LSE_AXIS0_NT_LOAD != 0, UA>(xo + r0 * st_xsr, st_xsr,
+                                                    (R - r0 < RB) ? (R - r0) : RB, v);
 #pragma unroll
       for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
     }
@@ -268,7 +324,10 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
   float r[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) r[w] = m[w] + logf(s[w]);
-  store_w<W>(out + o * st_yso + q * W, r);
+  if constexpr (UA)
+    store4_ua(out + o * st_yso + j0, r, skip);
+  else
+    store_w<W>(out + o * st_yso + j0, r);
 }
 
 #ifndef LSE_AXIS_WALK
@@ -440,48 +499,62 @@ __global__ __launch_bounds__(kWalkThreads) void lse_axis_walk_kernel(
 #define LSE_AXIS_LSM_OFF32_NT 1   // the 32-bit-offset log_softmax kernel stores non-temporally
 #endif
 // Store 4 values at a uniform plane pointer plus a 32-bit lane byte offset
-// (the store form of load_block_s).
-template <bool NT>
-__device__ __forceinline__ void store4_s(float *plane, uint32_t off, const float (&r)[4]) {
-  typedef float v4f __attribute__((ext_vector_type(4)));
+// (the store form of load_block_s).  A4: only 4-byte aligned; skip > 0 (the
+// last lane of a ragged run, see ua_columns): only the columns from skip on.
+template <bool NT, bool A4 = false>
+__device__ __forceinline__ void store4_s(float *plane, uint32_t off, const float (&r)[4],
+                                         int skip = 0) {
+  typedef float v4a16 __attribute__((ext_vector_type(4)));
+  typedef std::conditional_t<A4, v4a4, v4a16> v4f;
   typedef __attribute__((address_space(1))) char gbyte_w;
   typedef __attribute__((address_space(1))) v4f gv4f_w;
+  typedef __attribute__((address_space(1))) float gf_w;
   gbyte_w *p = (gbyte_w *)plane;
   asm volatile("" : "+s"(p));
   uint32_t ok = off;
   asm volatile("" : "+v"(ok));
-  const v4f t = {r[0], r[1], r[2], r[3]};
-  if constexpr (NT)
-    __builtin_nontemporal_store(t, (gv4f_w *)(p + ok));
-  else
-    *(gv4f_w *)(p + ok) = t;
+  if (!A4 || skip == 0) {
+    const v4f t = {r[0], r[1], r[2], r[3]};
+    if constexpr (NT)
+      __builtin_nontemporal_store(t, (gv4f_w *)(p + ok));
+    else
+      *(gv4f_w *)(p + ok) = t;
+  } else {
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      if (w >= skip) *(gf_w *)(p + ok + 4 * w) = r[w];
+  }
 }
 
 // y[o, r, j] = x[o, r, j] - LSE_r' x[o, r', j].  With R <= RB the R values stay
 // in registers between the reduction and the write (one read, one write);
 // otherwise a streaming reduction pass and a write pass (two reads).  OFF32:
 // W = 4 and every lane's x and y offsets fit 32 bits as bytes (scalar plane
-// pointers, as in load_block_s).
-template <int RB, int W, bool STR, bool OFF32 = false>
+// pointers, as in load_block_s).  UA: W = 4 on a ragged or only 4-byte aligned
+// layout (ua_columns).
+template <int RB, int W, bool STR, bool OFF32 = false, bool UA = false>
 __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
     const float *__restrict__ x, float *__restrict__ y, AxisDims d) {
+  static_assert(!UA || W == 4, "ragged runs take 4 columns per lane");
   const int64_t st_xsr = STR ? d.xsr : d.inner;
   int64_t o, q;
-  if (!axis_item<W, kLsmThreads>(d, x, st_xsr, o, q)) return;
+  if (!axis_item<W, kLsmThreads, UA>(d, x, st_xsr, o, q)) return;
   const int64_t st_xso = STR ? d.xso : d.R * d.inner;
   const int64_t st_ysr = STR ? d.ysr : d.inner;
   const int64_t st_yso = STR ? d.yso : d.R * d.inner;
   const int64_t R = d.R;
-  const float *xo = x + o * st_xso + q * W;
-  float *yo = y + o * st_yso + q * W;
-  const uint32_t xoff = (uint32_t)(o * st_xso + q * W) * 4u;
-  const uint32_t yoff = (uint32_t)(o * st_yso + q * W) * 4u;
+  int skip = 0;
+  const int64_t j0 = UA ? ua_columns(d, q, skip) : q * W;
+  const float *xo = x + o * st_xso + j0;
+  float *yo = y + o * st_yso + j0;
+  const uint32_t xoff = (uint32_t)(o * st_xso + j0) * 4u;
+  const uint32_t yoff = (uint32_t)(o * st_yso + j0) * 4u;
   // Planes r0 .. r0 + nb - 1 into v.
   auto load = [&](int64_t r0, int64_t nb, float (&v)[W][RB]) {
     if constexpr (OFF32)
-      load_block_s<RB>(x + r0 * st_xsr, st_xsr, nb, xoff, v);
+      load_block_s<RB, LSE_AXIS0_NT_LOAD != 0, UA>(x + r0 * st_xsr, st_xsr, nb, xoff, v);
     else
-      load_block<RB, W>(xo + r0 * st_xsr, st_xsr, nb, v);
+      load_block<RB, W, LSE_AXIS0_NT_LOAD != 0, UA>(xo + r0 * st_xsr, st_xsr, nb, v);
   };
   float m[W], s[W];
 #pragma unroll
@@ -514,7 +587,9 @@ __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
 #pragma unroll
         for (int w = 0; w < W; ++w) r[w] = (v[w][i] - m[w]) - lns[w];
         if constexpr (OFF32)
-          store4_s<LSE_AXIS_LSM_OFF32_NT != 0>(y + (r0 + i) * st_ysr, yoff, r);
+          store4_s<LSE_AXIS_LSM_OFF32_NT != 0, UA>(y + (r0 + i) * st_ysr, yoff, r, skip);
+        else if constexpr (UA)
+          store4_ua(yo + (r0 + i) * st_ysr, r, skip);
         else
           store_w<W>(yo + (r0 + i) * st_ysr, r);
       }
@@ -547,9 +622,10 @@ __device__ __forceinline__ void store_w_nt(float *p, const float (&r)[W]) {
 // load to the log_softmax write (one read, one write of x's bytes), and a lane
 // holds RBW x W values instead of R x W, so more waves fit on a SIMD to keep
 // loads in flight.  Larger R reads x a second time for the write.
-template <int RBW, int W, int P, int G, bool LSM, bool STR>
+template <int RBW, int W, int P, int G, bool LSM, bool STR, bool UA = false>
 __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
     const float *__restrict__ x, float *__restrict__ out, AxisDims d) {
+  static_assert(!UA || W == 4, "ragged runs take 4 columns per lane");
   const int64_t st_xsr = STR ? d.xsr : d.inner;
   const int64_t st_xso = STR ? d.xso : d.R * d.inner;
   const int64_t st_ysr = STR ? d.ysr : d.inner;
@@ -563,7 +639,8 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wv = wid % P, grp = wid / P;
   const int64_t R = d.R;
-  const int64_t nq = d.inner / W;  // W > 1: inner % W == 0 by dispatch
+  // W > 1 and !UA: inner % W == 0 by dispatch; UA: ragged runs (ua_columns)
+  const int64_t nq = UA ? (d.inner + 3) / 4 : d.inner / W;
   const int64_t item = (xcd_block(x, st_xsr) * G + grp) * kWave + lane;
   const bool valid = item < d.outer * nq;
   int64_t o = 0, q = 0;
@@ -571,12 +648,14 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
     o = (d.outer == 1) ? 0 : item / nq;
     q = item - o * nq;
   }
+  int skip = 0;
+  const int64_t j0 = UA ? ua_columns(d, q, skip) : q * W;
   const int64_t per = (R + P - 1) / P;
   const int64_t r0 = (int64_t)wv * per;
   int64_t nr = R - r0;  // planes of this wave's slice (0 for the last waves when P > R)
   nr = nr < 0 ? 0 : (nr > per ? per : nr);
-  const int64_t xoff = o * st_xso + q * W + r0 * st_xsr;
-  const int64_t yoff = o * st_yso + q * W + r0 * st_ysr;  // == xoff when contiguous
+  const int64_t xoff = o * st_xso + j0 + r0 * st_xsr;
+  const int64_t yoff = o * st_yso + j0 + r0 * st_ysr;  // == xoff when contiguous
   const float *xs = x + xoff;
 
   float m[W], s[W];
@@ -589,7 +668,7 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   const bool resident = per <= RBW;  // uniform
   for (int64_t b = 0; b < nr; b += RBW) {
     const int64_t nb = valid ? ((nr - b < RBW) ? (nr - b) : RBW) : 0;
-    load_block<RBW, W, kSplitNt>(xs + b * st_xsr, st_xsr, nb, v);
+    load_block<RBW, W, kSplitNt, UA>(xs + b * st_xsr, st_xsr, nb, v);
 #pragma unroll
     for (int w = 0; w < W; ++w) fold_block<RBW>(v[w], m[w], s[w]);
   }
@@ -622,7 +701,10 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
       float r[W];
 #pragma unroll
       for (int w = 0; w < W; ++w) r[w] = m[w] + logf(s[w]);
-      store_w<W>(out + o * st_yso + q * W, r);
+      if constexpr (UA)
+        store4_ua(out + o * st_yso + j0, r, skip);
+      else
+        store_w<W>(out + o * st_yso + j0, r);
     }
   } else {
     float lns[W];
@@ -631,18 +713,19 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
     float *ys = out + yoff;
     for (int64_t b = 0; b < nr; b += RBW) {
       const int64_t nb = (nr - b < RBW) ? (nr - b) : RBW;
-      if (!resident) load_block<RBW, W, kSplitNt>(xs + b * st_xsr, st_xsr, nb, v);
+      if (!resident) load_block<RBW, W, kSplitNt, UA>(xs + b * st_xsr, st_xsr, nb, v);
 #pragma unroll
       for (int i = 0; i < RBW; ++i) {
         if (i < nb) {
           float r[W];
 #pragma unroll
           for (int w = 0; w < W; ++w) r[w] = (v[w][i] - m[w]) - lns[w];
-#if LSE_AXIS_NT_STORE
-          store_w_nt<W>(ys + (b + i) * st_ysr, r);
-#else
-          store_w<W>(ys + (b + i) * st_ysr, r);
-#endif
+          if constexpr (UA)
+            store4_ua_nt<LSE_AXIS_NT_STORE != 0>(ys + (b + i) * st_ysr, r, skip);
+          else if constexpr (LSE_AXIS_NT_STORE)
+            store_w_nt<W>(ys + (b + i) * st_ysr, r);
+          else
+            store_w<W>(ys + (b + i) * st_ysr, r);
         }
       }
     }
@@ -678,37 +761,53 @@ constexpr int lsm_groups_per_cu(int rb) {
   return !LSE_AXIS0_CAP ? 0 : rb == 32 ? 3 : rb == 16 ? 4 : rb == 8 ? 6 : 0;
 }
 
+#ifndef LSE_AXIS_UA
+#define LSE_AXIS_UA 1   // ragged / 4-byte aligned layouts take the 128-bit kernels (ua_columns)
+#endif
+// The register-block kernels: vec = every plane and output row on a 16-byte
+// boundary (inner and strides multiples of 4); otherwise, with 4-byte aligned
+// x and output, inner >= 4 and lane offsets within 32 bits, the same kernels
+// with 16-byte accesses at 4-byte alignment and the ragged last lane of each
+// run clamped (UA); else one column per lane.
 template <int RB, bool LSM, bool STR>
 hipError_t launch_rb(const float *x, float *out, const AxisDims &d, bool vec,
                      hipStream_t stream) {
-  const int64_t items = d.outer * (vec ? d.inner / kVecW : d.inner);
-  const dim3 grid((uint32_t)((items + kAxis0Threads - 1) / kAxis0Threads));
+  // Largest lane offsets, in bytes, of x and of y.
+  const int64_t xspan = ((d.outer - 1) * (STR ? d.xso : d.R * d.inner) + d.inner) * 4;
+  const int64_t yspan =
+      LSM ? ((d.outer - 1) * (STR ? d.yso : d.R * d.inner) + d.inner) * 4 : 0;
+  const bool off32 = LSE_AXIS0_SADDR && kVecW == 4 && xspan <= (int64_t)0xffffffff &&
+                     yspan <= (int64_t)0xffffffff;
+  const bool ua = !vec && LSE_AXIS_UA && off32 && d.inner >= 4 &&
+                  (((uintptr_t)x | (uintptr_t)out) & 3u) == 0;
+  const int64_t items = d.outer * (vec ? d.inner / kVecW : ua ? (d.inner + 3) / 4 : d.inner);
   if constexpr (LSM) {
-    const dim3 lgrid((uint32_t)((items + kLsmThreads - 1) / kLsmThreads));
-    // Largest lane offsets, in bytes, of x and y.
-    const int64_t xspan = ((d.outer - 1) * (STR ? d.xso : d.R * d.inner) + d.inner) * 4;
-    const int64_t yspan = ((d.outer - 1) * (STR ? d.yso : d.R * d.inner) + d.inner) * 4;
-    const size_t lds = vec ? occupancy_lds(lsm_groups_per_cu(RB)) : 0;
-    if (vec && kVecW == 4 && LSE_AXIS0_SADDR && xspan <= (int64_t)0xffffffff &&
-        yspan <= (int64_t)0xffffffff)
-      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, 4, STR, true>), lgrid, dim3(kLsmThreads), lds,
+    const dim3 grid((uint32_t)((items + kLsmThreads - 1) / kLsmThreads));
+    const size_t lds = (vec || ua) ? occupancy_lds(lsm_groups_per_cu(RB)) : 0;
+    if (vec && off32)
+      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, 4, STR, true>), grid, dim3(kLsmThreads), lds,
                          stream, x, out, d);
     else if (vec)
-      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, kVecW, STR>), lgrid, dim3(kLsmThreads), lds,
+      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, kVecW, STR>), grid, dim3(kLsmThreads), lds,
                          stream, x, out, d);
+    else if (ua)
+      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, 4, STR, true, true>), grid, dim3(kLsmThreads),
+                         lds, stream, x, out, d);
     else
-      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, 1, STR>), lgrid, dim3(kLsmThreads), 0, stream,
+      hipLaunchKernelGGL((log_softmax_axis_kernel<RB, 1, STR>), grid, dim3(kLsmThreads), 0, stream,
                          x, out, d);
   } else {
-    // Largest lane offset, in bytes, of the 128-bit kernel's loads.
-    const int64_t span = ((d.outer - 1) * (STR ? d.xso : d.R * d.inner) + d.inner) * 4;
-    const size_t lds = vec ? occupancy_lds(axis0_waves_per_cu(RB)) : 0;
-    if (vec && kVecW == 4 && LSE_AXIS0_SADDR && span <= (int64_t)0xffffffff)
+    const dim3 grid((uint32_t)((items + kAxis0Threads - 1) / kAxis0Threads));
+    const size_t lds = (vec || ua) ? occupancy_lds(axis0_waves_per_cu(RB)) : 0;
+    if (vec && off32)
       hipLaunchKernelGGL((lse_axis_kernel<RB, 4, STR, true>), grid, dim3(kAxis0Threads), lds, stream,
                          x, out, d);
     else if (vec)
       hipLaunchKernelGGL((lse_axis_kernel<RB, kVecW, STR>), grid, dim3(kAxis0Threads), lds, stream, x,
                          out, d);
+    else if (ua)
+      hipLaunchKernelGGL((lse_axis_kernel<RB, 4, STR, true, true>), grid, dim3(kAxis0Threads), lds,
+                         stream, x, out, d);
     else
       hipLaunchKernelGGL((lse_axis_kernel<RB, 1, STR>), grid, dim3(kAxis0Threads), 0, stream, x, out,
                          d);
@@ -717,24 +816,29 @@ hipError_t launch_rb(const float *x, float *out, const AxisDims &d, bool vec,
 }
 
 template <int RBW, int W, int P, bool LSM, bool STR>
-hipError_t launch_split(const float *x, float *out, const AxisDims &d, hipStream_t stream) {
+hipError_t launch_split(const float *x, float *out, const AxisDims &d, bool ua,
+                        hipStream_t stream) {
   constexpr int G = (LSE_AXIS_SPLIT_WAVES / P) > 1 ? (LSE_AXIS_SPLIT_WAVES / P) : 1;
-  const int64_t items = d.outer * (d.inner / W);
+  const int64_t items = d.outer * (ua ? (d.inner + 3) / 4 : d.inner / W);
   const dim3 grid((uint32_t)((items + kWave * G - 1) / (kWave * G)));
-  hipLaunchKernelGGL((axis_split_kernel<RBW, W, P, G, LSM, STR>), grid, dim3(kWave * P * G), 0,
-                     stream, x, out, d);
+  if (ua)
+    hipLaunchKernelGGL((axis_split_kernel<RBW, 4, P, G, LSM, STR, true>), grid,
+                       dim3(kWave * P * G), 0, stream, x, out, d);
+  else
+    hipLaunchKernelGGL((axis_split_kernel<RBW, W, P, G, LSM, STR>), grid, dim3(kWave * P * G), 0,
+                       stream, x, out, d);
   return hipGetLastError();
 }
 
 template <int RBW, bool LSM, bool STR>
-hipError_t launch_split_p(int P, const float *x, float *out, const AxisDims &d,
+hipError_t launch_split_p(int P, const float *x, float *out, const AxisDims &d, bool ua,
                           hipStream_t stream) {
   switch (P) {
-    case 1: return launch_split<RBW, kVecW, 1, LSM, STR>(x, out, d, stream);
-    case 2: return launch_split<RBW, kVecW, 2, LSM, STR>(x, out, d, stream);
-    case 4: return launch_split<RBW, kVecW, 4, LSM, STR>(x, out, d, stream);
-    case 8: return launch_split<RBW, kVecW, 8, LSM, STR>(x, out, d, stream);
-    default: return launch_split<RBW, kVecW, 16, LSM, STR>(x, out, d, stream);
+    case 1: return launch_split<RBW, kVecW, 1, LSM, STR>(x, out, d, ua, stream);
+    case 2: return launch_split<RBW, kVecW, 2, LSM, STR>(x, out, d, ua, stream);
+    case 4: return launch_split<RBW, kVecW, 4, LSM, STR>(x, out, d, ua, stream);
+    case 8: return launch_split<RBW, kVecW, 8, LSM, STR>(x, out, d, ua, stream);
+    default: return launch_split<RBW, kVecW, 16, LSM, STR>(x, out, d, ua, stream);
   }
 }
 
@@ -762,24 +866,28 @@ hipError_t launch_axis_t(const float *x, float *out, const AxisDims &d, hipStrea
   // Every plane and output row must start on the vector boundary too.
   const int64_t st = d.inner | d.xso | d.xsr | d.yso | (LSM ? d.ysr : 0);
   const bool vec = (st % kVecW == 0) && (a % 16 == 0);
+  // Off the 16-byte grid: the same 4-column lanes with 16-byte accesses at
+  // 4-byte alignment and each run's ragged end clamped (ua_columns).
+  const bool ua = !vec && LSE_AXIS_UA && kVecW == 4 && d.inner >= 4 && (a & 3u) == 0;
   constexpr int RBW = LSE_AXIS_SPLIT_RBW;
-  if (vec && LSM && R >= LSE_AXIS_LSM_SPLIT_MINR) {
+  if ((vec || ua) && LSM && R >= LSE_AXIS_LSM_SPLIT_MINR) {
     // log_softmax: the fewest waves (a power of two up to 16) whose slices of
     // ceil(R / P) planes fit RBW registers each, so x is read once up to
     // R = 16 RBW.
     int P = 1;
     while (P < 16 && (int64_t)P * RBW < R) P *= 2;
-    return launch_split_p<RBW, true, STR>(P, x, out, d, stream);
+    return launch_split_p<RBW, true, STR>(P, x, out, d, ua, stream);
   }
-  const int64_t waves = (d.outer * (d.inner / kVecW) + kWave - 1) / kWave;
-  if (vec && !LSM && R >= LSE_AXIS_LSE_SPLIT_MINR && waves <= LSE_AXIS_LSE_SPLIT_MAXWAVES) {
+  const int64_t waves = (d.outer * ((d.inner + kVecW - 1) / kVecW) + kWave - 1) / kWave;
+  if ((vec || ua) && !LSM && R >= LSE_AXIS_LSE_SPLIT_MINR &&
+      waves <= LSE_AXIS_LSE_SPLIT_MAXWAVES) {
     // logsumexp over long R with few outputs: one wave per 256 outputs would
     // leave most of the GPU idle, so P waves share each output run, each
     // streaming at least 8 planes.
     int P = 1;
     while (P < 16 && waves * P < LSE_AXIS_LSE_SPLIT_TARGET) P *= 2;
     while (P > 1 && R < 8 * (int64_t)P) P /= 2;
-    if (P > 1) return launch_split_p<RBW, false, STR>(P, x, out, d, stream);
+    if (P > 1) return launch_split_p<RBW, false, STR>(P, x, out, d, ua, stream);
   }
 #if LSE_AXIS_WALK
   if constexpr (!LSM) {
@@ -803,7 +911,8 @@ hipError_t launch_axis_t(const float *x, float *out, const AxisDims &d, hipStrea
   if (R <= 8 || LSE_AXIS0_RBMAX <= 8) return launch_rb<8, LSM, STR>(x, out, d, vec, stream);
   if (R <= 16 || LSE_AXIS0_RBMAX <= 16) return launch_rb<16, LSM, STR>(x, out, d, vec, stream);
   if (LSM && R > 32 && R <= 128) {
-    // Unaligned log_softmax keeps all R values in registers for the write:
+    // log_softmax that the 4-column lanes cannot take (inner < 4, or x or y
+    // off the 4-byte grid) keeps all R values in registers for the write:
     // narrow the per-lane vector so that R x W stays at 128 values (2 outputs
     // per lane up to 64 planes, 1 up to 128) instead of reading x twice.
     const bool two = R <= 64 && st % 2 == 0 && a % 8 == 0;

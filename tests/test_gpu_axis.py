@@ -205,3 +205,30 @@ def test_axis_lane_offsets_beyond_32_bits(orc, outer, R, inner):
     torch.cuda.synchronize()
     compare(y[:, :, cols].cpu().numpy(), orc.log_softmax_axis(xs), what="lsm 64-bit offsets")
     assert torch.logsumexp(y[:, :, w].double(), dim=1).abs().max().item() < 1e-5
+
+
+@pytest.mark.parametrize("outer,R,inner,off", [(1, 3, 5, 1), (2, 8, 4, 1), (3, 16, 37, 2),
+                                               (1, 20, 4099, 3), (2, 32, 1027, 1), (1, 32, 4096, 1),
+                                               (2, 40, 258, 0), (1, 70, 513, 2), (4, 5, 7, 0),
+                                               (1, 1, 9, 1), (3, 2, 3, 1), (1, 150, 66, 3)])
+def test_axis_ragged_and_offset_runs(orc, outer, R, inner, off):
+    """Layouts off the 16-byte grid (x and the output at a 4-byte phase, inner
+    not a multiple of 4): 16-byte accesses at 4-byte alignment, the last lane
+    of each run re-reading the run's last 4 columns and writing only its own.
+    Every output against the oracle; the floats around the output untouched."""
+    n = outer * R * inner
+    buf = inputs.normal((n + 8,), seed=outer * 131 + R * 17 + inner + off, sigma=3.0, device=DEV)
+    x = buf[off:off + n].view(outer, R, inner)
+    xc = x.cpu().numpy()
+    big = torch.full((outer * R * inner + 16,), 7.0, device=DEV)
+    out = big[off:off + outer * inner].view(outer, inner)
+    L.lse_reduce_axis(x, 1, out)
+    torch.cuda.synchronize()
+    compare(out.cpu().numpy(), orc.lse_axis(xc), what=f"lse ragged {outer}x{R}x{inner}+{off}")
+    assert torch.all(big[:off] == 7.0) and torch.all(big[off + outer * inner:] == 7.0)
+    big.fill_(7.0)
+    y = big[off:off + n].view(outer, R, inner)
+    L.log_softmax_axis(x, 1, y)
+    torch.cuda.synchronize()
+    compare(y.cpu().numpy(), orc.log_softmax_axis(xc), what=f"lsm ragged {outer}x{R}x{inner}+{off}")
+    assert torch.all(big[:off] == 7.0) and torch.all(big[off + n:] == 7.0)
