@@ -116,6 +116,7 @@ struct ChainArgs {
   float eps;
   uint32_t spin_limit;
   uint32_t block_base;   // pair index (over all samples) of this launch's first workgroup
+  uint32_t xcd_order;    // 1: consecutive pairs on one XCD (xcd_pair)
   uint32_t stage_first;  // pair index of the first pair whose conv tiles sit in `stage`
   float *stage;          // kStats with staging, kApplyStaged: conv tiles of this batch
   float *out;
@@ -884,8 +885,14 @@ __global__ __launch_bounds__(kTeams * kThreads) void chain_merge_kernel(ChainArg
 // Cold path of the sample's last arrival: finish the ndef pairs of sample n
 // deferred before it (their statistics are all published).  Out of line so
 // that nothing of it stays alive through the common path.
-__device__ __noinline__ void finish_deferred(const ChainArgs a, int64_t n, uint32_t ndef,
+// ChainArgs is read from the kernel's argument segment (the kernel's only
+// argument, at offset 0): passed by value (or by its address), the compiler
+// copied it to the call frame in scratch at the start of every workgroup (16
+// bytes per lane: 33 MB of writes per launch of the (128, 8, 128, 128) chain,
+// for a call that almost never happens).
+__device__ __noinline__ void finish_deferred(const ChainArgs *ap, int64_t n, uint32_t ndef,
                                              float *xs_team, const float *wl, PairLds *Lp) {
+  const ChainArgs &a = *ap;
   PairLds &L = *Lp;
   __shared__ uint32_t s_pair;
   const uint32_t groups = (uint32_t)(a.tiles + kTeams - 1) / kTeams;
@@ -922,6 +929,27 @@ __device__ __noinline__ void finish_deferred(const ChainArgs a, int64_t n, uint3
   }
 }
 
+#ifndef LSE_CHAIN_XCD
+#define LSE_CHAIN_XCD 1
+#endif
+// The pair of this workgroup within its launch.  Workgroups go to the 8 XCDs
+// round robin (b to XCD b % 8), each with its own L2, and neighbouring pairs
+// share the 2 input rows at their boundary (the 3 x 3 halo).  With xcd_order
+// the launch's pairs are dealt to the XCDs in 8 contiguous ranges, so that
+// neighbours, and all pairs of a sample, run on one XCD: pair
+// (b % 8) F + b / 8, F = grid / 8, for b < 8 F (a bijection; the last grid % 8
+// keep their index).  The host sets it when a sample's pairs fit half of one
+// XCD (the fused launch waits on a sample's pairs) or for launches that never
+// wait.
+__device__ __forceinline__ uint32_t xcd_pair(const ChainArgs &a) {
+  const uint32_t b = blockIdx.x;
+  if (LSE_CHAIN_XCD && a.xcd_order) {
+    const uint32_t f = gridDim.x / 8;
+    if (b < 8 * f) return (b % 8) * f + b / 8;
+  }
+  return b;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kTeams * kThreads)
 __attribute__((amdgpu_waves_per_eu(LSE_CHAIN_PAIR_WAVES_PER_EU)))
@@ -936,7 +964,7 @@ void conv_chain_pair_kernel(ChainArgs a) {
   // (128, 8, 128, 128), with bit-identical results.
   std::conditional_t<kWino, WinoW, WRegs<kTeams * kThreads>> wr;
   if constexpr (MODE != kApplyStaged) load_w(a.w, wr);
-  const uint32_t pair = a.block_base + blockIdx.x;
+  const uint32_t pair = a.block_base + xcd_pair(a);
   const uint32_t groups = (uint32_t)(a.tiles + kTeams - 1) / kTeams;  // workgroups per sample
   const int64_t n = pair / groups;
   const uint32_t p = pair - (uint32_t)n * groups;
@@ -1036,7 +1064,9 @@ void conv_chain_pair_kernel(ChainArgs a) {
   merge_stats<kTeams * kThreads>(a, n, wd, tA == 0, ga, be, L);  // barriers: s_ndef visible
   if (active) tile_epilogue_lds(a, n, tile, acc, valid, L, twave);
   const uint32_t ndef = s_ndef;
-  if (ndef != 0) finish_deferred(a, n, ndef, xs[team], wl, &L);
+  if (ndef != 0)
+    finish_deferred((const ChainArgs *)__builtin_amdgcn_kernarg_segment_ptr(), n, ndef, xs[team],
+                    wl, &L);
 }
 
 // Clear n 64-bit words (the header, the statistics words and the queue);
@@ -1161,6 +1191,10 @@ hipError_t launch_conv_chain(const float *x, const float *w, const float *b, con
   a.arrivals = reinterpret_cast<uint64_t *>(base + L.arrivals_off);
   a.queue = reinterpret_cast<uint32_t *>(base + L.queue_off);
   a.block_base = 0;
+  // Pairs of a sample on one XCD: always for the launches that never wait;
+  // for the fused launch only while a sample holds at most half of one XCD's
+  // resident pairs (its pairs then all run at once on that XCD).
+  a.xcd_order = (L.path != kPathFused || L.per_sample * 8 <= fused_pair_limit()) ? 1u : 0u;
   // The header, the statistics words and the queue start at 0 (the staging
   // area is written before it is read).
   const size_t clear_end = L.path == kPathStaged ? L.stage_off : L.total;
