@@ -387,10 +387,11 @@ __device__ __forceinline__ void fold_one(float v, float &m, float &s) {
 // column more than ~14 below or ~16 above c, a non-finite value or reference)
 // redoes its columns, one vector at a time, with the exact running fold of
 // fold_block, which also gives the special-value results.
-template <int VL, bool STR>
+template <int VL, bool STR, bool UA = false>
 __global__ __launch_bounds__(kWalkThreads) void lse_axis_walk_kernel(
     const float *__restrict__ x, float *__restrict__ out, AxisDims d) {
-  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef float v4a16 __attribute__((ext_vector_type(4)));
+  typedef std::conditional_t<UA, v4a4, v4a16> v4f;  // UA: 4-byte aligned planes
   constexpr int NV = 4 * VL;
   const int64_t st_xsr = STR ? d.xsr : d.inner;
   const int64_t st_xso = STR ? d.xso : d.R * d.inner;
@@ -405,16 +406,17 @@ __global__ __launch_bounds__(kWalkThreads) void lse_axis_walk_kernel(
   // The tile's first output; this lane's vector k starts jl + 4 kWave k past it.
   const int64_t tb = t * kWalkCols;
   const uint32_t jl = (uint32_t)wave * (kWave * 4 * VL) + 4 * lane;
-  // A ragged last tile clamps the vectors past the end onto the plane's last
-  // vector (inner % 4 == 0): loads stay in bounds, and those columns are not
-  // stored.  Offsets within a tile fit 32 bits, so every load is a uniform
-  // plane pointer plus a 32-bit lane offset.
+  // A ragged last tile clamps every vector that would pass the end onto the
+  // plane's last 4 columns (inner >= 4): loads stay in bounds, a vector wholly
+  // past the end is not stored, and one that straddles it (UA: inner % 4 != 0)
+  // stores only its own columns.  Offsets within a tile fit 32 bits, so every
+  // load is a uniform plane pointer plus a 32-bit lane offset.
   const bool full = tb + kWalkCols <= d.inner;  // uniform
   uint32_t off[VL];  // byte offsets within the tile
 #pragma unroll
   for (int k = 0; k < VL; ++k) {
     const uint32_t j = jl + 4 * kWave * k;
-    off[k] = 4 * ((full || tb + j < d.inner) ? j : (uint32_t)(d.inner - 4 - tb));
+    off[k] = 4 * ((full || tb + j + 4 <= d.inner) ? j : (uint32_t)(d.inner - 4 - tb));
   }
   const float *xt = x + o * st_xso + tb;
   const int64_t R = d.R;
@@ -464,11 +466,17 @@ __global__ __launch_bounds__(kWalkThreads) void lse_axis_walk_kernel(
 #pragma unroll
     for (int k = 0; k < VL; ++k) {
       const uint32_t j = jl + 4 * kWave * k;
-      if (full || tb + j < d.inner) {
+      if (full || tb + j + 4 <= d.inner) {
         v4f q;
 #pragma unroll
         for (int e = 0; e < 4; ++e) q[e] = lm + logf(s[4 * k + e]);
         *reinterpret_cast<v4f *>(op + j) = q;
+      } else if (UA && tb + j < d.inner) {
+        float q[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = lm + logf(s[4 * k + e]);
+        const uint32_t j4 = off[k] / 4;  // the run's last 4 columns
+        store4_ua(op + j4, q, (int)(j - j4));
       }
     }
   } else {
@@ -476,6 +484,7 @@ __global__ __launch_bounds__(kWalkThreads) void lse_axis_walk_kernel(
     for (int k = 0; k < VL; ++k) {
       const uint32_t j = jl + 4 * kWave * k;
       if (!(full || tb + j < d.inner)) continue;
+      const uint32_t j4 = off[k] / 4;  // == j unless the vector straddles the end
       float m4[4], s4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -483,14 +492,17 @@ __global__ __launch_bounds__(kWalkThreads) void lse_axis_walk_kernel(
         s4[e] = 0.0f;
       }
       for (int64_t r = 0; r < R; ++r) {
-        const v4f q = *reinterpret_cast<const v4f *>(xt + r * st_xsr + j);
+        const v4f q = *reinterpret_cast<const v4f *>(xt + r * st_xsr + j4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) fold_one(q[e], m4[e], s4[e]);
       }
-      v4f res;
+      float res[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) res[e] = m4[e] + logf(s4[e]);
-      *reinterpret_cast<v4f *>(op + j) = res;
+      if (j4 == j)
+        *reinterpret_cast<v4f *>(op + j) = v4f{res[0], res[1], res[2], res[3]};
+      else
+        store4_ua(op + j4, res, (int)(j - j4));
     }
   }
 }
@@ -845,15 +857,19 @@ hipError_t launch_split_p(int P, const float *x, float *out, const AxisDims &d, 
 // Launches the plane walk with VL vectors per lane if its tiling suits d
 // (true, launch status in e); false leaves the call to other kernels.
 template <int VL, bool STR>
-bool launch_walk(const float *x, float *out, const AxisDims &d, hipStream_t stream,
+bool launch_walk(const float *x, float *out, const AxisDims &d, bool ua, hipStream_t stream,
                  hipError_t &e) {
   constexpr int64_t cols = walk_cols<VL>();
   const int64_t tiles = (d.inner + cols - 1) / cols;
   if (d.outer * tiles < LSE_AXIS_WALK_MIN_BLOCKS || tiles * cols * 8 > d.inner * 9 ||
       d.outer * tiles > 0x7fffffff)
     return false;
-  hipLaunchKernelGGL((lse_axis_walk_kernel<VL, STR>), dim3((uint32_t)(d.outer * tiles)),
-                     dim3(kWalkThreads), 0, stream, x, out, d);
+  if (ua)
+    hipLaunchKernelGGL((lse_axis_walk_kernel<VL, STR, true>), dim3((uint32_t)(d.outer * tiles)),
+                       dim3(kWalkThreads), 0, stream, x, out, d);
+  else
+    hipLaunchKernelGGL((lse_axis_walk_kernel<VL, STR>), dim3((uint32_t)(d.outer * tiles)),
+                       dim3(kWalkThreads), 0, stream, x, out, d);
   e = hipGetLastError();
   return true;
 }
@@ -891,18 +907,18 @@ hipError_t launch_axis_t(const float *x, float *out, const AxisDims &d, hipStrea
   }
 #if LSE_AXIS_WALK
   if constexpr (!LSM) {
-    if (vec && R >= LSE_AXIS_WALK_MINR) {
+    if ((vec || ua) && R >= LSE_AXIS_WALK_MINR) {
       // Many wide aligned planes: the plane walk, with the widest tile that
       // still gives enough workgroups and at most 1/8 padding.  Up to 32
       // planes the register-block kernel below is as fast or faster.
       hipError_t e = hipErrorInvalidValue;
-      if (launch_walk<kWalkVl, STR>(x, out, d, stream, e)) return e;
+      if (launch_walk<kWalkVl, STR>(x, out, d, ua, stream, e)) return e;
 #if LSE_AXIS_WALK_NARROW
       // Half-width tiles (16 KiB per plane and workgroup) still beat the
       // register-block kernel (the channel layout (128, 64, 15876): 5890 ->
       // 6480 GB/s); quarter-width ones measured 8 % slower than it.
       if constexpr (kWalkVl >= 2)
-        if (launch_walk<kWalkVl / 2, STR>(x, out, d, stream, e)) return e;
+        if (launch_walk<kWalkVl / 2, STR>(x, out, d, ua, stream, e)) return e;
 #endif
     }
   }

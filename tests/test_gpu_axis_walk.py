@@ -131,3 +131,39 @@ def test_walk_half_tiles_strided(orc):
     torch.cuda.synchronize()
     ref = orc.lse_axis(x.contiguous().cpu().numpy())
     compare(out.cpu().numpy(), ref, what="walk half tiles strided")
+
+
+@pytest.mark.parametrize("outer,R,inner,off", [
+    (1, 40, NARROW, 1),               # every plane at a 4-byte phase
+    (1, 33, NARROW + 4 * 37 + 3, 0),  # inner % 4 == 3: the last vector straddles the end
+    (2, 48, 256 * TILE + 1025, 2),    # both, two outer slices
+    (128, 64, 126 * 126 + 1, 3),      # half-width tiles, ragged per slice
+])
+def test_walk_off_grid(orc, outer, R, inner, off):
+    """The walk with 16-byte accesses at 4-byte alignment: x and the output at
+    another 4-byte phase and inner not a multiple of 4 (the run's last vector
+    re-reads the last 4 columns and writes only its own); guard values around
+    the output."""
+    n = outer * R * inner
+    buf = inputs.normal((n + 4,), seed=outer * 17 + R + inner % 997, sigma=2.0, device=DEV)
+    x = buf[off:off + n].view(outer, R, inner)
+    big = torch.full((outer * inner + 8,), 5.0, device=DEV)
+    out = big[off:off + outer * inner].view(outer, inner)
+    L.lse_reduce_axis(x, 1, out)
+    torch.cuda.synchronize()
+    compare(out.cpu().numpy(), orc.lse_axis(x.cpu().numpy()), what=f"walk off-grid {outer}x{R}x{inner}+{off}")
+    assert torch.all(big[:off] == 5.0) and torch.all(big[off + outer * inner:] == 5.0)
+
+
+def test_walk_off_grid_exact_redo(orc):
+    """The exact redo on the straddling vector of an off-grid run."""
+    R, inner = 36, NARROW + 4 * 5 + 2
+    x = inputs.normal((1, R, inner), seed=93, device=DEV).cpu()
+    x[0, :, -1] -= 300.0                       # last column far below its lane's reference
+    x[0, 3, -2] = float("inf")
+    x[0, :, 11] += 500.0
+    buf = torch.empty(R * inner + 1, device=DEV)
+    xd = buf[1:].view(1, R, inner)
+    xd.copy_(x.to(DEV))
+    got = _lse(xd).cpu().numpy().ravel()
+    compare(got, orc.lse_axis(x.numpy()).ravel(), what="walk off-grid redo")
