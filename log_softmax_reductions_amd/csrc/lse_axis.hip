@@ -634,10 +634,11 @@ __device__ __forceinline__ void store_w_nt(float *p, const float (&r)[W]) {
 // load to the log_softmax write (one read, one write of x's bytes), and a lane
 // holds RBW x W values instead of R x W, so more waves fit on a SIMD to keep
 // loads in flight.  Larger R reads x a second time for the write.
-template <int RBW, int W, int P, int G, bool LSM, bool STR, bool UA = false>
+template <int RBW, int W, int P, int G, bool LSM, bool STR, bool UA = false, bool OFF32 = false>
 __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
     const float *__restrict__ x, float *__restrict__ out, AxisDims d) {
   static_assert(!UA || W == 4, "ragged runs take 4 columns per lane");
+  static_assert(!OFF32 || W == 4, "scalar plane pointers take 4 columns per lane");
   const int64_t st_xsr = STR ? d.xsr : d.inner;
   const int64_t st_xso = STR ? d.xso : d.R * d.inner;
   const int64_t st_ysr = STR ? d.ysr : d.inner;
@@ -669,6 +670,10 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   const int64_t xoff = o * st_xso + j0 + r0 * st_xsr;
   const int64_t yoff = o * st_yso + j0 + r0 * st_ysr;  // == xoff when contiguous
   const float *xs = x + xoff;
+  // OFF32: plane pointers in scalar registers plus one 32-bit lane byte
+  // offset each for x and y (load_block_s, store4_s).
+  const uint32_t xo32 = (uint32_t)((o * st_xso + j0) * 4);
+  const uint32_t yo32 = (uint32_t)((o * st_yso + j0) * 4);
 
   float m[W], s[W];
 #pragma unroll
@@ -680,7 +685,10 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   const bool resident = per <= RBW;  // uniform
   for (int64_t b = 0; b < nr; b += RBW) {
     const int64_t nb = valid ? ((nr - b < RBW) ? (nr - b) : RBW) : 0;
-    load_block<RBW, W, kSplitNt, UA>(xs + b * st_xsr, st_xsr, nb, v);
+    if constexpr (OFF32)
+      load_block_s<RBW, kSplitNt, UA>(x + (r0 + b) * st_xsr, st_xsr, nb, xo32, v);
+    else
+      load_block<RBW, W, kSplitNt, UA>(xs + b * st_xsr, st_xsr, nb, v);
 #pragma unroll
     for (int w = 0; w < W; ++w) fold_block<RBW>(v[w], m[w], s[w]);
   }
@@ -725,14 +733,21 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
     float *ys = out + yoff;
     for (int64_t b = 0; b < nr; b += RBW) {
       const int64_t nb = (nr - b < RBW) ? (nr - b) : RBW;
-      if (!resident) load_block<RBW, W, kSplitNt, UA>(xs + b * st_xsr, st_xsr, nb, v);
+      if (!resident) {
+        if constexpr (OFF32)
+          load_block_s<RBW, kSplitNt, UA>(x + (r0 + b) * st_xsr, st_xsr, nb, xo32, v);
+        else
+          load_block<RBW, W, kSplitNt, UA>(xs + b * st_xsr, st_xsr, nb, v);
+      }
 #pragma unroll
       for (int i = 0; i < RBW; ++i) {
         if (i < nb) {
           float r[W];
 #pragma unroll
           for (int w = 0; w < W; ++w) r[w] = (v[w][i] - m[w]) - lns[w];
-          if constexpr (UA)
+          if constexpr (OFF32)
+            store4_s<LSE_AXIS_NT_STORE != 0, UA>(out + (r0 + b + i) * st_ysr, yo32, r, skip);
+          else if constexpr (UA)
             store4_ua_nt<LSE_AXIS_NT_STORE != 0>(ys + (b + i) * st_ysr, r, skip);
           else if constexpr (LSE_AXIS_NT_STORE)
             store_w_nt<W>(ys + (b + i) * st_ysr, r);
@@ -827,13 +842,33 @@ hipError_t launch_rb(const float *x, float *out, const AxisDims &d, bool vec,
   return hipGetLastError();
 }
 
+#ifndef LSE_AXIS_SPLIT_OFF32
+#define LSE_AXIS_SPLIT_OFF32 1   // the strided plane split with scalar plane pointers (load_block_s)
+#endif
 template <int RBW, int W, int P, bool LSM, bool STR>
 hipError_t launch_split(const float *x, float *out, const AxisDims &d, bool ua,
                         hipStream_t stream) {
   constexpr int G = (LSE_AXIS_SPLIT_WAVES / P) > 1 ? (LSE_AXIS_SPLIT_WAVES / P) : 1;
   const int64_t items = d.outer * (ua ? (d.inner + 3) / 4 : d.inner / W);
   const dim3 grid((uint32_t)((items + kWave * G - 1) / (kWave * G)));
-  if (ua)
+  // Largest lane offsets, in bytes, of x and of the output.
+  const int64_t xspan = ((d.outer - 1) * (STR ? d.xso : d.R * d.inner) + d.inner) * 4;
+  const int64_t yspan =
+      ((d.outer - 1) * (STR ? d.yso : (LSM ? d.R * d.inner : d.inner)) + d.inner) * 4;
+  // Strided calls only: with separate x and y strides the 64-bit form keeps
+  // both planes' addresses live (144-168 VGPRs, a spill at 16 waves), and the
+  // scalar plane pointers measured 8-49 % faster on padded views ((4, 256,
+  // 65536) with a 64-float pad: 3539 -> 5270 GB/s); on dense calls they ran
+  // up to 5 % slower ((128, 64, 15876): 214 -> 224 us), so those keep it.
+  const bool off32 = LSE_AXIS_SPLIT_OFF32 && STR && W == 4 && xspan <= (int64_t)0xffffffff &&
+                     yspan <= (int64_t)0xffffffff;
+  if (off32 && ua)
+    hipLaunchKernelGGL((axis_split_kernel<RBW, 4, P, G, LSM, STR, true, true>), grid,
+                       dim3(kWave * P * G), 0, stream, x, out, d);
+  else if (off32)
+    hipLaunchKernelGGL((axis_split_kernel<RBW, 4, P, G, LSM, STR, false, true>), grid,
+                       dim3(kWave * P * G), 0, stream, x, out, d);
+  else if (ua)
     hipLaunchKernelGGL((axis_split_kernel<RBW, 4, P, G, LSM, STR, true>), grid,
                        dim3(kWave * P * G), 0, stream, x, out, d);
   else
