@@ -29,6 +29,12 @@
 //     then reloads its own chunk; the first writer of a slot wins.  No global
 //     counter is touched and no workgroup can wait on one that never starts,
 //     whatever the dispatch order.
+//   * Rows off the 16-byte grid (odd lengths, views at another 4-byte phase,
+//     pitches not a multiple of 4): the register tile is framed on the output
+//     row's first 128-byte line, so the stores stay aligned 16-byte buffer
+//     stores, and the loads read x at its own 4-byte phase as 16-byte
+//     accesses; the at most 31 columns before the frame and 3 after its last
+//     whole vector are one extra value per lane for lanes 0..33 of wave 0.
 //   * The write is y = (x - M) - log(S): x - M is exact for the large entries,
 //     so the result keeps its accuracy when |M| is large.
 //   * A launch covers at most kMaxRowsWorkgroups workgroups (its work-item
