@@ -407,6 +407,66 @@ __device__ __forceinline__ bool wave_wait_pairs(const uint64_t *pairs, int64_t k
   }
 }
 
+#ifndef LSE_ROWS_WAVE_MAX
+#define LSE_ROWS_WAVE_MAX 1024   // rows up to this many columns take one wave each
+#endif
+constexpr int kWaveRowsPerGroup = 4;  // one wave per row, 4 rows per workgroup
+
+// Short rows (at most 64 VPL columns, 16-byte aligned with cols and pitches
+// multiples of 4): one wave per row.  Lane l holds the float4 vectors
+// q kWave + l (each load instruction of the wave one contiguous 1 KiB), the
+// row's max and sum are wave reductions (DPP and permlane swaps) with no LDS
+// and no barrier, and the write comes from registers: against one 512-lane
+// workgroup per row, no cross-wave step and no idle lanes for rows of a few
+// thousand columns.  Same pair arithmetic as chunk_pair.
+template <int VPL, bool SOFTMAX>
+__global__ __launch_bounds__(kWave * kWaveRowsPerGroup) void rows_wave_kernel(
+    const float *__restrict__ x, float *__restrict__ y, int64_t rows, int64_t cols, int64_t ldx,
+    int64_t ldy) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t row = (int64_t)blockIdx.x * kWaveRowsPerGroup + threadIdx.x / kWave;
+  if (row >= rows) return;  // whole waves
+  const float *xr = x + row * ldx;
+  float *yr = y + row * ldy;
+  float v[VPL];
+#pragma unroll
+  for (int q = 0; q < VPL / 4; ++q) {
+    const int64_t idx = ((int64_t)q * kWave + lane) * 4;
+    if (idx < cols) {  // cols % 4 == 0: a vector is wholly in or out
+#if LSE_ROWS_NT_LOAD
+      const v4f f = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(xr + idx));
+#else
+      const v4f f = *reinterpret_cast<const v4f *>(xr + idx);
+#endif
+      v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * q + r] = -__builtin_inff();
+    }
+  }
+  float lm = v[0];
+#pragma unroll
+  for (int e = 1; e < VPL; ++e) lm = fmaxf(lm, v[e]);
+  const float M = wave_allreduce(lm, OpMax{});
+  float ls = 0.0f;
+  if (is_finite(M)) {  // uniform: M is the same in every lane
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) ls += exp_base2(v[e] - M);
+  } else {
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) ls += pair_term_nonfinite(v[e], M);
+  }
+  const float S = wave_allreduce(ls, OpSum{});
+  const float k = out_scale<SOFTMAX>(S);
+#pragma unroll
+  for (int q = 0; q < VPL / 4; ++q) {
+    const int64_t idx = ((int64_t)q * kWave + lane) * 4;
+    if (idx < cols)
+      store4(yr + idx, out_value<SOFTMAX>(v[4 * q], M, k), out_value<SOFTMAX>(v[4 * q + 1], M, k),
+             out_value<SOFTMAX>(v[4 * q + 2], M, k), out_value<SOFTMAX>(v[4 * q + 3], M, k));
+  }
+}
+
 // One workgroup = one (row, chunk).  SPLIT: rows of nchunks > 1 chunks whose
 // pairs are merged through the workspace.  !SPLIT: one workgroup per row.
 //
@@ -962,6 +1022,25 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
   const RowsPlan p = rows_plan(cols);
   const bool vec = (cols % 4 == 0) && (p.chunk % 4 == 0) && (ldx % 4 == 0) &&
                    (ldy % 4 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0);
+  if (p.nchunks == 1 && vec && cols <= LSE_ROWS_WAVE_MAX) {
+    // one wave per row (rows_wave_kernel)
+    const int vw = cols <= 4 * kWave ? 4 : cols <= 8 * kWave ? 8 : cols <= 16 * kWave ? 16
+                 : cols <= 32 * kWave ? 32 : 64;
+    return for_row_batches(rows, kMaxRowsWorkgroups * 2, [&](int64_t r0, int64_t nr) {
+      const dim3 grid((uint32_t)((nr + kWaveRowsPerGroup - 1) / kWaveRowsPerGroup));
+      const dim3 block(kWave * kWaveRowsPerGroup);
+      const float *xb = x + r0 * ldx;
+      float *yb = y + r0 * ldy;
+      switch (vw) {
+        case 4: hipLaunchKernelGGL((rows_wave_kernel<4, SOFTMAX>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy); break;
+        case 8: hipLaunchKernelGGL((rows_wave_kernel<8, SOFTMAX>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy); break;
+        case 16: hipLaunchKernelGGL((rows_wave_kernel<16, SOFTMAX>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy); break;
+        case 32: hipLaunchKernelGGL((rows_wave_kernel<32, SOFTMAX>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy); break;
+        default: hipLaunchKernelGGL((rows_wave_kernel<64, SOFTMAX>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy); break;
+      }
+      return hipGetLastError();
+    });
+  }
   if (p.nchunks == 1) {
     return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
       return launch_rows_vpl<false, SOFTMAX>(vpl_for(cols), vec, dim3((uint32_t)nr), x + r0 * ldx,

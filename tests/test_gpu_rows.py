@@ -44,6 +44,44 @@ def test_rows_misaligned(orc, cols):
     compare(_lsm(x), ref, what="misaligned")
 
 
+@pytest.mark.parametrize("cols", [4, 256, 1000, 1024])
+@pytest.mark.parametrize("softmax", [False, True])
+def test_rows_one_wave_per_row_special_values(orc, cols, softmax):
+    """Short aligned rows run one wave per row (4 rows per workgroup): special
+    values in every position, a partial last workgroup (9 rows), and the
+    rows' results against the oracle."""
+    x = inputs.normal((9, cols), seed=cols + 7, device=DEV).cpu()
+    x[0, :] = -float("inf")                       # all -inf
+    x[1, cols // 2] = float("inf")                # +inf
+    x[2, cols - 1] = float("nan")                 # NaN
+    x[3, :] = -float("inf"); x[3, 0] = 2.5        # one finite entry
+    x[4, :] = 3.0                                 # equal values
+    x[5, 1] = 1e30                                # huge
+    x[6, ::2] = -float("inf")
+    xd = x.to(DEV)
+    if softmax:
+        y = L.softmax_rows(xd)
+        torch.cuda.synchronize()
+        compare(y.cpu().numpy(), orc.softmax_rows(x.numpy()), what=f"wave softmax {cols}",
+                rtol=1e-5, atol=1e-37)
+    else:
+        ref, _ = orc.log_softmax_rows(x.numpy())
+        compare(_lsm(xd), ref, what=f"wave rows {cols}")
+
+
+def test_rows_one_wave_per_row_many_rows(orc):
+    """200003 rows of 256: every row's log_softmax sums to 1, sampled rows
+    (first, last, partial last workgroup) against the oracle."""
+    rows, cols = 200003, 256
+    x = inputs.normal((rows, cols), seed=11, sigma=3.0, device=DEV)
+    y = L.log_softmax_rows(x)
+    torch.cuda.synchronize()
+    assert (torch.logsumexp(y.double(), 1)).abs().max().item() < 1e-5
+    idx = [0, 1, 2, 3, 4, rows // 2, rows - 4, rows - 3, rows - 2, rows - 1]
+    ref, _ = orc.log_softmax_rows(x[idx].cpu().numpy())
+    compare(y[idx].cpu().numpy(), ref, what="wave many rows")
+
+
 def test_rows_special_values(orc):
     cols = 40000   # split across 3 workgroups
     x = inputs.normal((8, cols), seed=5, device=DEV).cpu()
