@@ -21,8 +21,8 @@ rank 0 prints ONE JSON line.
 Flags: --gpus N (only 1 is supported: this build runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --no-secondary,
 --only {rows_large,axis0_large,axis0_walk,conv_chain,softmax_large,axis_chain_layout,copy,
-        copy_tile,copy_stream,rows_odd_cols,rows_offset_view,chain_600x520_recompute,
-        chain_600x520_staged,rows_large_reread}
+        copy_tile,copy_stream,copy_tile_1_per_cu,rows_odd_cols,rows_offset_view,
+        chain_600x520_recompute,chain_600x520_staged,rows_large_reread}
 to run just that kernel
 (for profiler runs; prints timing only).
 """
@@ -473,18 +473,23 @@ def run_only(which, steps, warmup):
         a = torch.empty(1 << 28, device="cuda")
         c = torch.empty_like(a)
         wall, ev = timed_launches(lambda: c.copy_(a), steps, warmup)
-    elif which in ("copy_tile", "copy_stream"):
+    elif which in ("copy_tile", "copy_stream", "copy_tile_1_per_cu"):
         # our copy kernels on the workload's bytes (the copy ceiling)
         import ctypes
         lib = ctypes.CDLL(BENCH_COPY_LIB)
         lib.bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                    ctypes.c_int, ctypes.c_void_p]
+        lib.bench_copy_capped.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_int, ctypes.c_void_p]
         a = inputs.make("rows_large", "cuda")
         c = torch.empty_like(a)
-        v = 0 if which == "copy_tile" else 1
-        wall, ev = timed_launches(
-            lambda: lib.bench_copy(a.data_ptr(), c.data_ptr(), a.numel(), v,
-                                   torch.cuda.current_stream().cuda_stream), steps, warmup)
+        st = torch.cuda.current_stream().cuda_stream
+        if which == "copy_tile_1_per_cu":
+            run = lambda: lib.bench_copy_capped(a.data_ptr(), c.data_ptr(), a.numel(), 81 * 1024, st)
+        else:
+            v = 0 if which == "copy_tile" else 1
+            run = lambda: lib.bench_copy(a.data_ptr(), c.data_ptr(), a.numel(), v, st)
+        wall, ev = timed_launches(run, steps, warmup)
     elif which in ("rows_odd_cols", "rows_offset_view"):
         cols, off = (COLS - 1, 0) if which == "rows_odd_cols" else (COLS, 1)
         buf = inputs.normal((ROWS * cols + off,), seed=41, device="cuda")
