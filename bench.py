@@ -22,7 +22,8 @@ Flags: --gpus N (only 1 is supported: this build runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline, --no-secondary,
 --only {rows_large,axis0_large,axis0_walk,conv_chain,softmax_large,axis_chain_layout,copy,
         copy_tile,copy_stream,copy_tile_1_per_cu,rows_odd_cols,rows_offset_view,
-        chain_600x520_recompute,chain_600x520_staged,rows_large_reread}
+        chain_600x520_recompute,chain_600x520_staged,rows_large_reread,short_rows_128,
+        short_rows_100}
 to run just that kernel
 (for profiler runs; prints timing only).
 """
@@ -237,6 +238,9 @@ def copy_ceiling(x, y, steps=5, warmup=2):
     return max(v for k, v in out.items() if k != "torch_copy_"), out
 
 
+SHORT_ROWS = 1 << 20
+
+
 def bench_secondary(steps=10, warmup=3):
     import torch
     import log_softmax_reductions_amd as L
@@ -381,6 +385,25 @@ def bench_secondary(steps=10, warmup=3):
                                  "ms": round(avg, 4), "GB/s": round(8 * x.numel() / avg / 1e6, 1),
                                  "hbm_frac": round(8 * x.numel() / avg / 1e6 / HBM_PEAK_GBS, 4)}
     del x, y
+    # short rows over the last dim (a segment of lanes per row, several rows per
+    # wave): 128 columns (16-byte rows) and 100 columns (4-byte loads)
+    for cols in (128, 100):
+        x = inputs.normal((SHORT_ROWS, cols), seed=17 + cols, sigma=2.0, device="cuda")
+        o = torch.empty((SHORT_ROWS,), device="cuda")
+        y = torch.empty_like(x)
+        _, ev = timed_launches(lambda: L.lse_reduce_axis(x, 1, o), steps, warmup)
+        lse_ms = sum(ev) / len(ev)
+        _, ev = timed_launches(lambda: L.log_softmax_axis(x, 1, y), steps, warmup)
+        lsm_ms = sum(ev) / len(ev)
+        nb_lse, nb_lsm = 4 * (x.numel() + o.numel()), 8 * x.numel()
+        out[f"short_rows_{cols}"] = {
+            "workload": f"logsumexp and log_softmax dim=1 of ({SHORT_ROWS},{cols}) fp32 N(0,4)",
+            "lse_ms": round(lse_ms, 4), "lse_GB/s": round(nb_lse / lse_ms / 1e6, 1),
+            "lse_hbm_frac": round(nb_lse / lse_ms / 1e6 / HBM_PEAK_GBS, 4),
+            "log_softmax_ms": round(lsm_ms, 4),
+            "log_softmax_GB/s": round(nb_lsm / lsm_ms / 1e6, 1),
+            "log_softmax_hbm_frac": round(nb_lsm / lsm_ms / 1e6 / HBM_PEAK_GBS, 4)}
+        del x, o, y
     # small cases: hot latency per call, eagerly from Python (host launch
     # included) and as back-to-back calls replayed from a HIP graph
     x = inputs.make("rows_small", "cuda")
@@ -442,6 +465,14 @@ def run_only(which, steps, warmup):
         o = torch.empty((128, 1, 126, 126), device="cuda")
         wall, ev = timed_launches(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, o),
                                   steps, warmup)
+    elif which in ("short_rows_128", "short_rows_100"):
+        # logsumexp then log_softmax over the last dim of (2^20, cols)
+        cols = int(which.rsplit("_", 1)[1])
+        x = inputs.normal((SHORT_ROWS, cols), seed=17 + cols, sigma=2.0, device="cuda")
+        o = torch.empty((SHORT_ROWS,), device="cuda")
+        y = torch.empty_like(x)
+        timed_launches(lambda: L.lse_reduce_axis(x, 1, o), steps, warmup)
+        wall, ev = timed_launches(lambda: L.log_softmax_axis(x, 1, y), steps, warmup)
     elif which in ("chain_600x520_recompute", "chain_600x520_staged"):
         # the two-launch chain on samples too large for one fused launch
         x, w, b, g, be = inputs.conv_chain_inputs(N=8, H=600, W=520, seed=5, device="cuda")

@@ -1019,20 +1019,12 @@ hipError_t launch_axis(const float *x, float *out, const AxisDims &d, hipStream_
 
 }  // namespace
 
-#ifndef LSE_AXIS_ROWS_MINR_LSE
-#define LSE_AXIS_ROWS_MINR_LSE 512
-#endif
-#ifndef LSE_AXIS_ROWS_MINR_LSM
-#define LSE_AXIS_ROWS_MINR_LSM 256
-#endif
 // A reduction over a contiguous last axis (inner = 1, unit R stride) is a row
-// reduction: from a few hundred values per row on, one workgroup per row
-// reads the row as one contiguous span, where the axis kernels would give each
-// lane a row of its own.
+// reduction: the row kernels read each row as contiguous spans (short rows a
+// segment of a wave each, long ones a workgroup or several), where the axis
+// kernels would give each lane a row of its own and read it value by value.
 static bool as_rows(const AxisDims &d, bool lsm) {
-  const int64_t minr = lsm ? LSE_AXIS_ROWS_MINR_LSM : LSE_AXIS_ROWS_MINR_LSE;
-  return d.inner == 1 && d.xsr == 1 && (!lsm || d.ysr == 1) && d.R >= minr &&
-         d.outer <= 0x7fffffff;
+  return d.inner == 1 && d.xsr == 1 && (!lsm || d.ysr == 1) && d.outer <= 0x7fffffff;
 }
 
 hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream) {

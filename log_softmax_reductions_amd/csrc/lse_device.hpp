@@ -44,22 +44,35 @@ struct OpSum {
   __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
 };
 
-// All 64 lanes end with op over the wave, bitwise identical in every lane
-// (each step combines the same two values, only in swapped operand order).
+// All-reduce inside aligned segments of G lanes (G a power of two, 1..64):
+// every lane ends with op over its segment, bitwise identical in every lane of
+// the segment (each step combines the same two values, only in swapped operand
+// order), and no value crosses a segment boundary.
+template <int G, class Op>
+__device__ __forceinline__ float seg_allreduce(float v, Op op) {
+  static_assert(G >= 1 && G <= kWave && (G & (G - 1)) == 0, "segment of 1..64 lanes");
+  if constexpr (G >= 2) v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (G >= 4) v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (G >= 8) v = op(v, dpp_mov<0x141>(v));  // row_half_mirror: the quads of 8
+  if constexpr (G >= 16) v = op(v, dpp_mov<0x140>(v)); // row_mirror: halves of a 16-lane row
+  if constexpr (G >= 32) {
+    // v_permlane16_swap: the returned pair holds, in every lane, the values of
+    // rows (0,1) or (2,3) of its row pair, so op of the two is the 32-lane result.
+    auto p = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+    v = op(bitsf(p[0]), bitsf(p[1]));
+  }
+  if constexpr (G >= 64) {
+    // v_permlane32_swap: the pair holds lane l % 32 and lane 32 + l % 32.
+    auto q = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
+    v = op(bitsf(q[0]), bitsf(q[1]));
+  }
+  return v;
+}
+
+// All 64 lanes end with op over the wave.
 template <class Op>
 __device__ __forceinline__ float wave_allreduce(float v, Op op) {
-  v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
-  v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
-  v = op(v, dpp_mov<0x141>(v));  // row_half_mirror: pairs the quads of 8 lanes
-  v = op(v, dpp_mov<0x140>(v));  // row_mirror: pairs the halves of a 16-lane row
-  // v_permlane16_swap: the returned pair holds, in every lane, the values of
-  // rows (0,1) or (2,3) of its row pair, so op of the two is the 32-lane result.
-  auto p = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
-  v = op(bitsf(p[0]), bitsf(p[1]));
-  // v_permlane32_swap: the pair holds lane l % 32 and lane 32 + l % 32.
-  auto q = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
-  v = op(bitsf(q[0]), bitsf(q[1]));
-  return v;
+  return seg_allreduce<kWave>(v, op);
 }
 
 // Workgroup all-reduce of NW waves through `lds` (NW floats).  Every thread

@@ -407,66 +407,6 @@ __device__ __forceinline__ bool wave_wait_pairs(const uint64_t *pairs, int64_t k
   }
 }
 
-#ifndef LSE_ROWS_WAVE_MAX
-#define LSE_ROWS_WAVE_MAX 1024   // rows up to this many columns take one wave each
-#endif
-constexpr int kWaveRowsPerGroup = 4;  // one wave per row, 4 rows per workgroup
-
-// Short rows (at most 64 VPL columns, 16-byte aligned with cols and pitches
-// multiples of 4): one wave per row.  Lane l holds the float4 vectors
-// q kWave + l (each load instruction of the wave one contiguous 1 KiB), the
-// row's max and sum are wave reductions (DPP and permlane swaps) with no LDS
-// and no barrier, and the write comes from registers: against one 512-lane
-// workgroup per row, no cross-wave step and no idle lanes for rows of a few
-// thousand columns.  Same pair arithmetic as chunk_pair.
-template <int VPL, bool SOFTMAX>
-__global__ __launch_bounds__(kWave * kWaveRowsPerGroup) void rows_wave_kernel(
-    const float *__restrict__ x, float *__restrict__ y, int64_t rows, int64_t cols, int64_t ldx,
-    int64_t ldy) {
-  const int lane = threadIdx.x % kWave;
-  const int64_t row = (int64_t)blockIdx.x * kWaveRowsPerGroup + threadIdx.x / kWave;
-  if (row >= rows) return;  // whole waves
-  const float *xr = x + row * ldx;
-  float *yr = y + row * ldy;
-  float v[VPL];
-#pragma unroll
-  for (int q = 0; q < VPL / 4; ++q) {
-    const int64_t idx = ((int64_t)q * kWave + lane) * 4;
-    if (idx < cols) {  // cols % 4 == 0: a vector is wholly in or out
-#if LSE_ROWS_NT_LOAD
-      const v4f f = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(xr + idx));
-#else
-      const v4f f = *reinterpret_cast<const v4f *>(xr + idx);
-#endif
-      v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * q + r] = -__builtin_inff();
-    }
-  }
-  float lm = v[0];
-#pragma unroll
-  for (int e = 1; e < VPL; ++e) lm = fmaxf(lm, v[e]);
-  const float M = wave_allreduce(lm, OpMax{});
-  float ls = 0.0f;
-  if (is_finite(M)) {  // uniform: M is the same in every lane
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) ls += exp_base2(v[e] - M);
-  } else {
-#pragma unroll
-    for (int e = 0; e < VPL; ++e) ls += pair_term_nonfinite(v[e], M);
-  }
-  const float S = wave_allreduce(ls, OpSum{});
-  const float k = out_scale<SOFTMAX>(S);
-#pragma unroll
-  for (int q = 0; q < VPL / 4; ++q) {
-    const int64_t idx = ((int64_t)q * kWave + lane) * 4;
-    if (idx < cols)
-      store4(yr + idx, out_value<SOFTMAX>(v[4 * q], M, k), out_value<SOFTMAX>(v[4 * q + 1], M, k),
-             out_value<SOFTMAX>(v[4 * q + 2], M, k), out_value<SOFTMAX>(v[4 * q + 3], M, k));
-  }
-}
-
 // One workgroup = one (row, chunk).  SPLIT: rows of nchunks > 1 chunks whose
 // pairs are merged through the workspace.  !SPLIT: one workgroup per row.
 //
@@ -892,6 +832,120 @@ __global__ __launch_bounds__(kRowsThreads) void rows_lse_stream_kernel(
   if (threadIdx.x == 0) out[row * ldo] = pair_lse(m, s);
 }
 
+#ifndef LSE_ROWS_SEG_MAX
+#define LSE_ROWS_SEG_MAX 1024   // rows up to this many columns take a segment of a wave
+#endif
+static_assert(LSE_ROWS_SEG_MAX >= 1 && LSE_ROWS_SEG_MAX <= 16 * 64,
+              "a wave-wide segment holds at most 16 values per lane");
+constexpr int kSegWaves = 4;    // waves per workgroup of the short-row kernel
+#ifndef LSE_ROWS_SEG_VALUES_LSE
+#define LSE_ROWS_SEG_VALUES_LSE 16  // values per lane in flight, row logsumexp only
+#endif
+#ifndef LSE_ROWS_SEG_VALUES_ROWS
+#define LSE_ROWS_SEG_VALUES_ROWS 4  // values per lane in flight, (log-)softmax rows
+#endif
+enum RowsOut { kOutLogSoftmax = 0, kOutSoftmax = 1, kOutLse = 2 };
+// Rows a segment takes per wave: enough that each lane has the values above
+// in flight before the first reduction.
+constexpr int seg_rows_per_pass(int vpl, int out) {
+  const int target = out == kOutLse ? LSE_ROWS_SEG_VALUES_LSE : LSE_ROWS_SEG_VALUES_ROWS;
+  return vpl >= target ? 1 : target / vpl;
+}
+
+// Short rows: a segment of G lanes (a power of two, 4..64) per row, 64 / G
+// rows per wave, kSegWaves waves per workgroup.  Lane s of a segment holds the
+// row's float4 vectors q G + s (VEC: x, y 16-byte aligned, cols and pitches
+// multiples of 4) or its values q G + s (any 4-byte alignment), padding with
+// -inf, so each load instruction of a segment reads one contiguous span of its
+// row and, for packed rows (pitch = cols), the wave's load is one contiguous
+// span across its rows.  The row's max and sum are all-reductions inside the
+// segment (DPP and permlane swaps): no LDS, no barrier, no idle lanes for rows
+// of a few to a thousand columns.  OUT picks the result: log_softmax or softmax
+// rows from the registers, or the row's logsumexp alone (y[row * ldy]).  Same
+// pair arithmetic as chunk_pair.
+template <int G, int VPL, int NR, bool VEC, int OUT>
+__global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
+    const float *__restrict__ x, float *__restrict__ y, int64_t rows, int64_t cols, int64_t ldx,
+    int64_t ldy) {
+  constexpr bool SOFTMAX = OUT == kOutSoftmax;
+  constexpr int kPerLoad = VEC ? 4 : 1;  // values per load
+  constexpr int kSegs = kWave / G;       // segments per wave
+  const int lane = threadIdx.x % kWave;
+  const int s = lane % G;
+  const int64_t row0 =
+      ((int64_t)blockIdx.x * kSegWaves + threadIdx.x / kWave) * (int64_t)(kSegs * NR);
+  if (row0 >= rows) return;  // whole waves
+  // Pass j of the wave covers rows row0 + j kSegs .. + kSegs - 1, one per
+  // segment; segments past the last row hold -inf and store nothing.
+  float v[NR][VPL];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int64_t row = row0 + j * kSegs + lane / G;
+    const bool live = row < rows;
+    const float *xr = x + (live ? row : row0) * ldx;
+#pragma unroll
+    for (int q = 0; q < VPL / kPerLoad; ++q) {
+      const int64_t idx = ((int64_t)q * G + s) * kPerLoad;
+      if constexpr (VEC) {
+        if (live && idx < cols) {  // cols % 4 == 0: a vector is wholly in or out
+#if LSE_ROWS_NT_LOAD
+          const v4f f = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(xr + idx));
+#else
+          const v4f f = *reinterpret_cast<const v4f *>(xr + idx);
+#endif
+          v[j][4 * q] = f.x; v[j][4 * q + 1] = f.y; v[j][4 * q + 2] = f.z; v[j][4 * q + 3] = f.w;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[j][4 * q + r] = -__builtin_inff();
+        }
+      } else {
+#if LSE_ROWS_NT_LOAD
+        v[j][q] = (live && idx < cols) ? __builtin_nontemporal_load(xr + idx) : -__builtin_inff();
+#else
+        v[j][q] = (live && idx < cols) ? xr[idx] : -__builtin_inff();
+#endif
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    float lm = v[j][0];
+#pragma unroll
+    for (int e = 1; e < VPL; ++e) lm = fmaxf(lm, v[j][e]);
+    const float M = seg_allreduce<G>(lm, OpMax{});
+    float ls = 0.0f;
+    if (is_finite(M)) {  // the same in every lane of the segment
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) ls += exp_base2(v[j][e] - M);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) ls += pair_term_nonfinite(v[j][e], M);
+    }
+    const float S = seg_allreduce<G>(ls, OpSum{});
+    const int64_t row = row0 + j * kSegs + lane / G;
+    if (row >= rows) continue;
+    if constexpr (OUT == kOutLse) {
+      if (s == 0) y[row * ldy] = pair_lse(M, S);
+    } else {
+      const float k = out_scale<SOFTMAX>(S);
+      float *yr = y + row * ldy;
+#pragma unroll
+      for (int q = 0; q < VPL / kPerLoad; ++q) {
+        const int64_t idx = ((int64_t)q * G + s) * kPerLoad;
+        if (idx < cols) {
+          if constexpr (VEC)
+            store4(yr + idx, out_value<SOFTMAX>(v[j][4 * q], M, k),
+                   out_value<SOFTMAX>(v[j][4 * q + 1], M, k),
+                   out_value<SOFTMAX>(v[j][4 * q + 2], M, k),
+                   out_value<SOFTMAX>(v[j][4 * q + 3], M, k));
+          else
+            yr[idx] = out_value<SOFTMAX>(v[j][q], M, k);
+        }
+      }
+    }
+  }
+}
+
 template <bool VEC, bool SOFTMAX>
 __global__ __launch_bounds__(kRowsThreads) void rows_stream_write_kernel(
     const float *__restrict__ x, float *__restrict__ y, int64_t cols, int64_t ldx,
@@ -1016,31 +1070,65 @@ hipError_t for_row_batches(int64_t rows, int64_t max_rows, F launch) {
   return hipSuccess;
 }
 
+template <int G, int VPL, int OUT>
+void launch_seg(bool vec, dim3 grid, hipStream_t stream, const float *x, float *y, int64_t rows,
+                int64_t cols, int64_t ldx, int64_t ldy) {
+  constexpr int NR = seg_rows_per_pass(VPL, OUT);
+  const dim3 block(kWave * kSegWaves);
+  if (vec)
+    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, true, OUT>), grid, block, 0, stream, x, y,
+                       rows, cols, ldx, ldy);
+  else
+    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, false, OUT>), grid, block, 0, stream, x, y,
+                       rows, cols, ldx, ldy);
+}
+
+// Rows of at most LSE_ROWS_SEG_MAX columns through rows_seg_kernel: the
+// segment is the smallest power of two of lanes, up to a wave, whose 4 values
+// per lane hold the row; a wave-wide segment holds 4, 8 or 16 values per lane.
+// vec: x (and y, for the row outputs) 16-byte aligned, cols and the pitches
+// multiples of 4.  For kOutLse, y[r * ldy] receives row r's logsumexp.
+template <int OUT>
+hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols, int64_t ldx,
+                           int64_t ldy, bool vec, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (cols < 1 || cols > LSE_ROWS_SEG_MAX) return hipErrorInvalidValue;
+  int g = 1;
+  while (g < kWave && 4 * g < cols) g *= 2;
+  int vpl = 4;
+  if (g == kWave)
+    while (vpl * kWave < cols) vpl *= 2;
+  const int64_t rows_per_group = (int64_t)kSegWaves * (kWave / g) * seg_rows_per_pass(vpl, OUT);
+  const int64_t max_groups = 0xffffffffll / (kWave * kSegWaves);  // 32-bit work-item count
+  return for_row_batches(rows, max_groups * rows_per_group, [&](int64_t r0, int64_t nr) {
+    const dim3 grid((uint32_t)((nr + rows_per_group - 1) / rows_per_group));
+    const float *xb = x + r0 * ldx;
+    float *yb = y + r0 * ldy;
+    switch (g == kWave ? kWave * vpl : g) {
+      case 1: launch_seg<1, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 2: launch_seg<2, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 4: launch_seg<4, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 8: launch_seg<8, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 16: launch_seg<16, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 32: launch_seg<32, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 4 * kWave: launch_seg<64, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 8 * kWave: launch_seg<64, 8, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 16 * kWave: launch_seg<64, 16, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  });
+}
+
 template <bool SOFTMAX>
 hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols, int64_t ldx,
                             int64_t ldy, void *ws, hipStream_t stream) {
   const RowsPlan p = rows_plan(cols);
   const bool vec = (cols % 4 == 0) && (p.chunk % 4 == 0) && (ldx % 4 == 0) &&
                    (ldy % 4 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0);
-  if (p.nchunks == 1 && vec && cols <= LSE_ROWS_WAVE_MAX) {
-    // one wave per row (rows_wave_kernel)
-    const int vw = cols <= 4 * kWave ? 4 : cols <= 8 * kWave ? 8 : cols <= 16 * kWave ? 16
-                 : cols <= 32 * kWave ? 32 : 64;
-    return for_row_batches(rows, kMaxRowsWorkgroups * 2, [&](int64_t r0, int64_t nr) {
-      const dim3 grid((uint32_t)((nr + kWaveRowsPerGroup - 1) / kWaveRowsPerGroup));
-      const dim3 block(kWave * kWaveRowsPerGroup);
-      const float *xb = x + r0 * ldx;
-      float *yb = y + r0 * ldy;
-      switch (vw) {
-        case 4: hipLaunchKernelGGL((rows_wave_kernel<4, SOFTMAX>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy); break;
-        case 8: hipLaunchKernelGGL((rows_wave_kernel<8, SOFTMAX>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy); break;
-        case 16: hipLaunchKernelGGL((rows_wave_kernel<16, SOFTMAX>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy); break;
-        case 32: hipLaunchKernelGGL((rows_wave_kernel<32, SOFTMAX>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy); break;
-        default: hipLaunchKernelGGL((rows_wave_kernel<64, SOFTMAX>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy); break;
-      }
-      return hipGetLastError();
-    });
-  }
+  if (p.nchunks == 1 && cols <= LSE_ROWS_SEG_MAX)
+    return launch_rows_seg<SOFTMAX ? kOutSoftmax : kOutLogSoftmax>(x, y, rows, cols, ldx, ldy,
+                                                                   vec, stream);
   if (p.nchunks == 1) {
     return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
       return launch_rows_vpl<false, SOFTMAX>(vpl_for(cols), vec, dim3((uint32_t)nr), x + r0 * ldx,
@@ -1147,6 +1235,8 @@ hipError_t launch_rows_lse(const float *x, int64_t rows, int64_t cols, int64_t l
                            int64_t ldo, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const bool vec = (cols % 4 == 0) && (ldx % 4 == 0) && ((uintptr_t)x % 16 == 0);
+  if (cols <= LSE_ROWS_SEG_MAX)
+    return launch_rows_seg<kOutLse>(x, out, rows, cols, ldx, ldo, vec, stream);
   return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
     const dim3 grid((uint32_t)nr);
     const float *xb = x + r0 * ldx;

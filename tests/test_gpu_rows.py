@@ -44,12 +44,17 @@ def test_rows_misaligned(orc, cols):
     compare(_lsm(x), ref, what="misaligned")
 
 
-@pytest.mark.parametrize("cols", [4, 256, 1000, 1024])
+SHORT_COLS = [1, 2, 3, 4, 5, 8, 10, 16, 17, 32, 64, 100, 128, 255, 256, 257, 512, 999, 1000,
+              1024]
+
+
+@pytest.mark.parametrize("cols", [4, 8, 16, 32, 64, 128, 256, 1000, 1024, 3, 10, 17, 255, 999])
 @pytest.mark.parametrize("softmax", [False, True])
-def test_rows_one_wave_per_row_special_values(orc, cols, softmax):
-    """Short aligned rows run one wave per row (4 rows per workgroup): special
-    values in every position, a partial last workgroup (9 rows), and the
-    rows' results against the oracle."""
+def test_rows_short_special_values(orc, cols, softmax):
+    """Rows of at most 1024 columns run one segment of lanes per row (several
+    rows per wave below 256 columns): special values in neighbouring rows of
+    one wave, a partial last workgroup (9 rows), aligned (cols % 4 == 0) and
+    scalar rows; the row logsumexp through lse_reduce_axis on the same rows."""
     x = inputs.normal((9, cols), seed=cols + 7, device=DEV).cpu()
     x[0, :] = -float("inf")                       # all -inf
     x[1, cols // 2] = float("inf")                # +inf
@@ -62,24 +67,65 @@ def test_rows_one_wave_per_row_special_values(orc, cols, softmax):
     if softmax:
         y = L.softmax_rows(xd)
         torch.cuda.synchronize()
-        compare(y.cpu().numpy(), orc.softmax_rows(x.numpy()), what=f"wave softmax {cols}",
+        compare(y.cpu().numpy(), orc.softmax_rows(x.numpy()), what=f"short softmax {cols}",
                 rtol=1e-5, atol=1e-37)
     else:
         ref, _ = orc.log_softmax_rows(x.numpy())
-        compare(_lsm(xd), ref, what=f"wave rows {cols}")
+        compare(_lsm(xd), ref, what=f"short rows {cols}")
+        out = L.lse_reduce_axis(xd, 1)
+        torch.cuda.synchronize()
+        compare(out.cpu().numpy(), orc.lse_axis(x.numpy().reshape(9, cols, 1)).reshape(9),
+                what=f"short row lse {cols}")
 
 
-def test_rows_one_wave_per_row_many_rows(orc):
-    """200003 rows of 256: every row's log_softmax sums to 1, sampled rows
-    (first, last, partial last workgroup) against the oracle."""
-    rows, cols = 200003, 256
-    x = inputs.normal((rows, cols), seed=11, sigma=3.0, device=DEV)
-    y = L.log_softmax_rows(x)
+@pytest.mark.parametrize("cols", SHORT_COLS)
+@pytest.mark.parametrize("layout", ["packed", "pitch", "offset"])
+def test_rows_short_ragged(orc, cols, layout):
+    """1037 short rows (a ragged last wave at every segment width): packed,
+    at a pitch of cols + 3 (a column slice), and at a 4-byte offset; the
+    log_softmax rows, the softmax rows and the row logsumexp against the
+    oracle, and the values around each output left alone."""
+    rows = 1037
+    pad, off = {"packed": (0, 0), "pitch": (3, 0), "offset": (0, 1)}[layout]
+    buf = inputs.normal((rows * (cols + pad) + off,), seed=cols * 3 + pad + off, sigma=3.0,
+                        device=DEV)
+    x = buf[off:].view(rows, cols + pad)[:, :cols]
+    xc = x.cpu().numpy()
+    ref, _ = orc.log_softmax_rows(xc)
+    compare(_lsm(x), ref, what=f"short ragged {layout} {cols}")
+    ybuf = torch.full((rows * (cols + pad) + off,), 7.0, device=DEV)
+    y = ybuf[off:].view(rows, cols + pad)[:, :cols]
+    L.softmax_rows(x, y)
+    obuf = torch.full((2 * rows + 1,), 7.0, device=DEV)
+    out = obuf[1:].view(rows, 2)[:, 0]            # every other float, one float in
+    L.lse_reduce_axis(x, 1, out=out)
     torch.cuda.synchronize()
-    assert (torch.logsumexp(y.double(), 1)).abs().max().item() < 1e-5
-    idx = [0, 1, 2, 3, 4, rows // 2, rows - 4, rows - 3, rows - 2, rows - 1]
-    ref, _ = orc.log_softmax_rows(x[idx].cpu().numpy())
-    compare(y[idx].cpu().numpy(), ref, what="wave many rows")
+    compare(y.cpu().numpy(), orc.softmax_rows(xc), what=f"short ragged softmax {layout} {cols}",
+            rtol=1e-5, atol=1e-37)
+    compare(out.cpu().numpy(), orc.lse_axis(xc.reshape(rows, cols, 1)).reshape(rows),
+            what=f"short ragged lse {layout} {cols}")
+    if pad:
+        assert (ybuf[off:].view(rows, cols + pad)[:, cols:] == 7.0).all()
+    assert ybuf[:off].eq(7.0).all() and obuf[0].item() == 7.0
+    assert (obuf[1:].view(rows, 2)[:, 1] == 7.0).all()
+
+
+def test_rows_short_many_rows(orc):
+    """200003 rows of 256 and 2000003 rows of 10: every row's log_softmax
+    sums to 1, sampled rows (first, last, partial last workgroup) against the
+    oracle, logsumexp and log_softmax."""
+    for rows, cols in ((200003, 256), (2000003, 10)):
+        x = inputs.normal((rows, cols), seed=11 + cols, sigma=3.0, device=DEV)
+        y = L.log_softmax_rows(x)
+        out = L.lse_reduce_axis(x, 1)
+        torch.cuda.synchronize()
+        assert (torch.logsumexp(y.double(), 1)).abs().max().item() < 1e-5
+        idx = [0, 1, 2, 3, 4, rows // 2, rows - 4, rows - 3, rows - 2, rows - 1]
+        xs = x[idx].cpu().numpy()
+        ref, _ = orc.log_softmax_rows(xs)
+        compare(y[idx].cpu().numpy(), ref, what=f"short many rows {cols}")
+        compare(out[idx].cpu().numpy(), orc.lse_axis(xs.reshape(len(idx), cols, 1)).reshape(-1),
+                what=f"short many rows lse {cols}")
 
 
 def test_rows_special_values(orc):
