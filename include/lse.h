@@ -129,6 +129,42 @@ lse_status_t log_softmax_axis_strided(const float *x, float *y, int64_t outer,
                                       int64_t y_stride_outer, int64_t y_stride_r,
                                       hipStream_t stream);
 
+/* The axis calls above with a caller's workspace, for few outputs over many
+ * planes (the logsumexp over dim 0 of (R, B, D) with B D small and R large):
+ * there the calls without a workspace leave most of the GPU idle, since the
+ * planes of one output run can only be split across the waves of one
+ * workgroup.  With a workspace the planes of each run of outputs are split
+ * across workgroups whose per-output (max, sum) pairs are merged by a second
+ * launch in a fixed order (log_softmax then writes y in a third launch, so x
+ * is read twice there), and long contiguous last-axis rows take the split-row
+ * kernels of case B.  The reduction each output receives is the same as
+ * without a workspace; only the order of the additions differs.
+ *   lse_axis_workspace_bytes: bytes the call with these sizes needs (0 when
+ *     none of the split paths applies, in which case ws may be NULL);
+ *     log_softmax != 0 for log_softmax_axis_strided_ws.  0 for invalid sizes.
+ *   ws: device memory of at least that many bytes, not overlapping x or the
+ *     output; its contents on entry are irrelevant and it is scratch until
+ *     the call's launches on `stream` have finished.  Concurrent calls need
+ *     separate workspaces.  Missing or too small: LSE_ERR_WORKSPACE; other
+ *     arguments and errors as for the calls without a workspace.
+ *                  [LSE0] task statement; [LSM] the two-phase (max, sum) merge. */
+size_t lse_axis_workspace_bytes(int64_t outer, int64_t R, int64_t inner,
+                                int log_softmax);
+lse_status_t lse_reduce_axis0_ws(const float *x, float *out, int64_t R,
+                                 int64_t inner, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+lse_status_t lse_reduce_axis_strided_ws(const float *x, float *out, int64_t outer,
+                                        int64_t R, int64_t inner,
+                                        int64_t x_stride_outer, int64_t x_stride_r,
+                                        int64_t out_stride_outer, void *ws,
+                                        size_t ws_bytes, hipStream_t stream);
+lse_status_t log_softmax_axis_strided_ws(const float *x, float *y, int64_t outer,
+                                         int64_t R, int64_t inner,
+                                         int64_t x_stride_outer, int64_t x_stride_r,
+                                         int64_t y_stride_outer, int64_t y_stride_r,
+                                         void *ws, size_t ws_bytes,
+                                         hipStream_t stream);
+
 /* ---------------------------------------------------------------- case B
  * Row-wise log_softmax over the last axis.           [LSM] opening formula
  *   y[r, c] = x[r, c] - LSE_c x[r, :],   (rows, cols) row-major.

@@ -34,7 +34,7 @@ __all__ = [
     "log_softmax_rows_plan", "lse_testing_set_spin_limit", "lse_testing_set_chain_path",
     "lse_testing_set_rows_reread", "lse_rows_num_chunks", "lse_rows_partial",
     "lse_rows_merge", "fused_conv_gn_act_lse", "fused_conv_gn_act_lse_workspace_bytes",
-    "lse_abi_version", "LseError",
+    "lse_abi_version", "LseError", "lse_axis_workspace_bytes",
 ]
 
 
@@ -109,8 +109,19 @@ def lse_abi_version() -> int:
     return int(_lib.load().lse_abi_version())
 
 
-def lse_reduce_axis0(x, out=None, stream=None):
-    """out[...] = logsumexp over dim 0 of x (shape x.shape[1:])."""
+def lse_axis_workspace_bytes(outer: int, R: int, inner: int, log_softmax: bool = False) -> int:
+    """Workspace bytes of the axis calls on these sizes (0: none needed)."""
+    return int(_lib.load().lse_axis_workspace_bytes(outer, R, inner, 1 if log_softmax else 0))
+
+
+def _ws_ptr(ws):
+    return None if ws is None else ctypes.c_void_p(ws.data_ptr())
+
+
+def lse_reduce_axis0(x, out=None, ws=None, stream=None):
+    """out[...] = logsumexp over dim 0 of x (shape x.shape[1:]).  Few outputs
+    over many planes take a workspace (`ws`, or a new one from torch's
+    allocator)."""
     import torch
     lib = _lib.load()
     if x.dim() == 0:
@@ -121,9 +132,10 @@ def lse_reduce_axis0(x, out=None, stream=None):
         out = torch.empty(x.shape[1:], dtype=torch.float32, device=x.device)
     if out.numel() != inner:
         raise ValueError("out has the wrong number of elements")
-    with _on(x, out):
-        _lib.check(lib.lse_reduce_axis0(_dev(x, "x"), _dev(out, "out"), R, inner,
-                                        _stream(stream)), "lse_reduce_axis0")
+    with _on(x, out, ws):
+        ws, ws_bytes = _workspace(lse_axis_workspace_bytes(1, R, inner), x.device, ws, stream)
+        _lib.check(lib.lse_reduce_axis0_ws(_dev(x, "x"), _dev(out, "out"), R, inner, _ws_ptr(ws),
+                                           ws_bytes, _stream(stream)), "lse_reduce_axis0")
     return out
 
 
@@ -164,10 +176,11 @@ def _strided_axis(t, d, name):
     return outer_st, strides[d]
 
 
-def lse_reduce_axis(x, dim, out=None, stream=None):
+def lse_reduce_axis(x, dim, out=None, ws=None, stream=None):
     """logsumexp over `dim` of an fp32 GPU tensor (dim removed).  x and out
     may be strided views whose dims after `dim` form one contiguous run and
-    whose dims before it merge into one stride."""
+    whose dims before it merge into one stride.  Few outputs over many planes
+    take a workspace (`ws`, or a new one from torch's allocator)."""
     import torch
     lib = _lib.load()
     d, outer, R, inner = _axis_view(x, dim)
@@ -178,16 +191,20 @@ def lse_reduce_axis(x, dim, out=None, stream=None):
         raise ValueError(f"out must have shape {shape}")
     xso, xsr = _strided_axis(x, d, "x")
     oso, _ = _strided_axis(out.unsqueeze(d), d, "out")
-    with _on(x, out):
-        _lib.check(lib.lse_reduce_axis_strided(_dev(x, "x", False), _dev(out, "out", False),
-                                               outer, R, inner, xso, xsr, oso, _stream(stream)),
+    with _on(x, out, ws):
+        ws, ws_bytes = _workspace(lse_axis_workspace_bytes(outer, R, inner), x.device, ws, stream)
+        _lib.check(lib.lse_reduce_axis_strided_ws(_dev(x, "x", False), _dev(out, "out", False),
+                                                  outer, R, inner, xso, xsr, oso, _ws_ptr(ws),
+                                                  ws_bytes, _stream(stream)),
                    "lse_reduce_axis")
     return out
 
 
-def log_softmax_axis(x, dim, y=None, stream=None):
+def log_softmax_axis(x, dim, y=None, ws=None, stream=None):
     """log_softmax over `dim` of an fp32 GPU tensor; x and y may be strided
-    views as for lse_reduce_axis (a new y is contiguous)."""
+    views as for lse_reduce_axis (a new y is contiguous).  Few outputs over
+    many planes, and long last-axis rows, take a workspace (`ws`, or a new
+    one from torch's allocator)."""
     import torch
     lib = _lib.load()
     d, outer, R, inner = _axis_view(x, dim)
@@ -197,9 +214,12 @@ def log_softmax_axis(x, dim, y=None, stream=None):
         raise ValueError("y must have x's shape")
     xso, xsr = _strided_axis(x, d, "x")
     yso, ysr = _strided_axis(y, d, "y")
-    with _on(x, y):
-        _lib.check(lib.log_softmax_axis_strided(_dev(x, "x", False), _dev(y, "y", False), outer,
-                                                R, inner, xso, xsr, yso, ysr, _stream(stream)),
+    with _on(x, y, ws):
+        ws, ws_bytes = _workspace(lse_axis_workspace_bytes(outer, R, inner, True), x.device, ws,
+                                  stream)
+        _lib.check(lib.log_softmax_axis_strided_ws(_dev(x, "x", False), _dev(y, "y", False),
+                                                   outer, R, inner, xso, xsr, yso, ysr,
+                                                   _ws_ptr(ws), ws_bytes, _stream(stream)),
                    "log_softmax_axis")
     return y
 

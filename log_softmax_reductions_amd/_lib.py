@@ -23,6 +23,12 @@ SIGNATURES = {
                                                _vp]),
     "log_softmax_axis_strided": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                                 _i64, _vp]),
+    "lse_axis_workspace_bytes": (_sz, [_i64, _i64, _i64, ctypes.c_int]),
+    "lse_reduce_axis0_ws": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "lse_reduce_axis_strided_ws": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                  _vp, _sz, _vp]),
+    "log_softmax_axis_strided_ws": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                   _i64, _vp, _sz, _vp]),
     "log_softmax_rows_strided": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     "softmax_rows_strided": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     "log_softmax_rows_workspace_bytes": (_sz, [_i64, _i64]),

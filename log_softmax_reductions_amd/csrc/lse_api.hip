@@ -204,6 +204,80 @@ LSE_EXPORT lse_status_t log_softmax_axis(const float *x, float *y, int64_t outer
   return log_softmax_axis_strided(x, y, outer, R, inner, so, inner, so, inner, stream);
 }
 
+// ------------------------------------------------- axis calls with a workspace
+LSE_EXPORT size_t lse_axis_workspace_bytes(int64_t outer, int64_t R, int64_t inner,
+                                           int log_softmax) {
+  int64_t t, total;
+  if (outer < 1 || R < 1 || inner < 1 || !mul_ok(outer, R, &t) || !mul_ok(t, inner, &total) ||
+      total > kMaxElems)
+    return 0;
+  return lse::axis_workspace_bytes(outer, R, inner, log_softmax != 0);
+}
+
+// The workspace of an axis call: required when the call's sizes take a split
+// path, and disjoint from x and the output.
+static lse_status_t check_axis_ws(const char *who, const void *x, const void *out, int64_t outer,
+                                  int64_t R, int64_t inner, int64_t xso, int64_t xsr,
+                                  int64_t yso, int64_t ysr, bool lsm, const void *ws,
+                                  size_t ws_bytes) {
+  const size_t need = lse::axis_workspace_bytes(outer, R, inner, lsm);
+  if (need == 0) return LSE_OK;
+  if (!ws) return fail(LSE_ERR_WORKSPACE, "%s: needs %zu workspace bytes", who, need);
+  if (ws_bytes < need)
+    return fail(LSE_ERR_WORKSPACE, "%s: workspace %zu < required %zu", who, ws_bytes, need);
+  int64_t xspan, yspan;
+  span_ok(outer, xso, R, xsr, inner, &xspan);  // checked by check_axis
+  span_ok(outer, yso, lsm ? R : 1, ysr, inner, &yspan);
+  if (overlaps(ws, (int64_t)need, x, xspan * 4) || overlaps(ws, (int64_t)need, out, yspan * 4))
+    return fail(LSE_ERR_OVERLAP, "%s: workspace overlaps x or the output", who);
+  return LSE_OK;
+}
+
+LSE_EXPORT lse_status_t lse_reduce_axis_strided_ws(const float *x, float *out, int64_t outer,
+                                                   int64_t R, int64_t inner,
+                                                   int64_t x_stride_outer, int64_t x_stride_r,
+                                                   int64_t out_stride_outer, void *ws,
+                                                   size_t ws_bytes, hipStream_t stream) {
+  const char *who = "lse_reduce_axis_strided_ws";
+  int64_t total;
+  lse_status_t st = check_axis(who, x, out, outer, R, inner, x_stride_outer, x_stride_r,
+                               out_stride_outer, 0, false, &total);
+  if (st != LSE_OK) return st;
+  if (total == 0) return ok();
+  st = check_axis_ws(who, x, out, outer, R, inner, x_stride_outer, x_stride_r, out_stride_outer,
+                     0, false, ws, ws_bytes);
+  if (st != LSE_OK) return st;
+  const lse::AxisDims d{outer, R, inner, x_stride_outer, x_stride_r, out_stride_outer, 0};
+  return from_hip(lse::launch_lse_axis(x, out, d, stream, true, ws), who);
+}
+
+LSE_EXPORT lse_status_t lse_reduce_axis0_ws(const float *x, float *out, int64_t R, int64_t inner,
+                                            void *ws, size_t ws_bytes, hipStream_t stream) {
+  int64_t xso = 0;  // negative sizes are reported by the strided call's checks
+  if (!mul_ok(R, inner, &xso) && R >= 1 && inner >= 0)
+    return fail(LSE_ERR_SHAPE, "lse_reduce_axis0_ws: R * inner overflows");
+  return lse_reduce_axis_strided_ws(x, out, 1, R, inner, xso, inner, inner, ws, ws_bytes, stream);
+}
+
+LSE_EXPORT lse_status_t log_softmax_axis_strided_ws(const float *x, float *y, int64_t outer,
+                                                    int64_t R, int64_t inner,
+                                                    int64_t x_stride_outer, int64_t x_stride_r,
+                                                    int64_t y_stride_outer, int64_t y_stride_r,
+                                                    void *ws, size_t ws_bytes,
+                                                    hipStream_t stream) {
+  const char *who = "log_softmax_axis_strided_ws";
+  int64_t total;
+  lse_status_t st = check_axis(who, x, y, outer, R, inner, x_stride_outer, x_stride_r,
+                               y_stride_outer, y_stride_r, true, &total);
+  if (st != LSE_OK) return st;
+  if (total == 0) return ok();
+  st = check_axis_ws(who, x, y, outer, R, inner, x_stride_outer, x_stride_r, y_stride_outer,
+                     y_stride_r, true, ws, ws_bytes);
+  if (st != LSE_OK) return st;
+  const lse::AxisDims d{outer, R, inner, x_stride_outer, x_stride_r, y_stride_outer, y_stride_r};
+  return from_hip(lse::launch_log_softmax_axis(x, y, d, stream, true, ws), who);
+}
+
 // ------------------------------------------------------------------ case B
 static lse_status_t check_rows(const char *who, int64_t rows, int64_t cols, int64_t *total) {
   if (rows < 0) return fail(LSE_ERR_SHAPE, "%s: rows = %lld must be >= 0", who, (long long)rows);

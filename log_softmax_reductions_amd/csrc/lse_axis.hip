@@ -81,24 +81,6 @@ constexpr int kLsmThreads = LSE_AXIS_LSM_THREADS;
 constexpr int kMaxAxisThreads = kAxis0Threads > kLsmThreads ? kAxis0Threads : kLsmThreads;
 constexpr int kVecW = LSE_AXIS0_W;
 
-__device__ __forceinline__ float safe_shift(float m) { return is_finite(m) ? m : 0.0f; }
-
-// Fold one block of NB planes (values v[0..NB)) into the running (m, s).
-template <int NB>
-__device__ __forceinline__ void fold_block(const float (&v)[NB], float &m, float &s) {
-  float bm = v[0];
-#pragma unroll
-  for (int i = 1; i < NB; ++i) bm = fmaxf(bm, v[i]);
-  const float mn = fmaxf(m, bm);
-  const float c = safe_shift(mn);
-  // s == 0 means nothing counted yet: skip the rescale (its factor may be inf).
-  float acc = (s == 0.0f) ? 0.0f : s * exp_base2(safe_shift(m) - c);
-#pragma unroll
-  for (int i = 0; i < NB; ++i) acc += exp_base2(v[i] - c);
-  m = mn;
-  s = acc;
-}
-
 // Four floats as one 16-byte access at an address known only to be 4-byte
 // aligned (gfx950 accepts dword-aligned 16-byte accesses).
 typedef float v4a4 __attribute__((ext_vector_type(4), aligned(4)));
@@ -1027,15 +1009,64 @@ static bool as_rows(const AxisDims &d, bool lsm) {
   return d.inner == 1 && d.xsr == 1 && (!lsm || d.ysr == 1) && d.outer <= 0x7fffffff;
 }
 
-hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream) {
-  if (as_rows(d, false)) return launch_rows_lse(x, d.outer, d.R, d.xso, out, d.yso, stream);
+#ifndef LSE_AXIS_COLS
+#define LSE_AXIS_COLS 1   // few outputs over many planes take the column split (lse_cols.hip)
+#endif
+#ifndef LSE_AXIS_ROWS_SPLIT_MAX_ROWS
+#define LSE_AXIS_ROWS_SPLIT_MAX_ROWS 1024   // logsumexp rows split with a workspace up to here
+#endif
+// Long last-axis logsumexp rows with a workspace: per-chunk pairs of the row
+// register tile, then one merge per row (few rows only: many rows fill the
+// GPU one workgroup per row).
+static bool lse_rows_split(const AxisDims &d) {
+  return d.outer <= LSE_AXIS_ROWS_SPLIT_MAX_ROWS && d.R > kRowsTile &&
+         (d.outer == 1 || d.yso == 1);
+}
+
+size_t axis_workspace_bytes(int64_t outer, int64_t R, int64_t inner, bool lsm) {
+  if (outer < 1 || R < 1 || inner < 1) return 0;
+  const AxisDims d{outer, R, inner, R * inner, inner, lsm ? R * inner : inner, lsm ? inner : 0};
+  size_t n = LSE_AXIS_COLS ? cols_workspace_bytes(d, lsm) : 0;
+  if (inner == 1) {
+    size_t r = 0;
+    if (lsm) {
+      r = rows_workspace_bytes(outer, R);
+    } else {
+      const AxisDims rd{outer, R, 1, R, 1, 1, 0};
+      if (lse_rows_split(rd))
+        r = (size_t)outer * (size_t)((R + kRowsTile - 1) / kRowsTile) * sizeof(float2);
+    }
+    if (r > n) n = r;
+  }
+  return n;
+}
+
+hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream,
+                           bool with_ws, void *ws) {
+  if (as_rows(d, false)) {
+    if (with_ws && ws != nullptr && lse_rows_split(d)) {
+      const int64_t nchunks = (d.R + kRowsTile - 1) / kRowsTile;
+      const hipError_t e = launch_lse_rows_partial(x, d.outer, d.R, d.xso, kRowsTile, ws, stream);
+      if (e != hipSuccess) return e;
+      return launch_lse_rows_merge(ws, d.outer, nchunks, out, stream);
+    }
+    return launch_rows_lse(x, d.outer, d.R, d.xso, out, d.yso, stream);
+  }
+  hipError_t e = hipSuccess;
+  if (LSE_AXIS_COLS && launch_cols(x, out, d, false, with_ws, ws, stream, e)) return e;
   return launch_axis<false>(x, out, d, stream);
 }
 
 hipError_t launch_log_softmax_axis(const float *x, float *y, const AxisDims &d,
-                                   hipStream_t stream) {
-  if (as_rows(d, true))
+                                   hipStream_t stream, bool with_ws, void *ws) {
+  if (as_rows(d, true)) {
+    if (with_ws && ws != nullptr && rows_plan(d.R).nchunks > 1 &&
+        d.outer * rows_plan(d.R).nchunks <= 0x7fffffff)
+      return launch_log_softmax_rows(x, y, d.outer, d.R, d.xso, d.yso, ws, stream);
     return launch_log_softmax_rows_no_ws(x, y, d.outer, d.R, d.xso, d.yso, stream);
+  }
+  hipError_t e = hipSuccess;
+  if (LSE_AXIS_COLS && launch_cols(x, y, d, true, with_ws, ws, stream, e)) return e;
   return launch_axis<true>(x, y, d, stream);
 }
 

@@ -1,0 +1,395 @@
+// lse_cols.hip — logsumexp and log_softmax over the middle axis of an
+// (outer, R, inner) array when there are few outputs (outer x inner) and many
+// planes: the logsumexp over dim 0 of (R, B, D) with R in the hundreds of
+// thousands and B D in the tens, say.
+//
+// POPCORNBENCH FW-GLM-5-1 l1_p29 (torch.logsumexp over dim 0 of (R,B,D)): every
+// output is an independent max-shifted sum over its R values.  With one lane
+// per 4 outputs, few outputs leave almost every lane of the GPU idle, and a
+// run of fewer than 256 outputs gives a wave's load of one plane only a few
+// bytes.  Here:
+//   * LPP lanes (a power of two up to 64) share each plane of a tile of
+//     4 LPP columns, so a wave reads 64 / LPP consecutive planes per load
+//     instruction and each load of a packed (R, inner) array is one contiguous
+//     span of up to 1 KiB; each lane folds its 4 columns' running (m, s) over
+//     blocks of 4 planes (fold_block: exact max, one rescale per block).
+//   * The planes of a tile are split into chunks, one workgroup each; with a
+//     workspace the chunks' (m, s) pairs are merged by a second launch (fixed
+//     chunk order, so results do not depend on timing).  Without one (the
+//     entry points that take none) each tile is one chunk.
+//   * Inside a workgroup the pairs of lanes sharing columns are merged with
+//     xor shuffles, then the 4 waves' through LDS, always in the same order.
+//   * log_softmax: (x - M) - log S is written by the same workgroup, which
+//     reads its planes again (one chunk per tile), or by an apply launch over
+//     the chunks after the merge launch has stored each column's (M, log S).
+#include <type_traits>
+
+#include "lse_device.hpp"
+#include "lse_internal.hpp"
+
+namespace lse {
+namespace {
+
+constexpr int kColsWaves = 4;
+constexpr int kColsThreads = kColsWaves * kWave;
+constexpr int kColsU = 4;  // plane steps loaded before they are folded
+#ifndef LSE_COLS_MAX_OUTPUTS
+#define LSE_COLS_MAX_OUTPUTS 32768   // up to this many outputs the column split is taken
+#endif
+#ifndef LSE_COLS_MINR
+#define LSE_COLS_MINR 64             // ... over at least this many planes
+#endif
+#ifndef LSE_COLS_TARGET_GROUPS
+#define LSE_COLS_TARGET_GROUPS 2048  // workgroups the chunking aims for
+#endif
+#ifndef LSE_COLS_MIN_PLANES
+#define LSE_COLS_MIN_PLANES 128      // planes per chunk at least (pair traffic <= 1/64 of x)
+#endif
+
+enum ColsMode { kColsPartial = 0, kColsLse = 1, kColsLsm = 2 };
+
+typedef float v4f16 __attribute__((ext_vector_type(4)));
+
+// Column e (0..3) of lane cl within a tile of 4 LPP columns: VEC lanes hold 4
+// consecutive columns (one 16-byte access), scalar lanes every LPP-th column.
+template <int LPP, bool VEC>
+__device__ __forceinline__ int tile_col(int cl, int e) {
+  return VEC ? 4 * cl + e : cl + LPP * e;
+}
+
+// The lane's 4 values of one plane row p (the tile's first column); columns
+// at or past ncols read -inf.
+template <int LPP, bool VEC, bool NT>
+__device__ __forceinline__ void cols_load(const float *p, int cl, int64_t ncols, float (&v)[4]) {
+  if constexpr (VEC) {  // ncols % 4 == 0: a vector is wholly in or out
+    if (4 * cl < ncols) {
+      const v4f16 *q = reinterpret_cast<const v4f16 *>(p + 4 * cl);
+      const v4f16 t = NT ? __builtin_nontemporal_load(q) : *q;
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = -__builtin_inff();
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = tile_col<LPP, false>(cl, e);
+      v[e] = (j < ncols) ? (NT ? __builtin_nontemporal_load(p + j) : p[j]) : -__builtin_inff();
+    }
+  }
+}
+
+template <int LPP, bool VEC>
+__device__ __forceinline__ void cols_store(float *p, int cl, int64_t ncols, const float (&r)[4]) {
+  if constexpr (VEC) {
+    if (4 * cl < ncols)
+      __builtin_nontemporal_store(v4f16{r[0], r[1], r[2], r[3]}, reinterpret_cast<v4f16 *>(p + 4 * cl));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = tile_col<LPP, false>(cl, e);
+      if (j < ncols) __builtin_nontemporal_store(r[e], p + j);
+    }
+  }
+}
+
+// Merge of the running pairs of lanes whose index differs only in bits >=
+// log2(LPP) (the lanes that hold the same columns): every such lane ends with
+// the same (M, S), each step combining the same two values.
+template <int LPP>
+__device__ __forceinline__ void merge_lanes(float &m, float &s) {
+  float M = m;
+#pragma unroll
+  for (int k = LPP; k < kWave; k <<= 1) M = fmaxf(M, __shfl_xor(M, k));
+  float S = fold_weighted(m, s, M);
+#pragma unroll
+  for (int k = LPP; k < kWave; k <<= 1) S += __shfl_xor(S, k);
+  m = M;
+  s = S;
+}
+
+// Workgroup (o, tile t, chunk c) of an (outer, ctiles, chunks) grid, chunk
+// fastest: folds planes [c rc, min(R, (c + 1) rc)) of the tile's columns.
+//   kColsPartial: pairs[((o ctiles + t) C + col) chunks + c] = the chunk's
+//                 (m, s) per column (each column's chunks contiguous)
+//   kColsLse (one chunk): out[o yso + j] = m + log s
+//   kColsLsm (one chunk): y[o yso + r ysr + j] = (x - m) - log s, re-reading x
+template <int LPP, bool VEC, int MODE>
+__global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
+    const float *__restrict__ x, float *__restrict__ out, AxisDims d, int64_t ctiles,
+    int64_t chunks, int64_t rc, float2 *__restrict__ pairs) {
+  constexpr int kGroups = kWave / LPP;          // planes per wave and step
+  constexpr int kStep = kColsWaves * kGroups;   // planes per workgroup and step
+  constexpr int C = 4 * LPP;                    // columns per tile
+  __shared__ float2 lds_pair[kColsWaves][C];
+  __shared__ float2 lds_fin[C];
+  const int64_t b = blockIdx.x;
+  const int64_t c = b % chunks;
+  const int64_t ot = b / chunks;
+  const int64_t t = ot % ctiles;
+  const int64_t o = ot / ctiles;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int cl = lane % LPP;
+  const int g = wave * kGroups + lane / LPP;  // the lane's plane within a step
+  const int64_t j0 = t * C;
+  const int64_t ncols = d.inner - j0;
+  const int64_t r0 = c * rc;
+  const int64_t r1 = (d.R - r0 < rc) ? d.R : r0 + rc;
+  const float *xt = x + o * d.xso + j0;
+  const int64_t xsr = d.xsr;
+  constexpr bool kNt = MODE != kColsLsm;  // log_softmax reads its planes again: keep them cached
+  float m[4], s[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m[e] = -__builtin_inff();
+    s[e] = 0.0f;
+  }
+  for (int64_t r = r0 + g; r < r1; r += kStep * kColsU) {
+    float v[4][kColsU];
+#pragma unroll
+    for (int u = 0; u < kColsU; ++u) {
+      const int64_t rr = r + u * kStep;
+      float q[4];
+      if (rr < r1) {
+        cols_load<LPP, VEC, kNt>(xt + rr * xsr, cl, ncols, q);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = -__builtin_inff();
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e][u] = q[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) fold_block<kColsU>(v[e], m[e], s[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) merge_lanes<LPP>(m[e], s[e]);
+  if (lane < LPP) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lds_pair[wave][tile_col<LPP, VEC>(cl, e)] = make_float2(m[e], s[e]);
+  }
+  __syncthreads();
+  if (threadIdx.x < C) {
+    const int col = threadIdx.x;
+    float M = lds_pair[0][col].x;
+#pragma unroll
+    for (int w = 1; w < kColsWaves; ++w) M = fmaxf(M, lds_pair[w][col].x);
+    float S = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kColsWaves; ++w) S += fold_weighted(lds_pair[w][col].x, lds_pair[w][col].y, M);
+    if constexpr (MODE == kColsPartial) {
+      pairs[(ot * C + col) * chunks + c] = make_float2(M, S);
+    } else if constexpr (MODE == kColsLse) {
+      if (col < ncols) out[o * d.yso + j0 + col] = M + logf(S);
+    } else {
+      lds_fin[col] = make_float2(M, logf(S));
+    }
+  }
+  if constexpr (MODE == kColsLsm) {
+    __syncthreads();
+    float fm[4], fl[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float2 f = lds_fin[tile_col<LPP, VEC>(cl, e)];
+      fm[e] = f.x;
+      fl[e] = f.y;
+    }
+    float *yt = out + o * d.yso + j0;
+    for (int64_t r = r0 + g; r < r1; r += kStep) {
+      float q[4];
+      cols_load<LPP, VEC, true>(xt + r * xsr, cl, ncols, q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = (q[e] - fm[e]) - fl[e];
+      cols_store<LPP, VEC>(yt + r * d.ysr, cl, ncols, q);
+    }
+  }
+}
+
+// One wave per (o, t, column) of the tiles, 4 per workgroup: lane l folds the
+// column's chunk pairs l, l + 64, ... in order, then the lanes' pairs merge
+// across the wave (the same order on every call).  LSM stores (M, log S) per
+// column for the apply launch, else writes the logsumexp.
+template <bool LSM>
+__global__ __launch_bounds__(256) void axis_cols_merge_kernel(const float2 *__restrict__ pairs,
+                                                              float *__restrict__ out,
+                                                              float2 *__restrict__ fin,
+                                                              AxisDims d, int64_t ctiles,
+                                                              int64_t chunks, int C) {
+  const int64_t i = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;  // (o, t, column)
+  const int lane = threadIdx.x % kWave;
+  if (i >= d.outer * ctiles * C) return;  // whole waves
+  const int64_t ot = i / C;
+  const int col = (int)(i - ot * C);
+  const int64_t t = ot % ctiles;
+  const int64_t o = ot / ctiles;
+  const int64_t j = t * C + col;
+  if (j >= d.inner) return;  // whole waves
+  const float2 *p = pairs + i * chunks;
+  float m = -__builtin_inff(), s = 0.0f;
+  for (int64_t k = lane; k < chunks; k += kWave) {
+    const float2 q = p[k];
+    const float mn = fmaxf(m, q.x);
+    s = fold_weighted(m, s, mn) + fold_weighted(q.x, q.y, mn);
+    m = mn;
+  }
+  merge_lanes<1>(m, s);
+  if (lane == 0) {
+    if constexpr (LSM)
+      fin[i] = make_float2(m, logf(s));
+    else
+      out[o * d.yso + j] = m + logf(s);
+  }
+}
+
+// log_softmax over the chunks' planes from the merged (M, log S) per column,
+// on the grid of the partial launch.
+template <int LPP, bool VEC>
+__global__ __launch_bounds__(kColsThreads) void axis_cols_apply_kernel(
+    const float *__restrict__ x, float *__restrict__ y, AxisDims d, int64_t ctiles,
+    int64_t chunks, int64_t rc, const float2 *__restrict__ fin) {
+  constexpr int kGroups = kWave / LPP;
+  constexpr int kStep = kColsWaves * kGroups;
+  constexpr int C = 4 * LPP;
+  const int64_t b = blockIdx.x;
+  const int64_t c = b % chunks;
+  const int64_t ot = b / chunks;
+  const int64_t t = ot % ctiles;
+  const int64_t o = ot / ctiles;
+  const int lane = threadIdx.x % kWave;
+  const int cl = lane % LPP;
+  const int g = (threadIdx.x / kWave) * kGroups + lane / LPP;
+  const int64_t j0 = t * C;
+  const int64_t ncols = d.inner - j0;
+  const int64_t r0 = c * rc;
+  const int64_t r1 = (d.R - r0 < rc) ? d.R : r0 + rc;
+  float fm[4], fl[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float2 f = fin[ot * C + tile_col<LPP, VEC>(cl, e)];
+    fm[e] = f.x;
+    fl[e] = f.y;
+  }
+  const float *xt = x + o * d.xso + j0;
+  float *yt = y + o * d.yso + j0;
+  for (int64_t r = r0 + g; r < r1; r += kStep) {
+    float q[4];
+    cols_load<LPP, VEC, true>(xt + r * d.xsr, cl, ncols, q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] = (q[e] - fm[e]) - fl[e];
+    cols_store<LPP, VEC>(yt + r * d.ysr, cl, ncols, q);
+  }
+}
+
+struct ColsPlan {
+  int lpp;
+  int64_t ctiles, chunks, rc;
+};
+
+// The column-split plan of a call, or false when the call keeps the other
+// axis kernels.  with_ws: the caller can supply cols_workspace_bytes().
+bool cols_plan(const AxisDims &d, bool with_ws, ColsPlan &p) {
+  if (d.outer < 1 || d.inner < 1 || d.R < LSE_COLS_MINR) return false;
+  if (d.inner > LSE_COLS_MAX_OUTPUTS || d.outer * d.inner > LSE_COLS_MAX_OUTPUTS) return false;
+  int lpp = 1;
+  while (lpp < kWave && 4 * lpp < d.inner) lpp *= 2;
+  const int64_t C = 4 * lpp;
+  p.lpp = lpp;
+  p.ctiles = (d.inner + C - 1) / C;
+  const int64_t groups = d.outer * p.ctiles;
+  if (!with_ws) {
+    p.chunks = 1;
+  } else {
+    const int64_t step = (int64_t)kColsWaves * (kWave / lpp) * kColsU;
+    const int64_t min_planes = step > LSE_COLS_MIN_PLANES ? step : LSE_COLS_MIN_PLANES;
+    int64_t k = (LSE_COLS_TARGET_GROUPS + groups - 1) / groups;
+    const int64_t kmax = d.R / min_planes;
+    if (k > kmax) k = kmax;
+    p.chunks = k < 1 ? 1 : k;
+  }
+  // One chunk per tile is only worth it while a tile holds the whole inner
+  // run (wider runs give the plane-split kernels more lanes).
+  if (p.chunks == 1 && p.ctiles > 1) return false;
+  p.rc = (d.R + p.chunks - 1) / p.chunks;
+  p.chunks = (d.R + p.rc - 1) / p.rc;  // no empty last chunk
+  return true;
+}
+
+size_t cols_ws_bytes(const AxisDims &d, const ColsPlan &p, bool lsm) {
+  if (p.chunks <= 1) return 0;
+  const int64_t cols = d.outer * p.ctiles * 4 * p.lpp;
+  return (size_t)(cols * p.chunks * 8 + (lsm ? cols * 8 : 0));
+}
+
+template <int LPP, bool VEC>
+hipError_t launch_cols_t(const float *x, float *out, const AxisDims &d, bool lsm,
+                         const ColsPlan &p, void *ws, hipStream_t stream) {
+  const dim3 grid((uint32_t)(d.outer * p.ctiles * p.chunks));
+  const dim3 block(kColsThreads);
+  if (p.chunks == 1) {
+    if (lsm)
+      hipLaunchKernelGGL((axis_cols_kernel<LPP, VEC, kColsLsm>), grid, block, 0, stream, x, out, d,
+                         p.ctiles, p.chunks, p.rc, nullptr);
+    else
+      hipLaunchKernelGGL((axis_cols_kernel<LPP, VEC, kColsLse>), grid, block, 0, stream, x, out, d,
+                         p.ctiles, p.chunks, p.rc, nullptr);
+    return hipGetLastError();
+  }
+  constexpr int C = 4 * LPP;
+  auto *pairs = reinterpret_cast<float2 *>(ws);
+  float2 *fin = pairs + d.outer * p.ctiles * p.chunks * C;
+  hipLaunchKernelGGL((axis_cols_kernel<LPP, VEC, kColsPartial>), grid, block, 0, stream, x, out, d,
+                     p.ctiles, p.chunks, p.rc, pairs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = d.outer * p.ctiles * C;  // one wave each
+  const dim3 mgrid((uint32_t)((n + 3) / 4));
+  if (lsm)
+    hipLaunchKernelGGL(axis_cols_merge_kernel<true>, mgrid, dim3(256), 0, stream, pairs, out, fin,
+                       d, p.ctiles, p.chunks, C);
+  else
+    hipLaunchKernelGGL(axis_cols_merge_kernel<false>, mgrid, dim3(256), 0, stream, pairs, out,
+                       fin, d, p.ctiles, p.chunks, C);
+  e = hipGetLastError();
+  if (e != hipSuccess || !lsm) return e;
+  hipLaunchKernelGGL((axis_cols_apply_kernel<LPP, VEC>), grid, block, 0, stream, x, out, d,
+                     p.ctiles, p.chunks, p.rc, fin);
+  return hipGetLastError();
+}
+
+template <bool VEC>
+hipError_t launch_cols_v(const float *x, float *out, const AxisDims &d, bool lsm,
+                         const ColsPlan &p, void *ws, hipStream_t stream) {
+  switch (p.lpp) {
+    case 1: return launch_cols_t<1, VEC>(x, out, d, lsm, p, ws, stream);
+    case 2: return launch_cols_t<2, VEC>(x, out, d, lsm, p, ws, stream);
+    case 4: return launch_cols_t<4, VEC>(x, out, d, lsm, p, ws, stream);
+    case 8: return launch_cols_t<8, VEC>(x, out, d, lsm, p, ws, stream);
+    case 16: return launch_cols_t<16, VEC>(x, out, d, lsm, p, ws, stream);
+    case 32: return launch_cols_t<32, VEC>(x, out, d, lsm, p, ws, stream);
+    case 64: return launch_cols_t<64, VEC>(x, out, d, lsm, p, ws, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+size_t cols_workspace_bytes(const AxisDims &d, bool lsm) {
+  ColsPlan p;
+  return cols_plan(d, true, p) ? cols_ws_bytes(d, p, lsm) : 0;
+}
+
+bool launch_cols(const float *x, float *out, const AxisDims &d, bool lsm, bool with_ws, void *ws,
+                 hipStream_t stream, hipError_t &e) {
+  ColsPlan p;
+  if (!cols_plan(d, with_ws, p)) return false;
+  if (p.chunks > 1 && ws == nullptr) return false;  // the caller passed no workspace after all
+  const uintptr_t a = (uintptr_t)x | (uintptr_t)out;
+  const int64_t st = d.inner | d.xso | d.xsr | (lsm ? (d.yso | d.ysr) : 0);
+  const bool vec = (st % 4 == 0) && ((lsm ? a : (uintptr_t)x) % 16 == 0);
+  e = vec ? launch_cols_v<true>(x, out, d, lsm, p, ws, stream)
+          : launch_cols_v<false>(x, out, d, lsm, p, ws, stream);
+  return true;
+}
+
+}  // namespace lse

@@ -112,6 +112,36 @@ __device__ __forceinline__ float merge_weight(float mk, float M) {
   return (mk == M) ? 1.0f : expf(mk - M);
 }
 
+// Shift of a running sum whose max is m: m itself when finite, 0 for +-inf
+// (then exp(v - 0) counts a +inf value as inf and a -inf one as 0, and the
+// final m + log s is +inf or -inf as it should be).
+__device__ __forceinline__ float safe_shift(float m) { return is_finite(m) ? m : 0.0f; }
+
+// Fold one block of NB values v[0..NB) of one output into its running (m, s):
+// s is kept relative to safe_shift(m); a NaN value makes s NaN (fmaxf drops
+// it from m), and m + log s is the logsumexp of everything folded.
+template <int NB>
+__device__ __forceinline__ void fold_block(const float (&v)[NB], float &m, float &s) {
+  float bm = v[0];
+#pragma unroll
+  for (int i = 1; i < NB; ++i) bm = fmaxf(bm, v[i]);
+  const float mn = fmaxf(m, bm);
+  const float c = safe_shift(mn);
+  // s == 0 means nothing counted yet: skip the rescale (its factor may be inf).
+  float acc = (s == 0.0f) ? 0.0f : s * exp_base2(safe_shift(m) - c);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) acc += exp_base2(v[i] - c);
+  m = mn;
+  s = acc;
+}
+
+// Weight-and-add step of merging running pairs (m_p, s_p) kept by fold_block
+// into the merged max M: s_p exp(m_p - M) relative to safe_shift(M); a pair
+// that counted nothing is skipped (its weight may be inf).
+__device__ __forceinline__ float fold_weighted(float mp, float sp, float M) {
+  return (sp != 0.0f) ? sp * exp_base2(safe_shift(mp) - safe_shift(M)) : 0.0f;
+}
+
 // Packed pair for single-word publication: low 32 bits m, high 32 bits s.  A
 // real pair never packs to 0 (m = +0 implies s >= 1), so 0 means "not yet
 // written" in a cleared workspace.

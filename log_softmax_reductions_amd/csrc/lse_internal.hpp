@@ -18,9 +18,24 @@ struct AxisDims {
   int64_t xso, xsr;
   int64_t yso, ysr;
 };
-hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream);
+// with_ws: the call comes from an entry point that takes a workspace, and ws
+// holds at least axis_workspace_bytes(d.outer, d.R, d.inner, lsm) bytes (ws
+// may be null when that is 0).
+hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream,
+                           bool with_ws = false, void *ws = nullptr);
 hipError_t launch_log_softmax_axis(const float *x, float *y, const AxisDims &d,
-                                   hipStream_t stream);
+                                   hipStream_t stream, bool with_ws = false, void *ws = nullptr);
+// Workspace of the entry points that take one: enough for whichever of the
+// split paths (column split, split rows) the call's sizes can take; 0 when
+// none of them splits.
+size_t axis_workspace_bytes(int64_t outer, int64_t R, int64_t inner, bool lsm);
+
+// Few outputs over many planes (lse_cols.hip): the planes of each tile of
+// columns split across workgroups.  launch_cols returns false when the call
+// does not take this path; otherwise e is the launch status.
+size_t cols_workspace_bytes(const AxisDims &d, bool lsm);
+bool launch_cols(const float *x, float *out, const AxisDims &d, bool lsm, bool with_ws, void *ws,
+                 hipStream_t stream, hipError_t &e);
 
 // ---------------------------------------------------------------- case B
 // Tile geometry of the row kernels (overridable at build time for sweeps).

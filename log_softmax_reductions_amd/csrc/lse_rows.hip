@@ -59,6 +59,13 @@ constexpr int kNW = kRowsThreads / kWave;  // waves per workgroup
 #ifndef LSE_ROWS_NT_STORE
 #define LSE_ROWS_NT_STORE 1       // y is never re-read: non-temporal stores
 #endif
+#ifndef LSE_ROWS_WAIT_MAX_CHUNKS
+// Rows of up to this many chunks merge by waiting for their sibling
+// workgroups; longer ones (more than 2M columns) take three launches, since a
+// row's chunks may then not all fit on the GPU at once and the waiting
+// workgroups would fall back to recomputing their siblings' pairs.
+#define LSE_ROWS_WAIT_MAX_CHUNKS 64
+#endif
 constexpr uint32_t kDefaultSpinLimit = 1u << 24;
 // Poll limit of the split rows' and the conv chain's waits, per host thread
 // (a test hook: 0 forces every pair through the helping path).
@@ -985,9 +992,14 @@ __global__ __launch_bounds__(kRowsThreads) void rows_stream_write_kernel(
 }
 
 // One wave per row: row_lse = M + log(S) of the row's nchunks pairs.
+// One wave per row, 4 rows per workgroup: merges the row's chunk pairs.
+// OUT = kOutLse writes the row's logsumexp to out[row]; kOutLogSoftmax /
+// kOutSoftmax write the pair (M, log S) / (M, 1 / S) of the row to
+// ((float2 *)out)[row] for rows_apply_kernel.
+template <int OUT>
 __global__ __launch_bounds__(256) void lse_rows_merge_kernel(const float2 *__restrict__ partials,
                                                              int64_t rows, int64_t nchunks,
-                                                             float *__restrict__ row_lse) {
+                                                             float *__restrict__ out) {
   const int64_t row = (int64_t)blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
   if (row >= rows) return;  // whole wave exits together
   const int lane = threadIdx.x % kWave;
@@ -1007,12 +1019,50 @@ __global__ __launch_bounds__(256) void lse_rows_merge_kernel(const float2 *__res
   }
   const float S = wave_allreduce(ls, OpSum{});
   if (lane == 0) {
-    float r;
-    if (__builtin_amdgcn_ballot_w64(nan_seen) != 0)
-      r = __builtin_nanf("");
-    else
-      r = is_finite(M) ? M + logf(S) : M;
-    row_lse[row] = r;
+    const bool nan = __builtin_amdgcn_ballot_w64(nan_seen) != 0;
+    if constexpr (OUT == kOutLse) {
+      out[row] = nan ? __builtin_nanf("") : (is_finite(M) ? M + logf(S) : M);
+    } else {
+      const float k = nan ? __builtin_nanf("") : out_scale<OUT == kOutSoftmax>(S);
+      reinterpret_cast<float2 *>(out)[row] = make_float2(M, k);
+    }
+  }
+}
+
+// Third launch of a row split into more chunks than can wait for each other:
+// y = out_value(x, M, k) over one kRowsTile chunk of one row per workgroup,
+// from the row's merged (M, k).  VEC: x, y 16-byte aligned, cols and pitches
+// multiples of 4.
+template <bool VEC, bool SOFTMAX>
+__global__ __launch_bounds__(kRowsThreads) void rows_apply_kernel(
+    const float *__restrict__ x, float *__restrict__ y, int64_t cols, int64_t ldx, int64_t ldy,
+    int64_t nchunks, const float2 *__restrict__ fin) {
+  constexpr int kVec = (int)(kRowsTile / (4 * kRowsThreads));  // float4 per lane
+  const int64_t b = blockIdx.x;
+  const int64_t row = b / nchunks;
+  const int64_t c0 = (b - row * nchunks) * kRowsTile;
+  const int64_t len = (cols - c0 < kRowsTile) ? cols - c0 : kRowsTile;
+  const float2 f = fin[row];
+  const float *xr = x + row * ldx + c0;
+  float *yr = y + row * ldy + c0;
+  const int t = threadIdx.x;
+  if constexpr (VEC) {
+    v4f v[kVec];
+#pragma unroll
+    for (int q = 0; q < kVec; ++q) {
+      const int64_t idx = ((int64_t)q * kRowsThreads + t) * 4;
+      if (idx < len) v[q] = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(xr + idx));
+    }
+#pragma unroll
+    for (int q = 0; q < kVec; ++q) {
+      const int64_t idx = ((int64_t)q * kRowsThreads + t) * 4;
+      if (idx < len)
+        store4(yr + idx, out_value<SOFTMAX>(v[q].x, f.x, f.y), out_value<SOFTMAX>(v[q].y, f.x, f.y),
+               out_value<SOFTMAX>(v[q].z, f.x, f.y), out_value<SOFTMAX>(v[q].w, f.x, f.y));
+    }
+  } else {
+    for (int64_t i = t; i < len; i += kRowsThreads)
+      yr[i] = out_value<SOFTMAX>(__builtin_nontemporal_load(xr + i), f.x, f.y);
   }
 }
 
@@ -1136,6 +1186,33 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
                                              nullptr, 0u, stream);
     });
   }
+  if (p.nchunks > LSE_ROWS_WAIT_MAX_CHUNKS) {
+    // More chunks than can count on waiting for each other: the chunk pairs
+    // of the register tile, a merge per row, then the write from the merged
+    // (M, k) (x read twice).
+    const int64_t nc = (cols + kRowsTile - 1) / kRowsTile;
+    auto *part = reinterpret_cast<float2 *>(reinterpret_cast<char *>(ws) + sizeof(RowsWsHeader));
+    float2 *fin = part + rows * nc;
+    hipError_t e = launch_lse_rows_partial(x, rows, cols, ldx, kRowsTile, part, stream);
+    if (e != hipSuccess) return e;
+    e = for_row_batches(rows, 4 * (0xffffffffll / 256), [&](int64_t r0, int64_t nr) {
+      hipLaunchKernelGGL((lse_rows_merge_kernel<SOFTMAX ? kOutSoftmax : kOutLogSoftmax>),
+                         dim3((uint32_t)((nr + 3) / 4)), dim3(256), 0, stream, part + r0 * nc, nr,
+                         nc, reinterpret_cast<float *>(fin + r0));
+      return hipGetLastError();
+    });
+    if (e != hipSuccess) return e;
+    return for_row_batches(rows, kMaxRowsWorkgroups / nc, [&](int64_t r0, int64_t nr) {
+      const dim3 grid((uint32_t)(nr * nc));
+      if (vec)
+        hipLaunchKernelGGL((rows_apply_kernel<true, SOFTMAX>), grid, dim3(kRowsThreads), 0, stream,
+                           x + r0 * ldx, y + r0 * ldy, cols, ldx, ldy, nc, fin + r0);
+      else
+        hipLaunchKernelGGL((rows_apply_kernel<false, SOFTMAX>), grid, dim3(kRowsThreads), 0,
+                           stream, x + r0 * ldx, y + r0 * ldy, cols, ldx, ldy, nc, fin + r0);
+      return hipGetLastError();
+    });
+  }
   auto *hdr = reinterpret_cast<RowsWsHeader *>(ws);
   auto *pairs = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(ws) + sizeof(RowsWsHeader));
   const int64_t words = (int64_t)(rows_workspace_bytes(rows, cols) / sizeof(uint64_t));
@@ -1182,6 +1259,9 @@ RowsPlan rows_plan(int64_t cols) {
 size_t rows_workspace_bytes(int64_t rows, int64_t cols) {
   const RowsPlan p = rows_plan(cols);
   if (p.nchunks <= 1) return 0;
+  if (p.nchunks > LSE_ROWS_WAIT_MAX_CHUNKS)  // three launches: tile pairs, then (M, k) per row
+    return sizeof(RowsWsHeader) +
+           (size_t)rows * (size_t)((cols + kRowsTile - 1) / kRowsTile + 1) * sizeof(float2);
   return sizeof(RowsWsHeader) + (size_t)rows * (size_t)p.nchunks * sizeof(uint64_t);
 }
 
@@ -1303,7 +1383,7 @@ hipError_t launch_lse_rows_merge(const void *partials, int64_t rows, int64_t nch
   // one wave per row, 4 rows per 256-lane workgroup
   return for_row_batches(rows, 4 * (0xffffffffll / 256), [&](int64_t r0, int64_t nr) {
     const int64_t blocks = (nr + 3) / 4;
-    hipLaunchKernelGGL(lse_rows_merge_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(lse_rows_merge_kernel<kOutLse>, dim3((uint32_t)blocks), dim3(256), 0, stream,
                        reinterpret_cast<const float2 *>(partials) + r0 * nchunks, nr, nchunks,
                        row_lse + r0);
     return hipGetLastError();

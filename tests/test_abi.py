@@ -39,7 +39,7 @@ def test_exports_match_header(lib):
     import subprocess
     from log_softmax_reductions_amd import _lib
     declared = declared_functions()
-    assert len(declared) == 23
+    assert len(declared) == 27
     for name in declared:
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -112,6 +112,38 @@ def test_strided_validation(lib):
     assert lib.softmax_rows_strided(FAKE, FAKE2, 16, 393216, 393220, 393216, None, 0,
                                     None) == LSE_ERR_WORKSPACE
     assert rs(None, None, 0, 8, 8, 8, None, 0, None) == LSE_OK
+
+
+def test_axis_workspace_validation(lib):
+    wb = lib.lse_axis_workspace_bytes
+    # few outputs over many planes: pairs per (column, chunk), plus (M, log S)
+    # per column for log_softmax; 976 chunks of 1025 planes for (1e6, 4)
+    assert wb(1, 1000000, 4, 0) == 4 * 976 * 8
+    assert wb(1, 1000000, 4, 1) == 4 * 976 * 8 + 4 * 8
+    assert wb(128, 64, 15876, 0) == 0 and wb(128, 64, 15876, 1) == 0   # many outputs
+    assert wb(1, 63, 64, 0) == 0                                        # too few planes
+    assert wb(0, 10, 10, 0) == 0 and wb(-1, 10, 10, 0) == 0 and wb(1, 1 << 40, 1 << 40, 0) == 0
+    # long last-axis rows: the split rows' workspace
+    assert wb(1, 100000000, 1, 1) >= lib.log_softmax_rows_workspace_bytes(1, 100000000)
+    assert wb(4, 100000, 1, 0) >= 4 * 7 * 8
+    ax, ax0 = lib.lse_reduce_axis_strided_ws, lib.lse_reduce_axis0_ws
+    lsm = lib.log_softmax_axis_strided_ws
+    need = wb(1, 1000000, 4, 0)
+    far = ctypes.c_void_p(0x7000000000)
+    assert ax(FAKE, FAKE2, 1, 1000000, 4, 4000000, 4, 4, None, 0, None) == LSE_ERR_WORKSPACE
+    assert ax(FAKE, FAKE2, 1, 1000000, 4, 4000000, 4, 4, far, need - 1, None) == LSE_ERR_WORKSPACE
+    assert ax(FAKE, FAKE2, 1, 1000000, 4, 4000000, 4, 4, FAKE, need, None) == LSE_ERR_OVERLAP
+    assert ax(FAKE, FAKE2, 1, 1000000, 4, 4000000, 4, 4, FAKE2, need, None) == LSE_ERR_OVERLAP
+    assert ax(FAKE, FAKE2, 1, 0, 4, 0, 4, 4, far, need, None) == LSE_ERR_SHAPE
+    assert ax(None, FAKE2, 1, 1000000, 4, 4000000, 4, 4, far, need, None) == LSE_ERR_NULL
+    assert ax0(FAKE, FAKE2, 1000000, 4, None, 0, None) == LSE_ERR_WORKSPACE
+    assert ax0(FAKE, FAKE2, -1, 4, None, 0, None) == LSE_ERR_SHAPE
+    need_y = wb(1, 1000000, 4, 1)
+    assert lsm(FAKE, FAKE2, 1, 1000000, 4, 4000000, 4, 4000000, 4, far, need_y - 1,
+               None) == LSE_ERR_WORKSPACE
+    assert lsm(FAKE, FAKE2, 1, 1000000, 4, 4000000, 4, 4000000, 3, far, need_y,
+               None) == LSE_ERR_SHAPE
+    assert ax(None, None, 0, 3, 8, 24, 8, 8, None, 0, None) == LSE_OK     # empty: no-op
 
 
 def test_rows_validation(lib):
