@@ -30,9 +30,15 @@
 namespace lse {
 namespace {
 
-constexpr int kColsWaves = 4;
+#ifndef LSE_COLS_WAVES
+#define LSE_COLS_WAVES 4   // waves per workgroup
+#endif
+#ifndef LSE_COLS_U
+#define LSE_COLS_U 4       // plane steps loaded before they are folded
+#endif
+constexpr int kColsWaves = LSE_COLS_WAVES;
 constexpr int kColsThreads = kColsWaves * kWave;
-constexpr int kColsU = 4;  // plane steps loaded before they are folded
+constexpr int kColsU = LSE_COLS_U;
 #ifndef LSE_COLS_MAX_OUTPUTS
 #define LSE_COLS_MAX_OUTPUTS 32768   // up to this many outputs the column split is taken
 #endif
@@ -42,8 +48,11 @@ constexpr int kColsU = 4;  // plane steps loaded before they are folded
 #ifndef LSE_COLS_TARGET_GROUPS
 #define LSE_COLS_TARGET_GROUPS 2048  // workgroups the chunking aims for
 #endif
+#ifndef LSE_COLS_MIN_ITERS
+#define LSE_COLS_MIN_ITERS 4         // ... and at least this many loop trips per lane
+#endif
 #ifndef LSE_COLS_MIN_PLANES
-#define LSE_COLS_MIN_PLANES 128      // planes per chunk at least (pair traffic <= 1/64 of x)
+#define LSE_COLS_MIN_PLANES 512      // planes per chunk at least
 #endif
 
 enum ColsMode { kColsPartial = 0, kColsLse = 1, kColsLsm = 2 };
@@ -89,6 +98,28 @@ __device__ __forceinline__ void cols_store(float *p, int cl, int64_t ncols, cons
     for (int e = 0; e < 4; ++e) {
       const int j = tile_col<LPP, false>(cl, e);
       if (j < ncols) __builtin_nontemporal_store(r[e], p + j);
+    }
+  }
+}
+
+// y = (x - M) - log S over the lane's planes r, r + STEP, ... < r1, kColsU
+// planes loaded before any is written.
+template <int LPP, bool VEC, int STEP>
+__device__ __forceinline__ void cols_write(const float *xt, float *yt, int64_t xsr, int64_t ysr,
+                                           int64_t r, int64_t r1, int cl, int64_t ncols,
+                                           const float (&fm)[4], const float (&fl)[4]) {
+  for (; r < r1; r += STEP * kColsU) {
+    float q[kColsU][4];
+#pragma unroll
+    for (int u = 0; u < kColsU; ++u)
+      if (r + u * STEP < r1) cols_load<LPP, VEC, true>(xt + (r + u * STEP) * xsr, cl, ncols, q[u]);
+#pragma unroll
+    for (int u = 0; u < kColsU; ++u) {
+      if (r + u * STEP < r1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[u][e] = (q[u][e] - fm[e]) - fl[e];
+        cols_store<LPP, VEC>(yt + (r + u * STEP) * ysr, cl, ncols, q[u]);
+      }
     }
   }
 }
@@ -170,8 +201,7 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
     for (int e = 0; e < 4; ++e) lds_pair[wave][tile_col<LPP, VEC>(cl, e)] = make_float2(m[e], s[e]);
   }
   __syncthreads();
-  if (threadIdx.x < C) {
-    const int col = threadIdx.x;
+  for (int col = threadIdx.x; col < C; col += kColsThreads) {
     float M = lds_pair[0][col].x;
 #pragma unroll
     for (int w = 1; w < kColsWaves; ++w) M = fmaxf(M, lds_pair[w][col].x);
@@ -196,13 +226,7 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
       fl[e] = f.y;
     }
     float *yt = out + o * d.yso + j0;
-    for (int64_t r = r0 + g; r < r1; r += kStep) {
-      float q[4];
-      cols_load<LPP, VEC, true>(xt + r * xsr, cl, ncols, q);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) q[e] = (q[e] - fm[e]) - fl[e];
-      cols_store<LPP, VEC>(yt + r * d.ysr, cl, ncols, q);
-    }
+    cols_write<LPP, VEC, kStep>(xt, yt, xsr, d.ysr, r0 + g, r1, cl, ncols, fm, fl);
   }
 }
 
@@ -272,13 +296,7 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_apply_kernel(
   }
   const float *xt = x + o * d.xso + j0;
   float *yt = y + o * d.yso + j0;
-  for (int64_t r = r0 + g; r < r1; r += kStep) {
-    float q[4];
-    cols_load<LPP, VEC, true>(xt + r * d.xsr, cl, ncols, q);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) q[e] = (q[e] - fm[e]) - fl[e];
-    cols_store<LPP, VEC>(yt + r * d.ysr, cl, ncols, q);
-  }
+  cols_write<LPP, VEC, kStep>(xt, yt, d.xsr, d.ysr, r0 + g, r1, cl, ncols, fm, fl);
 }
 
 struct ColsPlan {
@@ -300,7 +318,7 @@ bool cols_plan(const AxisDims &d, bool with_ws, ColsPlan &p) {
   if (!with_ws) {
     p.chunks = 1;
   } else {
-    const int64_t step = (int64_t)kColsWaves * (kWave / lpp) * kColsU;
+    const int64_t step = (int64_t)kColsWaves * (kWave / lpp) * kColsU * LSE_COLS_MIN_ITERS;
     const int64_t min_planes = step > LSE_COLS_MIN_PLANES ? step : LSE_COLS_MIN_PLANES;
     int64_t k = (LSE_COLS_TARGET_GROUPS + groups - 1) / groups;
     const int64_t kmax = d.R / min_planes;

@@ -117,9 +117,9 @@ def test_strided_validation(lib):
 def test_axis_workspace_validation(lib):
     wb = lib.lse_axis_workspace_bytes
     # few outputs over many planes: pairs per (column, chunk), plus (M, log S)
-    # per column for log_softmax; 976 chunks of 1025 planes for (1e6, 4)
-    assert wb(1, 1000000, 4, 0) == 4 * 976 * 8
-    assert wb(1, 1000000, 4, 1) == 4 * 976 * 8 + 4 * 8
+    # per column for log_softmax; 244 chunks of 4099 planes for (1e6, 4)
+    assert wb(1, 1000000, 4, 0) == 4 * 244 * 8
+    assert wb(1, 1000000, 4, 1) == 4 * 244 * 8 + 4 * 8
     assert wb(128, 64, 15876, 0) == 0 and wb(128, 64, 15876, 1) == 0   # many outputs
     assert wb(1, 63, 64, 0) == 0                                        # too few planes
     assert wb(0, 10, 10, 0) == 0 and wb(-1, 10, 10, 0) == 0 and wb(1, 1 << 40, 1 << 40, 0) == 0
