@@ -23,7 +23,7 @@ Flags: --gpus N (only 1 is supported: this build runs on one GPU),
 --only {rows_large,axis0_large,axis0_walk,conv_chain,softmax_large,axis_chain_layout,copy,
         copy_tile,copy_stream,copy_tile_1_per_cu,rows_odd_cols,rows_offset_view,
         chain_600x520_recompute,chain_600x520_staged,rows_large_reread,short_rows_128,
-        short_rows_100}
+        short_rows_99,few_outputs,one_long_row}
 to run just that kernel
 (for profiler runs; prints timing only).
 """
@@ -239,6 +239,8 @@ def copy_ceiling(x, y, steps=5, warmup=2):
 
 
 SHORT_ROWS = 1 << 20
+FEW_OUT_SHAPE = (1 << 20, 64)   # 64 outputs over 2^20 planes
+LONG_ROW = 100_000_000
 
 
 def bench_secondary(steps=10, warmup=3):
@@ -386,8 +388,8 @@ def bench_secondary(steps=10, warmup=3):
                                  "hbm_frac": round(8 * x.numel() / avg / 1e6 / HBM_PEAK_GBS, 4)}
     del x, y
     # short rows over the last dim (a segment of lanes per row, several rows per
-    # wave): 128 columns (16-byte rows) and 100 columns (4-byte loads)
-    for cols in (128, 100):
+    # wave): 128 columns (16-byte rows) and 99 columns (odd length: 4-byte loads)
+    for cols in (128, 99):
         x = inputs.normal((SHORT_ROWS, cols), seed=17 + cols, sigma=2.0, device="cuda")
         o = torch.empty((SHORT_ROWS,), device="cuda")
         y = torch.empty_like(x)
@@ -404,6 +406,39 @@ def bench_secondary(steps=10, warmup=3):
             "log_softmax_GB/s": round(nb_lsm / lsm_ms / 1e6, 1),
             "log_softmax_hbm_frac": round(nb_lsm / lsm_ms / 1e6 / HBM_PEAK_GBS, 4)}
         del x, o, y
+    # few outputs over many planes (the column split, workspace from the
+    # binding) and one very long row (split logsumexp / three-launch log_softmax)
+    x = inputs.normal(FEW_OUT_SHAPE, seed=19, sigma=2.0, device="cuda")
+    o = torch.empty(FEW_OUT_SHAPE[1:], device="cuda")
+    y = torch.empty_like(x)
+    _, ev = timed_launches(lambda: L.lse_reduce_axis0(x, o), steps, warmup)
+    lse_ms = sum(ev) / len(ev)
+    _, ev = timed_launches(lambda: L.log_softmax_axis(x, 0, y), steps, warmup)
+    lsm_ms = sum(ev) / len(ev)
+    nb_lse, nb_lsm = 4 * (x.numel() + o.numel()), 8 * x.numel()
+    out["few_outputs"] = {
+        "workload": f"logsumexp and log_softmax dim=0 of {FEW_OUT_SHAPE} fp32 N(0,4)",
+        "lse_ms": round(lse_ms, 4), "lse_GB/s": round(nb_lse / lse_ms / 1e6, 1),
+        "lse_hbm_frac": round(nb_lse / lse_ms / 1e6 / HBM_PEAK_GBS, 4),
+        "log_softmax_ms": round(lsm_ms, 4), "log_softmax_GB/s": round(nb_lsm / lsm_ms / 1e6, 1),
+        "log_softmax_hbm_frac": round(nb_lsm / lsm_ms / 1e6 / HBM_PEAK_GBS, 4),
+        "note": "log_softmax reads x twice here (pairs, merge, write launches)"}
+    del x, o, y
+    x = inputs.normal((1, LONG_ROW), seed=23, device="cuda")
+    o = torch.empty((1,), device="cuda")
+    y = torch.empty_like(x)
+    _, ev = timed_launches(lambda: L.lse_reduce_axis(x, 1, o), steps, warmup)
+    lse_ms = sum(ev) / len(ev)
+    _, ev = timed_launches(lambda: L.log_softmax_rows(x, y), steps, warmup)
+    lsm_ms = sum(ev) / len(ev)
+    out["one_long_row"] = {
+        "workload": f"logsumexp and log_softmax of one row of {LONG_ROW} fp32 N(0,1)",
+        "lse_ms": round(lse_ms, 4), "lse_GB/s": round(4 * LONG_ROW / lse_ms / 1e6, 1),
+        "log_softmax_ms": round(lsm_ms, 4),
+        "log_softmax_GB/s": round(8 * LONG_ROW / lsm_ms / 1e6, 1),
+        "log_softmax_hbm_frac": round(8 * LONG_ROW / lsm_ms / 1e6 / HBM_PEAK_GBS, 4),
+        "note": "log_softmax reads x twice here (more chunks than can wait for each other)"}
+    del x, o, y
     # small cases: hot latency per call, eagerly from Python (host launch
     # included) and as back-to-back calls replayed from a HIP graph
     x = inputs.make("rows_small", "cuda")
@@ -465,7 +500,7 @@ def run_only(which, steps, warmup):
         o = torch.empty((128, 1, 126, 126), device="cuda")
         wall, ev = timed_launches(lambda: L.fused_conv_gn_act_lse(x, w, b, g, be, 16, 1e-5, o),
                                   steps, warmup)
-    elif which in ("short_rows_128", "short_rows_100"):
+    elif which in ("short_rows_128", "short_rows_99"):
         # logsumexp then log_softmax over the last dim of (2^20, cols)
         cols = int(which.rsplit("_", 1)[1])
         x = inputs.normal((SHORT_ROWS, cols), seed=17 + cols, sigma=2.0, device="cuda")
@@ -473,6 +508,19 @@ def run_only(which, steps, warmup):
         y = torch.empty_like(x)
         timed_launches(lambda: L.lse_reduce_axis(x, 1, o), steps, warmup)
         wall, ev = timed_launches(lambda: L.log_softmax_axis(x, 1, y), steps, warmup)
+    elif which == "few_outputs":
+        # logsumexp then log_softmax over dim 0 of (2^20, 64)
+        x = inputs.normal(FEW_OUT_SHAPE, seed=19, sigma=2.0, device="cuda")
+        o = torch.empty(FEW_OUT_SHAPE[1:], device="cuda")
+        y = torch.empty_like(x)
+        timed_launches(lambda: L.lse_reduce_axis0(x, o), steps, warmup)
+        wall, ev = timed_launches(lambda: L.log_softmax_axis(x, 0, y), steps, warmup)
+    elif which == "one_long_row":
+        x = inputs.normal((1, LONG_ROW), seed=23, device="cuda")
+        o = torch.empty((1,), device="cuda")
+        y = torch.empty_like(x)
+        timed_launches(lambda: L.lse_reduce_axis(x, 1, o), steps, warmup)
+        wall, ev = timed_launches(lambda: L.log_softmax_rows(x, y), steps, warmup)
     elif which in ("chain_600x520_recompute", "chain_600x520_staged"):
         # the two-launch chain on samples too large for one fused launch
         x, w, b, g, be = inputs.conv_chain_inputs(N=8, H=600, W=520, seed=5, device="cuda")

@@ -230,35 +230,56 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
   }
 }
 
-// One wave per (o, t, column) of the tiles, 4 per workgroup: lane l folds the
-// column's chunk pairs l, l + 64, ... in order, then the lanes' pairs merge
-// across the wave (the same order on every call).  LSM stores (M, log S) per
-// column for the apply launch, else writes the logsumexp.
-template <bool LSM>
+// WAVES waves per (o, t, column) of the tiles (1 or 4; 256-lane workgroups):
+// lane i of the column's lanes folds its chunk pairs i, i + 64 WAVES, ... in
+// order (4 loads in flight), then the pairs of the wave's lanes and of the
+// column's waves merge (the same order on every call).  LSM stores (M, log S)
+// per column for the apply launch, else writes the logsumexp.
+template <bool LSM, int WAVES>
 __global__ __launch_bounds__(256) void axis_cols_merge_kernel(const float2 *__restrict__ pairs,
                                                               float *__restrict__ out,
                                                               float2 *__restrict__ fin,
                                                               AxisDims d, int64_t ctiles,
                                                               int64_t chunks, int C) {
-  const int64_t i = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;  // (o, t, column)
-  const int lane = threadIdx.x % kWave;
-  if (i >= d.outer * ctiles * C) return;  // whole waves
+  constexpr int kLanes = WAVES * kWave;  // lanes per column
+  __shared__ float2 lds[4];
+  const int64_t i = (int64_t)blockIdx.x * (4 / WAVES) + threadIdx.x / kLanes;  // (o, t, column)
+  const int tc = threadIdx.x % kLanes;
+  if (i >= d.outer * ctiles * C) return;  // whole columns
   const int64_t ot = i / C;
   const int col = (int)(i - ot * C);
   const int64_t t = ot % ctiles;
   const int64_t o = ot / ctiles;
   const int64_t j = t * C + col;
-  if (j >= d.inner) return;  // whole waves
+  if (j >= d.inner) return;  // whole columns
   const float2 *p = pairs + i * chunks;
   float m = -__builtin_inff(), s = 0.0f;
-  for (int64_t k = lane; k < chunks; k += kWave) {
-    const float2 q = p[k];
-    const float mn = fmaxf(m, q.x);
-    s = fold_weighted(m, s, mn) + fold_weighted(q.x, q.y, mn);
-    m = mn;
+  for (int64_t k0 = tc; k0 < chunks; k0 += 4 * kLanes) {
+    float2 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      q[u] = (k0 + u * kLanes < chunks) ? p[k0 + u * kLanes] : make_float2(-__builtin_inff(), 0.0f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float mn = fmaxf(m, q[u].x);
+      s = fold_weighted(m, s, mn) + fold_weighted(q[u].x, q[u].y, mn);
+      m = mn;
+    }
   }
   merge_lanes<1>(m, s);
-  if (lane == 0) {
+  if constexpr (WAVES > 1) {
+    const int w = threadIdx.x / kWave;
+    if (threadIdx.x % kWave == 0) lds[w] = make_float2(m, s);
+    __syncthreads();
+    m = lds[0].x;
+#pragma unroll
+    for (int v = 1; v < WAVES; ++v) m = fmaxf(m, lds[v].x);
+    float S = 0.0f;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) S += fold_weighted(lds[v].x, lds[v].y, m);
+    s = S;
+  }
+  if (tc == 0) {
     if constexpr (LSM)
       fin[i] = make_float2(m, logf(s));
     else
@@ -360,14 +381,25 @@ hipError_t launch_cols_t(const float *x, float *out, const AxisDims &d, bool lsm
                      p.ctiles, p.chunks, p.rc, pairs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t n = d.outer * p.ctiles * C;  // one wave each
-  const dim3 mgrid((uint32_t)((n + 3) / 4));
-  if (lsm)
-    hipLaunchKernelGGL(axis_cols_merge_kernel<true>, mgrid, dim3(256), 0, stream, pairs, out, fin,
-                       d, p.ctiles, p.chunks, C);
-  else
-    hipLaunchKernelGGL(axis_cols_merge_kernel<false>, mgrid, dim3(256), 0, stream, pairs, out,
-                       fin, d, p.ctiles, p.chunks, C);
+  // a workgroup per column for long chunk lists, else a wave per column
+  const int64_t ncol = d.outer * p.ctiles * C;
+  const bool wide = p.chunks > 4 * kWave;
+  const dim3 mgrid((uint32_t)(wide ? ncol : (ncol + 3) / 4));
+  if (lsm) {
+    if (wide)
+      hipLaunchKernelGGL((axis_cols_merge_kernel<true, 4>), mgrid, dim3(256), 0, stream, pairs,
+                         out, fin, d, p.ctiles, p.chunks, C);
+    else
+      hipLaunchKernelGGL((axis_cols_merge_kernel<true, 1>), mgrid, dim3(256), 0, stream, pairs,
+                         out, fin, d, p.ctiles, p.chunks, C);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((axis_cols_merge_kernel<false, 4>), mgrid, dim3(256), 0, stream, pairs,
+                         out, fin, d, p.ctiles, p.chunks, C);
+    else
+      hipLaunchKernelGGL((axis_cols_merge_kernel<false, 1>), mgrid, dim3(256), 0, stream, pairs,
+                         out, fin, d, p.ctiles, p.chunks, C);
+  }
   e = hipGetLastError();
   if (e != hipSuccess || !lsm) return e;
   hipLaunchKernelGGL((axis_cols_apply_kernel<LPP, VEC>), grid, block, 0, stream, x, out, d,

@@ -1029,6 +1029,78 @@ __global__ __launch_bounds__(256) void lse_rows_merge_kernel(const float2 *__res
   }
 }
 
+// Running merge of pair (mk, sk) into (m, s), both in the chunk pairs'
+// convention (s relative to m; +inf counted, -inf and NaN-free as in
+// chunk_pair): the same in either operand order, bit for bit.
+__device__ __forceinline__ void merge_pair_into(float &m, float &s, float mk, float sk) {
+  const float mn = fmaxf(m, mk);
+  s = s * merge_weight(m, mn) + sk * merge_weight(mk, mn);
+  m = mn;
+}
+
+// lse_rows_merge_kernel for rows of many chunks: one 256-lane workgroup per
+// row, lane i merging chunks i, i + 256, ... (4 loads in flight) in one pass,
+// then the lanes' pairs merge across the wave and the 4 waves in a fixed
+// order.  A NaN anywhere makes the sum NaN, and the row's result NaN.
+template <int OUT>
+__global__ __launch_bounds__(256) void rows_merge_wide_kernel(const float2 *__restrict__ partials,
+                                                              int64_t nchunks,
+                                                              float *__restrict__ out) {
+  __shared__ float2 lds[4];
+  const int64_t row = blockIdx.x;
+  const float2 *pr = partials + row * nchunks;
+  float m = -__builtin_inff(), s = 0.0f;
+  for (int64_t k0 = threadIdx.x; k0 < nchunks; k0 += 4 * 256) {
+    float2 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      q[u] = (k0 + u * 256 < nchunks) ? pr[k0 + u * 256] : make_float2(-__builtin_inff(), 0.0f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) merge_pair_into(m, s, q[u].x, q[u].y);
+  }
+#pragma unroll
+  for (int k = 1; k < kWave; k <<= 1) {
+    const float mo = __shfl_xor(m, k), so = __shfl_xor(s, k);
+    merge_pair_into(m, s, mo, so);
+  }
+  if (threadIdx.x % kWave == 0) lds[threadIdx.x / kWave] = make_float2(m, s);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = lds[0].x, S = lds[0].y;
+#pragma unroll
+    for (int w = 1; w < 4; ++w) merge_pair_into(M, S, lds[w].x, lds[w].y);
+    const bool nan = S != S;
+    if constexpr (OUT == kOutLse) {
+      out[row] = nan ? __builtin_nanf("") : (is_finite(M) ? M + logf(S) : M);
+    } else {
+      const float k = nan ? __builtin_nanf("") : out_scale<OUT == kOutSoftmax>(S);
+      reinterpret_cast<float2 *>(out)[row] = make_float2(M, k);
+    }
+  }
+}
+
+// Row merges: a wave per row, or a workgroup per row past 256 chunks.
+#ifndef LSE_ROWS_MERGE_WIDE
+#define LSE_ROWS_MERGE_WIDE 256
+#endif
+template <int OUT>
+hipError_t launch_rows_merge(const float2 *partials, int64_t rows, int64_t nchunks, float *out,
+                             hipStream_t stream) {
+  const int64_t per = (OUT == kOutLse) ? 1 : 2;  // floats of output per row
+  if (nchunks > LSE_ROWS_MERGE_WIDE) {
+    return for_row_batches(rows, 0xffffffffll / 256, [&](int64_t r0, int64_t nr) {
+      hipLaunchKernelGGL(rows_merge_wide_kernel<OUT>, dim3((uint32_t)nr), dim3(256), 0, stream,
+                         partials + r0 * nchunks, nchunks, out + r0 * per);
+      return hipGetLastError();
+    });
+  }
+  return for_row_batches(rows, 4 * (0xffffffffll / 256), [&](int64_t r0, int64_t nr) {
+    hipLaunchKernelGGL(lse_rows_merge_kernel<OUT>, dim3((uint32_t)((nr + 3) / 4)), dim3(256), 0,
+                       stream, partials + r0 * nchunks, nr, nchunks, out + r0 * per);
+    return hipGetLastError();
+  });
+}
+
 // Third launch of a row split into more chunks than can wait for each other:
 // y = out_value(x, M, k) over one kRowsTile chunk of one row per workgroup,
 // from the row's merged (M, k).  VEC: x, y 16-byte aligned, cols and pitches
@@ -1195,12 +1267,8 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
     float2 *fin = part + rows * nc;
     hipError_t e = launch_lse_rows_partial(x, rows, cols, ldx, kRowsTile, part, stream);
     if (e != hipSuccess) return e;
-    e = for_row_batches(rows, 4 * (0xffffffffll / 256), [&](int64_t r0, int64_t nr) {
-      hipLaunchKernelGGL((lse_rows_merge_kernel<SOFTMAX ? kOutSoftmax : kOutLogSoftmax>),
-                         dim3((uint32_t)((nr + 3) / 4)), dim3(256), 0, stream, part + r0 * nc, nr,
-                         nc, reinterpret_cast<float *>(fin + r0));
-      return hipGetLastError();
-    });
+    e = launch_rows_merge<SOFTMAX ? kOutSoftmax : kOutLogSoftmax>(
+        part, rows, nc, reinterpret_cast<float *>(fin), stream);
     if (e != hipSuccess) return e;
     return for_row_batches(rows, kMaxRowsWorkgroups / nc, [&](int64_t r0, int64_t nr) {
       const dim3 grid((uint32_t)(nr * nc));
@@ -1380,14 +1448,8 @@ hipError_t launch_log_softmax_rows_no_ws(const float *x, float *y, int64_t rows,
 hipError_t launch_lse_rows_merge(const void *partials, int64_t rows, int64_t nchunks,
                                  float *row_lse, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  // one wave per row, 4 rows per 256-lane workgroup
-  return for_row_batches(rows, 4 * (0xffffffffll / 256), [&](int64_t r0, int64_t nr) {
-    const int64_t blocks = (nr + 3) / 4;
-    hipLaunchKernelGGL(lse_rows_merge_kernel<kOutLse>, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                       reinterpret_cast<const float2 *>(partials) + r0 * nchunks, nr, nchunks,
-                       row_lse + r0);
-    return hipGetLastError();
-  });
+  return launch_rows_merge<kOutLse>(reinterpret_cast<const float2 *>(partials), rows, nchunks,
+                                    row_lse, stream);
 }
 
 }  // namespace lse
