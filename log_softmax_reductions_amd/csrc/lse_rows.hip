@@ -859,24 +859,45 @@ constexpr int seg_rows_per_pass(int vpl, int out) {
   return vpl >= target ? 1 : target / vpl;
 }
 
-// Short rows: a segment of G lanes (a power of two, 4..64) per row, 64 / G
-// rows per wave, kSegWaves waves per workgroup.  Lane s of a segment holds the
-// row's float4 vectors q G + s (VEC: x, y 16-byte aligned, cols and pitches
-// multiples of 4) or its values q G + s (any 4-byte alignment), padding with
-// -inf, so each load instruction of a segment reads one contiguous span of its
-// row and, for packed rows (pitch = cols), the wave's load is one contiguous
-// span across its rows.  The row's max and sum are all-reductions inside the
+// Short rows: a segment of G lanes (a power of two, 1..64) per row, 64 / G
+// rows per wave (NR passes of them), kSegWaves waves per workgroup.  Lane s of
+// a segment holds the row's 4-value vectors q G + s, padding with -inf: one
+// 16-byte access each, at 16-byte alignment (kSegA16) or at the 4-byte phase
+// all rows share (kSegA4: a view one float off the grid), or, when rows sit at
+// differing phases, its values q G + s one per access (16-byte accesses
+// straddling lines measured up to 18 % slower there).  Each load instruction
+// of a segment reads one contiguous span of its row and, for packed rows
+// (pitch = cols), the wave's load is one contiguous span across its rows.  The row's max and sum are all-reductions inside the
 // segment (DPP and permlane swaps): no LDS, no barrier, no idle lanes for rows
 // of a few to a thousand columns.  OUT picks the result: log_softmax or softmax
 // rows from the registers, or the row's logsumexp alone (y[row * ldy]).  Same
 // pair arithmetic as chunk_pair.
-template <int G, int VPL, int NR, bool VEC, int OUT>
+enum SegLayout {
+  kSegA16 = 0,    // x, y 16-byte aligned, cols and pitches multiples of 4
+  kSegA4 = 1,     // cols and pitches multiples of 4, x or y at another 4-byte phase
+  kSegScalar = 2  // rows at differing phases (cols or a pitch not a multiple of 4)
+};
+
+// 16-byte load / non-temporal store at 4-byte alignment (gfx950 accepts
+// dword-aligned 16-byte global accesses).
+__device__ __forceinline__ v4a4 load4_a4(const float *p) {
+#if LSE_ROWS_NT_LOAD
+  return __builtin_nontemporal_load(reinterpret_cast<const v4a4 *>(p));
+#else
+  return *reinterpret_cast<const v4a4 *>(p);
+#endif
+}
+__device__ __forceinline__ void store4_a4(float *p, float a, float b, float c, float d) {
+  __builtin_nontemporal_store(v4a4{a, b, c, d}, reinterpret_cast<v4a4 *>(p));
+}
+
+template <int G, int VPL, int NR, int LAY, int OUT>
 __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
     const float *__restrict__ x, float *__restrict__ y, int64_t rows, int64_t cols, int64_t ldx,
     int64_t ldy) {
   constexpr bool SOFTMAX = OUT == kOutSoftmax;
-  constexpr int kPerLoad = VEC ? 4 : 1;  // values per load
-  constexpr int kSegs = kWave / G;       // segments per wave
+  constexpr int kPerLoad = LAY == kSegScalar ? 1 : 4;  // values per load
+  constexpr int kSegs = kWave / G;                     // segments per wave
   const int lane = threadIdx.x % kWave;
   const int s = lane % G;
   const int64_t row0 =
@@ -893,23 +914,32 @@ __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
 #pragma unroll
     for (int q = 0; q < VPL / kPerLoad; ++q) {
       const int64_t idx = ((int64_t)q * G + s) * kPerLoad;
-      if constexpr (VEC) {
+      float *vq = &v[j][kPerLoad * q];
+      if constexpr (LAY == kSegA16) {
         if (live && idx < cols) {  // cols % 4 == 0: a vector is wholly in or out
 #if LSE_ROWS_NT_LOAD
           const v4f f = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(xr + idx));
 #else
           const v4f f = *reinterpret_cast<const v4f *>(xr + idx);
 #endif
-          v[j][4 * q] = f.x; v[j][4 * q + 1] = f.y; v[j][4 * q + 2] = f.z; v[j][4 * q + 3] = f.w;
+          vq[0] = f.x; vq[1] = f.y; vq[2] = f.z; vq[3] = f.w;
         } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[j][4 * q + r] = -__builtin_inff();
+          for (int r = 0; r < 4; ++r) vq[r] = -__builtin_inff();
+        }
+      } else if constexpr (LAY == kSegA4) {
+        if (live && idx < cols) {  // cols % 4 == 0: a vector is wholly in or out
+          const v4a4 f = load4_a4(xr + idx);
+          vq[0] = f.x; vq[1] = f.y; vq[2] = f.z; vq[3] = f.w;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vq[r] = -__builtin_inff();
         }
       } else {
 #if LSE_ROWS_NT_LOAD
-        v[j][q] = (live && idx < cols) ? __builtin_nontemporal_load(xr + idx) : -__builtin_inff();
+        vq[0] = (live && idx < cols) ? __builtin_nontemporal_load(xr + idx) : -__builtin_inff();
 #else
-        v[j][q] = (live && idx < cols) ? xr[idx] : -__builtin_inff();
+        vq[0] = (live && idx < cols) ? xr[idx] : -__builtin_inff();
 #endif
       }
     }
@@ -939,14 +969,17 @@ __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
 #pragma unroll
       for (int q = 0; q < VPL / kPerLoad; ++q) {
         const int64_t idx = ((int64_t)q * G + s) * kPerLoad;
+        const float *vq = &v[j][kPerLoad * q];
         if (idx < cols) {
-          if constexpr (VEC)
-            store4(yr + idx, out_value<SOFTMAX>(v[j][4 * q], M, k),
-                   out_value<SOFTMAX>(v[j][4 * q + 1], M, k),
-                   out_value<SOFTMAX>(v[j][4 * q + 2], M, k),
-                   out_value<SOFTMAX>(v[j][4 * q + 3], M, k));
-          else
-            yr[idx] = out_value<SOFTMAX>(v[j][q], M, k);
+          if constexpr (LAY == kSegA16) {
+            store4(yr + idx, out_value<SOFTMAX>(vq[0], M, k), out_value<SOFTMAX>(vq[1], M, k),
+                   out_value<SOFTMAX>(vq[2], M, k), out_value<SOFTMAX>(vq[3], M, k));
+          } else if constexpr (LAY == kSegA4) {
+            store4_a4(yr + idx, out_value<SOFTMAX>(vq[0], M, k), out_value<SOFTMAX>(vq[1], M, k),
+                      out_value<SOFTMAX>(vq[2], M, k), out_value<SOFTMAX>(vq[3], M, k));
+          } else {
+            yr[idx] = out_value<SOFTMAX>(vq[0], M, k);
+          }
         }
       }
     }
@@ -1193,16 +1226,19 @@ hipError_t for_row_batches(int64_t rows, int64_t max_rows, F launch) {
 }
 
 template <int G, int VPL, int OUT>
-void launch_seg(bool vec, dim3 grid, hipStream_t stream, const float *x, float *y, int64_t rows,
+void launch_seg(int lay, dim3 grid, hipStream_t stream, const float *x, float *y, int64_t rows,
                 int64_t cols, int64_t ldx, int64_t ldy) {
   constexpr int NR = seg_rows_per_pass(VPL, OUT);
   const dim3 block(kWave * kSegWaves);
-  if (vec)
-    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, true, OUT>), grid, block, 0, stream, x, y,
+  if (lay == kSegA16)
+    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegA16, OUT>), grid, block, 0, stream, x, y,
+                       rows, cols, ldx, ldy);
+  else if (lay == kSegA4)
+    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegA4, OUT>), grid, block, 0, stream, x, y,
                        rows, cols, ldx, ldy);
   else
-    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, false, OUT>), grid, block, 0, stream, x, y,
-                       rows, cols, ldx, ldy);
+    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegScalar, OUT>), grid, block, 0, stream, x,
+                       y, rows, cols, ldx, ldy);
 }
 
 // Rows of at most LSE_ROWS_SEG_MAX columns through rows_seg_kernel: the
@@ -1220,6 +1256,9 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
   int vpl = 4;
   if (g == kWave)
     while (vpl * kWave < cols) vpl *= 2;
+  // 16-byte accesses when all rows share one 4-byte phase
+  const bool one_phase = cols % 4 == 0 && ldx % 4 == 0 && (OUT == kOutLse || ldy % 4 == 0);
+  const int lay = vec ? kSegA16 : (one_phase ? kSegA4 : kSegScalar);
   const int64_t rows_per_group = (int64_t)kSegWaves * (kWave / g) * seg_rows_per_pass(vpl, OUT);
   const int64_t max_groups = 0xffffffffll / (kWave * kSegWaves);  // 32-bit work-item count
   return for_row_batches(rows, max_groups * rows_per_group, [&](int64_t r0, int64_t nr) {
@@ -1227,15 +1266,15 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
     const float *xb = x + r0 * ldx;
     float *yb = y + r0 * ldy;
     switch (g == kWave ? kWave * vpl : g) {
-      case 1: launch_seg<1, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 2: launch_seg<2, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 4: launch_seg<4, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 8: launch_seg<8, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 16: launch_seg<16, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 32: launch_seg<32, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 4 * kWave: launch_seg<64, 4, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 8 * kWave: launch_seg<64, 8, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 16 * kWave: launch_seg<64, 16, OUT>(vec, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 1: launch_seg<1, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 2: launch_seg<2, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 4: launch_seg<4, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 8: launch_seg<8, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 16: launch_seg<16, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 32: launch_seg<32, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 4 * kWave: launch_seg<64, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 8 * kWave: launch_seg<64, 8, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 16 * kWave: launch_seg<64, 16, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
