@@ -289,6 +289,42 @@ static void case_axis0(hipStream_t s) {
   CHECK_HIP(hipFree(dx)); CHECK_HIP(hipFree(dout));
 }
 
+/* Few outputs over many planes with a workspace (column split), and the same
+   call without one. */
+static void case_axis0_ws(hipStream_t s) {
+  const int64_t R = 300000, inner = 12, n = R * inner;
+  float *x = normal_array(n, 2.0, 14), *dx = to_device(x, n), *dout = to_device(NULL, inner);
+  float *dy = to_device(NULL, n);
+  double *ref = (double *)malloc(inner * sizeof(double));
+  const size_t wl = lse_axis_workspace_bytes(1, R, inner, 0);
+  const size_t wm = lse_axis_workspace_bytes(1, R, inner, 1);
+  EXPECT(wl > 0 && wm > wl, "few-output workspace sizes");
+  void *ws = NULL;
+  CHECK_HIP(hipMalloc(&ws, wm));
+  EXPECT(lse_reduce_axis0_ws(dx, dout, R, inner, NULL, 0, s) == LSE_ERR_WORKSPACE,
+         "missing workspace");
+  check_status(lse_reduce_axis0_ws(dx, dout, R, inner, ws, wl, s), "lse_reduce_axis0_ws");
+  CHECK_HIP(hipStreamSynchronize(s));
+  float *got = from_device(dout, inner);
+  oracle_lse_axis0(x, R, inner, ref, 0);
+  compare("lse_reduce_axis0_ws (300000, 12)", got, ref, inner, 1e-5, 2e-6);
+  free(got);
+  check_status(lse_reduce_axis0(dx, dout, R, inner, s), "lse_reduce_axis0 few outputs");
+  CHECK_HIP(hipStreamSynchronize(s));
+  got = from_device(dout, inner);
+  compare("lse_reduce_axis0 (300000, 12)", got, ref, inner, 1e-5, 2e-6);
+  free(got);
+  double *yref = (double *)malloc(n * sizeof(double));
+  check_status(log_softmax_axis_strided_ws(dx, dy, 1, R, inner, n, inner, n, inner, ws, wm, s),
+               "log_softmax_axis_strided_ws");
+  CHECK_HIP(hipStreamSynchronize(s));
+  got = from_device(dy, n);
+  oracle_log_softmax_axis(x, 1, R, inner, yref, 0);
+  compare("log_softmax_axis_strided_ws (1, 300000, 12)", got, yref, n, 1e-5, 2e-6);
+  free(got); free(x); free(ref); free(yref);
+  CHECK_HIP(hipFree(dx)); CHECK_HIP(hipFree(dout)); CHECK_HIP(hipFree(dy)); CHECK_HIP(hipFree(ws));
+}
+
 static void case_rows(hipStream_t s) {
   const int64_t rows = 3, cols = 100000, n = rows * cols;
   float *x = normal_array(n, 3.0, 12), *dx = to_device(x, n), *dy = to_device(NULL, n);
@@ -395,6 +431,7 @@ int main(int argc, char **argv) {
     CHECK_HIP(hipSetDevice(0));
     CHECK_HIP(hipStreamCreate(&s));
     case_axis0(s);
+    case_axis0_ws(s);
     case_rows(s);
     case_strided(s);
     case_chain(s);

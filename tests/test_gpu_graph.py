@@ -117,6 +117,31 @@ def test_graph_strided_calls():
     _check_graph(run, [o1, o2, yr])
 
 
+def test_graph_split_axis_and_long_rows():
+    """The split paths: 16 outputs over 200000 planes (column split, the
+    binding's workspace allocated inside the capture), a row of 2.2M columns
+    (three launches), split logsumexp rows, short rows in segments."""
+    x = inputs.normal((200000, 16), seed=10, device=DEV)
+    o1 = torch.empty(16, device=DEV)
+    o2 = torch.empty_like(x)
+    x2 = inputs.normal((1, 2200000), seed=11, device=DEV)
+    y2 = torch.empty_like(x2)
+    ws2 = torch.empty(L.log_softmax_rows_workspace_bytes(1, 2200000), dtype=torch.uint8,
+                      device=DEV)
+    x3 = inputs.normal((4, 40000), seed=12, device=DEV)
+    o3 = torch.empty(4, device=DEV)
+    x4 = inputs.normal((3000, 100), seed=13, device=DEV)
+    y4 = torch.empty_like(x4)
+
+    def run():
+        L.lse_reduce_axis0(x, o1)
+        L.log_softmax_axis(x, 0, o2)
+        L.log_softmax_rows(x2, y2, ws2)
+        L.lse_reduce_axis(x3, 1, o3)
+        L.log_softmax_rows(x4, y4)
+    _check_graph(run, [o1, o2, y2, o3, y4])
+
+
 def test_concurrent_streams_match_sequential():
     """Calls on two streams at once, each with its own workspace, give the
     sequential results bit for bit: no state is shared between calls."""
