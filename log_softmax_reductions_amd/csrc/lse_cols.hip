@@ -48,6 +48,9 @@ constexpr int kColsU = LSE_COLS_U;
 #ifndef LSE_COLS_TARGET_GROUPS
 #define LSE_COLS_TARGET_GROUPS 2048  // workgroups the chunking aims for
 #endif
+#ifndef LSE_COLS_LSM_KEEP
+#define LSE_COLS_LSM_KEEP 1          // log_softmax pairs read x with cached loads
+#endif
 #ifndef LSE_COLS_MIN_ITERS
 #define LSE_COLS_MIN_ITERS 4         // ... and at least this many loop trips per lane
 #endif
@@ -55,7 +58,9 @@ constexpr int kColsU = LSE_COLS_U;
 #define LSE_COLS_MIN_PLANES 512      // planes per chunk at least
 #endif
 
-enum ColsMode { kColsPartial = 0, kColsLse = 1, kColsLsm = 2 };
+// kColsPartialKeep: the pairs of a log_softmax, whose apply launch reads x
+// again (cached loads, so that x may still be in the Infinity Cache).
+enum ColsMode { kColsPartial = 0, kColsLse = 1, kColsLsm = 2, kColsPartialKeep = 3 };
 
 typedef float v4f16 __attribute__((ext_vector_type(4)));
 
@@ -169,7 +174,9 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
   const int64_t r1 = (d.R - r0 < rc) ? d.R : r0 + rc;
   const float *xt = x + o * d.xso + j0;
   const int64_t xsr = d.xsr;
-  constexpr bool kNt = MODE != kColsLsm;  // log_softmax reads its planes again: keep them cached
+  // log_softmax reads its planes again: keep them cached
+  constexpr bool kNt = MODE != kColsLsm && MODE != kColsPartialKeep;
+  constexpr bool kPartial = MODE == kColsPartial || MODE == kColsPartialKeep;
   float m[4], s[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
     float S = 0.0f;
 #pragma unroll
     for (int w = 0; w < kColsWaves; ++w) S += fold_weighted(lds_pair[w][col].x, lds_pair[w][col].y, M);
-    if constexpr (MODE == kColsPartial) {
+    if constexpr (kPartial) {
       pairs[(ot * C + col) * chunks + c] = make_float2(M, S);
     } else if constexpr (MODE == kColsLse) {
       if (col < ncols) out[o * d.yso + j0 + col] = M + logf(S);
@@ -377,8 +384,12 @@ hipError_t launch_cols_t(const float *x, float *out, const AxisDims &d, bool lsm
   constexpr int C = 4 * LPP;
   auto *pairs = reinterpret_cast<float2 *>(ws);
   float2 *fin = pairs + d.outer * p.ctiles * p.chunks * C;
-  hipLaunchKernelGGL((axis_cols_kernel<LPP, VEC, kColsPartial>), grid, block, 0, stream, x, out, d,
-                     p.ctiles, p.chunks, p.rc, pairs);
+  if (lsm && LSE_COLS_LSM_KEEP)
+    hipLaunchKernelGGL((axis_cols_kernel<LPP, VEC, kColsPartialKeep>), grid, block, 0, stream, x,
+                       out, d, p.ctiles, p.chunks, p.rc, pairs);
+  else
+    hipLaunchKernelGGL((axis_cols_kernel<LPP, VEC, kColsPartial>), grid, block, 0, stream, x, out,
+                       d, p.ctiles, p.chunks, p.rc, pairs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // a workgroup per column for long chunk lists, else a wave per column

@@ -78,8 +78,10 @@ size_t rows_workspace_bytes(int64_t rows, int64_t cols);
 hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows, int64_t cols,
                                    int64_t ldx, int64_t ldy, void *ws, hipStream_t stream,
                                    bool softmax = false);
+// keep: x is read again by a later launch (cached loads instead of non-temporal).
 hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, int64_t ldx,
-                                   int64_t chunk, void *partials, hipStream_t stream);
+                                   int64_t chunk, void *partials, hipStream_t stream,
+                                   bool keep = false);
 hipError_t launch_lse_rows_merge(const void *partials, int64_t rows,
                                  int64_t nchunks, float *row_lse,
                                  hipStream_t stream);

@@ -59,6 +59,9 @@ constexpr int kNW = kRowsThreads / kWave;  // waves per workgroup
 #ifndef LSE_ROWS_NT_STORE
 #define LSE_ROWS_NT_STORE 1       // y is never re-read: non-temporal stores
 #endif
+#ifndef LSE_ROWS_KEEP_FOR_APPLY
+#define LSE_ROWS_KEEP_FOR_APPLY 1  // three-launch rows: the pair launch reads x with cached loads
+#endif
 #ifndef LSE_ROWS_WAIT_MAX_CHUNKS
 // Rows of up to this many chunks merge by waiting for their sibling
 // workgroups; longer ones (more than 2M columns) take three launches, since a
@@ -103,7 +106,7 @@ typedef float v4a4 __attribute__((ext_vector_type(4), aligned(4)));
 // common case) takes an unchecked path.  p needs 4-byte alignment only (a
 // row whose output is line-aligned and input is not loads 16 bytes at x's own
 // phase); len is a multiple of 4.
-template <int VPL, bool VEC, bool A16 = true>
+template <int VPL, bool VEC, bool A16 = true, bool NT = LSE_ROWS_NT_LOAD != 0>
 __device__ __forceinline__ void load_chunk(const float *__restrict__ p, int64_t len,
                                            float (&v)[VPL]) {
   typedef float v4a16 __attribute__((ext_vector_type(4)));
@@ -114,11 +117,11 @@ __device__ __forceinline__ void load_chunk(const float *__restrict__ p, int64_t 
       const v4 *p4 = reinterpret_cast<const v4 *>(p);
 #pragma unroll
       for (int q = 0; q < VPL / 4; ++q) {
-#if LSE_ROWS_NT_LOAD
-        const v4 f = __builtin_nontemporal_load(p4 + vec4_index<VPL>(q, t));
-#else
-        const v4 f = p4[vec4_index<VPL>(q, t)];
-#endif
+        v4 f;
+        if constexpr (NT)
+          f = __builtin_nontemporal_load(p4 + vec4_index<VPL>(q, t));
+        else
+          f = p4[vec4_index<VPL>(q, t)];
         v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
       }
       return;
@@ -545,10 +548,13 @@ uint32_t clear_blocks(int64_t words) {
 
 // ------------------------------------------------------------ partial/merge
 // One workgroup per (row, chunk) of a chunk that fits the register tile.
-template <int VPL, bool VEC>
+// KEEP: x is read again by a later launch (the three-launch rows): cached
+// loads, so that it may still be in the Infinity Cache.
+template <int VPL, bool VEC, bool KEEP = false>
 __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_kernel(
     const float *__restrict__ x, int64_t cols, int64_t ldx, int64_t nchunks, int64_t chunk,
     float2 *__restrict__ partials) {
+  constexpr bool kNt = LSE_ROWS_NT_LOAD != 0 && !KEEP;
   __shared__ float red[kNW];
   const int64_t t = blockIdx.x;
   const int64_t row = t / nchunks, c = t - row * nchunks;
@@ -558,11 +564,11 @@ __global__ __launch_bounds__(kRowsThreads) void lse_rows_partial_kernel(
   float v[VPL];
   float m, s;
   if constexpr (VEC) {
-    load_chunk<VPL, true>(xc, len, v);
+    load_chunk<VPL, true, true, kNt>(xc, len, v);
     chunk_pair<VPL>(v, red, m, s);
   } else {  // the chunk's aligned body in the tile, its head and tail as extras
     const SpanSplit sp(xc, len);
-    load_chunk<VPL, true>(xc + sp.h, sp.body, v);
+    load_chunk<VPL, true, true, kNt>(xc + sp.h, sp.body, v);
     int64_t col;
     const float xe = extra_value(xc, sp, true, true, col);
     chunk_pair<VPL, true>(v, red, m, s, xe);
@@ -1304,7 +1310,8 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
     const int64_t nc = (cols + kRowsTile - 1) / kRowsTile;
     auto *part = reinterpret_cast<float2 *>(reinterpret_cast<char *>(ws) + sizeof(RowsWsHeader));
     float2 *fin = part + rows * nc;
-    hipError_t e = launch_lse_rows_partial(x, rows, cols, ldx, kRowsTile, part, stream);
+    hipError_t e = launch_lse_rows_partial(x, rows, cols, ldx, kRowsTile, part, stream,
+                                           LSE_ROWS_KEEP_FOR_APPLY != 0);
     if (e != hipSuccess) return e;
     e = launch_rows_merge<SOFTMAX ? kOutSoftmax : kOutLogSoftmax>(
         part, rows, nc, reinterpret_cast<float *>(fin), stream);
@@ -1381,7 +1388,7 @@ hipError_t launch_log_softmax_rows(const float *x, float *y, int64_t rows, int64
 }
 
 hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, int64_t ldx,
-                                   int64_t chunk, void *partials, hipStream_t stream) {
+                                   int64_t chunk, void *partials, hipStream_t stream, bool keep) {
   if (rows == 0) return hipSuccess;
   const int64_t nchunks = (cols + chunk - 1) / chunk;
   const bool vec =
@@ -1398,9 +1405,15 @@ hipError_t launch_lse_rows_partial(const float *x, int64_t rows, int64_t cols, i
     }
 #define LSE_PART_CASE(V)                                                                       \
   case V:                                                                                      \
-    if (vec)                                                                                   \
+    if (vec && keep)                                                                           \
+      hipLaunchKernelGGL((lse_rows_partial_kernel<V, true, true>), grid, dim3(kRowsThreads),   \
+                         0, stream, xb, cols, ldx, nchunks, chunk, out);                       \
+    else if (vec)                                                                              \
       hipLaunchKernelGGL((lse_rows_partial_kernel<V, true>), grid, dim3(kRowsThreads), 0,      \
                          stream, xb, cols, ldx, nchunks, chunk, out);                          \
+    else if (keep)                                                                             \
+      hipLaunchKernelGGL((lse_rows_partial_kernel<V, false, true>), grid, dim3(kRowsThreads),  \
+                         0, stream, xb, cols, ldx, nchunks, chunk, out);                       \
     else                                                                                       \
       hipLaunchKernelGGL((lse_rows_partial_kernel<V, false>), grid, dim3(kRowsThreads), 0,     \
                          stream, xb, cols, ldx, nchunks, chunk, out);                          \
