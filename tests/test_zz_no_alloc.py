@@ -34,6 +34,14 @@ def test_noalloc_two_calls_second_smaller(orc):
     _both(orc, 64, 4096, seed=92, sample=[0, 63])            # one chunk: no scratch used
 
 
+def test_noalloc_long_rows_three_launches(orc):
+    """Rows of more than 64 chunks (three launches; tile pairs and the per-row
+    (M, log S) in the scratch), then a shorter split row."""
+    print("case: noalloc (2, 3000001) then (3, 300000)", flush=True)
+    _both(orc, 2, 3000001, seed=93, sample=[0, 1])
+    _both(orc, 3, 300000, seed=94, sample=[0, 2])
+
+
 def test_noalloc_rejects_more_pairs_than_the_scratch():
     """10921 rows of 393216 columns need 131052 pairs, 12 more than the static
     scratch holds: refused before anything is launched."""
