@@ -24,6 +24,9 @@
 // 4-byte alignment, and the last lane of each run reads the run's last 4
 // columns and writes only those its neighbour does not (ua_columns).
 //
+// A contiguous last axis (inner = 1) runs as rows (lse_rows.hip), and few
+// outputs over many planes as the column split (lse_cols.hip).
+//
 // Running state per output: m = max so far, s = sum of exp(v - c(m)) with the
 // shift c(m) = m when m is finite and 0 when m is +-inf (all values -inf, or
 // some +inf), which makes m + log(s) the literal log(sum(exp(v))) in every

@@ -37,6 +37,14 @@
 //     whole vector are one extra value per lane for lanes 0..33 of wave 0.
 //   * The write is y = (x - M) - log(S): x - M is exact for the large entries,
 //     so the result keeps its accuracy when |M| is large.
+//   * Rows of up to 1024 columns are one segment of 1-64 lanes each, several
+//     rows per wave (rows_seg_kernel), with segment-wide DPP / permlane
+//     reductions and no LDS; the last-axis reductions of the axis calls run
+//     here too (logsumexp alone: one value per row).
+//   * Rows of more than 64 chunks, whose chunks may not all be resident at
+//     once to wait for each other, take three launches: chunk pairs (cached
+//     loads), a merge per row, the write from the merged (M, log S), reading x
+//     twice.
 //   * A launch covers at most kMaxRowsWorkgroups workgroups (its work-item
 //     count must fit 32 bits); longer grids are split into launches over
 //     consecutive rows.
