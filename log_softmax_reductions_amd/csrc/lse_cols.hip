@@ -344,6 +344,10 @@ bool cols_plan(const AxisDims &d, bool with_ws, ColsPlan &p) {
   p.ctiles = (d.inner + C - 1) / C;
   const int64_t groups = d.outer * p.ctiles;
   if (!with_ws) {
+    // One workgroup per tile: more lanes than the plane split (at most 16
+    // waves on a run of outputs, ceil(inner / 4) lanes of each busy) only
+    // while 4 LPP <= 32 columns.
+    if (lpp > 8) return false;
     p.chunks = 1;
   } else {
     const int64_t step = (int64_t)kColsWaves * (kWave / lpp) * kColsU * LSE_COLS_MIN_ITERS;
