@@ -40,7 +40,22 @@ constexpr int kColsWaves = LSE_COLS_WAVES;
 constexpr int kColsThreads = kColsWaves * kWave;
 constexpr int kColsU = LSE_COLS_U;
 #ifndef LSE_COLS_MAX_OUTPUTS
-#define LSE_COLS_MAX_OUTPUTS 32768   // up to this many outputs the column split is taken
+#define LSE_COLS_MAX_OUTPUTS 32768   // without a workspace: up to this many outputs
+#endif
+#ifndef LSE_COLS_MAX_WAVES
+#define LSE_COLS_MAX_WAVES 1024      // with one: while the axis kernels would get this few waves
+#endif
+#ifndef LSE_COLS_NARROW
+#define LSE_COLS_NARROW 128          // ... for inner runs up to this wide,
+#endif
+#ifndef LSE_COLS_WIDE_MAX_WAVES
+#define LSE_COLS_WIDE_MAX_WAVES 128  // ... and this few for wider ones
+#endif
+#ifndef LSE_COLS_LSM_MAX_WAVES
+#define LSE_COLS_LSM_MAX_WAVES 64    // ... or this few, for log_softmax over up to 256 planes
+#endif
+#ifndef LSE_COLS_MIN_PLANES_LOW
+#define LSE_COLS_MIN_PLANES_LOW 128  // chunks down to this many planes when few workgroups
 #endif
 #ifndef LSE_COLS_MINR
 #define LSE_COLS_MINR 64             // ... over at least this many planes
@@ -334,9 +349,8 @@ struct ColsPlan {
 
 // The column-split plan of a call, or false when the call keeps the other
 // axis kernels.  with_ws: the caller can supply cols_workspace_bytes().
-bool cols_plan(const AxisDims &d, bool with_ws, ColsPlan &p) {
+bool cols_plan(const AxisDims &d, bool lsm, bool with_ws, ColsPlan &p) {
   if (d.outer < 1 || d.inner < 1 || d.R < LSE_COLS_MINR) return false;
-  if (d.inner > LSE_COLS_MAX_OUTPUTS || d.outer * d.inner > LSE_COLS_MAX_OUTPUTS) return false;
   int lpp = 1;
   while (lpp < kWave && 4 * lpp < d.inner) lpp *= 2;
   const int64_t C = 4 * lpp;
@@ -344,22 +358,37 @@ bool cols_plan(const AxisDims &d, bool with_ws, ColsPlan &p) {
   p.ctiles = (d.inner + C - 1) / C;
   const int64_t groups = d.outer * p.ctiles;
   if (!with_ws) {
+    if (d.outer * d.inner > LSE_COLS_MAX_OUTPUTS) return false;
     // One workgroup per tile: more lanes than the plane split (at most 16
     // waves on a run of outputs, ceil(inner / 4) lanes of each busy) only
-    // while 4 LPP <= 32 columns.
-    if (lpp > 8) return false;
+    // while a tile holds the whole inner run of at most 32 columns.
+    if (lpp > 8 || p.ctiles > 1) return false;
     p.chunks = 1;
   } else {
+    // The axis kernels give each lane 4 outputs, a wave 256 of one run per
+    // plane: they are left the call when that gives them enough waves, or,
+    // for runs wider than LSE_COLS_NARROW columns (each wave reading 512 B or
+    // more per plane), a moderate number of them; and, for log_softmax over up
+    // to 256 planes, which they read once, unless it leaves them hardly any.
+    const int64_t waves = (d.outer * ((d.inner + 3) / 4) + kWave - 1) / kWave;
+    const int64_t max_waves =
+        d.inner <= LSE_COLS_NARROW ? LSE_COLS_MAX_WAVES : LSE_COLS_WIDE_MAX_WAVES;
+    if (waves > max_waves || groups > (int64_t(1) << 24)) return false;
+    if (lsm && d.R <= 256 && waves > LSE_COLS_LSM_MAX_WAVES) return false;
     const int64_t step = (int64_t)kColsWaves * (kWave / lpp) * kColsU * LSE_COLS_MIN_ITERS;
-    const int64_t min_planes = step > LSE_COLS_MIN_PLANES ? step : LSE_COLS_MIN_PLANES;
+    // Chunks of at least LSE_COLS_MIN_PLANES planes while that still gives
+    // half the target workgroups, else down to LSE_COLS_MIN_PLANES_LOW.
+    int64_t min_planes = step > LSE_COLS_MIN_PLANES ? step : LSE_COLS_MIN_PLANES;
+    if (groups * (d.R / min_planes) < LSE_COLS_TARGET_GROUPS / 2)
+      min_planes = step > LSE_COLS_MIN_PLANES_LOW ? step : LSE_COLS_MIN_PLANES_LOW;
     int64_t k = (LSE_COLS_TARGET_GROUPS + groups - 1) / groups;
     const int64_t kmax = d.R / min_planes;
     if (k > kmax) k = kmax;
     p.chunks = k < 1 ? 1 : k;
+    // One chunk per tile is only worth it while a tile holds the whole
+    // inner run (wider runs give the plane-split kernels more lanes).
+    if (p.chunks == 1 && p.ctiles > 1) return false;
   }
-  // One chunk per tile is only worth it while a tile holds the whole inner
-  // run (wider runs give the plane-split kernels more lanes).
-  if (p.chunks == 1 && p.ctiles > 1) return false;
   p.rc = (d.R + p.chunks - 1) / p.chunks;
   p.chunks = (d.R + p.rc - 1) / p.rc;  // no empty last chunk
   return true;
@@ -441,13 +470,13 @@ hipError_t launch_cols_v(const float *x, float *out, const AxisDims &d, bool lsm
 
 size_t cols_workspace_bytes(const AxisDims &d, bool lsm) {
   ColsPlan p;
-  return cols_plan(d, true, p) ? cols_ws_bytes(d, p, lsm) : 0;
+  return cols_plan(d, lsm, true, p) ? cols_ws_bytes(d, p, lsm) : 0;
 }
 
 bool launch_cols(const float *x, float *out, const AxisDims &d, bool lsm, bool with_ws, void *ws,
                  hipStream_t stream, hipError_t &e) {
   ColsPlan p;
-  if (!cols_plan(d, with_ws, p)) return false;
+  if (!cols_plan(d, lsm, with_ws, p)) return false;
   if (p.chunks > 1 && ws == nullptr) return false;  // the caller passed no workspace after all
   const uintptr_t a = (uintptr_t)x | (uintptr_t)out;
   const int64_t st = d.inner | d.xso | d.xsr | (lsm ? (d.yso | d.ysr) : 0);

@@ -30,7 +30,9 @@ def _raw_axis(x, R, inner, lsm):
 # tiles and chunks, several outer blocks, the plane-count threshold
 COLS_SHAPES = [(1, 200000, 4), (1, 100003, 7), (1, 50000, 16), (2, 30011, 33), (1, 20000, 100),
                (1, 10000, 256), (1, 3001, 1000), (3, 2000, 4096), (1, 60000, 2), (4, 9000, 3),
-               (1, 64, 64), (1, 63, 64), (5, 777, 40), (1, 131072, 1)]
+               (1, 64, 64), (1, 63, 64), (5, 777, 40), (1, 131072, 1),
+               # many outer blocks of narrow runs
+               (300, 500, 16), (120, 300, 64), (2000, 100, 4), (64, 1000, 100)]
 
 
 @pytest.mark.parametrize("outer,R,inner", COLS_SHAPES)
