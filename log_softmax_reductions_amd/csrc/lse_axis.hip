@@ -1015,6 +1015,9 @@ static bool as_rows(const AxisDims &d, bool lsm) {
 #ifndef LSE_AXIS_COLS
 #define LSE_AXIS_COLS 1   // few outputs over many planes take the column split (lse_cols.hip)
 #endif
+#ifndef LSE_AXIS_SEG
+#define LSE_AXIS_SEG 1    // short (R, 2 or 4) blocks take the short-row segments (lse_rows.hip)
+#endif
 #ifndef LSE_AXIS_ROWS_SPLIT_MAX_ROWS
 #define LSE_AXIS_ROWS_SPLIT_MAX_ROWS 1024   // logsumexp rows split with a workspace up to here
 #endif
@@ -1056,6 +1059,7 @@ hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStr
     return launch_rows_lse(x, d.outer, d.R, d.xso, out, d.yso, stream);
   }
   hipError_t e = hipSuccess;
+  if (LSE_AXIS_SEG && launch_axis_seg(x, out, d, false, stream, e)) return e;
   if (LSE_AXIS_COLS && launch_cols(x, out, d, false, with_ws, ws, stream, e)) return e;
   return launch_axis<false>(x, out, d, stream);
 }
@@ -1069,6 +1073,7 @@ hipError_t launch_log_softmax_axis(const float *x, float *y, const AxisDims &d,
     return launch_log_softmax_rows_no_ws(x, y, d.outer, d.R, d.xso, d.yso, stream);
   }
   hipError_t e = hipSuccess;
+  if (LSE_AXIS_SEG && launch_axis_seg(x, y, d, true, stream, e)) return e;
   if (LSE_AXIS_COLS && launch_cols(x, y, d, true, with_ws, ws, stream, e)) return e;
   return launch_axis<true>(x, y, d, stream);
 }

@@ -93,6 +93,12 @@ hipError_t launch_rows_lse(const float *x, int64_t rows, int64_t cols, int64_t l
 hipError_t launch_log_softmax_rows_no_ws(const float *x, float *y, int64_t rows, int64_t cols,
                                          int64_t ldx, int64_t ldy, hipStream_t stream,
                                          bool softmax = false);
+// Axis reductions whose (R, inner) blocks are short contiguous rows (inner 2
+// or 4, planes contiguous in a block, R * inner <= 1024 and a multiple of 4,
+// block pitches multiples of 4): the short-row segments with interleaved
+// outputs.  False when the call does not fit; otherwise e is the launch status.
+bool launch_axis_seg(const float *x, float *out, const AxisDims &d, bool lsm,
+                     hipStream_t stream, hipError_t &e);
 void set_spin_limit(uint32_t polls);
 void set_rows_reread(bool on);
 uint32_t chain_spin_limit();

@@ -905,10 +905,16 @@ __device__ __forceinline__ void store4_a4(float *p, float a, float b, float c, f
   __builtin_nontemporal_store(v4a4{a, b, c, d}, reinterpret_cast<v4a4 *>(p));
 }
 
-template <int G, int VPL, int NR, int LAY, int OUT>
+// INNER > 1 (2 or 4, 16-byte layouts only): each row is an (R, INNER) block
+// of an axis reduction over R with INNER interleaved outputs; value e of a
+// lane's 4-value vector belongs to output e % INNER, so every lane keeps one
+// (max, sum) per output and the segment reduces each of them.
+template <int G, int VPL, int NR, int LAY, int OUT, int INNER = 1>
 __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
     const float *__restrict__ x, float *__restrict__ y, int64_t rows, int64_t cols, int64_t ldx,
     int64_t ldy) {
+  static_assert(INNER == 1 || (LAY != kSegScalar && 4 % INNER == 0),
+                "interleaved outputs need 4-value vectors");
   constexpr bool SOFTMAX = OUT == kOutSoftmax;
   constexpr int kPerLoad = LAY == kSegScalar ? 1 : 4;  // values per load
   constexpr int kSegs = kWave / G;                     // segments per wave
@@ -960,39 +966,65 @@ __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
   }
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
-    float lm = v[j][0];
+    float M[INNER], S[INNER];
 #pragma unroll
-    for (int e = 1; e < VPL; ++e) lm = fmaxf(lm, v[j][e]);
-    const float M = seg_allreduce<G>(lm, OpMax{});
-    float ls = 0.0f;
-    if (is_finite(M)) {  // the same in every lane of the segment
+    for (int c = 0; c < INNER; ++c) {
+      float lm = v[j][c];
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) ls += exp_base2(v[j][e] - M);
-    } else {
+      for (int e = c + INNER; e < VPL; e += INNER) lm = fmaxf(lm, v[j][e]);
+      M[c] = seg_allreduce<G>(lm, OpMax{});
+      float ls = 0.0f;
+      if (is_finite(M[c])) {  // the same in every lane of the segment
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) ls += pair_term_nonfinite(v[j][e], M);
+        for (int e = c; e < VPL; e += INNER) ls += exp_base2(v[j][e] - M[c]);
+      } else {
+#pragma unroll
+        for (int e = c; e < VPL; e += INNER) ls += pair_term_nonfinite(v[j][e], M[c]);
+      }
+      S[c] = seg_allreduce<G>(ls, OpSum{});
     }
-    const float S = seg_allreduce<G>(ls, OpSum{});
     const int64_t row = row0 + j * kSegs + lane / G;
     if (row >= rows) continue;
     if constexpr (OUT == kOutLse) {
-      if (s == 0) y[row * ldy] = pair_lse(M, S);
+      if constexpr (INNER == 1) {
+        if (s == 0) y[row * ldy] = pair_lse(M[0], S[0]);
+      } else {
+        // lane s of the segment writes outputs s, s + G, ... (G < INNER for
+        // blocks of fewer than 4 planes)
+#pragma unroll
+        for (int c0 = 0; c0 < INNER; c0 += G) {
+          const int cs = c0 + s;
+          if (cs < INNER) {
+            float mc = M[0], sc = S[0];
+#pragma unroll
+            for (int c = 1; c < INNER; ++c) {
+              mc = (cs == c) ? M[c] : mc;
+              sc = (cs == c) ? S[c] : sc;
+            }
+            y[row * ldy + cs] = pair_lse(mc, sc);
+          }
+        }
+      }
     } else {
-      const float k = out_scale<SOFTMAX>(S);
+      float k[INNER];
+#pragma unroll
+      for (int c = 0; c < INNER; ++c) k[c] = out_scale<SOFTMAX>(S[c]);
       float *yr = y + row * ldy;
 #pragma unroll
       for (int q = 0; q < VPL / kPerLoad; ++q) {
         const int64_t idx = ((int64_t)q * G + s) * kPerLoad;
         const float *vq = &v[j][kPerLoad * q];
         if (idx < cols) {
-          if constexpr (LAY == kSegA16) {
-            store4(yr + idx, out_value<SOFTMAX>(vq[0], M, k), out_value<SOFTMAX>(vq[1], M, k),
-                   out_value<SOFTMAX>(vq[2], M, k), out_value<SOFTMAX>(vq[3], M, k));
-          } else if constexpr (LAY == kSegA4) {
-            store4_a4(yr + idx, out_value<SOFTMAX>(vq[0], M, k), out_value<SOFTMAX>(vq[1], M, k),
-                      out_value<SOFTMAX>(vq[2], M, k), out_value<SOFTMAX>(vq[3], M, k));
+          if constexpr (LAY == kSegScalar) {
+            yr[idx] = out_value<SOFTMAX>(vq[0], M[0], k[0]);
           } else {
-            yr[idx] = out_value<SOFTMAX>(vq[0], M, k);
+            float o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = out_value<SOFTMAX>(vq[r], M[r % INNER], k[r % INNER]);
+            if constexpr (LAY == kSegA16)
+              store4(yr + idx, o[0], o[1], o[2], o[3]);
+            else
+              store4_a4(yr + idx, o[0], o[1], o[2], o[3]);
           }
         }
       }
@@ -1239,18 +1271,18 @@ hipError_t for_row_batches(int64_t rows, int64_t max_rows, F launch) {
   return hipSuccess;
 }
 
-template <int G, int VPL, int OUT>
+template <int G, int VPL, int OUT, int INNER>
 void launch_seg(int lay, dim3 grid, hipStream_t stream, const float *x, float *y, int64_t rows,
                 int64_t cols, int64_t ldx, int64_t ldy) {
   constexpr int NR = seg_rows_per_pass(VPL, OUT);
   const dim3 block(kWave * kSegWaves);
   if (lay == kSegA16)
-    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegA16, OUT>), grid, block, 0, stream, x, y,
-                       rows, cols, ldx, ldy);
+    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegA16, OUT, INNER>), grid, block, 0, stream,
+                       x, y, rows, cols, ldx, ldy);
   else if (lay == kSegA4)
-    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegA4, OUT>), grid, block, 0, stream, x, y,
-                       rows, cols, ldx, ldy);
-  else
+    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegA4, OUT, INNER>), grid, block, 0, stream,
+                       x, y, rows, cols, ldx, ldy);
+  else if constexpr (INNER == 1)
     hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegScalar, OUT>), grid, block, 0, stream, x,
                        y, rows, cols, ldx, ldy);
 }
@@ -1260,7 +1292,7 @@ void launch_seg(int lay, dim3 grid, hipStream_t stream, const float *x, float *y
 // per lane hold the row; a wave-wide segment holds 4, 8 or 16 values per lane.
 // vec: x (and y, for the row outputs) 16-byte aligned, cols and the pitches
 // multiples of 4.  For kOutLse, y[r * ldy] receives row r's logsumexp.
-template <int OUT>
+template <int OUT, int INNER = 1>
 hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols, int64_t ldx,
                            int64_t ldy, bool vec, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
@@ -1273,6 +1305,7 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
   // 16-byte accesses when all rows share one 4-byte phase
   const bool one_phase = cols % 4 == 0 && ldx % 4 == 0 && (OUT == kOutLse || ldy % 4 == 0);
   const int lay = vec ? kSegA16 : (one_phase ? kSegA4 : kSegScalar);
+  if (INNER > 1 && lay == kSegScalar) return hipErrorInvalidValue;
   const int64_t rows_per_group = (int64_t)kSegWaves * (kWave / g) * seg_rows_per_pass(vpl, OUT);
   const int64_t max_groups = 0xffffffffll / (kWave * kSegWaves);  // 32-bit work-item count
   return for_row_batches(rows, max_groups * rows_per_group, [&](int64_t r0, int64_t nr) {
@@ -1280,15 +1313,15 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
     const float *xb = x + r0 * ldx;
     float *yb = y + r0 * ldy;
     switch (g == kWave ? kWave * vpl : g) {
-      case 1: launch_seg<1, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 2: launch_seg<2, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 4: launch_seg<4, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 8: launch_seg<8, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 16: launch_seg<16, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 32: launch_seg<32, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 4 * kWave: launch_seg<64, 4, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 8 * kWave: launch_seg<64, 8, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
-      case 16 * kWave: launch_seg<64, 16, OUT>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 1: launch_seg<1, 4, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 2: launch_seg<2, 4, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 4: launch_seg<4, 4, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 8: launch_seg<8, 4, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 16: launch_seg<16, 4, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 32: launch_seg<32, 4, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 4 * kWave: launch_seg<64, 4, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 8 * kWave: launch_seg<64, 8, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 16 * kWave: launch_seg<64, 16, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1503,6 +1536,24 @@ hipError_t launch_log_softmax_rows_no_ws(const float *x, float *y, int64_t rows,
 #undef LSE_ROWSTREAM
     return hipGetLastError();
   });
+}
+
+bool launch_axis_seg(const float *x, float *out, const AxisDims &d, bool lsm,
+                     hipStream_t stream, hipError_t &e) {
+  const int64_t cols = d.R * d.inner;
+  if ((d.inner != 2 && d.inner != 4) || d.xsr != d.inner || (lsm && d.ysr != d.inner) ||
+      cols > LSE_ROWS_SEG_MAX || cols % 4 != 0 || d.xso % 4 != 0 || (lsm && d.yso % 4 != 0) ||
+      d.outer < 1 || d.outer > 0x7fffffff)
+    return false;
+  const bool vec = ((uintptr_t)x % 16 == 0) && (!lsm || (uintptr_t)out % 16 == 0);
+  if (lsm)
+    e = d.inner == 2
+            ? launch_rows_seg<kOutLogSoftmax, 2>(x, out, d.outer, cols, d.xso, d.yso, vec, stream)
+            : launch_rows_seg<kOutLogSoftmax, 4>(x, out, d.outer, cols, d.xso, d.yso, vec, stream);
+  else
+    e = d.inner == 2 ? launch_rows_seg<kOutLse, 2>(x, out, d.outer, cols, d.xso, d.yso, vec, stream)
+                     : launch_rows_seg<kOutLse, 4>(x, out, d.outer, cols, d.xso, d.yso, vec, stream);
+  return true;
 }
 
 hipError_t launch_lse_rows_merge(const void *partials, int64_t rows, int64_t nchunks,

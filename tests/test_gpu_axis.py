@@ -232,3 +232,37 @@ def test_axis_ragged_and_offset_runs(orc, outer, R, inner, off):
     torch.cuda.synchronize()
     compare(y.cpu().numpy(), orc.log_softmax_axis(xc), what=f"lsm ragged {outer}x{R}x{inner}+{off}")
     assert torch.all(big[:off] == 7.0) and torch.all(big[off + n:] == 7.0)
+
+
+@pytest.mark.parametrize("outer,R,inner", [(1000, 1, 4), (1000, 2, 2), (777, 2, 4), (1001, 3, 4),
+                                           (500, 6, 2), (300, 16, 4), (300, 100, 4), (257, 256, 4),
+                                           (100, 512, 2), (60, 255, 4), (50, 511, 2)])
+@pytest.mark.parametrize("layout", ["packed", "offset", "pitched"])
+def test_axis_short_interleaved_blocks(orc, outer, R, inner, layout):
+    """Blocks of R planes x 2 or 4 outputs, contiguous and at most 1024 values:
+    segments of lanes per block, each lane folding its 4-value vectors into
+    the outputs they interleave (16-byte loads, at a 4-byte offset too;
+    blocks at a padded pitch; special values in one block; outputs between
+    guard values)."""
+    pad = 4 if layout == "pitched" else 0
+    off = 1 if layout == "offset" else 0
+    blk = R * inner + pad
+    buf = inputs.normal((outer * blk + off,), seed=outer + R * 7 + inner, sigma=3.0, device=DEV)
+    x = buf[off:].view(outer, blk)[:, :R * inner].view(outer, R, inner)
+    xs = x[min(5, outer - 1)]
+    xs[:, 0] = -float("inf")                        # an all -inf output
+    if R > 1:
+        xs[R // 2, 1] = float("inf")
+    xc = x.contiguous().cpu().numpy()
+    obuf = torch.full((outer, inner + 3), 7.0, device=DEV)
+    out = L.lse_reduce_axis(x, 1, out=obuf[:, :inner])
+    ybuf = torch.full((outer * blk + off,), 7.0, device=DEV)
+    yv = ybuf[off:].view(outer, blk)[:, :R * inner].view(outer, R, inner)
+    y = L.log_softmax_axis(x, 1, y=yv)
+    torch.cuda.synchronize()
+    what = f"interleaved {layout} {outer}x{R}x{inner}"
+    compare(out.cpu().numpy(), orc.lse_axis(xc), what="lse " + what)
+    compare(y.cpu().numpy(), orc.log_softmax_axis(xc), what="lsm " + what)
+    assert (obuf[:, inner:] == 7.0).all()
+    if pad:
+        assert (ybuf[off:].view(outer, blk)[:, R * inner:] == 7.0).all()
