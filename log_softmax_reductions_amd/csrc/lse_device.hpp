@@ -69,6 +69,41 @@ __device__ __forceinline__ float seg_allreduce(float v, Op op) {
   return v;
 }
 
+// All-reduce over the lanes of a G-lane segment that agree mod LPC (powers of
+// two, LPC <= G): LPC = 1 is seg_allreduce; otherwise the quad permute for
+// lane ^ 2, then inside each 16-lane row a rotation by 8 (lane ^ 8) and by 4
+// (after which every lane holds its residue class mod 4 of the row), and the
+// permlane swaps for lane ^ 16 and lane ^ 32.  Every lane of a set ends with
+// bitwise the same value (each step combines the same values in either order).
+template <int LPC, int G, class Op>
+__device__ __forceinline__ float coset_allreduce(float v, Op op) {
+  static_assert(LPC >= 1 && LPC <= G && G <= kWave, "sets inside a segment");
+  if constexpr (LPC == 1) {
+    return seg_allreduce<G>(v, op);
+  } else {
+    if constexpr (LPC == 2 && G >= 4) v = op(v, dpp_mov<0x4E>(v));  // lane ^ 2
+    if constexpr (G >= 16) {
+      if constexpr (LPC <= 4) {
+        v = op(v, dpp_mov<0x128>(v));  // row_ror:8 = lane ^ 8
+        v = op(v, dpp_mov<0x124>(v));  // row_ror:4: the row's residue classes mod 4
+      } else if constexpr (LPC == 8) {
+        v = op(v, dpp_mov<0x128>(v));
+      }
+    } else if constexpr (G == 8 && LPC <= 4) {
+      v = op(v, __shfl_xor(v, 4));  // lane ^ 4 inside an 8-lane segment
+    }
+    if constexpr (G >= 32 && LPC <= 16) {
+      auto p = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+      v = op(bitsf(p[0]), bitsf(p[1]));
+    }
+    if constexpr (G >= 64 && LPC <= 32) {
+      auto q = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
+      v = op(bitsf(q[0]), bitsf(q[1]));
+    }
+    return v;
+  }
+}
+
 // All 64 lanes end with op over the wave.
 template <class Op>
 __device__ __forceinline__ float wave_allreduce(float v, Op op) {

@@ -905,16 +905,23 @@ __device__ __forceinline__ void store4_a4(float *p, float a, float b, float c, f
   __builtin_nontemporal_store(v4a4{a, b, c, d}, reinterpret_cast<v4a4 *>(p));
 }
 
-// INNER > 1 (2 or 4, 16-byte layouts only): each row is an (R, INNER) block
-// of an axis reduction over R with INNER interleaved outputs; value e of a
-// lane's 4-value vector belongs to output e % INNER, so every lane keeps one
-// (max, sum) per output and the segment reduces each of them.
+// INNER > 1 (2, or a power of two from 4, 16-byte layouts only): each row is
+// an (R, INNER) block of an axis reduction over R with INNER interleaved
+// outputs.  INNER = 2: value e of a lane's 4-value vector belongs to output
+// e % 2, and every lane keeps a (max, sum) for both.  INNER >= 4: a lane's
+// vectors all start at the same column 4 (s % (INNER / 4)) of their planes
+// (G is a multiple of INNER / 4), so value e belongs to output that + e % 4,
+// and the lanes holding the same outputs (s equal mod INNER / 4) reduce
+// together.
 template <int G, int VPL, int NR, int LAY, int OUT, int INNER = 1>
 __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
     const float *__restrict__ x, float *__restrict__ y, int64_t rows, int64_t cols, int64_t ldx,
     int64_t ldy) {
-  static_assert(INNER == 1 || (LAY != kSegScalar && 4 % INNER == 0),
+  static_assert(INNER == 1 || (LAY != kSegScalar && (INNER & (INNER - 1)) == 0),
                 "interleaved outputs need 4-value vectors");
+  constexpr int NACC = INNER >= 4 ? 4 : INNER;  // outputs a lane holds
+  constexpr int LPC = INNER >= 4 ? INNER / 4 : 1;  // lanes per plane; s % LPC picks the outputs
+  static_assert(G % LPC == 0, "a segment covers whole planes");
   constexpr bool SOFTMAX = OUT == kOutSoftmax;
   constexpr int kPerLoad = LAY == kSegScalar ? 1 : 4;  // values per load
   constexpr int kSegs = kWave / G;                     // segments per wave
@@ -966,28 +973,46 @@ __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
   }
 #pragma unroll
   for (int j = 0; j < NR; ++j) {
-    float M[INNER], S[INNER];
+    float M[NACC], S[NACC];
 #pragma unroll
-    for (int c = 0; c < INNER; ++c) {
+    for (int c = 0; c < NACC; ++c) {
       float lm = v[j][c];
 #pragma unroll
-      for (int e = c + INNER; e < VPL; e += INNER) lm = fmaxf(lm, v[j][e]);
-      M[c] = seg_allreduce<G>(lm, OpMax{});
+      for (int e = c + NACC; e < VPL; e += NACC) lm = fmaxf(lm, v[j][e]);
+      M[c] = coset_allreduce<LPC, G>(lm, OpMax{});
       float ls = 0.0f;
-      if (is_finite(M[c])) {  // the same in every lane of the segment
+      if (is_finite(M[c])) {  // the same in every lane holding output c
 #pragma unroll
-        for (int e = c; e < VPL; e += INNER) ls += exp_base2(v[j][e] - M[c]);
+        for (int e = c; e < VPL; e += NACC) ls += exp_base2(v[j][e] - M[c]);
       } else {
 #pragma unroll
-        for (int e = c; e < VPL; e += INNER) ls += pair_term_nonfinite(v[j][e], M[c]);
+        for (int e = c; e < VPL; e += NACC) ls += pair_term_nonfinite(v[j][e], M[c]);
       }
-      S[c] = seg_allreduce<G>(ls, OpSum{});
+      S[c] = coset_allreduce<LPC, G>(ls, OpSum{});
     }
     const int64_t row = row0 + j * kSegs + lane / G;
     if (row >= rows) continue;
     if constexpr (OUT == kOutLse) {
       if constexpr (INNER == 1) {
         if (s == 0) y[row * ldy] = pair_lse(M[0], S[0]);
+      } else if constexpr (INNER >= 4) {
+        // The G / LPC lanes of a set share its 4 outputs: lane s writes output
+        // s / LPC of its set, and s / LPC + G / LPC, ... when the set has
+        // fewer than 4 lanes.
+        constexpr int kSetLanes = G / LPC;
+#pragma unroll
+        for (int c0 = 0; c0 < 4; c0 += kSetLanes) {
+          const int cs = c0 + s / LPC;
+          if (cs < 4) {
+            float mc = M[0], sc = S[0];
+#pragma unroll
+            for (int c = 1; c < 4; ++c) {
+              mc = (cs == c) ? M[c] : mc;
+              sc = (cs == c) ? S[c] : sc;
+            }
+            y[row * ldy + 4 * (s % LPC) + cs] = pair_lse(mc, sc);
+          }
+        }
       } else {
         // lane s of the segment writes outputs s, s + G, ... (G < INNER for
         // blocks of fewer than 4 planes)
@@ -1006,9 +1031,9 @@ __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
         }
       }
     } else {
-      float k[INNER];
+      float k[NACC];
 #pragma unroll
-      for (int c = 0; c < INNER; ++c) k[c] = out_scale<SOFTMAX>(S[c]);
+      for (int c = 0; c < NACC; ++c) k[c] = out_scale<SOFTMAX>(S[c]);
       float *yr = y + row * ldy;
 #pragma unroll
       for (int q = 0; q < VPL / kPerLoad; ++q) {
@@ -1020,7 +1045,7 @@ __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
           } else {
             float o[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = out_value<SOFTMAX>(vq[r], M[r % INNER], k[r % INNER]);
+            for (int r = 0; r < 4; ++r) o[r] = out_value<SOFTMAX>(vq[r], M[r % NACC], k[r % NACC]);
             if constexpr (LAY == kSegA16)
               store4(yr + idx, o[0], o[1], o[2], o[3]);
             else
@@ -1276,7 +1301,9 @@ void launch_seg(int lay, dim3 grid, hipStream_t stream, const float *x, float *y
                 int64_t cols, int64_t ldx, int64_t ldy) {
   constexpr int NR = seg_rows_per_pass(VPL, OUT);
   const dim3 block(kWave * kSegWaves);
-  if (lay == kSegA16)
+  if constexpr (INNER >= 4 && G % (INNER / 4) != 0)
+    return;  // never chosen: a block of R >= 1 planes gives G >= INNER / 4
+  else if (lay == kSegA16)
     hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegA16, OUT, INNER>), grid, block, 0, stream,
                        x, y, rows, cols, ldx, ldy);
   else if (lay == kSegA4)
@@ -1306,6 +1333,7 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
   const bool one_phase = cols % 4 == 0 && ldx % 4 == 0 && (OUT == kOutLse || ldy % 4 == 0);
   const int lay = vec ? kSegA16 : (one_phase ? kSegA4 : kSegScalar);
   if (INNER > 1 && lay == kSegScalar) return hipErrorInvalidValue;
+  if (INNER >= 4 && g < INNER / 4) return hipErrorInvalidValue;
   const int64_t rows_per_group = (int64_t)kSegWaves * (kWave / g) * seg_rows_per_pass(vpl, OUT);
   const int64_t max_groups = 0xffffffffll / (kWave * kSegWaves);  // 32-bit work-item count
   return for_row_batches(rows, max_groups * rows_per_group, [&](int64_t r0, int64_t nr) {
@@ -1541,18 +1569,33 @@ hipError_t launch_log_softmax_rows_no_ws(const float *x, float *y, int64_t rows,
 bool launch_axis_seg(const float *x, float *out, const AxisDims &d, bool lsm,
                      hipStream_t stream, hipError_t &e) {
   const int64_t cols = d.R * d.inner;
-  if ((d.inner != 2 && d.inner != 4) || d.xsr != d.inner || (lsm && d.ysr != d.inner) ||
+  const bool pow2 = d.inner >= 2 && d.inner <= 256 && (d.inner & (d.inner - 1)) == 0;
+  if (!pow2 || d.xsr != d.inner || (lsm && d.ysr != d.inner) ||
       cols > LSE_ROWS_SEG_MAX || cols % 4 != 0 || d.xso % 4 != 0 || (lsm && d.yso % 4 != 0) ||
       d.outer < 1 || d.outer > 0x7fffffff)
     return false;
+  // logsumexp over runs of 8+ outputs in blocks of at most 256 values: the
+  // axis kernels' lanes, which need no cross-lane steps, measured faster
+  // ((300000, 32, 8): 3410 against 3140 GB/s) unless the blocks have only a
+  // few planes
+  if (!lsm && d.inner >= 8 && cols <= 256 && d.R > 8) return false;
   const bool vec = ((uintptr_t)x % 16 == 0) && (!lsm || (uintptr_t)out % 16 == 0);
-  if (lsm)
-    e = d.inner == 2
-            ? launch_rows_seg<kOutLogSoftmax, 2>(x, out, d.outer, cols, d.xso, d.yso, vec, stream)
-            : launch_rows_seg<kOutLogSoftmax, 4>(x, out, d.outer, cols, d.xso, d.yso, vec, stream);
-  else
-    e = d.inner == 2 ? launch_rows_seg<kOutLse, 2>(x, out, d.outer, cols, d.xso, d.yso, vec, stream)
-                     : launch_rows_seg<kOutLse, 4>(x, out, d.outer, cols, d.xso, d.yso, vec, stream);
+  auto go = [&](auto inner_c) {
+    constexpr int I = decltype(inner_c)::value;
+    return lsm ? launch_rows_seg<kOutLogSoftmax, I>(x, out, d.outer, cols, d.xso, d.yso, vec,
+                                                    stream)
+               : launch_rows_seg<kOutLse, I>(x, out, d.outer, cols, d.xso, d.yso, vec, stream);
+  };
+  switch (d.inner) {
+    case 2: e = go(std::integral_constant<int, 2>{}); break;
+    case 4: e = go(std::integral_constant<int, 4>{}); break;
+    case 8: e = go(std::integral_constant<int, 8>{}); break;
+    case 16: e = go(std::integral_constant<int, 16>{}); break;
+    case 32: e = go(std::integral_constant<int, 32>{}); break;
+    case 64: e = go(std::integral_constant<int, 64>{}); break;
+    case 128: e = go(std::integral_constant<int, 128>{}); break;
+    default: e = go(std::integral_constant<int, 256>{}); break;
+  }
   return true;
 }
 

@@ -236,12 +236,15 @@ def test_axis_ragged_and_offset_runs(orc, outer, R, inner, off):
 
 @pytest.mark.parametrize("outer,R,inner", [(1000, 1, 4), (1000, 2, 2), (777, 2, 4), (1001, 3, 4),
                                            (500, 6, 2), (300, 16, 4), (300, 100, 4), (257, 256, 4),
-                                           (100, 512, 2), (60, 255, 4), (50, 511, 2)])
+                                           (100, 512, 2), (60, 255, 4), (50, 511, 2),
+                                           (300, 100, 8), (1000, 3, 8), (200, 64, 16),
+                                           (100, 16, 64), (64, 1, 256), (50, 4, 256),
+                                           (70, 33, 16)])
 @pytest.mark.parametrize("layout", ["packed", "offset", "pitched"])
 def test_axis_short_interleaved_blocks(orc, outer, R, inner, layout):
-    """Blocks of R planes x 2 or 4 outputs, contiguous and at most 1024 values:
-    segments of lanes per block, each lane folding its 4-value vectors into
-    the outputs they interleave (16-byte loads, at a 4-byte offset too;
+    """Blocks of R planes x 2, 4, ... 256 outputs, contiguous and at most 1024
+    values: segments of lanes per block, each lane folding its 4-value vectors
+    into the outputs they interleave (16-byte loads, at a 4-byte offset too;
     blocks at a padded pitch; special values in one block; outputs between
     guard values)."""
     pad = 4 if layout == "pitched" else 0
