@@ -856,6 +856,10 @@ __global__ __launch_bounds__(kRowsThreads) void rows_lse_stream_kernel(
 #ifndef LSE_ROWS_SEG_MAX
 #define LSE_ROWS_SEG_MAX 1024   // rows up to this many columns take a segment of a wave
 #endif
+// Interleaved blocks (axis calls with inner > 1) take a wave-wide segment up
+// to 64 values per lane: the axis kernels they would fall back to read such
+// blocks 8-16 bytes per plane and lane.
+constexpr int64_t kSegInterleavedMax = 64 * 64;
 static_assert(LSE_ROWS_SEG_MAX >= 1 && LSE_ROWS_SEG_MAX <= 16 * 64,
               "a wave-wide segment holds at most 16 values per lane");
 constexpr int kSegWaves = 4;    // waves per workgroup of the short-row kernel
@@ -1323,7 +1327,8 @@ template <int OUT, int INNER = 1>
 hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols, int64_t ldx,
                            int64_t ldy, bool vec, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  if (cols < 1 || cols > LSE_ROWS_SEG_MAX) return hipErrorInvalidValue;
+  if (cols < 1 || cols > (INNER > 1 ? kSegInterleavedMax : LSE_ROWS_SEG_MAX))
+    return hipErrorInvalidValue;
   int g = 1;
   while (g < kWave && 4 * g < cols) g *= 2;
   int vpl = 4;
@@ -1350,6 +1355,20 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
       case 4 * kWave: launch_seg<64, 4, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
       case 8 * kWave: launch_seg<64, 8, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
       case 16 * kWave: launch_seg<64, 16, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
+      case 32 * kWave:
+        if constexpr (INNER > 1) {
+          launch_seg<64, 32, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy);
+          break;
+        } else {
+          return hipErrorInvalidValue;
+        }
+      case 64 * kWave:
+        if constexpr (INNER > 1) {
+          launch_seg<64, 64, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy);
+          break;
+        } else {
+          return hipErrorInvalidValue;
+        }
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1571,7 +1590,7 @@ bool launch_axis_seg(const float *x, float *out, const AxisDims &d, bool lsm,
   const int64_t cols = d.R * d.inner;
   const bool pow2 = d.inner >= 2 && d.inner <= 256 && (d.inner & (d.inner - 1)) == 0;
   if (!pow2 || d.xsr != d.inner || (lsm && d.ysr != d.inner) ||
-      cols > LSE_ROWS_SEG_MAX || cols % 4 != 0 || d.xso % 4 != 0 || (lsm && d.yso % 4 != 0) ||
+      cols > kSegInterleavedMax || cols % 4 != 0 || d.xso % 4 != 0 || (lsm && d.yso % 4 != 0) ||
       d.outer < 1 || d.outer > 0x7fffffff)
     return false;
   // logsumexp over runs of 8+ outputs in blocks of at most 256 values: the

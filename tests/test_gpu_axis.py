@@ -239,10 +239,13 @@ def test_axis_ragged_and_offset_runs(orc, outer, R, inner, off):
                                            (100, 512, 2), (60, 255, 4), (50, 511, 2),
                                            (300, 100, 8), (1000, 3, 8), (200, 64, 16),
                                            (100, 16, 64), (64, 1, 256), (50, 4, 256),
-                                           (70, 33, 16)])
+                                           (70, 33, 16),
+                                           # wave-wide segments of up to 64 values per lane
+                                           (40, 1000, 2), (30, 300, 8), (20, 1024, 4),
+                                           (10, 17, 256)])
 @pytest.mark.parametrize("layout", ["packed", "offset", "pitched"])
 def test_axis_short_interleaved_blocks(orc, outer, R, inner, layout):
-    """Blocks of R planes x 2, 4, ... 256 outputs, contiguous and at most 1024
+    """Blocks of R planes x 2, 4, ... 256 outputs, contiguous and at most 4096
     values: segments of lanes per block, each lane folding its 4-value vectors
     into the outputs they interleave (16-byte loads, at a 4-byte offset too;
     blocks at a padded pitch; special values in one block; outputs between
