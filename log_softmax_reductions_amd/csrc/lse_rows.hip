@@ -856,6 +856,12 @@ __global__ __launch_bounds__(kRowsThreads) void rows_lse_stream_kernel(
 #ifndef LSE_ROWS_SEG_MAX
 #define LSE_ROWS_SEG_MAX 1024   // rows up to this many columns take a segment of a wave
 #endif
+#ifndef LSE_ROWS_SEG_A8
+#define LSE_ROWS_SEG_A8 1  // rows of 2..32 values at differing phases: 8-byte accesses
+#endif
+// (same box, GB/s logsumexp / log_softmax, one value -> 8 bytes per access:
+// 3 columns 3908 / 3378 -> 4886 / 4014, 17 columns 3568 / 3395 -> 3600 / 3857;
+// from 99 columns on 8-byte accesses measured 6-15 % slower)
 // Interleaved blocks (axis calls with inner > 1) take a wave-wide segment up
 // to 64 values per lane: the axis kernels they would fall back to read such
 // blocks 8-16 bytes per plane and lane.
@@ -893,8 +899,10 @@ constexpr int seg_rows_per_pass(int vpl, int out) {
 enum SegLayout {
   kSegA16 = 0,    // x, y 16-byte aligned, cols and pitches multiples of 4
   kSegA4 = 1,     // cols and pitches multiples of 4, x or y at another 4-byte phase
-  kSegScalar = 2  // rows at differing phases (cols or a pitch not a multiple of 4)
+  kSegScalar = 2,  // rows at differing phases, one value per access
+  kSegA8 = 3       // rows at differing phases, 8-byte accesses at 4-byte alignment
 };
+typedef float v2a4 __attribute__((ext_vector_type(2), aligned(4)));
 
 // 16-byte load / non-temporal store at 4-byte alignment (gfx950 accepts
 // dword-aligned 16-byte global accesses).
@@ -921,13 +929,13 @@ template <int G, int VPL, int NR, int LAY, int OUT, int INNER = 1>
 __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
     const float *__restrict__ x, float *__restrict__ y, int64_t rows, int64_t cols, int64_t ldx,
     int64_t ldy) {
-  static_assert(INNER == 1 || (LAY != kSegScalar && (INNER & (INNER - 1)) == 0),
+  static_assert(INNER == 1 || (LAY != kSegScalar && LAY != kSegA8 && (INNER & (INNER - 1)) == 0),
                 "interleaved outputs need 4-value vectors");
   constexpr int NACC = INNER >= 4 ? 4 : INNER;  // outputs a lane holds
   constexpr int LPC = INNER >= 4 ? INNER / 4 : 1;  // lanes per plane; s % LPC picks the outputs
   static_assert(G % LPC == 0, "a segment covers whole planes");
   constexpr bool SOFTMAX = OUT == kOutSoftmax;
-  constexpr int kPerLoad = LAY == kSegScalar ? 1 : 4;  // values per load
+  constexpr int kPerLoad = LAY == kSegScalar ? 1 : (LAY == kSegA8 ? 2 : 4);  // values per load
   constexpr int kSegs = kWave / G;                     // segments per wave
   const int lane = threadIdx.x % kWave;
   const int s = lane % G;
@@ -965,6 +973,18 @@ __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) vq[r] = -__builtin_inff();
+        }
+      } else if constexpr (LAY == kSegA8) {
+        if (live && idx + 2 <= cols) {
+#if LSE_ROWS_NT_LOAD
+          const v2a4 f = __builtin_nontemporal_load(reinterpret_cast<const v2a4 *>(xr + idx));
+#else
+          const v2a4 f = *reinterpret_cast<const v2a4 *>(xr + idx);
+#endif
+          vq[0] = f.x; vq[1] = f.y;
+        } else {  // the last value of an odd row, or past the row
+          vq[0] = (live && idx < cols) ? xr[idx] : -__builtin_inff();
+          vq[1] = -__builtin_inff();
         }
       } else {
 #if LSE_ROWS_NT_LOAD
@@ -1046,6 +1066,13 @@ __global__ __launch_bounds__(kWave * kSegWaves) void rows_seg_kernel(
         if (idx < cols) {
           if constexpr (LAY == kSegScalar) {
             yr[idx] = out_value<SOFTMAX>(vq[0], M[0], k[0]);
+          } else if constexpr (LAY == kSegA8) {
+            const float o0 = out_value<SOFTMAX>(vq[0], M[0], k[0]);
+            if (idx + 2 <= cols)
+              __builtin_nontemporal_store(v2a4{o0, out_value<SOFTMAX>(vq[1], M[0], k[0])},
+                                          reinterpret_cast<v2a4 *>(yr + idx));
+            else
+              yr[idx] = o0;
           } else {
             float o[4];
 #pragma unroll
@@ -1313,9 +1340,14 @@ void launch_seg(int lay, dim3 grid, hipStream_t stream, const float *x, float *y
   else if (lay == kSegA4)
     hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegA4, OUT, INNER>), grid, block, 0, stream,
                        x, y, rows, cols, ldx, ldy);
-  else if constexpr (INNER == 1)
-    hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegScalar, OUT>), grid, block, 0, stream, x,
-                       y, rows, cols, ldx, ldy);
+  else if constexpr (INNER == 1) {
+    if (lay == kSegA8)
+      hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegA8, OUT>), grid, block, 0, stream, x, y,
+                         rows, cols, ldx, ldy);
+    else
+      hipLaunchKernelGGL((rows_seg_kernel<G, VPL, NR, kSegScalar, OUT>), grid, block, 0, stream,
+                         x, y, rows, cols, ldx, ldy);
+  }
 }
 
 // Rows of at most LSE_ROWS_SEG_MAX columns through rows_seg_kernel: the
@@ -1336,8 +1368,10 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
     while (vpl * kWave < cols) vpl *= 2;
   // 16-byte accesses when all rows share one 4-byte phase
   const bool one_phase = cols % 4 == 0 && ldx % 4 == 0 && (OUT == kOutLse || ldy % 4 == 0);
-  const int lay = vec ? kSegA16 : (one_phase ? kSegA4 : kSegScalar);
-  if (INNER > 1 && lay == kSegScalar) return hipErrorInvalidValue;
+  const int lay = vec ? kSegA16
+                : one_phase ? kSegA4
+                : (LSE_ROWS_SEG_A8 && cols >= 2 && cols <= 32) ? kSegA8 : kSegScalar;
+  if (INNER > 1 && (lay == kSegScalar || lay == kSegA8)) return hipErrorInvalidValue;
   if (INNER >= 4 && g < INNER / 4) return hipErrorInvalidValue;
   const int64_t rows_per_group = (int64_t)kSegWaves * (kWave / g) * seg_rows_per_pass(vpl, OUT);
   const int64_t max_groups = 0xffffffffll / (kWave * kSegWaves);  // 32-bit work-item count
