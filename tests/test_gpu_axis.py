@@ -272,3 +272,37 @@ def test_axis_short_interleaved_blocks(orc, outer, R, inner, layout):
     assert (obuf[:, inner:] == 7.0).all()
     if pad:
         assert (ybuf[off:].view(outer, blk)[:, R * inner:] == 7.0).all()
+
+
+@pytest.mark.parametrize("outer,R,inner", [(1000, 16, 3), (300, 100, 5), (100, 50, 12),
+                                           (77, 257, 6), (50, 300, 9), (1000, 1, 7), (200, 3, 11),
+                                           (64, 200, 15), (500, 64, 3)])
+@pytest.mark.parametrize("layout", ["packed", "offset", "pitched"])
+def test_axis_blocks_with_odd_outputs(orc, outer, R, inner, layout):
+    """Blocks of R planes x 3..15 outputs (not a power of two), which the
+    axis kernels (or the column split) take: x at a 4-byte offset and blocks
+    at a padded pitch too; special values in one block; guard values around
+    the outputs."""
+    pad = 3 if layout == "pitched" else 0
+    off = 1 if layout == "offset" else 0
+    blk = R * inner + pad
+    buf = inputs.normal((outer * blk + off,), seed=outer + R * 5 + inner, sigma=3.0, device=DEV)
+    x = buf[off:].view(outer, blk)[:, :R * inner].view(outer, R, inner)
+    xs = x[min(3, outer - 1)]
+    xs[:, 0] = -float("inf")
+    xs[R // 2, inner - 1] = float("nan")
+    if R > 1:
+        xs[R - 1, 1] = float("inf")
+    xc = x.contiguous().cpu().numpy()
+    obuf = torch.full((outer, inner + 2), 7.0, device=DEV)
+    out = L.lse_reduce_axis(x, 1, out=obuf[:, :inner])
+    ybuf = torch.full((outer * blk + off,), 7.0, device=DEV)
+    yv = ybuf[off:].view(outer, blk)[:, :R * inner].view(outer, R, inner)
+    y = L.log_softmax_axis(x, 1, y=yv)
+    torch.cuda.synchronize()
+    what = f"odd outputs {layout} {outer}x{R}x{inner}"
+    compare(out.cpu().numpy(), orc.lse_axis(xc), what="lse " + what)
+    compare(y.cpu().numpy(), orc.log_softmax_axis(xc), what="lsm " + what)
+    assert (obuf[:, inner:] == 7.0).all()
+    if pad:
+        assert (ybuf[off:].view(outer, blk)[:, R * inner:] == 7.0).all()
