@@ -1,7 +1,9 @@
 // lse_cols.hip — logsumexp and log_softmax over the middle axis of an
-// (outer, R, inner) array when there are few outputs (outer x inner) and many
-// planes: the logsumexp over dim 0 of (R, B, D) with R in the hundreds of
-// thousands and B D in the tens, say.
+// (outer, R, inner) array when the axis kernels' 4-output lanes would leave
+// the GPU short of waves: few outputs (outer x inner) over many planes (the
+// logsumexp over dim 0 of (R, B, D) with R in the hundreds of thousands and
+// B D in the tens, say), or narrow inner runs over a few thousand outer
+// blocks.
 //
 // POPCORNBENCH FW-GLM-5-1 l1_p29 (torch.logsumexp over dim 0 of (R,B,D)): every
 // output is an independent max-shifted sum over its R values.  With one lane
@@ -21,7 +23,9 @@
 //     xor shuffles, then the 4 waves' through LDS, always in the same order.
 //   * log_softmax: (x - M) - log S is written by the same workgroup, which
 //     reads its planes again (one chunk per tile), or by an apply launch over
-//     the chunks after the merge launch has stored each column's (M, log S).
+//     the chunks after the merge launch has stored each column's (M, log S);
+//     the pair launch then reads x with cached loads, so that part of the
+//     second read can come from the Infinity Cache.
 #include <type_traits>
 
 #include "lse_device.hpp"
