@@ -34,6 +34,12 @@
 namespace lse {
 namespace {
 
+#ifndef LSE_COLS_A4
+#define LSE_COLS_A4 1      // log_softmax runs off the 16-byte grid: 16-byte accesses at 4-byte alignment
+#endif
+// (logsumexp keeps one value per access there: 16-byte accesses at differing
+// 4-byte phases measured 7-25 % slower for it, and up to 25 % faster for the
+// log_softmax launches)
 #ifndef LSE_COLS_WAVES
 #define LSE_COLS_WAVES 4   // waves per workgroup
 #endif
@@ -53,10 +59,16 @@ constexpr int kColsU = LSE_COLS_U;
 #define LSE_COLS_NARROW 128          // ... for inner runs up to this wide,
 #endif
 #ifndef LSE_COLS_WIDE_MAX_WAVES
-#define LSE_COLS_WIDE_MAX_WAVES 128  // ... and this few for wider ones
+#define LSE_COLS_WIDE_MAX_WAVES 64   // ... and this few for wider ones
 #endif
 #ifndef LSE_COLS_LSM_MAX_WAVES
-#define LSE_COLS_LSM_MAX_WAVES 64    // ... or this few, for log_softmax over up to 256 planes
+#define LSE_COLS_LSM_MAX_WAVES 64    // ... and, with more waves than this,
+#endif
+#ifndef LSE_COLS_LSM_MINR
+#define LSE_COLS_LSM_MINR 1024       // ... log_softmax over at least this many planes
+#endif
+#ifndef LSE_COLS_OFFGRID_MINR
+#define LSE_COLS_OFFGRID_MINR 768    // ... logsumexp off the 16-byte grid over at least this many
 #endif
 #ifndef LSE_COLS_MIN_PLANES_LOW
 #define LSE_COLS_MIN_PLANES_LOW 128  // chunks down to this many planes when few workgroups
@@ -83,44 +95,82 @@ enum ColsMode { kColsPartial = 0, kColsLse = 1, kColsLsm = 2, kColsPartialKeep =
 
 typedef float v4f16 __attribute__((ext_vector_type(4)));
 
-// Column e (0..3) of lane cl within a tile of 4 LPP columns: VEC lanes hold 4
-// consecutive columns (one 16-byte access), scalar lanes every LPP-th column.
-template <int LPP, bool VEC>
+// How a lane's 4 columns are read and written: one 16-byte access at 16-byte
+// alignment (kColA16: x, y, inner and the strides all multiples of 4 floats)
+// or at 4-byte alignment (kColA4: inner >= 4; the run's last vector, which
+// would pass its end, is read as the run's last 4 values, those the lane
+// before holds counted as -inf, and written value by value), or one value per
+// access (kColScalar: inner < 4).
+enum ColLayout { kColA16 = 0, kColA4 = 1, kColScalar = 2 };
+typedef float v4a4c __attribute__((ext_vector_type(4), aligned(4)));
+
+// Column e (0..3) of lane cl within a tile of 4 LPP columns: vector lanes hold
+// 4 consecutive columns, scalar lanes every LPP-th column.
+template <int LPP, int LAY>
 __device__ __forceinline__ int tile_col(int cl, int e) {
-  return VEC ? 4 * cl + e : cl + LPP * e;
+  return LAY != kColScalar ? 4 * cl + e : cl + LPP * e;
 }
 
 // The lane's 4 values of one plane row p (the tile's first column); columns
 // at or past ncols read -inf.
-template <int LPP, bool VEC, bool NT>
+template <int LPP, int LAY, bool NT>
 __device__ __forceinline__ void cols_load(const float *p, int cl, int64_t ncols, float (&v)[4]) {
-  if constexpr (VEC) {  // ncols % 4 == 0: a vector is wholly in or out
+  const float ninf = -__builtin_inff();
+  if constexpr (LAY == kColA16) {  // ncols % 4 == 0: a vector is wholly in or out
     if (4 * cl < ncols) {
       const v4f16 *q = reinterpret_cast<const v4f16 *>(p + 4 * cl);
       const v4f16 t = NT ? __builtin_nontemporal_load(q) : *q;
       v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = -__builtin_inff();
+      for (int e = 0; e < 4; ++e) v[e] = ninf;
+    }
+  } else if constexpr (LAY == kColA4) {
+    const int j = 4 * cl;
+    if (j + 4 <= ncols) {
+      const v4a4c *q = reinterpret_cast<const v4a4c *>(p + j);
+      const v4a4c t = NT ? __builtin_nontemporal_load(q) : *q;
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else if (j < ncols) {
+      // the run's last 4 values (p + ncols - 4 is in the plane: inner >= 4)
+      const v4a4c *q = reinterpret_cast<const v4a4c *>(p + ncols - 4);
+      const v4a4c t = NT ? __builtin_nontemporal_load(q) : *q;
+      const int64_t rem = ncols - j;  // 1..3 of them are this lane's
+      v[0] = rem == 3 ? t.y : (rem == 2 ? t.z : t.w);
+      v[1] = rem == 3 ? t.z : (rem == 2 ? t.w : ninf);
+      v[2] = rem == 3 ? t.w : ninf;
+      v[3] = ninf;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = ninf;
     }
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int j = tile_col<LPP, false>(cl, e);
-      v[e] = (j < ncols) ? (NT ? __builtin_nontemporal_load(p + j) : p[j]) : -__builtin_inff();
+      const int j = tile_col<LPP, kColScalar>(cl, e);
+      v[e] = (j < ncols) ? (NT ? __builtin_nontemporal_load(p + j) : p[j]) : ninf;
     }
   }
 }
 
-template <int LPP, bool VEC>
+template <int LPP, int LAY>
 __device__ __forceinline__ void cols_store(float *p, int cl, int64_t ncols, const float (&r)[4]) {
-  if constexpr (VEC) {
+  if constexpr (LAY == kColA16) {
     if (4 * cl < ncols)
       __builtin_nontemporal_store(v4f16{r[0], r[1], r[2], r[3]}, reinterpret_cast<v4f16 *>(p + 4 * cl));
+  } else if constexpr (LAY == kColA4) {
+    const int j = 4 * cl;
+    if (j + 4 <= ncols) {
+      __builtin_nontemporal_store(v4a4c{r[0], r[1], r[2], r[3]}, reinterpret_cast<v4a4c *>(p + j));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 3; ++e)
+        if (j + e < ncols) __builtin_nontemporal_store(r[e], p + j + e);
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int j = tile_col<LPP, false>(cl, e);
+      const int j = tile_col<LPP, kColScalar>(cl, e);
       if (j < ncols) __builtin_nontemporal_store(r[e], p + j);
     }
   }
@@ -128,7 +178,7 @@ __device__ __forceinline__ void cols_store(float *p, int cl, int64_t ncols, cons
 
 // y = (x - M) - log S over the lane's planes r, r + STEP, ... < r1, kColsU
 // planes loaded before any is written.
-template <int LPP, bool VEC, int STEP>
+template <int LPP, int LAY, int STEP>
 __device__ __forceinline__ void cols_write(const float *xt, float *yt, int64_t xsr, int64_t ysr,
                                            int64_t r, int64_t r1, int cl, int64_t ncols,
                                            const float (&fm)[4], const float (&fl)[4]) {
@@ -136,13 +186,13 @@ __device__ __forceinline__ void cols_write(const float *xt, float *yt, int64_t x
     float q[kColsU][4];
 #pragma unroll
     for (int u = 0; u < kColsU; ++u)
-      if (r + u * STEP < r1) cols_load<LPP, VEC, true>(xt + (r + u * STEP) * xsr, cl, ncols, q[u]);
+      if (r + u * STEP < r1) cols_load<LPP, LAY, true>(xt + (r + u * STEP) * xsr, cl, ncols, q[u]);
 #pragma unroll
     for (int u = 0; u < kColsU; ++u) {
       if (r + u * STEP < r1) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) q[u][e] = (q[u][e] - fm[e]) - fl[e];
-        cols_store<LPP, VEC>(yt + (r + u * STEP) * ysr, cl, ncols, q[u]);
+        cols_store<LPP, LAY>(yt + (r + u * STEP) * ysr, cl, ncols, q[u]);
       }
     }
   }
@@ -169,7 +219,7 @@ __device__ __forceinline__ void merge_lanes(float &m, float &s) {
 //                 (m, s) per column (each column's chunks contiguous)
 //   kColsLse (one chunk): out[o yso + j] = m + log s
 //   kColsLsm (one chunk): y[o yso + r ysr + j] = (x - m) - log s, re-reading x
-template <int LPP, bool VEC, int MODE>
+template <int LPP, int LAY, int MODE>
 __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
     const float *__restrict__ x, float *__restrict__ out, AxisDims d, int64_t ctiles,
     int64_t chunks, int64_t rc, float2 *__restrict__ pairs) {
@@ -209,7 +259,7 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
       const int64_t rr = r + u * kStep;
       float q[4];
       if (rr < r1) {
-        cols_load<LPP, VEC, kNt>(xt + rr * xsr, cl, ncols, q);
+        cols_load<LPP, LAY, kNt>(xt + rr * xsr, cl, ncols, q);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) q[e] = -__builtin_inff();
@@ -224,7 +274,7 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
   for (int e = 0; e < 4; ++e) merge_lanes<LPP>(m[e], s[e]);
   if (lane < LPP) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) lds_pair[wave][tile_col<LPP, VEC>(cl, e)] = make_float2(m[e], s[e]);
+    for (int e = 0; e < 4; ++e) lds_pair[wave][tile_col<LPP, LAY>(cl, e)] = make_float2(m[e], s[e]);
   }
   __syncthreads();
   for (int col = threadIdx.x; col < C; col += kColsThreads) {
@@ -247,12 +297,12 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
     float fm[4], fl[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float2 f = lds_fin[tile_col<LPP, VEC>(cl, e)];
+      const float2 f = lds_fin[tile_col<LPP, LAY>(cl, e)];
       fm[e] = f.x;
       fl[e] = f.y;
     }
     float *yt = out + o * d.yso + j0;
-    cols_write<LPP, VEC, kStep>(xt, yt, xsr, d.ysr, r0 + g, r1, cl, ncols, fm, fl);
+    cols_write<LPP, LAY, kStep>(xt, yt, xsr, d.ysr, r0 + g, r1, cl, ncols, fm, fl);
   }
 }
 
@@ -315,7 +365,7 @@ __global__ __launch_bounds__(256) void axis_cols_merge_kernel(const float2 *__re
 
 // log_softmax over the chunks' planes from the merged (M, log S) per column,
 // on the grid of the partial launch.
-template <int LPP, bool VEC>
+template <int LPP, int LAY>
 __global__ __launch_bounds__(kColsThreads) void axis_cols_apply_kernel(
     const float *__restrict__ x, float *__restrict__ y, AxisDims d, int64_t ctiles,
     int64_t chunks, int64_t rc, const float2 *__restrict__ fin) {
@@ -337,13 +387,13 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_apply_kernel(
   float fm[4], fl[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const float2 f = fin[ot * C + tile_col<LPP, VEC>(cl, e)];
+    const float2 f = fin[ot * C + tile_col<LPP, LAY>(cl, e)];
     fm[e] = f.x;
     fl[e] = f.y;
   }
   const float *xt = x + o * d.xso + j0;
   float *yt = y + o * d.yso + j0;
-  cols_write<LPP, VEC, kStep>(xt, yt, d.xsr, d.ysr, r0 + g, r1, cl, ncols, fm, fl);
+  cols_write<LPP, LAY, kStep>(xt, yt, d.xsr, d.ysr, r0 + g, r1, cl, ncols, fm, fl);
 }
 
 struct ColsPlan {
@@ -378,7 +428,18 @@ bool cols_plan(const AxisDims &d, bool lsm, bool with_ws, ColsPlan &p) {
     const int64_t max_waves =
         d.inner <= LSE_COLS_NARROW ? LSE_COLS_MAX_WAVES : LSE_COLS_WIDE_MAX_WAVES;
     if (waves > max_waves || groups > (int64_t(1) << 24)) return false;
-    if (lsm && d.R <= 256 && waves > LSE_COLS_LSM_MAX_WAVES) return false;
+    // Beyond hardly any waves, shorter reductions over runs that the axis
+    // kernels read well stay with them: log_softmax (one launch there, three
+    // here) over runs wider than 16 columns that are off the 16-byte grid or
+    // wider than LSE_COLS_NARROW, and logsumexp over runs off the grid
+    // (scalar lanes here, 16-byte ones there).
+    const bool grid16 = d.inner % 4 == 0;
+    if (waves > LSE_COLS_LSM_MAX_WAVES) {
+      if (lsm && d.R < LSE_COLS_LSM_MINR && d.inner > 16 &&
+          !(grid16 && d.inner <= LSE_COLS_NARROW))
+        return false;
+      if (!lsm && !grid16 && d.R < LSE_COLS_OFFGRID_MINR) return false;
+    }
     const int64_t step = (int64_t)kColsWaves * (kWave / lpp) * kColsU * LSE_COLS_MIN_ITERS;
     // Chunks of at least LSE_COLS_MIN_PLANES planes while that still gives
     // half the target workgroups, else down to LSE_COLS_MIN_PLANES_LOW.
@@ -404,17 +465,17 @@ size_t cols_ws_bytes(const AxisDims &d, const ColsPlan &p, bool lsm) {
   return (size_t)(cols * p.chunks * 8 + (lsm ? cols * 8 : 0));
 }
 
-template <int LPP, bool VEC>
+template <int LPP, int LAY>
 hipError_t launch_cols_t(const float *x, float *out, const AxisDims &d, bool lsm,
                          const ColsPlan &p, void *ws, hipStream_t stream) {
   const dim3 grid((uint32_t)(d.outer * p.ctiles * p.chunks));
   const dim3 block(kColsThreads);
   if (p.chunks == 1) {
     if (lsm)
-      hipLaunchKernelGGL((axis_cols_kernel<LPP, VEC, kColsLsm>), grid, block, 0, stream, x, out, d,
+      hipLaunchKernelGGL((axis_cols_kernel<LPP, LAY, kColsLsm>), grid, block, 0, stream, x, out, d,
                          p.ctiles, p.chunks, p.rc, nullptr);
     else
-      hipLaunchKernelGGL((axis_cols_kernel<LPP, VEC, kColsLse>), grid, block, 0, stream, x, out, d,
+      hipLaunchKernelGGL((axis_cols_kernel<LPP, LAY, kColsLse>), grid, block, 0, stream, x, out, d,
                          p.ctiles, p.chunks, p.rc, nullptr);
     return hipGetLastError();
   }
@@ -422,10 +483,10 @@ hipError_t launch_cols_t(const float *x, float *out, const AxisDims &d, bool lsm
   auto *pairs = reinterpret_cast<float2 *>(ws);
   float2 *fin = pairs + d.outer * p.ctiles * p.chunks * C;
   if (lsm && LSE_COLS_LSM_KEEP)
-    hipLaunchKernelGGL((axis_cols_kernel<LPP, VEC, kColsPartialKeep>), grid, block, 0, stream, x,
+    hipLaunchKernelGGL((axis_cols_kernel<LPP, LAY, kColsPartialKeep>), grid, block, 0, stream, x,
                        out, d, p.ctiles, p.chunks, p.rc, pairs);
   else
-    hipLaunchKernelGGL((axis_cols_kernel<LPP, VEC, kColsPartial>), grid, block, 0, stream, x, out,
+    hipLaunchKernelGGL((axis_cols_kernel<LPP, LAY, kColsPartial>), grid, block, 0, stream, x, out,
                        d, p.ctiles, p.chunks, p.rc, pairs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -450,22 +511,22 @@ hipError_t launch_cols_t(const float *x, float *out, const AxisDims &d, bool lsm
   }
   e = hipGetLastError();
   if (e != hipSuccess || !lsm) return e;
-  hipLaunchKernelGGL((axis_cols_apply_kernel<LPP, VEC>), grid, block, 0, stream, x, out, d,
+  hipLaunchKernelGGL((axis_cols_apply_kernel<LPP, LAY>), grid, block, 0, stream, x, out, d,
                      p.ctiles, p.chunks, p.rc, fin);
   return hipGetLastError();
 }
 
-template <bool VEC>
+template <int LAY>
 hipError_t launch_cols_v(const float *x, float *out, const AxisDims &d, bool lsm,
                          const ColsPlan &p, void *ws, hipStream_t stream) {
   switch (p.lpp) {
-    case 1: return launch_cols_t<1, VEC>(x, out, d, lsm, p, ws, stream);
-    case 2: return launch_cols_t<2, VEC>(x, out, d, lsm, p, ws, stream);
-    case 4: return launch_cols_t<4, VEC>(x, out, d, lsm, p, ws, stream);
-    case 8: return launch_cols_t<8, VEC>(x, out, d, lsm, p, ws, stream);
-    case 16: return launch_cols_t<16, VEC>(x, out, d, lsm, p, ws, stream);
-    case 32: return launch_cols_t<32, VEC>(x, out, d, lsm, p, ws, stream);
-    case 64: return launch_cols_t<64, VEC>(x, out, d, lsm, p, ws, stream);
+    case 1: return launch_cols_t<1, LAY>(x, out, d, lsm, p, ws, stream);
+    case 2: return launch_cols_t<2, LAY>(x, out, d, lsm, p, ws, stream);
+    case 4: return launch_cols_t<4, LAY>(x, out, d, lsm, p, ws, stream);
+    case 8: return launch_cols_t<8, LAY>(x, out, d, lsm, p, ws, stream);
+    case 16: return launch_cols_t<16, LAY>(x, out, d, lsm, p, ws, stream);
+    case 32: return launch_cols_t<32, LAY>(x, out, d, lsm, p, ws, stream);
+    case 64: return launch_cols_t<64, LAY>(x, out, d, lsm, p, ws, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -485,8 +546,12 @@ bool launch_cols(const float *x, float *out, const AxisDims &d, bool lsm, bool w
   const uintptr_t a = (uintptr_t)x | (uintptr_t)out;
   const int64_t st = d.inner | d.xso | d.xsr | (lsm ? (d.yso | d.ysr) : 0);
   const bool vec = (st % 4 == 0) && ((lsm ? a : (uintptr_t)x) % 16 == 0);
-  e = vec ? launch_cols_v<true>(x, out, d, lsm, p, ws, stream)
-          : launch_cols_v<false>(x, out, d, lsm, p, ws, stream);
+  if (vec)
+    e = launch_cols_v<kColA16>(x, out, d, lsm, p, ws, stream);
+  else if (d.inner >= 4 && lsm && LSE_COLS_A4)
+    e = launch_cols_v<kColA4>(x, out, d, lsm, p, ws, stream);
+  else
+    e = launch_cols_v<kColScalar>(x, out, d, lsm, p, ws, stream);
   return true;
 }
 
