@@ -1021,12 +1021,19 @@ static bool as_rows(const AxisDims &d, bool lsm) {
 #ifndef LSE_AXIS_ROWS_SPLIT_MAX_ROWS
 #define LSE_AXIS_ROWS_SPLIT_MAX_ROWS 1024   // logsumexp rows split with a workspace up to here
 #endif
+#ifndef LSE_AXIS_ROWS_SPLIT_OFFGRID
+#define LSE_AXIS_ROWS_SPLIT_OFFGRID 1   // ... and any number of rows off the 16-byte grid
+#endif
 // Long last-axis logsumexp rows with a workspace: per-chunk pairs of the row
 // register tile, then one merge per row (few rows only: many rows fill the
 // GPU one workgroup per row).
-static bool lse_rows_split(const AxisDims &d) {
-  return d.outer <= LSE_AXIS_ROWS_SPLIT_MAX_ROWS && d.R > kRowsTile &&
-         (d.outer == 1 || d.yso == 1);
+// Also any number of rows that the one-workgroup-per-row kernel would read
+// one value per access (off the 16-byte grid): the chunk pairs read them as
+// 16-byte vectors at their own phase.
+static bool lse_rows_split(const AxisDims &d, const float *x) {
+  const bool vec = d.R % 4 == 0 && d.xso % 4 == 0 && (uintptr_t)x % 16 == 0;
+  return (d.outer <= LSE_AXIS_ROWS_SPLIT_MAX_ROWS || (!vec && LSE_AXIS_ROWS_SPLIT_OFFGRID)) &&
+         d.R > kRowsTile && (d.outer == 1 || d.yso == 1);
 }
 
 size_t axis_workspace_bytes(int64_t outer, int64_t R, int64_t inner, bool lsm) {
@@ -1037,10 +1044,8 @@ size_t axis_workspace_bytes(int64_t outer, int64_t R, int64_t inner, bool lsm) {
     size_t r = 0;
     if (lsm) {
       r = rows_workspace_bytes(outer, R);
-    } else {
-      const AxisDims rd{outer, R, 1, R, 1, 1, 0};
-      if (lse_rows_split(rd))
-        r = (size_t)outer * (size_t)((R + kRowsTile - 1) / kRowsTile) * sizeof(float2);
+    } else if (R > kRowsTile) {  // lse_rows_split, whatever the alignment
+      r = (size_t)outer * (size_t)((R + kRowsTile - 1) / kRowsTile) * sizeof(float2);
     }
     if (r > n) n = r;
   }
@@ -1050,7 +1055,7 @@ size_t axis_workspace_bytes(int64_t outer, int64_t R, int64_t inner, bool lsm) {
 hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStream_t stream,
                            bool with_ws, void *ws) {
   if (as_rows(d, false)) {
-    if (with_ws && ws != nullptr && lse_rows_split(d)) {
+    if (with_ws && ws != nullptr && lse_rows_split(d, x)) {
       const int64_t nchunks = (d.R + kRowsTile - 1) / kRowsTile;
       const hipError_t e = launch_lse_rows_partial(x, d.outer, d.R, d.xso, kRowsTile, ws, stream);
       if (e != hipSuccess) return e;

@@ -862,6 +862,9 @@ __global__ __launch_bounds__(kRowsThreads) void rows_lse_stream_kernel(
 // (same box, GB/s logsumexp / log_softmax, one value -> 8 bytes per access:
 // 3 columns 3908 / 3378 -> 4886 / 4014, 17 columns 3568 / 3395 -> 3600 / 3857;
 // from 99 columns on 8-byte accesses measured 6-15 % slower)
+#ifndef LSE_ROWS_LSE_SEG_MAX
+#define LSE_ROWS_LSE_SEG_MAX 2048  // logsumexp-only rows up to this long take a segment
+#endif
 // Interleaved blocks (axis calls with inner > 1) take a wave-wide segment up
 // to 64 values per lane: the axis kernels they would fall back to read such
 // blocks 8-16 bytes per plane and lane.
@@ -1359,7 +1362,7 @@ template <int OUT, int INNER = 1>
 hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols, int64_t ldx,
                            int64_t ldy, bool vec, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  if (cols < 1 || cols > (INNER > 1 ? kSegInterleavedMax : LSE_ROWS_SEG_MAX))
+  if (cols < 1 || cols > (INNER > 1 || OUT == kOutLse ? kSegInterleavedMax : LSE_ROWS_SEG_MAX))
     return hipErrorInvalidValue;
   int g = 1;
   while (g < kWave && 4 * g < cols) g *= 2;
@@ -1390,14 +1393,14 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
       case 8 * kWave: launch_seg<64, 8, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
       case 16 * kWave: launch_seg<64, 16, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy); break;
       case 32 * kWave:
-        if constexpr (INNER > 1) {
+        if constexpr (INNER > 1 || OUT == kOutLse) {
           launch_seg<64, 32, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy);
           break;
         } else {
           return hipErrorInvalidValue;
         }
       case 64 * kWave:
-        if constexpr (INNER > 1) {
+        if constexpr (INNER > 1 || OUT == kOutLse) {
           launch_seg<64, 64, OUT, INNER>(lay, grid, stream, xb, yb, nr, cols, ldx, ldy);
           break;
         } else {
@@ -1557,7 +1560,7 @@ hipError_t launch_rows_lse(const float *x, int64_t rows, int64_t cols, int64_t l
                            int64_t ldo, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const bool vec = (cols % 4 == 0) && (ldx % 4 == 0) && ((uintptr_t)x % 16 == 0);
-  if (cols <= LSE_ROWS_SEG_MAX)
+  if (cols <= LSE_ROWS_LSE_SEG_MAX)
     return launch_rows_seg<kOutLse>(x, out, rows, cols, ldx, ldo, vec, stream);
   return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
     const dim3 grid((uint32_t)nr);

@@ -110,6 +110,24 @@ def test_rows_short_ragged(orc, cols, layout):
     assert (obuf[1:].view(rows, 2)[:, 1] == 7.0).all()
 
 
+@pytest.mark.parametrize("rows,cols,off", [(3000, 1025, 0), (2000, 1500, 1), (1000, 2048, 0),
+                                           (500, 2049, 0), (40, 50257, 0), (30, 50257, 1),
+                                           (2000, 16385, 0)])
+def test_row_logsumexp_segments_and_split(orc, rows, cols, off):
+    """Last-axis logsumexp: rows up to 2048 values in wave-wide segments (up
+    to 32 values per lane), longer rows off the 16-byte grid (odd lengths, a
+    4-byte offset) split into chunk pairs whatever the number of rows."""
+    buf = inputs.normal((rows * cols + off,), seed=rows + cols + off, sigma=3.0, device=DEV)
+    x = buf[off:].view(rows, cols)
+    x[1, 7] = float("inf")
+    x[2, :] = -float("inf")
+    x[3, cols - 1] = float("nan")
+    out = L.lse_reduce_axis(x, 1)
+    torch.cuda.synchronize()
+    ref = orc.lse_axis(x.cpu().numpy().reshape(rows, cols, 1)).reshape(rows)
+    compare(out.cpu().numpy(), ref, what=f"row lse {rows}x{cols}+{off}")
+
+
 def test_rows_short_many_rows(orc):
     """200003 rows of 256 and 2000003 rows of 10: every row's log_softmax
     sums to 1, sampled rows (first, last, partial last workgroup) against the
