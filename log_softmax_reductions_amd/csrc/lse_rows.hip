@@ -1129,8 +1129,7 @@ __global__ __launch_bounds__(kRowsThreads) void rows_stream_write_kernel(
   }
 }
 
-// One wave per row: row_lse = M + log(S) of the row's nchunks pairs.
-// One wave per row, 4 rows per workgroup: merges the row's chunk pairs.
+// One wave per row, 4 rows per workgroup: merges the row's nchunks chunk pairs.
 // OUT = kOutLse writes the row's logsumexp to out[row]; kOutLogSoftmax /
 // kOutSoftmax write the pair (M, log S) / (M, 1 / S) of the row to
 // ((float2 *)out)[row] for rows_apply_kernel.
