@@ -23,7 +23,7 @@ Flags: --gpus N (only 1 is supported: this build runs on one GPU),
 --only {rows_large,axis0_large,axis0_walk,conv_chain,softmax_large,axis_chain_layout,copy,
         copy_tile,copy_stream,copy_tile_1_per_cu,rows_odd_cols,rows_offset_view,
         chain_600x520_recompute,chain_600x520_staged,rows_large_reread,short_rows_128,
-        short_rows_99,few_outputs,one_long_row}
+        short_rows_99,few_outputs,channel_blocks,one_long_row}
 to run just that kernel
 (for profiler runs; prints timing only).
 """
@@ -240,6 +240,7 @@ def copy_ceiling(x, y, steps=5, warmup=2):
 
 SHORT_ROWS = 1 << 20
 FEW_OUT_SHAPE = (1 << 20, 64)   # 64 outputs over 2^20 planes
+CHANNEL_SHAPE = (1024, 2048, 49)  # channel reduction over 7 x 7 maps (contiguous blocks)
 LONG_ROW = 100_000_000
 
 
@@ -424,6 +425,24 @@ def bench_secondary(steps=10, warmup=3):
         "log_softmax_hbm_frac": round(nb_lsm / lsm_ms / 1e6 / HBM_PEAK_GBS, 4),
         "note": "log_softmax reads x twice here (pairs, merge, write launches)"}
     del x, o, y
+    # a channel reduction over small feature maps: contiguous (2048, 49) blocks
+    # read as flat sweeps
+    x = inputs.normal(CHANNEL_SHAPE, seed=29, sigma=2.0, device="cuda")
+    o = torch.empty((CHANNEL_SHAPE[0], CHANNEL_SHAPE[2]), device="cuda")
+    y = torch.empty_like(x)
+    _, ev = timed_launches(lambda: L.lse_reduce_axis(x, 1, o), steps, warmup)
+    lse_ms = sum(ev) / len(ev)
+    _, ev = timed_launches(lambda: L.log_softmax_axis(x, 1, y), steps, warmup)
+    lsm_ms = sum(ev) / len(ev)
+    nb_lse, nb_lsm = 4 * (x.numel() + o.numel()), 8 * x.numel()
+    out["channel_blocks"] = {
+        "workload": f"logsumexp and log_softmax dim=1 of {CHANNEL_SHAPE} fp32 N(0,4)",
+        "lse_ms": round(lse_ms, 4), "lse_GB/s": round(nb_lse / lse_ms / 1e6, 1),
+        "lse_hbm_frac": round(nb_lse / lse_ms / 1e6 / HBM_PEAK_GBS, 4),
+        "log_softmax_ms": round(lsm_ms, 4), "log_softmax_GB/s": round(nb_lsm / lsm_ms / 1e6, 1),
+        "log_softmax_hbm_frac": round(nb_lsm / lsm_ms / 1e6 / HBM_PEAK_GBS, 4),
+        "note": "log_softmax reads x twice here (pairs, then merge and write)"}
+    del x, o, y
     x = inputs.normal((1, LONG_ROW), seed=23, device="cuda")
     o = torch.empty((1,), device="cuda")
     y = torch.empty_like(x)
@@ -515,6 +534,13 @@ def run_only(which, steps, warmup):
         y = torch.empty_like(x)
         timed_launches(lambda: L.lse_reduce_axis0(x, o), steps, warmup)
         wall, ev = timed_launches(lambda: L.log_softmax_axis(x, 0, y), steps, warmup)
+    elif which == "channel_blocks":
+        # logsumexp then log_softmax over dim 1 of (1024, 2048, 49)
+        x = inputs.normal(CHANNEL_SHAPE, seed=29, sigma=2.0, device="cuda")
+        o = torch.empty((CHANNEL_SHAPE[0], CHANNEL_SHAPE[2]), device="cuda")
+        y = torch.empty_like(x)
+        timed_launches(lambda: L.lse_reduce_axis(x, 1, o), steps, warmup)
+        wall, ev = timed_launches(lambda: L.log_softmax_axis(x, 1, y), steps, warmup)
     elif which == "one_long_row":
         x = inputs.normal((1, LONG_ROW), seed=23, device="cuda")
         o = torch.empty((1,), device="cuda")

@@ -136,8 +136,9 @@ lse_status_t log_softmax_axis_strided(const float *x, float *y, int64_t outer,
  * workgroup.  With a workspace the planes of each run of outputs are split
  * across workgroups whose per-output (max, sum) pairs are merged by a second
  * launch in a fixed order (log_softmax then writes y in a third launch, so x
- * is read twice there), and long contiguous last-axis rows take the split-row
- * kernels of case B.  The reduction each output receives is the same as
+ * is read twice there); contiguous (R, inner) blocks of short runs split the
+ * same way along the block; and long contiguous last-axis rows take the
+ * split-row kernels of case B.  The reduction each output receives is the same as
  * without a workspace; only the order of the additions differs.
  *   lse_axis_workspace_bytes: bytes the call with these sizes needs (0 when
  *     none of the split paths applies, in which case ws may be NULL);

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblse.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["lse_axis.hip", "lse_cols.hip", "lse_rows.hip", "conv_chain.hip", "lse_noalloc.hip", "lse_api.hip"]
+SOURCES = ["lse_axis.hip", "lse_cols.hip", "lse_blocks.hip", "lse_rows.hip", "conv_chain.hip", "lse_noalloc.hip", "lse_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [

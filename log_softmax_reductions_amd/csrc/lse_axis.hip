@@ -24,8 +24,9 @@
 // 4-byte alignment, and the last lane of each run reads the run's last 4
 // columns and writes only those its neighbour does not (ua_columns).
 //
-// A contiguous last axis (inner = 1) runs as rows (lse_rows.hip), and few
-// outputs over many planes as the column split (lse_cols.hip).
+// A contiguous last axis (inner = 1) runs as rows (lse_rows.hip), contiguous
+// blocks of short runs as flat sweeps (lse_blocks.hip), and few outputs over
+// many planes as the column split (lse_cols.hip).
 //
 // Running state per output: m = max so far, s = sum of exp(v - c(m)) with the
 // shift c(m) = m when m is finite and 0 when m is +-inf (all values -inf, or
@@ -1015,6 +1016,9 @@ static bool as_rows(const AxisDims &d, bool lsm) {
 #ifndef LSE_AXIS_COLS
 #define LSE_AXIS_COLS 1   // few outputs over many planes take the column split (lse_cols.hip)
 #endif
+#ifndef LSE_AXIS_BLOCKS
+#define LSE_AXIS_BLOCKS 1 // contiguous blocks with short inner runs read flat (lse_blocks.hip)
+#endif
 #ifndef LSE_AXIS_SEG
 #define LSE_AXIS_SEG 1    // short (R, 2 or 4) blocks take the short-row segments (lse_rows.hip)
 #endif
@@ -1040,6 +1044,10 @@ size_t axis_workspace_bytes(int64_t outer, int64_t R, int64_t inner, bool lsm) {
   if (outer < 1 || R < 1 || inner < 1) return 0;
   const AxisDims d{outer, R, inner, R * inner, inner, lsm ? R * inner : inner, lsm ? inner : 0};
   size_t n = LSE_AXIS_COLS ? cols_workspace_bytes(d, lsm) : 0;
+  if (LSE_AXIS_BLOCKS) {
+    const size_t k = blocks_workspace_bytes(d, lsm);
+    if (k > n) n = k;
+  }
   if (inner == 1) {
     size_t r = 0;
     if (lsm) {
@@ -1065,6 +1073,7 @@ hipError_t launch_lse_axis(const float *x, float *out, const AxisDims &d, hipStr
   }
   hipError_t e = hipSuccess;
   if (LSE_AXIS_SEG && launch_axis_seg(x, out, d, false, stream, e)) return e;
+  if (LSE_AXIS_BLOCKS && launch_blocks(x, out, d, false, with_ws, ws, stream, e)) return e;
   if (LSE_AXIS_COLS && launch_cols(x, out, d, false, with_ws, ws, stream, e)) return e;
   return launch_axis<false>(x, out, d, stream);
 }
@@ -1079,6 +1088,7 @@ hipError_t launch_log_softmax_axis(const float *x, float *y, const AxisDims &d,
   }
   hipError_t e = hipSuccess;
   if (LSE_AXIS_SEG && launch_axis_seg(x, y, d, true, stream, e)) return e;
+  if (LSE_AXIS_BLOCKS && launch_blocks(x, y, d, true, with_ws, ws, stream, e)) return e;
   if (LSE_AXIS_COLS && launch_cols(x, y, d, true, with_ws, ws, stream, e)) return e;
   return launch_axis<true>(x, y, d, stream);
 }

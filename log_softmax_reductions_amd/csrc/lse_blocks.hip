@@ -1,0 +1,409 @@
+// lse_blocks.hip — logsumexp and log_softmax over the middle axis of an
+// (outer, R, inner) array whose (R, inner) blocks are each one contiguous run
+// of memory and whose inner run is short and off the 4-column grid: 2 to 256
+// columns, such as a reduction over the channels of 7 x 7 feature maps.  A
+// plane of such a block is a few hundred bytes, so kernels that give each
+// lane columns of its own read it in short pieces, one value per access when
+// the run is not a multiple of 4.
+//
+// POPCORNBENCH FW-GLM-5-1 l1_p29 (torch.logsumexp over a leading axis): each
+// output is the max-shifted sum over its R values, which here lie inner
+// floats apart inside the block.  The block is read as the flat run it is:
+//   * 4 consecutive floats per lane, a workgroup's lanes covering a sweep of
+//     W consecutive floats, W a multiple of both 4 and inner (the largest
+//     such W up to 1024); the next sweep is W floats on, so every lane meets
+//     the same 4 columns, (4 t + e) mod inner, on every sweep and keeps one
+//     running (m, s) for each (16-byte accesses at the block's own 4-byte
+//     phase, shared by all lanes);
+//   * the W / inner partials of each column are merged in a fixed order
+//     through LDS;
+//   * with a workspace, a block's planes are split into chunks, one
+//     workgroup each, whose (m, s) pairs per column are merged afterwards in
+//     chunk order (a merge launch for logsumexp; for log_softmax each
+//     workgroup of the apply launch merges its block's pairs itself, the same
+//     way, and writes (x - M) - log S over its chunk).  Without one, one
+//     workgroup takes a whole block, and log_softmax reads it again.
+#include "lse_device.hpp"
+#include "lse_internal.hpp"
+
+namespace lse {
+namespace {
+
+#ifndef LSE_BLK_MAX_INNER
+#define LSE_BLK_MAX_INNER 256      // widest inner run the kernels take
+#endif
+#ifndef LSE_BLK_TARGET_GROUPS
+#define LSE_BLK_TARGET_GROUPS 1024 // workgroups the chunking aims for
+#endif
+#ifndef LSE_BLK_MAX_CHUNKS
+#define LSE_BLK_MAX_CHUNKS 64      // chunks per block at most (their pairs are merged serially)
+#endif
+#ifndef LSE_BLK_U
+#define LSE_BLK_U 4                // 16-byte loads per lane in flight
+#endif
+#ifndef LSE_BLK_MIN_TRIPS
+#define LSE_BLK_MIN_TRIPS 4        // chunks of at least this many U-sweep trips
+#endif
+#ifndef LSE_BLK_GATE
+#define LSE_BLK_GATE 1             // 0: never; 1: the shapes measured faster here; 2: every eligible call
+#endif
+#ifndef LSE_BLK_NOWS_MIN_OUTER
+#define LSE_BLK_NOWS_MIN_OUTER 512 // without a workspace: at least this many blocks
+#endif
+#ifndef LSE_BLK_MIN_BLOCK
+#define LSE_BLK_MIN_BLOCK 2048     // gate 1: blocks of at least this many floats,
+#endif
+#ifndef LSE_BLK_MIN_OUTER
+#define LSE_BLK_MIN_OUTER 32       // ... at least this many of them,
+#endif
+#ifndef LSE_BLK_GATE_INNER
+#define LSE_BLK_GATE_INNER 128     // ... inner runs up to this wide,
+#endif
+#ifndef LSE_BLK_BIG_BLOCK
+#define LSE_BLK_BIG_BLOCK 65536    // ... or, for logsumexp, blocks of at least this many floats
+#endif
+
+constexpr int kBlkThreads = 256;
+constexpr int kBlkU = LSE_BLK_U;
+constexpr int kBlkMaxInner = LSE_BLK_MAX_INNER;
+static_assert(kBlkMaxInner <= kBlkThreads, "a period of at most one workgroup");
+
+enum BlkMode {
+  kBlkPartial = 0,      // the chunk's (m, s) per column into the workspace
+  kBlkPartialKeep = 1,  // the same, x read with cached loads (the apply reads it again)
+  kBlkLse = 2,          // one chunk: the logsumexp
+  kBlkLsm = 3           // one chunk: log_softmax, the block read again
+};
+
+typedef float v4b4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// Sweep geometry of an inner run: lp lanes cover one period of lcm(4, inner)
+// floats, a workgroup's act = (256 / lp) lp lanes a sweep of 4 act floats.
+struct BlkSweep {
+  int lp, act, w;
+};
+__host__ __device__ inline BlkSweep blk_sweep(int inner) {
+  const int g = (inner % 4 == 0) ? 4 : ((inner % 2 == 0) ? 2 : 1);
+  BlkSweep s;
+  s.lp = inner / g;
+  s.act = (kBlkThreads / s.lp) * s.lp;
+  s.w = 4 * s.act;
+  return s;
+}
+
+// The lane's 4 floats at j of a run ending at f (floats at or past f read as
+// fill).
+template <bool NT>
+__device__ __forceinline__ void blk_load4(const float *p, int64_t j, int64_t f, float fill,
+                                          float (&v)[4]) {
+  if (j + 4 <= f) {
+    const v4b4 *a = reinterpret_cast<const v4b4 *>(p + j);
+    const v4b4 q = NT ? __builtin_nontemporal_load(a) : *a;
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = (j + e < f) ? (NT ? __builtin_nontemporal_load(p + j + e) : p[j + e]) : fill;
+  }
+}
+
+// y = (x - M_e) - L_e over the lane's floats j, j + w, ... < f1 of the block
+// (M_e, L_e: its 4 columns'), kBlkU loads in flight.
+__device__ __forceinline__ void blk_write(const float *xb, float *yb, int64_t j, int64_t f1, int w,
+                                          const float (&fm)[4], const float (&fl)[4]) {
+  for (; j < f1; j += (int64_t)w * kBlkU) {
+    float q[kBlkU][4];
+#pragma unroll
+    for (int u = 0; u < kBlkU; ++u) blk_load4<true>(xb, j + (int64_t)u * w, f1, 0.0f, q[u]);
+#pragma unroll
+    for (int u = 0; u < kBlkU; ++u) {
+      const int64_t jj = j + (int64_t)u * w;
+      float r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = (q[u][e] - fm[e]) - fl[e];
+      if (jj + 4 <= f1) {
+        __builtin_nontemporal_store(v4b4{r[0], r[1], r[2], r[3]}, reinterpret_cast<v4b4 *>(yb + jj));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 3; ++e)
+          if (jj + e < f1) __builtin_nontemporal_store(r[e], yb + jj + e);
+      }
+    }
+  }
+}
+
+// (M, log S) of column t < inner from the block's chunk pairs (fixed order).
+__device__ __forceinline__ float2 blk_merge_pairs(const float2 *p, int64_t chunks) {
+  float M = p[0].x;
+  for (int64_t k = 1; k < chunks; ++k) M = fmaxf(M, p[k].x);
+  float S = 0.0f;
+  for (int64_t k = 0; k < chunks; ++k) S += fold_weighted(p[k].x, p[k].y, M);
+  return make_float2(M, S);
+}
+
+// Merge of the nk partials of each column c < inner, which sit at part[c +
+// k inner] (flat index 4 lane + e of the sweep), into res[c] = (M, S): G
+// lanes per column, lane g folding partials g, g + G, ... (max first, then
+// the weighted sum), then reduced across the G lanes; the same order on every
+// call.  G = the largest power of two up to nk / 4 (at most 64).
+template <int G>
+__device__ __forceinline__ void blk_merge_g(const float2 *part, float2 *res, int inner, int nk,
+                                            int t) {
+  constexpr int kCpw = kWave / G;  // columns per wave and round
+  const int lane = t % kWave, wave = t / kWave;
+  const int g = lane % G;
+  for (int c0 = wave * kCpw; c0 < inner; c0 += (kBlkThreads / kWave) * kCpw) {
+    const int c = c0 + lane / G;
+    float m = -__builtin_inff();
+    if (c < inner)
+      for (int k = g; k < nk; k += G) m = fmaxf(m, part[c + k * inner].x);
+    m = seg_allreduce<G>(m, OpMax{});
+    float s = 0.0f;
+    if (c < inner)
+      for (int k = g; k < nk; k += G) s += fold_weighted(part[c + k * inner].x, part[c + k * inner].y, m);
+    s = seg_allreduce<G>(s, OpSum{});
+    if (g == 0 && c < inner) res[c] = make_float2(m, s);
+  }
+}
+
+__device__ __forceinline__ void blk_merge_cols(const float2 *part, float2 *res, int inner, int nk,
+                                               int t) {
+  const int q = nk / 4;
+  if (q >= 64) blk_merge_g<64>(part, res, inner, nk, t);
+  else if (q >= 32) blk_merge_g<32>(part, res, inner, nk, t);
+  else if (q >= 16) blk_merge_g<16>(part, res, inner, nk, t);
+  else if (q >= 8) blk_merge_g<8>(part, res, inner, nk, t);
+  else if (q >= 4) blk_merge_g<4>(part, res, inner, nk, t);
+  else if (q >= 2) blk_merge_g<2>(part, res, inner, nk, t);
+  else blk_merge_g<1>(part, res, inner, nk, t);
+}
+
+// Workgroup (o, c) of an (outer, chunks) grid, chunk fastest: planes
+// [c rc, min(R, (c + 1) rc)) of block o (rc a multiple of 4, so every chunk
+// starts on a period).  Lane t < act folds floats 4 t + k w .. + 3 of the
+// chunk into the running pairs of columns (4 (t mod lp) + e) mod inner.
+//   kBlkPartial(Keep): pairs[(o inner + col) chunks + c] = (m, s)
+//   kBlkLse:           out[o yso + col] = m + log s
+//   kBlkLsm:           y[o yso + k] = (x - m) - log s, reading the block again
+template <int MODE>
+__global__ __launch_bounds__(kBlkThreads) void axis_block_kernel(const float *__restrict__ x,
+                                                                 float *__restrict__ out,
+                                                                 AxisDims d, int64_t chunks,
+                                                                 int64_t rc,
+                                                                 float2 *__restrict__ pairs) {
+  __shared__ float2 part[4 * kBlkThreads];
+  __shared__ float2 res[kBlkMaxInner];
+  float2 *tab = res;  // log_softmax: (M, log S) in place of (M, S)
+  constexpr bool kNt = MODE == kBlkPartial || MODE == kBlkLse;  // else x is read again
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  const int64_t c = b % chunks;
+  const int64_t o = b / chunks;
+  const int inner = (int)d.inner;
+  const BlkSweep sw = blk_sweep(inner);
+  const int64_t r0 = c * rc;
+  const int64_t r1 = (d.R - r0 < rc) ? d.R : r0 + rc;
+  const int64_t f0 = r0 * inner, f1 = r1 * inner;
+  const float *xb = x + o * d.xso;
+  const float ninf = -__builtin_inff();
+  float m[4], s[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m[e] = ninf;
+    s[e] = 0.0f;
+  }
+  if (t < sw.act) {
+    for (int64_t j = f0 + 4 * t; j < f1; j += (int64_t)sw.w * kBlkU) {
+      float q[kBlkU][4];
+#pragma unroll
+      for (int u = 0; u < kBlkU; ++u) blk_load4<kNt>(xb, j + (int64_t)u * sw.w, f1, ninf, q[u]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v[kBlkU];
+#pragma unroll
+        for (int u = 0; u < kBlkU; ++u) v[u] = q[u][e];
+        fold_block<kBlkU>(v, m[e], s[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[4 * t + e] = make_float2(m[e], s[e]);
+  }
+  __syncthreads();
+  blk_merge_cols(part, res, inner, sw.w / inner, t);
+  __syncthreads();
+  if (t < inner) {
+    const float M = res[t].x, S = res[t].y;
+    if constexpr (MODE == kBlkPartial || MODE == kBlkPartialKeep) {
+      pairs[(o * inner + t) * chunks + c] = make_float2(M, S);
+    } else if constexpr (MODE == kBlkLse) {
+      out[o * d.yso + t] = M + logf(S);
+    } else {
+      tab[t] = make_float2(M, logf(S));
+    }
+  }
+  if constexpr (MODE == kBlkLsm) {
+    __syncthreads();
+    if (t < sw.act) {
+      float fm[4], fl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 v = tab[(4 * (t % sw.lp) + e) % inner];
+        fm[e] = v.x;
+        fl[e] = v.y;
+      }
+      blk_write(xb, out + o * d.yso, f0 + 4 * t, f1, sw.w, fm, fl);
+    }
+  }
+}
+
+// logsumexp of a block's columns from their chunk pairs: one thread per
+// (o, col), chunks merged in order.
+__global__ __launch_bounds__(256) void axis_block_merge_kernel(const float2 *__restrict__ pairs,
+                                                               float *__restrict__ out,
+                                                               AxisDims d, int64_t chunks) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= d.outer * d.inner) return;
+  const int64_t o = i / d.inner;
+  const int64_t col = i - o * d.inner;
+  const float2 f = blk_merge_pairs(pairs + i * chunks, chunks);
+  out[o * d.yso + col] = f.x + logf(f.y);
+}
+
+// log_softmax over chunk c of block o (the pair launch's grid): the block's
+// chunk pairs are merged first (the order of the merge kernel), then written.
+__global__ __launch_bounds__(kBlkThreads) void axis_block_apply_kernel(
+    const float *__restrict__ x, float *__restrict__ y, AxisDims d, int64_t chunks, int64_t rc,
+    const float2 *__restrict__ pairs) {
+  __shared__ float2 tab[kBlkMaxInner];
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  const int64_t c = b % chunks;
+  const int64_t o = b / chunks;
+  const int inner = (int)d.inner;
+  const BlkSweep sw = blk_sweep(inner);
+  if (t < inner) {
+    const float2 f = blk_merge_pairs(pairs + (o * inner + t) * chunks, chunks);
+    tab[t] = make_float2(f.x, logf(f.y));
+  }
+  __syncthreads();
+  if (t >= sw.act) return;
+  float fm[4], fl[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float2 v = tab[(4 * (t % sw.lp) + e) % inner];
+    fm[e] = v.x;
+    fl[e] = v.y;
+  }
+  const int64_t r0 = c * rc;
+  const int64_t r1 = (d.R - r0 < rc) ? d.R : r0 + rc;
+  blk_write(x + o * d.xso, y + o * d.yso, r0 * inner + 4 * t, r1 * inner, sw.w, fm, fl);
+}
+
+struct BlkPlan {
+  int64_t chunks, rc;
+  int mode;
+};
+
+// The block plan of a call, or false when the call keeps the other axis
+// kernels.  with_ws: the caller can supply blocks_workspace_bytes().
+bool blk_plan(const AxisDims &d, bool lsm, bool with_ws, BlkPlan &p) {
+  if (LSE_BLK_GATE == 0) return false;
+  if (d.outer < 1 || d.R < 1 || d.inner < 2 || d.inner > kBlkMaxInner) return false;
+  if (d.xsr != d.inner || (lsm && d.ysr != d.inner)) return false;
+  if (d.R * d.inner > (int64_t(1) << 40)) return false;
+  const BlkSweep sw = blk_sweep((int)d.inner);
+  // chunks of whole periods (4 planes) and at least LSE_BLK_MIN_TRIPS trips
+  const int64_t trip = (int64_t)sw.w * kBlkU;
+  int64_t min_planes = (LSE_BLK_MIN_TRIPS * trip + d.inner - 1) / d.inner;
+  min_planes = (min_planes + 3) / 4 * 4;
+  p.chunks = 1;
+  if (with_ws) {
+    int64_t k = (LSE_BLK_TARGET_GROUPS + d.outer - 1) / d.outer;
+    const int64_t kmax = d.R / min_planes;
+    if (k > kmax) k = kmax;
+    if (k > LSE_BLK_MAX_CHUNKS) k = LSE_BLK_MAX_CHUNKS;
+    p.chunks = k < 1 ? 1 : k;
+  } else if (d.outer < LSE_BLK_NOWS_MIN_OUTER) {
+    return false;
+  }
+  p.rc = ((d.R + p.chunks - 1) / p.chunks + 3) / 4 * 4;
+  p.chunks = (d.R + p.rc - 1) / p.rc;
+  if (d.outer * p.chunks > 0x7fffffffLL) return false;
+  p.mode = p.chunks > 1 ? (lsm ? kBlkPartialKeep : kBlkPartial) : (lsm ? kBlkLsm : kBlkLse);
+  return true;
+}
+
+// Which calls take the blocks (measured against the axis kernels, the column
+// split and the plane split on the same shapes): blocks of at least
+// LSE_BLK_MIN_BLOCK floats (smaller ones leave most of a sweep's lanes idle
+// and make workgroups too short) and at least LSE_BLK_MIN_OUTER of them (a
+// few long blocks split into more chunks in the column split); then inner
+// runs up to LSE_BLK_GATE_INNER, with a workspace only off the 16-byte grid
+// (on it the axis kernels and the column split were about as fast), except
+// logsumexp over blocks of LSE_BLK_BIG_BLOCK floats or more, which the
+// blocks read faster whatever the run (wider runs the axis kernels read well
+// otherwise, and their log_softmax reads x once).
+bool blk_wanted(const AxisDims &d, bool lsm, bool with_ws, const float *x, const float *out) {
+  if (LSE_BLK_GATE == 2) return true;
+  const int64_t n = d.R * d.inner;
+  if (n < LSE_BLK_MIN_BLOCK || d.outer < LSE_BLK_MIN_OUTER) return false;
+  const bool big_lse = !lsm && n >= LSE_BLK_BIG_BLOCK;
+  if (d.inner > LSE_BLK_GATE_INNER) return big_lse;
+  const uintptr_t a = (uintptr_t)x | (lsm ? (uintptr_t)out : 0);
+  const int64_t st = d.inner | d.xso | (lsm ? d.yso : 0);
+  const bool grid16 = st % 4 == 0 && a % 16 == 0;
+  return !grid16 || !with_ws || big_lse;
+}
+
+size_t blk_ws_bytes(const AxisDims &d, const BlkPlan &p) {
+  return p.chunks > 1 ? (size_t)(d.outer * d.inner * p.chunks * 8) : 0;
+}
+
+}  // namespace
+
+size_t blocks_workspace_bytes(const AxisDims &d, bool lsm) {
+  BlkPlan p;
+  return blk_plan(d, lsm, true, p) ? blk_ws_bytes(d, p) : 0;
+}
+
+bool launch_blocks(const float *x, float *out, const AxisDims &d, bool lsm, bool with_ws,
+                   void *ws, hipStream_t stream, hipError_t &e) {
+  BlkPlan p;
+  if (!blk_plan(d, lsm, with_ws, p) || !blk_wanted(d, lsm, with_ws, x, out)) return false;
+  if (p.chunks > 1 && ws == nullptr) return false;
+  const dim3 grid((uint32_t)(d.outer * p.chunks));
+  const dim3 block(kBlkThreads);
+  auto *pairs = reinterpret_cast<float2 *>(ws);
+  switch (p.mode) {
+    case kBlkPartial:
+      hipLaunchKernelGGL((axis_block_kernel<kBlkPartial>), grid, block, 0, stream, x, out, d,
+                         p.chunks, p.rc, pairs);
+      break;
+    case kBlkPartialKeep:
+      hipLaunchKernelGGL((axis_block_kernel<kBlkPartialKeep>), grid, block, 0, stream, x, out, d,
+                         p.chunks, p.rc, pairs);
+      break;
+    case kBlkLse:
+      hipLaunchKernelGGL((axis_block_kernel<kBlkLse>), grid, block, 0, stream, x, out, d, p.chunks,
+                         p.rc, pairs);
+      break;
+    default:
+      hipLaunchKernelGGL((axis_block_kernel<kBlkLsm>), grid, block, 0, stream, x, out, d, p.chunks,
+                         p.rc, pairs);
+      break;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess || p.chunks == 1) return true;
+  if (!lsm) {
+    const int64_t cols = d.outer * d.inner;
+    hipLaunchKernelGGL(axis_block_merge_kernel, dim3((uint32_t)((cols + 255) / 256)), dim3(256), 0,
+                       stream, pairs, out, d, p.chunks);
+  } else {
+    hipLaunchKernelGGL(axis_block_apply_kernel, grid, block, 0, stream, x, out, d, p.chunks, p.rc,
+                       pairs);
+  }
+  e = hipGetLastError();
+  return true;
+}
+
+}  // namespace lse

@@ -37,6 +37,13 @@ size_t cols_workspace_bytes(const AxisDims &d, bool lsm);
 bool launch_cols(const float *x, float *out, const AxisDims &d, bool lsm, bool with_ws, void *ws,
                  hipStream_t stream, hipError_t &e);
 
+// Contiguous (R, inner) blocks with a short inner run (lse_blocks.hip): each
+// block read as one flat run through LDS.  launch_blocks returns false when
+// the call does not take this path; otherwise e is the launch status.
+size_t blocks_workspace_bytes(const AxisDims &d, bool lsm);
+bool launch_blocks(const float *x, float *out, const AxisDims &d, bool lsm, bool with_ws,
+                   void *ws, hipStream_t stream, hipError_t &e);
+
 // ---------------------------------------------------------------- case B
 // Tile geometry of the row kernels (overridable at build time for sweeps).
 #ifndef LSE_ROWS_THREADS
