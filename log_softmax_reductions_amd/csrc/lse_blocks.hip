@@ -1,7 +1,7 @@
 // lse_blocks.hip — logsumexp and log_softmax over the middle axis of an
 // (outer, R, inner) array whose (R, inner) blocks are each one contiguous run
-// of memory and whose inner run is short and off the 4-column grid: 2 to 256
-// columns, such as a reduction over the channels of 7 x 7 feature maps.  A
+// of memory and whose inner run is short: 2 to 256 columns, such as a
+// reduction over the channels of 7 x 7 feature maps.  A
 // plane of such a block is a few hundred bytes, so kernels that give each
 // lane columns of its own read it in short pieces, one value per access when
 // the run is not a multiple of 4.
@@ -22,7 +22,18 @@
 //     chunk order (a merge launch for logsumexp; for log_softmax each
 //     workgroup of the apply launch merges its block's pairs itself, the same
 //     way, and writes (x - M) - log S over its chunk).  Without one, one
-//     workgroup takes a whole block, and log_softmax reads it again.
+//     workgroup takes a whole block, and log_softmax reads it again;
+//   * log_softmax keeps its values in registers where they fit (the split-row
+//     protocol of log_softmax_rows, per column): a block of up to 16 sweeps
+//     is one workgroup's, loaded once and written from registers; a longer
+//     one (with a workspace) is split into chunks of 16 sweeps whose
+//     workgroups publish their (m, s) per column into zeroed slots
+//     (compare-and-swap from 0), wait for their siblings', merge them in
+//     chunk order and write from registers.  A workgroup that has waited too
+//     long computes every still-missing sibling chunk's pairs itself from x,
+//     in the owner's order (the first writer of a slot wins), so progress
+//     never depends on dispatch order and the results not on who computed a
+//     pair.
 #include "lse_device.hpp"
 #include "lse_internal.hpp"
 
@@ -58,6 +69,18 @@ namespace {
 #endif
 #ifndef LSE_BLK_GATE_INNER
 #define LSE_BLK_GATE_INNER 128     // ... inner runs up to this wide,
+#endif
+#ifndef LSE_BLK_RESIDENT
+#define LSE_BLK_RESIDENT 1         // log_softmax from registers (one chunk, or chunks that wait)
+#endif
+#ifndef LSE_BLK_RES_MAX_CHUNKS
+#define LSE_BLK_RES_MAX_CHUNKS 32  // ... for blocks of at most this many 16-sweep chunks
+#endif
+#ifndef LSE_BLK_RES_MIN_GROUPS
+#define LSE_BLK_RES_MIN_GROUPS 4096 // ... and at least this many workgroups
+#endif
+#ifndef LSE_BLK_SLEEP
+#define LSE_BLK_SLEEP 8            // s_sleep argument between polls (x 64 clocks)
 #endif
 #ifndef LSE_BLK_BIG_BLOCK
 #define LSE_BLK_BIG_BLOCK 65536    // ... or, for logsumexp, blocks of at least this many floats
@@ -299,10 +322,231 @@ __global__ __launch_bounds__(kBlkThreads) void axis_block_apply_kernel(
   blk_write(x + o * d.xso, y + o * d.yso, r0 * inner + 4 * t, r1 * inner, sw.w, fm, fl);
 }
 
+// ------------------------------------------------------- register-resident
+// Sweeps per workgroup of the register-resident log_softmax: 16 x 4 floats
+// per lane.
+#ifndef LSE_BLK_RES_K
+#define LSE_BLK_RES_K 16
+#endif
+constexpr int kBlkResK = LSE_BLK_RES_K;
+#ifndef LSE_BLK_RES_WPE
+#define LSE_BLK_RES_WPE 4          // waves per SIMD the split kernel's registers must allow (0: any)
+#endif
+
+// Fold of one chunk of K sweeps into per-lane pairs for its 4 columns, from
+// nothing: exact max over the K values of each column slot, then their shifted
+// sum in sweep order.  The owner folds its registers (blk_fold_fresh); a
+// helper re-reads the chunk from x, one sweep at a time (blk_fold_fresh_mem):
+// the same arithmetic in the same order, so both produce the same bits.
+template <int K>
+__device__ __forceinline__ void blk_fold_fresh(const float (&q)[K][4], float (&m)[4],
+                                               float (&s)[4]) {
+  float c[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float bm = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < K; ++k) bm = fmaxf(bm, q[k][e]);
+    m[e] = bm;
+    c[e] = safe_shift(bm);
+    s[e] = 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] += exp_base2(q[k][e] - c[e]);
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void blk_fold_fresh_mem(const float *xb, int64_t j, int64_t f, int w,
+                                                   bool act, float (&m)[4], float (&s)[4]) {
+  const float ninf = -__builtin_inff();
+  float bm[4] = {ninf, ninf, ninf, ninf};
+  if (act) {
+#pragma unroll 1
+    for (int k = 0; k < K; ++k) {
+      float v[4];
+      blk_load4<false>(xb, j + (int64_t)k * w, f, ninf, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bm[e] = fmaxf(bm[e], v[e]);
+    }
+  }
+  float c[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m[e] = bm[e];
+    c[e] = safe_shift(bm[e]);
+    s[e] = 0.0f;
+  }
+#pragma unroll 1
+  for (int k = 0; k < K; ++k) {
+    float v[4] = {ninf, ninf, ninf, ninf};
+    if (act) blk_load4<false>(xb, j + (int64_t)k * w, f, ninf, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] += exp_base2(v[e] - c[e]);
+  }
+}
+
+// The chunk's (M, S) per column into res[0..inner) (through part and the
+// column merge; trailing barrier included).
+__device__ __forceinline__ void blk_chunk_columns(const float (&m)[4], const float (&s)[4],
+                                                  float2 *part, float2 *res, int inner,
+                                                  const BlkSweep &sw, int t) {
+  if (t < sw.act) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[4 * t + e] = make_float2(m[e], s[e]);
+  }
+  __syncthreads();
+  blk_merge_cols(part, res, inner, sw.w / inner, t);
+  __syncthreads();
+}
+
+// Wave 0 polls until all k slots are non-zero (true), or the poll limit or
+// the time threshold (50 us of the 100 MHz real-time counter; a real wait is
+// a few microseconds) runs out (false).
+__device__ __forceinline__ bool blk_wait_slots(const uint64_t *slots, int64_t k, uint32_t limit) {
+  const int lane = threadIdx.x % kWave;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (uint32_t it = 0;; ++it) {
+    bool missing = false;
+    for (int64_t j = lane; j < k; j += kWave) missing |= (load_pair_agent(slots + j) == 0);
+    if (__builtin_amdgcn_ballot_w64(missing) == 0) return true;
+    if (it >= limit || __builtin_amdgcn_s_memrealtime() - t0 > 5000ull) return false;
+    __builtin_amdgcn_s_sleep(LSE_BLK_SLEEP);
+  }
+}
+
+// log_softmax with the values in registers.  Workgroup (o, c) of an
+// (outer, chunks) grid, chunk fastest, holds floats f0 + 4 t + k w (k < K) of
+// chunk c (rc = K w / inner planes, a whole number of periods).
+//   !SPLIT (chunks = 1): the block's (M, S) per column come from this
+//     workgroup alone.
+//   SPLIT: slots[(o chunks + c) inner + col] receive the chunk's packed
+//     (m, s) (zeroed beforehand); the workgroup waits for the block's other
+//     chunks (or computes the missing ones itself), merges the block's pairs
+//     per column in chunk order, and writes.  spin_limit 0 is a test mode in
+//     which owners publish nothing, so every pair comes from a helper.
+template <int K, bool SPLIT>
+__global__ __launch_bounds__(kBlkThreads)
+#if LSE_BLK_RES_WPE
+__attribute__((amdgpu_waves_per_eu(LSE_BLK_RES_WPE)))
+#endif
+void axis_block_resident_kernel(
+    const float *__restrict__ x, float *__restrict__ y, AxisDims d, int64_t chunks, int64_t rc,
+    uint64_t *__restrict__ slots, uint32_t spin_limit) {
+  __shared__ float2 part[4 * kBlkThreads];
+  __shared__ float2 res[kBlkMaxInner];
+  __shared__ int s_state;
+  const int t = threadIdx.x;
+  const int64_t b = blockIdx.x;
+  const int64_t c = b % chunks;
+  const int64_t o = b / chunks;
+  const int inner = (int)d.inner;
+  const BlkSweep sw = blk_sweep(inner);
+  const int64_t r0 = c * rc;
+  const int64_t r1 = (d.R - r0 < rc) ? d.R : r0 + rc;
+  const int64_t f0 = r0 * inner, f1 = r1 * inner;
+  const float *xb = x + o * d.xso;
+  const float ninf = -__builtin_inff();
+  const bool act = t < sw.act;
+  float q[K][4];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (act) {
+      blk_load4<true>(xb, f0 + 4 * t + (int64_t)k * sw.w, f1, ninf, q[k]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[k][e] = ninf;
+    }
+  }
+  float m[4], s[4];
+  blk_fold_fresh<K>(q, m, s);
+  blk_chunk_columns(m, s, part, res, inner, sw, t);
+  if constexpr (SPLIT) {
+    uint64_t *bs = slots + o * chunks * inner;
+    if (t < inner && spin_limit != 0)
+      publish_pair_once(bs + c * inner + t, pack_pair(res[t].x, res[t].y));
+    for (;;) {
+      if (t < kWave) {
+        const bool all = blk_wait_slots(bs, chunks * inner, spin_limit);
+        if (t == 0) s_state = all ? 1 : 0;
+      }
+      __syncthreads();
+      if (s_state == 1) break;  // uniform: every thread read the same LDS word
+      // Help: recompute each sibling chunk with a missing slot from x.
+      for (int64_t j = 0; j < chunks; ++j) {
+        __syncthreads();
+        if (t == 0) s_state = 0;
+        __syncthreads();
+        if (t < inner && load_pair_agent(bs + j * inner + t) == 0) s_state = 2;
+        __syncthreads();
+        if (s_state != 2) continue;  // uniform, as above
+        const int64_t hr0 = j * rc;
+        const int64_t hf1 = ((d.R - hr0 < rc) ? d.R : hr0 + rc) * inner;
+        const int64_t hj = hr0 * inner + 4 * t;
+        float hm[4], hs[4];
+        blk_fold_fresh_mem<K>(xb, hj, hf1, sw.w, act, hm, hs);
+        blk_chunk_columns(hm, hs, part, res, inner, sw, t);
+        if (t < inner) publish_pair_once(bs + j * inner + t, pack_pair(res[t].x, res[t].y));
+      }
+      __syncthreads();
+    }
+    if (t < inner) {
+      float M = -__builtin_inff();
+      for (int64_t j = 0; j < chunks; ++j) M = fmaxf(M, pair_m(load_pair_agent(bs + j * inner + t)));
+      float S = 0.0f;
+      for (int64_t j = 0; j < chunks; ++j) {
+        const uint64_t p = load_pair_agent(bs + j * inner + t);
+        S += fold_weighted(pair_m(p), pair_s(p), M);
+      }
+      res[t] = make_float2(M, logf(S));
+    }
+  } else if (t < inner) {
+    res[t] = make_float2(res[t].x, logf(res[t].y));
+  }
+  __syncthreads();
+  if (!act) return;
+  float fm[4], fl[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float2 v = res[(4 * (t % sw.lp) + e) % inner];
+    fm[e] = v.x;
+    fl[e] = v.y;
+  }
+  float *yb = y + o * d.yso;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int64_t jj = f0 + 4 * t + (int64_t)k * sw.w;
+    if (jj < f1) {
+      float r[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = (q[k][e] - fm[e]) - fl[e];
+      if (jj + 4 <= f1) {
+        __builtin_nontemporal_store(v4b4{r[0], r[1], r[2], r[3]}, reinterpret_cast<v4b4 *>(yb + jj));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 3; ++e)
+          if (jj + e < f1) __builtin_nontemporal_store(r[e], yb + jj + e);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void blk_clear_kernel(uint64_t *__restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0;
+}
+
 struct BlkPlan {
   int64_t chunks, rc;
-  int mode;
+  int mode, k;
 };
+
+enum BlkLaunch { kLaunchFold = 0, kLaunchResident = 1, kLaunchResidentSplit = 2 };
+
+// Workgroups of one launch: the dispatch's work-item count must fit 32 bits.
+constexpr int64_t kMaxBlkGroups = 0xffffffffLL / kBlkThreads;
 
 // The block plan of a call, or false when the call keeps the other axis
 // kernels.  with_ws: the caller can supply blocks_workspace_bytes().
@@ -312,6 +556,39 @@ bool blk_plan(const AxisDims &d, bool lsm, bool with_ws, BlkPlan &p) {
   if (d.xsr != d.inner || (lsm && d.ysr != d.inner)) return false;
   if (d.R * d.inner > (int64_t(1) << 40)) return false;
   const BlkSweep sw = blk_sweep((int)d.inner);
+  const int64_t n = d.R * d.inner;
+  p.k = 0;
+  if (lsm && LSE_BLK_RESIDENT) {
+    // one workgroup per block, held in registers
+    for (int k = 4; k <= kBlkResK; k *= 2) {
+      if (n <= (int64_t)k * sw.w && d.outer <= kMaxBlkGroups) {
+        p.chunks = 1;
+        p.rc = d.R;
+        p.k = k;
+        p.mode = kLaunchResident;
+        return true;
+      }
+    }
+    // chunks of at most kBlkResK sweeps, of near-equal whole periods, that
+    // wait for each other; only on grids of several workgroups per slot
+    // (with about one, loading and waiting do not overlap across workgroups)
+    if (with_ws) {
+      const int64_t per = (int64_t)sw.lp * 4 / d.inner;  // planes per period
+      const int64_t rc_max = (int64_t)kBlkResK * sw.w / d.inner;
+      int64_t chunks = (d.R + rc_max - 1) / rc_max;
+      int64_t rc = (d.R + chunks - 1) / chunks;
+      rc = (rc + per - 1) / per * per;
+      chunks = (d.R + rc - 1) / rc;
+      if (chunks <= LSE_BLK_RES_MAX_CHUNKS && d.outer * chunks >= LSE_BLK_RES_MIN_GROUPS &&
+          d.outer * chunks <= kMaxBlkGroups) {
+        p.chunks = chunks;
+        p.rc = rc;
+        p.k = kBlkResK;
+        p.mode = kLaunchResidentSplit;
+        return true;
+      }
+    }
+  }
   // chunks of whole periods (4 planes) and at least LSE_BLK_MIN_TRIPS trips
   const int64_t trip = (int64_t)sw.w * kBlkU;
   int64_t min_planes = (LSE_BLK_MIN_TRIPS * trip + d.inner - 1) / d.inner;
@@ -328,8 +605,8 @@ bool blk_plan(const AxisDims &d, bool lsm, bool with_ws, BlkPlan &p) {
   }
   p.rc = ((d.R + p.chunks - 1) / p.chunks + 3) / 4 * 4;
   p.chunks = (d.R + p.rc - 1) / p.rc;
-  if (d.outer * p.chunks > 0x7fffffffLL) return false;
-  p.mode = p.chunks > 1 ? (lsm ? kBlkPartialKeep : kBlkPartial) : (lsm ? kBlkLsm : kBlkLse);
+  if (d.outer * p.chunks > kMaxBlkGroups) return false;
+  p.mode = kLaunchFold;
   return true;
 }
 
@@ -356,6 +633,7 @@ bool blk_wanted(const AxisDims &d, bool lsm, bool with_ws, const float *x, const
 }
 
 size_t blk_ws_bytes(const AxisDims &d, const BlkPlan &p) {
+  // fold: a float2 pair per column and chunk; resident split: a packed pair
   return p.chunks > 1 ? (size_t)(d.outer * d.inner * p.chunks * 8) : 0;
 }
 
@@ -373,24 +651,51 @@ bool launch_blocks(const float *x, float *out, const AxisDims &d, bool lsm, bool
   if (p.chunks > 1 && ws == nullptr) return false;
   const dim3 grid((uint32_t)(d.outer * p.chunks));
   const dim3 block(kBlkThreads);
+  if (p.mode == kLaunchResident) {
+    switch (p.k) {
+      case 4:
+        hipLaunchKernelGGL((axis_block_resident_kernel<4, false>), grid, block, 0, stream, x, out,
+                           d, p.chunks, p.rc, nullptr, 0u);
+        break;
+      case 8:
+        hipLaunchKernelGGL((axis_block_resident_kernel<8, false>), grid, block, 0, stream, x, out,
+                           d, p.chunks, p.rc, nullptr, 0u);
+        break;
+      default:
+        hipLaunchKernelGGL((axis_block_resident_kernel<kBlkResK, false>), grid, block, 0, stream,
+                           x, out, d, p.chunks, p.rc, nullptr, 0u);
+        break;
+    }
+    e = hipGetLastError();
+    return true;
+  }
+  if (p.mode == kLaunchResidentSplit) {
+    auto *slots = reinterpret_cast<uint64_t *>(ws);
+    const int64_t words = d.outer * p.chunks * d.inner;
+    const int64_t cb = (words + 255) / 256;
+    hipLaunchKernelGGL(blk_clear_kernel, dim3((uint32_t)(cb < 4096 ? cb : 4096)), dim3(256), 0,
+                       stream, slots, words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return true;
+    hipLaunchKernelGGL((axis_block_resident_kernel<kBlkResK, true>), grid, block, 0, stream, x,
+                       out, d, p.chunks, p.rc, slots, chain_spin_limit());
+    e = hipGetLastError();
+    return true;
+  }
   auto *pairs = reinterpret_cast<float2 *>(ws);
-  switch (p.mode) {
-    case kBlkPartial:
-      hipLaunchKernelGGL((axis_block_kernel<kBlkPartial>), grid, block, 0, stream, x, out, d,
-                         p.chunks, p.rc, pairs);
-      break;
-    case kBlkPartialKeep:
+  if (p.chunks > 1) {
+    if (lsm)
       hipLaunchKernelGGL((axis_block_kernel<kBlkPartialKeep>), grid, block, 0, stream, x, out, d,
                          p.chunks, p.rc, pairs);
-      break;
-    case kBlkLse:
-      hipLaunchKernelGGL((axis_block_kernel<kBlkLse>), grid, block, 0, stream, x, out, d, p.chunks,
-                         p.rc, pairs);
-      break;
-    default:
-      hipLaunchKernelGGL((axis_block_kernel<kBlkLsm>), grid, block, 0, stream, x, out, d, p.chunks,
-                         p.rc, pairs);
-      break;
+    else
+      hipLaunchKernelGGL((axis_block_kernel<kBlkPartial>), grid, block, 0, stream, x, out, d,
+                         p.chunks, p.rc, pairs);
+  } else if (lsm) {
+    hipLaunchKernelGGL((axis_block_kernel<kBlkLsm>), grid, block, 0, stream, x, out, d, p.chunks,
+                       p.rc, pairs);
+  } else {
+    hipLaunchKernelGGL((axis_block_kernel<kBlkLse>), grid, block, 0, stream, x, out, d, p.chunks,
+                       p.rc, pairs);
   }
   e = hipGetLastError();
   if (e != hipSuccess || p.chunks == 1) return true;

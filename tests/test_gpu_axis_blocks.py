@@ -128,3 +128,21 @@ def test_blocks_bit_identical_reruns():
         b, yb = L.lse_reduce_axis(x, 1), L.log_softmax_axis(x, 1)
         torch.cuda.synchronize()
         assert torch.equal(a, b) and torch.equal(ya, yb)
+
+
+@pytest.mark.parametrize("outer,R,inner", [(1100, 1000, 49), (2100, 4003, 5), (700, 701, 127)])
+def test_blocks_resident_helping_bit_identical(orc, outer, R, inner):
+    """log_softmax over blocks split into chunks that wait for each other (at
+    least 4096 workgroups; ragged last chunks): at a poll limit of 0 no owner
+    publishes, so every chunk's pairs come from the helping path (re-read from
+    x); the result must equal the default run bit for bit, and the oracle."""
+    x = inputs.normal((outer, R, inner), seed=outer + R + inner, sigma=3.0, device=DEV)
+    y = L.log_softmax_axis(x, 1).clone()
+    try:
+        L.lse_testing_set_spin_limit(0)
+        yh = L.log_softmax_axis(x, 1)
+        torch.cuda.synchronize()
+    finally:
+        L.lse_testing_set_spin_limit(1 << 24)
+    assert torch.equal(y, yh)
+    compare(yh.cpu().numpy(), orc.log_softmax_axis(x.cpu().numpy()), what=f"helped {outer}x{R}x{inner}")
