@@ -142,6 +142,28 @@ def test_graph_split_axis_and_long_rows():
     _check_graph(run, [o1, o2, y2, o3, y4])
 
 
+def test_graph_contiguous_blocks():
+    """Contiguous blocks of short runs: chunk pairs then a merge (logsumexp),
+    register-resident chunks that wait for each other after a clear kernel
+    (log_softmax over 4400 chunk workgroups), a block per workgroup held in
+    registers, workspaces passed in (no allocation inside the capture)."""
+    x = inputs.normal((40, 4000, 49), seed=14, device=DEV)
+    o = torch.empty((40, 49), device=DEV)
+    wso = torch.empty(max(1, L.lse_axis_workspace_bytes(40, 4000, 49)), dtype=torch.uint8, device=DEV)
+    x2 = inputs.normal((1100, 1000, 49), seed=15, device=DEV)
+    y2 = torch.empty_like(x2)
+    ws2 = torch.empty(L.lse_axis_workspace_bytes(1100, 1000, 49, True), dtype=torch.uint8,
+                      device=DEV)
+    x3 = inputs.normal((3000, 100, 49), seed=16, device=DEV)
+    y3 = torch.empty_like(x3)
+
+    def run():
+        L.lse_reduce_axis(x, 1, o, ws=wso)
+        L.log_softmax_axis(x2, 1, y2, ws=ws2)
+        L.log_softmax_axis(x3, 1, y3)
+    _check_graph(run, [o, y2, y3])
+
+
 def test_concurrent_streams_match_sequential():
     """Calls on two streams at once, each with its own workspace, give the
     sequential results bit for bit: no state is shared between calls."""
