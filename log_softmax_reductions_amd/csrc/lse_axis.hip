@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "lse_device.hpp"
+#include "lse_fold.hpp"
 #include "lse_internal.hpp"
 
 namespace lse {
@@ -281,11 +282,12 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
   const int64_t R = d.R;
   int skip = 0;
   const int64_t j0 = UA ? ua_columns(d, q, skip) : q * W;
-  float m[W], s[W];
+  float m[W], s[W], comp[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) {
     m[w] = -__builtin_inff();
     s[w] = 0.0f;
+    comp[w] = 0.0f;
   }
   if constexpr (OFF32) {
     static_assert(W == 4, "scalar-base loads are 128-bit");
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
       load_block_s<RB, LSE_AXIS0_NT_LOAD != 0, UA>(x + r0 * st_xsr, st_xsr,
                                                    (R - r0 < RB) ? (R - r0) : RB, off, v);
 #pragma unroll
-      for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
+      for (int w = 0; w < W; ++w) fold_block_c<RB>(v[w], m[w], s[w], comp[w]);
     }
   } else {
     const float *xo = x + o * st_xso + j0;
@@ -304,12 +306,12 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
       load_block<RB, W, LSE_AXIS0_NT_LOAD != 0, UA>(xo + r0 * st_xsr, st_xsr,
                                                     (R - r0 < RB) ? (R - r0) : RB, v);
 #pragma unroll
-      for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
+      for (int w = 0; w < W; ++w) fold_block_c<RB>(v[w], m[w], s[w], comp[w]);
     }
   }
   float r[W];
 #pragma unroll
-  for (int w = 0; w < W; ++w) r[w] = m[w] + logf(s[w]);
+  for (int w = 0; w < W; ++w) r[w] = m[w] + logf(fold_total(s[w], comp[w]));
   if constexpr (UA)
     store4_ua(out + o * st_yso + j0, r, skip);
   else
@@ -566,11 +568,16 @@ __global__ __launch_bounds__(kMaxAxisThreads) void log_softmax_axis_kernel(
 #pragma unroll
     for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
   } else {
+    float comp[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) comp[w] = 0.0f;
     for (int64_t r0 = 0; r0 < R; r0 += RB) {
       load(r0, (R - r0 < RB) ? (R - r0) : RB, v);
 #pragma unroll
-      for (int w = 0; w < W; ++w) fold_block<RB>(v[w], m[w], s[w]);
+      for (int w = 0; w < W; ++w) fold_block_c<RB>(v[w], m[w], s[w], comp[w]);
     }
+#pragma unroll
+    for (int w = 0; w < W; ++w) s[w] = fold_total(s[w], comp[w]);
   }
   float lns[W];
 #pragma unroll
@@ -669,6 +676,9 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
   }
   float v[W][RBW];
   const bool resident = per <= RBW;  // uniform
+  float comp[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) comp[w] = 0.0f;
   for (int64_t b = 0; b < nr; b += RBW) {
     const int64_t nb = valid ? ((nr - b < RBW) ? (nr - b) : RBW) : 0;
     if constexpr (OFF32)
@@ -676,8 +686,10 @@ __global__ __launch_bounds__(kWave * P * G) void axis_split_kernel(
     else
       load_block<RBW, W, kSplitNt, UA>(xs + b * st_xsr, st_xsr, nb, v);
 #pragma unroll
-    for (int w = 0; w < W; ++w) fold_block<RBW>(v[w], m[w], s[w]);
+    for (int w = 0; w < W; ++w) fold_block_c<RBW>(v[w], m[w], s[w], comp[w]);
   }
+#pragma unroll
+  for (int w = 0; w < W; ++w) s[w] = fold_total(s[w], comp[w]);
 #pragma unroll
   for (int w = 0; w < W; ++w) {
     lds_m[grp][wv][w][lane] = m[w];

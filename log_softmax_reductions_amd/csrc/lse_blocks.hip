@@ -21,7 +21,8 @@
 //     workgroup each, whose (m, s) pairs per column are merged afterwards in
 //     chunk order (a merge launch for logsumexp; for log_softmax each
 //     workgroup of the apply launch merges its block's pairs itself, the same
-//     way, and writes (x - M) - log S over its chunk).  Without one, one
+//     way, and writes (x - M) - log S over its chunk; past 8 chunks a merge
+//     launch with a wave per column does it for both).  Without one, one
 //     workgroup takes a whole block, and log_softmax reads it again;
 //   * log_softmax keeps its values in registers where they fit (the split-row
 //     protocol of log_softmax_rows, per column): a block of up to 16 sweeps
@@ -35,6 +36,7 @@
 //     never depends on dispatch order and the results not on who computed a
 //     pair.
 #include "lse_device.hpp"
+#include "lse_fold.hpp"
 #include "lse_internal.hpp"
 
 namespace lse {
@@ -47,7 +49,10 @@ namespace {
 #define LSE_BLK_TARGET_GROUPS 1024 // workgroups the chunking aims for
 #endif
 #ifndef LSE_BLK_MAX_CHUNKS
-#define LSE_BLK_MAX_CHUNKS 64      // chunks per block at most (their pairs are merged serially)
+#define LSE_BLK_MAX_CHUNKS 4096    // chunks per block at most
+#endif
+#ifndef LSE_BLK_SERIAL_CHUNKS
+#define LSE_BLK_SERIAL_CHUNKS 8    // up to this many, one thread per column merges them
 #endif
 #ifndef LSE_BLK_U
 #define LSE_BLK_U 4                // 16-byte loads per lane in flight
@@ -63,9 +68,6 @@ namespace {
 #endif
 #ifndef LSE_BLK_MIN_BLOCK
 #define LSE_BLK_MIN_BLOCK 2048     // gate 1: blocks of at least this many floats,
-#endif
-#ifndef LSE_BLK_MIN_OUTER
-#define LSE_BLK_MIN_OUTER 32       // ... at least this many of them,
 #endif
 #ifndef LSE_BLK_GATE_INNER
 #define LSE_BLK_GATE_INNER 128     // ... inner runs up to this wide,
@@ -229,11 +231,12 @@ __global__ __launch_bounds__(kBlkThreads) void axis_block_kernel(const float *__
   const int64_t f0 = r0 * inner, f1 = r1 * inner;
   const float *xb = x + o * d.xso;
   const float ninf = -__builtin_inff();
-  float m[4], s[4];
+  float m[4], s[4], comp[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     m[e] = ninf;
     s[e] = 0.0f;
+    comp[e] = 0.0f;
   }
   if (t < sw.act) {
     for (int64_t j = f0 + 4 * t; j < f1; j += (int64_t)sw.w * kBlkU) {
@@ -245,11 +248,11 @@ __global__ __launch_bounds__(kBlkThreads) void axis_block_kernel(const float *__
         float v[kBlkU];
 #pragma unroll
         for (int u = 0; u < kBlkU; ++u) v[u] = q[u][e];
-        fold_block<kBlkU>(v, m[e], s[e]);
+        fold_block_c<kBlkU>(v, m[e], s[e], comp[e]);
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) part[4 * t + e] = make_float2(m[e], s[e]);
+    for (int e = 0; e < 4; ++e) part[4 * t + e] = make_float2(m[e], fold_total(s[e], comp[e]));
   }
   __syncthreads();
   blk_merge_cols(part, res, inner, sw.w / inner, t);
@@ -292,11 +295,50 @@ __global__ __launch_bounds__(256) void axis_block_merge_kernel(const float2 *__r
   out[o * d.yso + col] = f.x + logf(f.y);
 }
 
+// The same merge for long chunk lists: a wave per (o, col), lane l folding
+// chunks l, l + 64, ... (4 loads in flight) into a running pair, then the
+// lanes' pairs reduced across the wave (the same order on every call).
+// LSM: fin[o inner + col] = (M, log S) for the apply launch; else the
+// logsumexp into out.
+template <bool LSM>
+__global__ __launch_bounds__(256) void axis_block_merge_wide_kernel(
+    const float2 *__restrict__ pairs, float *__restrict__ out, float2 *__restrict__ fin,
+    AxisDims d, int64_t chunks) {
+  const int64_t i = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;  // (o, col)
+  const int lane = threadIdx.x % kWave;
+  if (i >= d.outer * d.inner) return;  // whole waves
+  const float2 *p = pairs + i * chunks;
+  float m = -__builtin_inff(), s = 0.0f;
+  for (int64_t k0 = lane; k0 < chunks; k0 += 4 * kWave) {
+    float2 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      q[u] = (k0 + u * kWave < chunks) ? p[k0 + u * kWave] : make_float2(-__builtin_inff(), 0.0f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float mn = fmaxf(m, q[u].x);
+      s = fold_weighted(m, s, mn) + fold_weighted(q[u].x, q[u].y, mn);
+      m = mn;
+    }
+  }
+  const float M = wave_allreduce(m, OpMax{});
+  const float S = wave_allreduce(fold_weighted(m, s, M), OpSum{});
+  if (lane == 0) {
+    if constexpr (LSM) {
+      fin[i] = make_float2(M, logf(S));
+    } else {
+      const int64_t o = i / d.inner;
+      out[o * d.yso + (i - o * d.inner)] = M + logf(S);
+    }
+  }
+}
+
 // log_softmax over chunk c of block o (the pair launch's grid): the block's
-// chunk pairs are merged first (the order of the merge kernel), then written.
+// chunk pairs are merged first (the order of the merge kernel), or read
+// merged from fin, then written.
 __global__ __launch_bounds__(kBlkThreads) void axis_block_apply_kernel(
     const float *__restrict__ x, float *__restrict__ y, AxisDims d, int64_t chunks, int64_t rc,
-    const float2 *__restrict__ pairs) {
+    const float2 *__restrict__ pairs, const float2 *__restrict__ fin) {
   __shared__ float2 tab[kBlkMaxInner];
   const int t = threadIdx.x;
   const int64_t b = blockIdx.x;
@@ -305,8 +347,12 @@ __global__ __launch_bounds__(kBlkThreads) void axis_block_apply_kernel(
   const int inner = (int)d.inner;
   const BlkSweep sw = blk_sweep(inner);
   if (t < inner) {
-    const float2 f = blk_merge_pairs(pairs + (o * inner + t) * chunks, chunks);
-    tab[t] = make_float2(f.x, logf(f.y));
+    if (fin != nullptr) {  // merged by axis_block_merge_wide_kernel
+      tab[t] = fin[o * inner + t];
+    } else {
+      const float2 f = blk_merge_pairs(pairs + (o * inner + t) * chunks, chunks);
+      tab[t] = make_float2(f.x, logf(f.y));
+    }
   }
   __syncthreads();
   if (t >= sw.act) return;
@@ -613,8 +659,7 @@ bool blk_plan(const AxisDims &d, bool lsm, bool with_ws, BlkPlan &p) {
 // Which calls take the blocks (measured against the axis kernels, the column
 // split and the plane split on the same shapes): blocks of at least
 // LSE_BLK_MIN_BLOCK floats (smaller ones leave most of a sweep's lanes idle
-// and make workgroups too short) and at least LSE_BLK_MIN_OUTER of them (a
-// few long blocks split into more chunks in the column split); then inner
+// and make workgroups too short), any number of them; then inner
 // runs up to LSE_BLK_GATE_INNER, with a workspace only off the 16-byte grid
 // (on it the axis kernels and the column split were about as fast), except
 // logsumexp over blocks of LSE_BLK_BIG_BLOCK floats or more, which the
@@ -623,7 +668,7 @@ bool blk_plan(const AxisDims &d, bool lsm, bool with_ws, BlkPlan &p) {
 bool blk_wanted(const AxisDims &d, bool lsm, bool with_ws, const float *x, const float *out) {
   if (LSE_BLK_GATE == 2) return true;
   const int64_t n = d.R * d.inner;
-  if (n < LSE_BLK_MIN_BLOCK || d.outer < LSE_BLK_MIN_OUTER) return false;
+  if (n < LSE_BLK_MIN_BLOCK) return false;
   const bool big_lse = !lsm && n >= LSE_BLK_BIG_BLOCK;
   if (d.inner > LSE_BLK_GATE_INNER) return big_lse;
   const uintptr_t a = (uintptr_t)x | (lsm ? (uintptr_t)out : 0);
@@ -632,16 +677,21 @@ bool blk_wanted(const AxisDims &d, bool lsm, bool with_ws, const float *x, const
   return !grid16 || !with_ws || big_lse;
 }
 
-size_t blk_ws_bytes(const AxisDims &d, const BlkPlan &p) {
-  // fold: a float2 pair per column and chunk; resident split: a packed pair
-  return p.chunks > 1 ? (size_t)(d.outer * d.inner * p.chunks * 8) : 0;
+size_t blk_ws_bytes(const AxisDims &d, const BlkPlan &p, bool lsm) {
+  // fold: a float2 pair per column and chunk (and, merged by a wave per
+  // column, a float2 (M, log S) per column for log_softmax); resident split:
+  // a packed pair per column and chunk
+  if (p.chunks <= 1) return 0;
+  const size_t cols = (size_t)(d.outer * d.inner);
+  const bool fin = lsm && p.mode == kLaunchFold && p.chunks > LSE_BLK_SERIAL_CHUNKS;
+  return cols * (size_t)p.chunks * 8 + (fin ? cols * 8 : 0);
 }
 
 }  // namespace
 
 size_t blocks_workspace_bytes(const AxisDims &d, bool lsm) {
   BlkPlan p;
-  return blk_plan(d, lsm, true, p) ? blk_ws_bytes(d, p) : 0;
+  return blk_plan(d, lsm, true, p) ? blk_ws_bytes(d, p, lsm) : 0;
 }
 
 bool launch_blocks(const float *x, float *out, const AxisDims &d, bool lsm, bool with_ws,
@@ -699,14 +749,28 @@ bool launch_blocks(const float *x, float *out, const AxisDims &d, bool lsm, bool
   }
   e = hipGetLastError();
   if (e != hipSuccess || p.chunks == 1) return true;
-  if (!lsm) {
-    const int64_t cols = d.outer * d.inner;
+  const int64_t cols = d.outer * d.inner;
+  float2 *fin = nullptr;
+  if (p.chunks > LSE_BLK_SERIAL_CHUNKS) {  // a wave per column
+    const dim3 mgrid((uint32_t)((cols + 3) / 4));
+    if (lsm) {
+      fin = pairs + cols * p.chunks;
+      hipLaunchKernelGGL((axis_block_merge_wide_kernel<true>), mgrid, dim3(256), 0, stream, pairs,
+                         out, fin, d, p.chunks);
+    } else {
+      hipLaunchKernelGGL((axis_block_merge_wide_kernel<false>), mgrid, dim3(256), 0, stream, pairs,
+                         out, fin, d, p.chunks);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess || !lsm) return true;
+  } else if (!lsm) {
     hipLaunchKernelGGL(axis_block_merge_kernel, dim3((uint32_t)((cols + 255) / 256)), dim3(256), 0,
                        stream, pairs, out, d, p.chunks);
-  } else {
-    hipLaunchKernelGGL(axis_block_apply_kernel, grid, block, 0, stream, x, out, d, p.chunks, p.rc,
-                       pairs);
+    e = hipGetLastError();
+    return true;
   }
+  hipLaunchKernelGGL(axis_block_apply_kernel, grid, block, 0, stream, x, out, d, p.chunks, p.rc,
+                     pairs, fin);
   e = hipGetLastError();
   return true;
 }

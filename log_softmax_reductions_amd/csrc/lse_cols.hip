@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "lse_device.hpp"
+#include "lse_fold.hpp"
 #include "lse_internal.hpp"
 
 namespace lse {
@@ -246,11 +247,12 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
   // log_softmax reads its planes again: keep them cached
   constexpr bool kNt = MODE != kColsLsm && MODE != kColsPartialKeep;
   constexpr bool kPartial = MODE == kColsPartial || MODE == kColsPartialKeep;
-  float m[4], s[4];
+  float m[4], s[4], comp[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     m[e] = -__builtin_inff();
     s[e] = 0.0f;
+    comp[e] = 0.0f;
   }
   for (int64_t r = r0 + g; r < r1; r += kStep * kColsU) {
     float v[4][kColsU];
@@ -268,10 +270,13 @@ __global__ __launch_bounds__(kColsThreads) void axis_cols_kernel(
       for (int e = 0; e < 4; ++e) v[e][u] = q[e];
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) fold_block<kColsU>(v[e], m[e], s[e]);
+    for (int e = 0; e < 4; ++e) fold_block_c<kColsU>(v[e], m[e], s[e], comp[e]);
   }
 #pragma unroll
-  for (int e = 0; e < 4; ++e) merge_lanes<LPP>(m[e], s[e]);
+  for (int e = 0; e < 4; ++e) {
+    s[e] = fold_total(s[e], comp[e]);
+    merge_lanes<LPP>(m[e], s[e]);
+  }
   if (lane < LPP) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) lds_pair[wave][tile_col<LPP, LAY>(cl, e)] = make_float2(m[e], s[e]);

@@ -34,7 +34,9 @@ BLOCK_SHAPES = [(40, 4000, 49), (33, 5001, 5), (64, 2000, 3), (48, 3001, 13), (3
                 (100, 900, 63), (36, 1000, 127), (40, 400, 100), (50, 2500, 6), (1100, 100, 49),
                 (1500, 41, 50), (1024, 199, 7), (1200, 30, 86), (3000, 1000, 5), (700, 500, 2),
                 # logsumexp over large blocks of wider runs (one partial per lane and column)
-                (40, 600, 196), (36, 520, 255), (33, 300, 256)]
+                (40, 600, 196), (36, 520, 255), (33, 300, 256),
+                # few long blocks: hundreds of chunks per block, merged by a wave per column
+                (1, 300000, 49), (3, 100003, 7), (2, 200000, 6), (1, 150001, 100)]
 
 
 @pytest.mark.parametrize("outer,R,inner", BLOCK_SHAPES)

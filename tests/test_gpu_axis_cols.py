@@ -191,3 +191,18 @@ def test_lse_last_axis_split_rows(orc, rows, cols):
     torch.cuda.synchronize()
     compare(out.cpu().numpy(), orc.lse_axis(x.cpu().numpy().reshape(rows, cols, 1)).reshape(rows),
             what=f"lse split rows {rows}x{cols}")
+
+
+@pytest.mark.parametrize("outer,R,inner,lsm", [(1, 1048576, 64, False), (16, 65536, 64, False),
+                                               (1, 300000, 49, True), (1, 100000, 1000, False)])
+def test_long_streams_within_tolerance(orc, outer, R, inner, lsm):
+    """The entry points without a workspace fold hundreds of thousands of
+    planes per lane into one running sum: small terms must not be rounded
+    away against it (the plain running sum ran 1.9 x over the tolerance on
+    (1, 1048576, 64))."""
+    x = inputs.normal((outer, R, inner), seed=R + inner, sigma=3.0, device=DEV)
+    got = _raw_axis(x, R, inner, lsm)
+    torch.cuda.synchronize()
+    xc = x.cpu().numpy()
+    ref = orc.log_softmax_axis(xc) if lsm else orc.lse_axis(xc)
+    compare(got.cpu().numpy(), ref, what=f"long stream {outer}x{R}x{inner} lsm={lsm}")
