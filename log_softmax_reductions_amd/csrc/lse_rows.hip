@@ -372,7 +372,16 @@ __device__ __forceinline__ void stream_chunk_pair(const float *__restrict__ p, i
   m = block_allreduce<kNW>(lm, OpMax{}, red);
   float ls = 0.0f;
   if (is_finite(m)) {
-    for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) ls += exp_base2(p[i] - m);
+    // compensated: over thousands of terms per lane the small ones would be
+    // rounded away against the running sum
+    float lc = 0.0f;
+    for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) {
+      const float y = exp_base2(p[i] - m) - lc;
+      const float t = ls + y;
+      lc = (t - ls) - y;
+      ls = t;
+    }
+    ls -= lc;
   } else {
     for (int64_t i = threadIdx.x; i < len; i += kRowsThreads) ls += pair_term_general(p[i], m);
   }
@@ -653,27 +662,46 @@ __device__ __forceinline__ void stream_row_pair(const float *__restrict__ p, int
 // recurrence of the log_softmax page: a new maximum rescales the sum by
 // exp(m_old - m_new), then each value adds exp(v - m).  The same conventions
 // as chunk_pair: m is the largest non-NaN value, s counts +inf values when
-// m = +inf, is 0 while m = -inf, and becomes NaN with any NaN.
+// m = +inf, is 0 while m = -inf, and becomes NaN with any NaN.  Finite terms
+// join s with Kahan's compensation c (a lane may add millions of them, most
+// far below s, which plain addition would round away); total() is the
+// compensated sum.
 struct OnlinePair {
-  float m = -__builtin_inff(), s = 0.0f;
+  float m = -__builtin_inff(), s = 0.0f, c = 0.0f;
   __device__ __forceinline__ void rescale_to(float mn) {
     if (mn != m) {  // m < mn: exp(m - mn) is 0 when m = -inf or mn = +inf
-      s *= exp_base2(m - mn);
+      const float f = exp_base2(m - mn);
+      s *= f;
+      c *= f;
       m = mn;
     }
   }
-  __device__ __forceinline__ void add4(float a, float b, float c, float d) {
-    rescale_to(fmaxf(m, fmaxf(fmaxf(a, b), fmaxf(c, d))));
-    if (is_finite(m))
-      s += (exp_base2(a - m) + exp_base2(b - m)) + (exp_base2(c - m) + exp_base2(d - m));
-    else
+  __device__ __forceinline__ void add_finite(float g) {
+    const float y = g - c;
+    const float t = s + y;
+    c = is_finite(t) ? (t - s) - y : 0.0f;
+    s = t;
+  }
+  __device__ __forceinline__ void add4(float a, float b, float c4, float d) {
+    rescale_to(fmaxf(m, fmaxf(fmaxf(a, b), fmaxf(c4, d))));
+    if (is_finite(m)) {
+      add_finite((exp_base2(a - m) + exp_base2(b - m)) + (exp_base2(c4 - m) + exp_base2(d - m)));
+    } else {
       s += (pair_term_nonfinite(a, m) + pair_term_nonfinite(b, m)) +
-           (pair_term_nonfinite(c, m) + pair_term_nonfinite(d, m));
+           (pair_term_nonfinite(c4, m) + pair_term_nonfinite(d, m));
+      c = 0.0f;
+    }
   }
   __device__ __forceinline__ void add1(float a) {
     rescale_to(fmaxf(m, a));
-    s += is_finite(m) ? exp_base2(a - m) : pair_term_nonfinite(a, m);
+    if (is_finite(m)) {
+      add_finite(exp_base2(a - m));
+    } else {
+      s += pair_term_nonfinite(a, m);
+      c = 0.0f;
+    }
   }
+  __device__ __forceinline__ float total() const { return is_finite(s) ? s - c : s; }
 };
 
 // The pair of a whole row read once: each lane folds its strided values with
@@ -703,7 +731,7 @@ __device__ __forceinline__ void online_row_pair(const float *__restrict__ p, int
   }
   M = block_allreduce<kNW>(op.m, OpMax{}, red);
   const float w = (op.m == M) ? 1.0f : exp_base2(op.m - M);
-  S = block_allreduce<kNW>(op.s * w, OpSum{}, red);
+  S = block_allreduce<kNW>(op.total() * w, OpSum{}, red);
 }
 
 // ------------------------------------------------- MALL re-read variant
@@ -735,7 +763,7 @@ __device__ __forceinline__ void cached_chunk_pair(const float *__restrict__ p, i
   }
   M = block_allreduce<kNW>(op.m, OpMax{}, red);
   const float w = (op.m == M) ? 1.0f : exp_base2(op.m - M);
-  S = block_allreduce<kNW>(op.s * w, OpSum{}, red);
+  S = block_allreduce<kNW>(op.total() * w, OpSum{}, red);
 }
 
 template <bool SOFTMAX>

@@ -467,3 +467,30 @@ def test_rows_reread_variant(orc, rows, cols, softmax):
         compare(y.cpu().numpy(), orc.softmax_rows(xc), atol=1e-37, rtol=1e-5, what="reread sm")
     else:
         compare(y.cpu().numpy(), orc.log_softmax_rows(xc)[0], what="reread")
+
+
+@pytest.mark.parametrize("cols,off", [(50000003, 0), (40000000, 1)])
+def test_rows_long_streams_within_tolerance(orc, cols, off):
+    """Whole rows streamed by one workgroup (the axis entry points without a
+    workspace over a contiguous last axis): each lane adds ~100K terms, most
+    far below its running sum; the plain sum rounded them away (2.2 x the
+    tolerance for the logsumexp of (2, 50000003) at sigma 3, 3.6 x for its
+    log_softmax).  The logsumexp is checked against the oracle, log_softmax at
+    sampled columns against x - LSE in fp64."""
+    from log_softmax_reductions_amd import _lib
+    lib = _lib.load()
+    rows = 2
+    buf = inputs.normal((rows * cols + off,), seed=cols, sigma=3.0, device="cuda")
+    x = buf[off:].view(rows, cols)
+    st = torch.cuda.current_stream().cuda_stream
+    o = torch.empty(rows, device="cuda")
+    y = torch.empty_like(x)
+    _lib.check(lib.lse_reduce_axis(x.data_ptr(), o.data_ptr(), rows, cols, 1, st), "lse")
+    _lib.check(lib.log_softmax_axis(x.data_ptr(), y.data_ptr(), rows, cols, 1, st), "lsm")
+    torch.cuda.synchronize()
+    xc = x.cpu().numpy()
+    _, lse = orc.log_softmax_rows(xc, want_y=False)
+    compare(o.cpu().numpy(), lse, what=f"long row lse ({rows},{cols})+{off}")
+    idx = np.arange(0, cols, 997)
+    ref = xc[:, idx].astype(np.float64) - lse[:, None]
+    compare(y.cpu().numpy()[:, idx], ref, what=f"long row lsm ({rows},{cols})+{off}")
