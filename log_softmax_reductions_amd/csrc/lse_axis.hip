@@ -321,6 +321,9 @@ __global__ __launch_bounds__(kMaxAxisThreads) void lse_axis_kernel(
 #ifndef LSE_AXIS_WALK
 #define LSE_AXIS_WALK 1   // wide aligned logsumexp over many planes walks them (lse_axis_walk_kernel)
 #endif
+#ifndef LSE_AXIS_WALK_COMP
+#define LSE_AXIS_WALK_COMP 1   // the walk's column sums with Kahan compensation
+#endif
 #ifndef LSE_AXIS_WALK_VL
 #define LSE_AXIS_WALK_VL 4   // 16-byte loads per lane and plane
 #endif
@@ -426,22 +429,41 @@ __global__ __launch_bounds__(kWalkThreads) void lse_axis_walk_kernel(
       v[4 * k] = q.x; v[4 * k + 1] = q.y; v[4 * k + 2] = q.z; v[4 * k + 3] = q.w;
     }
   };
-  float va[NV], s[NV];
+  float va[NV], s[NV], cs[NV];
   load(va, xt);
   float lm = va[0];  // the lane's reference c
 #pragma unroll
   for (int i = 1; i < NV; ++i) lm = fmaxf(lm, va[i]);
 #pragma unroll
-  for (int i = 0; i < NV; ++i) s[i] = 0.0f;
+  for (int i = 0; i < NV; ++i) {
+    s[i] = 0.0f;
+    cs[i] = 0.0f;
+  }
+  // Each term joins its column's sum with Kahan's compensation cs: over
+  // thousands of planes most terms sit far below the sum and plain addition
+  // would round them away (0.78 of the tolerance at R = 8192, sigma 3).  A
+  // non-finite term makes the sum NaN here, which sends the lane to the
+  // exact redo below.
   auto acc = [&](const float (&v)[NV]) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) s[i] += exp_base2(v[i] - lm);
+    for (int i = 0; i < NV; ++i) {
+      if constexpr (LSE_AXIS_WALK_COMP) {
+        const float y = exp_base2(v[i] - lm) - cs[i];
+        const float t = s[i] + y;
+        cs[i] = (t - s[i]) - y;
+        s[i] = t;
+      } else {
+        s[i] += exp_base2(v[i] - lm);
+      }
+    }
   };
   acc(va);
   for (int64_t r = 1; r < R; ++r) {
     load(va, xt + r * st_xsr);
     acc(va);
   }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) s[i] -= cs[i];
   float lo = s[0], hi = s[0], tot = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
