@@ -79,7 +79,7 @@ namespace {
 #define LSE_BLK_RES_MAX_CHUNKS 32  // ... for blocks of at most this many 16-sweep chunks
 #endif
 #ifndef LSE_BLK_RES_MIN_GROUPS
-#define LSE_BLK_RES_MIN_GROUPS 4096 // ... and at least this many workgroups
+#define LSE_BLK_RES_MIN_GROUPS 2048 // ... and at least this many workgroups
 #endif
 #ifndef LSE_BLK_SLEEP
 #define LSE_BLK_SLEEP 8            // s_sleep argument between polls (x 64 clocks)
@@ -107,11 +107,11 @@ typedef float v4b4 __attribute__((ext_vector_type(4), aligned(4)));
 struct BlkSweep {
   int lp, act, w;
 };
-__host__ __device__ inline BlkSweep blk_sweep(int inner) {
+__host__ __device__ inline BlkSweep blk_sweep(int inner, int threads = kBlkThreads) {
   const int g = (inner % 4 == 0) ? 4 : ((inner % 2 == 0) ? 2 : 1);
   BlkSweep s;
   s.lp = inner / g;
-  s.act = (kBlkThreads / s.lp) * s.lp;
+  s.act = (threads / s.lp) * s.lp;
   s.w = 4 * s.act;
   return s;
 }
@@ -171,13 +171,13 @@ __device__ __forceinline__ float2 blk_merge_pairs(const float2 *p, int64_t chunk
 // lanes per column, lane g folding partials g, g + G, ... (max first, then
 // the weighted sum), then reduced across the G lanes; the same order on every
 // call.  G = the largest power of two up to nk / 4 (at most 64).
-template <int G>
+template <int G, int NT>
 __device__ __forceinline__ void blk_merge_g(const float2 *part, float2 *res, int inner, int nk,
                                             int t) {
   constexpr int kCpw = kWave / G;  // columns per wave and round
   const int lane = t % kWave, wave = t / kWave;
   const int g = lane % G;
-  for (int c0 = wave * kCpw; c0 < inner; c0 += (kBlkThreads / kWave) * kCpw) {
+  for (int c0 = wave * kCpw; c0 < inner; c0 += (NT / kWave) * kCpw) {
     const int c = c0 + lane / G;
     float m = -__builtin_inff();
     if (c < inner)
@@ -191,16 +191,17 @@ __device__ __forceinline__ void blk_merge_g(const float2 *part, float2 *res, int
   }
 }
 
+template <int NT = kBlkThreads>
 __device__ __forceinline__ void blk_merge_cols(const float2 *part, float2 *res, int inner, int nk,
                                                int t) {
   const int q = nk / 4;
-  if (q >= 64) blk_merge_g<64>(part, res, inner, nk, t);
-  else if (q >= 32) blk_merge_g<32>(part, res, inner, nk, t);
-  else if (q >= 16) blk_merge_g<16>(part, res, inner, nk, t);
-  else if (q >= 8) blk_merge_g<8>(part, res, inner, nk, t);
-  else if (q >= 4) blk_merge_g<4>(part, res, inner, nk, t);
-  else if (q >= 2) blk_merge_g<2>(part, res, inner, nk, t);
-  else blk_merge_g<1>(part, res, inner, nk, t);
+  if (q >= 64) blk_merge_g<64, NT>(part, res, inner, nk, t);
+  else if (q >= 32) blk_merge_g<32, NT>(part, res, inner, nk, t);
+  else if (q >= 16) blk_merge_g<16, NT>(part, res, inner, nk, t);
+  else if (q >= 8) blk_merge_g<8, NT>(part, res, inner, nk, t);
+  else if (q >= 4) blk_merge_g<4, NT>(part, res, inner, nk, t);
+  else if (q >= 2) blk_merge_g<2, NT>(part, res, inner, nk, t);
+  else blk_merge_g<1, NT>(part, res, inner, nk, t);
 }
 
 // Workgroup (o, c) of an (outer, chunks) grid, chunk fastest: planes
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(kBlkThreads) void axis_block_kernel(const float *__
     for (int e = 0; e < 4; ++e) part[4 * t + e] = make_float2(m[e], fold_total(s[e], comp[e]));
   }
   __syncthreads();
-  blk_merge_cols(part, res, inner, sw.w / inner, t);
+  blk_merge_cols<kBlkThreads>(part, res, inner, sw.w / inner, t);
   __syncthreads();
   if (t < inner) {
     const float M = res[t].x, S = res[t].y;
@@ -375,6 +376,9 @@ __global__ __launch_bounds__(kBlkThreads) void axis_block_apply_kernel(
 #define LSE_BLK_RES_K 16
 #endif
 constexpr int kBlkResK = LSE_BLK_RES_K;
+// Lanes per workgroup of the register-resident log_softmax: 256 for blocks of
+// up to 16 of their sweeps, 512 for larger ones and for split blocks.
+constexpr int kBlkResWide = 2 * kBlkThreads;
 #ifndef LSE_BLK_RES_WPE
 #define LSE_BLK_RES_WPE 4          // waves per SIMD the split kernel's registers must allow (0: any)
 #endif
@@ -436,6 +440,7 @@ __device__ __forceinline__ void blk_fold_fresh_mem(const float *xb, int64_t j, i
 
 // The chunk's (M, S) per column into res[0..inner) (through part and the
 // column merge; trailing barrier included).
+template <int NT>
 __device__ __forceinline__ void blk_chunk_columns(const float (&m)[4], const float (&s)[4],
                                                   float2 *part, float2 *res, int inner,
                                                   const BlkSweep &sw, int t) {
@@ -444,7 +449,7 @@ __device__ __forceinline__ void blk_chunk_columns(const float (&m)[4], const flo
     for (int e = 0; e < 4; ++e) part[4 * t + e] = make_float2(m[e], s[e]);
   }
   __syncthreads();
-  blk_merge_cols(part, res, inner, sw.w / inner, t);
+  blk_merge_cols<NT>(part, res, inner, sw.w / inner, t);
   __syncthreads();
 }
 
@@ -473,15 +478,15 @@ __device__ __forceinline__ bool blk_wait_slots(const uint64_t *slots, int64_t k,
 //     chunks (or computes the missing ones itself), merges the block's pairs
 //     per column in chunk order, and writes.  spin_limit 0 is a test mode in
 //     which owners publish nothing, so every pair comes from a helper.
-template <int K, bool SPLIT>
-__global__ __launch_bounds__(kBlkThreads)
+template <int K, bool SPLIT, int NT>
+__global__ __launch_bounds__(NT)
 #if LSE_BLK_RES_WPE
 __attribute__((amdgpu_waves_per_eu(LSE_BLK_RES_WPE)))
 #endif
 void axis_block_resident_kernel(
     const float *__restrict__ x, float *__restrict__ y, AxisDims d, int64_t chunks, int64_t rc,
     uint64_t *__restrict__ slots, uint32_t spin_limit) {
-  __shared__ float2 part[4 * kBlkThreads];
+  __shared__ float2 part[4 * NT];
   __shared__ float2 res[kBlkMaxInner];
   __shared__ int s_state;
   const int t = threadIdx.x;
@@ -489,7 +494,7 @@ void axis_block_resident_kernel(
   const int64_t c = b % chunks;
   const int64_t o = b / chunks;
   const int inner = (int)d.inner;
-  const BlkSweep sw = blk_sweep(inner);
+  const BlkSweep sw = blk_sweep(inner, NT);
   const int64_t r0 = c * rc;
   const int64_t r1 = (d.R - r0 < rc) ? d.R : r0 + rc;
   const int64_t f0 = r0 * inner, f1 = r1 * inner;
@@ -508,7 +513,7 @@ void axis_block_resident_kernel(
   }
   float m[4], s[4];
   blk_fold_fresh<K>(q, m, s);
-  blk_chunk_columns(m, s, part, res, inner, sw, t);
+  blk_chunk_columns<NT>(m, s, part, res, inner, sw, t);
   if constexpr (SPLIT) {
     uint64_t *bs = slots + o * chunks * inner;
     if (t < inner && spin_limit != 0)
@@ -533,7 +538,7 @@ void axis_block_resident_kernel(
         const int64_t hj = hr0 * inner + 4 * t;
         float hm[4], hs[4];
         blk_fold_fresh_mem<K>(xb, hj, hf1, sw.w, act, hm, hs);
-        blk_chunk_columns(hm, hs, part, res, inner, sw, t);
+        blk_chunk_columns<NT>(hm, hs, part, res, inner, sw, t);
         if (t < inner) publish_pair_once(bs + j * inner + t, pack_pair(res[t].x, res[t].y));
       }
       __syncthreads();
@@ -586,7 +591,7 @@ __global__ __launch_bounds__(256) void blk_clear_kernel(uint64_t *__restrict__ p
 
 struct BlkPlan {
   int64_t chunks, rc;
-  int mode, k;
+  int mode, k, nt;
 };
 
 enum BlkLaunch { kLaunchFold = 0, kLaunchResident = 1, kLaunchResidentSplit = 2 };
@@ -605,31 +610,41 @@ bool blk_plan(const AxisDims &d, bool lsm, bool with_ws, BlkPlan &p) {
   const int64_t n = d.R * d.inner;
   p.k = 0;
   if (lsm && LSE_BLK_RESIDENT) {
-    // one workgroup per block, held in registers
-    for (int k = 4; k <= kBlkResK; k *= 2) {
-      if (n <= (int64_t)k * sw.w && d.outer <= kMaxBlkGroups) {
+    // one workgroup per block, held in registers: 256 lanes with 4, 8 or 16
+    // sweeps, else 512 lanes with 16 (wider workgroups leave most lanes of a
+    // small block idle: (40000, 200, 13) 5900 -> 3700 GB/s)
+    const BlkSweep rs = blk_sweep((int)d.inner, kBlkThreads);
+    const BlkSweep rw = blk_sweep((int)d.inner, kBlkResWide);
+    const int64_t cap[4] = {4LL * rs.w, 8LL * rs.w, 16LL * rs.w, (int64_t)kBlkResK * rw.w};
+    const int ks[4] = {4, 8, 16, kBlkResK};
+    for (int i = 0; i < 4; ++i) {
+      const int nt = i < 3 ? kBlkThreads : kBlkResWide;
+      if (n <= cap[i] && d.outer <= 0xffffffffLL / nt) {
         p.chunks = 1;
         p.rc = d.R;
-        p.k = k;
+        p.k = ks[i];
+        p.nt = nt;
         p.mode = kLaunchResident;
         return true;
       }
     }
-    // chunks of at most kBlkResK sweeps, of near-equal whole periods, that
-    // wait for each other; only on grids of several workgroups per slot
-    // (with about one, loading and waiting do not overlap across workgroups)
+    // chunks of at most kBlkResK sweeps of 512 lanes, of near-equal whole
+    // periods, that wait for each other; only on grids of several
+    // workgroups per slot (with about one, loading and waiting do not
+    // overlap across workgroups)
     if (with_ws) {
-      const int64_t per = (int64_t)sw.lp * 4 / d.inner;  // planes per period
-      const int64_t rc_max = (int64_t)kBlkResK * sw.w / d.inner;
+      const int64_t per = (int64_t)rw.lp * 4 / d.inner;  // planes per period
+      const int64_t rc_max = (int64_t)kBlkResK * rw.w / d.inner;
       int64_t chunks = (d.R + rc_max - 1) / rc_max;
       int64_t rc = (d.R + chunks - 1) / chunks;
       rc = (rc + per - 1) / per * per;
       chunks = (d.R + rc - 1) / rc;
       if (chunks <= LSE_BLK_RES_MAX_CHUNKS && d.outer * chunks >= LSE_BLK_RES_MIN_GROUPS &&
-          d.outer * chunks <= kMaxBlkGroups) {
+          d.outer * chunks <= 0xffffffffLL / kBlkResWide) {
         p.chunks = chunks;
         p.rc = rc;
         p.k = kBlkResK;
+        p.nt = kBlkResWide;
         p.mode = kLaunchResidentSplit;
         return true;
       }
@@ -702,20 +717,19 @@ bool launch_blocks(const float *x, float *out, const AxisDims &d, bool lsm, bool
   const dim3 grid((uint32_t)(d.outer * p.chunks));
   const dim3 block(kBlkThreads);
   if (p.mode == kLaunchResident) {
-    switch (p.k) {
-      case 4:
-        hipLaunchKernelGGL((axis_block_resident_kernel<4, false>), grid, block, 0, stream, x, out,
-                           d, p.chunks, p.rc, nullptr, 0u);
-        break;
-      case 8:
-        hipLaunchKernelGGL((axis_block_resident_kernel<8, false>), grid, block, 0, stream, x, out,
-                           d, p.chunks, p.rc, nullptr, 0u);
-        break;
-      default:
-        hipLaunchKernelGGL((axis_block_resident_kernel<kBlkResK, false>), grid, block, 0, stream,
-                           x, out, d, p.chunks, p.rc, nullptr, 0u);
-        break;
-    }
+    const dim3 rblock((uint32_t)p.nt);
+    if (p.nt == kBlkResWide)
+      hipLaunchKernelGGL((axis_block_resident_kernel<kBlkResK, false, kBlkResWide>), grid, rblock,
+                         0, stream, x, out, d, p.chunks, p.rc, nullptr, 0u);
+    else if (p.k == 4)
+      hipLaunchKernelGGL((axis_block_resident_kernel<4, false, kBlkThreads>), grid, rblock, 0,
+                         stream, x, out, d, p.chunks, p.rc, nullptr, 0u);
+    else if (p.k == 8)
+      hipLaunchKernelGGL((axis_block_resident_kernel<8, false, kBlkThreads>), grid, rblock, 0,
+                         stream, x, out, d, p.chunks, p.rc, nullptr, 0u);
+    else
+      hipLaunchKernelGGL((axis_block_resident_kernel<16, false, kBlkThreads>), grid, rblock, 0,
+                         stream, x, out, d, p.chunks, p.rc, nullptr, 0u);
     e = hipGetLastError();
     return true;
   }
@@ -727,8 +741,9 @@ bool launch_blocks(const float *x, float *out, const AxisDims &d, bool lsm, bool
                        stream, slots, words);
     e = hipGetLastError();
     if (e != hipSuccess) return true;
-    hipLaunchKernelGGL((axis_block_resident_kernel<kBlkResK, true>), grid, block, 0, stream, x,
-                       out, d, p.chunks, p.rc, slots, chain_spin_limit());
+    hipLaunchKernelGGL((axis_block_resident_kernel<kBlkResK, true, kBlkResWide>), grid,
+                       dim3(kBlkResWide), 0, stream, x, out, d, p.chunks, p.rc, slots,
+                       chain_spin_limit());
     e = hipGetLastError();
     return true;
   }

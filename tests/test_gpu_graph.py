@@ -145,7 +145,7 @@ def test_graph_split_axis_and_long_rows():
 def test_graph_contiguous_blocks():
     """Contiguous blocks of short runs: chunk pairs then a merge (logsumexp),
     register-resident chunks that wait for each other after a clear kernel
-    (log_softmax over 4400 chunk workgroups), a block per workgroup held in
+    (log_softmax over 2200 chunk workgroups), a block per workgroup held in
     registers, workspaces passed in (no allocation inside the capture)."""
     x = inputs.normal((40, 4000, 49), seed=14, device=DEV)
     o = torch.empty((40, 49), device=DEV)
