@@ -441,7 +441,7 @@ def bench_secondary(steps=10, warmup=3):
         "lse_hbm_frac": round(nb_lse / lse_ms / 1e6 / HBM_PEAK_GBS, 4),
         "log_softmax_ms": round(lsm_ms, 4), "log_softmax_GB/s": round(nb_lsm / lsm_ms / 1e6, 1),
         "log_softmax_hbm_frac": round(nb_lsm / lsm_ms / 1e6 / HBM_PEAK_GBS, 4),
-        "note": "log_softmax: 7 chunks per block held in registers, pairs exchanged through the workspace"}
+        "note": "log_softmax: 4 chunks per block held in registers, pairs exchanged through the workspace"}
     del x, o, y
     x = inputs.normal((1, LONG_ROW), seed=23, device="cuda")
     o = torch.empty((1,), device="cuda")
