@@ -1,10 +1,10 @@
 // lse_blocks.hip — logsumexp and log_softmax over the middle axis of an
 // (outer, R, inner) array whose (R, inner) blocks are each one contiguous run
 // of memory and whose inner run is short: 2 to 256 columns, such as a
-// reduction over the channels of 7 x 7 feature maps.  A
-// plane of such a block is a few hundred bytes, so kernels that give each
-// lane columns of its own read it in short pieces, one value per access when
-// the run is not a multiple of 4.
+// reduction over the channels of 7 x 7 feature maps.  A plane of such a block
+// is a few hundred bytes, so kernels that give each lane columns of its own
+// read it in short pieces, one value per access when the run is not a
+// multiple of 4.
 //
 // POPCORNBENCH FW-GLM-5-1 l1_p29 (torch.logsumexp over a leading axis): each
 // output is the max-shifted sum over its R values, which here lie inner
@@ -26,9 +26,10 @@
 //     workgroup takes a whole block, and log_softmax reads it again;
 //   * log_softmax keeps its values in registers where they fit (the split-row
 //     protocol of log_softmax_rows, per column): a block of up to 16 sweeps
-//     is one workgroup's, loaded once and written from registers; a longer
-//     one (with a workspace) is split into chunks of 16 sweeps whose
-//     workgroups publish their (m, s) per column into zeroed slots
+//     of a 256- or 512-lane workgroup is that workgroup's, loaded once and
+//     written from registers; a longer one (with a workspace) is split into
+//     chunks of up to 16 sweeps of 512 lanes whose workgroups publish their
+//     (m, s) per column into zeroed slots
 //     (compare-and-swap from 0), wait for their siblings', merge them in
 //     chunk order and write from registers.  A workgroup that has waited too
 //     long computes every still-missing sibling chunk's pairs itself from x,
@@ -469,8 +470,9 @@ __device__ __forceinline__ bool blk_wait_slots(const uint64_t *slots, int64_t k,
 }
 
 // log_softmax with the values in registers.  Workgroup (o, c) of an
-// (outer, chunks) grid, chunk fastest, holds floats f0 + 4 t + k w (k < K) of
-// chunk c (rc = K w / inner planes, a whole number of periods).
+// (outer, chunks) grid of NT-lane workgroups, chunk fastest, holds floats
+// f0 + 4 t + k w (k < K) of chunk c (rc planes, a whole number of periods,
+// rc inner <= K w).
 //   !SPLIT (chunks = 1): the block's (M, S) per column come from this
 //     workgroup alone.
 //   SPLIT: slots[(o chunks + c) inner + col] receive the chunk's packed
