@@ -187,3 +187,23 @@ def test_concurrent_streams_match_sequential():
         torch.cuda.synchronize()
         for got, ref in zip((ya, yb, oa, ob), seq):
             assert torch.equal(got, ref)
+
+
+def test_concurrent_streams_block_split():
+    """Two streams each running the register-resident block split (chunks that
+    wait for each other, workspaces from the binding) while the other holds
+    part of the GPU: both results equal the sequential ones bit for bit."""
+    xa = inputs.normal((1100, 1000, 49), seed=21, device=DEV)
+    xb = inputs.normal((700, 701, 127), seed=22, device=DEV)
+    seq = [L.log_softmax_axis(xa, 1), L.log_softmax_axis(xb, 1)]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            ya = L.log_softmax_axis(xa, 1)
+        with torch.cuda.stream(s2):
+            yb = L.log_softmax_axis(xb, 1)
+        torch.cuda.synchronize()
+        assert torch.equal(ya, seq[0]) and torch.equal(yb, seq[1])
