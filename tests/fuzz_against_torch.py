@@ -3,7 +3,8 @@ the GPU (a supplementary check, not a parity test: parity is against the fp64
 oracle in the test_gpu_* files).  Shapes, views (offsets, padded planes and
 runs, row pitches), scales and special values are drawn at random; every call
 goes through the Python binding (workspace entry points) and the axis calls
-also through the entry points without a workspace.
+also through the entry points without a workspace; the fused conv chain is
+checked against conv2d, group_norm, tanh and hardswish in float64 torch.
 
 torch's log_softmax and softmax give NaN for every entry of a row or column
 holding +inf; the oracle and the kernels give -inf (log_softmax) or 0
@@ -37,7 +38,7 @@ def bad(got, ref, atol=1e-5, rtol=2e-6):
 def logu(lo, hi): return int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
 t0 = time.time(); n_cases = 0; fails = []
 while time.time() - t0 < budget_s:
-    kind = rng.choice(["axis", "axis", "rows"])
+    kind = rng.choice(["axis", "axis", "rows", "chain"])
     sigma = float(rng.choice([0.5, 2.0, 8.0]))
     if kind == "axis":
         inner = logu(1, 5000); R = logu(1, 200000)
@@ -65,6 +66,25 @@ while time.time() - t0 < budget_s:
         nb += bad(o2, ref_l) + (0 if pinf else bad(y2, ref_y))
         tag = f"axis {outer}x{R}x{inner} pad {pad_pl},{pad_in} off {off} sigma {sigma}"
         del buf, x, xd, o2, y2, got_l, got_y, ref_l, ref_y
+    elif kind == "chain":
+        # conv 3x3 (8 -> 64) -> GroupNorm -> tanh -> hardswish -> + conv -> logsumexp over
+        # channels, against the same steps in float64 torch; 5e-4 relative, as the chain's tests
+        N = int(rng.integers(1, 5)); H = logu(3, 200); W = logu(3, 200)
+        groups = int(rng.choice([1, 2, 4, 8, 16]))
+        x = torch.randn(N, 8, H, W, device=DEV) * sigma
+        w = (torch.rand(64, 8, 3, 3, device=DEV) * 2 - 1) / math.sqrt(72)
+        b = (torch.rand(64, device=DEV) * 2 - 1) / math.sqrt(72)
+        g = 1 + (torch.rand(64, device=DEV) - 0.5) if rng.random() < 0.5 else torch.ones(64, device=DEV)
+        be = (torch.rand(64, device=DEV) - 0.5) if rng.random() < 0.5 else torch.zeros(64, device=DEV)
+        got = L.fused_conv_gn_act_lse(x, w, b, g, be, groups, 1e-5)
+        c = torch.nn.functional.conv2d(x.double(), w.double(), b.double())
+        gn = torch.nn.functional.group_norm(c, groups, g.double(), be.double(), 1e-5)
+        u = c + torch.nn.functional.hardswish(torch.tanh(gn))
+        ref = torch.logsumexp(u, 1, keepdim=True)
+        torch.cuda.synchronize()
+        nb = bad(got, ref, atol=0.0, rtol=5e-4)
+        tag = f"chain N={N} H={H} W={W} groups={groups} sigma {sigma}"
+        del x, w, b, g, be, got, c, gn, u, ref
     else:
         cols = logu(1, 3_000_000); rows = logu(1, max(1, min(5000, 20_000_000 // cols)))
         pitch = cols + int(rng.choice([0, 0, 1, 4, 33])); off = int(rng.choice([0, 0, 1, 3]))
