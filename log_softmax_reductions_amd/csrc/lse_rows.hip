@@ -891,8 +891,14 @@ __global__ __launch_bounds__(kRowsThreads) void rows_lse_stream_kernel(
 // 3 columns 3908 / 3378 -> 4886 / 4014, 17 columns 3568 / 3395 -> 3600 / 3857;
 // from 99 columns on 8-byte accesses measured 6-15 % slower)
 #ifndef LSE_ROWS_LSE_SEG_MAX
-#define LSE_ROWS_LSE_SEG_MAX 2048  // logsumexp-only rows up to this long take a segment
+#define LSE_ROWS_LSE_SEG_MAX 2048  // logsumexp-only rows up to this long take a segment,
 #endif
+#ifndef LSE_ROWS_LSE_SEG_VEC_MAX
+#define LSE_ROWS_LSE_SEG_VEC_MAX 3072  // ... and up to 4096 unless 16-byte aligned and longer than this
+#endif
+// (same box, GB/s: (200000, 2049) 4520 -> 6485, (50000, 2500) 5342 -> 6467, (131072, 3072)
+// 6373 -> 6640, (100000, 4096) at a 4-byte offset 6360 -> 6561; aligned (100000, 4096) 7104 ->
+// 6551 in a segment, so it keeps the workgroup kernel)
 // Interleaved blocks (axis calls with inner > 1) take a wave-wide segment up
 // to 64 values per lane: the axis kernels they would fall back to read such
 // blocks 8-16 bytes per plane and lane.
@@ -1587,7 +1593,11 @@ hipError_t launch_rows_lse(const float *x, int64_t rows, int64_t cols, int64_t l
                            int64_t ldo, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const bool vec = (cols % 4 == 0) && (ldx % 4 == 0) && ((uintptr_t)x % 16 == 0);
-  if (cols <= LSE_ROWS_LSE_SEG_MAX)
+  // Segments up to 2048 values, and up to 4096 for rows the workgroup kernel
+  // reads one value per access (off the 16-byte grid) or that leave most of
+  // its lanes with few values (up to 3072 columns).
+  if (cols <= LSE_ROWS_LSE_SEG_MAX ||
+      (cols <= kSegInterleavedMax && !(vec && cols > LSE_ROWS_LSE_SEG_VEC_MAX)))
     return launch_rows_seg<kOutLse>(x, out, rows, cols, ldx, ldo, vec, stream);
   return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
     const dim3 grid((uint32_t)nr);

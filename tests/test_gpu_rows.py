@@ -111,12 +111,15 @@ def test_rows_short_ragged(orc, cols, layout):
 
 
 @pytest.mark.parametrize("rows,cols,off", [(3000, 1025, 0), (2000, 1500, 1), (1000, 2048, 0),
-                                           (500, 2049, 0), (40, 50257, 0), (30, 50257, 1),
-                                           (2000, 16385, 0)])
+                                           (500, 2049, 0), (700, 3001, 1), (600, 3072, 0),
+                                           (500, 4095, 0), (400, 4096, 1), (300, 4096, 0),
+                                           (40, 50257, 0), (30, 50257, 1), (2000, 16385, 0)])
 def test_row_logsumexp_segments_and_split(orc, rows, cols, off):
     """Last-axis logsumexp: rows up to 2048 values in wave-wide segments (up
-    to 32 values per lane), longer rows off the 16-byte grid (odd lengths, a
-    4-byte offset) split into chunk pairs whatever the number of rows."""
+    to 32 values per lane), up to 4096 off the 16-byte grid or up to 3072
+    aligned (64 per lane; aligned 4096 keeps the workgroup kernel), longer rows
+    off the 16-byte grid (odd lengths, a 4-byte offset) split into chunk pairs
+    whatever the number of rows."""
     buf = inputs.normal((rows * cols + off,), seed=rows + cols + off, sigma=3.0, device=DEV)
     x = buf[off:].view(rows, cols)
     x[1, 7] = float("inf")
