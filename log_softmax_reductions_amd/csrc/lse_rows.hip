@@ -1445,6 +1445,83 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
   });
 }
 
+// ---------------------------------------------------------- multi-row
+// Aligned rows of 6144-16384 columns, at least 8192 of them: one 512-lane
+// workgroup per row would hold only 12-32 values per lane (24-64 KiB per
+// workgroup, its two reductions and barriers amortized over few bytes).  Here
+// RPW rows share a workgroup, 512 / RPW lanes each with 64 values per lane (up
+// to 128 KiB per workgroup, as the 32768-column rows): the row's waves
+// all-reduce its max and sum through LDS, and y is written from the registers.
+// (Same box, log_softmax GB/s: (50000, 8192) 5434 -> 5950, (25000, 16384) 4997
+// -> 5527, (40000, 10000) 5469 -> 5783; rows of 4100 columns, half of each
+// row's lanes idle, 5628 -> 5275, and (128, 16384), half the workgroups, 2185 ->
+// 1698, keep one workgroup per row.)
+#ifndef LSE_ROWS_MULTI
+#define LSE_ROWS_MULTI 1
+#endif
+template <int RPW, bool SOFTMAX>
+__global__ __launch_bounds__(kRowsThreads) void rows_multi_kernel(const float *__restrict__ x,
+                                                                  float *__restrict__ y,
+                                                                  int64_t rows, int64_t cols,
+                                                                  int64_t ldx, int64_t ldy) {
+  constexpr int kLanes = kRowsThreads / RPW;  // lanes per row
+  constexpr int kWpr = kLanes / kWave;        // waves per row
+  constexpr int VPL = 64;
+  __shared__ float red[kNW];
+  const int t = threadIdx.x;
+  const int r = t / kLanes, tl = t % kLanes;
+  const int wave = t / kWave, lane = t % kWave;
+  const int64_t row = (int64_t)blockIdx.x * RPW + r;
+  const bool live = row < rows;
+  const float *xr = x + (live ? row : 0) * ldx;
+  float v[VPL];
+#pragma unroll
+  for (int q = 0; q < VPL / 4; ++q) {
+    const int64_t idx = ((int64_t)q * kLanes + tl) * 4;  // a wave reads 1 KiB per q
+    if (live && idx < cols) {  // cols % 4 == 0: a vector is wholly in or out
+      const v4f f = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(xr + idx));
+      v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = -__builtin_inff();
+    }
+  }
+  float lm = v[0];
+#pragma unroll
+  for (int i = 1; i < VPL; ++i) lm = fmaxf(lm, v[i]);
+  lm = wave_allreduce(lm, OpMax{});
+  if (lane == 0) red[wave] = lm;
+  __syncthreads();
+  float M = red[r * kWpr];
+#pragma unroll
+  for (int w = 1; w < kWpr; ++w) M = fmaxf(M, red[r * kWpr + w]);
+  __syncthreads();
+  float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (is_finite(M)) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) ls[i % 4] += exp_base2(v[i] - M);
+  } else {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) ls[i % 4] += pair_term_nonfinite(v[i], M);
+  }
+  const float lsum = wave_allreduce((ls[0] + ls[1]) + (ls[2] + ls[3]), OpSum{});
+  if (lane == 0) red[wave] = lsum;
+  __syncthreads();
+  float S = red[r * kWpr];
+#pragma unroll
+  for (int w = 1; w < kWpr; ++w) S += red[r * kWpr + w];
+  if (!live) return;
+  const float k = out_scale<SOFTMAX>(S);
+  float *yr = y + row * ldy;
+#pragma unroll
+  for (int q = 0; q < VPL / 4; ++q) {
+    const int64_t idx = ((int64_t)q * kLanes + tl) * 4;
+    if (idx < cols)
+      store4(yr + idx, out_value<SOFTMAX>(v[4 * q], M, k), out_value<SOFTMAX>(v[4 * q + 1], M, k),
+             out_value<SOFTMAX>(v[4 * q + 2], M, k), out_value<SOFTMAX>(v[4 * q + 3], M, k));
+  }
+}
+
 template <bool SOFTMAX>
 hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols, int64_t ldx,
                             int64_t ldy, void *ws, hipStream_t stream) {
@@ -1454,6 +1531,19 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
   if (p.nchunks == 1 && cols <= LSE_ROWS_SEG_MAX)
     return launch_rows_seg<SOFTMAX ? kOutSoftmax : kOutLogSoftmax>(x, y, rows, cols, ldx, ldy,
                                                                    vec, stream);
+  if (LSE_ROWS_MULTI && p.nchunks == 1 && vec && cols >= 6144 && cols <= 16384 && rows >= 8192) {
+    const int rpw = cols <= 8192 ? 4 : 2;
+    return for_row_batches(rows, kMaxRowsWorkgroups * rpw, [&](int64_t r0, int64_t nr) {
+      const dim3 grid((uint32_t)((nr + rpw - 1) / rpw));
+      if (rpw == 4)
+        hipLaunchKernelGGL((rows_multi_kernel<4, SOFTMAX>), grid, dim3(kRowsThreads), 0, stream,
+                           x + r0 * ldx, y + r0 * ldy, nr, cols, ldx, ldy);
+      else
+        hipLaunchKernelGGL((rows_multi_kernel<2, SOFTMAX>), grid, dim3(kRowsThreads), 0, stream,
+                           x + r0 * ldx, y + r0 * ldy, nr, cols, ldx, ldy);
+      return hipGetLastError();
+    });
+  }
   if (p.nchunks == 1) {
     return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
       return launch_rows_vpl<false, SOFTMAX>(vpl_for(cols), vec, dim3((uint32_t)nr), x + r0 * ldx,

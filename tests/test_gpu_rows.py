@@ -497,3 +497,30 @@ def test_rows_long_streams_within_tolerance(orc, cols, off):
     idx = np.arange(0, cols, 997)
     ref = xc[:, idx].astype(np.float64) - lse[:, None]
     compare(y.cpu().numpy()[:, idx], ref, what=f"long row lsm ({rows},{cols})+{off}")
+
+
+@pytest.mark.parametrize("rows,cols", [(8193, 8192), (8195, 6144), (8192, 12288), (8194, 16384)])
+@pytest.mark.parametrize("softmax", [False, True])
+def test_rows_multi_row_workgroups(orc, rows, cols, softmax):
+    """Aligned rows of 6144-16384 columns, at least 8192 of them, share a
+    workgroup (4 or 2 rows, 64 values per lane); a ragged last workgroup and
+    special values in rows of one workgroup.  Sampled rows against the oracle,
+    every row through the property that its outputs are a distribution."""
+    x = inputs.normal((rows, cols), seed=rows + cols, sigma=3.0, device=DEV)
+    x[0, :] = -float("inf")
+    x[1, 5] = float("inf")
+    x[2, cols - 1] = float("nan")
+    x[3, :] = -float("inf"); x[3, 17] = 2.0
+    y = L.softmax_rows(x) if softmax else L.log_softmax_rows(x)
+    torch.cuda.synchronize()
+    idx = [0, 1, 2, 3, 4, 5, rows // 2, rows - 3, rows - 2, rows - 1]
+    xs = x[idx].cpu().numpy()
+    if softmax:
+        compare(y[idx].cpu().numpy(), orc.softmax_rows(xs), rtol=1e-5, atol=1e-37,
+                what=f"multi-row softmax {rows}x{cols}")
+        tot = y[4:].double().sum(1)
+    else:
+        ref, _ = orc.log_softmax_rows(xs)
+        compare(y[idx].cpu().numpy(), ref, what=f"multi-row log_softmax {rows}x{cols}")
+        tot = y[4:].double().exp().sum(1)
+    assert (tot - 1.0).abs().max().item() < 1e-4
