@@ -1446,9 +1446,9 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
 }
 
 // ---------------------------------------------------------- multi-row
-// Aligned rows of 6144-16384 columns, at least 8192 of them: one 512-lane
-// workgroup per row would hold only 12-32 values per lane (24-64 KiB per
-// workgroup, its two reductions and barriers amortized over few bytes).  Here
+// Rows of 6144-16384 columns, at least 8192 of them: one 512-lane workgroup
+// per row would hold only 12-32 values per lane (24-64 KiB per workgroup, its
+// two reductions and barriers amortized over few bytes).  Here
 // RPW rows share a workgroup, 512 / RPW lanes each with 64 values per lane (up
 // to 128 KiB per workgroup, as the 32768-column rows): the row's waves
 // all-reduce its max and sum through LDS, and y is written from the registers.
@@ -1459,14 +1459,26 @@ hipError_t launch_rows_seg(const float *x, float *y, int64_t rows, int64_t cols,
 #ifndef LSE_ROWS_MULTI
 #define LSE_ROWS_MULTI 1
 #endif
-template <int RPW, bool SOFTMAX>
+#ifndef LSE_ROWS_MULTI_A4
+#define LSE_ROWS_MULTI_A4 1   // ... also rows off the 16-byte grid
+#endif
+#ifndef LSE_ROWS_MULTI_LSE
+#define LSE_ROWS_MULTI_LSE 1  // ... and the row logsumexp
+#endif
+template <int RPW, int OUT, bool A4>
 __global__ __launch_bounds__(kRowsThreads) void rows_multi_kernel(const float *__restrict__ x,
                                                                   float *__restrict__ y,
                                                                   int64_t rows, int64_t cols,
                                                                   int64_t ldx, int64_t ldy) {
+  // A4: rows at their own 4-byte phase (an odd length or pitch, an offset
+  // view): the row's lanes share it, so 16-byte accesses at 4-byte alignment
+  // over the row's whole vectors; its last cols % 4 values ride in up to
+  // three extra registers of the lane that would hold the next vector.
   constexpr int kLanes = kRowsThreads / RPW;  // lanes per row
   constexpr int kWpr = kLanes / kWave;        // waves per row
   constexpr int VPL = 64;
+  constexpr bool SOFTMAX = OUT == kOutSoftmax;
+  const float ninf = -__builtin_inff();
   __shared__ float red[kNW];
   const int t = threadIdx.x;
   const int r = t / kLanes, tl = t % kLanes;
@@ -1474,21 +1486,33 @@ __global__ __launch_bounds__(kRowsThreads) void rows_multi_kernel(const float *_
   const int64_t row = (int64_t)blockIdx.x * RPW + r;
   const bool live = row < rows;
   const float *xr = x + (live ? row : 0) * ldx;
+  const int64_t c4 = cols & ~(int64_t)3;  // the whole vectors
   float v[VPL];
 #pragma unroll
   for (int q = 0; q < VPL / 4; ++q) {
     const int64_t idx = ((int64_t)q * kLanes + tl) * 4;  // a wave reads 1 KiB per q
-    if (live && idx < cols) {  // cols % 4 == 0: a vector is wholly in or out
-      const v4f f = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(xr + idx));
+    if (live && idx < c4) {
+      v4f f;
+      if constexpr (A4) {
+        const v4a4 g = load4_a4(xr + idx);
+        f = v4f{g.x, g.y, g.z, g.w};
+      } else {
+        f = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(xr + idx));
+      }
       v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * q + e] = -__builtin_inff();
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = ninf;
     }
   }
-  float lm = v[0];
+  const int tail = (int)(cols - c4);
+  const bool tail_lane = A4 && live && tail > 0 && tl == (int)((c4 / 4) % kLanes);
+  float xt[3] = {ninf, ninf, ninf};
+  if (tail_lane)
+    for (int e = 0; e < tail; ++e) xt[e] = xr[c4 + e];
+  float lm = fmaxf(xt[0], fmaxf(xt[1], xt[2]));
 #pragma unroll
-  for (int i = 1; i < VPL; ++i) lm = fmaxf(lm, v[i]);
+  for (int i = 0; i < VPL; ++i) lm = fmaxf(lm, v[i]);
   lm = wave_allreduce(lm, OpMax{});
   if (lane == 0) red[wave] = lm;
   __syncthreads();
@@ -1500,9 +1524,13 @@ __global__ __launch_bounds__(kRowsThreads) void rows_multi_kernel(const float *_
   if (is_finite(M)) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) ls[i % 4] += exp_base2(v[i] - M);
+#pragma unroll
+    for (int e = 0; e < 3; ++e) ls[e] += exp_base2(xt[e] - M);
   } else {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) ls[i % 4] += pair_term_nonfinite(v[i], M);
+#pragma unroll
+    for (int e = 0; e < 3; ++e) ls[e] += pair_term_nonfinite(xt[e], M);
   }
   const float lsum = wave_allreduce((ls[0] + ls[1]) + (ls[2] + ls[3]), OpSum{});
   if (lane == 0) red[wave] = lsum;
@@ -1511,15 +1539,54 @@ __global__ __launch_bounds__(kRowsThreads) void rows_multi_kernel(const float *_
 #pragma unroll
   for (int w = 1; w < kWpr; ++w) S += red[r * kWpr + w];
   if (!live) return;
-  const float k = out_scale<SOFTMAX>(S);
-  float *yr = y + row * ldy;
+  if constexpr (OUT == kOutLse) {
+    if (tl == 0) y[row * ldy] = pair_lse(M, S);
+  } else {
+    const float k = out_scale<SOFTMAX>(S);
+    float *yr = y + row * ldy;
 #pragma unroll
-  for (int q = 0; q < VPL / 4; ++q) {
-    const int64_t idx = ((int64_t)q * kLanes + tl) * 4;
-    if (idx < cols)
-      store4(yr + idx, out_value<SOFTMAX>(v[4 * q], M, k), out_value<SOFTMAX>(v[4 * q + 1], M, k),
-             out_value<SOFTMAX>(v[4 * q + 2], M, k), out_value<SOFTMAX>(v[4 * q + 3], M, k));
+    for (int q = 0; q < VPL / 4; ++q) {
+      const int64_t idx = ((int64_t)q * kLanes + tl) * 4;
+      if (idx < c4) {
+        const float o0 = out_value<SOFTMAX>(v[4 * q], M, k);
+        const float o1 = out_value<SOFTMAX>(v[4 * q + 1], M, k);
+        const float o2 = out_value<SOFTMAX>(v[4 * q + 2], M, k);
+        const float o3 = out_value<SOFTMAX>(v[4 * q + 3], M, k);
+        if constexpr (A4)
+          store4_a4(yr + idx, o0, o1, o2, o3);
+        else
+          store4(yr + idx, o0, o1, o2, o3);
+      }
+    }
+    if (tail_lane)
+      for (int e = 0; e < tail; ++e)
+        __builtin_nontemporal_store(out_value<SOFTMAX>(xt[e], M, k), yr + c4 + e);
   }
+}
+
+// Rows of 6144-16384 columns, at least 8192 of them, through
+// rows_multi_kernel; false when the call does not fit.  vec: x and y rows
+// 16-byte aligned with cols and the pitches multiples of 4.
+template <int OUT>
+bool launch_rows_multi(const float *x, float *y, int64_t rows, int64_t cols, int64_t ldx,
+                       int64_t ldy, bool vec, hipStream_t stream, hipError_t &e) {
+  if (!LSE_ROWS_MULTI || cols < 6144 || cols > 16384 || rows < 8192) return false;
+  if (!vec && !LSE_ROWS_MULTI_A4) return false;
+  const int rpw = cols <= 8192 ? 4 : 2;
+  e = for_row_batches(rows, kMaxRowsWorkgroups * rpw, [&](int64_t r0, int64_t nr) {
+    const dim3 grid((uint32_t)((nr + rpw - 1) / rpw)), block(kRowsThreads);
+    const float *xb = x + r0 * ldx;
+    float *yb = y + r0 * ldy;  // the row logsumexp: out[row * ldy]
+    if (rpw == 4) {
+      if (vec) hipLaunchKernelGGL((rows_multi_kernel<4, OUT, false>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy);
+      else hipLaunchKernelGGL((rows_multi_kernel<4, OUT, true>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy);
+    } else {
+      if (vec) hipLaunchKernelGGL((rows_multi_kernel<2, OUT, false>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy);
+      else hipLaunchKernelGGL((rows_multi_kernel<2, OUT, true>), grid, block, 0, stream, xb, yb, nr, cols, ldx, ldy);
+    }
+    return hipGetLastError();
+  });
+  return true;
 }
 
 template <bool SOFTMAX>
@@ -1531,18 +1598,11 @@ hipError_t launch_rows_mode(const float *x, float *y, int64_t rows, int64_t cols
   if (p.nchunks == 1 && cols <= LSE_ROWS_SEG_MAX)
     return launch_rows_seg<SOFTMAX ? kOutSoftmax : kOutLogSoftmax>(x, y, rows, cols, ldx, ldy,
                                                                    vec, stream);
-  if (LSE_ROWS_MULTI && p.nchunks == 1 && vec && cols >= 6144 && cols <= 16384 && rows >= 8192) {
-    const int rpw = cols <= 8192 ? 4 : 2;
-    return for_row_batches(rows, kMaxRowsWorkgroups * rpw, [&](int64_t r0, int64_t nr) {
-      const dim3 grid((uint32_t)((nr + rpw - 1) / rpw));
-      if (rpw == 4)
-        hipLaunchKernelGGL((rows_multi_kernel<4, SOFTMAX>), grid, dim3(kRowsThreads), 0, stream,
-                           x + r0 * ldx, y + r0 * ldy, nr, cols, ldx, ldy);
-      else
-        hipLaunchKernelGGL((rows_multi_kernel<2, SOFTMAX>), grid, dim3(kRowsThreads), 0, stream,
-                           x + r0 * ldx, y + r0 * ldy, nr, cols, ldx, ldy);
-      return hipGetLastError();
-    });
+  if (p.nchunks == 1) {
+    hipError_t e = hipSuccess;
+    if (launch_rows_multi<SOFTMAX ? kOutSoftmax : kOutLogSoftmax>(x, y, rows, cols, ldx, ldy, vec,
+                                                                  stream, e))
+      return e;
   }
   if (p.nchunks == 1) {
     return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
@@ -1689,6 +1749,10 @@ hipError_t launch_rows_lse(const float *x, int64_t rows, int64_t cols, int64_t l
   if (cols <= LSE_ROWS_LSE_SEG_MAX ||
       (cols <= kSegInterleavedMax && !(vec && cols > LSE_ROWS_LSE_SEG_VEC_MAX)))
     return launch_rows_seg<kOutLse>(x, out, rows, cols, ldx, ldo, vec, stream);
+  if (LSE_ROWS_MULTI_LSE) {
+    hipError_t e = hipSuccess;
+    if (launch_rows_multi<kOutLse>(x, out, rows, cols, ldx, ldo, vec, stream, e)) return e;
+  }
   return for_row_batches(rows, kMaxRowsWorkgroups, [&](int64_t r0, int64_t nr) {
     const dim3 grid((uint32_t)nr);
     const float *xb = x + r0 * ldx;

@@ -499,14 +499,20 @@ def test_rows_long_streams_within_tolerance(orc, cols, off):
     compare(y.cpu().numpy()[:, idx], ref, what=f"long row lsm ({rows},{cols})+{off}")
 
 
-@pytest.mark.parametrize("rows,cols", [(8193, 8192), (8195, 6144), (8192, 12288), (8194, 16384)])
+@pytest.mark.parametrize("rows,cols,off", [(8193, 8192, 0), (8195, 6144, 0), (8192, 12288, 0),
+                                           (8194, 16384, 0), (8193, 8191, 0), (8192, 16383, 0),
+                                           (8195, 6145, 0), (8192, 16384, 1), (8193, 8192, 3)])
 @pytest.mark.parametrize("softmax", [False, True])
-def test_rows_multi_row_workgroups(orc, rows, cols, softmax):
-    """Aligned rows of 6144-16384 columns, at least 8192 of them, share a
-    workgroup (4 or 2 rows, 64 values per lane); a ragged last workgroup and
-    special values in rows of one workgroup.  Sampled rows against the oracle,
-    every row through the property that its outputs are a distribution."""
-    x = inputs.normal((rows, cols), seed=rows + cols, sigma=3.0, device=DEV)
+def test_rows_multi_row_workgroups(orc, rows, cols, off, softmax):
+    """Rows of 6144-16384 columns, at least 8192 of them, share a workgroup (4
+    or 2 rows, 64 values per lane): aligned, odd lengths (16-byte accesses at
+    each row's phase, the last cols % 4 values in extra registers) and views
+    at a 4- or 12-byte offset; a ragged last workgroup and special values in
+    rows of one workgroup.  Sampled rows against the oracle, every row through
+    the property that its outputs are a distribution, and the row logsumexp
+    of sampled rows."""
+    buf = inputs.normal((rows * cols + off,), seed=rows + cols + off, sigma=3.0, device=DEV)
+    x = buf[off:].view(rows, cols)
     x[0, :] = -float("inf")
     x[1, 5] = float("inf")
     x[2, cols - 1] = float("nan")
@@ -517,10 +523,14 @@ def test_rows_multi_row_workgroups(orc, rows, cols, softmax):
     xs = x[idx].cpu().numpy()
     if softmax:
         compare(y[idx].cpu().numpy(), orc.softmax_rows(xs), rtol=1e-5, atol=1e-37,
-                what=f"multi-row softmax {rows}x{cols}")
+                what=f"multi-row softmax {rows}x{cols}+{off}")
         tot = y[4:].double().sum(1)
     else:
         ref, _ = orc.log_softmax_rows(xs)
-        compare(y[idx].cpu().numpy(), ref, what=f"multi-row log_softmax {rows}x{cols}")
+        compare(y[idx].cpu().numpy(), ref, what=f"multi-row log_softmax {rows}x{cols}+{off}")
         tot = y[4:].double().exp().sum(1)
     assert (tot - 1.0).abs().max().item() < 1e-4
+    out = L.lse_reduce_axis(x, 1)
+    torch.cuda.synchronize()
+    compare(out[idx].cpu().numpy(), orc.lse_axis(xs.reshape(len(idx), cols, 1)).reshape(-1),
+            what=f"multi-row logsumexp {rows}x{cols}+{off}")
