@@ -297,11 +297,13 @@ __global__ __launch_bounds__(256) void axis_block_merge_kernel(const float2 *__r
   out[o * d.yso + col] = f.x + logf(f.y);
 }
 
-// The same merge for long chunk lists: a wave per (o, col), lane l folding
-// chunks l, l + 64, ... (4 loads in flight) into a running pair, then the
-// lanes' pairs reduced across the wave (the same order on every call).
-// LSM: fin[o inner + col] = (M, log S) for the apply launch; else the
-// logsumexp into out.
+// The same merge for long chunk lists: a wave per (o, col), lane l loading
+// chunks l, l + 64, ..., l + 15 * 64 at once (one round of loads for up to
+// 1024 chunks) and folding them into its running pair against one shared
+// maximum, then the lanes' pairs reduced across the wave (the same order on
+// every call).  LSM: fin[o inner + col] = (M, log S) for the apply launch;
+// else the logsumexp into out.
+constexpr int kBlkMergeQ = 16;
 template <bool LSM>
 __global__ __launch_bounds__(256) void axis_block_merge_wide_kernel(
     const float2 *__restrict__ pairs, float *__restrict__ out, float2 *__restrict__ fin,
@@ -311,17 +313,19 @@ __global__ __launch_bounds__(256) void axis_block_merge_wide_kernel(
   if (i >= d.outer * d.inner) return;  // whole waves
   const float2 *p = pairs + i * chunks;
   float m = -__builtin_inff(), s = 0.0f;
-  for (int64_t k0 = lane; k0 < chunks; k0 += 4 * kWave) {
-    float2 q[4];
+  for (int64_t k0 = lane; k0 < chunks; k0 += kBlkMergeQ * kWave) {
+    float2 q[kBlkMergeQ];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kBlkMergeQ; ++u)
       q[u] = (k0 + u * kWave < chunks) ? p[k0 + u * kWave] : make_float2(-__builtin_inff(), 0.0f);
+    float mn = m;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float mn = fmaxf(m, q[u].x);
-      s = fold_weighted(m, s, mn) + fold_weighted(q[u].x, q[u].y, mn);
-      m = mn;
-    }
+    for (int u = 0; u < kBlkMergeQ; ++u) mn = fmaxf(mn, q[u].x);
+    float t = fold_weighted(m, s, mn);
+#pragma unroll
+    for (int u = 0; u < kBlkMergeQ; ++u) t += fold_weighted(q[u].x, q[u].y, mn);
+    s = t;
+    m = mn;
   }
   const float M = wave_allreduce(m, OpMax{});
   const float S = wave_allreduce(fold_weighted(m, s, M), OpSum{});
@@ -681,13 +685,19 @@ bool blk_plan(const AxisDims &d, bool lsm, bool with_ws, BlkPlan &p) {
 // (on it the axis kernels and the column split were about as fast), except
 // logsumexp over blocks of LSE_BLK_BIG_BLOCK floats or more, which the
 // blocks read faster whatever the run (wider runs the axis kernels read well
-// otherwise, and their log_softmax reads x once).
+// otherwise, and their log_softmax reads x once), and log_softmax over blocks
+// of LSE_BLK_LSM_BIG floats or more (few long blocks, where both read x twice:
+// 2-12 % faster there, 5-23 % slower on blocks of 1-2 M floats).
+#ifndef LSE_BLK_LSM_BIG
+#define LSE_BLK_LSM_BIG 4194304
+#endif
 bool blk_wanted(const AxisDims &d, bool lsm, bool with_ws, const float *x, const float *out) {
   if (LSE_BLK_GATE == 2) return true;
   const int64_t n = d.R * d.inner;
   if (n < LSE_BLK_MIN_BLOCK) return false;
   const bool big_lse = !lsm && n >= LSE_BLK_BIG_BLOCK;
   if (d.inner > LSE_BLK_GATE_INNER) return big_lse;
+  if (LSE_BLK_LSM_BIG && lsm && n >= LSE_BLK_LSM_BIG) return true;
   const uintptr_t a = (uintptr_t)x | (lsm ? (uintptr_t)out : 0);
   const int64_t st = d.inner | d.xso | (lsm ? d.yso : 0);
   const bool grid16 = st % 4 == 0 && a % 16 == 0;

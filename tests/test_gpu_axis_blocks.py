@@ -36,7 +36,10 @@ BLOCK_SHAPES = [(40, 4000, 49), (33, 5001, 5), (64, 2000, 3), (48, 3001, 13), (3
                 # logsumexp over large blocks of wider runs (one partial per lane and column)
                 (40, 600, 196), (36, 520, 255), (33, 300, 256),
                 # few long blocks: hundreds of chunks per block, merged by a wave per column
-                (1, 300000, 49), (3, 100003, 7), (2, 200000, 6), (1, 150001, 100)]
+                (1, 300000, 49), (3, 100003, 7), (2, 200000, 6), (1, 150001, 100),
+                # log_softmax over few long blocks of aligned runs (pairs, a wave per
+                # column merging up to 1024 chunks per round of loads, then the apply)
+                (1, 300000, 64), (3, 100001, 16), (2, 600000, 8), (5, 40000, 128)]
 
 
 @pytest.mark.parametrize("outer,R,inner", BLOCK_SHAPES)
