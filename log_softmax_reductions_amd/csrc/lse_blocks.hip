@@ -80,7 +80,16 @@ namespace {
 #define LSE_BLK_RES_MAX_CHUNKS 32  // ... for blocks of at most this many 16-sweep chunks
 #endif
 #ifndef LSE_BLK_RES_MIN_GROUPS
-#define LSE_BLK_RES_MIN_GROUPS 2048 // ... and at least this many workgroups
+#define LSE_BLK_RES_MIN_GROUPS 2048 // ... and at least this many workgroups,
+#endif
+#ifndef LSE_BLK_RES_FEW_CHUNKS
+#define LSE_BLK_RES_FEW_CHUNKS 16  // ... or, for blocks of at most this many chunks,
+#endif
+#ifndef LSE_BLK_RES_FEW_GROUPS
+#define LSE_BLK_RES_FEW_GROUPS 256 // ... at least this many (160 up to 8 chunks),
+#endif
+#ifndef LSE_BLK_RES_SLOTS
+#define LSE_BLK_RES_SLOTS 512      // ... outside (1, 2) x the 512-lane workgroups resident at once
 #endif
 #ifndef LSE_BLK_SLEEP
 #define LSE_BLK_SLEEP 8            // s_sleep argument between polls (x 64 clocks)
@@ -635,9 +644,11 @@ bool blk_plan(const AxisDims &d, bool lsm, bool with_ws, BlkPlan &p) {
       }
     }
     // chunks of at most kBlkResK sweeps of 512 lanes, of near-equal whole
-    // periods, that wait for each other; only on grids of several
-    // workgroups per slot (with about one, loading and waiting do not
-    // overlap across workgroups)
+    // periods, that wait for each other; on grids of several workgroups per
+    // slot (with about one, loading and waiting do not overlap across
+    // workgroups), or of blocks of few chunks (same box, GB/s, fold path ->
+    // resident: (256, 2048, 49) 3430 -> 4240, (64, 8000, 25) 2820 -> 3610,
+    // (32, 30000, 5) 1560 -> 1920; 640 workgroups of 16 chunks -9 %)
     if (with_ws) {
       const int64_t per = (int64_t)rw.lp * 4 / d.inner;  // planes per period
       const int64_t rc_max = (int64_t)kBlkResK * rw.w / d.inner;
@@ -645,7 +656,14 @@ bool blk_plan(const AxisDims &d, bool lsm, bool with_ws, BlkPlan &p) {
       int64_t rc = (d.R + chunks - 1) / chunks;
       rc = (rc + per - 1) / per * per;
       chunks = (d.R + rc - 1) / rc;
-      if (chunks <= LSE_BLK_RES_MAX_CHUNKS && d.outer * chunks >= LSE_BLK_RES_MIN_GROUPS &&
+      // grids of fewer workgroups: blocks of few chunks, most CUs busy, and
+      // not just past one round of resident workgroups (whose last blocks
+      // would then run alone)
+      const int64_t g = d.outer * chunks;
+      const bool few = chunks <= LSE_BLK_RES_FEW_CHUNKS &&
+                       g >= (chunks <= 8 ? 160 : LSE_BLK_RES_FEW_GROUPS) &&
+                       (g <= LSE_BLK_RES_SLOTS || g >= 2 * LSE_BLK_RES_SLOTS);
+      if (chunks <= LSE_BLK_RES_MAX_CHUNKS && (g >= LSE_BLK_RES_MIN_GROUPS || few) &&
           d.outer * chunks <= 0xffffffffLL / kBlkResWide) {
         p.chunks = chunks;
         p.rc = rc;

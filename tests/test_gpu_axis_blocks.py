@@ -135,10 +135,12 @@ def test_blocks_bit_identical_reruns():
         assert torch.equal(a, b) and torch.equal(ya, yb)
 
 
-@pytest.mark.parametrize("outer,R,inner", [(1100, 1000, 49), (1100, 8001, 5), (700, 701, 127)])
+@pytest.mark.parametrize("outer,R,inner", [(1100, 1000, 49), (1100, 8001, 5), (700, 701, 127),
+                                           (50, 4000, 49), (32, 30000, 5), (20, 50000, 10),
+                                           (256, 2048, 49), (100, 6000, 63)])
 def test_blocks_resident_helping_bit_identical(orc, outer, R, inner):
-    """log_softmax over blocks split into chunks that wait for each other (at
-    least 4096 workgroups; ragged last chunks): at a poll limit of 0 no owner
+    """log_softmax over blocks split into chunks that wait for each other (grids
+    of 160 to 2200 workgroups; ragged last chunks): at a poll limit of 0 no owner
     publishes, so every chunk's pairs come from the helping path (re-read from
     x); the result must equal the default run bit for bit, and the oracle."""
     x = inputs.normal((outer, R, inner), seed=outer + R + inner, sigma=3.0, device=DEV)
