@@ -172,7 +172,7 @@ lse_status_t log_softmax_axis_strided_ws(const float *x, float *y, int64_t outer
  * Rows longer than one workgroup's register tile are split across several
  * workgroups whose (max, sum) partials are merged through `ws`
  *                                           [LSM] multi-block-per-row idea.
- * Rows of up to 64 such chunks (2M columns) read x once; longer rows take
+ * Rows of up to 128 such chunks (4M columns) read x once; longer rows take
  * three launches (chunk pairs, a merge per row, the write), reading x twice.
  * ws: device workspace of at least log_softmax_rows_workspace_bytes(rows,
  * cols) bytes (0 for short rows, in which case ws may be NULL).  Its contents
@@ -189,7 +189,7 @@ lse_status_t log_softmax_rows(const float *x, float *y, int64_t rows,
  * workspace is a static device array inside the library (1 MiB per GPU the
  * library runs on, held until the process ends) instead of a caller buffer.
  * It allocates nothing.  Calls whose pairs exceed that array (rows x
- * ceil(cols / 32768) > 131040 for rows of up to 64 chunks, e.g. more than
+ * ceil(cols / 32768) > 131040 for rows of up to 128 chunks, e.g. more than
  * 10920 rows of 393216 columns; rows x (ceil(cols / 16384) + 1) > 131040 for
  * longer rows) return LSE_ERR_WORKSPACE with nothing launched.  All calls on one
  * GPU share the array: calls that overlap on one GPU (other streams, other

@@ -41,7 +41,7 @@
 //     rows per wave (rows_seg_kernel), with segment-wide DPP / permlane
 //     reductions and no LDS; the last-axis reductions of the axis calls run
 //     here too (logsumexp alone: one value per row).
-//   * Rows of more than 64 chunks, whose chunks may not all be resident at
+//   * Rows of more than 128 chunks, whose chunks may not all be resident at
 //     once to wait for each other, take three launches: chunk pairs (cached
 //     loads), a merge per row, the write from the merged (M, log S), reading x
 //     twice.
@@ -72,10 +72,12 @@ constexpr int kNW = kRowsThreads / kWave;  // waves per workgroup
 #endif
 #ifndef LSE_ROWS_WAIT_MAX_CHUNKS
 // Rows of up to this many chunks merge by waiting for their sibling
-// workgroups; longer ones (more than 2M columns) take three launches, since a
+// workgroups; longer ones (more than 4M columns) take three launches, since a
 // row's chunks may then not all fit on the GPU at once and the waiting
-// workgroups would fall back to recomputing their siblings' pairs.
-#define LSE_ROWS_WAIT_MAX_CHUNKS 64
+// workgroups would fall back to recomputing their siblings' pairs (one row of
+// 153 chunks waiting: 12 % slower than three launches; rows of 65-128 chunks:
+// 1-56 % faster, e.g. (64, 2200000) 3900 -> 5300 GB/s).
+#define LSE_ROWS_WAIT_MAX_CHUNKS 128
 #endif
 constexpr uint32_t kDefaultSpinLimit = 1u << 24;
 // Poll limit of the split rows' and the conv chain's waits, per host thread

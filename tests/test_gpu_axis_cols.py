@@ -140,13 +140,13 @@ def test_cols_workspace_reuse_and_determinism(orc):
             what="cols ws reuse")
 
 
-@pytest.mark.parametrize("rows,cols,off", [(2, 2097153, 0), (1, 4194304, 0), (1, 3000001, 1),
-                                           (3, 2097152, 0)])
+@pytest.mark.parametrize("rows,cols,off", [(2, 4194305, 0), (1, 5000000, 0), (1, 4500001, 1),
+                                           (3, 4194304, 0), (2, 2097153, 0), (1, 3000001, 1)])
 @pytest.mark.parametrize("softmax", [False, True])
 def test_rows_many_chunks(orc, rows, cols, off, softmax):
-    """Rows of more than 64 chunks (2M columns) take three launches (tile
-    pairs, merge per row, write); exactly 64 chunks still wait for each other.
-    Odd lengths and a 4-byte offset take the scalar write."""
+    """Rows of more than 128 chunks (4M columns) take three launches (tile
+    pairs, merge per row, write); exactly 128 chunks, and 65-92, still wait
+    for each other.  Odd lengths and a 4-byte offset take the scalar write."""
     buf = inputs.normal((rows * cols + off,), seed=cols + off, sigma=2.0, device=DEV)
     x = buf[off:].view(rows, cols)
     xc = x.cpu().numpy()
@@ -166,7 +166,7 @@ def test_rows_many_chunks(orc, rows, cols, off, softmax):
 
 def test_rows_many_chunks_special(orc):
     """Three-launch rows: all -inf, +inf, NaN in the last tile, one finite value."""
-    cols = 2200000
+    cols = 4400000
     x = inputs.normal((4, cols), seed=21, device=DEV)
     x[0, :] = -float("inf")
     x[1, 1234567] = float("inf")

@@ -119,14 +119,14 @@ def test_graph_strided_calls():
 
 def test_graph_split_axis_and_long_rows():
     """The split paths: 16 outputs over 200000 planes (column split, the
-    binding's workspace allocated inside the capture), a row of 2.2M columns
+    binding's workspace allocated inside the capture), a row of 4.4M columns
     (three launches), split logsumexp rows, short rows in segments."""
     x = inputs.normal((200000, 16), seed=10, device=DEV)
     o1 = torch.empty(16, device=DEV)
     o2 = torch.empty_like(x)
-    x2 = inputs.normal((1, 2200000), seed=11, device=DEV)
+    x2 = inputs.normal((1, 4400000), seed=11, device=DEV)
     y2 = torch.empty_like(x2)
-    ws2 = torch.empty(L.log_softmax_rows_workspace_bytes(1, 2200000), dtype=torch.uint8,
+    ws2 = torch.empty(L.log_softmax_rows_workspace_bytes(1, 4400000), dtype=torch.uint8,
                       device=DEV)
     x3 = inputs.normal((4, 40000), seed=12, device=DEV)
     o3 = torch.empty(4, device=DEV)

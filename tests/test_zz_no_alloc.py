@@ -35,10 +35,10 @@ def test_noalloc_two_calls_second_smaller(orc):
 
 
 def test_noalloc_long_rows_three_launches(orc):
-    """Rows of more than 64 chunks (three launches; tile pairs and the per-row
+    """Rows of more than 128 chunks (three launches; tile pairs and the per-row
     (M, log S) in the scratch), then a shorter split row."""
-    print("case: noalloc (2, 3000001) then (3, 300000)", flush=True)
-    _both(orc, 2, 3000001, seed=93, sample=[0, 1])
+    print("case: noalloc (2, 4500001) then (3, 300000)", flush=True)
+    _both(orc, 2, 4500001, seed=93, sample=[0, 1])
     _both(orc, 3, 300000, seed=94, sample=[0, 2])
 
 
